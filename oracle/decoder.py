@@ -1,0 +1,273 @@
+"""Plain CPU definition of one batch-1 greedy decode step (test infrastructure only).
+
+This is the oracle the GPU tile schedule is checked against.  It computes the
+standard pre-norm Llama / Qwen3 decoder step with no blocking, splitting,
+fusion or reordering: the tile graph on the GPU is an exact regrouping of the
+same arithmetic (row tiles of each matrix-vector product, split-KV softmax),
+so the only legitimate differences are FP32 summation order and the
+exp/rsqrt/sin implementations.
+
+Sources (the pages give the workload, not the formulas):
+
+* Tiles page ("Tiles: Scheduling LLM Decoding as a Graph of Tiles"), intro and
+  "What the code contains": Llama 3.2 1B, BF16, batch 1, greedy selection, a
+  CPU reference checked against the Hugging Face model.
+* TileInfer.jl roadmap ("History and roadmap"), "M8 so far" table: the fused
+  decode ops are q/k norm + RoPE + KV write, residual add + RMSNorm, and
+  SwiGLU; "Milestones" M2: the reference model computes in Float32.
+
+Readings of points the pages leave open (each is also listed in the design doc):
+
+R1  RMSNorm is y = x / sqrt(mean(x^2) + eps) * g (plain gain), the mean taken
+    over the whole vector (over head_dim for the per-head q/k norm).
+R2  RoPE uses the "rotate-half" pairing (i, i + hd/2) with inverse frequency
+    theta^(-2i/hd) and no frequency scaling.  The angle p * theta^(-2i/hd) is
+    formed in FP64 and cos/sin are rounded to FP32 (FP64 mode keeps FP64).
+R3  GQA: query head h reads KV head h // (n_heads / n_kv_heads).
+R4  Attention scale 1/sqrt(hd); causal, including the current position; no
+    biases, soft-caps or windows.
+R5  K is cached after q/k norm and RoPE; K and V are rounded to BF16
+    (round-to-nearest-even) when written, and the current step attends to the
+    rounded values read back from the cache.
+R6  Activations and the residual stream stay in FP32; only weights and the
+    KV cache are BF16.
+R7  SwiGLU: a = silu(W_gate h) * (W_up h), silu(z) = z * sigmoid(z).
+R8  Greedy selection is argmax over the logits, lowest index on ties.
+R9  The per-layer hidden state is the residual stream after the layer's MLP
+    residual add.
+R10 With tied embeddings the LM head is the embedding matrix.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "bf16_round",
+    "bf16_bits_to_float",
+    "float_to_bf16_bits",
+    "rmsnorm",
+    "rope_cos_sin",
+    "apply_rope",
+    "attend",
+    "silu",
+    "OracleModel",
+]
+
+# ---------------------------------------------------------------------------
+# BF16 (definition: IEEE-754 binary32 truncated to 8 significant bits, rounded
+# to nearest, ties to even; exponent range of binary32).
+# ---------------------------------------------------------------------------
+
+_BF16_MIN_EXP = -126          # smallest normal exponent (as in binary32)
+_BF16_SIG_BITS = 8            # significant bits including the implicit one
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest BF16 value, ties to even, returned as float64.
+
+    Written from the definition of the format (8 significant bits, binary32
+    exponent range, gradual underflow, overflow to +-inf) rather than by bit
+    manipulation, so it is independent of any library conversion routine.
+    Works for float32 and float64 inputs alike.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    finite = np.isfinite(x) & (x != 0.0)
+    xf = x[finite]
+    _, e = np.frexp(xf)                    # xf = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, _BF16_MIN_EXP + 1)   # gradual underflow below 2**-126
+    ulp = np.ldexp(1.0, e - _BF16_SIG_BITS)
+    r = np.round(xf / ulp) * ulp           # np.round: half to even; exact scaling
+    with np.errstate(over="ignore"):
+        r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    out[finite] = r
+    return out
+
+
+def float_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) of round-to-nearest-even(x)."""
+    r = bf16_round(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f = r.astype(np.float32)           # exact: r has <= 8 significant bits
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    bits[np.isnan(r)] = 0x7FC0
+    return bits
+
+
+def bf16_bits_to_float(u: np.ndarray, dtype=np.float32) -> np.ndarray:
+    """Exact widening of BF16 bit patterns (uint16) to float32 / float64."""
+    u = np.asarray(u, dtype=np.uint16)
+    f = (u.astype(np.uint32) << 16).view(np.float32)
+    return f.astype(dtype, copy=False)
+
+
+# ---------------------------------------------------------------------------
+# Layer pieces
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """R1: y = x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    dt = x.dtype
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return (x / np.sqrt(ms + dt.type(eps))) * g
+
+
+def rope_cos_sin(pos: int, hd: int, theta: float, dtype=np.float32):
+    """R2: cos/sin of p * theta^(-2i/hd), i < hd/2, angles in FP64."""
+    i = np.arange(hd // 2, dtype=np.float64)
+    inv_freq = float(theta) ** (-2.0 * i / hd)
+    phi = float(pos) * inv_freq
+    return np.cos(phi).astype(dtype), np.sin(phi).astype(dtype)
+
+
+def apply_rope(u: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """R2: rotate pairs (i, i + hd/2) of every row of u by the angles."""
+    half = u.shape[-1] // 2
+    a = u[..., :half]
+    b = u[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """R4: softmax(K q / sqrt(hd)) V for one query head over L positions.
+
+    q: [hd], K, V: [L, hd] (already widened).  Max-subtracted softmax.
+    """
+    dt = q.dtype
+    s = (K @ q) * dt.type(1.0 / math.sqrt(q.shape[-1]))
+    w = np.exp(s - s.max())
+    w = w / w.sum()
+    return w @ V
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """R7: z * sigmoid(z)."""
+    one = z.dtype.type(1.0)
+    return z / (one + np.exp(-z))
+
+
+# ---------------------------------------------------------------------------
+# Whole decode step
+# ---------------------------------------------------------------------------
+
+
+class OracleModel:
+    """The decoder with BF16 weights given as uint16 bit arrays.
+
+    ``cfg`` is any object with the attributes n_layers, hidden, n_heads,
+    n_kv_heads, head_dim, ffn, vocab, rope_theta, rms_eps, qk_norm and
+    tie_embeddings.  ``weights`` is a dict of uint16 arrays:
+    ``embed`` [V, H], ``final_norm`` [H], optional ``lm_head`` [V, H] and
+    ``layers``: a list of dicts with attn_norm [H], wq [n_q*hd, H],
+    wk/wv [n_kv*hd, H], optional q_norm/k_norm [hd], wo [H, n_q*hd],
+    mlp_norm [H], w_gate/w_up [F, H], w_down [H, F].
+
+    The KV cache is a dict with uint16 arrays ``k`` and ``v`` of shape
+    [n_layers, n_kv_heads, capacity, hd]; :meth:`step` writes position ``pos``.
+    """
+
+    def __init__(self, cfg, weights: dict, dtype=np.float32, widen_once: bool = True):
+        self.cfg = cfg
+        self.dtype = np.dtype(dtype)
+        self.w = weights
+        self.widen_once = widen_once
+        self._cache: dict = {}
+
+    # widened weights -------------------------------------------------------
+    def _get(self, layer: Optional[int], name: str) -> np.ndarray:
+        key = (layer, name)
+        if key in self._cache:
+            return self._cache[key]
+        src = self.w[name] if layer is None else self.w["layers"][layer][name]
+        arr = bf16_bits_to_float(src, self.dtype)
+        if self.widen_once:
+            self._cache[key] = arr
+        return arr
+
+    def _embed_row(self, token: int) -> np.ndarray:
+        return bf16_bits_to_float(self.w["embed"][token], self.dtype).copy()
+
+    def _lm_head(self) -> np.ndarray:
+        if self.cfg.tie_embeddings or self.w.get("lm_head") is None:
+            return self._get(None, "embed")
+        return self._get(None, "lm_head")
+
+    # one step ----------------------------------------------------------------
+    def step(self, kv: dict, token: int, pos: int):
+        """Run one decode step for ``token`` at position ``pos``.
+
+        Returns (logits [V], hidden [n_layers, H]); writes K/V at ``pos``.
+        """
+        c = self.cfg
+        dt = self.dtype
+        nq, nkv, hd = c.n_heads, c.n_kv_heads, c.head_dim
+        group = nq // nkv
+        eps = float(c.rms_eps)
+        if not (0 <= token < c.vocab):
+            raise ValueError("token out of range")
+        if pos >= kv["k"].shape[2]:
+            raise ValueError("KV capacity exceeded")
+        x = self._embed_row(token)
+        hidden = np.empty((c.n_layers, c.hidden), dtype=dt)
+        if dt == np.float64:
+            cos, sin = rope_cos_sin(pos, hd, c.rope_theta, np.float64)
+        else:
+            cos, sin = rope_cos_sin(pos, hd, c.rope_theta, np.float32)
+        for l in range(c.n_layers):
+            h = rmsnorm(x, self._get(l, "attn_norm"), eps)
+            q = (self._get(l, "wq") @ h).reshape(nq, hd)
+            k = (self._get(l, "wk") @ h).reshape(nkv, hd)
+            v = (self._get(l, "wv") @ h).reshape(nkv, hd)
+            if c.qk_norm:
+                q = rmsnorm(q, self._get(l, "q_norm"), eps)
+                k = rmsnorm(k, self._get(l, "k_norm"), eps)
+            q = apply_rope(q, cos, sin)
+            k = apply_rope(k, cos, sin)
+            kv["k"][l, :, pos, :] = float_to_bf16_bits(k)        # R5
+            kv["v"][l, :, pos, :] = float_to_bf16_bits(v)
+            attn = np.empty((nq, hd), dtype=dt)
+            for hh in range(nq):
+                g = hh // group                                    # R3
+                Kc = bf16_bits_to_float(kv["k"][l, g, : pos + 1], dt)
+                Vc = bf16_bits_to_float(kv["v"][l, g, : pos + 1], dt)
+                attn[hh] = attend(q[hh], Kc, Vc)
+            x = x + self._get(l, "wo") @ attn.reshape(-1)
+            h = rmsnorm(x, self._get(l, "mlp_norm"), eps)
+            a = silu(self._get(l, "w_gate") @ h) * (self._get(l, "w_up") @ h)
+            x = x + self._get(l, "w_down") @ a
+            hidden[l] = x                                          # R9
+        hf = rmsnorm(x, self._get(None, "final_norm"), eps)
+        logits = self._lm_head() @ hf
+        if not np.all(np.isfinite(logits)):
+            raise FloatingPointError("non-finite logit")
+        return logits, hidden
+
+    # drivers -----------------------------------------------------------------
+    def decode(self, kv: dict, token: int, pos0: int, n_steps: int,
+               teacher: Optional[Sequence[int]] = None, keep_hidden: bool = True):
+        """Greedy decode ``n_steps`` steps starting with ``token`` at ``pos0``.
+
+        Step i consumes ``token`` (i = 0), else the previous step's argmax
+        (free-running) or ``teacher[i - 1]`` (teacher-forced).  Returns a dict
+        with ``tokens`` [n] (argmax of each step, R8), ``logits`` [n, V] and
+        ``hidden`` [n, n_layers, H] (or None).
+        """
+        toks = np.empty(n_steps, dtype=np.int64)
+        logits_all = np.empty((n_steps, self.cfg.vocab), dtype=self.dtype)
+        hidden_all = (np.empty((n_steps, self.cfg.n_layers, self.cfg.hidden), dtype=self.dtype)
+                      if keep_hidden else None)
+        t = int(token)
+        for i in range(n_steps):
+            if i > 0:
+                t = int(teacher[i - 1]) if teacher is not None else int(toks[i - 1])
+            logits, hidden = self.step(kv, t, pos0 + i)
+            toks[i] = int(np.argmax(logits))                       # R8: first max
+            logits_all[i] = logits
+            if keep_hidden:
+                hidden_all[i] = hidden
+        return {"tokens": toks, "logits": logits_all, "hidden": hidden_all}

@@ -1,0 +1,458 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+library conversions, closed forms, invariants, hand-worked examples and brute
+force on tiny inputs.  Each test names the plausible mistake it would catch.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (OracleModel, apply_rope, attend, bf16_bits_to_float, bf16_round, float_to_bf16_bits, rmsnorm,
+                    rope_cos_sin, silu)
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------------------
+# BF16 rounding: pinned to torch's float32 -> bfloat16 conversion (RNE).
+# Catches: truncation instead of rounding, ties-away, wrong overflow/underflow.
+# ---------------------------------------------------------------------------
+
+def _torch_bits(x32):
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_round_matches_torch_random_and_ties():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(200_000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 200_000),
+        rng.standard_normal(1000).astype(np.float32),
+    ]).astype(np.float32)
+    # exact ties: low 16 bits = 0x8000 with both parities of bit 16
+    u = rng.integers(0x00800000, 0x7F000000, 20_000, dtype=np.uint32)
+    u = (u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    ties = u.view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    assert np.array_equal(float_to_bf16_bits(x), _torch_bits(x))
+
+
+def test_bf16_round_special_values():
+    f32 = np.finfo(np.float32)
+    x = np.array([0.0, -0.0, np.inf, -np.inf, f32.max, -f32.max, f32.tiny, f32.tiny / 3, 1e-45, -1e-45,
+                  3.3895314e38, 3.3961e38, 3.39e38, 1.0, 1.00390625, 1.005859375, 65504.0], dtype=np.float32)
+    assert np.array_equal(float_to_bf16_bits(x), _torch_bits(x))
+    nan_bits = float_to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(bf16_bits_to_float(nan_bits))[0]
+
+
+def test_bf16_round_float64_input_is_correctly_rounded():
+    # fp64 input exactly halfway between two bf16 values in fp64 but not in fp32 must still round correctly:
+    # 1 + 2^-8 (a tie -> 1.0), 1 + 2^-8 + 2^-40 (above the tie -> 1 + 2^-7).
+    x = np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8], dtype=np.float64)
+    assert list(bf16_round(x)) == [1.0, 1 + 2.0 ** -7, 1 + 4 * 2.0 ** -8]
+
+
+def test_bf16_widening_is_exact_for_every_pattern():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = bf16_bits_to_float(allbits)
+    t = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    finite = np.isfinite(t)
+    assert np.array_equal(f[finite], t[finite])
+    back = float_to_bf16_bits(f[finite])
+    assert np.array_equal(back, allbits[finite])
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm.  Catches: mean vs sum, missing sqrt, eps outside the sqrt, (1+g).
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_unit_rms_before_gain():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 2048)).astype(np.float32) * 3
+    g = (1 + 0.01 * rng.standard_normal(2048)).astype(np.float32)
+    y = rmsnorm(x, g, 0.0)
+    rms = np.sqrt(np.mean((y / g).astype(np.float64) ** 2, axis=-1))
+    assert np.allclose(rms, 1.0, atol=1e-6)
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    for c in [0.5, 3.0, -2.0, 1e-3]:
+        for eps in [1e-5, 1e-6, 0.25]:
+            x = np.full(64, c, dtype=np.float64)
+            y = rmsnorm(x, np.ones(64), eps)
+            assert np.allclose(y, c / math.sqrt(c * c + eps), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# RoPE.  Catches: interleaved vs rotate-half pairing, wrong frequency exponent,
+# sign of the rotation, angle in FP32.
+# ---------------------------------------------------------------------------
+
+def test_rope_hand_worked_example():
+    # hd = 4, theta = 100: inverse frequencies 100^0 = 1 and 100^(-1/2) = 0.1; pairs (0,2), (1,3).
+    cos, sin = rope_cos_sin(1, 4, 100.0, np.float64)
+    u = np.array([1.0, 2.0, 3.0, 4.0])
+    got = apply_rope(u, cos, sin)
+    want = [1 * math.cos(1) - 3 * math.sin(1),
+            2 * math.cos(0.1) - 4 * math.sin(0.1),
+            3 * math.cos(1) + 1 * math.sin(1),
+            4 * math.cos(0.1) + 2 * math.sin(0.1)]
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_hd2_is_plane_rotation_by_p_radians():
+    for p in [0, 1, 7, 1023, 32790]:
+        cos, sin = rope_cos_sin(p, 2, 5e5, np.float64)
+        got = apply_rope(np.array([1.0, 0.0]), cos, sin)
+        assert np.allclose(got, [math.cos(p), math.sin(p)], atol=1e-12)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    hd, theta = 128, 1e6
+    q = rng.standard_normal(hd)
+    k = rng.standard_normal(hd)
+    c0, s0 = rope_cos_sin(0, hd, theta, np.float64)
+    assert np.array_equal(apply_rope(q, c0, s0), q)
+    for p in [1, 100, 32767]:
+        c, s = rope_cos_sin(p, hd, theta, np.float64)
+        assert np.isclose(np.linalg.norm(apply_rope(q, c, s)), np.linalg.norm(q), rtol=1e-13)
+    # <R_m q, R_n k> depends only on m - n
+    def dot(m, n):
+        cm, sm = rope_cos_sin(m, hd, theta, np.float64)
+        cn, sn = rope_cos_sin(n, hd, theta, np.float64)
+        return apply_rope(q, cm, sm) @ apply_rope(k, cn, sn)
+    assert np.isclose(dot(10, 3), dot(1007, 1000), rtol=1e-9)
+    assert np.isclose(dot(5, 5), q @ k, rtol=1e-12)
+
+
+def test_rope_angle_formed_in_fp64():
+    # at p = 32790 an FP32 angle p*inv_freq would be off by up to ~1e-3 rad; the FP64 angle rounded once is not.
+    hd, theta, p = 128, 1e6, 32790
+    c, s = rope_cos_sin(p, hd, theta, np.float32)
+    i = np.arange(hd // 2)
+    phi = p * theta ** (-2.0 * i / hd)
+    assert np.array_equal(c, np.cos(phi).astype(np.float32))
+    assert np.array_equal(s, np.sin(phi).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Attention.  Catches: missing 1/sqrt(hd), softmax over the wrong axis,
+# missing max subtraction overflow, wrong weighting of V.
+# ---------------------------------------------------------------------------
+
+def _attend_bruteforce(q, K, V):
+    L, hd = K.shape
+    s = []
+    for j in range(L):
+        acc = 0.0
+        for d in range(hd):
+            acc += float(q[d]) * float(K[j, d])
+        s.append(acc / math.sqrt(hd))
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    z = sum(e)
+    out = []
+    for d in range(hd):
+        out.append(sum(e[j] / z * float(V[j, d]) for j in range(L)))
+    return np.array(out)
+
+
+def test_attend_bruteforce_tiny():
+    rng = np.random.default_rng(3)
+    for L in [1, 2, 5, 8]:
+        for hd in [2, 4, 8]:
+            q = rng.standard_normal(hd)
+            K = rng.standard_normal((L, hd)) * 2
+            V = rng.standard_normal((L, hd))
+            assert np.allclose(attend(q, K, V), _attend_bruteforce(q, K, V), rtol=1e-12, atol=1e-13)
+
+
+def test_attend_weights_sum_to_one_and_scale():
+    rng = np.random.default_rng(4)
+    L = 16
+    q = rng.standard_normal(L)
+    K = rng.standard_normal((L, L)) * 3
+    w = attend(q, K, np.eye(L))           # V = I returns the softmax weights
+    assert np.isclose(w.sum(), 1.0, rtol=1e-14)
+    assert np.all(w > 0)
+    # two keys along e0: weights are a logistic of (a - b) q0 / sqrt(hd)
+    hd = 16
+    q = np.zeros(hd); q[0] = 2.0
+    K = np.zeros((2, hd)); K[0, 0] = 1.5; K[1, 0] = -0.5
+    w = attend(q, K, np.eye(2, hd))[:2]
+    p0 = 1.0 / (1.0 + math.exp(-(2.0 * 1.5 - 2.0 * -0.5) / math.sqrt(hd)))
+    assert np.allclose(w, [p0, 1 - p0], rtol=1e-14)
+
+
+def test_attend_single_position_returns_v_exactly():
+    rng = np.random.default_rng(5)
+    for dt in [np.float32, np.float64]:
+        q = rng.standard_normal(64).astype(dt) * 100
+        K = rng.standard_normal((1, 64)).astype(dt)
+        V = rng.standard_normal((1, 64)).astype(dt)
+        assert np.array_equal(attend(q, K, V), V[0])
+
+
+def test_attend_equal_keys_is_mean_of_v():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal(8)
+    K = np.tile(rng.standard_normal(8), (10, 1))
+    V = rng.standard_normal((10, 8))
+    assert np.allclose(attend(q, K, V), V.mean(axis=0), rtol=1e-13)
+
+
+def test_attend_large_scores_do_not_overflow():
+    q = np.full(64, 50.0, dtype=np.float32)
+    K = np.full((3, 64), 40.0, dtype=np.float32)
+    K[1] = 41.0
+    V = np.eye(3, 64, dtype=np.float32)
+    w = attend(q, K, V)[:3]
+    assert np.all(np.isfinite(w)) and np.isclose(w.sum(), 1.0, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# SiLU.  Catches: sigmoid instead of silu, sign errors.
+# ---------------------------------------------------------------------------
+
+def test_silu_values():
+    z = np.array([0.0, 1.0, -1.0, 30.0, -30.0])
+    s = silu(z)
+    assert s[0] == 0.0
+    assert np.isclose(s[1], 0.7310585786300049, rtol=1e-15)        # 1 / (1 + e^-1)
+    assert np.isclose(s[2], -0.2689414213699951, rtol=1e-15)       # -1 / (1 + e)
+    assert np.isclose(s[3], 30.0, rtol=1e-12)
+    assert abs(s[4]) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# FP32 matrix-vector products stay within the classical error bound.
+# ---------------------------------------------------------------------------
+
+def test_fp32_matvec_within_error_bound():
+    rng = np.random.default_rng(7)
+    for K in [256, 2048, 9728]:
+        W = (rng.standard_normal((64, K)) * 0.02).astype(np.float32)
+        x = rng.standard_normal(K).astype(np.float32)
+        y32 = (W @ x).astype(np.float64)
+        y64 = W.astype(np.float64) @ x.astype(np.float64)
+        bound = K * 2.0 ** -24 * (np.abs(W).astype(np.float64) @ np.abs(x).astype(np.float64))
+        assert np.all(np.abs(y32 - y64) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# Whole decode step: closed forms on hand-built models.
+# ---------------------------------------------------------------------------
+
+class Cfg:
+    def __init__(self, **kw):
+        self.n_layers = 2
+        self.hidden = 8
+        self.n_heads = 2
+        self.n_kv_heads = 1
+        self.head_dim = 4
+        self.ffn = 8
+        self.vocab = 16
+        self.rope_theta = 10000.0
+        self.rms_eps = 1e-5
+        self.qk_norm = False
+        self.tie_embeddings = True
+        self.__dict__.update(kw)
+
+
+def _b(a):
+    return float_to_bf16_bits(np.asarray(a, dtype=np.float64))
+
+
+def _zero_model(c, rng):
+    H, F, hd = c.hidden, c.ffn, c.head_dim
+    qr, kr = c.n_heads * hd, c.n_kv_heads * hd
+    layers = []
+    for _ in range(c.n_layers):
+        d = dict(attn_norm=_b(np.ones(H)), wq=_b(np.zeros((qr, H))), wk=_b(np.zeros((kr, H))),
+                 wv=_b(np.zeros((kr, H))), wo=_b(np.zeros((H, qr))), mlp_norm=_b(np.ones(H)),
+                 w_gate=_b(np.zeros((F, H))), w_up=_b(np.zeros((F, H))), w_down=_b(np.zeros((H, F))))
+        if c.qk_norm:
+            d["q_norm"] = _b(np.ones(hd))
+            d["k_norm"] = _b(np.ones(hd))
+        layers.append(d)
+    return {"embed": _b(rng.standard_normal((c.vocab, H)) * 0.5), "final_norm": _b(np.ones(H)), "layers": layers}
+
+
+def _kv(c, cap):
+    shape = (c.n_layers, c.n_kv_heads, cap, c.head_dim)
+    return {"k": np.zeros(shape, np.uint16), "v": np.zeros(shape, np.uint16)}
+
+
+def test_step_residual_identity_and_head_closed_form():
+    """W_o = W_down = 0: the residual stream stays E[t]; with E[t] = c*1 the final
+    norm is c/sqrt(c^2+eps) and logits[r] = that times the row sum of E[r].
+    Catches: residual not carried, head applied to un-normed x, wrong final gain."""
+    c = Cfg()
+    rng = np.random.default_rng(8)
+    w = _zero_model(c, rng)
+    w["embed"][3] = _b(np.full(c.hidden, 0.75))
+    m = OracleModel(c, w, np.float64)
+    logits, hidden = m.step(_kv(c, 4), 3, 0)
+    assert np.array_equal(hidden[0], np.full(c.hidden, 0.75)) and np.array_equal(hidden[1], hidden[0])
+    E = bf16_bits_to_float(w["embed"], np.float64)
+    s = 0.75 / math.sqrt(0.75 ** 2 + c.rms_eps)
+    assert np.allclose(logits, s * E.sum(axis=1), rtol=1e-13)
+
+
+def test_step_uniform_attention_is_mean_of_cached_v_including_current():
+    """W_q = 0 makes every score 0, so each head returns the mean of V over
+    positions 0..p, where V[p] is this step's bf16-rounded v.  With W_o = I
+    and no MLP, x1 = x0 + concat_h mean_j V[g(h)][j].
+    Catches: current position excluded, v not rounded, GQA map, residual order."""
+    c = Cfg(n_layers=1, n_heads=2, n_kv_heads=1, head_dim=4, hidden=8)
+    rng = np.random.default_rng(9)
+    w = _zero_model(c, rng)
+    w["embed"][5] = _b(np.full(8, 0.5))
+    wv = np.zeros((4, 8)); wv[0, 0] = 0.3; wv[1, 1] = -1.7; wv[2, :] = 0.125; wv[3, 7] = 2.0
+    w["layers"][0]["wv"] = _b(wv)
+    w["layers"][0]["wo"] = _b(np.eye(8))
+    kv = _kv(c, 8)
+    p = 3
+    cached = rng.standard_normal((p, 4))
+    kv["v"][0, 0, :p] = _b(cached)
+    m = OracleModel(c, w, np.float64)
+    _, hidden = m.step(kv, 5, p)
+    s = 0.5 / math.sqrt(0.25 + c.rms_eps)                     # rmsnorm of 0.5*1
+    v_now = (torch.tensor(bf16_bits_to_float(w["layers"][0]["wv"], np.float64) @ np.full(8, s))
+             .to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy())
+    allv = np.vstack([bf16_bits_to_float(_b(cached), np.float64), v_now])
+    mean_v = allv.mean(axis=0)
+    want = 0.5 + np.concatenate([mean_v, mean_v])           # both q heads read KV head 0
+    assert np.allclose(hidden[0], want, rtol=1e-13)
+    assert np.array_equal(kv["v"][0, 0, p], _torch_bits(v_now.astype(np.float32)))
+
+
+def test_step_gqa_mapping_consecutive_heads_share_kv():
+    """n_heads = 4, n_kv_heads = 2: heads 0, 1 read KV head 0 and heads 2, 3 read
+    KV head 1 (h // 2), not h % 2.  Catches a wrong GQA map."""
+    c = Cfg(n_layers=1, n_heads=4, n_kv_heads=2, head_dim=2, hidden=8)
+    rng = np.random.default_rng(10)
+    w = _zero_model(c, rng)
+    w["layers"][0]["wo"] = _b(np.eye(8))
+    kv = _kv(c, 4)
+    p = 2
+    kv["v"][0, 0, :p] = _b(np.full((p, 2), 1.0))
+    kv["v"][0, 1, :p] = _b(np.full((p, 2), 4.0))
+    m = OracleModel(c, w, np.float64)
+    x0 = bf16_bits_to_float(w["embed"][1], np.float64)
+    _, hidden = m.step(kv, 1, p)
+    a, b = 1.0 * p / (p + 1), 4.0 * p / (p + 1)             # current v = 0 (W_v = 0)
+    assert np.allclose(hidden[0] - x0, [a, a, a, a, b, b, b, b], rtol=1e-13)
+
+
+def test_step_mlp_closed_form():
+    """Attention off; W_gate = W_up = W_down = I (H = F = 2), x = [a, b]:
+    x_out = x + silu(h) * h with h = x / rms(x).  Catches gate/up swap in the
+    product, silu on the wrong branch, missing MLP norm."""
+    c = Cfg(n_layers=1, hidden=2, ffn=2, n_heads=1, n_kv_heads=1, head_dim=2, vocab=4)
+    rng = np.random.default_rng(11)
+    w = _zero_model(c, rng)
+    w["embed"][2] = _b([0.5, -1.25])
+    w["layers"][0]["w_gate"] = _b(np.eye(2) * 2.0)
+    w["layers"][0]["w_up"] = _b(np.eye(2))
+    w["layers"][0]["w_down"] = _b(np.eye(2))
+    m = OracleModel(c, w, np.float64)
+    _, hidden = m.step(_kv(c, 2), 2, 0)
+    x = np.array([0.5, -1.25])
+    h = x / math.sqrt((0.25 + 1.5625) / 2 + c.rms_eps)
+    sig = 1.0 / (1.0 + np.exp(-2.0 * h))
+    want = x + (2.0 * h * sig) * h
+    assert np.allclose(hidden[0], want, rtol=1e-13)
+
+
+def test_step_qk_norm_makes_scores_scale_invariant():
+    """With q/k RMSNorm, scaling W_q and W_k by 8 changes nothing (up to eps);
+    without it the output changes.  Catches a q/k norm that is skipped."""
+    rng = np.random.default_rng(12)
+    outs = {}
+    for qk in [True, False]:
+        c = Cfg(n_layers=1, n_heads=2, n_kv_heads=1, head_dim=4, hidden=8, qk_norm=qk, rms_eps=1e-12)
+        base = _zero_model(c, rng)
+        wq = rng.standard_normal((8, 8)); wk = rng.standard_normal((4, 8)); wv = rng.standard_normal((4, 8))
+        res = []
+        for scale in [1.0, 8.0]:
+            w = {**base, "layers": [dict(base["layers"][0])]}
+            w["layers"][0]["wq"] = _b(wq * scale)
+            w["layers"][0]["wk"] = _b(wk * scale)
+            w["layers"][0]["wv"] = _b(wv)
+            w["layers"][0]["wo"] = _b(np.eye(8))
+            kv = _kv(c, 4)
+            kv["k"][0, 0, :2] = _b(rng.standard_normal((2, 4)) * 0 + np.array([[1, 2, 3, 4], [-2, 1, 0.5, 3]]))
+            kv["v"][0, 0, :2] = _b(np.array([[1, 0, 0, 0], [0, 1, 0, 0]]))
+            _, hid = OracleModel(c, w, np.float64).step(kv, 0, 2)
+            res.append(hid[0])
+        outs[qk] = res
+    assert np.allclose(outs[True][0], outs[True][1], rtol=1e-9)
+    assert not np.allclose(outs[False][0], outs[False][1], rtol=1e-3)
+
+
+def test_step_untied_head_equal_to_embedding_matches_tied():
+    c = Cfg()
+    rng = np.random.default_rng(13)
+    w = _zero_model(c, rng)
+    w["layers"][0]["wv"] = _b(rng.standard_normal((4, 8)) * 0.3)
+    w["layers"][0]["wo"] = _b(rng.standard_normal((8, 8)) * 0.3)
+    l1, _ = OracleModel(c, w, np.float64).step(_kv(c, 2), 1, 0)
+    c2 = Cfg(tie_embeddings=False)
+    w2 = dict(w, lm_head=w["embed"].copy())
+    l2, _ = OracleModel(c2, w2, np.float64).step(_kv(c2, 2), 1, 0)
+    assert np.array_equal(l1, l2)
+    w3 = dict(w, lm_head=_b(rng.standard_normal((c.vocab, c.hidden))))
+    l3, _ = OracleModel(c2, w3, np.float64).step(_kv(c2, 2), 1, 0)
+    assert not np.allclose(l1, l3)
+
+
+def test_step_kv_written_after_rope_at_position():
+    """k is cached after RoPE at position p: with hd = 2 and W_k giving k = [r, 0],
+    the cached key is bf16([r cos p, r sin p]).  Catches caching the unrotated key."""
+    c = Cfg(n_layers=1, n_heads=1, n_kv_heads=1, head_dim=2, hidden=2, ffn=2, vocab=4)
+    rng = np.random.default_rng(14)
+    w = _zero_model(c, rng)
+    w["embed"][1] = _b([1.0, 1.0])
+    wk = np.array([[0.75, 0.0], [0.0, 0.0]])
+    w["layers"][0]["wk"] = _b(wk)
+    kv = _kv(c, 8)
+    p = 5
+    OracleModel(c, w, np.float64).step(kv, 1, p)
+    s = 1.0 / math.sqrt(1.0 + c.rms_eps)
+    r = 0.75 * s
+    want = torch.tensor([r * math.cos(p), r * math.sin(p)], dtype=torch.float64).to(torch.float32)
+    assert np.array_equal(kv["k"][0, 0, p], _torch_bits(want.numpy()))
+
+
+def test_decode_teacher_forced_on_own_tokens_equals_free_running():
+    c = Cfg(vocab=32)
+    rng = np.random.default_rng(15)
+    w = _zero_model(c, rng)
+    for d in w["layers"]:
+        for k in ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]:
+            d[k] = _b(rng.standard_normal(bf16_bits_to_float(d[k]).shape) * 0.3)
+    w["embed"] = _b(rng.standard_normal((32, 8)))
+    m = OracleModel(c, w, np.float32)
+    free = m.decode(_kv(c, 12), 7, 0, 10)
+    forced = m.decode(_kv(c, 12), 7, 0, 10, teacher=list(free["tokens"][:-1]))
+    assert np.array_equal(free["tokens"], forced["tokens"])
+    assert np.array_equal(free["logits"], forced["logits"])
+
+
+def test_fp32_oracle_close_to_fp64_on_tiny_synthetic_model():
+    from tile_scheduled_persistent_amd import synth
+    from tile_scheduled_persistent_amd.configs import TINY
+    w = synth.weights_as_bits(synth.make_weights(TINY))
+    k, v = synth.make_kv(TINY, 24, 10)
+    kv32 = {"k": synth.bits(k), "v": synth.bits(v)}
+    kv64 = {"k": kv32["k"].copy(), "v": kv32["v"].copy()}
+    toks = synth.make_tokens(TINY, 4)
+    r32 = OracleModel(TINY, w, np.float32).decode(kv32, toks[0], 10, 4, teacher=toks[1:])
+    r64 = OracleModel(TINY, w, np.float64).decode(kv64, toks[0], 10, 4, teacher=toks[1:])
+    rel = np.linalg.norm(r32["hidden"] - r64["hidden"], axis=-1) / np.linalg.norm(r64["hidden"], axis=-1)
+    assert rel.max() < 1e-5
+    assert np.abs(r32["logits"] - r64["logits"]).max() < 1e-4

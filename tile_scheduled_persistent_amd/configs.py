@@ -1,0 +1,112 @@
+"""Model shapes and decode workloads.
+
+The shapes are the decoders the pages run: Llama 3.2 1B (Tiles page, intro:
+"Llama 3.2 1B in BF16 at batch size one"), Qwen3-0.6B and Qwen3-4B
+(TileInfer.jl roadmap, "Where it stands" table: decode "after 1,023 cached
+positions"), plus a tiny decoder that a CPU oracle finishes in well under a
+second and a long-context Qwen3-4B workload whose attention carries a large
+share of the bytes (the roadmap's "M8 so far" table measures 4B decode at 32k
+positions).  Weights are random (no checkpoints are used); see ``synth``.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict
+
+
+@dataclass(frozen=True)
+class ModelConfig:
+    name: str
+    n_layers: int
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    rope_theta: float
+    rms_eps: float
+    qk_norm: bool
+    tie_embeddings: bool = True
+
+    @property
+    def q_rows(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def kv_rows(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    def param_count(self) -> int:
+        """Parameters read once per token: every linear layer, every norm
+        gain, the LM head (the embedding matrix when tied) and one embedding
+        row."""
+        H, F, V = self.hidden, self.ffn, self.vocab
+        per_layer = (H * (self.q_rows + 2 * self.kv_rows) + self.q_rows * H + 3 * H * F + 2 * H)
+        if self.qk_norm:
+            per_layer += 2 * self.head_dim
+        head = V * H
+        return self.n_layers * per_layer + H + head + H  # final norm, LM head, one embedding row
+
+    def weight_bytes_per_token(self) -> int:
+        return 2 * self.param_count()
+
+    def kv_bytes_per_position(self) -> int:
+        """K and V bytes of one position over all layers (BF16)."""
+        return 2 * 2 * self.n_layers * self.n_kv_heads * self.head_dim
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A decode run: ``n_cached`` positions already in the KV cache, then
+    ``n_steps`` greedy steps (one launch of up to 64 steps each)."""
+    key: str
+    model: ModelConfig
+    n_cached: int
+    n_steps: int
+    prompt_len: int = 0          # >0: prefill that many prompt tokens one step at a time
+    key_scale: bool = False      # per-(layer, kv head, channel) key scales ~ U(0.5, 4)
+    description: str = ""
+
+    @property
+    def capacity(self) -> int:
+        return self.n_cached + self.prompt_len + self.n_steps
+
+    def avg_attended(self) -> float:
+        """Mean attended positions L over the timed steps (L = cached + 1 at
+        the first step)."""
+        return self.n_cached + (self.n_steps + 1) / 2.0
+
+    def bytes_per_token(self) -> float:
+        """Algorithmic HBM bytes per decoded token: weights read once, K/V of
+        every attended position read once, one K/V position written."""
+        m = self.model
+        return (m.weight_bytes_per_token() + m.kv_bytes_per_position() * self.avg_attended()
+                + m.kv_bytes_per_position())
+
+
+TINY = ModelConfig("tiny", 2, 256, 4, 2, 64, 1024, 4096, 1e4, 1e-5, False)
+LLAMA_1B = ModelConfig("llama-3.2-1b-shaped", 16, 2048, 32, 8, 64, 8192, 128256, 5e5, 1e-5, False)
+QWEN3_06B = ModelConfig("qwen3-0.6b-shaped", 28, 1024, 16, 8, 128, 3072, 151936, 1e6, 1e-6, True)
+QWEN3_4B = ModelConfig("qwen3-4b-shaped", 36, 2560, 32, 8, 128, 9728, 151936, 1e6, 1e-6, True)
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", TINY, 0, 15, prompt_len=8,
+                     description="tiny decoder: 8-token prompt prefilled one token per step, "
+                                 "then 16 greedy tokens (23 forward steps)"),
+    "llama1b": Workload("llama1b", LLAMA_1B, 1023, 64,
+                        description="Llama-3.2-1B-shaped decode, 64 tokens after 1023 cached positions"),
+    "qwen06b": Workload("qwen06b", QWEN3_06B, 1023, 64,
+                        description="Qwen3-0.6B-shaped decode, 64 tokens after 1023 cached positions"),
+    "qwen4b": Workload("qwen4b", QWEN3_4B, 1023, 64,
+                       description="Qwen3-4B-shaped decode, 64 tokens after 1023 cached positions"),
+    "qwen4b_32k": Workload("qwen4b_32k", QWEN3_4B, 32767, 32, key_scale=True,
+                           description="Qwen3-4B-shaped decode, 32 tokens after 32767 cached positions, "
+                                       "per-channel key scales"),
+}
+
+
+def scaled(cfg: ModelConfig, **kw) -> ModelConfig:
+    """A copy of ``cfg`` with some fields replaced (e.g. fewer layers)."""
+    return replace(cfg, **kw)
