@@ -1,0 +1,234 @@
+"""Decode benchmark: batch-1 greedy BF16 decode tok/s and the fraction of the HBM
+bytes-per-token roofline, for the tile-scheduled persistent kernel on one MI355X.
+
+A "step" is one cooperative launch that decodes a whole workload (64 tokens after
+1023 cached positions for the Llama-3.2-1B-shaped model) from the same starting
+KV state; inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line.  The CPU oracle is timed on the host cores on a bounded
+sample of the same workload (``cpu_baseline``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at batch 1 and % of HBM roofline (weight+KV bytes/token)"
+HBM_PEAK_GBS = 8000.0
+KERNEL_NAME = "tiles_worker"
+
+
+def _counter_traffic(workload_key: str, build_id: int):
+    """HBM traffic per launch from a committed rocprofv3 counter summary of the same
+    kernel build (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), else None."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload_key}_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if int(d.get("build_id", "0"), 16) != build_id:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
+    """Time the CPU oracle (as it stands) on the host cores: free-running steps of the
+    same workload from the same starting state, after one warm-up step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import OracleModel
+
+    w_bits, kv_bits = setup_bits
+    o = OracleModel(m, w_bits, np.float32)
+    kv = {"k": kv_bits["k"].copy(), "v": kv_bits["v"].copy()}
+    t_prep = time.perf_counter()
+    logits, _ = o.step(kv, token, wl.n_cached)  # warm-up (also widens the weights once)
+    prep = time.perf_counter() - t_prep
+    tok = int(np.argmax(logits))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        logits, _ = o.step(kv, tok, wl.n_cached + 1 + n)
+        tok = int(np.argmax(logits))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= wl.n_steps - 1:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n / el, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} free-running decode steps of the same workload after 1 warm-up step "
+                      f"({el:.1f} s timed; warm-up incl. BF16->FP32 widening {prep:.1f} s), NumPy FP32"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama1b")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
+    ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--combine-mode", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path has no multi-GPU "
+                                   "component (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tile_scheduled_persistent_amd import synth, tiles
+    from tile_scheduled_persistent_amd.configs import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    m = wl.model
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    w = synth.make_weights(m, device=dev)
+    k0, v0 = synth.make_kv(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, device=dev)
+    token = synth.make_tokens(m, 1)[0]
+    stream = torch.cuda.current_stream()
+    plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
+                      stream=stream)
+    info = plan.info()
+    kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
+    n_tok = wl.n_steps
+    out_t = torch.zeros(n_tok, dtype=torch.int32, device=dev)
+    out_l = torch.zeros((n_tok, m.vocab), dtype=torch.float32, device=dev)
+
+    def launch():
+        kv.length = wl.n_cached
+        plan.decode(kv, token, n_tok, out_t, None)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    if plan.status() != tiles.TILES_OK:
+        raise RuntimeError(tiles.last_error())
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if plan.status() != tiles.TILES_OK:
+        raise RuntimeError(tiles.last_error())
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(launch_ms))
+
+    bpt = wl.bytes_per_token()
+    tok_s = args.steps * n_tok / wall
+    achieved = bpt * n_tok / (avg_ms * 1e-3) / 1e9
+    traffic = _counter_traffic(args.workload, info.build_id)
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "batch": 1, "cached_positions": wl.n_cached,
+                   "tokens_per_step": n_tok, "parallelism": "single GPU, one workgroup per CU"},
+        "pct_hbm_roofline": round(100.0 * tok_s * bpt / (HBM_PEAK_GBS * 1e9), 2),
+        "bytes_per_token": int(bpt),
+        "launch_ms": {"min": round(min(launch_ms), 4), "median": round(float(np.median(launch_ms)), 4),
+                      "max": round(max(launch_ms), 4)},
+        "plan": {"waves_per_token": info.waves_per_step, "kv_splits": info.kv_splits,
+                 "combine": "o_proj prologue" if info.combine_mode == 1 else "own wave",
+                 "workers": info.n_workers, "block_threads": info.block_threads},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+
+    if args.trace_report:
+        _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info)
+
+    if not args.no_cpu_baseline:
+        w_bits = synth.weights_as_bits(w)
+        kv_bits = {"k": synth.bits(k0), "v": synth.bits(v0)}
+        del w
+        result["cpu_baseline"] = cpu_baseline((w_bits, kv_bits), m, wl, token, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+def _trace_report(path, m, wl, w, k0, v0, token, args, info):
+    """Per-wave duration, GB/s and barrier wait from the in-kernel trace (separate launch)."""
+    import numpy as np
+    import torch
+
+    from tile_scheduled_persistent_amd import tiles
+
+    plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits,
+                      combine_mode=args.combine_mode)
+    kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
+    out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
+    plan.decode(kv, token, wl.n_steps, out_t, None)
+    _, tr = plan.read_debug(hidden=False, trace=True)
+    waves = plan.waves()
+    plan.close()
+    tr = tr.astype(np.int64)  # [steps, waves, W, 3] 100 MHz ticks
+    steps = tr.shape[0]
+    names = tiles.WAVE_KINDS
+    # wave duration: from the latest release of the previous wave to the latest release of this wave
+    rel = tr[:, :, :, 2].max(axis=2)  # [steps, waves]
+    start = tr[:, :, :, 0].min(axis=2)
+    work = (tr[:, :, :, 1] - tr[:, :, :, 0])  # per worker busy time before arriving
+    wait = (tr[:, :, :, 2] - tr[:, :, :, 1])  # per worker barrier time
+    lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz)",
+             f"# workload: {wl.description}; steps traced: {steps}; waves per step: {len(waves)}",
+             "wave\tkind\tlayer\tMB\tdur_us(median over steps)\tGB/s\tmax_work_us\tmean_barrier_us"]
+    tot_dur = 0.0
+    per_kind = {}
+    for i, wv in enumerate(waves):
+        prev_rel = rel[:, i - 1] if i > 0 else start[:, 0]
+        dur = np.median(rel[:, i] - prev_rel) * 0.01  # us
+        tot_dur += dur
+        mb = wv.weight_bytes / 1e6
+        gbs = (wv.weight_bytes / 1e9) / (dur * 1e-6) if dur > 0 else 0.0
+        mw = np.median(work[:, i, :].max(axis=1)) * 0.01
+        bw = np.median(wait[:, i, :].mean(axis=1)) * 0.01
+        k = names.get(wv.kind, str(wv.kind))
+        d = per_kind.setdefault(k, [0.0, 0.0, 0.0])
+        d[0] += dur
+        d[1] += wv.weight_bytes
+        d[2] += bw
+        lines.append(f"{i}\t{k}\t{wv.layer}\t{mb:.2f}\t{dur:.2f}\t{gbs:.0f}\t{mw:.2f}\t{bw:.2f}")
+    lines.append("# per kind: total us per token, GB/s, summed mean barrier us")
+    for k, (dur, by, bw) in per_kind.items():
+        lines.append(f"# {k}\t{dur:.1f} us\t{by / 1e9 / (dur * 1e-6) if dur else 0:.0f} GB/s\tbarrier {bw:.1f} us")
+    step_us = np.median(np.diff(rel[:, -1])) * 0.01 if steps > 1 else tot_dur
+    lines.append(f"# token time (median step-to-step) {step_us:.1f} us; sum of wave medians {tot_dur:.1f} us")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

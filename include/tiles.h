@@ -1,0 +1,188 @@
+/*
+ * tiles.h -- C ABI of the tile-scheduled persistent decoder for AMD MI355X (gfx950).
+ *
+ * One batch-1 greedy BF16 decode step of a Llama/Qwen3-style decoder runs as a
+ * static graph of tiles: a host planner cuts every operator into output-row
+ * tiles, assigns each tile to a fixed workgroup (one per compute unit), groups
+ * the tiles into waves separated by grid barriers, validates the schedule and
+ * packs the weights tile-contiguously; one cooperative persistent kernel then
+ * executes that schedule for up to 64 tokens per launch, with greedy selection
+ * inside the kernel.
+ *
+ * Sources: "Tiles: Scheduling LLM Decoding as a Graph of Tiles" (intro: tiles
+ * as the unit of scheduled work, a fixed worker per tile, byte balancing,
+ * waves separated by grid barriers, validation before launch, bit-identical
+ * runs; "What the code contains": TilePlan probes occupancy, builds and
+ * validates the tile graph and packs the weights; TileInfer re-validates the
+ * plan, checks it against the worker binary and GPU, runs up to 64 tokens per
+ * cooperative launch with greedy selection in the kernel).  The fused
+ * operations follow "History and roadmap" (TileInfer.jl), "M8 so far" table:
+ * q/k norm + RoPE + KV write, residual add + RMSNorm, SwiGLU in the GEMV;
+ * split-KV decode attention follows its "Milestones" table, M5.
+ *
+ * Conventions for every entry point:
+ *   - Return value: TILES_OK (0) or a negative TILES_E_* code; the text of the
+ *     last error of the calling thread is available from tiles_last_error().
+ *   - Pointers marked "device" are HIP device memory on the current device;
+ *     pointers marked "host" are ordinary host memory.
+ *   - No entry point takes ownership of caller memory.
+ *   - BF16 tensors are raw IEEE bfloat16 bit patterns (uint16), row-major.
+ */
+#ifndef TILES_H
+#define TILES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define TILES_OK 0
+#define TILES_E_ARG (-1)     /* null pointer, out-of-range token / n_steps, KV capacity exceeded */
+#define TILES_E_CONFIG (-2)  /* model shape the planner cannot tile (e.g. heads not dividing) */
+#define TILES_E_PLAN (-3)    /* schedule validation failed or the plan was modified after creation */
+#define TILES_E_DEVICE (-4)  /* not gfx950, CU count differs from the plan, no cooperative launch, occupancy < 1 */
+#define TILES_E_HIP (-5)     /* a HIP runtime call failed; its message is in tiles_last_error() */
+#define TILES_E_KERNEL (-6)  /* the kernel reported a fault (barrier watchdog expired) */
+
+/* ---- plan flags (tiles_config_t.flags) --------------------------------- */
+#define TILES_DEBUG_HIDDEN 0x1u /* record the residual stream after every layer of every step */
+#define TILES_TRACE 0x2u        /* record per-worker, per-wave timestamps (100 MHz wall clock) */
+#define TILES_POISON 0x4u       /* NaN-fill the per-step scratch at every step start */
+
+/* ---- model + plan options ---------------------------------------------- */
+typedef struct tiles_config {
+  int32_t n_layers;       /* decoder layers */
+  int32_t hidden;         /* H */
+  int32_t n_heads;        /* query heads */
+  int32_t n_kv_heads;     /* key/value heads; must divide n_heads (grouped-query attention) */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t ffn;            /* SwiGLU intermediate size F */
+  int32_t vocab;          /* V */
+  float rope_theta;       /* RoPE base */
+  float rms_eps;          /* RMSNorm epsilon (also used for the q/k norms) */
+  int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
+  int32_t tie_embeddings; /* 1: the LM head is the embedding matrix */
+  int32_t max_positions;  /* largest KV length (cached + decoded) the plan supports */
+  uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON */
+  int32_t kv_splits;      /* split-KV count per KV head; 0 lets the planner choose */
+  int32_t combine_mode;   /* 0 planner choice, 1 combine splits in the o_proj prologue, 2 own wave */
+  int32_t n_workers;      /* 0 = one workgroup per compute unit (required on the GPU) */
+  void *stream;           /* hipStream_t used by create (copies) and by every decode; NULL = null stream */
+} tiles_config_t;
+
+/* Per-layer weights, BF16, row-major [out, in]:
+ *   attn_norm, mlp_norm [H]; q_norm, k_norm [head_dim] (only read when qk_norm);
+ *   wq [n_heads*head_dim, H]; wk, wv [n_kv_heads*head_dim, H]; wo [H, n_heads*head_dim];
+ *   w_gate, w_up [F, H]; w_down [H, F]. */
+typedef struct tiles_layer_weights {
+  const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} tiles_layer_weights_t;
+
+typedef struct tiles_weights {
+  const void *embed;                   /* [V, H] */
+  const void *final_norm;              /* [H] */
+  const void *lm_head;                 /* [V, H]; NULL when tie_embeddings */
+  const tiles_layer_weights_t *layers; /* host array of n_layers entries */
+  int32_t on_device;                   /* 1: the tensors are device memory, 0: host memory */
+} tiles_weights_t;
+
+/* KV cache, caller-owned device memory, BF16 [n_layers][n_kv_heads][capacity][head_dim].
+ * Keys are stored after q/k norm and RoPE. */
+typedef struct tiles_kv {
+  void *k;
+  void *v;
+  int64_t capacity; /* positions allocated */
+  int64_t length;   /* positions already cached; tiles_decode adds n_steps on success */
+} tiles_kv_t;
+
+typedef struct tiles_plan tiles_plan_t;
+
+/* Summary of a plan (see tiles_plan_info). */
+typedef struct tiles_plan_info {
+  int32_t n_workers;          /* workgroups = grid size */
+  int32_t block_threads;      /* threads per workgroup */
+  int32_t lds_bytes;          /* dynamic LDS per workgroup */
+  int32_t waves_per_step;     /* grid barriers per decoded token */
+  int32_t n_tiles;            /* tiles per step (all waves) */
+  int32_t kv_splits;          /* S */
+  int32_t combine_mode;       /* 1 prologue, 2 own wave */
+  int32_t occupancy;          /* workgroups per CU the kernel can hold (0 in a dry run) */
+  int64_t packed_bytes;       /* device bytes of the packed weights */
+  int64_t weight_bytes_per_step; /* weight bytes one token streams (algorithmic) */
+  double max_over_mean;       /* worst per-wave worker byte imbalance (max / mean over busy waves) */
+  uint64_t checksum;          /* schedule checksum (re-checked at every decode) */
+  uint64_t build_id;          /* worker-kernel build id the plan was made for */
+} tiles_plan_info_t;
+
+/* One wave of the per-step schedule (see tiles_plan_wave). */
+typedef struct tiles_wave_info {
+  int32_t kind;        /* 1 QKV, 2 attention, 3 split combine, 4 o_proj, 5 gate/up, 6 down, 7 LM head */
+  int32_t layer;       /* -1 for the LM head */
+  int32_t busy_workers;
+  int32_t pad;
+  int64_t weight_bytes;   /* weight bytes streamed by the wave, all workers */
+  int64_t max_worker_bytes;
+} tiles_wave_info_t;
+
+/* Build, validate and upload a plan.  cfg and w are read only during the call;
+ * the source weights may be freed afterwards (the plan keeps a packed copy).
+ * Returns NULL on error (see tiles_last_error()).  Allocates device memory:
+ * packed weights (= model bytes), RoPE table [max_positions][head_dim/2] x2 FP32,
+ * per-step scratch, barrier words, and the debug/trace buffers when flagged. */
+tiles_plan_t *tiles_plan_create(const tiles_config_t *cfg, const tiles_weights_t *w);
+
+/* Greedy-decode n_steps tokens (1..64) in one cooperative launch on the plan's stream.
+ * Step i consumes `token` (i = 0) or out_tokens[i-1], at position kv->length + i, writes
+ * that position's K and V, and stores its argmax (lowest index on ties) in out_tokens[i].
+ *   kv          : host struct; kv->k / kv->v device BF16 cache; kv->length is advanced by
+ *                 n_steps when the launch has been enqueued successfully.
+ *   token       : 0 <= token < vocab.
+ *   out_tokens  : device int32 [n_steps].
+ *   out_logits  : device float [n_steps][vocab], or NULL to skip writing logits.
+ * Asynchronous: results are valid after the stream synchronizes.  Errors detected on the
+ * host (arguments, capacity, plan checksum, device identity) return before launching.
+ * Allocates nothing. */
+int tiles_decode(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, int32_t *out_tokens,
+                 float *out_logits);
+
+/* Release every resource of the plan (synchronizes its stream first).  NULL-safe. */
+void tiles_plan_destroy(tiles_plan_t *plan);
+
+/* Message of the last error raised on the calling thread ("" if none). */
+const char *tiles_last_error(void);
+
+/* Fill *info for a plan. */
+int tiles_plan_info(const tiles_plan_t *plan, tiles_plan_info_t *info);
+
+/* Describe wave `wave` (0 <= wave < waves_per_step) of a plan. */
+int tiles_plan_wave(const tiles_plan_t *plan, int32_t wave, tiles_wave_info_t *out);
+
+/* Host-only planning: build and validate the schedule for `n_workers` workers without
+ * touching any GPU (no device memory, no kernel).  Fills *info (occupancy = 0). */
+int tiles_plan_dry_run(const tiles_config_t *cfg, int32_t n_workers, tiles_plan_info_t *info);
+
+/* Change the stream used by subsequent decodes (hipStream_t, NULL = null stream). */
+int tiles_plan_set_stream(tiles_plan_t *plan, void *stream);
+
+/* Synchronize the plan's stream and report a device-side fault of the last launch:
+ * TILES_OK or TILES_E_KERNEL (and clears the fault word). */
+int tiles_plan_status(tiles_plan_t *plan);
+
+/* Copy debug buffers to host memory after synchronizing the plan's stream.
+ *   hidden : host float [n_steps_of_last_decode][n_layers][H] or NULL (needs TILES_DEBUG_HIDDEN);
+ *   trace  : host uint64 [n_steps][waves_per_step][n_workers][3] or NULL (needs TILES_TRACE):
+ *            wave start, barrier arrival and barrier release, 100 MHz ticks.
+ *   *n_steps_out receives the step count of the last decode. */
+int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t *n_steps_out);
+
+/* Test hook: corrupt one byte of the host copy of the schedule so that the next
+ * decode must fail its checksum (TILES_E_PLAN).  Does not touch the device. */
+int tiles_plan_debug_corrupt(tiles_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TILES_H */

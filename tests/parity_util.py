@@ -1,0 +1,103 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on both sides, the
+oracle, and the comparison bars.
+
+Bars (from the decode contract of this library): per-layer hidden states
+within relative L2 1e-2 of the oracle, logits within max-abs 5e-2, greedy
+tokens identical wherever the oracle's top-2 logit margin exceeds 0.1, and
+bit-identical results across repeated GPU runs.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import OracleModel
+from tile_scheduled_persistent_amd import synth, tiles
+
+HIDDEN_REL_L2 = 1e-2
+LOGIT_MAX_ABS = 5e-2
+MARGIN = 0.1
+
+
+def top2_margin(logits: np.ndarray) -> float:
+    part = np.partition(logits.astype(np.float64), -2)
+    return float(part[-1] - part[-2])
+
+
+class Setup:
+    """Seeded weights and KV cache for a model, resident on the GPU, plus host bit
+    views for the oracle.  `gen_device` is where the generators run."""
+
+    def __init__(self, m, capacity: int, n_cached: int, key_scale: bool = False, gen_device: str = "cpu",
+                 widen_once: bool = True):
+        self.m = m
+        self.capacity = capacity
+        self.n_cached = n_cached
+        w = synth.make_weights(m, device=gen_device)
+        k, v = synth.make_kv(m, capacity, n_cached, key_scale=key_scale, device=gen_device)
+        self.w_bits = synth.weights_as_bits(w)
+        self.kv_bits = {"k": synth.bits(k), "v": synth.bits(v)}
+        if gen_device == "cpu":
+            w = {"embed": w["embed"].cuda(), "final_norm": w["final_norm"].cuda(),
+                 "layers": [{kk: vv.cuda() for kk, vv in d.items()} for d in w["layers"]],
+                 **({"lm_head": w["lm_head"].cuda()} if "lm_head" in w else {})}
+            k, v = k.cuda(), v.cuda()
+        self.w_dev = w
+        self.k0, self.v0 = k, v
+        self.widen_once = widen_once
+        self._oracle = None
+
+    def fresh_kv(self) -> tiles.KVCache:
+        return tiles.KVCache(self.k0.clone(), self.v0.clone(), self.n_cached)
+
+    def oracle(self) -> OracleModel:
+        if self._oracle is None:
+            self._oracle = OracleModel(self.m, self.w_bits, np.float32, widen_once=self.widen_once)
+        return self._oracle
+
+    def oracle_kv(self):
+        return {"k": self.kv_bits["k"].copy(), "v": self.kv_bits["v"].copy()}
+
+    def plan(self, flags=tiles.TILES_DEBUG_HIDDEN, **kw) -> tiles.Plan:
+        return tiles.Plan(self.m, self.w_dev, self.capacity, flags=flags, **kw)
+
+
+def run_gpu(plan: tiles.Plan, kv: tiles.KVCache, token: int, n: int, want_hidden=True):
+    """One launch of n steps; returns (tokens [n], logits [n, V], hidden [n, L, H] or None)."""
+    out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+    out_l = torch.zeros((n, plan.model.vocab), dtype=torch.float32, device="cuda")
+    plan.decode(kv, token, n, out_t, out_l)
+    assert plan.status() == tiles.TILES_OK, tiles.last_error()
+    torch.cuda.synchronize()
+    hid = plan.read_debug(hidden=True)[0] if want_hidden else None
+    return out_t.cpu().numpy().astype(np.int64), out_l.cpu().numpy(), hid
+
+
+def check_step(tag: str, g_logits, g_hidden, o_logits, o_hidden, g_tok: int, o_tok: int):
+    """Assert the bars for one step.  Returns the oracle margin."""
+    if g_hidden is not None:
+        num = np.linalg.norm((g_hidden - o_hidden).astype(np.float64), axis=-1)
+        den = np.linalg.norm(o_hidden.astype(np.float64), axis=-1)
+        rel = num / den
+        assert rel.max() <= HIDDEN_REL_L2, f"{tag}: hidden rel L2 {rel.max():.3e} (layer {int(rel.argmax())})"
+    err = np.abs(g_logits.astype(np.float64) - o_logits.astype(np.float64)).max()
+    assert err <= LOGIT_MAX_ABS, f"{tag}: logits max abs err {err:.3e}"
+    margin = top2_margin(o_logits)
+    if margin > MARGIN:
+        assert g_tok == o_tok, f"{tag}: token {g_tok} != oracle {o_tok} at margin {margin:.3f}"
+    return margin
+
+
+def compare_free_running(tag, g_tokens, g_logits, g_hidden, o_res, n_check: int):
+    """Compare a free-running GPU launch with a free-running oracle for the first
+    n_check steps while both consumed the same input token.  Returns the number
+    of steps compared."""
+    compared = 0
+    for i in range(n_check):
+        check_step(f"{tag} step {i}", g_logits[i], None if g_hidden is None else g_hidden[i], o_res["logits"][i],
+                   o_res["hidden"][i], int(g_tokens[i]), int(o_res["tokens"][i]))
+        compared += 1
+        if int(g_tokens[i]) != int(o_res["tokens"][i]):
+            break  # inputs of later steps differ; allowed only at a low-margin step (checked above)
+    return compared

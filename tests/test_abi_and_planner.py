@@ -1,0 +1,108 @@
+"""Host-side checks that need no GPU: the C-ABI library loads and exports every
+declared entry point, and the planner builds, balances and validates schedules
+(dry runs) or rejects shapes it cannot tile."""
+
+import os
+import re
+
+import pytest
+
+from tile_scheduled_persistent_amd import tiles
+from tile_scheduled_persistent_amd.configs import LLAMA_1B, QWEN3_06B, QWEN3_4B, TINY, WORKLOADS, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(tiles_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    L = tiles.lib()
+    declared = _declared_functions()
+    assert "tiles_plan_create" in declared and "tiles_decode" in declared and "tiles_plan_destroy" in declared
+    missing = [n for n in declared if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_null_arguments_are_rejected_without_a_gpu():
+    L = tiles.lib()
+    assert L.tiles_decode(None, None, 0, 1, None, None) == tiles.TILES_E_ARG
+    assert "null" in tiles.last_error()
+    assert L.tiles_plan_create(None, None) is None
+    L.tiles_plan_destroy(None)  # NULL-safe
+    assert L.tiles_plan_status(None) == tiles.TILES_E_ARG
+
+
+@pytest.mark.parametrize("key", list(WORKLOADS))
+def test_dry_run_every_workload(key):
+    wl = WORKLOADS[key]
+    m = wl.model
+    info = tiles.dry_run(m, wl.capacity, n_workers=256)
+    per = 5 if info.combine_mode == 1 else 6
+    assert info.waves_per_step == per * m.n_layers + 1
+    assert info.n_workers == 256 and info.block_threads == 512
+    assert 84 * 1024 <= info.lds_bytes <= 160 * 1024
+    assert info.weight_bytes_per_step == m.weight_bytes_per_token()
+    # balanced to within one row of a perfect split
+    assert info.max_over_mean < 1.05
+    assert info.kv_splits >= 1 and info.kv_splits * m.n_kv_heads <= 256
+
+
+def test_dry_run_is_deterministic():
+    a = tiles.dry_run(LLAMA_1B, 1087)
+    b = tiles.dry_run(LLAMA_1B, 1087)
+    assert a.checksum == b.checksum
+    c = tiles.dry_run(LLAMA_1B, 1088)
+    assert c.checksum != a.checksum
+
+
+def test_llama_wave_geometry():
+    info = tiles.dry_run(LLAMA_1B, 1087)
+    # 12 QKV rows, 8 o_proj rows, 32 gate/up pairs, 8 down rows, 501 vocab rows per worker
+    assert info.packed_bytes >= LLAMA_1B.weight_bytes_per_token() - 2 * LLAMA_1B.hidden
+
+
+@pytest.mark.parametrize("kw", [dict(kv_splits=1, combine_mode=1), dict(kv_splits=8, combine_mode=2),
+                                dict(kv_splits=32, combine_mode=2)])
+def test_forced_split_and_combine_modes(kw):
+    info = tiles.dry_run(QWEN3_4B, 1087, **kw)
+    assert info.kv_splits == kw["kv_splits"]
+    assert info.combine_mode == kw["combine_mode"]
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(head_dim=96), tiles.TILES_E_CONFIG),
+    (dict(n_kv_heads=3), tiles.TILES_E_CONFIG),
+    (dict(n_heads=40, n_kv_heads=8), tiles.TILES_E_CONFIG),   # 5 query heads per KV head
+    (dict(n_layers=0), tiles.TILES_E_CONFIG),
+])
+def test_untileable_shapes_are_rejected(bad, code):
+    m = scaled(TINY, **bad)
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(m, 32)
+    assert e.value.code == code
+
+
+def test_too_many_splits_rejected():
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(LLAMA_1B, 1087, kv_splits=33)
+    assert e.value.code == tiles.TILES_E_CONFIG
+
+
+def test_ragged_shape_plans():
+    m = scaled(TINY, name="ragged", n_layers=3, hidden=384, n_heads=6, n_kv_heads=2, ffn=1000, vocab=1000)
+    info = tiles.dry_run(m, 40)
+    assert info.weight_bytes_per_step == m.weight_bytes_per_token()
+
+
+def test_small_worker_counts_plan():
+    for W in [16, 37, 100]:
+        info = tiles.dry_run(QWEN3_06B, 200, n_workers=W)
+        assert info.n_workers == W

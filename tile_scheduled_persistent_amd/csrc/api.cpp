@@ -1,0 +1,449 @@
+// C-ABI runtime: plan creation (device probe, planning, validation, weight packing,
+// uploads), cooperative launches of the persistent worker, status and debug read-back.
+//
+// "Tiles: Scheduling LLM Decoding as a Graph of Tiles", "What the code contains": the
+// planner probes the compiled worker kernel for occupancy, builds and validates the tile
+// graph and its schedule and packs the weights; the runtime re-validates the plan, checks
+// that it was made for this worker binary and GPU, and runs up to 64 tokens per
+// cooperative launch with greedy selection inside the kernel.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tiles.h"
+#include "plan_types.h"
+#include "planner.h"
+
+#ifndef TILES_BUILD_ID
+#define TILES_BUILD_ID 0x0ull
+#endif
+
+namespace tiles {
+const void* worker_kernel(int head_dim, int group);
+}
+
+using namespace tiles;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) {                                                              \
+      return set_err(TILES_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));   \
+    }                                                                                    \
+  } while (0)
+
+constexpr int MAX_STEPS = 64;
+
+}  // namespace
+
+struct tiles_plan {
+  HostPlan hp;
+  tiles_config_t cfg;
+  int device = -1;
+  int cu_count = 0;
+  char arch[64] = {0};
+  char pci[32] = {0};
+  uint64_t build_id = TILES_BUILD_ID;
+  const void* kernel = nullptr;
+  int occupancy = 0;
+  hipStream_t stream = nullptr;
+  // device memory
+  uint8_t* packed = nullptr;
+  TileDesc* d_tiles = nullptr;
+  WaveDesc* d_waves = nullptr;
+  LayerSmall* d_small = nullptr;
+  float* d_rope = nullptr;
+  uint8_t* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  float *x = nullptr, *qkv = nullptr, *part = nullptr, *attn = nullptr, *act = nullptr;
+  uint32_t* lmpart = nullptr;
+  uint32_t* sync = nullptr;
+  size_t sync_bytes = 0;
+  float* dbg_hidden = nullptr;
+  uint64_t* trace = nullptr;
+  int last_steps = 0;
+};
+
+namespace {
+
+int probe_device(tiles_plan* p) {
+  HIP_TRY(hipGetDevice(&p->device));
+  hipDeviceProp_t pr;
+  HIP_TRY(hipGetDeviceProperties(&pr, p->device));
+  std::snprintf(p->arch, sizeof(p->arch), "%s", pr.gcnArchName);
+  std::snprintf(p->pci, sizeof(p->pci), "%04x:%02x:%02x", pr.pciDomainID, pr.pciBusID, pr.pciDeviceID);
+  p->cu_count = pr.multiProcessorCount;
+  if (std::strncmp(pr.gcnArchName, "gfx950", 6) != 0)
+    return set_err(TILES_E_DEVICE, std::string("worker kernel is built for gfx950, device is ") + pr.gcnArchName);
+  if (!pr.cooperativeLaunch) return set_err(TILES_E_DEVICE, "device does not support cooperative launches");
+  return TILES_OK;
+}
+
+const void* src_ptr(const tiles_weights_t* w, int32_t tensor, int32_t layer) {
+  const tiles_layer_weights_t* L = layer >= 0 ? &w->layers[layer] : nullptr;
+  switch (tensor) {
+    case SRC_EMBED: return w->embed;
+    case SRC_FINAL_NORM: return w->final_norm;
+    case SRC_LM_HEAD: return w->lm_head;
+    case SRC_ATTN_NORM: return L->attn_norm;
+    case SRC_WQ: return L->wq;
+    case SRC_WK: return L->wk;
+    case SRC_WV: return L->wv;
+    case SRC_Q_NORM: return L->q_norm;
+    case SRC_K_NORM: return L->k_norm;
+    case SRC_WO: return L->wo;
+    case SRC_MLP_NORM: return L->mlp_norm;
+    case SRC_WGATE: return L->w_gate;
+    case SRC_WUP: return L->w_up;
+    case SRC_WDOWN: return L->w_down;
+  }
+  return nullptr;
+}
+
+void release(tiles_plan* p) {
+  if (!p) return;
+  if (p->stream || p->device >= 0) (void)hipStreamSynchronize(p->stream);
+  void* bufs[] = {p->packed, p->d_tiles, p->d_waves, p->d_small, p->d_rope, p->scratch, p->dbg_hidden, p->trace};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  delete p;
+}
+
+int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan** out) {
+  *out = nullptr;
+  if (!cfg || !w) return set_err(TILES_E_ARG, "null config or weights");
+  if (!w->embed || !w->final_norm || !w->layers) return set_err(TILES_E_ARG, "missing weight tensor");
+  if (!cfg->tie_embeddings && !w->lm_head) return set_err(TILES_E_ARG, "untied model without lm_head");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const tiles_layer_weights_t& L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up || !L.w_down)
+      return set_err(TILES_E_ARG, "missing layer weight tensor");
+    if (cfg->qk_norm && (!L.q_norm || !L.k_norm)) return set_err(TILES_E_ARG, "missing q_norm/k_norm");
+  }
+  tiles_plan* p = new tiles_plan();
+  p->cfg = *cfg;
+  p->stream = static_cast<hipStream_t>(cfg->stream);
+  int rc = probe_device(p);
+  if (rc != TILES_OK) {
+    release(p);
+    return rc;
+  }
+  if (cfg->n_workers != 0 && cfg->n_workers != p->cu_count) {
+    release(p);
+    return set_err(TILES_E_DEVICE, "n_workers must equal the CU count on the GPU");
+  }
+  std::string err;
+  rc = build_plan(*cfg, p->cu_count, p->hp, err);
+  if (rc != TILES_OK) {
+    release(p);
+    return set_err(rc, err);
+  }
+  const HostPlan& hp = p->hp;
+  // occupancy probe of the worker binary
+  p->kernel = worker_kernel(hp.s.hd, hp.s.G);
+  if (!p->kernel) {
+    release(p);
+    return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
+  }
+  hipError_t e = hipFuncSetAttribute(p->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, hp.lds_bytes);
+  if (e != hipSuccess) {
+    release(p);
+    return set_err(TILES_E_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(e));
+  }
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&p->occupancy, p->kernel, BLOCK_THREADS, hp.lds_bytes);
+  if (e != hipSuccess || p->occupancy < 1) {
+    release(p);
+    return set_err(TILES_E_DEVICE, "worker kernel cannot be resident (occupancy < 1)");
+  }
+
+#define TRY(expr)                                                                    \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess) {                                                          \
+      std::string m = std::string(#expr) + ": " + hipGetErrorString(e_);             \
+      release(p);                                                                    \
+      return set_err(TILES_E_HIP, m);                                                \
+    }                                                                                \
+  } while (0)
+
+  // packed weights
+  TRY(hipMalloc(&p->packed, hp.packed_bytes));
+  TRY(hipMemsetAsync(p->packed, 0, hp.packed_bytes, p->stream));
+  const hipMemcpyKind kind = w->on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  for (const CopySeg& c : hp.copies) {
+    const uint8_t* src = static_cast<const uint8_t*>(src_ptr(w, c.tensor, c.layer));
+    if (!src) {
+      release(p);
+      return set_err(TILES_E_ARG, "missing weight tensor for packing");
+    }
+    src += c.src_row * c.cols * 2;
+    if (c.dst_pitch == c.cols * 2) {
+      TRY(hipMemcpyAsync(p->packed + c.dst_off, src, c.nrows * c.cols * 2, kind, p->stream));
+    } else {
+      TRY(hipMemcpy2DAsync(p->packed + c.dst_off, c.dst_pitch, src, c.cols * 2, c.cols * 2, c.nrows, kind, p->stream));
+    }
+  }
+  // schedule
+  TRY(hipMalloc(&p->d_tiles, hp.tiles.size() * sizeof(TileDesc)));
+  TRY(hipMemcpyAsync(p->d_tiles, hp.tiles.data(), hp.tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice, p->stream));
+  TRY(hipMalloc(&p->d_waves, hp.waves.size() * sizeof(WaveDesc)));
+  TRY(hipMemcpyAsync(p->d_waves, hp.waves.data(), hp.waves.size() * sizeof(WaveDesc), hipMemcpyHostToDevice, p->stream));
+  TRY(hipMalloc(&p->d_small, hp.small.size() * sizeof(LayerSmall)));
+  TRY(hipMemcpyAsync(p->d_small, hp.small.data(), hp.small.size() * sizeof(LayerSmall), hipMemcpyHostToDevice, p->stream));
+  // RoPE table: angles p * theta^(-2i/hd) in double, cos/sin rounded to float
+  {
+    const int half = hp.s.hd / 2;
+    std::vector<float> rope((size_t)hp.s.max_positions * half * 2);
+    for (int pos = 0; pos < hp.s.max_positions; ++pos)
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow((double)cfg->rope_theta, -2.0 * i / hp.s.hd);
+        const double ang = (double)pos * inv;
+        rope[((size_t)pos * half + i) * 2] = (float)std::cos(ang);
+        rope[((size_t)pos * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    TRY(hipMalloc(&p->d_rope, rope.size() * sizeof(float)));
+    TRY(hipMemcpy(p->d_rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice));
+  }
+  // scratch (one allocation, 256-byte aligned pieces)
+  {
+    size_t off = 0;
+    auto piece = [&](size_t bytes) {
+      size_t o = off;
+      off += (bytes + 255) / 256 * 256;
+      return o;
+    };
+    const size_t o_x = piece((size_t)hp.s.H * 4);
+    const size_t o_qkv = piece((size_t)hp.s.qkv_rows * 4);
+    const size_t o_part = piece((size_t)hp.s.n_heads * hp.S * (hp.s.hd + 2) * 4);
+    const size_t o_attn = piece((size_t)hp.s.n_heads * hp.s.hd * 4);
+    const size_t o_act = piece((size_t)hp.s.F * 4);
+    const size_t o_lm = piece((size_t)hp.W * 8);
+    p->sync_bytes = (size_t)sync_words(hp.W) * 4;
+    const size_t o_sync = piece(p->sync_bytes);
+    p->scratch_bytes = off;
+    TRY(hipMalloc(&p->scratch, p->scratch_bytes));
+    TRY(hipMemsetAsync(p->scratch, 0, p->scratch_bytes, p->stream));
+    p->x = reinterpret_cast<float*>(p->scratch + o_x);
+    p->qkv = reinterpret_cast<float*>(p->scratch + o_qkv);
+    p->part = reinterpret_cast<float*>(p->scratch + o_part);
+    p->attn = reinterpret_cast<float*>(p->scratch + o_attn);
+    p->act = reinterpret_cast<float*>(p->scratch + o_act);
+    p->lmpart = reinterpret_cast<uint32_t*>(p->scratch + o_lm);
+    p->sync = reinterpret_cast<uint32_t*>(p->scratch + o_sync);
+  }
+  if (cfg->flags & TILES_DEBUG_HIDDEN) {
+    const size_t n = (size_t)MAX_STEPS * hp.s.n_layers * hp.s.H;
+    TRY(hipMalloc(&p->dbg_hidden, n * sizeof(float)));
+    TRY(hipMemsetAsync(p->dbg_hidden, 0, n * sizeof(float), p->stream));
+  }
+  if (cfg->flags & TILES_TRACE) {
+    const size_t n = (size_t)MAX_STEPS * hp.waves.size() * hp.W * 3;
+    TRY(hipMalloc(&p->trace, n * sizeof(uint64_t)));
+    TRY(hipMemsetAsync(p->trace, 0, n * sizeof(uint64_t), p->stream));
+  }
+  TRY(hipStreamSynchronize(p->stream));
+#undef TRY
+  *out = p;
+  return TILES_OK;
+}
+
+int check_identity(const tiles_plan* p) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != p->device) return set_err(TILES_E_DEVICE, "plan was created for another device");
+  if (p->build_id != (uint64_t)TILES_BUILD_ID) return set_err(TILES_E_DEVICE, "plan was made for another worker binary");
+  if (p->hp.W != p->cu_count) return set_err(TILES_E_DEVICE, "plan worker count differs from the CU count");
+  if (plan_checksum(p->hp) != p->hp.checksum) return set_err(TILES_E_PLAN, "plan checksum mismatch (schedule modified)");
+  return TILES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tiles_plan_t* tiles_plan_create(const tiles_config_t* cfg, const tiles_weights_t* w) {
+  g_err.clear();
+  tiles_plan* p = nullptr;
+  int rc = create_impl(cfg, w, &p);
+  if (rc != TILES_OK) return nullptr;
+  return p;
+}
+
+int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
+                 float* out_logits) {
+  if (!p || !kv || !out_tokens) return set_err(TILES_E_ARG, "null plan, kv or out_tokens");
+  if (!kv->k || !kv->v) return set_err(TILES_E_ARG, "null KV buffers");
+  if (n_steps < 1 || n_steps > MAX_STEPS) return set_err(TILES_E_ARG, "n_steps must be in [1, 64]");
+  const HostPlan& hp = p->hp;
+  if (token < 0 || token >= hp.s.V) return set_err(TILES_E_ARG, "token out of range");
+  if (kv->length < 0 || kv->capacity < 1) return set_err(TILES_E_ARG, "bad KV length or capacity");
+  const int64_t limit = kv->capacity < hp.s.max_positions ? kv->capacity : hp.s.max_positions;
+  if (kv->length + n_steps > limit) return set_err(TILES_E_ARG, "KV length + n_steps exceeds capacity / max_positions");
+  int rc = check_identity(p);
+  if (rc != TILES_OK) return rc;
+
+  KernelArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.tiles = p->d_tiles;
+  a.waves = p->d_waves;
+  a.small = p->d_small;
+  a.packed = p->packed;
+  a.rope = p->d_rope;
+  a.final_norm_off = hp.final_norm_off;
+  a.embed_off = hp.embed_off;
+  a.embed_stride = hp.embed_stride;
+  a.x = p->x;
+  a.qkv = p->qkv;
+  a.part = p->part;
+  a.attn = p->attn;
+  a.act = p->act;
+  a.lmpart = p->lmpart;
+  a.sync = p->sync;
+  a.kv_k = static_cast<uint16_t*>(kv->k);
+  a.kv_v = static_cast<uint16_t*>(kv->v);
+  a.kv_cap = kv->capacity;
+  a.out_tokens = out_tokens;
+  a.out_logits = out_logits;
+  a.dbg_hidden = p->dbg_hidden;
+  a.trace = p->trace;
+  a.token0 = token;
+  a.pos0 = (int32_t)kv->length;
+  a.n_steps = n_steps;
+  a.n_waves = (int32_t)hp.waves.size();
+  a.W = hp.W;
+  a.n_layers = hp.s.n_layers;
+  a.H = hp.s.H;
+  a.Hpad = hp.s.Hpad;
+  a.n_heads = hp.s.n_heads;
+  a.n_kv = hp.s.n_kv;
+  a.head_dim = hp.s.hd;
+  a.F = hp.s.F;
+  a.Fpad = hp.s.Fpad;
+  a.V = hp.s.V;
+  a.qkv_rows = hp.s.qkv_rows;
+  a.Qpad = hp.s.Qpad;
+  a.S = hp.S;
+  a.combine_in_o = hp.combine_in_o;
+  a.poison = (p->cfg.flags & TILES_POISON) ? 1 : 0;
+  a.eps = p->cfg.rms_eps;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)hp.s.hd));
+  a.spin_limit = 1u << 22;
+  a.lds_vec_floats = hp.lds_vec_floats;
+  a.lds_part_floats = hp.lds_part_floats;
+
+  HIP_TRY(hipMemsetAsync(p->sync, 0, p->sync_bytes, p->stream));
+  void* args[] = {&a};
+  HIP_TRY(hipLaunchCooperativeKernel(p->kernel, dim3(hp.W), dim3(BLOCK_THREADS), args, hp.lds_bytes, p->stream));
+  kv->length += n_steps;
+  p->last_steps = n_steps;
+  return TILES_OK;
+}
+
+void tiles_plan_destroy(tiles_plan_t* p) { release(p); }
+
+const char* tiles_last_error(void) { return g_err.c_str(); }
+
+static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tiles_plan_info_t* info) {
+  std::memset(info, 0, sizeof(*info));
+  info->n_workers = hp.W;
+  info->block_threads = BLOCK_THREADS;
+  info->lds_bytes = hp.lds_bytes;
+  info->waves_per_step = (int32_t)hp.waves.size();
+  int32_t n = 0;
+  for (const TileDesc& t : hp.tiles) n += t.kind != KIND_NONE;
+  info->n_tiles = n;
+  info->kv_splits = hp.S;
+  info->combine_mode = hp.combine_in_o ? 1 : 2;
+  info->occupancy = occupancy;
+  info->packed_bytes = hp.packed_bytes;
+  info->weight_bytes_per_step = hp.weight_bytes_per_step;
+  info->max_over_mean = hp.max_over_mean;
+  info->checksum = hp.checksum;
+  info->build_id = build_id;
+}
+
+int tiles_plan_info(const tiles_plan_t* p, tiles_plan_info_t* info) {
+  if (!p || !info) return set_err(TILES_E_ARG, "null plan or info");
+  fill_info(p->hp, p->occupancy, p->build_id, info);
+  return TILES_OK;
+}
+
+int tiles_plan_wave(const tiles_plan_t* p, int32_t wave, tiles_wave_info_t* out) {
+  if (!p || !out) return set_err(TILES_E_ARG, "null plan or output");
+  if (wave < 0 || wave >= (int32_t)p->hp.waves.size()) return set_err(TILES_E_ARG, "wave out of range");
+  std::memset(out, 0, sizeof(*out));
+  out->kind = p->hp.waves[wave].kind;
+  out->layer = p->hp.waves[wave].layer;
+  out->busy_workers = p->hp.wave_busy[wave];
+  out->weight_bytes = p->hp.wave_bytes[wave];
+  out->max_worker_bytes = p->hp.wave_max_bytes[wave];
+  return TILES_OK;
+}
+
+int tiles_plan_dry_run(const tiles_config_t* cfg, int32_t n_workers, tiles_plan_info_t* info) {
+  if (!cfg || !info) return set_err(TILES_E_ARG, "null config or info");
+  HostPlan hp;
+  std::string err;
+  int rc = build_plan(*cfg, n_workers, hp, err);
+  if (rc != TILES_OK) return set_err(rc, err);
+  fill_info(hp, 0, TILES_BUILD_ID, info);
+  return TILES_OK;
+}
+
+int tiles_plan_set_stream(tiles_plan_t* p, void* stream) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  p->stream = static_cast<hipStream_t>(stream);
+  return TILES_OK;
+}
+
+int tiles_plan_status(tiles_plan_t* p) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  uint32_t status = 0;
+  HIP_TRY(hipMemcpy(&status, p->sync + SYNC_STATUS_WORD, 4, hipMemcpyDeviceToHost));
+  if (status != 0) {
+    HIP_TRY(hipMemset(p->sync, 0, p->sync_bytes));
+    return set_err(TILES_E_KERNEL, "device barrier watchdog expired in the last launch");
+  }
+  return TILES_OK;
+}
+
+int tiles_read_debug(tiles_plan_t* p, float* hidden, uint64_t* trace, int32_t* n_steps_out) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  const HostPlan& hp = p->hp;
+  if (n_steps_out) *n_steps_out = p->last_steps;
+  if (hidden) {
+    if (!p->dbg_hidden) return set_err(TILES_E_ARG, "plan was created without TILES_DEBUG_HIDDEN");
+    HIP_TRY(hipMemcpy(hidden, p->dbg_hidden, (size_t)p->last_steps * hp.s.n_layers * hp.s.H * sizeof(float),
+                      hipMemcpyDeviceToHost));
+  }
+  if (trace) {
+    if (!p->trace) return set_err(TILES_E_ARG, "plan was created without TILES_TRACE");
+    HIP_TRY(hipMemcpy(trace, p->trace, (size_t)p->last_steps * hp.waves.size() * hp.W * 3 * sizeof(uint64_t),
+                      hipMemcpyDeviceToHost));
+  }
+  return TILES_OK;
+}
+
+int tiles_plan_debug_corrupt(tiles_plan_t* p) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  if (p->hp.tiles.empty()) return set_err(TILES_E_PLAN, "empty plan");
+  p->hp.tiles[p->hp.tiles.size() / 2].woff ^= 0x400;
+  return TILES_OK;
+}
+
+}  // extern "C"

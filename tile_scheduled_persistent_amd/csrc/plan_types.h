@@ -1,0 +1,98 @@
+// Plain-old-data structures shared by the host planner and the persistent kernel.
+//
+// A plan is a per-step schedule: `n_waves` waves, each holding one tile slot per
+// worker (workgroup).  The same schedule repeats for every decoded token; only the
+// token, the position and the attended length change between steps.
+#pragma once
+#include <stdint.h>
+
+namespace tiles {
+
+// Kinds of wave (and of the tiles they hold).  Values are part of the C ABI
+// (tiles_wave_info_t.kind).
+enum : int32_t {
+  KIND_NONE = 0,
+  KIND_QKV = 1,      // RMSNorm prologue + rows of [Wq; Wk; Wv]
+  KIND_ATTN = 2,     // q/k norm + RoPE + KV write + split-KV attention for one (KV head, split)
+  KIND_COMBINE = 3,  // merge the splits of one query head
+  KIND_O = 4,        // (combine prologue) + rows of Wo + residual add
+  KIND_GU = 5,       // RMSNorm prologue + paired rows of W_gate / W_up + SwiGLU
+  KIND_DOWN = 6,     // rows of W_down + residual add
+  KIND_LM = 7,       // final RMSNorm prologue + vocabulary rows + partial argmax
+};
+
+// Geometry of the GEMV inner loop: one "chunk" is 64 lanes x 16 bytes = 512 BF16
+// columns of one row.  Every GEMV row is padded to a multiple of CHUNK_COLS.
+constexpr int CHUNK_COLS = 512;
+constexpr int CHUNK_BYTES = 1024;
+constexpr int BLOCK_THREADS = 512;
+constexpr int NWAVES = BLOCK_THREADS / 64;
+constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
+constexpr int MAX_BLOCK_ROWS = 640;  // GEMV rows staged per LDS block
+
+struct TileDesc {   // 32 bytes
+  int32_t kind;
+  int32_t row0;     // GEMV: first output row (GU: first j). ATTN: KV head. COMBINE: query head.
+  int32_t nrows;    // GEMV: output rows (GU: number of j; the tile holds 2*nrows rows, gate/up interleaved). ATTN: split.
+  int32_t kpad;     // GEMV: packed columns per row (multiple of CHUNK_COLS)
+  int64_t woff;     // GEMV: byte offset of the tile's first packed row
+  int32_t aux0;     // reserved
+  int32_t aux1;     // reserved
+};
+
+struct WaveDesc {   // 16 bytes
+  int32_t kind;
+  int32_t layer;    // -1 for the LM head
+  int32_t max_rows; // largest GEMV row count of any tile in the wave (sizes the LDS partial area)
+  int32_t pad;
+};
+
+// Offsets (bytes) of the per-layer norm gains inside the packed buffer.
+struct LayerSmall {
+  int64_t attn_norm, mlp_norm, q_norm, k_norm;
+};
+
+// Sync area layout (uint32 words).  Each worker owns one 64-byte line of arrivals.
+constexpr int SYNC_LINE_WORDS = 16;
+constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = barrier watchdog)
+constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
+constexpr int SYNC_ARRIVE_BASE = 64;     // arrive[w] at SYNC_ARRIVE_BASE + w * SYNC_LINE_WORDS
+
+inline int64_t sync_words(int W) { return SYNC_ARRIVE_BASE + (int64_t)W * SYNC_LINE_WORDS; }
+
+struct KernelArgs {
+  const TileDesc* tiles;     // [n_waves][W]
+  const WaveDesc* waves;     // [n_waves]
+  const LayerSmall* small;   // [n_layers]
+  const uint8_t* packed;     // packed weights
+  const float* rope;         // [max_positions][head_dim/2][2] (cos, sin)
+  int64_t final_norm_off;    // bytes into packed
+  int64_t embed_off;         // bytes into packed: embedding row 0
+  int64_t embed_stride;      // bytes between embedding rows
+  // per-step scratch (FP32 unless noted)
+  float* x;                  // [H] residual stream
+  float* qkv;                // [(n_heads + 2 n_kv_heads) * head_dim]
+  float* part;               // [n_heads][S][head_dim + 2] split partials (m, l, acc...)
+  float* attn;               // [n_heads * head_dim] combined attention output
+  float* act;                // [F] SwiGLU output
+  uint32_t* lmpart;          // [W][2] (max logit bits, index)
+  uint32_t* sync;            // sync words
+  uint16_t* kv_k;            // BF16 cache
+  uint16_t* kv_v;
+  int64_t kv_cap;
+  int32_t* out_tokens;
+  float* out_logits;         // may be null
+  float* dbg_hidden;         // [n_steps][n_layers][H] or null
+  uint64_t* trace;           // [n_steps][n_waves][W][3] or null
+  int32_t token0, pos0, n_steps, n_waves;
+  int32_t W, n_layers, H, Hpad, n_heads, n_kv, head_dim, F, Fpad, V, qkv_rows, Qpad, S;
+  int32_t combine_in_o;      // 1: the o_proj prologue merges the splits
+  int32_t poison;
+  float eps;
+  float qscale;              // log2(e) / sqrt(head_dim): scores in the base-2 domain
+  uint32_t spin_limit;       // barrier watchdog (polls)
+  int32_t lds_vec_floats;    // LDS layout
+  int32_t lds_part_floats;
+};
+
+}  // namespace tiles

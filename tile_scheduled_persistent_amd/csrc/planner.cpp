@@ -1,0 +1,484 @@
+// Host planner: cuts every operator of a decoder step into output-row tiles, assigns the
+// tiles of each wave to fixed workers, picks the split-KV count, lays out the packed
+// weights and validates the result.
+//
+// The planning rules follow "Tiles: Scheduling LLM Decoding as a Graph of Tiles" (intro):
+// a tile is a small range of output rows plus the work that produces it; small operations
+// fold into neighbouring tiles; each tile has a fixed worker, one worker per compute unit;
+// the planner balances the bytes each worker streams and groups tiles into waves separated
+// by grid barriers; the schedule is validated before launch.  The fusions are those of the
+// "M8 so far" table of the TileInfer.jl roadmap (residual add + RMSNorm, SwiGLU in the GEMV,
+// q/k norm + RoPE + KV write), and attention is split over KV positions as in its "Milestones"
+// table (M5, split-KV decode kernel); the roadmap's "Tried and not kept" table found a
+// separate combine faster than one fused into the split kernel, which is the reason the
+// split merge lives in the o_proj prologue or a wave of its own, never in the split tiles.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <sstream>
+
+namespace tiles {
+
+namespace {
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// rows [lo, hi) of `R` rows for worker w of W: balanced to within one row.
+void row_split(int64_t R, int32_t W, int32_t w, int64_t& lo, int64_t& hi) {
+  lo = R * w / W;
+  hi = R * (w + 1) / W;
+}
+
+struct TileIO {  // read and write sets of one tile, for the hazard check
+  std::vector<Interval> reads, writes;
+};
+
+int fail(std::string& err, int code, const std::string& msg) {
+  err = msg;
+  return code;
+}
+
+// Split count: about `target` bytes of K+V per split tile at the largest attended
+// length, at least 1, at most as many tiles as workers.
+int32_t choose_splits(const Shape& s, int32_t W) {
+  const int64_t kv_head_bytes = (int64_t)s.max_positions * s.hd * 2 /*K,V*/ * 2 /*bf16*/;
+  const int64_t target = 96 * 1024;
+  int64_t S = (kv_head_bytes + target / 2) / target;
+  S = std::max<int64_t>(1, std::min<int64_t>(S, W / s.n_kv));
+  return (int32_t)S;
+}
+
+}  // namespace
+
+uint64_t plan_checksum(const HostPlan& p) {
+  // 64-bit words mixed with a multiply-xorshift step (FNV-style); fast enough to run before every launch.
+  uint64_t h = 1469598103934665603ull;
+  auto word = [&](uint64_t v) {
+    h ^= v;
+    h *= 1099511628211ull;
+    h ^= h >> 29;
+  };
+  auto mix = [&](const void* data, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(data);
+    size_t i = 0;
+    for (; i + 8 <= n; i += 8) {
+      uint64_t v;
+      std::memcpy(&v, b + i, 8);
+      word(v);
+    }
+    uint64_t tail = 0;
+    if (i < n) std::memcpy(&tail, b + i, n - i);
+    word(tail ^ ((uint64_t)n << 56));
+  };
+  const Shape& s = p.s;
+  const int64_t dims[] = {s.n_layers, s.H, s.n_heads, s.n_kv, s.hd, s.F, s.V, s.G, s.qkv_rows, s.Hpad, s.Qpad, s.Fpad,
+                          s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o,
+                          p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
+                          p.lds_part_floats, p.lds_bytes};
+  mix(dims, sizeof(dims));
+  if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
+  if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
+  if (!p.small.empty()) mix(p.small.data(), p.small.size() * sizeof(LayerSmall));
+  return h;
+}
+
+int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::string& err) {
+  p = HostPlan();
+  Shape& s = p.s;
+  s.n_layers = cfg.n_layers;
+  s.H = cfg.hidden;
+  s.n_heads = cfg.n_heads;
+  s.n_kv = cfg.n_kv_heads;
+  s.hd = cfg.head_dim;
+  s.F = cfg.ffn;
+  s.V = cfg.vocab;
+  s.qk_norm = cfg.qk_norm != 0;
+  s.tied = cfg.tie_embeddings != 0;
+  s.max_positions = cfg.max_positions;
+  if (s.n_layers < 1 || s.H < 1 || s.n_heads < 1 || s.n_kv < 1 || s.F < 1 || s.V < 1)
+    return fail(err, TILES_E_CONFIG, "non-positive model dimension");
+  if (s.hd != 64 && s.hd != 128) return fail(err, TILES_E_CONFIG, "head_dim must be 64 or 128");
+  if (s.n_heads % s.n_kv != 0) return fail(err, TILES_E_CONFIG, "n_kv_heads must divide n_heads");
+  s.G = s.n_heads / s.n_kv;
+  if (s.G > MAX_GROUP) return fail(err, TILES_E_CONFIG, "more than 4 query heads per KV head");
+  if (s.max_positions < 1) return fail(err, TILES_E_CONFIG, "max_positions must be >= 1");
+  if (!(cfg.rms_eps > 0.0f) || !(cfg.rope_theta > 1.0f)) return fail(err, TILES_E_CONFIG, "bad rms_eps or rope_theta");
+  if (n_workers < 1) return fail(err, TILES_E_CONFIG, "n_workers must be >= 1");
+  if (n_workers < s.n_heads || n_workers < s.n_kv) return fail(err, TILES_E_CONFIG, "fewer workers than attention heads");
+  if (s.n_heads * s.hd > 65536 || s.H > 65536 || s.F > 65536) return fail(err, TILES_E_CONFIG, "dimension too large");
+  p.W = n_workers;
+  const int32_t W = n_workers;
+  s.qkv_rows = (s.n_heads + 2 * s.n_kv) * s.hd;
+  s.Hpad = (int32_t)round_up(s.H, CHUNK_COLS);
+  s.Qpad = (int32_t)round_up((int64_t)s.n_heads * s.hd, CHUNK_COLS);
+  s.Fpad = (int32_t)round_up(s.F, CHUNK_COLS);
+
+  // split-KV and combine placement
+  p.S = cfg.kv_splits > 0 ? cfg.kv_splits : choose_splits(s, W);
+  if (p.S < 1 || (int64_t)p.S * s.n_kv > W) return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads exceeds workers");
+  const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 2) * 4;
+  if (cfg.combine_mode == 1) p.combine_in_o = 1;
+  else if (cfg.combine_mode == 2) p.combine_in_o = 0;
+  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= 40 * 1024 ? 1 : 0;
+  else return fail(err, TILES_E_CONFIG, "combine_mode must be 0, 1 or 2");
+
+  // ---- packed layout: norm gains first, then the GEMV waves in execution order ----
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  p.small.resize(s.n_layers);
+  for (int l = 0; l < s.n_layers; ++l) {
+    LayerSmall& ls = p.small[l];
+    ls.attn_norm = take((int64_t)s.H * 2);
+    p.copies.push_back({SRC_ATTN_NORM, l, 0, 1, s.H, ls.attn_norm, (int64_t)s.H * 2});
+    ls.mlp_norm = take((int64_t)s.H * 2);
+    p.copies.push_back({SRC_MLP_NORM, l, 0, 1, s.H, ls.mlp_norm, (int64_t)s.H * 2});
+    if (s.qk_norm) {
+      ls.q_norm = take((int64_t)s.hd * 2);
+      p.copies.push_back({SRC_Q_NORM, l, 0, 1, s.hd, ls.q_norm, (int64_t)s.hd * 2});
+      ls.k_norm = take((int64_t)s.hd * 2);
+      p.copies.push_back({SRC_K_NORM, l, 0, 1, s.hd, ls.k_norm, (int64_t)s.hd * 2});
+    } else {
+      ls.q_norm = ls.k_norm = -1;
+    }
+  }
+  p.final_norm_off = take((int64_t)s.H * 2);
+  p.copies.push_back({SRC_FINAL_NORM, -1, 0, 1, s.H, p.final_norm_off, (int64_t)s.H * 2});
+  off = round_up(off, CHUNK_BYTES);
+
+  int64_t wbytes = 0;  // algorithmic weight bytes per step
+  for (int l = 0; l < s.n_layers; ++l) wbytes += (int64_t)s.H * 2 * 2 + (s.qk_norm ? (int64_t)s.hd * 2 * 2 : 0);
+  wbytes += (int64_t)s.H * 2;  // final norm
+
+  auto new_wave = [&](int32_t kind, int32_t layer) {
+    p.waves.push_back({kind, layer, 0, 0});
+    p.tiles.resize(p.waves.size() * (size_t)W);
+    for (int w = 0; w < W; ++w) {
+      TileDesc& t = p.tiles[(p.waves.size() - 1) * W + w];
+      std::memset(&t, 0, sizeof(t));
+      t.kind = KIND_NONE;
+    }
+    return (int32_t)p.waves.size() - 1;
+  };
+  auto tile_at = [&](int32_t wave, int32_t w) -> TileDesc& { return p.tiles[(size_t)wave * W + w]; };
+
+  // A GEMV wave over R output rows of width K (padded to kpad).  `seg` emits the
+  // copy segments for worker rows [lo, hi) given the destination offset.
+  auto gemv_wave = [&](int32_t kind, int32_t layer, int64_t R, int32_t K, int32_t kpad, int32_t rows_per_out,
+                       auto&& seg) {
+    int32_t wv = new_wave(kind, layer);
+    int32_t max_rows = 0;
+    for (int w = 0; w < W; ++w) {
+      int64_t lo, hi;
+      row_split(R, W, w, lo, hi);
+      if (hi <= lo) continue;
+      TileDesc& t = tile_at(wv, w);
+      t.kind = kind;
+      t.row0 = (int32_t)lo;
+      t.nrows = (int32_t)(hi - lo);
+      t.kpad = kpad;
+      t.woff = off;
+      seg(lo, hi, off);
+      const int64_t rows = (hi - lo) * rows_per_out;
+      max_rows = std::max<int32_t>(max_rows, (int32_t)rows);
+      off += rows * kpad * 2;
+    }
+    p.waves[wv].max_rows = max_rows;
+    wbytes += R * rows_per_out * (int64_t)K * 2;
+    return wv;
+  };
+
+  for (int l = 0; l < s.n_layers; ++l) {
+    // QKV: rows of [Wq; Wk; Wv]
+    const int64_t qr = (int64_t)s.n_heads * s.hd, kr = (int64_t)s.n_kv * s.hd;
+    gemv_wave(KIND_QKV, l, s.qkv_rows, s.H, s.Hpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
+      const int64_t bounds[4] = {0, qr, qr + kr, qr + 2 * kr};
+      const int32_t src[3] = {SRC_WQ, SRC_WK, SRC_WV};
+      for (int m = 0; m < 3; ++m) {
+        int64_t a = std::max(lo, bounds[m]), b = std::min(hi, bounds[m + 1]);
+        if (b > a) p.copies.push_back({src[m], l, a - bounds[m], b - a, s.H, dst + (a - lo) * s.Hpad * 2, (int64_t)s.Hpad * 2});
+      }
+    });
+    // attention: one tile per (KV head, split)
+    {
+      int32_t wv = new_wave(KIND_ATTN, l);
+      for (int g = 0; g < s.n_kv; ++g)
+        for (int sp = 0; sp < p.S; ++sp) {
+          TileDesc& t = tile_at(wv, g * p.S + sp);
+          t.kind = KIND_ATTN;
+          t.row0 = g;
+          t.nrows = sp;
+        }
+    }
+    if (!p.combine_in_o) {
+      int32_t wv = new_wave(KIND_COMBINE, l);
+      for (int h = 0; h < s.n_heads; ++h) {
+        TileDesc& t = tile_at(wv, h);
+        t.kind = KIND_COMBINE;
+        t.row0 = h;
+      }
+    }
+    gemv_wave(KIND_O, l, s.H, s.n_heads * s.hd, s.Qpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
+      p.copies.push_back({SRC_WO, l, lo, hi - lo, (int64_t)s.n_heads * s.hd, dst, (int64_t)s.Qpad * 2});
+    });
+    // gate and up rows interleaved (gate j, up j, gate j+1, ...) so any even row block holds whole pairs
+    gemv_wave(KIND_GU, l, s.F, s.H, s.Hpad, 2, [&](int64_t lo, int64_t hi, int64_t dst) {
+      p.copies.push_back({SRC_WGATE, l, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * 2 * 2});
+      p.copies.push_back({SRC_WUP, l, lo, hi - lo, s.H, dst + (int64_t)s.Hpad * 2, (int64_t)s.Hpad * 2 * 2});
+    });
+    gemv_wave(KIND_DOWN, l, s.H, s.F, s.Fpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
+      p.copies.push_back({SRC_WDOWN, l, lo, hi - lo, s.F, dst, (int64_t)s.Fpad * 2});
+    });
+  }
+  const int64_t lm_base = off;
+  gemv_wave(KIND_LM, -1, s.V, s.H, s.Hpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
+    p.copies.push_back({s.tied ? SRC_EMBED : SRC_LM_HEAD, -1, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * 2});
+  });
+  wbytes += (int64_t)s.H * 2;  // one embedding row per token
+  if (s.tied) {
+    p.embed_off = lm_base;  // LM-head rows are the embedding rows, in order
+  } else {
+    p.embed_off = off;
+    p.copies.push_back({SRC_EMBED, -1, 0, s.V, s.H, off, (int64_t)s.Hpad * 2});
+    off += (int64_t)s.V * s.Hpad * 2;
+  }
+  p.embed_stride = (int64_t)s.Hpad * 2;
+  p.packed_bytes = round_up(off, 4096);
+  p.weight_bytes_per_step = wbytes;
+
+  // ---- per-wave bytes and balance ----
+  const int nw = (int)p.waves.size();
+  p.wave_bytes.assign(nw, 0);
+  p.wave_max_bytes.assign(nw, 0);
+  p.wave_busy.assign(nw, 0);
+  double worst = 1.0;
+  for (int wv = 0; wv < nw; ++wv) {
+    int64_t tot = 0, mx = 0, row_bytes = 0;
+    int busy = 0;
+    for (int w = 0; w < W; ++w) {
+      const TileDesc& t = p.tiles[(size_t)wv * W + w];
+      if (t.kind == KIND_NONE) continue;
+      ++busy;
+      int64_t b = 0;
+      if (t.kind != KIND_ATTN && t.kind != KIND_COMBINE) {
+        const int64_t rows = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1);
+        b = rows * t.kpad * 2;
+        row_bytes = (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1);
+      }
+      tot += b;
+      mx = std::max(mx, b);
+    }
+    p.wave_bytes[wv] = tot;
+    p.wave_max_bytes[wv] = mx;
+    p.wave_busy[wv] = busy;
+    if (tot > 0) {
+      const double mean = (double)tot / W;
+      worst = std::max(worst, (double)mx / mean);
+      (void)row_bytes;
+    }
+  }
+  p.max_over_mean = worst;
+
+  // ---- LDS sizing ----
+  int32_t vec = std::max({s.Hpad, s.Qpad, s.Fpad});
+  // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NWAVES] in LDS)
+  int32_t part = 0;
+  for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NWAVES);
+  // attention tile: q[G][hd], k[hd], v[hd] and the wave states [NWAVES][G][hd + 2]
+  part = std::max(part, s.G * s.hd + 2 * s.hd + NWAVES * s.G * (s.hd + 2));
+  part = std::max(part, p.S * (s.hd + 2));                                  // one head's splits (combine tile)
+  if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * (s.hd + 2));  // all splits (o_proj prologue)
+  p.lds_vec_floats = (int32_t)round_up(vec, 64);
+  p.lds_part_floats = (int32_t)round_up(part, 64);
+  const int32_t small_bytes = 4096;
+  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats) * 4 + small_bytes;
+  // more than half the LDS of a CU: at most one workgroup per compute unit
+  p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
+  if (p.lds_bytes > 160 * 1024) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
+
+  int rc = validate_plan(p, err);
+  if (rc != TILES_OK) return rc;
+  p.checksum = plan_checksum(p);
+  return TILES_OK;
+}
+
+int validate_plan(const HostPlan& p, std::string& err) {
+  const Shape& s = p.s;
+  const int32_t W = p.W;
+  const int nw = (int)p.waves.size();
+  std::ostringstream os;
+  if ((size_t)nw * W != p.tiles.size()) return fail(err, TILES_E_PLAN, "tile table size mismatch");
+
+  // wave order: per layer QKV, ATTN, [COMBINE], O, GU, DOWN; then LM
+  {
+    std::vector<int32_t> want;
+    for (int l = 0; l < s.n_layers; ++l) {
+      want.push_back(KIND_QKV);
+      want.push_back(KIND_ATTN);
+      if (!p.combine_in_o) want.push_back(KIND_COMBINE);
+      want.push_back(KIND_O);
+      want.push_back(KIND_GU);
+      want.push_back(KIND_DOWN);
+    }
+    want.push_back(KIND_LM);
+    if ((int)want.size() != nw) return fail(err, TILES_E_PLAN, "unexpected number of waves");
+    int per = p.combine_in_o ? 5 : 6;
+    for (int wv = 0; wv < nw; ++wv) {
+      if (p.waves[wv].kind != want[wv]) return fail(err, TILES_E_PLAN, "waves out of dependency order");
+      const int32_t layer = wv == nw - 1 ? -1 : wv / per;
+      if (p.waves[wv].layer != layer) return fail(err, TILES_E_PLAN, "wave layer mismatch");
+    }
+  }
+
+  // per-wave coverage, packing bounds and hazards
+  std::vector<std::pair<int64_t, int64_t>> packed_ranges;
+  for (int wv = 0; wv < nw; ++wv) {
+    const int32_t kind = p.waves[wv].kind;
+    const int32_t layer = p.waves[wv].layer;
+    std::vector<TileIO> io(W);
+    int64_t covered = 0, expect_next = 0;
+    std::vector<int> seen;
+    for (int w = 0; w < W; ++w) {
+      const TileDesc& t = p.tiles[(size_t)wv * W + w];
+      if (t.kind == KIND_NONE) continue;
+      if (t.kind != kind) return fail(err, TILES_E_PLAN, "tile kind differs from its wave");
+      TileIO& x = io[w];
+      switch (kind) {
+        case KIND_QKV: case KIND_O: case KIND_GU: case KIND_DOWN: case KIND_LM: {
+          int64_t R = kind == KIND_QKV ? s.qkv_rows : kind == KIND_GU ? s.F : kind == KIND_LM ? s.V : s.H;
+          int32_t kp = kind == KIND_O ? s.Qpad : kind == KIND_DOWN ? s.Fpad : s.Hpad;
+          if (t.nrows < 1 || t.row0 != expect_next || t.row0 + (int64_t)t.nrows > R)
+            return fail(err, TILES_E_PLAN, "GEMV rows not an ordered exact cover");
+          if (t.kpad != kp || kp % CHUNK_COLS != 0) return fail(err, TILES_E_PLAN, "bad GEMV width");
+          expect_next = t.row0 + t.nrows;
+          covered += t.nrows;
+          const int64_t bytes = (int64_t)t.nrows * (kind == KIND_GU ? 2 : 1) * t.kpad * 2;
+          if (t.woff % CHUNK_BYTES != 0 || t.woff < 0 || t.woff + bytes > p.packed_bytes)
+            return fail(err, TILES_E_PLAN, "packed weights out of bounds or misaligned");
+          packed_ranges.push_back({t.woff, t.woff + bytes});
+          const int64_t lo = t.row0, hi = t.row0 + t.nrows;
+          if (kind == KIND_QKV) {
+            x.reads.push_back({BUF_X, 0, s.H});
+            x.writes.push_back({BUF_QKV, lo, hi});
+          } else if (kind == KIND_O) {
+            if (p.combine_in_o) x.reads.push_back({BUF_PART, 0, (int64_t)s.n_heads * p.S});
+            else x.reads.push_back({BUF_ATTN, 0, (int64_t)s.n_heads * s.hd});
+            x.reads.push_back({BUF_X, lo, hi});
+            x.writes.push_back({BUF_X, lo, hi});
+          } else if (kind == KIND_GU) {
+            x.reads.push_back({BUF_X, 0, s.H});
+            x.writes.push_back({BUF_ACT, lo, hi});
+          } else if (kind == KIND_DOWN) {
+            x.reads.push_back({BUF_ACT, 0, s.F});
+            x.reads.push_back({BUF_X, lo, hi});
+            x.writes.push_back({BUF_X, lo, hi});
+          } else {
+            x.reads.push_back({BUF_X, 0, s.H});
+            x.writes.push_back({BUF_LMPART, w, w + 1});
+            x.writes.push_back({BUF_LOGITS, lo, hi});
+          }
+          break;
+        }
+        case KIND_ATTN: {
+          if (t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S)
+            return fail(err, TILES_E_PLAN, "attention tile out of range");
+          seen.push_back(t.row0 * p.S + t.nrows);
+          x.reads.push_back({BUF_QKV, 0, s.qkv_rows});
+          // cached positions of this KV head (all positions before the current one)
+          const int64_t kvbase = ((int64_t)layer * s.n_kv + t.row0) * s.max_positions;
+          x.reads.push_back({BUF_KV, kvbase, kvbase + s.max_positions - 1});
+          // The current position is written by exactly one split (the one holding L-1, checked
+          // for every L below); the model gives that write to split 0 and a slot past every read.
+          if (t.nrows == 0) x.writes.push_back({BUF_KV, kvbase + s.max_positions - 1, kvbase + s.max_positions});
+          for (int g2 = 0; g2 < s.G; ++g2) {
+            int64_t h = (int64_t)t.row0 * s.G + g2;
+            x.writes.push_back({BUF_PART, h * p.S + t.nrows, h * p.S + t.nrows + 1});
+          }
+          break;
+        }
+        case KIND_COMBINE: {
+          if (t.row0 < 0 || t.row0 >= s.n_heads) return fail(err, TILES_E_PLAN, "combine tile out of range");
+          seen.push_back(t.row0);
+          x.reads.push_back({BUF_PART, (int64_t)t.row0 * p.S, (int64_t)(t.row0 + 1) * p.S});
+          x.writes.push_back({BUF_ATTN, (int64_t)t.row0 * s.hd, (int64_t)(t.row0 + 1) * s.hd});
+          break;
+        }
+        default:
+          return fail(err, TILES_E_PLAN, "unknown tile kind");
+      }
+    }
+    if (kind == KIND_ATTN || kind == KIND_COMBINE) {
+      std::sort(seen.begin(), seen.end());
+      const int want_n = kind == KIND_ATTN ? s.n_kv * p.S : s.n_heads;
+      if ((int)seen.size() != want_n) return fail(err, TILES_E_PLAN, "attention/combine tiles do not cover every head");
+      for (int i = 0; i < want_n; ++i)
+        if (seen[i] != i) return fail(err, TILES_E_PLAN, "attention/combine tile duplicated or missing");
+    } else {
+      int64_t R = kind == KIND_QKV ? s.qkv_rows : kind == KIND_GU ? s.F : kind == KIND_LM ? s.V : s.H;
+      if (covered != R || expect_next != R) return fail(err, TILES_E_PLAN, "GEMV rows not covered exactly once");
+    }
+    // hazards: a write of one worker may not meet a read or write of another worker in the same wave
+    for (int a = 0; a < W; ++a)
+      for (const Interval& wr : io[a].writes)
+        for (int b = 0; b < W; ++b) {
+          if (b == a) continue;
+          for (const Interval& o : io[b].reads)
+            if (o.buf == wr.buf && o.lo < wr.hi && wr.lo < o.hi) {
+              os << "read/write hazard in wave " << wv << " between workers " << a << " and " << b;
+              return fail(err, TILES_E_PLAN, os.str());
+            }
+          for (const Interval& o : io[b].writes)
+            if (o.buf == wr.buf && o.lo < wr.hi && wr.lo < o.hi) {
+              os << "write/write hazard in wave " << wv << " between workers " << a << " and " << b;
+              return fail(err, TILES_E_PLAN, os.str());
+            }
+        }
+  }
+  // packed ranges of different tiles never overlap
+  std::sort(packed_ranges.begin(), packed_ranges.end());
+  for (size_t i = 1; i < packed_ranges.size(); ++i)
+    if (packed_ranges[i].first < packed_ranges[i - 1].second) return fail(err, TILES_E_PLAN, "packed tiles overlap");
+
+  // split-KV: for every attended length the splits partition [0, L) and exactly one holds L-1
+  for (int64_t L = 1; L <= s.max_positions; ++L) {
+    int64_t next = 0;
+    int holders = 0;
+    for (int sp = 0; sp < p.S; ++sp) {
+      int64_t lo, hi;
+      split_range(L, p.S, sp, lo, hi);
+      if (hi > lo) {
+        if (lo != next) return fail(err, TILES_E_PLAN, "KV splits do not partition the positions");
+        next = hi;
+        if (lo <= L - 1 && L - 1 < hi) ++holders;
+      }
+    }
+    if (next != L || holders != 1) return fail(err, TILES_E_PLAN, "KV splits do not partition the positions");
+    // the KV write happens in the split holding L-1; the kernel makes that split write
+  }
+
+  // byte balance: max/mean within one row of a perfect split
+  for (int wv = 0; wv < nw; ++wv) {
+    if (p.wave_bytes.empty() || p.wave_bytes[wv] == 0) continue;
+    const double mean = (double)p.wave_bytes[wv] / W;
+    int64_t row_bytes = 0;
+    for (int w = 0; w < W; ++w) {
+      const TileDesc& t = p.tiles[(size_t)wv * W + w];
+      if (t.kind != KIND_NONE) row_bytes = std::max<int64_t>(row_bytes, (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1));
+    }
+    if ((double)p.wave_max_bytes[wv] > mean + row_bytes + 0.5) return fail(err, TILES_E_PLAN, "worker bytes unbalanced");
+  }
+
+  // LDS capacity for every wave's staging
+  if (p.lds_part_floats / NWAVES < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
+  if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
+  if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 2) > p.lds_part_floats)
+    return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
+  return TILES_OK;
+}
+
+}  // namespace tiles

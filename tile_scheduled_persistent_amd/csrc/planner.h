@@ -1,0 +1,85 @@
+// Host planner: tile graph, static schedule, validation and weight-packing layout.
+// Pure C++ (no HIP): it runs without a GPU and is exercised by tiles_plan_dry_run.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/tiles.h"
+#include "plan_types.h"
+
+namespace tiles {
+
+// Which source tensor a packing copy reads.
+enum SrcTensor : int32_t {
+  SRC_EMBED, SRC_FINAL_NORM, SRC_LM_HEAD,
+  SRC_ATTN_NORM, SRC_WQ, SRC_WK, SRC_WV, SRC_Q_NORM, SRC_K_NORM, SRC_WO, SRC_MLP_NORM, SRC_WGATE, SRC_WUP, SRC_WDOWN,
+};
+
+// Copy `nrows` rows of `cols` BF16 values starting at row `src_row` of a source tensor
+// into the packed buffer at `dst_off`, rows `dst_pitch` bytes apart (padding stays zero).
+struct CopySeg {
+  int32_t tensor;
+  int32_t layer;
+  int64_t src_row;
+  int64_t nrows;
+  int64_t cols;
+  int64_t dst_off;
+  int64_t dst_pitch;
+};
+
+// Buffers named by the hazard check.
+enum BufId : int32_t { BUF_X, BUF_QKV, BUF_PART, BUF_ATTN, BUF_ACT, BUF_LMPART, BUF_KV, BUF_LOGITS, BUF_COUNT };
+
+struct Interval {
+  int32_t buf;
+  int64_t lo, hi;  // [lo, hi)
+};
+
+struct Shape {
+  int32_t n_layers, H, n_heads, n_kv, hd, F, V;
+  int32_t G;                  // query heads per KV head
+  int32_t qkv_rows;           // (n_heads + 2 n_kv) * hd
+  int32_t Hpad, Qpad, Fpad;   // padded GEMV widths (multiples of CHUNK_COLS)
+  bool qk_norm, tied;
+  int32_t max_positions;
+};
+
+struct HostPlan {
+  Shape s;
+  int32_t W = 0;               // workers
+  int32_t S = 1;               // KV splits
+  int32_t combine_in_o = 1;    // 1 prologue, 0 own wave
+  std::vector<WaveDesc> waves;
+  std::vector<TileDesc> tiles; // [n_waves][W]
+  std::vector<LayerSmall> small;
+  int64_t final_norm_off = 0, embed_off = 0, embed_stride = 0;
+  int64_t packed_bytes = 0;
+  int64_t weight_bytes_per_step = 0;  // algorithmic (unpadded) weight bytes per token
+  std::vector<CopySeg> copies;
+  std::vector<int64_t> wave_bytes, wave_max_bytes;  // padded bytes streamed per wave (all / max worker)
+  std::vector<int32_t> wave_busy;
+  double max_over_mean = 1.0;
+  int32_t lds_vec_floats = 0, lds_part_floats = 0, lds_bytes = 0;
+  uint64_t checksum = 0;
+};
+
+// Build and validate a plan.  Returns TILES_OK or a TILES_E_* code with `err` set.
+int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& plan, std::string& err);
+
+// Re-run every structural check on an existing plan (used at create and by tests).
+int validate_plan(const HostPlan& plan, std::string& err);
+
+// 64-bit FNV-1a over the schedule and its geometry.
+uint64_t plan_checksum(const HostPlan& plan);
+
+// The split [lo, hi) of KV positions that split `s` of `S` covers when `L` positions are attended.
+inline void split_range(int64_t L, int32_t S, int32_t s, int64_t& lo, int64_t& hi) {
+  int64_t c = (L + S - 1) / S;
+  lo = (int64_t)s * c;
+  hi = lo + c < L ? lo + c : L;
+  if (lo > L) lo = L;
+}
+
+}  // namespace tiles

@@ -1,0 +1,266 @@
+"""Python binding of ``include/tiles.h`` (ctypes; argument marshalling only).
+
+Every step of the decode runs in the HIP library; this module only converts
+torch tensors to raw device pointers and back.  If ``libtiles.so`` is missing the
+import of the library raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from .configs import ModelConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtiles.so")
+
+TILES_OK = 0
+TILES_E_ARG = -1
+TILES_E_CONFIG = -2
+TILES_E_PLAN = -3
+TILES_E_DEVICE = -4
+TILES_E_HIP = -5
+TILES_E_KERNEL = -6
+
+TILES_DEBUG_HIDDEN = 0x1
+TILES_TRACE = 0x2
+TILES_POISON = 0x4
+
+WAVE_KINDS = {1: "qkv", 2: "attn", 3: "combine", 4: "o_proj", 5: "gate_up", 6: "down", 7: "lm_head"}
+
+
+class TilesError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tiles error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+        ("qk_norm", ctypes.c_int32), ("tie_embeddings", ctypes.c_int32), ("max_positions", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("kv_splits", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
+        ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
+    ]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "mlp_norm", "w_gate", "w_up", "w_down"]]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights)), ("on_device", ctypes.c_int32)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("length", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_workers", ctypes.c_int32), ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("waves_per_step", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("kv_splits", ctypes.c_int32),
+        ("combine_mode", ctypes.c_int32), ("occupancy", ctypes.c_int32), ("packed_bytes", ctypes.c_int64),
+        ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
+        ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64),
+    ]
+
+
+class WaveInfo(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("layer", ctypes.c_int32), ("busy_workers", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("weight_bytes", ctypes.c_int64), ("max_worker_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libtiles.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tile_scheduled_persistent_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tiles_plan_create.restype = ctypes.c_void_p
+        L.tiles_plan_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights)]
+        L.tiles_decode.restype = ctypes.c_int
+        L.tiles_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_plan_destroy.restype = None
+        L.tiles_plan_destroy.argtypes = [ctypes.c_void_p]
+        L.tiles_last_error.restype = ctypes.c_char_p
+        L.tiles_last_error.argtypes = []
+        L.tiles_plan_info.restype = ctypes.c_int
+        L.tiles_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]
+        L.tiles_plan_wave.restype = ctypes.c_int
+        L.tiles_plan_wave.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(WaveInfo)]
+        L.tiles_plan_dry_run.restype = ctypes.c_int
+        L.tiles_plan_dry_run.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.POINTER(PlanInfo)]
+        L.tiles_plan_set_stream.restype = ctypes.c_int
+        L.tiles_plan_set_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_plan_status.restype = ctypes.c_int
+        L.tiles_plan_status.argtypes = [ctypes.c_void_p]
+        L.tiles_read_debug.restype = ctypes.c_int
+        L.tiles_read_debug.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_int32)]
+        L.tiles_plan_debug_corrupt.restype = ctypes.c_int
+        L.tiles_plan_debug_corrupt.argtypes = [ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().tiles_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != TILES_OK:
+        raise TilesError(rc, last_error())
+
+
+def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
+                n_workers: int = 0, stream: Optional[int] = None) -> Config:
+    return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
+                  float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
+                  int(kv_splits), int(combine_mode), int(n_workers), stream)
+
+
+def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
+    """Plan on the host only (no GPU); raises TilesError if planning/validation fails."""
+    info = PlanInfo()
+    cfg = make_config(m, max_positions, **kw)
+    _check(lib().tiles_plan_dry_run(ctypes.byref(cfg), n_workers, ctypes.byref(info)))
+    return info
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+@dataclass
+class KVCache:
+    """Caller-owned BF16 cache [n_layers, n_kv_heads, capacity, head_dim] (device)."""
+    k: torch.Tensor
+    v: torch.Tensor
+    length: int = 0
+
+    @property
+    def capacity(self) -> int:
+        return self.k.shape[2]
+
+
+class Plan:
+    """A tile plan for one model on the current device (owns a packed copy of the weights)."""
+
+    def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
+                 combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None):
+        self.model = m
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream)
+        on_device = weights["embed"].is_cuda
+        layers = (LayerWeights * m.n_layers)()
+        for i, d in enumerate(weights["layers"]):
+            for name, _ in LayerWeights._fields_:
+                t = d.get(name)
+                if t is not None:
+                    if t.dtype != torch.bfloat16 or t.is_cuda != on_device:
+                        raise ValueError(f"layer {i} {name}: expected bf16 on the same device as embed")
+                    setattr(layers[i], name, _ptr(t))
+        w = Weights(_ptr(weights["embed"]), _ptr(weights["final_norm"]), _ptr(weights.get("lm_head")), layers,
+                    1 if on_device else 0)
+        self._weights_struct = (w, layers)
+        h = lib().tiles_plan_create(ctypes.byref(self._cfg), ctypes.byref(w))
+        if not h:
+            raise TilesError(-99, last_error())
+        self._h = h
+        self._weights_struct = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().tiles_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ------------------------------------------------------------------
+    def decode(self, kv: KVCache, token: int, n_steps: int, out_tokens: torch.Tensor,
+               out_logits: Optional[torch.Tensor] = None) -> int:
+        """Enqueue one cooperative launch of ``n_steps`` greedy steps; returns TILES_OK or raises."""
+        if out_tokens.dtype != torch.int32 or not out_tokens.is_cuda or out_tokens.numel() < n_steps:
+            raise ValueError("out_tokens must be a device int32 tensor with n_steps entries")
+        if out_logits is not None and (out_logits.dtype != torch.float32 or not out_logits.is_cuda
+                                       or out_logits.numel() < n_steps * self.model.vocab):
+            raise ValueError("out_logits must be a device float32 tensor [n_steps, vocab]")
+        for t in (kv.k, kv.v):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("KV tensors must be contiguous device bf16")
+        c = KV(_ptr(kv.k), _ptr(kv.v), kv.capacity, kv.length)
+        rc = lib().tiles_decode(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(out_tokens),
+                                _ptr(out_logits))
+        _check(rc)
+        kv.length = c.length
+        return rc
+
+    def status(self) -> int:
+        return lib().tiles_plan_status(self._h)
+
+    def info(self) -> PlanInfo:
+        info = PlanInfo()
+        _check(lib().tiles_plan_info(self._h, ctypes.byref(info)))
+        return info
+
+    def waves(self) -> List[WaveInfo]:
+        out = []
+        for i in range(self.info().waves_per_step):
+            wi = WaveInfo()
+            _check(lib().tiles_plan_wave(self._h, i, ctypes.byref(wi)))
+            out.append(wi)
+        return out
+
+    def read_debug(self, hidden: bool = True, trace: bool = False):
+        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, 3] uint64 or None)."""
+        info = self.info()
+        n = ctypes.c_int32(0)
+        _check(lib().tiles_read_debug(self._h, None, None, ctypes.byref(n)))
+        hid = tr = None
+        hp = tp = None
+        if hidden:
+            hid = np.zeros((n.value, self.model.n_layers, self.model.hidden), dtype=np.float32)
+            hp = hid.ctypes.data
+        if trace:
+            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, 3), dtype=np.uint64)
+            tp = tr.ctypes.data
+        _check(lib().tiles_read_debug(self._h, hp, tp, None))
+        return hid, tr
+
+    def set_stream(self, stream: torch.cuda.Stream):
+        self.stream = stream
+        _check(lib().tiles_plan_set_stream(self._h, stream.cuda_stream))
+
+    def debug_corrupt(self):
+        _check(lib().tiles_plan_debug_corrupt(self._h))
