@@ -194,37 +194,43 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     _, tr = plan.read_debug(hidden=False, trace=True)
     waves = plan.waves()
     plan.close()
-    tr = tr.astype(np.int64)  # [steps, waves, W, 3] 100 MHz ticks
+    tr = tr.astype(np.int64)  # [steps, waves, W, 5] 100 MHz ticks: start, staged, computed, arrived, released
     steps = tr.shape[0]
     names = tiles.WAVE_KINDS
-    # wave duration: from the latest release of the previous wave to the latest release of this wave
-    rel = tr[:, :, :, 2].max(axis=2)  # [steps, waves]
+    rel = tr[:, :, :, 4].max(axis=2)  # [steps, waves] last release
     start = tr[:, :, :, 0].min(axis=2)
-    work = (tr[:, :, :, 1] - tr[:, :, :, 0])  # per worker busy time before arriving
-    wait = (tr[:, :, :, 2] - tr[:, :, :, 1])  # per worker barrier time
-    lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz)",
+    busy = tr[:, :, :, 0] != 0
+    def phase(a, b):  # per (step, wave): max over busy workers of t_b - t_a, in us
+        d = np.where(busy, tr[:, :, :, b] - tr[:, :, :, a], 0)
+        return d.max(axis=2) * 0.01
+    pro, cmp_, epi = phase(0, 1), phase(1, 2), phase(2, 3)
+    wait = (tr[:, :, :, 4] - tr[:, :, :, 3]).mean(axis=2) * 0.01
+    lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz); phase columns are the max over",
+             "# workers of: prologue (inputs staged), compute (weights consumed), epilogue (outputs stored);",
+             "# barrier = mean wait from arrival to release",
              f"# workload: {wl.description}; steps traced: {steps}; waves per step: {len(waves)}",
-             "wave\tkind\tlayer\tMB\tdur_us(median over steps)\tGB/s\tmax_work_us\tmean_barrier_us"]
+             "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tprologue_us\tcompute_us\tepilogue_us\tbarrier_us"]
     tot_dur = 0.0
     per_kind = {}
     for i, wv in enumerate(waves):
         prev_rel = rel[:, i - 1] if i > 0 else start[:, 0]
-        dur = np.median(rel[:, i] - prev_rel) * 0.01  # us
+        dur = float(np.median(rel[:, i] - prev_rel)) * 0.01
         tot_dur += dur
-        mb = wv.weight_bytes / 1e6
         gbs = (wv.weight_bytes / 1e9) / (dur * 1e-6) if dur > 0 else 0.0
-        mw = np.median(work[:, i, :].max(axis=1)) * 0.01
-        bw = np.median(wait[:, i, :].mean(axis=1)) * 0.01
         k = names.get(wv.kind, str(wv.kind))
-        d = per_kind.setdefault(k, [0.0, 0.0, 0.0])
+        ph = [float(np.median(x[:, i])) for x in (pro, cmp_, epi, wait)]
+        d = per_kind.setdefault(k, [0.0, 0.0, 0.0, 0.0, 0.0, 0.0])
         d[0] += dur
         d[1] += wv.weight_bytes
-        d[2] += bw
-        lines.append(f"{i}\t{k}\t{wv.layer}\t{mb:.2f}\t{dur:.2f}\t{gbs:.0f}\t{mw:.2f}\t{bw:.2f}")
-    lines.append("# per kind: total us per token, GB/s, summed mean barrier us")
-    for k, (dur, by, bw) in per_kind.items():
-        lines.append(f"# {k}\t{dur:.1f} us\t{by / 1e9 / (dur * 1e-6) if dur else 0:.0f} GB/s\tbarrier {bw:.1f} us")
-    step_us = np.median(np.diff(rel[:, -1])) * 0.01 if steps > 1 else tot_dur
+        for j in range(4):
+            d[2 + j] += ph[j]
+        lines.append(f"{i}\t{k}\t{wv.layer}\t{wv.weight_bytes / 1e6:.2f}\t{dur:.2f}\t{gbs:.0f}\t" +
+                     "\t".join(f"{x:.2f}" for x in ph))
+    lines.append("# per kind (us per token): total | GB/s | prologue | compute | epilogue | barrier")
+    for k, d in per_kind.items():
+        lines.append(f"# {k}\t{d[0]:.1f}\t{d[1] / 1e9 / (d[0] * 1e-6) if d[0] else 0:.0f} GB/s\t"
+                     f"{d[2]:.1f}\t{d[3]:.1f}\t{d[4]:.1f}\t{d[5]:.1f}")
+    step_us = float(np.median(np.diff(rel[:, -1]))) * 0.01 if steps > 1 else tot_dur
     lines.append(f"# token time (median step-to-step) {step_us:.1f} us; sum of wave medians {tot_dur:.1f} us")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")

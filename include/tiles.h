@@ -173,8 +173,9 @@ int tiles_plan_status(tiles_plan_t *plan);
 
 /* Copy debug buffers to host memory after synchronizing the plan's stream.
  *   hidden : host float [n_steps_of_last_decode][n_layers][H] or NULL (needs TILES_DEBUG_HIDDEN);
- *   trace  : host uint64 [n_steps][waves_per_step][n_workers][3] or NULL (needs TILES_TRACE):
- *            wave start, barrier arrival and barrier release, 100 MHz ticks.
+ *   trace  : host uint64 [n_steps][waves_per_step][n_workers][5] or NULL (needs TILES_TRACE):
+ *            wave start, input staged, compute done, barrier arrival, barrier release
+ *            (100 MHz wall-clock ticks).
  *   *n_steps_out receives the step count of the last decode. */
 int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t *n_steps_out);
 

@@ -250,7 +250,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
     TRY(hipMemsetAsync(p->dbg_hidden, 0, n * sizeof(float), p->stream));
   }
   if (cfg->flags & TILES_TRACE) {
-    const size_t n = (size_t)MAX_STEPS * hp.waves.size() * hp.W * 3;
+    const size_t n = (size_t)MAX_STEPS * hp.waves.size() * hp.W * TRACE_WORDS;
     TRY(hipMalloc(&p->trace, n * sizeof(uint64_t)));
     TRY(hipMemsetAsync(p->trace, 0, n * sizeof(uint64_t), p->stream));
   }
@@ -433,7 +433,7 @@ int tiles_read_debug(tiles_plan_t* p, float* hidden, uint64_t* trace, int32_t* n
   }
   if (trace) {
     if (!p->trace) return set_err(TILES_E_ARG, "plan was created without TILES_TRACE");
-    HIP_TRY(hipMemcpy(trace, p->trace, (size_t)p->last_steps * hp.waves.size() * hp.W * 3 * sizeof(uint64_t),
+    HIP_TRY(hipMemcpy(trace, p->trace, (size_t)p->last_steps * hp.waves.size() * hp.W * TRACE_WORDS * sizeof(uint64_t),
                       hipMemcpyDeviceToHost));
   }
   return TILES_OK;

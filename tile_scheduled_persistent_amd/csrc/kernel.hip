@@ -6,27 +6,36 @@
 // own ("Tiles: Scheduling LLM Decoding as a Graph of Tiles", intro): tiles, workers,
 // wave order and split boundaries are all fixed by the plan and the attended length.
 //
-// Tile bodies:
-//   * GEMV tiles stream their packed BF16 rows with 16-byte coalesced loads
-//     (one "chunk" = 64 lanes x 16 B = 512 columns of a row), multiply by an FP32
-//     input vector staged in LDS and reduce across the wavefront with DPP.
-//     Prologues fold RMSNorm (and, at layer 0, the embedding lookup); epilogues fold
-//     the residual add, SwiGLU and the greedy partial argmax ("History and roadmap",
-//     TileInfer.jl, "M8 so far" table: residual add + RMSNorm, SwiGLU in the GEMV).
-//   * Attention tiles apply q/k RMSNorm and RoPE, write the step's K/V (BF16) and run
-//     one split of grouped-query attention with an online softmax whose per-wavefront
-//     states are merged through LDS; splits are merged in the o_proj prologue or in a
-//     wave of their own (roadmap "Milestones", M5: split-KV decode attention;
-//     "Tried and not kept": combine kept out of the split kernel).
-//   * The LM-head tile writes logits and a (max, lowest index) partial; after the
-//     last barrier of a step every worker reduces all partials in worker order, so
-//     all workers agree on the next token without another barrier.
+// Workgroup organisation (512 threads = 8 wavefronts):
+//   * wavefront 0 is the control wave: it stages each tile's input vector in LDS
+//     (folding RMSNorm, the embedding lookup, the split merge, q/k norm, RoPE and the
+//     KV write), runs the epilogues (residual add, SwiGLU, partial argmax), performs
+//     every global store and takes part in the grid barrier;
+//   * wavefronts 1..7 are compute waves.  Each streams its share of the worker's packed
+//     weights through its own LDS ring with direct-to-LDS 16-byte loads
+//     (global_load_lds_dwordx4).  The ring is refilled in consumption order across
+//     wave boundaries, so while the workgroup waits at a grid barrier the weights of
+//     the next tiles keep arriving: weights do not depend on activations, only the dot
+//     products do (the Tiles page credits this prefetch idea to the megakernel it
+//     builds on).
 //
-// Cross-worker data (activations, partials, barrier words, the KV rows written this
-// launch) moves with device-coherent accesses: stores and loads carry the sc1 cache
-// policy, so they are performed at the device coherence point and need no L2
-// write-back or invalidate; a worker waits for its own stores to complete before it
-// signals the barrier.  Weights are read with non-temporal loads.
+// Tile bodies:
+//   * GEMV tiles: one "chunk" = 64 lanes x 16 B = 512 columns of one row; FP32 dot
+//     products against the LDS input vector, reduced across the wavefront with DPP
+//     ("History and roadmap", TileInfer.jl, "M8 so far": residual add + RMSNorm and
+//     SwiGLU fused into the GEMV).
+//   * Attention tiles: one split of grouped-query attention over the BF16 KV cache with
+//     an online softmax; the compute waves' states are merged through LDS and the
+//     splits are merged in the o_proj prologue or in a wave of their own (roadmap
+//     "Milestones", M5: split-KV decode; "Tried and not kept": no combine inside the
+//     split kernel).
+//   * LM head: logits and a (max, lowest index) partial per worker; after the last
+//     barrier of a step every worker reduces all partials in worker order.
+//
+// Cross-worker data (activations, partials, barrier words, KV rows written in this
+// launch) moves with device-coherent accesses (sc1 cache policy), so no L2 write-back
+// or invalidate is needed; the control wave waits for its stores to complete before it
+// signals the barrier.  Weights are read with plain loads into LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,18 +44,15 @@
 namespace tiles {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int SC1 = 16;  // buffer-instruction cache policy: device-coherent
+constexpr int SC1 = 16;  // buffer-instruction cache policy bit: device-coherent access
 
 // ---------------------------------------------------------------------------
 // coherent memory helpers
 // ---------------------------------------------------------------------------
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
 __device__ inline uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -63,12 +69,18 @@ __device__ inline void st_u64(uint64_t* p, uint64_t v) {
 __device__ inline uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ inline u32x4 ld_u32x4(const u32x4* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t lo = ld_u64(q), hi = ld_u64(q + 1);
-  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+// Buffer descriptor over a scratch array (byte offsets < 4 GB).  Device-coherent buffer
+// loads through it are plain (non-atomic) loads the compiler can issue back to back.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0xffffffffu, 0x00020000);
 }
+__device__ inline u32x4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, SC1);
+}
+__device__ inline f32x4 as_f32x4(u32x4 u) {
+  return f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+}
+#define COMPILER_FENCE() asm volatile("" ::: "memory")
 
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -96,20 +108,17 @@ constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within 16
 
-// sum over groups of 8 consecutive lanes
 __device__ inline float sum8(float v) {
   v += dpp<DPP_XOR1>(v);
   v += dpp<DPP_XOR2>(v);
   v += dpp<DPP_HALF_MIRROR>(v);
   return v;
 }
-// sum over groups of 16 consecutive lanes
 __device__ inline float sum16(float v) {
   v = sum8(v);
   v += dpp<DPP_MIRROR>(v);
   return v;
 }
-// sum over the whole wavefront (result in every lane)
 __device__ inline float wave_sum(float v) {
   v = sum16(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -120,51 +129,112 @@ __device__ inline float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// kernel state
+// LDS layout (dynamic): ring [NCOMP][RING_SLOTS][1 KB] | vec | part | small | segs.
+// small[] words written by the control wave before barrier A of every wave:
+constexpr int SM_DONE = 0;   // int: no more waves (end of launch or abort)
+constexpr int SM_KIND = 1;   // int: tile kind
+constexpr int SM_ROW0 = 2;   // int
+constexpr int SM_NROWS = 3;  // int
+constexpr int SM_LAYER = 4;  // int
+constexpr int SM_C = 5;      // int: chunks per GEMV row
+constexpr int SM_POS = 6;    // int: position of the current step
 // ---------------------------------------------------------------------------
 
-struct Ctx {
-  const KernelArgs* a;
-  float* vec;    // LDS input vector (lds_vec_floats)
-  float* part;   // LDS partial area (lds_part_floats)
-  float* small;  // LDS scratch (1024 floats)
-  int bid, tid, wave, lane;
-  int step, pos, L, tok;
-  bool aborted;
+struct Lds {
+  unsigned char* ring;
+  uint32_t ring_addr;  // LDS byte address of the ring
+  float* vec;
+  float* part;
+  float* small;
+  SegDesc* segs;
 };
 
-// block-wide sum; all threads receive the result; deterministic order
-__device__ inline float block_sum(Ctx& c, float v) {
-  v = wave_sum(v);
-  __syncthreads();
-  if (c.lane == 0) c.small[c.wave] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < NWAVES; ++w) s += c.small[w];
-  __syncthreads();
-  return s;
+__device__ inline bool is_gemv(int kind) {
+  return kind == KIND_QKV || kind == KIND_O || kind == KIND_GU || kind == KIND_DOWN || kind == KIND_LM;
 }
-
-// vec[i] = src[i] * rsqrt(mean(src^2) + eps) * gain[i] for i < n; vec[n..npad) = 0.
-// src is either an FP32 device-coherent vector or a BF16 embedding row.
-__device__ void norm_prologue(Ctx& c, const float* src_f32, const uint16_t* src_bf16, const uint16_t* gain, int n,
-                              int npad) {
-  float ss = 0.f;
-  for (int i = c.tid; i < npad; i += BLOCK_THREADS) {
-    float v = 0.f;
-    if (i < n) v = src_bf16 ? bf16_to_f32(src_bf16[i]) : ld_f32(src_f32 + i);
-    c.vec[i] = v;
-    ss += v * v;
-  }
-  const float tot = block_sum(c, ss);
-  const float rs = 1.0f / sqrtf(tot / (float)n + c.a->eps);
-  for (int i = c.tid; i < n; i += BLOCK_THREADS) c.vec[i] = c.vec[i] * rs * bf16_to_f32(gain[i]);
-  __syncthreads();
-}
+// chunk range of compute wave c over n chunks
+__device__ inline int chunk_lo(int n, int c) { return (int)(((int64_t)n * c) / NCOMP); }
 
 // ---------------------------------------------------------------------------
-// GEMV tile: part[r * NWAVES + wave] = partial dot of packed row r with vec
+// weight prefetcher of one compute wave: walks the worker's GEMV chunks in the
+// order the wave consumes them, across blocks, waves and steps.
+// ---------------------------------------------------------------------------
+
+struct Cursor {
+  int k, r0, i, ihi;
+  int64_t base;  // byte offset of the current block's first chunk
+};
+
+__device__ inline bool cursor_set(Cursor& cu, const SegDesc& s, int block_rows, int c) {
+  const int nr = min(block_rows, s.rows - cu.r0);
+  const int n = nr * s.chunks_per_row;
+  cu.i = chunk_lo(n, c);
+  cu.ihi = chunk_lo(n, c + 1);
+  cu.base = s.woff + (int64_t)cu.r0 * s.chunks_per_row * CHUNK_BYTES;
+  return cu.i < cu.ihi;
+}
+
+// Move to the next non-empty (wave, block) range; wraps to the next step.  A compute wave
+// with no chunk in the whole step parks on a valid address (loads that are never consumed).
+__device__ inline void cursor_next(Cursor& cu, const SegDesc* segs, int n_waves, int block_rows, int c) {
+  if (cu.k == -2) {  // parked: keep re-reading the first chunk of the packed buffer
+    cu.i = 0;
+    cu.ihi = 1;
+    return;
+  }
+  for (int guard = 0; guard < 4 * n_waves + 4; ++guard) {
+    if (cu.k >= 0 && cu.r0 + block_rows < segs[cu.k].rows) {
+      cu.r0 += block_rows;
+    } else {
+      cu.k = cu.k + 1 >= n_waves ? 0 : cu.k + 1;
+      cu.r0 = 0;
+      if (segs[cu.k].rows == 0) continue;
+    }
+    if (cursor_set(cu, segs[cu.k], block_rows, c)) return;
+  }
+  cu.k = -2;
+  cu.r0 = 0;
+  cu.base = 0;
+  cu.i = 0;
+  cu.ihi = 1;
+}
+
+// Direct-to-LDS 16-byte load of one chunk: lane l's 16 bytes land at lds_addr + 16 l.
+// Issued through inline assembly so that the compiler neither reorders LDS reads of the
+// ring around it nor adds waits for it: the ring protocol below does the waiting.
+__device__ inline void dma_chunk(const void* gaddr, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by construction
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off\n\t" ::"v"(gaddr),
+      "s"(lds_addr)
+      : "memory", "m0");
+}
+// The chunk consumed next was issued RING_SLOTS-1 loads ago (one load is issued per
+// consumed chunk, into the slot consumed one iteration earlier), so at most RING_SLOTS-2
+// younger loads are in flight; vector-memory loads complete in issue order.  Any other
+// load issued in between only makes this wait stricter.
+__device__ inline void ring_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING_SLOTS - 2) : "memory"); }
+__device__ inline void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct Prefetcher {
+  Cursor cu;
+  int slot;       // ring slot of the next chunk to consume
+  int free_slot;  // slot consumed in the previous iteration (refilled now)
+  uint32_t ring_addr;
+  const uint8_t* packed;
+  int lane;
+
+  __device__ inline void issue(const SegDesc* segs, int n_waves, int block_rows, int c, int into) {
+    const u32x4* g = reinterpret_cast<const u32x4*>(packed + cu.base) + (int64_t)cu.i * 64 + lane;
+    dma_chunk(g, ring_addr + (uint32_t)into * CHUNK_BYTES);
+    if (++cu.i >= cu.ihi) cursor_next(cu, segs, n_waves, block_rows, c);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// compute wave: GEMV block -> part[row * NCOMP + c]
 // ---------------------------------------------------------------------------
 
 __device__ inline float dot8(const u32x4 w, const float* v) {
@@ -181,169 +251,231 @@ __device__ inline float dot8(const u32x4 w, const float* v) {
   return s0 + s1;
 }
 
-// chunk range of wave w over n chunks
-__device__ inline int chunk_lo(int n, int w) { return (int)(((int64_t)n * w) / NWAVES); }
-
-constexpr int GEMV_BATCH = 8;
-
-__device__ void gemv_tile(Ctx& c, int64_t woff, int kpad, int rows) {
-  const int C = kpad / CHUNK_COLS;
-  const int n = rows * C;
-  const int c0 = chunk_lo(n, c.wave), c1 = chunk_lo(n, c.wave + 1);
-  const u32x4* base = reinterpret_cast<const u32x4*>(c.a->packed + woff) + c.lane;
-  const float* vlane = c.vec + c.lane * 8;
-  if (c0 < c1) {
-    int row = c0 / C, seg = c0 - row * C;
-    float acc = 0.f;
-    int i = c0;
-    u32x4 wa[GEMV_BATCH], wb[GEMV_BATCH];
-    int na = min(GEMV_BATCH, c1 - i);
-#pragma unroll
-    for (int u = 0; u < GEMV_BATCH; ++u)
-      if (u < na) wa[u] = __builtin_nontemporal_load(base + (int64_t)(i + u) * 64);
-    while (true) {
-      const int inext = i + na;
-      const int nb = min(GEMV_BATCH, c1 - inext);
-#pragma unroll
-      for (int u = 0; u < GEMV_BATCH; ++u)
-        if (u < nb) wb[u] = __builtin_nontemporal_load(base + (int64_t)(inext + u) * 64);
-#pragma unroll
-      for (int u = 0; u < GEMV_BATCH; ++u) {
-        if (u < na) {
-          acc += dot8(wa[u], vlane + seg * CHUNK_COLS);
-          if (++seg == C) {
-            const float s = wave_sum(acc);
-            if (c.lane == 0) c.part[row * NWAVES + c.wave] = s;
-            acc = 0.f;
-            seg = 0;
-            ++row;
-          }
-        }
-      }
-      if (nb <= 0) break;
-      i = inext;
-      na = nb;
-#pragma unroll
-      for (int u = 0; u < GEMV_BATCH; ++u) wa[u] = wb[u];
-    }
-    if (seg != 0) {  // range ended inside a row
+__device__ void compute_gemv_block(Prefetcher& pf, const Lds& L, int n_waves, int block_rows, int c, int lane, int C,
+                                   int nr) {
+  const int n = nr * C;
+  int i = chunk_lo(n, c);
+  const int ihi = chunk_lo(n, c + 1);
+  if (i >= ihi) return;
+  int row = i / C, seg = i - row * C;
+  float acc = 0.f;
+  const unsigned char* ring_c = L.ring + (size_t)c * RING_SLOTS * CHUNK_BYTES + lane * 16;
+  const float* vlane = L.vec + lane * 8;
+  for (; i < ihi; ++i) {
+    ring_wait();
+    const u32x4 w = *reinterpret_cast<const u32x4*>(ring_c + pf.slot * CHUNK_BYTES);
+    pf.issue(L.segs, n_waves, block_rows, c, pf.free_slot);
+    pf.free_slot = pf.slot;
+    pf.slot = pf.slot + 1 == RING_SLOTS ? 0 : pf.slot + 1;
+    acc += dot8(w, vlane + seg * CHUNK_COLS);
+    if (++seg == C) {
       const float s = wave_sum(acc);
-      if (c.lane == 0) c.part[row * NWAVES + c.wave] = s;
+      if (lane == 0) L.part[row * NCOMP + c] = s;
+      acc = 0.f;
+      seg = 0;
+      ++row;
     }
   }
-  __syncthreads();
+  if (seg != 0) {
+    const float s = wave_sum(acc);
+    if (lane == 0) L.part[row * NCOMP + c] = s;
+  }
 }
 
-// total of row r: sum of the partials of the waves whose chunk ranges touch it, in wave order
-__device__ inline float gemv_row_total(const Ctx& c, int rows, int C, int r) {
-  const int n = rows * C;
+// total of row r of a block: partials of the compute waves whose ranges touch it, in order
+__device__ inline float row_total(const Lds& L, int nr, int C, int r) {
+  const int n = nr * C;
   const int first = r * C, last = r * C + C - 1;
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < NWAVES; ++w) {
-    const int lo = chunk_lo(n, w), hi = chunk_lo(n, w + 1);
-    if (lo < hi && lo <= last && first < hi) s += c.part[r * NWAVES + w];
+  for (int c = 0; c < NCOMP; ++c) {
+    const int lo = chunk_lo(n, c), hi = chunk_lo(n, c + 1);
+    if (lo < hi && lo <= last && first < hi) s += L.part[r * NCOMP + c];
   }
   return s;
 }
 
-// Run a GEMV tile in row blocks that fit the LDS partial area; `epi(r0, nr, C)` consumes
-// block [r0, r0 + nr) through gemv_row_total before the next block overwrites the partials.
-template <typename Epi>
-__device__ inline void gemv_rows(Ctx& c, const TileDesc& t, int rows, Epi&& epi) {
-  const int block = (c.a->lds_part_floats / NWAVES) & ~1;
-  const int C = t.kpad / CHUNK_COLS;
-  for (int r0 = 0; r0 < rows; r0 += block) {
-    const int nr = min(block, rows - r0);
-    gemv_tile(c, t.woff + (int64_t)r0 * t.kpad * 2, t.kpad, nr);
-    epi(r0, nr, C);
-    __syncthreads();
+// ---------------------------------------------------------------------------
+// control wave: prologues
+// ---------------------------------------------------------------------------
+
+// Coherent copy of n floats (n % 4 == 0) from a scratch vector into LDS, zero-padded to npad;
+// loads are issued in batches of 16 per lane before any is consumed.
+__device__ void cw_load_vec(float* dst, const float* src, int n, int npad, int lane) {
+  constexpr int B = 16;
+  const __amdgpu_buffer_rsrc_t r = rsrc(src);
+  COMPILER_FENCE();
+  for (int base = 0; base < npad; base += B * 256) {
+    u32x4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      v[u] = i < n ? cld4(r, (uint32_t)i * 4) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      if (i < npad) *reinterpret_cast<f32x4*>(dst + i) = as_f32x4(v[u]);
+    }
+  }
+  COMPILER_FENCE();
+}
+
+// RMSNorm prologue with the scale folded out: vec[i] = src[i] * gain[i] (i < n), vec[n..npad) = 0,
+// and the return value rs = 1 / sqrt(mean(src^2) + eps) multiplies the GEMV results instead
+// (W (rs x * g) = rs W (x * g)).  src is an FP32 device-coherent vector or a BF16 embedding
+// row; the source and gain loads of a batch are issued together.
+__device__ float cw_norm(const Lds& L, int lane, const float* src_f32, const uint16_t* src_bf16, const uint16_t* gain,
+                         int n, int npad, float eps) {
+  constexpr int B = 8;
+  const __amdgpu_buffer_rsrc_t r = rsrc(src_f32 ? (const void*)src_f32 : (const void*)src_bf16);
+  float ss = 0.f;
+  COMPILER_FENCE();
+  for (int base = 0; base < npad; base += B * 256) {
+    u32x4 xv[B];
+    uint2 gv[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      xv[u] = u32x4{0u, 0u, 0u, 0u};
+      gv[u] = uint2{0u, 0u};
+      if (i < n) {
+        if (src_f32) {
+          xv[u] = cld4(r, (uint32_t)i * 4);
+        } else {
+          const uint2 e = *reinterpret_cast<const uint2*>(src_bf16 + i);
+          xv[u] = u32x4{e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+        }
+        gv[u] = *reinterpret_cast<const uint2*>(gain + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      const f32x4 x = as_f32x4(xv[u]);
+      ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      const f32x4 v = {x.x * bf16_lo(gv[u].x), x.y * bf16_hi(gv[u].x), x.z * bf16_lo(gv[u].y), x.w * bf16_hi(gv[u].y)};
+      if (i < npad) *reinterpret_cast<f32x4*>(L.vec + i) = v;
+    }
+  }
+  COMPILER_FENCE();
+  const float tot = wave_sum(ss);
+  return 1.0f / sqrtf(tot / (float)n + eps);
+}
+
+// merge the S splits of one query head (Ph -> [S][HD + 2]) for output dim d, fixed split order
+__device__ inline float merge_splits(const float* Ph, int S, int HD, int d) {
+  float mm = -INFINITY;
+  for (int s = 0; s < S; ++s) mm = fmaxf(mm, Ph[s * (HD + 2)]);
+  if (mm == -INFINITY) return 0.f;
+  float ll = 0.f, aa = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* st = Ph + s * (HD + 2);
+    if (st[1] == 0.f) continue;
+    const float f = __builtin_amdgcn_exp2f(st[0] - mm);
+    ll += f * st[1];
+    aa += f * st[2 + d];
+  }
+  return aa / ll;
+}
+
+// attention prologue: q (scaled to the base-2 domain), rounded k and v of the current
+// position into LDS; the split holding the current position writes K/V to the cache.
+template <int HD, int G>
+__device__ void cw_attn_prologue(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp, int pos,
+                                 int64_t L_att) {
+  float* q = L.part;
+  float* kc = q + G * HD;
+  float* vc = kc + HD;
+  const int qbase = g * G * HD;
+  const int kbase = a.n_heads * HD + g * HD;
+  const int vbase = a.n_heads * HD + a.n_kv * HD + g * HD;
+  constexpr int HALF = HD / 2;
+  // raw q (G heads), k, v of this KV group: (G + 2) * HD floats, staged through LDS
+  float* raw = L.vec;
+  cw_load_vec(raw, a.qkv + qbase, G * HD, G * HD, lane);
+  cw_load_vec(raw + G * HD, a.qkv + kbase, HD, HD, lane);
+  cw_load_vec(raw + (G + 1) * HD, a.qkv + vbase, HD, HD, lane);
+  const bool qkn = a.small[layer].q_norm >= 0;
+  // G query heads and the key: optional RMSNorm over HD, then RoPE on pairs (i, i + HD/2)
+  float co = 0.f, si = 0.f;
+  if (lane < HALF) {
+    const float* cs = a.rope + ((int64_t)pos * HALF + lane) * 2;
+    co = cs[0];
+    si = cs[1];
+  }
+  for (int u = 0; u <= G; ++u) {
+    float u0 = 0.f, u1 = 0.f;
+    if (lane < HALF) {
+      u0 = raw[u * HD + lane];
+      u1 = raw[u * HD + lane + HALF];
+    }
+    if (qkn) {
+      const float ss = wave_sum(u0 * u0 + u1 * u1);
+      const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
+      const uint16_t* gn =
+          reinterpret_cast<const uint16_t*>(a.packed + (u < G ? a.small[layer].q_norm : a.small[layer].k_norm));
+      if (lane < HALF) {
+        u0 = u0 * rs * bf16_to_f32(gn[lane]);
+        u1 = u1 * rs * bf16_to_f32(gn[lane + HALF]);
+      }
+    }
+    if (lane < HALF) {
+      const float r0 = u0 * co - u1 * si;
+      const float r1 = u1 * co + u0 * si;
+      if (u < G) {
+        q[u * HD + lane] = r0 * a.qscale;
+        q[u * HD + lane + HALF] = r1 * a.qscale;
+      } else {
+        kc[lane] = bf16_round(r0);
+        kc[lane + HALF] = bf16_round(r1);
+      }
+    }
+  }
+  for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
+  // KV write by the split that holds the current position
+  const int64_t ch = (L_att + a.S - 1) / a.S;
+  const int64_t lo = (int64_t)sp * ch;
+  const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
+  const int64_t cur = L_att - 1;
+  if (lo <= cur && cur < hi && lane < HD / 2) {
+    const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
+    const uint32_t kb = f32_to_bf16_bits(kc[2 * lane]) | (f32_to_bf16_bits(kc[2 * lane + 1]) << 16);
+    const uint32_t vb = f32_to_bf16_bits(vc[2 * lane]) | (f32_to_bf16_bits(vc[2 * lane + 1]) << 16);
+    st_u32(reinterpret_cast<uint32_t*>(a.kv_k + row * HD) + lane, kb);
+    st_u32(reinterpret_cast<uint32_t*>(a.kv_v + row * HD) + lane, vb);
   }
 }
 
 // ---------------------------------------------------------------------------
-// attention: one (KV head, split) tile.  HD = head_dim, G = query heads per KV head.
+// compute wave: one share of an attention split
 // ---------------------------------------------------------------------------
 
+template <int HD>
+__device__ inline void unpack8(const u32x4 w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
 template <int HD, int G>
-__device__ void attention_tile(Ctx& c, const TileDesc& t, int layer) {
-  const KernelArgs& a = *c.a;
-  const int g = t.row0, sp = t.nrows;
-  // LDS layout inside part: q[G][HD] | k[HD] | v[HD] | wave states [NWAVES][G][HD + 2]
-  float* q = c.part;
-  float* kc = q + G * HD;
-  float* vc = kc + HD;
-  float* ws = vc + HD;
-  const float* qkv = a.qkv;
-  const int qbase = g * G * HD;
-  const int kbase = a.n_heads * HD + g * HD;
-  const int vbase = a.n_heads * HD + a.n_kv * HD + g * HD;
-  for (int i = c.tid; i < G * HD; i += BLOCK_THREADS) q[i] = ld_f32(qkv + qbase + i);
-  for (int i = c.tid; i < HD; i += BLOCK_THREADS) {
-    kc[i] = ld_f32(qkv + kbase + i);
-    vc[i] = ld_f32(qkv + vbase + i);
-  }
-  __syncthreads();
-  // q/k RMSNorm (optional) + RoPE: wave h < G handles query head h, wave G the key.
-  if (c.wave <= G) {
-    float* u = c.wave < G ? q + c.wave * HD : kc;
-    constexpr int HALF = HD / 2;
-    float u0 = 0.f, u1 = 0.f;
-    if (c.lane < HALF) {
-      u0 = u[c.lane];
-      u1 = u[c.lane + HALF];
-    }
-    if (a.small[layer].q_norm >= 0) {
-      const float ss = wave_sum(u0 * u0 + u1 * u1);
-      const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
-      const uint16_t* gn =
-          reinterpret_cast<const uint16_t*>(a.packed + (c.wave < G ? a.small[layer].q_norm : a.small[layer].k_norm));
-      if (c.lane < HALF) {
-        u0 = u0 * rs * bf16_to_f32(gn[c.lane]);
-        u1 = u1 * rs * bf16_to_f32(gn[c.lane + HALF]);
-      }
-    }
-    if (c.lane < HALF) {
-      const float* cs = a.rope + ((int64_t)c.pos * HALF + c.lane) * 2;
-      const float co = cs[0], si = cs[1];
-      const float r0 = u0 * co - u1 * si;
-      const float r1 = u1 * co + u0 * si;
-      if (c.wave < G) {
-        u[c.lane] = r0 * a.qscale;
-        u[c.lane + HALF] = r1 * a.qscale;
-      } else {
-        u[c.lane] = bf16_round(r0);
-        u[c.lane + HALF] = bf16_round(r1);
-      }
-    }
-  } else if (c.wave == G + 1) {
-    for (int i = c.lane; i < HD; i += 64) vc[i] = bf16_round(vc[i]);
-  }
-  __syncthreads();
-
-  int64_t lo, hi;
-  {
-    const int64_t L = c.L;
-    const int64_t ch = (L + a.S - 1) / a.S;
-    lo = (int64_t)sp * ch;
-    hi = lo + ch < L ? lo + ch : L;
-    if (lo > L) lo = L;
-  }
-  const int64_t cur = c.L - 1;  // current position: taken from LDS, written to the cache by its split
+__device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int lane, int layer, int g, int sp,
+                                  int64_t L_att) {
+  const float* q = L.part;
+  const float* kc = q + G * HD;
+  const float* vc = kc + HD;
+  float* ws = L.part + G * HD + 2 * HD;
+  const int64_t ch = (L_att + a.S - 1) / a.S;
+  int64_t lo = (int64_t)sp * ch;
+  const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
+  if (lo > L_att) lo = L_att;
+  const int64_t cur = L_att - 1;
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
-  if (lo <= cur && cur < hi && c.tid < HD / 2) {
-    const uint32_t kb = f32_to_bf16_bits(kc[2 * c.tid]) | (f32_to_bf16_bits(kc[2 * c.tid + 1]) << 16);
-    const uint32_t vb = f32_to_bf16_bits(vc[2 * c.tid]) | (f32_to_bf16_bits(vc[2 * c.tid + 1]) << 16);
-    st_u32(reinterpret_cast<uint32_t*>(a.kv_k + (kvrow0 + cur) * HD) + c.tid, kb);
-    st_u32(reinterpret_cast<uint32_t*>(a.kv_v + (kvrow0 + cur) * HD) + c.tid, vb);
-  }
-
-  // per-wave sub-range
-  constexpr int LPP = HD / 8;     // lanes per position
-  constexpr int P = 64 / LPP;     // positions per load
-  const int64_t n = hi - lo;
-  const int64_t wlo = lo + (n * c.wave) / NWAVES, whi = lo + (n * (c.wave + 1)) / NWAVES;
-  const int pp = c.lane / LPP, dseg = c.lane % LPP;
+  constexpr int LPP = HD / 8;  // lanes per position
+  constexpr int P = 64 / LPP;  // positions per load
+  constexpr int U = 4;         // loads in flight per operand
+  const int64_t n = hi > lo ? hi - lo : 0;
+  const int64_t wlo = lo + (n * c) / NCOMP, whi = lo + (n * (c + 1)) / NCOMP;
+  const int pp = lane / LPP, dseg = lane % LPP;
   float qr[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -359,49 +491,60 @@ __device__ void attention_tile(Ctx& c, const TileDesc& t, int layer) {
   }
   const u32x4* kbase_p = reinterpret_cast<const u32x4*>(a.kv_k + kvrow0 * HD);
   const u32x4* vbase_p = reinterpret_cast<const u32x4*>(a.kv_v + kvrow0 * HD);
-  for (int64_t j0 = wlo; j0 < whi; j0 += P) {
-    const int64_t j = j0 + pp;
-    const bool valid = j < whi;
-    float kf[8], vf[8];
-    if (valid && j != cur) {
-      u32x4 kw, vw;
-      if (j < a.pos0) {  // cached before this launch: streaming loads
-        kw = __builtin_nontemporal_load(kbase_p + j * LPP + dseg);
-        vw = __builtin_nontemporal_load(vbase_p + j * LPP + dseg);
-      } else {           // written by another worker during this launch: device-coherent loads
-        kw = ld_u32x4(kbase_p + j * LPP + dseg);
-        vw = ld_u32x4(vbase_p + j * LPP + dseg);
-      }
-      kf[0] = bf16_lo(kw.x); kf[1] = bf16_hi(kw.x); kf[2] = bf16_lo(kw.y); kf[3] = bf16_hi(kw.y);
-      kf[4] = bf16_lo(kw.z); kf[5] = bf16_hi(kw.z); kf[6] = bf16_lo(kw.w); kf[7] = bf16_hi(kw.w);
-      vf[0] = bf16_lo(vw.x); vf[1] = bf16_hi(vw.x); vf[2] = bf16_lo(vw.y); vf[3] = bf16_hi(vw.y);
-      vf[4] = bf16_lo(vw.z); vf[5] = bf16_hi(vw.z); vf[6] = bf16_lo(vw.w); vf[7] = bf16_hi(vw.w);
-    } else {
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kbase_p), rv = rsrc(vbase_p);
+  for (int64_t jb = wlo; jb < whi; jb += U * P) {
+    // issue the loads of U position groups, then consume them
+    u32x4 kw[U], vw[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kf[e] = valid ? kc[dseg * 8 + e] : 0.f;
-        vf[e] = valid ? vc[dseg * 8 + e] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = jb + u * P + pp;
+      kw[u] = u32x4{0u, 0u, 0u, 0u};
+      vw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < whi && j != cur) {
+        if (j < a.pos0) {  // cached before this launch: streaming loads
+          kw[u] = __builtin_nontemporal_load(kbase_p + j * LPP + dseg);
+          vw[u] = __builtin_nontemporal_load(vbase_p + j * LPP + dseg);
+        } else {           // written by another worker during this launch: device-coherent loads
+          kw[u] = cld4(rk, (uint32_t)((j * LPP + dseg) * 16));
+          vw[u] = cld4(rv, (uint32_t)((j * LPP + dseg) * 16));
+        }
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d0 = qr[h][0] * kf[0], d1 = qr[h][1] * kf[1];
-      d0 = fmaf(qr[h][2], kf[2], d0);
-      d1 = fmaf(qr[h][3], kf[3], d1);
-      d0 = fmaf(qr[h][4], kf[4], d0);
-      d1 = fmaf(qr[h][5], kf[5], d1);
-      d0 = fmaf(qr[h][6], kf[6], d0);
-      d1 = fmaf(qr[h][7], kf[7], d1);
-      float s = d0 + d1;
-      s = LPP == 8 ? sum8(s) : sum16(s);
-      if (valid) {
-        const float mn = fmaxf(m[h], s);
-        const float al = __builtin_amdgcn_exp2f(m[h] - mn);
-        const float p = __builtin_amdgcn_exp2f(s - mn);
-        l[h] = l[h] * al + p;
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = jb + u * P + pp;
+      const bool valid = j < whi;
+      float kf[8], vf[8];
+      if (j == cur) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
-        m[h] = mn;
+        for (int e = 0; e < 8; ++e) {
+          kf[e] = kc[dseg * 8 + e];
+          vf[e] = vc[dseg * 8 + e];
+        }
+      } else {
+        unpack8<HD>(kw[u], kf);
+        unpack8<HD>(vw[u], vf);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d0 = qr[h][0] * kf[0], d1 = qr[h][1] * kf[1];
+        d0 = fmaf(qr[h][2], kf[2], d0);
+        d1 = fmaf(qr[h][3], kf[3], d1);
+        d0 = fmaf(qr[h][4], kf[4], d0);
+        d1 = fmaf(qr[h][5], kf[5], d1);
+        d0 = fmaf(qr[h][6], kf[6], d0);
+        d1 = fmaf(qr[h][7], kf[7], d1);
+        float s = d0 + d1;
+        s = LPP == 8 ? sum8(s) : sum16(s);
+        if (valid) {
+          const float mn = fmaxf(m[h], s);
+          const float al = __builtin_amdgcn_exp2f(m[h] - mn);
+          const float p = __builtin_amdgcn_exp2f(s - mn);
+          l[h] = l[h] * al + p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
+          m[h] = mn;
+        }
       }
     }
   }
@@ -425,11 +568,10 @@ __device__ void attention_tile(Ctx& c, const TileDesc& t, int layer) {
       }
     }
   }
-  // this wave's state -> LDS
   if (pp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* st = ws + (c.wave * G + h) * (HD + 2);
+      float* st = ws + (c * G + h) * (HD + 2);
       if (dseg == 0) {
         st[0] = m[h];
         st[1] = l[h];
@@ -438,13 +580,17 @@ __device__ void attention_tile(Ctx& c, const TileDesc& t, int layer) {
       for (int e = 0; e < 8; ++e) st[2 + dseg * 8 + e] = acc[h][e];
     }
   }
-  __syncthreads();
-  // merge the waves in order; thread (h, d) produces the tile's partial
-  if (c.tid < G * HD) {
-    const int h = c.tid / HD, d = c.tid % HD;
+}
+
+// control wave: merge the compute waves' states in order and store the split's partial
+template <int HD, int G>
+__device__ void cw_attn_merge(const KernelArgs& a, const Lds& L, int lane, int g, int sp) {
+  const float* ws = L.part + G * HD + 2 * HD;
+  for (int idx = lane; idx < G * HD; idx += 64) {
+    const int h = idx / HD, d = idx % HD;
     float mm = -INFINITY, ll = 0.f, aa = 0.f;
-    for (int w = 0; w < NWAVES; ++w) {
-      const float* st = ws + (w * G + h) * (HD + 2);
+    for (int c = 0; c < NCOMP; ++c) {
+      const float* st = ws + (c * G + h) * (HD + 2);
       const float m2 = st[0];
       const float mn = fmaxf(mm, m2);
       if (mn == -INFINITY) continue;
@@ -462,282 +608,328 @@ __device__ void attention_tile(Ctx& c, const TileDesc& t, int layer) {
   }
 }
 
-// merge the S splits of one query head (Ph -> [S][HD + 2]) for output dim d, fixed split order
-__device__ inline float merge_splits(const float* Ph, int S, int HD, int d) {
-  float mm = -INFINITY;
-  for (int s = 0; s < S; ++s) mm = fmaxf(mm, Ph[s * (HD + 2)]);
-  if (mm == -INFINITY) return 0.f;
-  float ll = 0.f, aa = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* st = Ph + s * (HD + 2);
-    if (st[1] == 0.f) continue;
-    const float f = __builtin_amdgcn_exp2f(st[0] - mm);
-    ll += f * st[1];
-    aa += f * st[2 + d];
+// LDS-only prologue work shared by all eight wavefronts between barriers P and A:
+// merging the split partials into the o_proj input vector.  wave_index in [0, NWAVES).
+template <int HD>
+__device__ inline void prologue_lds_phase(const KernelArgs& a, const Lds& L, int kind, int wave_index, int lane) {
+  if (kind == KIND_O && a.combine_in_o) {
+    const int nq = a.n_heads * HD;
+    for (int i = wave_index * 64 + lane; i < nq; i += BLOCK_THREADS)
+      L.vec[i] = merge_splits(L.part + (i / HD) * a.S * (HD + 2), a.S, HD, i % HD);
   }
-  return aa / ll;
 }
 
 // ---------------------------------------------------------------------------
-// grid barrier: every worker publishes its generation on its own 64-byte line and
-// wavefront 0 of every worker polls all lines.  A watchdog bounds every wait.
+// grid barrier (control wave): every worker publishes its generation on its own
+// 64-byte line and polls all lines.  A watchdog bounds every wait.
 // ---------------------------------------------------------------------------
 
-__device__ void grid_barrier(Ctx& c, uint32_t gen) {
-  const KernelArgs& a = *c.a;
-  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores are complete
-  __syncthreads();
-  __shared__ int s_abort;
-  if (c.wave == 0) {
-    uint32_t* arrive = a.sync + SYNC_ARRIVE_BASE;
-    if (c.lane == 0) st_u32(arrive + c.bid * SYNC_LINE_WORDS, gen);
-    uint32_t spins = 0;
-    bool ab = false;
-    for (;;) {
-      bool ok = true;
-      for (int w = c.lane; w < a.W; w += 64) ok &= (int32_t)(ld_u32(arrive + w * SYNC_LINE_WORDS) - gen) >= 0;
-      if (__all(ok)) break;
-      if ((++spins & 63) == 0) {
-        if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) {
-          ab = true;
-          break;
+__device__ bool cw_grid_barrier(const KernelArgs& a, int bid, int lane, uint32_t gen) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+  uint32_t* arrive = a.sync + SYNC_ARRIVE_BASE;
+  if (lane == 0) st_u32(arrive + bid * SYNC_LINE_WORDS, gen);
+  uint32_t spins = 0;
+  for (;;) {
+    bool ok = true;
+    for (int w = lane; w < a.W; w += 64) ok &= (int32_t)(ld_u32(arrive + w * SYNC_LINE_WORDS) - gen) >= 0;
+    if (__all(ok)) return false;
+    if ((++spins & 63) == 0) {
+      if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) return true;
+      if (spins > a.spin_limit) {
+        if (lane == 0) {
+          st_u32(a.sync + SYNC_STATUS_WORD, 1u);
+          st_u32(a.sync + SYNC_ABORT_WORD, 1u);
         }
-        if (spins > a.spin_limit) {
-          if (c.lane == 0) {
-            st_u32(a.sync + SYNC_STATUS_WORD, 1u);
-            st_u32(a.sync + SYNC_ABORT_WORD, 1u);
-          }
-          ab = true;
-          break;
-        }
+        return true;
       }
     }
-    if (c.lane == 0) s_abort = ab ? 1 : 0;
   }
-  __syncthreads();
-  c.aborted = s_abort != 0;
 }
 
 // ---------------------------------------------------------------------------
-// the persistent kernel
+// control wave main loop
 // ---------------------------------------------------------------------------
 
 template <int HD, int G>
-__global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
-  extern __shared__ float lds[];
-  Ctx c;
-  c.a = &args;
-  const KernelArgs& a = args;
-  c.vec = lds;
-  c.part = lds + a.lds_vec_floats;
-  c.small = c.part + a.lds_part_floats;
-  c.bid = blockIdx.x;
-  c.tid = threadIdx.x;
-  c.wave = c.tid >> 6;
-  c.lane = c.tid & 63;
-  c.aborted = false;
-  c.tok = a.token0;
+__device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
+  int* smi = reinterpret_cast<int*>(L.small);
   uint32_t gen = 0;
+  int tok = a.token0;
+  bool aborted = false;
   const int H = a.H;
-  for (int step = 0; step < a.n_steps && !c.aborted; ++step) {
-    c.step = step;
-    c.pos = a.pos0 + step;
-    c.L = c.pos + 1;
-    const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)c.tok * a.embed_stride);
+  for (int step = 0; step < a.n_steps && !aborted; ++step) {
+    const int pos = a.pos0 + step;
+    const int64_t L_att = (int64_t)pos + 1;
+    const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)tok * a.embed_stride);
     if (a.poison) {
       const float nan = __uint_as_float(0x7fc00000u);
-      const int64_t gid = (int64_t)c.bid * BLOCK_THREADS + c.tid, gsz = (int64_t)a.W * BLOCK_THREADS;
+      const int64_t gid = (int64_t)bid * 64 + lane, gsz = (int64_t)a.W * 64;
       for (int64_t i = gid; i < a.qkv_rows; i += gsz) st_f32(a.qkv + i, nan);
-      for (int64_t i = gid; i < (int64_t)a.n_heads * a.S * (a.head_dim + 2); i += gsz) st_f32(a.part + i, nan);
-      for (int64_t i = gid; i < (int64_t)a.n_heads * a.head_dim; i += gsz) st_f32(a.attn + i, nan);
+      for (int64_t i = gid; i < (int64_t)a.n_heads * a.S * (HD + 2); i += gsz) st_f32(a.part + i, nan);
+      for (int64_t i = gid; i < (int64_t)a.n_heads * HD; i += gsz) st_f32(a.attn + i, nan);
       for (int64_t i = gid; i < a.F; i += gsz) st_f32(a.act + i, nan);
-      grid_barrier(c, ++gen);
-      if (c.aborted) break;
+      aborted = cw_grid_barrier(a, bid, lane, ++gen);
+      if (aborted) break;
     }
+    float lm_best = -INFINITY;
+    int lm_idx = 0x7fffffff;
     for (int wv = 0; wv < a.n_waves; ++wv) {
-      const WaveDesc wd = a.waves[wv];
-      const TileDesc t = a.tiles[(int64_t)wv * a.W + c.bid];
-      uint64_t t0 = 0, t1 = 0;
-      if (a.trace && c.tid == 0) t0 = wall_clock64();
-      const int layer = wd.layer;
+      const TileDesc t = a.tiles[(int64_t)wv * a.W + bid];
+      const int layer = a.waves[wv].layer;
+      uint64_t t0 = 0;
+      if (a.trace) t0 = wall_clock64();
+      // ---- prologue (global loads by the control wave) ----
+      float rs = 1.0f;  // RMSNorm scale folded out of the input vector, applied to the GEMV results
       switch (t.kind) {
-        case KIND_QKV: {
-          const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].attn_norm);
-          norm_prologue(c, layer == 0 ? nullptr : a.x, layer == 0 ? erow : nullptr, gain, H, t.kpad);
-          gemv_rows(c, t, t.nrows, [&](int r0, int nr, int C) {
-            for (int r = c.tid; r < nr; r += BLOCK_THREADS) st_f32(a.qkv + t.row0 + r0 + r, gemv_row_total(c, nr, C, r));
-          });
+        case KIND_QKV:
+          rs = cw_norm(L, lane, layer == 0 ? nullptr : a.x, layer == 0 ? erow : nullptr,
+                       reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].attn_norm), H, t.kpad, a.eps);
           break;
-        }
-        case KIND_ATTN:
-          attention_tile<HD, G>(c, t, layer);
+        case KIND_GU:
+          rs = cw_norm(L, lane, a.x, nullptr, reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].mlp_norm), H,
+                       t.kpad, a.eps);
           break;
-        case KIND_COMBINE: {
-          if (c.tid < HD) {
-            // read the S partials of head t.row0 through the coherent path into LDS, then merge
-            float* P = c.part;
-            for (int i = c.tid; i < a.S * (HD + 2); i += HD) P[i] = ld_f32(a.part + (int64_t)t.row0 * a.S * (HD + 2) + i);
-          }
-          __syncthreads();
-          if (c.tid < HD) st_f32(a.attn + (int64_t)t.row0 * HD + c.tid, merge_splits(c.part, a.S, HD, c.tid));
+        case KIND_LM:
+          rs = cw_norm(L, lane, a.x, nullptr, reinterpret_cast<const uint16_t*>(a.packed + a.final_norm_off), H, t.kpad,
+                       a.eps);
           break;
-        }
         case KIND_O: {
           const int nq = a.n_heads * HD;
           if (a.combine_in_o) {
-            const int np = a.n_heads * a.S * (HD + 2);
-            for (int i = c.tid; i < np; i += BLOCK_THREADS) c.part[i] = ld_f32(a.part + i);
-            __syncthreads();
-            for (int i = c.tid; i < nq; i += BLOCK_THREADS)
-              c.vec[i] = merge_splits(c.part + (i / HD) * a.S * (HD + 2), a.S, HD, i % HD);
+            // stage all split partials; all wavefronts merge them after barrier P
+            const int np = a.n_heads * a.S * (HD + 2);  // even
+            cw_load_vec(L.part, a.part, np & ~3, np & ~3, lane);
+            for (int i = (np & ~3) + lane; i < np; i += 64) L.part[i] = ld_f32(a.part + i);
+            for (int i = nq + lane; i < t.kpad; i += 64) L.vec[i] = 0.f;
           } else {
-            for (int i = c.tid; i < nq; i += BLOCK_THREADS) c.vec[i] = ld_f32(a.attn + i);
-          }
-          for (int i = nq + c.tid; i < t.kpad; i += BLOCK_THREADS) c.vec[i] = 0.f;
-          __syncthreads();
-          gemv_rows(c, t, t.nrows, [&](int r0, int nr, int C) {
-            for (int r = c.tid; r < nr; r += BLOCK_THREADS) {
-              const int j = t.row0 + r0 + r;
-              const float old = layer == 0 ? bf16_to_f32(erow[j]) : ld_f32(a.x + j);
-              st_f32(a.x + j, old + gemv_row_total(c, nr, C, r));
-            }
-          });
-          break;
-        }
-        case KIND_GU: {
-          const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].mlp_norm);
-          norm_prologue(c, a.x, nullptr, gain, H, t.kpad);
-          // rows are interleaved gate/up pairs
-          gemv_rows(c, t, 2 * t.nrows, [&](int r0, int nr, int C) {
-            for (int p = c.tid; p < nr / 2; p += BLOCK_THREADS) {
-              const float gt = gemv_row_total(c, nr, C, 2 * p);
-              const float up = gemv_row_total(c, nr, C, 2 * p + 1);
-              const float si = gt / (1.0f + __expf(-gt));
-              st_f32(a.act + t.row0 + r0 / 2 + p, si * up);
-            }
-          });
-          break;
-        }
-        case KIND_DOWN: {
-          for (int i = c.tid; i < t.kpad; i += BLOCK_THREADS) c.vec[i] = i < a.F ? ld_f32(a.act + i) : 0.f;
-          __syncthreads();
-          gemv_rows(c, t, t.nrows, [&](int r0, int nr, int C) {
-            for (int r = c.tid; r < nr; r += BLOCK_THREADS) {
-              const int j = t.row0 + r0 + r;
-              const float nx = ld_f32(a.x + j) + gemv_row_total(c, nr, C, r);
-              st_f32(a.x + j, nx);
-              if (a.dbg_hidden) a.dbg_hidden[((int64_t)c.step * a.n_layers + layer) * H + j] = nx;
-            }
-          });
-          break;
-        }
-        case KIND_LM: {
-          const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + a.final_norm_off);
-          norm_prologue(c, a.x, nullptr, gain, H, t.kpad);
-          float best = -INFINITY;
-          int bidx = 0x7fffffff;
-          gemv_rows(c, t, t.nrows, [&](int r0, int nr, int C) {
-            for (int r = c.tid; r < nr; r += BLOCK_THREADS) {
-              const float v = gemv_row_total(c, nr, C, r);
-              const int idx = t.row0 + r0 + r;
-              if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)c.step * a.V + idx);
-              if (v > best) {  // each thread visits its rows in increasing order: first maximum kept
-                best = v;
-                bidx = idx;
-              }
-            }
-          });
-          // block argmax (greater value, then lower index)
-          for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(best, off);
-            const int oi = __shfl_xor(bidx, off);
-            if (ov > best || (ov == best && oi < bidx)) {
-              best = ov;
-              bidx = oi;
-            }
-          }
-          __syncthreads();
-          if (c.lane == 0) {
-            c.small[2 * c.wave] = best;
-            reinterpret_cast<int*>(c.small)[2 * c.wave + 1] = bidx;
-          }
-          __syncthreads();
-          if (c.tid == 0) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int w = 0; w < NWAVES; ++w) {
-              const float v = c.small[2 * w];
-              const int ix = reinterpret_cast<int*>(c.small)[2 * w + 1];
-              if (v > bv || (v == bv && ix < bi)) {
-                bv = v;
-                bi = ix;
-              }
-            }
-            st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + c.bid,
-                   (uint64_t)__float_as_uint(bv) | ((uint64_t)(uint32_t)bi << 32));
+            cw_load_vec(L.vec, a.attn, nq, t.kpad, lane);
           }
           break;
         }
+        case KIND_DOWN:
+          cw_load_vec(L.vec, a.act, a.F, t.kpad, lane);
+          break;
+        case KIND_ATTN:
+          cw_attn_prologue<HD, G>(a, L, lane, layer, t.row0, t.nrows, pos, L_att);
+          break;
         default:
-          if (wd.kind == KIND_LM && c.tid == 0)
-            st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + c.bid,
-                   (uint64_t)__float_as_uint(-INFINITY) | ((uint64_t)0x7fffffffu << 32));
           break;
       }
-      if (a.trace && c.tid == 0) t1 = wall_clock64();
-      grid_barrier(c, ++gen);
-      if (a.trace && c.tid == 0) {
-        uint64_t* tr = a.trace + (((int64_t)c.step * a.n_waves + wv) * a.W + c.bid) * 3;
+      uint64_t t_pro = 0, t_cmp = 0;
+      if (a.trace) t_pro = wall_clock64();
+      if (lane == 0) {
+        smi[SM_KIND] = t.kind;
+        smi[SM_ROW0] = t.row0;
+        smi[SM_NROWS] = t.nrows;
+        smi[SM_LAYER] = layer;
+        smi[SM_C] = t.kpad / CHUNK_COLS;
+        smi[SM_POS] = pos;
+      }
+      __syncthreads();  // P: global inputs staged in LDS
+      prologue_lds_phase<HD>(a, L, t.kind, 0, lane);
+      __syncthreads();  // A: inputs ready
+      // ---- compute waves run; epilogues ----
+      if (is_gemv(t.kind)) {
+        const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
+        const int C = t.kpad / CHUNK_COLS;
+        for (int r0 = 0; r0 < rows; r0 += block_rows) {
+          const int nr = min(block_rows, rows - r0);
+          __syncthreads();  // B: partials of this block ready
+          if (a.trace && r0 == 0) t_cmp = wall_clock64();
+          switch (t.kind) {
+            case KIND_QKV:
+              for (int r = lane; r < nr; r += 64) st_f32(a.qkv + t.row0 + r0 + r, rs * row_total(L, nr, C, r));
+              break;
+            case KIND_O:
+              for (int r = lane; r < nr; r += 64) {
+                const int j = t.row0 + r0 + r;
+                const float old = layer == 0 ? bf16_to_f32(erow[j]) : ld_f32(a.x + j);
+                st_f32(a.x + j, old + row_total(L, nr, C, r));
+              }
+              break;
+            case KIND_GU:  // interleaved gate/up rows
+              for (int p = lane; p < nr / 2; p += 64) {
+                const float gt = rs * row_total(L, nr, C, 2 * p);
+                const float up = rs * row_total(L, nr, C, 2 * p + 1);
+                st_f32(a.act + t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up);
+              }
+              break;
+            case KIND_DOWN:
+              for (int r = lane; r < nr; r += 64) {
+                const int j = t.row0 + r0 + r;
+                const float nx = ld_f32(a.x + j) + row_total(L, nr, C, r);
+                st_f32(a.x + j, nx);
+                if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = nx;
+              }
+              break;
+            case KIND_LM:
+              for (int r = lane; r < nr; r += 64) {
+                const float v = rs * row_total(L, nr, C, r);
+                const int idx = t.row0 + r0 + r;
+                if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
+                if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
+                  lm_best = v;
+                  lm_idx = idx;
+                }
+              }
+              break;
+          }
+          if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
+        }
+      } else {
+        __syncthreads();  // B
+        if (a.trace) t_cmp = wall_clock64();
+        if (t.kind == KIND_ATTN) {
+          cw_attn_merge<HD, G>(a, L, lane, t.row0, t.nrows);
+        } else if (t.kind == KIND_COMBINE) {
+          float* P = L.part;
+          const int np = a.S * (HD + 2);
+          for (int i = lane; i < np; i += 64) P[i] = ld_f32(a.part + (int64_t)t.row0 * np + i);
+          for (int d = lane; d < HD; d += 64) st_f32(a.attn + (int64_t)t.row0 * HD + d, merge_splits(P, a.S, HD, d));
+        }
+      }
+      if (a.waves[wv].kind == KIND_LM) {
+        // worker partial (max, lowest index); also written by workers without vocabulary rows
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float ov = __shfl_xor(lm_best, off);
+          const int oi = __shfl_xor(lm_idx, off);
+          if (ov > lm_best || (ov == lm_best && oi < lm_idx)) {
+            lm_best = ov;
+            lm_idx = oi;
+          }
+        }
+        if (lane == 0)
+          st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
+                 (uint64_t)__float_as_uint(lm_best) | ((uint64_t)(uint32_t)lm_idx << 32));
+      }
+      uint64_t t1 = 0;
+      if (a.trace) t1 = wall_clock64();
+      aborted = cw_grid_barrier(a, bid, lane, ++gen);
+      if (a.trace && lane == 0) {
+        uint64_t* tr = a.trace + (((int64_t)step * a.n_waves + wv) * a.W + bid) * TRACE_WORDS;
         tr[0] = t0;
-        tr[1] = t1;
-        tr[2] = wall_clock64();
+        tr[1] = t_pro;
+        tr[2] = t_cmp;
+        tr[3] = t1;
+        tr[4] = wall_clock64();
       }
-      if (c.aborted) break;
+      if (aborted) break;
     }
-    if (c.aborted) break;
+    if (aborted) break;
     // next token: argmax over all workers' partials, in worker order
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
     {
-      float best = -INFINITY;
-      int bidx = 0x7fffffff;
-      for (int w = c.tid; w < a.W; w += BLOCK_THREADS) {
-        const uint64_t pv = ld_u64(reinterpret_cast<const uint64_t*>(a.lmpart) + w);
-        const float v = __uint_as_float((uint32_t)pv);
-        const int ix = (int)(uint32_t)(pv >> 32);
-        if (v > best || (v == best && ix < bidx)) {
-          best = v;
-          bidx = ix;
+      const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
+      COMPILER_FENCE();
+      for (int base = 0; base < a.W; base += 4 * 128) {  // 2 partials per 16-byte load, 4 loads in flight
+        u32x4 pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int w = base + u * 128 + lane * 2;
+          pv[u] = w < a.W ? cld4(r, (uint32_t)w * 8) : u32x4{0xff800000u, 0x7fffffffu, 0xff800000u, 0x7fffffffu};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int w = base + u * 128 + lane * 2;
+          for (int e = 0; e < 2; ++e) {
+            const float v = __uint_as_float(e ? pv[u].z : pv[u].x);
+            const int ix = (int)(e ? pv[u].w : pv[u].y);
+            if (w + e < a.W && (v > best || (v == best && ix < bidx))) {
+              best = v;
+              bidx = ix;
+            }
+          }
         }
       }
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bidx, off);
-        if (ov > best || (ov == best && oi < bidx)) {
-          best = ov;
-          bidx = oi;
-        }
+      COMPILER_FENCE();
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bidx, off);
+      if (ov > best || (ov == best && oi < bidx)) {
+        best = ov;
+        bidx = oi;
       }
-      __syncthreads();
-      if (c.lane == 0) {
-        c.small[2 * c.wave] = best;
-        reinterpret_cast<int*>(c.small)[2 * c.wave + 1] = bidx;
+    }
+    if (bidx < 0 || bidx >= a.V) bidx = 0;  // only reachable with non-finite logits
+    tok = bidx;
+    if (bid == 0 && lane == 0) a.out_tokens[step] = bidx;
+  }
+  // release the compute waves: one more barrier (their P) with the done flag set
+  if (lane == 0) smi[SM_DONE] = 1;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// compute wave main loop
+// ---------------------------------------------------------------------------
+
+template <int HD, int G>
+__device__ void compute_loop(const KernelArgs& a, const Lds& L, int c, int lane, int block_rows) {
+  const volatile int* smi = reinterpret_cast<const volatile int*>(L.small);
+  Prefetcher pf;
+  pf.ring_addr = __builtin_amdgcn_readfirstlane(L.ring_addr + (uint32_t)(c * RING_SLOTS * CHUNK_BYTES));
+  pf.packed = a.packed;
+  pf.lane = lane;
+  pf.cu.k = -1;
+  pf.cu.r0 = 0;
+  cursor_next(pf.cu, L.segs, a.n_waves, block_rows, c);
+  for (int s = 0; s < RING_SLOTS - 1; ++s) pf.issue(L.segs, a.n_waves, block_rows, c, s);
+  pf.slot = 0;
+  pf.free_slot = RING_SLOTS - 1;
+  for (;;) {  // one iteration per wave of every step, until the control wave raises the done flag
+    __syncthreads();  // P
+    if (smi[SM_DONE]) break;
+    prologue_lds_phase<HD>(a, L, smi[SM_KIND], c + 1, lane);
+    __syncthreads();  // A
+    const int kind = smi[SM_KIND];
+    const int row0 = smi[SM_ROW0];
+    const int nrows = smi[SM_NROWS];
+    const int layer = smi[SM_LAYER];
+    const int C = smi[SM_C];
+    const int pos = smi[SM_POS];
+    if (is_gemv(kind)) {
+      const int rows = kind == KIND_GU ? 2 * nrows : nrows;
+      for (int r0 = 0; r0 < rows; r0 += block_rows) {
+        const int nr = min(block_rows, rows - r0);
+        compute_gemv_block(pf, L, a.n_waves, block_rows, c, lane, C, nr);
+        __syncthreads();                              // B
+        if (r0 + block_rows < rows) __syncthreads();  // C
       }
-      __syncthreads();
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int w = 0; w < NWAVES; ++w) {
-        const float v = c.small[2 * w];
-        const int ix = reinterpret_cast<int*>(c.small)[2 * w + 1];
-        if (v > bv || (v == bv && ix < bi)) {
-          bv = v;
-          bi = ix;
-        }
-      }
-      __syncthreads();
-      if (bi < 0 || bi >= a.V) bi = 0;  // only reachable with non-finite logits
-      c.tok = bi;
-      if (c.bid == 0 && c.tid == 0) a.out_tokens[step] = bi;
+    } else {
+      if (kind == KIND_ATTN) compute_attention<HD, G>(a, L, c, lane, layer, row0, nrows, (int64_t)pos + 1);
+      __syncthreads();  // B
     }
   }
+  vm_drain();
+}
+
+template <int HD, int G>
+__global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  const KernelArgs& a = args;
+  Lds L;
+  L.ring = lds_raw;
+  L.ring_addr = (uint32_t)(uintptr_t)(LDS_AS unsigned char*)lds_raw;
+  L.vec = reinterpret_cast<float*>(lds_raw + RING_BYTES);
+  L.part = L.vec + a.lds_vec_floats;
+  L.small = L.part + a.lds_part_floats;
+  L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, bid = blockIdx.x;
+  for (int k = tid; k < a.n_waves; k += BLOCK_THREADS) {
+    const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
+    SegDesc s;
+    s.woff = t.woff;
+    s.chunks_per_row = t.kpad / CHUNK_COLS;
+    s.rows = is_gemv(t.kind) ? (t.kind == KIND_GU ? 2 * t.nrows : t.nrows) : 0;
+    L.segs[k] = s;
+  }
+  if (tid == 0) reinterpret_cast<int*>(L.small)[SM_DONE] = 0;
+  __syncthreads();
+  const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
+  if (wave == 0) control_loop<HD, G>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G>(a, L, wave - 1, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------

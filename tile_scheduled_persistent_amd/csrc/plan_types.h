@@ -27,6 +27,17 @@ constexpr int CHUNK_COLS = 512;
 constexpr int CHUNK_BYTES = 1024;
 constexpr int BLOCK_THREADS = 512;
 constexpr int NWAVES = BLOCK_THREADS / 64;
+// Wavefront 0 of every workgroup is the control wave (prologues, epilogues, stores, grid
+// barrier); wavefronts 1..NCOMP stream weights through per-wave LDS rings and compute.
+constexpr int NCOMP = NWAVES - 1;
+constexpr int RING_SLOTS = 12;                              // 1 KB chunks per compute wave
+constexpr int RING_BYTES = NCOMP * RING_SLOTS * CHUNK_BYTES;
+constexpr int SMALL_FLOATS = 1024;                          // LDS scratch for reductions / broadcasts
+struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the weight prefetcher)
+  int64_t woff;
+  int32_t chunks_per_row;
+  int32_t rows;  // weight rows of the tile (0: no GEMV tile in this wave)
+};
 constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
 constexpr int MAX_BLOCK_ROWS = 640;  // GEMV rows staged per LDS block
 
@@ -57,6 +68,10 @@ constexpr int SYNC_LINE_WORDS = 16;
 constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = barrier watchdog)
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
 constexpr int SYNC_ARRIVE_BASE = 64;     // arrive[w] at SYNC_ARRIVE_BASE + w * SYNC_LINE_WORDS
+
+// In-kernel trace record per (step, wave, worker): wave start, input staged, compute done,
+// barrier arrival, barrier release (100 MHz wall clock).
+constexpr int TRACE_WORDS = 5;
 
 inline int64_t sync_words(int W) { return SYNC_ARRIVE_BASE + (int64_t)W * SYNC_LINE_WORDS; }
 

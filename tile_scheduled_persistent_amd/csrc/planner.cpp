@@ -108,6 +108,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (n_workers < 1) return fail(err, TILES_E_CONFIG, "n_workers must be >= 1");
   if (n_workers < s.n_heads || n_workers < s.n_kv) return fail(err, TILES_E_CONFIG, "fewer workers than attention heads");
   if (s.n_heads * s.hd > 65536 || s.H > 65536 || s.F > 65536) return fail(err, TILES_E_CONFIG, "dimension too large");
+  if (s.H % 4 != 0 || s.F % 4 != 0) return fail(err, TILES_E_CONFIG, "hidden and ffn must be multiples of 4");
   p.W = n_workers;
   const int32_t W = n_workers;
   s.qkv_rows = (s.n_heads + 2 * s.n_kv) * s.hd;
@@ -285,18 +286,19 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.max_over_mean = worst;
 
   // ---- LDS sizing ----
-  int32_t vec = std::max({s.Hpad, s.Qpad, s.Fpad});
-  // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NWAVES] in LDS)
+  // vec: GEMV input vector, or the raw q/k/v of an attention tile
+  int32_t vec = std::max({s.Hpad, s.Qpad, s.Fpad, (s.G + 2) * s.hd});
+  // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS)
   int32_t part = 0;
-  for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NWAVES);
-  // attention tile: q[G][hd], k[hd], v[hd] and the wave states [NWAVES][G][hd + 2]
-  part = std::max(part, s.G * s.hd + 2 * s.hd + NWAVES * s.G * (s.hd + 2));
+  for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
+  // attention tile: q[G][hd], k[hd], v[hd] and the compute-wave states [NCOMP][G][hd + 2]
+  part = std::max(part, s.G * s.hd + 2 * s.hd + NCOMP * s.G * (s.hd + 2));
   part = std::max(part, p.S * (s.hd + 2));                                  // one head's splits (combine tile)
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * (s.hd + 2));  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
-  const int32_t small_bytes = 4096;
-  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats) * 4 + small_bytes;
+  p.lds_bytes = RING_BYTES + (p.lds_vec_floats + p.lds_part_floats + SMALL_FLOATS) * 4 +
+                (int32_t)round_up((int64_t)p.waves.size() * (int64_t)sizeof(SegDesc), 256);
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
   if (p.lds_bytes > 160 * 1024) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
@@ -474,7 +476,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
   }
 
   // LDS capacity for every wave's staging
-  if (p.lds_part_floats / NWAVES < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
+  if (p.lds_part_floats / NCOMP < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
   if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 2) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");

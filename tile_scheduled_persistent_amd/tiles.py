@@ -243,7 +243,7 @@ class Plan:
         return out
 
     def read_debug(self, hidden: bool = True, trace: bool = False):
-        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, 3] uint64 or None)."""
+        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, 5] uint64 or None)."""
         info = self.info()
         n = ctypes.c_int32(0)
         _check(lib().tiles_read_debug(self._h, None, None, ctypes.byref(n)))
@@ -253,7 +253,7 @@ class Plan:
             hid = np.zeros((n.value, self.model.n_layers, self.model.hidden), dtype=np.float32)
             hp = hid.ctypes.data
         if trace:
-            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, 3), dtype=np.uint64)
+            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, 5), dtype=np.uint64)
             tp = tr.ctypes.data
         _check(lib().tiles_read_debug(self._h, hp, tp, None))
         return hid, tr
