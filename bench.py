@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
+    ap.add_argument("--barrier-gather", action="store_true", help="gather/release grid barrier")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed launches, run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -102,7 +105,8 @@ def main():
     k0, v0 = synth.make_kv(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, device=dev)
     token = synth.make_tokens(m, 1)[0]
     stream = torch.cuda.current_stream()
-    plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
+    base_flags = tiles.TILES_BARRIER_GATHER if args.barrier_gather else 0
+    plan = tiles.Plan(m, w, wl.capacity, flags=base_flags, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
                       stream=stream)
     info = plan.info()
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
@@ -133,6 +137,13 @@ def main():
     if plan.status() != tiles.TILES_OK:
         raise RuntimeError(tiles.last_error())
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if args.calib_copy_mb:
+        # a plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of this kernel calibrate the counters
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     avg_ms = float(np.mean(launch_ms))
 
     bpt = wl.bytes_per_token()
@@ -159,6 +170,7 @@ def main():
         "launch_ms": {"min": round(min(launch_ms), 4), "median": round(float(np.median(launch_ms)), 4),
                       "max": round(max(launch_ms), 4)},
         "plan": {"waves_per_token": info.waves_per_step, "kv_splits": info.kv_splits,
+                 "barrier": "gather/release" if args.barrier_gather else "all-poll",
                  "combine": "o_proj prologue" if info.combine_mode == 1 else "own wave",
                  "workers": info.n_workers, "block_threads": info.block_threads},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -186,7 +198,8 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
 
     from tile_scheduled_persistent_amd import tiles
 
-    plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits,
+    plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE | (tiles.TILES_BARRIER_GATHER if args.barrier_gather else 0),
+                      kv_splits=args.kv_splits,
                       combine_mode=args.combine_mode)
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")

@@ -51,6 +51,8 @@ extern "C" {
 #define TILES_DEBUG_HIDDEN 0x1u /* record the residual stream after every layer of every step */
 #define TILES_TRACE 0x2u        /* record per-worker, per-wave timestamps (100 MHz wall clock) */
 #define TILES_POISON 0x4u       /* NaN-fill the per-step scratch at every step start */
+#define TILES_BARRIER_GATHER 0x8u /* grid barrier: worker 0 gathers all arrivals and releases each worker
+                                     (instead of every worker polling every arrival) */
 
 /* ---- model + plan options ---------------------------------------------- */
 typedef struct tiles_config {
@@ -66,7 +68,7 @@ typedef struct tiles_config {
   int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
   int32_t tie_embeddings; /* 1: the LM head is the embedding matrix */
   int32_t max_positions;  /* largest KV length (cached + decoded) the plan supports */
-  uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON */
+  uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON | TILES_BARRIER_GATHER */
   int32_t kv_splits;      /* split-KV count per KV head; 0 lets the planner choose */
   int32_t combine_mode;   /* 0 planner choice, 1 combine splits in the o_proj prologue, 2 own wave */
   int32_t n_workers;      /* 0 = one workgroup per compute unit (required on the GPU) */

@@ -24,6 +24,7 @@
 
 namespace tiles {
 const void* worker_kernel(int head_dim, int group);
+hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 }
 
 using namespace tiles;
@@ -182,18 +183,39 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   // packed weights
   TRY(hipMalloc(&p->packed, hp.packed_bytes));
   TRY(hipMemsetAsync(p->packed, 0, hp.packed_bytes, p->stream));
-  const hipMemcpyKind kind = w->on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-  for (const CopySeg& c : hp.copies) {
-    const uint8_t* src = static_cast<const uint8_t*>(src_ptr(w, c.tensor, c.layer));
-    if (!src) {
-      release(p);
-      return set_err(TILES_E_ARG, "missing weight tensor for packing");
+  if (w->on_device) {
+    // device-resident sources: one packing kernel for every segment
+    std::vector<PackSeg> segs;
+    segs.reserve(hp.copies.size());
+    for (const CopySeg& c : hp.copies) {
+      const uint8_t* src = static_cast<const uint8_t*>(src_ptr(w, c.tensor, c.layer));
+      if (!src) {
+        release(p);
+        return set_err(TILES_E_ARG, "missing weight tensor for packing");
+      }
+      segs.push_back({src + c.src_row * c.cols * 2, c.cols * 2, c.dst_off, c.dst_pitch, c.nrows, c.cols * 2});
     }
-    src += c.src_row * c.cols * 2;
-    if (c.dst_pitch == c.cols * 2) {
-      TRY(hipMemcpyAsync(p->packed + c.dst_off, src, c.nrows * c.cols * 2, kind, p->stream));
-    } else {
-      TRY(hipMemcpy2DAsync(p->packed + c.dst_off, c.dst_pitch, src, c.cols * 2, c.cols * 2, c.nrows, kind, p->stream));
+    PackSeg* d_segs = nullptr;
+    TRY(hipMalloc(&d_segs, segs.size() * sizeof(PackSeg)));
+    hipError_t e1 = hipMemcpyAsync(d_segs, segs.data(), segs.size() * sizeof(PackSeg), hipMemcpyHostToDevice, p->stream);
+    if (e1 == hipSuccess) e1 = launch_pack(d_segs, (int)segs.size(), p->packed, p->stream);
+    if (e1 == hipSuccess) e1 = hipStreamSynchronize(p->stream);
+    (void)hipFree(d_segs);
+    if (e1 != hipSuccess) {
+      std::string m = std::string("weight packing: ") + hipGetErrorString(e1);
+      release(p);
+      return set_err(TILES_E_HIP, m);
+    }
+  } else {
+    for (const CopySeg& c : hp.copies) {
+      const uint8_t* src = static_cast<const uint8_t*>(src_ptr(w, c.tensor, c.layer));
+      if (!src) {
+        release(p);
+        return set_err(TILES_E_ARG, "missing weight tensor for packing");
+      }
+      src += c.src_row * c.cols * 2;
+      TRY(hipMemcpy2DAsync(p->packed + c.dst_off, c.dst_pitch, src, c.cols * 2, c.cols * 2, c.nrows,
+                           hipMemcpyHostToDevice, p->stream));
     }
   }
   // schedule
@@ -338,6 +360,7 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.S = hp.S;
   a.combine_in_o = hp.combine_in_o;
   a.poison = (p->cfg.flags & TILES_POISON) ? 1 : 0;
+  a.barrier_mode = (p->cfg.flags & TILES_BARRIER_GATHER) ? 1 : 0;
   a.eps = p->cfg.rms_eps;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)hp.s.hd));
   a.spin_limit = 1u << 22;

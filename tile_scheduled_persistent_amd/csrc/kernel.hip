@@ -129,7 +129,7 @@ __device__ inline float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout (dynamic): ring [NCOMP][RING_SLOTS][1 KB] | vec | part | small | segs.
+// LDS layout (dynamic): vec | part | small | segs.
 // small[] words written by the control wave before barrier A of every wave:
 constexpr int SM_DONE = 0;   // int: no more waves (end of launch or abort)
 constexpr int SM_KIND = 1;   // int: tile kind
@@ -141,8 +141,6 @@ constexpr int SM_POS = 6;    // int: position of the current step
 // ---------------------------------------------------------------------------
 
 struct Lds {
-  unsigned char* ring;
-  uint32_t ring_addr;  // LDS byte address of the ring
   float* vec;
   float* part;
   float* small;
@@ -156,86 +154,15 @@ __device__ inline bool is_gemv(int kind) {
 __device__ inline int chunk_lo(int n, int c) { return (int)(((int64_t)n * c) / NCOMP); }
 
 // ---------------------------------------------------------------------------
-// weight prefetcher of one compute wave: walks the worker's GEMV chunks in the
-// order the wave consumes them, across blocks, waves and steps.
+// compute wave: weight streaming.  Each compute wave reads its share of a GEMV block (a
+// contiguous chunk range) with 16-byte loads into registers, double-buffered in batches of
+// STREAM_BATCH chunks.  Before a tile's last batch is consumed, the wave issues the loads of
+// the first PREFETCH_CHUNKS chunks of its next GEMV tile, so those bytes arrive while the
+// workgroup goes through the epilogue, the grid barrier and the next prologue.
 // ---------------------------------------------------------------------------
 
-struct Cursor {
-  int k, r0, i, ihi;
-  int64_t base;  // byte offset of the current block's first chunk
-};
-
-__device__ inline bool cursor_set(Cursor& cu, const SegDesc& s, int block_rows, int c) {
-  const int nr = min(block_rows, s.rows - cu.r0);
-  const int n = nr * s.chunks_per_row;
-  cu.i = chunk_lo(n, c);
-  cu.ihi = chunk_lo(n, c + 1);
-  cu.base = s.woff + (int64_t)cu.r0 * s.chunks_per_row * CHUNK_BYTES;
-  return cu.i < cu.ihi;
-}
-
-// Move to the next non-empty (wave, block) range; wraps to the next step.  A compute wave
-// with no chunk in the whole step parks on a valid address (loads that are never consumed).
-__device__ inline void cursor_next(Cursor& cu, const SegDesc* segs, int n_waves, int block_rows, int c) {
-  if (cu.k == -2) {  // parked: keep re-reading the first chunk of the packed buffer
-    cu.i = 0;
-    cu.ihi = 1;
-    return;
-  }
-  for (int guard = 0; guard < 4 * n_waves + 4; ++guard) {
-    if (cu.k >= 0 && cu.r0 + block_rows < segs[cu.k].rows) {
-      cu.r0 += block_rows;
-    } else {
-      cu.k = cu.k + 1 >= n_waves ? 0 : cu.k + 1;
-      cu.r0 = 0;
-      if (segs[cu.k].rows == 0) continue;
-    }
-    if (cursor_set(cu, segs[cu.k], block_rows, c)) return;
-  }
-  cu.k = -2;
-  cu.r0 = 0;
-  cu.base = 0;
-  cu.i = 0;
-  cu.ihi = 1;
-}
-
-// Direct-to-LDS 16-byte load of one chunk: lane l's 16 bytes land at lds_addr + 16 l.
-// Issued through inline assembly so that the compiler neither reorders LDS reads of the
-// ring around it nor adds waits for it: the ring protocol below does the waiting.
-__device__ inline void dma_chunk(const void* gaddr, uint32_t lds_addr) {
-  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);  // wave-uniform by construction
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off\n\t" ::"v"(gaddr),
-      "s"(lds_addr)
-      : "memory", "m0");
-}
-// The chunk consumed next was issued RING_SLOTS-1 loads ago (one load is issued per
-// consumed chunk, into the slot consumed one iteration earlier), so at most RING_SLOTS-2
-// younger loads are in flight; vector-memory loads complete in issue order.  Any other
-// load issued in between only makes this wait stricter.
-__device__ inline void ring_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING_SLOTS - 2) : "memory"); }
-__device__ inline void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-struct Prefetcher {
-  Cursor cu;
-  int slot;       // ring slot of the next chunk to consume
-  int free_slot;  // slot consumed in the previous iteration (refilled now)
-  uint32_t ring_addr;
-  const uint8_t* packed;
-  int lane;
-
-  __device__ inline void issue(const SegDesc* segs, int n_waves, int block_rows, int c, int into) {
-    const u32x4* g = reinterpret_cast<const u32x4*>(packed + cu.base) + (int64_t)cu.i * 64 + lane;
-    dma_chunk(g, ring_addr + (uint32_t)into * CHUNK_BYTES);
-    if (++cu.i >= cu.ihi) cursor_next(cu, segs, n_waves, block_rows, c);
-  }
-};
-
-// ---------------------------------------------------------------------------
-// compute wave: GEMV block -> part[row * NCOMP + c]
-// ---------------------------------------------------------------------------
+constexpr int STREAM_BATCH = 4;
+constexpr int PREFETCH_CHUNKS = 12;  // register budget: 8 are used when a KV head serves 3-4 query heads
 
 __device__ inline float dot8(const u32x4 w, const float* v) {
   const f32x4 v0 = *reinterpret_cast<const f32x4*>(v);
@@ -251,22 +178,75 @@ __device__ inline float dot8(const u32x4 w, const float* v) {
   return s0 + s1;
 }
 
-__device__ void compute_gemv_block(Prefetcher& pf, const Lds& L, int n_waves, int block_rows, int c, int lane, int C,
-                                   int nr) {
-  const int n = nr * C;
-  int i = chunk_lo(n, c);
-  const int ihi = chunk_lo(n, c + 1);
-  if (i >= ihi) return;
+// Chunk range [i, ihi) of compute wave c in block r0 of a GEMV segment.
+struct Range {
+  int k;         // schedule wave (-1: none)
+  int C;         // chunks per row
+  int i, ihi;
+  int64_t base;  // byte offset of the block's first chunk
+};
+
+__device__ inline Range block_range(const SegDesc& s, int k, int r0, int block_rows, int c) {
+  Range r;
+  r.k = k;
+  r.C = s.chunks_per_row;
+  const int nr = min(block_rows, s.rows - r0);
+  const int n = nr * s.chunks_per_row;
+  r.i = chunk_lo(n, c);
+  r.ihi = chunk_lo(n, c + 1);
+  r.base = s.woff + (int64_t)r0 * s.chunks_per_row * CHUNK_BYTES;
+  return r;
+}
+
+// First block of the next GEMV wave after `k` (wrapping into the next step) in which compute
+// wave c has chunks; k = -1 when there is none.
+__device__ inline Range next_gemv(const SegDesc* segs, int n_waves, int k, int block_rows, int c) {
+  for (int d = 1; d <= n_waves; ++d) {
+    const int kk = (k + d) % n_waves;
+    if (segs[kk].rows == 0) continue;
+    const Range r = block_range(segs[kk], kk, 0, block_rows, c);
+    if (r.i < r.ihi) return r;
+  }
+  Range none;
+  none.k = -1;
+  none.C = 1;
+  none.i = none.ihi = 0;
+  none.base = 0;
+  return none;
+}
+
+template <int PF>
+struct Prefetch {
+  u32x4 v[PF];
+  int n;  // valid entries
+  int k;  // schedule wave they belong to (-1: none)
+};
+
+template <int PF>
+__device__ inline void issue_prefetch(Prefetch<PF>& pf, const Range& r, const uint8_t* packed, int lane) {
+  pf.k = r.k;
+  pf.n = r.k < 0 ? 0 : min(PF, r.ihi - r.i);
+  const u32x4* g = reinterpret_cast<const u32x4*>(packed + r.base) + (int64_t)r.i * 64 + lane;
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < pf.n) pf.v[u] = __builtin_nontemporal_load(g + u * 64);
+}
+
+// Consume chunks [r.i, r.ihi): the first `npf` come from pf (when use_pf), the rest are streamed.
+// Per-row partial sums go to part[row * NCOMP + c].  When `refill` is set, the loads of the next
+// tile's prefetch are issued as early as the current tile allows.
+template <int PF>
+__device__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane, Prefetch<PF>& pf,
+                             bool use_pf, bool refill, const Range& nxt) {
+  const int C = r.C;
+  int i = r.i;
+  const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
   float acc = 0.f;
-  const unsigned char* ring_c = L.ring + (size_t)c * RING_SLOTS * CHUNK_BYTES + lane * 16;
   const float* vlane = L.vec + lane * 8;
-  for (; i < ihi; ++i) {
-    ring_wait();
-    const u32x4 w = *reinterpret_cast<const u32x4*>(ring_c + pf.slot * CHUNK_BYTES);
-    pf.issue(L.segs, n_waves, block_rows, c, pf.free_slot);
-    pf.free_slot = pf.slot;
-    pf.slot = pf.slot + 1 == RING_SLOTS ? 0 : pf.slot + 1;
+  const u32x4* g = reinterpret_cast<const u32x4*>(packed + r.base) + lane;
+  const int npf = use_pf ? pf.n : 0;
+  auto consume = [&](const u32x4& w) {
     acc += dot8(w, vlane + seg * CHUNK_COLS);
     if (++seg == C) {
       const float s = wave_sum(acc);
@@ -275,6 +255,39 @@ __device__ void compute_gemv_block(Prefetcher& pf, const Lds& L, int n_waves, in
       seg = 0;
       ++row;
     }
+  };
+  // first streamed batch is issued before the prefetched chunks are consumed
+  u32x4 wa[STREAM_BATCH], wb[STREAM_BATCH];
+  int j = i + npf;
+  int na = min(STREAM_BATCH, ihi - j);
+#pragma unroll
+  for (int u = 0; u < STREAM_BATCH; ++u)
+    if (u < na) wa[u] = __builtin_nontemporal_load(g + (int64_t)(j + u) * 64);
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < npf) consume(pf.v[u]);
+  bool refilled = false;
+  if (na <= 0) {
+    if (refill) issue_prefetch(pf, nxt, packed, lane);
+    refilled = true;
+  }
+  while (na > 0) {
+    const int jn = j + na;
+    const int nb = min(STREAM_BATCH, ihi - jn);
+#pragma unroll
+    for (int u = 0; u < STREAM_BATCH; ++u)
+      if (u < nb) wb[u] = __builtin_nontemporal_load(g + (int64_t)(jn + u) * 64);
+    if (nb <= 0 && !refilled) {  // last batch in flight: start the next tile's loads now
+      if (refill) issue_prefetch(pf, nxt, packed, lane);
+      refilled = true;
+    }
+#pragma unroll
+    for (int u = 0; u < STREAM_BATCH; ++u)
+      if (u < na) consume(wa[u]);
+    j = jn;
+    na = nb;
+#pragma unroll
+    for (int u = 0; u < STREAM_BATCH; ++u) wa[u] = wb[u];
   }
   if (seg != 0) {
     const float s = wave_sum(acc);
@@ -379,38 +392,56 @@ __device__ inline float merge_splits(const float* Ph, int S, int HD, int d) {
   return aa / ll;
 }
 
-// attention prologue: q (scaled to the base-2 domain), rounded k and v of the current
-// position into LDS; the split holding the current position writes K/V to the cache.
+// Attention tile LDS layout (inside `part`): q[G][HD] (normed, roped, scaled to the base-2
+// domain) | kc[HD] (normed, roped, BF16-rounded) | vc[HD] (BF16-rounded) | compute-wave states
+// [NCOMP][G][HD + 2] | merged partial [G][HD + 2].  The raw q/k/v are staged in `vec`.
 template <int HD, int G>
-__device__ void cw_attn_prologue(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp, int pos,
-                                 int64_t L_att) {
-  float* q = L.part;
-  float* kc = q + G * HD;
-  float* vc = kc + HD;
+__device__ inline float* attn_ws(const Lds& L) { return L.part + G * HD + 2 * HD; }
+template <int HD, int G>
+__device__ inline float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * (HD + 2); }
+
+// control wave, before barrier P: raw q (G heads), k, v of KV group g into vec (one batch of loads)
+template <int HD, int G>
+__device__ void cw_attn_load(const KernelArgs& a, const Lds& L, int lane, int g) {
+  constexpr int N = (G + 2) * HD;
+  constexpr int B = (N + 255) / 256;
+  const __amdgpu_buffer_rsrc_t r = rsrc(a.qkv);
   const int qbase = g * G * HD;
   const int kbase = a.n_heads * HD + g * HD;
   const int vbase = a.n_heads * HD + a.n_kv * HD + g * HD;
-  constexpr int HALF = HD / 2;
-  // raw q (G heads), k, v of this KV group: (G + 2) * HD floats, staged through LDS
-  float* raw = L.vec;
-  cw_load_vec(raw, a.qkv + qbase, G * HD, G * HD, lane);
-  cw_load_vec(raw + G * HD, a.qkv + kbase, HD, HD, lane);
-  cw_load_vec(raw + (G + 1) * HD, a.qkv + vbase, HD, HD, lane);
-  const bool qkn = a.small[layer].q_norm >= 0;
-  // G query heads and the key: optional RMSNorm over HD, then RoPE on pairs (i, i + HD/2)
-  float co = 0.f, si = 0.f;
-  if (lane < HALF) {
-    const float* cs = a.rope + ((int64_t)pos * HALF + lane) * 2;
-    co = cs[0];
-    si = cs[1];
+  COMPILER_FENCE();
+  u32x4 v[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int i = u * 256 + lane * 4;
+    const int src = i < G * HD ? qbase + i : i < (G + 1) * HD ? kbase + (i - G * HD) : vbase + (i - (G + 1) * HD);
+    v[u] = i < N ? cld4(r, (uint32_t)src * 4) : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int u = 0; u <= G; ++u) {
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int i = u * 256 + lane * 4;
+    if (i < N) *reinterpret_cast<f32x4*>(L.vec + i) = as_f32x4(v[u]);
+  }
+  COMPILER_FENCE();
+}
+
+// all wavefronts, between barriers P and A: wave u < G normalises (optional) and rotates query
+// head u, wave G the key; wave G + 1 rounds the value.  LDS only (plus read-only tables).
+template <int HD, int G>
+__device__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos) {
+  constexpr int HALF = HD / 2;
+  float* q = L.part;
+  float* kc = q + G * HD;
+  float* vc = kc + HD;
+  const float* raw = L.vec;
+  if (wave_index <= G) {
+    const int u = wave_index;
     float u0 = 0.f, u1 = 0.f;
     if (lane < HALF) {
       u0 = raw[u * HD + lane];
       u1 = raw[u * HD + lane + HALF];
     }
-    if (qkn) {
+    if (a.small[layer].q_norm >= 0) {
       const float ss = wave_sum(u0 * u0 + u1 * u1);
       const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
       const uint16_t* gn =
@@ -421,6 +452,8 @@ __device__ void cw_attn_prologue(const KernelArgs& a, const Lds& L, int lane, in
       }
     }
     if (lane < HALF) {
+      const float* cs = a.rope + ((int64_t)pos * HALF + lane) * 2;
+      const float co = cs[0], si = cs[1];
       const float r0 = u0 * co - u1 * si;
       const float r1 = u1 * co + u0 * si;
       if (u < G) {
@@ -431,9 +464,17 @@ __device__ void cw_attn_prologue(const KernelArgs& a, const Lds& L, int lane, in
         kc[lane + HALF] = bf16_round(r1);
       }
     }
+  } else if (wave_index == G + 1) {
+    for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
   }
-  for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
-  // KV write by the split that holds the current position
+}
+
+// control wave, after barrier A: the split holding the current position writes its K/V row
+template <int HD, int G>
+__device__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
+                                 int64_t L_att) {
+  const float* kc = L.part + G * HD;
+  const float* vc = kc + HD;
   const int64_t ch = (L_att + a.S - 1) / a.S;
   const int64_t lo = (int64_t)sp * ch;
   const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
@@ -463,7 +504,7 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
-  float* ws = L.part + G * HD + 2 * HD;
+  float* ws = attn_ws<HD, G>(L);
   const int64_t ch = (L_att + a.S - 1) / a.S;
   int64_t lo = (int64_t)sp * ch;
   const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
@@ -472,15 +513,11 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   constexpr int LPP = HD / 8;  // lanes per position
   constexpr int P = 64 / LPP;  // positions per load
-  constexpr int U = 4;         // loads in flight per operand
+  constexpr int U = 2;         // position groups per batch (two batches in flight)
   const int64_t n = hi > lo ? hi - lo : 0;
   const int64_t wlo = lo + (n * c) / NCOMP, whi = lo + (n * (c + 1)) / NCOMP;
   const int pp = lane / LPP, dseg = lane % LPP;
-  float qr[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qr[h][e] = q[h * HD + dseg * 8 + e];
+  const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -492,9 +529,7 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
   const u32x4* kbase_p = reinterpret_cast<const u32x4*>(a.kv_k + kvrow0 * HD);
   const u32x4* vbase_p = reinterpret_cast<const u32x4*>(a.kv_v + kvrow0 * HD);
   const __amdgpu_buffer_rsrc_t rk = rsrc(kbase_p), rv = rsrc(vbase_p);
-  for (int64_t jb = wlo; jb < whi; jb += U * P) {
-    // issue the loads of U position groups, then consume them
-    u32x4 kw[U], vw[U];
+  auto load = [&](int64_t jb, u32x4* kw, u32x4* vw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t j = jb + u * P + pp;
@@ -510,6 +545,8 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
         }
       }
     }
+  };
+  auto consume = [&](int64_t jb, const u32x4* kw, const u32x4* vw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t j = jb + u * P + pp;
@@ -527,13 +564,15 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d0 = qr[h][0] * kf[0], d1 = qr[h][1] * kf[1];
-        d0 = fmaf(qr[h][2], kf[2], d0);
-        d1 = fmaf(qr[h][3], kf[3], d1);
-        d0 = fmaf(qr[h][4], kf[4], d0);
-        d1 = fmaf(qr[h][5], kf[5], d1);
-        d0 = fmaf(qr[h][6], kf[6], d0);
-        d1 = fmaf(qr[h][7], kf[7], d1);
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlane + h * HD + 4);
+        float d0 = q0.x * kf[0], d1 = q0.y * kf[1];
+        d0 = fmaf(q0.z, kf[2], d0);
+        d1 = fmaf(q0.w, kf[3], d1);
+        d0 = fmaf(q1.x, kf[4], d0);
+        d1 = fmaf(q1.y, kf[5], d1);
+        d0 = fmaf(q1.z, kf[6], d0);
+        d1 = fmaf(q1.w, kf[7], d1);
         float s = d0 + d1;
         s = LPP == 8 ? sum8(s) : sum16(s);
         if (valid) {
@@ -546,6 +585,19 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
           m[h] = mn;
         }
       }
+    }
+  };
+  if (wlo < whi) {
+    u32x4 ka[U], va[U], kb[U], vb[U];
+    load(wlo, ka, va);
+    for (int64_t jb = wlo; jb < whi; jb += 2 * U * P) {
+      const int64_t jn = jb + U * P;
+      if (jn < whi) load(jn, kb, vb);
+      consume(jb, ka, va);
+      if (jn >= whi) break;
+      const int64_t jnn = jn + U * P;
+      if (jnn < whi) load(jnn, ka, va);
+      consume(jn, kb, vb);
     }
   }
   // merge the P position groups of this wave (lanes differing by multiples of LPP)
@@ -582,11 +634,13 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
   }
 }
 
-// control wave: merge the compute waves' states in order and store the split's partial
+// all wavefronts, between barriers B and E: merge the compute waves' states in wave order into
+// the tile's partial (m, l, acc) per query head
 template <int HD, int G>
-__device__ void cw_attn_merge(const KernelArgs& a, const Lds& L, int lane, int g, int sp) {
-  const float* ws = L.part + G * HD + 2 * HD;
-  for (int idx = lane; idx < G * HD; idx += 64) {
+__device__ void attn_merge_phase(const Lds& L, int wave_index, int lane) {
+  const float* ws = attn_ws<HD, G>(L);
+  float* mrg = attn_merged<HD, G>(L);
+  for (int idx = wave_index * 64 + lane; idx < G * HD; idx += BLOCK_THREADS) {
     const int h = idx / HD, d = idx % HD;
     float mm = -INFINITY, ll = 0.f, aa = 0.f;
     for (int c = 0; c < NCOMP; ++c) {
@@ -599,20 +653,33 @@ __device__ void cw_attn_merge(const KernelArgs& a, const Lds& L, int lane, int g
       aa = aa * f1 + st[2 + d] * f2;
       mm = mn;
     }
-    float* dst = a.part + ((int64_t)(g * G + h) * a.S + sp) * (HD + 2);
+    float* dst = mrg + h * (HD + 2);
     if (d == 0) {
-      st_f32(dst, mm);
-      st_f32(dst + 1, ll);
+      dst[0] = mm;
+      dst[1] = ll;
     }
-    st_f32(dst + 2 + d, aa);
+    dst[2 + d] = aa;
+  }
+}
+
+// control wave, after barrier E: store the merged partials of query heads g*G .. g*G+G-1, split sp
+template <int HD, int G>
+__device__ void cw_attn_store(const KernelArgs& a, const Lds& L, int lane, int g, int sp) {
+  const float* mrg = attn_merged<HD, G>(L);
+  for (int idx = lane; idx < G * (HD + 2); idx += 64) {
+    const int h = idx / (HD + 2), e = idx % (HD + 2);
+    st_f32(a.part + ((int64_t)(g * G + h) * a.S + sp) * (HD + 2) + e, mrg[idx]);
   }
 }
 
 // LDS-only prologue work shared by all eight wavefronts between barriers P and A:
 // merging the split partials into the o_proj input vector.  wave_index in [0, NWAVES).
-template <int HD>
-__device__ inline void prologue_lds_phase(const KernelArgs& a, const Lds& L, int kind, int wave_index, int lane) {
-  if (kind == KIND_O && a.combine_in_o) {
+template <int HD, int G>
+__device__ inline void prologue_lds_phase(const KernelArgs& a, const Lds& L, int kind, int wave_index, int lane,
+                                          int layer, int pos) {
+  if (kind == KIND_ATTN) {
+    attn_lds_prep<HD, G>(a, L, wave_index, lane, layer, pos);
+  } else if (kind == KIND_O && a.combine_in_o) {
     const int nq = a.n_heads * HD;
     for (int i = wave_index * 64 + lane; i < nq; i += BLOCK_THREADS)
       L.vec[i] = merge_splits(L.part + (i / HD) * a.S * (HD + 2), a.S, HD, i % HD);
@@ -624,15 +691,12 @@ __device__ inline void prologue_lds_phase(const KernelArgs& a, const Lds& L, int
 // 64-byte line and polls all lines.  A watchdog bounds every wait.
 // ---------------------------------------------------------------------------
 
-__device__ bool cw_grid_barrier(const KernelArgs& a, int bid, int lane, uint32_t gen) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
-  uint32_t* arrive = a.sync + SYNC_ARRIVE_BASE;
-  if (lane == 0) st_u32(arrive + bid * SYNC_LINE_WORDS, gen);
+// Spin until every lane's predicate holds; false = released, true = aborted (watchdog or peer abort).
+template <typename Ready>
+__device__ inline bool cw_spin(const KernelArgs& a, int lane, Ready ready) {
   uint32_t spins = 0;
   for (;;) {
-    bool ok = true;
-    for (int w = lane; w < a.W; w += 64) ok &= (int32_t)(ld_u32(arrive + w * SYNC_LINE_WORDS) - gen) >= 0;
-    if (__all(ok)) return false;
+    if (__all(ready())) return false;
     if ((++spins & 63) == 0) {
       if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) return true;
       if (spins > a.spin_limit) {
@@ -644,6 +708,25 @@ __device__ bool cw_grid_barrier(const KernelArgs& a, int bid, int lane, uint32_t
       }
     }
   }
+}
+
+__device__ bool cw_grid_barrier(const KernelArgs& a, int bid, int lane, uint32_t gen) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+  uint32_t* arrive = a.sync + SYNC_ARRIVE_BASE;
+  uint32_t* release = arrive + (int64_t)a.W * SYNC_LINE_WORDS;
+  if (lane == 0) st_u32(arrive + bid * SYNC_LINE_WORDS, gen);
+  auto all_arrived = [&]() {
+    bool ok = true;
+    for (int w = lane; w < a.W; w += 64) ok &= (int32_t)(ld_u32(arrive + w * SYNC_LINE_WORDS) - gen) >= 0;
+    return ok;
+  };
+  if (a.barrier_mode == 0) return cw_spin(a, lane, all_arrived);
+  // gather/release: worker 0 waits for every arrival, then writes each worker's release line
+  if (bid == 0) {
+    if (cw_spin(a, lane, all_arrived)) return true;
+    for (int w = lane; w < a.W; w += 64) st_u32(release + w * SYNC_LINE_WORDS, gen);
+  }
+  return cw_spin(a, lane, [&]() { return (int32_t)(ld_u32(release + bid * SYNC_LINE_WORDS) - gen) >= 0; });
 }
 
 // ---------------------------------------------------------------------------
@@ -710,7 +793,7 @@ __device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lan
           cw_load_vec(L.vec, a.act, a.F, t.kpad, lane);
           break;
         case KIND_ATTN:
-          cw_attn_prologue<HD, G>(a, L, lane, layer, t.row0, t.nrows, pos, L_att);
+          cw_attn_load<HD, G>(a, L, lane, t.row0);
           break;
         default:
           break;
@@ -726,8 +809,9 @@ __device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lan
         smi[SM_POS] = pos;
       }
       __syncthreads();  // P: global inputs staged in LDS
-      prologue_lds_phase<HD>(a, L, t.kind, 0, lane);
+      prologue_lds_phase<HD, G>(a, L, t.kind, 0, lane, layer, pos);
       __syncthreads();  // A: inputs ready
+      if (t.kind == KIND_ATTN) cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
       // ---- compute waves run; epilogues ----
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
@@ -780,7 +864,9 @@ __device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lan
         __syncthreads();  // B
         if (a.trace) t_cmp = wall_clock64();
         if (t.kind == KIND_ATTN) {
-          cw_attn_merge<HD, G>(a, L, lane, t.row0, t.nrows);
+          attn_merge_phase<HD, G>(L, 0, lane);
+          __syncthreads();  // E: merged partial ready
+          cw_attn_store<HD, G>(a, L, lane, t.row0, t.nrows);
         } else if (t.kind == KIND_COMBINE) {
           float* P = L.part;
           const int np = a.S * (HD + 2);
@@ -868,41 +954,46 @@ __device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lan
 template <int HD, int G>
 __device__ void compute_loop(const KernelArgs& a, const Lds& L, int c, int lane, int block_rows) {
   const volatile int* smi = reinterpret_cast<const volatile int*>(L.small);
-  Prefetcher pf;
-  pf.ring_addr = __builtin_amdgcn_readfirstlane(L.ring_addr + (uint32_t)(c * RING_SLOTS * CHUNK_BYTES));
-  pf.packed = a.packed;
-  pf.lane = lane;
-  pf.cu.k = -1;
-  pf.cu.r0 = 0;
-  cursor_next(pf.cu, L.segs, a.n_waves, block_rows, c);
-  for (int s = 0; s < RING_SLOTS - 1; ++s) pf.issue(L.segs, a.n_waves, block_rows, c, s);
-  pf.slot = 0;
-  pf.free_slot = RING_SLOTS - 1;
-  for (;;) {  // one iteration per wave of every step, until the control wave raises the done flag
+  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
+  issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
+  int k = -1;  // schedule wave being executed
+  for (;;) {   // one iteration per wave of every step, until the control wave raises the done flag
     __syncthreads();  // P
     if (smi[SM_DONE]) break;
-    prologue_lds_phase<HD>(a, L, smi[SM_KIND], c + 1, lane);
+    k = k + 1 == a.n_waves ? 0 : k + 1;
+    prologue_lds_phase<HD, G>(a, L, smi[SM_KIND], c + 1, lane, smi[SM_LAYER], smi[SM_POS]);
     __syncthreads();  // A
     const int kind = smi[SM_KIND];
     const int row0 = smi[SM_ROW0];
     const int nrows = smi[SM_NROWS];
     const int layer = smi[SM_LAYER];
-    const int C = smi[SM_C];
     const int pos = smi[SM_POS];
     if (is_gemv(kind)) {
-      const int rows = kind == KIND_GU ? 2 * nrows : nrows;
+      const SegDesc sd = L.segs[k];
+      const int rows = sd.rows;
       for (int r0 = 0; r0 < rows; r0 += block_rows) {
-        const int nr = min(block_rows, rows - r0);
-        compute_gemv_block(pf, L, a.n_waves, block_rows, c, lane, C, nr);
+        const Range r = block_range(sd, k, r0, block_rows, c);
+        const bool last_block = r0 + block_rows >= rows;
+        const Range nxt = last_block ? next_gemv(L.segs, a.n_waves, k, block_rows, c) : r;
+        if (r.i < r.ihi) {
+          stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, last_block, nxt);
+        } else if (last_block) {
+          issue_prefetch(pf, nxt, a.packed, lane);
+        }
         __syncthreads();                              // B
         if (r0 + block_rows < rows) __syncthreads();  // C
       }
     } else {
-      if (kind == KIND_ATTN) compute_attention<HD, G>(a, L, c, lane, layer, row0, nrows, (int64_t)pos + 1);
-      __syncthreads();  // B
+      if (kind == KIND_ATTN) {
+        compute_attention<HD, G>(a, L, c, lane, layer, row0, nrows, (int64_t)pos + 1);
+        __syncthreads();  // B
+        attn_merge_phase<HD, G>(L, c + 1, lane);
+        __syncthreads();  // E
+      } else {
+        __syncthreads();  // B
+      }
     }
   }
-  vm_drain();
 }
 
 template <int HD, int G>
@@ -910,9 +1001,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
   Lds L;
-  L.ring = lds_raw;
-  L.ring_addr = (uint32_t)(uintptr_t)(LDS_AS unsigned char*)lds_raw;
-  L.vec = reinterpret_cast<float*>(lds_raw + RING_BYTES);
+  L.vec = reinterpret_cast<float*>(lds_raw);
   L.part = L.vec + a.lds_vec_floats;
   L.small = L.part + a.lds_part_floats;
   L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
@@ -930,6 +1019,35 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
   if (wave == 0) control_loop<HD, G>(a, L, bid, lane, block_rows);
   else compute_loop<HD, G>(a, L, wave - 1, lane, block_rows);
+}
+
+// ---------------------------------------------------------------------------
+// weight packing (plan creation): one launch copies every segment.  Rows whose byte counts
+// and addresses are 16-byte multiples move with 16-byte accesses, others with 2-byte ones.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) pack_weights(const PackSeg* __restrict__ segs, int nseg, uint8_t* __restrict__ dst) {
+  for (int sidx = blockIdx.x; sidx < nseg; sidx += gridDim.x) {
+    const PackSeg g = segs[sidx];
+    const bool v16 = ((g.row_bytes | g.src_pitch | g.dst_pitch | g.dst_off | (int64_t)(uintptr_t)g.src) & 15) == 0;
+    for (int64_t r = 0; r < g.rows; ++r) {
+      const uint8_t* s = g.src + r * g.src_pitch;
+      uint8_t* d = dst + g.dst_off + r * g.dst_pitch;
+      if (v16) {
+        for (int64_t b = (int64_t)threadIdx.x * 16; b < g.row_bytes; b += 256 * 16)
+          *reinterpret_cast<u32x4*>(d + b) = *reinterpret_cast<const u32x4*>(s + b);
+      } else {
+        for (int64_t b = (int64_t)threadIdx.x * 2; b < g.row_bytes; b += 256 * 2)
+          *reinterpret_cast<uint16_t*>(d + b) = *reinterpret_cast<const uint16_t*>(s + b);
+      }
+    }
+  }
+}
+
+hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream) {
+  const int grid = nseg < 4096 ? (nseg > 0 ? nseg : 1) : 4096;
+  hipLaunchKernelGGL(pack_weights, dim3(grid), dim3(256), 0, stream, segs, nseg, dst);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

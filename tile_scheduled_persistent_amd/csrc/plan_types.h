@@ -28,12 +28,10 @@ constexpr int CHUNK_BYTES = 1024;
 constexpr int BLOCK_THREADS = 512;
 constexpr int NWAVES = BLOCK_THREADS / 64;
 // Wavefront 0 of every workgroup is the control wave (prologues, epilogues, stores, grid
-// barrier); wavefronts 1..NCOMP stream weights through per-wave LDS rings and compute.
+// barrier); wavefronts 1..NCOMP stream weights into registers and compute.
 constexpr int NCOMP = NWAVES - 1;
-constexpr int RING_SLOTS = 12;                              // 1 KB chunks per compute wave
-constexpr int RING_BYTES = NCOMP * RING_SLOTS * CHUNK_BYTES;
 constexpr int SMALL_FLOATS = 1024;                          // LDS scratch for reductions / broadcasts
-struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the weight prefetcher)
+struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the weight prefetch)
   int64_t woff;
   int32_t chunks_per_row;
   int32_t rows;  // weight rows of the tile (0: no GEMV tile in this wave)
@@ -68,12 +66,24 @@ constexpr int SYNC_LINE_WORDS = 16;
 constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = barrier watchdog)
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
 constexpr int SYNC_ARRIVE_BASE = 64;     // arrive[w] at SYNC_ARRIVE_BASE + w * SYNC_LINE_WORDS
+// release[w] (gather/release barrier) at SYNC_ARRIVE_BASE + (W + w) * SYNC_LINE_WORDS
 
 // In-kernel trace record per (step, wave, worker): wave start, input staged, compute done,
 // barrier arrival, barrier release (100 MHz wall clock).
 constexpr int TRACE_WORDS = 5;
 
-inline int64_t sync_words(int W) { return SYNC_ARRIVE_BASE + (int64_t)W * SYNC_LINE_WORDS; }
+inline int64_t sync_words(int W) { return SYNC_ARRIVE_BASE + 2 * (int64_t)W * SYNC_LINE_WORDS; }
+
+// One weight-packing copy executed on the device: `rows` rows of `row_bytes` bytes from
+// `src` (rows `src_pitch` apart) to packed + dst_off (rows `dst_pitch` apart).
+struct PackSeg {
+  const uint8_t* src;
+  int64_t src_pitch;
+  int64_t dst_off;
+  int64_t dst_pitch;
+  int64_t rows;
+  int64_t row_bytes;
+};
 
 struct KernelArgs {
   const TileDesc* tiles;     // [n_waves][W]
@@ -103,6 +113,7 @@ struct KernelArgs {
   int32_t W, n_layers, H, Hpad, n_heads, n_kv, head_dim, F, Fpad, V, qkv_rows, Qpad, S;
   int32_t combine_in_o;      // 1: the o_proj prologue merges the splits
   int32_t poison;
+  int32_t barrier_mode;      // 0: every worker polls every arrival line; 1: worker 0 gathers, then releases each worker
   float eps;
   float qscale;              // log2(e) / sqrt(head_dim): scores in the base-2 domain
   uint32_t spin_limit;       // barrier watchdog (polls)

@@ -291,13 +291,13 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS)
   int32_t part = 0;
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
-  // attention tile: q[G][hd], k[hd], v[hd] and the compute-wave states [NCOMP][G][hd + 2]
-  part = std::max(part, s.G * s.hd + 2 * s.hd + NCOMP * s.G * (s.hd + 2));
+  // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 2] and the merged partial
+  part = std::max(part, s.G * s.hd + 2 * s.hd + (NCOMP + 1) * s.G * (s.hd + 2));
   part = std::max(part, p.S * (s.hd + 2));                                  // one head's splits (combine tile)
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * (s.hd + 2));  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
-  p.lds_bytes = RING_BYTES + (p.lds_vec_floats + p.lds_part_floats + SMALL_FLOATS) * 4 +
+  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + SMALL_FLOATS) * 4 +
                 (int32_t)round_up((int64_t)p.waves.size() * (int64_t)sizeof(SegDesc), 256);
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
