@@ -4,6 +4,10 @@
         per-kernel calls, total / average / min / max duration (from --kernel-trace)
     python -m tile_scheduled_persistent_amd.prof counters DB --kernel NAME [--cmd "..."]
         per-dispatch counter values of one kernel (from --pmc runs), e.g. FETCH_SIZE / WRITE_SIZE
+    python -m tile_scheduled_persistent_amd.prof traffic FETCH_DB WRITE_DB --calib-bytes B --build-id ID [--cmd "..."]
+        HBM bytes per launch of one kernel as JSON: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+        each scaled by what the same counter reads for the largest copy-kernel dispatch in the
+        same run, a plain copy of B bytes (reads B, writes B)
 
 The text goes to stdout; the command that produced the database is echoed in the header.
 """
@@ -47,13 +51,61 @@ def counter_values(db: str, kernel: str):
     return agg
 
 
+def _largest_copy(agg_by_kernel: dict) -> float:
+    vals = [v for name, per in agg_by_kernel.items() if "copyBuffer" in name for v in per.values()]
+    if not vals:
+        raise SystemExit("no copy-kernel dispatch in the database: run with a calibration copy")
+    return max(vals)
+
+
+def _per_kernel(db: str, counter: str) -> dict:
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, dispatch_id, value from counters_collection where counter_name = ?",
+                       (counter,)).fetchall()
+    out = {}
+    for name, did, val in rows:
+        out.setdefault(str(name), {}).setdefault(did, 0.0)
+        out[str(name)][did] += float(val)
+    return out
+
+
+def traffic(fetch_db: str, write_db: str, kernel: str, calib_bytes: int) -> dict:
+    res = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        per = _per_kernel(db, counter)
+        copy_kib = _largest_copy(per)
+        factor = calib_bytes / (copy_kib * 1024.0)
+        mine = [v for name, d in per.items() if kernel in name for v in d.values()]
+        if not mine:
+            raise SystemExit(f"no dispatch of {kernel} in {db}")
+        res[counter] = {"kib_per_dispatch": [round(v, 1) for v in mine], "mean_kib": statistics.mean(mine),
+                        "copy_kib": copy_kib, "factor": factor,
+                        "bytes_per_launch": statistics.mean(mine) * 1024.0 * factor}
+    res["traffic_bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["kernels", "counters"])
+    ap.add_argument("mode", choices=["kernels", "counters", "traffic"])
     ap.add_argument("db")
+    ap.add_argument("db2", nargs="?")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--build-id", default="")
+    ap.add_argument("--workload", default="")
     ap.add_argument("--kernel", default="tiles_worker")
     ap.add_argument("--cmd", default="")
     args = ap.parse_args(argv)
+    if args.mode == "traffic":
+        import json
+        if not args.db2:
+            raise SystemExit("traffic needs the FETCH_SIZE and the WRITE_SIZE database")
+        d = traffic(args.db, args.db2, args.kernel, args.calib_bytes)
+        d.update({"kernel": args.kernel, "workload": args.workload, "build_id": args.build_id,
+                  "calibration": f"largest __amd_rocclr_copyBuffer dispatch of the same run, a copy of {args.calib_bytes} bytes",
+                  "command": args.cmd})
+        print(json.dumps(d, indent=1))
+        return 0
     if args.cmd:
         print(f"# command: {args.cmd}")
     if args.mode == "kernels":
