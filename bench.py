@@ -80,7 +80,6 @@ def main():
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
-    ap.add_argument("--barrier-gather", action="store_true", help="gather/release grid barrier")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed launches, run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -105,8 +104,7 @@ def main():
     k0, v0 = synth.make_kv(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, device=dev)
     token = synth.make_tokens(m, 1)[0]
     stream = torch.cuda.current_stream()
-    base_flags = tiles.TILES_BARRIER_GATHER if args.barrier_gather else 0
-    plan = tiles.Plan(m, w, wl.capacity, flags=base_flags, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
+    plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
                       stream=stream)
     info = plan.info()
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
@@ -170,7 +168,7 @@ def main():
         "launch_ms": {"min": round(min(launch_ms), 4), "median": round(float(np.median(launch_ms)), 4),
                       "max": round(max(launch_ms), 4)},
         "plan": {"waves_per_token": info.waves_per_step, "kv_splits": info.kv_splits,
-                 "barrier": "gather/release" if args.barrier_gather else "all-poll",
+                 "sync": "tagged data (parity bit), no grid barrier",
                  "combine": "o_proj prologue" if info.combine_mode == 1 else "own wave",
                  "workers": info.n_workers, "block_threads": info.block_threads},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -192,14 +190,13 @@ def main():
 
 
 def _trace_report(path, m, wl, w, k0, v0, token, args, info):
-    """Per-wave duration, GB/s and barrier wait from the in-kernel trace (separate launch)."""
+    """Per-wave timing from the in-kernel trace (separate launch)."""
     import numpy as np
     import torch
 
     from tile_scheduled_persistent_amd import tiles
 
-    plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE | (tiles.TILES_BARRIER_GATHER if args.barrier_gather else 0),
-                      kv_splits=args.kv_splits,
+    plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits,
                       combine_mode=args.combine_mode)
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
@@ -207,44 +204,44 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     _, tr = plan.read_debug(hidden=False, trace=True)
     waves = plan.waves()
     plan.close()
-    tr = tr.astype(np.int64)  # [steps, waves, W, 5] 100 MHz ticks: start, staged, computed, arrived, released
-    steps = tr.shape[0]
+    # [steps, waves, W, 5] 100 MHz ticks: wave start, inputs staged, compute done, published, (published)
+    tr = tr.astype(np.int64)
+    steps, nw = tr.shape[0], tr.shape[1]
     names = tiles.WAVE_KINDS
-    rel = tr[:, :, :, 4].max(axis=2)  # [steps, waves] last release
-    start = tr[:, :, :, 0].min(axis=2)
-    busy = tr[:, :, :, 0] != 0
-    def phase(a, b):  # per (step, wave): max over busy workers of t_b - t_a, in us
-        d = np.where(busy, tr[:, :, :, b] - tr[:, :, :, a], 0)
-        return d.max(axis=2) * 0.01
-    pro, cmp_, epi = phase(0, 1), phase(1, 2), phase(2, 3)
-    wait = (tr[:, :, :, 4] - tr[:, :, :, 3]).mean(axis=2) * 0.01
-    lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz); phase columns are the max over",
-             "# workers of: prologue (inputs staged), compute (weights consumed), epilogue (outputs stored);",
-             "# barrier = mean wait from arrival to release",
-             f"# workload: {wl.description}; steps traced: {steps}; waves per step: {len(waves)}",
-             "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tprologue_us\tcompute_us\tepilogue_us\tbarrier_us"]
-    tot_dur = 0.0
+    end = tr[:, :, :, 3].max(axis=2)                      # [steps, waves] last worker's publish
+    prev_end = np.concatenate([np.concatenate([[tr[0, 0, :, 0].min()], end[:-1, -1]])[:, None], end[:, :-1]], axis=1)
+    dur = (end - prev_end) * 0.01
+    edge = (tr[:, :, :, 1].max(axis=2) - prev_end) * 0.01  # last producer's publish -> last consumer staged
+    def phase(a, b):  # per (step, wave): max over workers of t_b - t_a, in us
+        return (tr[:, :, :, b] - tr[:, :, :, a]).max(axis=2) * 0.01
+    wait, cmp_, pub = phase(0, 1), phase(1, 2), phase(2, 3)
+    lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz).  dur = last publish of this wave",
+             "# minus last publish of the previous one; edge = last worker's inputs staged minus the previous",
+             "# wave's last publish; wait / compute / publish = max over workers of each phase",
+             f"# workload: {wl.description}; steps traced: {steps}; waves per step: {nw}",
+             "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tedge_us\twait_us\tcompute_us\tpublish_us"]
+    sl = slice(1, None) if steps > 2 else slice(None)  # the first step includes the launch ramp
+    tot = 0.0
     per_kind = {}
     for i, wv in enumerate(waves):
-        prev_rel = rel[:, i - 1] if i > 0 else start[:, 0]
-        dur = float(np.median(rel[:, i] - prev_rel)) * 0.01
-        tot_dur += dur
-        gbs = (wv.weight_bytes / 1e9) / (dur * 1e-6) if dur > 0 else 0.0
+        d_us = float(np.median(dur[sl, i]))
+        tot += d_us
+        gbs = (wv.weight_bytes / 1e9) / (d_us * 1e-6) if d_us > 0 else 0.0
         k = names.get(wv.kind, str(wv.kind))
-        ph = [float(np.median(x[:, i])) for x in (pro, cmp_, epi, wait)]
-        d = per_kind.setdefault(k, [0.0, 0.0, 0.0, 0.0, 0.0, 0.0])
-        d[0] += dur
-        d[1] += wv.weight_bytes
+        ph = [float(np.median(x[sl, i])) for x in (edge, wait, cmp_, pub)]
+        acc = per_kind.setdefault(k, [0.0, 0.0, 0.0, 0.0, 0.0, 0.0])
+        acc[0] += d_us
+        acc[1] += wv.weight_bytes
         for j in range(4):
-            d[2 + j] += ph[j]
-        lines.append(f"{i}\t{k}\t{wv.layer}\t{wv.weight_bytes / 1e6:.2f}\t{dur:.2f}\t{gbs:.0f}\t" +
+            acc[2 + j] += ph[j]
+        lines.append(f"{i}\t{k}\t{wv.layer}\t{wv.weight_bytes / 1e6:.2f}\t{d_us:.2f}\t{gbs:.0f}\t" +
                      "\t".join(f"{x:.2f}" for x in ph))
-    lines.append("# per kind (us per token): total | GB/s | prologue | compute | epilogue | barrier")
+    lines.append("# per kind (us per token): total | GB/s | edge | wait | compute | publish")
     for k, d in per_kind.items():
         lines.append(f"# {k}\t{d[0]:.1f}\t{d[1] / 1e9 / (d[0] * 1e-6) if d[0] else 0:.0f} GB/s\t"
                      f"{d[2]:.1f}\t{d[3]:.1f}\t{d[4]:.1f}\t{d[5]:.1f}")
-    step_us = float(np.median(np.diff(rel[:, -1]))) * 0.01 if steps > 1 else tot_dur
-    lines.append(f"# token time (median step-to-step) {step_us:.1f} us; sum of wave medians {tot_dur:.1f} us")
+    step_us = float(np.median(np.diff(end[:, -1]))) * 0.01 if steps > 1 else tot
+    lines.append(f"# token time (median step-to-step) {step_us:.1f} us; sum of wave medians {tot:.1f} us")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 

@@ -4,10 +4,12 @@
  * One batch-1 greedy BF16 decode step of a Llama/Qwen3-style decoder runs as a
  * static graph of tiles: a host planner cuts every operator into output-row
  * tiles, assigns each tile to a fixed workgroup (one per compute unit), groups
- * the tiles into waves separated by grid barriers, validates the schedule and
- * packs the weights tile-contiguously; one cooperative persistent kernel then
- * executes that schedule for up to 64 tokens per launch, with greedy selection
- * inside the kernel.
+ * the tiles into dependency-ordered waves, validates the schedule and packs the
+ * weights tile-contiguously; one cooperative persistent kernel then executes
+ * that schedule for up to 64 tokens per launch, with greedy selection inside the
+ * kernel.  The pages separate waves with grid barriers; this kernel carries each
+ * dependency in the data instead (every published value holds the step's parity
+ * in its lowest mantissa bit and consumers poll the values themselves).
  *
  * Sources: "Tiles: Scheduling LLM Decoding as a Graph of Tiles" (intro: tiles
  * as the unit of scheduled work, a fixed worker per tile, byte balancing,
@@ -45,14 +47,14 @@ extern "C" {
 #define TILES_E_PLAN (-3)    /* schedule validation failed or the plan was modified after creation */
 #define TILES_E_DEVICE (-4)  /* not gfx950, CU count differs from the plan, no cooperative launch, occupancy < 1 */
 #define TILES_E_HIP (-5)     /* a HIP runtime call failed; its message is in tiles_last_error() */
-#define TILES_E_KERNEL (-6)  /* the kernel reported a fault (barrier watchdog expired) */
+#define TILES_E_KERNEL (-6)  /* the kernel reported a fault (the watchdog of a wait expired) */
 
 /* ---- plan flags (tiles_config_t.flags) --------------------------------- */
 #define TILES_DEBUG_HIDDEN 0x1u /* record the residual stream after every layer of every step */
 #define TILES_TRACE 0x2u        /* record per-worker, per-wave timestamps (100 MHz wall clock) */
-#define TILES_POISON 0x4u       /* NaN-fill the per-step scratch at every step start */
-#define TILES_BARRIER_GATHER 0x8u /* grid barrier: worker 0 gathers all arrivals and releases each worker
-                                     (instead of every worker polling every arrival) */
+#define TILES_POISON 0x4u       /* before every launch, NaN-fill the KV rows the launch will write
+                                   (positions length .. length+n_steps-1 of every layer and KV head),
+                                   so that a read before the kernel's own write shows up as NaN */
 
 /* ---- model + plan options ---------------------------------------------- */
 typedef struct tiles_config {
@@ -68,7 +70,7 @@ typedef struct tiles_config {
   int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
   int32_t tie_embeddings; /* 1: the LM head is the embedding matrix */
   int32_t max_positions;  /* largest KV length (cached + decoded) the plan supports */
-  uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON | TILES_BARRIER_GATHER */
+  uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON */
   int32_t kv_splits;      /* split-KV count per KV head; 0 lets the planner choose */
   int32_t combine_mode;   /* 0 planner choice, 1 combine splits in the o_proj prologue, 2 own wave */
   int32_t n_workers;      /* 0 = one workgroup per compute unit (required on the GPU) */
@@ -107,7 +109,7 @@ typedef struct tiles_plan_info {
   int32_t n_workers;          /* workgroups = grid size */
   int32_t block_threads;      /* threads per workgroup */
   int32_t lds_bytes;          /* dynamic LDS per workgroup */
-  int32_t waves_per_step;     /* grid barriers per decoded token */
+  int32_t waves_per_step;     /* waves (dependency levels) per decoded token */
   int32_t n_tiles;            /* tiles per step (all waves) */
   int32_t kv_splits;          /* S */
   int32_t combine_mode;       /* 1 prologue, 2 own wave */
@@ -133,7 +135,8 @@ typedef struct tiles_wave_info {
  * the source weights may be freed afterwards (the plan keeps a packed copy).
  * Returns NULL on error (see tiles_last_error()).  Allocates device memory:
  * packed weights (= model bytes), RoPE table [max_positions][head_dim/2] x2 FP32,
- * per-step scratch, barrier words, and the debug/trace buffers when flagged. */
+ * the tagged-data buffers (one per wave), status words, and the debug/trace
+ * buffers when flagged. */
 tiles_plan_t *tiles_plan_create(const tiles_config_t *cfg, const tiles_weights_t *w);
 
 /* Greedy-decode n_steps tokens (1..64) in one cooperative launch on the plan's stream.
@@ -176,8 +179,8 @@ int tiles_plan_status(tiles_plan_t *plan);
 /* Copy debug buffers to host memory after synchronizing the plan's stream.
  *   hidden : host float [n_steps_of_last_decode][n_layers][H] or NULL (needs TILES_DEBUG_HIDDEN);
  *   trace  : host uint64 [n_steps][waves_per_step][n_workers][5] or NULL (needs TILES_TRACE):
- *            wave start, input staged, compute done, barrier arrival, barrier release
- *            (100 MHz wall-clock ticks).
+ *            wave start, inputs staged (after waiting for the producers), compute done,
+ *            outputs published, and the same again (100 MHz wall-clock ticks).
  *   *n_steps_out receives the step count of the last decode. */
 int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t *n_steps_out);
 

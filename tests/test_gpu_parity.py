@@ -225,13 +225,3 @@ def test_llama_full_size_repeatable_and_chunk_invariant():
             assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
             t = int(t1[0])
     assert torch.equal(kv.k, a[3].k) and torch.equal(kv.v, a[3].v)
-
-
-def test_gather_release_barrier_matches_all_poll_barrier():
-    """The barrier variant changes synchronisation only: results are bit-identical."""
-    s = Setup(TINY, 40, 20)
-    a = _full_run(s, 11, 15)
-    b = _full_run(s, 11, 15, flags=tiles.TILES_DEBUG_HIDDEN | tiles.TILES_BARRIER_GATHER)
-    assert np.array_equal(a[0], b[0])
-    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
-    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))

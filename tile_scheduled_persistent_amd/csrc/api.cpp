@@ -25,6 +25,8 @@
 namespace tiles {
 const void* worker_kernel(int head_dim, int group);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
+hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
+hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
 }
 
 using namespace tiles;
@@ -69,8 +71,9 @@ struct tiles_plan {
   float* d_rope = nullptr;
   uint8_t* scratch = nullptr;
   size_t scratch_bytes = 0;
-  float *x = nullptr, *qkv = nullptr, *part = nullptr, *attn = nullptr, *act = nullptr;
+  uint32_t* ll = nullptr;      // tagged-data buffers; lmpart follows them in the same fill range
   uint32_t* lmpart = nullptr;
+  int64_t fill_words = 0;      // ll .. lmpart end, refilled before every launch
   uint32_t* sync = nullptr;
   size_t sync_bytes = 0;
   float* dbg_hidden = nullptr;
@@ -247,23 +250,17 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
       off += (bytes + 255) / 256 * 256;
       return o;
     };
-    const size_t o_x = piece((size_t)hp.s.H * 4);
-    const size_t o_qkv = piece((size_t)hp.s.qkv_rows * 4);
-    const size_t o_part = piece((size_t)hp.s.n_heads * hp.S * (hp.s.hd + 2) * 4);
-    const size_t o_attn = piece((size_t)hp.s.n_heads * hp.s.hd * 4);
-    const size_t o_act = piece((size_t)hp.s.F * 4);
+    const size_t o_ll = piece((size_t)hp.ll_words * 4);
     const size_t o_lm = piece((size_t)hp.W * 8);
-    p->sync_bytes = (size_t)sync_words(hp.W) * 4;
+    const size_t lm_end = off;
+    p->sync_bytes = (size_t)SYNC_WORDS * 4;
     const size_t o_sync = piece(p->sync_bytes);
     p->scratch_bytes = off;
     TRY(hipMalloc(&p->scratch, p->scratch_bytes));
     TRY(hipMemsetAsync(p->scratch, 0, p->scratch_bytes, p->stream));
-    p->x = reinterpret_cast<float*>(p->scratch + o_x);
-    p->qkv = reinterpret_cast<float*>(p->scratch + o_qkv);
-    p->part = reinterpret_cast<float*>(p->scratch + o_part);
-    p->attn = reinterpret_cast<float*>(p->scratch + o_attn);
-    p->act = reinterpret_cast<float*>(p->scratch + o_act);
+    p->ll = reinterpret_cast<uint32_t*>(p->scratch + o_ll);
     p->lmpart = reinterpret_cast<uint32_t*>(p->scratch + o_lm);
+    p->fill_words = (int64_t)(lm_end - o_ll) / 4;
     p->sync = reinterpret_cast<uint32_t*>(p->scratch + o_sync);
   }
   if (cfg->flags & TILES_DEBUG_HIDDEN) {
@@ -327,11 +324,7 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.final_norm_off = hp.final_norm_off;
   a.embed_off = hp.embed_off;
   a.embed_stride = hp.embed_stride;
-  a.x = p->x;
-  a.qkv = p->qkv;
-  a.part = p->part;
-  a.attn = p->attn;
-  a.act = p->act;
+  a.ll = p->ll;
   a.lmpart = p->lmpart;
   a.sync = p->sync;
   a.kv_k = static_cast<uint16_t*>(kv->k);
@@ -359,15 +352,23 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.Qpad = hp.s.Qpad;
   a.S = hp.S;
   a.combine_in_o = hp.combine_in_o;
-  a.poison = (p->cfg.flags & TILES_POISON) ? 1 : 0;
-  a.barrier_mode = (p->cfg.flags & TILES_BARRIER_GATHER) ? 1 : 0;
   a.eps = p->cfg.rms_eps;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)hp.s.hd));
   a.spin_limit = 1u << 22;
   a.lds_vec_floats = hp.lds_vec_floats;
   a.lds_part_floats = hp.lds_part_floats;
+  a.lds_xres_floats = hp.lds_xres_floats;
 
-  HIP_TRY(hipMemsetAsync(p->sync, 0, p->sync_bytes, p->stream));
+  // Kernels rather than memsets, so that the launch sequence can be captured in a graph.
+  HIP_TRY(launch_fill(p->ll, p->fill_words, TAG_FILL, p->stream));
+  HIP_TRY(launch_fill(p->sync, SYNC_WORDS, 0u, p->stream));
+  if (p->cfg.flags & TILES_POISON) {
+    // NaN into the rows this launch writes: a read before the write would surface as NaN
+    const int nblk = hp.s.n_layers * hp.s.n_kv;
+    const int64_t stride = kv->capacity * hp.s.hd, first = kv->length * hp.s.hd, count = (int64_t)n_steps * hp.s.hd;
+    HIP_TRY(launch_fill_blocks(a.kv_k + first, nblk, stride, count, 0x7fc0, p->stream));
+    HIP_TRY(launch_fill_blocks(a.kv_v + first, nblk, stride, count, 0x7fc0, p->stream));
+  }
   void* args[] = {&a};
   HIP_TRY(hipLaunchCooperativeKernel(p->kernel, dim3(hp.W), dim3(BLOCK_THREADS), args, hp.lds_bytes, p->stream));
   kv->length += n_steps;
@@ -439,7 +440,7 @@ int tiles_plan_status(tiles_plan_t* p) {
   HIP_TRY(hipMemcpy(&status, p->sync + SYNC_STATUS_WORD, 4, hipMemcpyDeviceToHost));
   if (status != 0) {
     HIP_TRY(hipMemset(p->sync, 0, p->sync_bytes));
-    return set_err(TILES_E_KERNEL, "device barrier watchdog expired in the last launch");
+    return set_err(TILES_E_KERNEL, "a wait's watchdog expired in the last launch");
   }
   return TILES_OK;
 }

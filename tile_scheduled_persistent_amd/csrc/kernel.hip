@@ -1,23 +1,35 @@
 // The persistent tile worker for gfx950 (CDNA4).
 //
 // One workgroup per compute unit executes the static per-step schedule built by the
-// host planner: for every decoded token, for every wave, run this worker's tile (if
-// any), then wait at a grid barrier.  The kernel makes no scheduling decision of its
-// own ("Tiles: Scheduling LLM Decoding as a Graph of Tiles", intro): tiles, workers,
+// host planner: for every decoded token, for every wave, gather the tile's inputs, run
+// the tile (if any) and publish its outputs.  The kernel makes no scheduling decision of
+// its own ("Tiles: Scheduling LLM Decoding as a Graph of Tiles", intro): tiles, workers,
 // wave order and split boundaries are all fixed by the plan and the attended length.
 //
+// Synchronisation between waves is carried by the data itself.  Every FP32 value a tile
+// publishes for other workers holds the step's parity in the lowest mantissa bit (the
+// value consumers use is the published one with that bit cleared); consumers poll the
+// producer wave's output buffer with device-coherent 16-byte loads until every element
+// they need shows the current parity.  One memory round trip thus both signals and moves
+// the data: there is no grid barrier, no flag and no wait for store completion on the
+// critical path.  Each wave has its own output buffer, written once per step; a worker can
+// only write step s+1 of a buffer after every worker has consumed step s of it (every
+// wave's inputs depend on all workers' outputs of the previous waves), so one parity bit
+// separates the generations.  The buffers are filled with a quiet NaN of parity 0 before
+// every launch; step 0 publishes parity 1.
+//
 // Workgroup organisation (512 threads = 8 wavefronts):
-//   * wavefront 0 is the control wave: it stages each tile's input vector in LDS
-//     (folding RMSNorm, the embedding lookup, the split merge, q/k norm, RoPE and the
-//     KV write), runs the epilogues (residual add, SwiGLU, partial argmax), performs
-//     every global store and takes part in the grid barrier;
-//   * wavefronts 1..7 are compute waves.  Each streams its share of the worker's packed
-//     weights through its own LDS ring with direct-to-LDS 16-byte loads
-//     (global_load_lds_dwordx4).  The ring is refilled in consumption order across
-//     wave boundaries, so while the workgroup waits at a grid barrier the weights of
-//     the next tiles keep arriving: weights do not depend on activations, only the dot
-//     products do (the Tiles page credits this prefetch idea to the megakernel it
-//     builds on).
+//   * all eight wavefronts share the input gather of every wave (each polls its share of
+//     the 16-byte units) and the LDS-only prologue work (norm scale, q/k norm + RoPE,
+//     split merge);
+//   * wavefront 0 is the control wave: it runs the epilogues (residual add, SwiGLU,
+//     partial argmax), the KV write and every global store;
+//   * wavefronts 1..7 are compute waves: each streams its share of the worker's packed
+//     weights into registers (16-byte loads, double-buffered) and, before a tile's last
+//     batch is consumed, issues the loads of its next GEMV tile, so those bytes arrive
+//     while the workgroup gathers the next inputs: weights do not depend on activations,
+//     only the dot products do (the Tiles page credits this prefetch idea to the
+//     megakernel it builds on).
 //
 // Tile bodies:
 //   * GEMV tiles: one "chunk" = 64 lanes x 16 B = 512 columns of one row; FP32 dot
@@ -29,13 +41,8 @@
 //     splits are merged in the o_proj prologue or in a wave of their own (roadmap
 //     "Milestones", M5: split-KV decode; "Tried and not kept": no combine inside the
 //     split kernel).
-//   * LM head: logits and a (max, lowest index) partial per worker; after the last
-//     barrier of a step every worker reduces all partials in worker order.
-//
-// Cross-worker data (activations, partials, barrier words, KV rows written in this
-// launch) moves with device-coherent accesses (sc1 cache policy), so no L2 write-back
-// or invalidate is needed; the control wave waits for its stores to complete before it
-// signals the barrier.  Weights are read with plain loads into LDS.
+//   * LM head: logits and a (max, lowest index) partial per worker; the next step's
+//     first wave reduces all partials in worker order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,7 +52,6 @@ namespace tiles {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int SC1 = 16;  // buffer-instruction cache policy bit: device-coherent access
 
@@ -53,54 +59,62 @@ constexpr int SC1 = 16;  // buffer-instruction cache policy bit: device-coherent
 // coherent memory helpers
 // ---------------------------------------------------------------------------
 
-__device__ inline uint32_t ld_u32(const uint32_t* p) {
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void st_u32(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline float ld_f32(const float* p) {
-  return __uint_as_float(ld_u32(reinterpret_cast<const uint32_t*>(p)));
-}
-__device__ inline void st_f32(float* p, float v) { st_u32(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
-__device__ inline void st_u64(uint64_t* p, uint64_t v) {
+__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Buffer descriptor over a scratch array (byte offsets < 4 GB).  Device-coherent buffer
 // loads through it are plain (non-atomic) loads the compiler can issue back to back.
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0xffffffffu, 0x00020000);
 }
-__device__ inline u32x4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+__device__ __forceinline__ u32x4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, SC1);
-}
-__device__ inline f32x4 as_f32x4(u32x4 u) {
-  return f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
 }
 #define COMPILER_FENCE() asm volatile("" ::: "memory")
 
-__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // Round-to-nearest-even FP32 -> BF16 (NaN kept quiet).
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
-__device__ inline float bf16_round(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
+__device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
+
+// ---------------------------------------------------------------------------
+// tagged data: parity in the lowest mantissa bit
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t step_parity(int step) { return (uint32_t)((step + 1) & 1); }
+// the value every consumer (and the producer itself) uses
+__device__ __forceinline__ float tag_clear(float v) { return __uint_as_float(__float_as_uint(v) & ~1u); }
+__device__ __forceinline__ void publish(uint32_t* buf, int64_t i, float v, uint32_t par) {
+  st_u32(buf + i, (__float_as_uint(v) & ~1u) | par);
+}
+__device__ __forceinline__ bool unit_ready(const u32x4 v, uint32_t par) {
+  return par ? ((v.x & v.y & v.z & v.w) & 1u) != 0 : ((v.x | v.y | v.z | v.w) & 1u) == 0;
+}
+__device__ __forceinline__ f32x4 unit_values(const u32x4 v) {
+  return f32x4{__uint_as_float(v.x & ~1u), __uint_as_float(v.y & ~1u), __uint_as_float(v.z & ~1u),
+               __uint_as_float(v.w & ~1u)};
+}
 
 // ---------------------------------------------------------------------------
 // wavefront reductions (DPP butterflies; every lane ends with the same value)
 // ---------------------------------------------------------------------------
 
 template <int CTRL>
-__device__ inline float dpp(float v) {
+__device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
@@ -108,18 +122,18 @@ constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within 16
 
-__device__ inline float sum8(float v) {
+__device__ __forceinline__ float sum8(float v) {
   v += dpp<DPP_XOR1>(v);
   v += dpp<DPP_XOR2>(v);
   v += dpp<DPP_HALF_MIRROR>(v);
   return v;
 }
-__device__ inline float sum16(float v) {
+__device__ __forceinline__ float sum16(float v) {
   v = sum8(v);
   v += dpp<DPP_MIRROR>(v);
   return v;
 }
-__device__ inline float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
   v = sum16(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
@@ -129,42 +143,223 @@ __device__ inline float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout (dynamic): vec | part | small | segs.
-// small[] words written by the control wave before barrier A of every wave:
-constexpr int SM_DONE = 0;   // int: no more waves (end of launch or abort)
-constexpr int SM_KIND = 1;   // int: tile kind
-constexpr int SM_ROW0 = 2;   // int
-constexpr int SM_NROWS = 3;  // int
-constexpr int SM_LAYER = 4;  // int
-constexpr int SM_C = 5;      // int: chunks per GEMV row
-constexpr int SM_POS = 6;    // int: position of the current step
+// LDS layout (dynamic): vec | part | xres | small | segs.
+//   vec   GEMV input vector (or the raw q/k/v of an attention tile)
+//   part  GEMV row partials, attention work areas, gathered split partials
+//   xres  the residual stream x as last gathered (read by the o_proj / down epilogues)
+//   small per-wave words: the abort flag and the per-wavefront sums of squares
 // ---------------------------------------------------------------------------
+constexpr int SM_ABORT = 0;  // int: some wavefront gave up waiting (all leave after barrier P)
+constexpr int SM_SS = 8;     // float[NWAVES]: sums of squares of each wavefront's share of x
 
 struct Lds {
   float* vec;
   float* part;
+  float* xres;
   float* small;
   SegDesc* segs;
 };
 
-__device__ inline bool is_gemv(int kind) {
+__device__ __forceinline__ bool is_gemv(int kind) {
   return kind == KIND_QKV || kind == KIND_O || kind == KIND_GU || kind == KIND_DOWN || kind == KIND_LM;
 }
 // chunk range of compute wave c over n chunks
-__device__ inline int chunk_lo(int n, int c) { return (int)(((int64_t)n * c) / NCOMP); }
+__device__ __forceinline__ int chunk_lo(int n, int c) { return (int)(((int64_t)n * c) / NCOMP); }
+
+// ---------------------------------------------------------------------------
+// waiting: every poll loop is bounded (watchdog) and leaves when any worker has aborted
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool watch_tick(const KernelArgs& a, uint32_t& spins, int lane) {
+  ++spins;
+  if ((spins & 31) == 0) {
+    if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) return true;
+    if (spins > a.spin_limit) {
+      if (lane == 0) {
+        st_u32(a.sync + SYNC_STATUS_WORD, 1u);
+        st_u32(a.sync + SYNC_ABORT_WORD, 1u);
+      }
+      return true;
+    }
+  }
+  return false;
+}
+
+// Poll-gather `nunits` 16-byte units of tagged floats.  Unit u of the gathered vector sits at
+// unit map(u) of `src`; the units are dealt to `nslots` wavefronts, this one taking
+// u = (i * nslots + slot) * 64 + lane.  prep(i, u) runs once per owned unit before polling
+// (to issue independent loads early), sink(i, u, x) once the unit shows parity `par`.
+// Only units not yet seen are re-read.  Returns true when the wait was abandoned.
+template <int GB, typename Map, typename Prep, typename Sink>
+__device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src, int nunits, int slot, int nslots, uint32_t par,
+                       int lane, Map map, Prep prep, Sink sink) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(src);
+  for (int base = 0; base < nunits; base += GB * nslots * 64) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int i = 0; i < GB; ++i) {
+      const int u = base + (i * nslots + slot) * 64 + lane;
+      if (u < nunits) {
+        pending |= 1u << i;
+        prep(i, u);
+      }
+    }
+    uint32_t spins = 0;
+    for (;;) {
+      u32x4 v[GB];
+      COMPILER_FENCE();
+#pragma unroll
+      for (int i = 0; i < GB; ++i) {
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        if ((pending >> i) & 1u) v[i] = cld4(r, (uint32_t)map(base + (i * nslots + slot) * 64 + lane) * 16u);
+      }
+      COMPILER_FENCE();
+#pragma unroll
+      for (int i = 0; i < GB; ++i) {
+        if (((pending >> i) & 1u) && unit_ready(v[i], par)) {
+          sink(i, base + (i * nslots + slot) * 64 + lane, unit_values(v[i]));
+          pending &= ~(1u << i);
+        }
+      }
+      if (__all(pending == 0)) break;
+      if (watch_tick(a, spins, lane)) return true;
+    }
+  }
+  return false;
+}
+
+constexpr int GATHER_UNITS = 8;  // units per lane per polling pass (8 wavefronts x 64 lanes x 8 = 16384 floats)
+
+struct Identity {
+  __device__ int operator()(int u) const { return u; }
+};
+struct NoPrep {
+  __device__ void operator()(int, int) const {}
+};
+
+// x (n floats, tagged) -> xres = x, vec = x * gain, and this wavefront's sum of squares of its share
+__device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, const uint32_t* src, int n, const uint16_t* gain,
+                            int slot, int lane, uint32_t par, float& ss) {
+  uint2 gv[GATHER_UNITS];
+  float s = 0.f;
+  const bool ab = gather<GATHER_UNITS>(
+      a, src, n / 4, slot, NWAVES, par, lane, Identity{},
+      [&](int i, int u) { gv[i] = *reinterpret_cast<const uint2*>(gain + u * 4); },
+      [&](int i, int u, const f32x4 x) {
+        *reinterpret_cast<f32x4*>(L.xres + u * 4) = x;
+        const f32x4 v = {x.x * bf16_lo(gv[i].x), x.y * bf16_hi(gv[i].x), x.z * bf16_lo(gv[i].y), x.w * bf16_hi(gv[i].y)};
+        *reinterpret_cast<f32x4*>(L.vec + u * 4) = v;
+        s += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      });
+  ss = wave_sum(s);
+  return ab;
+}
+
+// plain tagged vector -> dst
+__device__ __forceinline__ bool gather_plain(const KernelArgs& a, float* dst, const uint32_t* src, int n, int slot, int lane,
+                             uint32_t par) {
+  return gather<GATHER_UNITS>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
+                              [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(dst + u * 4) = x; });
+}
+
+// embedding row of `tok` (BF16, exact in FP32) -> xres, vec = x * gain; returns the sum of squares
+__device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds& L, int tok, const uint16_t* gain, int lane) {
+  const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)tok * a.embed_stride);
+  constexpr int B = 8;
+  float ss = 0.f;
+  for (int base = 0; base < a.H; base += B * 256) {
+    uint2 ev[B], gv[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      ev[u] = uint2{0u, 0u};
+      gv[u] = uint2{0u, 0u};
+      if (i < a.H) {
+        ev[u] = *reinterpret_cast<const uint2*>(erow + i);
+        gv[u] = *reinterpret_cast<const uint2*>(gain + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int i = base + u * 256 + lane * 4;
+      if (i < a.H) {
+        const f32x4 x = {bf16_lo(ev[u].x), bf16_hi(ev[u].x), bf16_lo(ev[u].y), bf16_hi(ev[u].y)};
+        *reinterpret_cast<f32x4*>(L.xres + i) = x;
+        const f32x4 v = {x.x * bf16_lo(gv[u].x), x.y * bf16_hi(gv[u].x), x.z * bf16_lo(gv[u].y), x.w * bf16_hi(gv[u].y)};
+        *reinterpret_cast<f32x4*>(L.vec + i) = v;
+        ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      }
+    }
+  }
+  return wave_sum(ss);
+}
+
+// Next token: reduce the W LM-head partials (value, index | parity << 31) of the step with
+// parity `par`, greater value first, lower index on ties.  Returns true when abandoned.
+__device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint32_t par, int& tok) {
+  constexpr int B = 4;  // up to 4 x 128 workers
+  const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
+  float best = -INFINITY;
+  int bidx = 0x7fffffff;
+  uint32_t pending = 0;
+#pragma unroll
+  for (int u = 0; u < B; ++u)
+    if (u * 128 + lane * 2 < a.W) pending |= 1u << u;
+  uint32_t spins = 0;
+  for (;;) {
+    u32x4 pv[B];
+    COMPILER_FENCE();
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      pv[u] = u32x4{0u, 0u, 0u, 0u};
+      if ((pending >> u) & 1u) pv[u] = cld4(r, (uint32_t)(u * 128 + lane * 2) * 8u);
+    }
+    COMPILER_FENCE();
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (!((pending >> u) & 1u)) continue;
+      const int w = u * 128 + lane * 2;
+      const bool two = w + 1 < a.W;
+      const bool ok = (pv[u].y >> 31) == par && (!two || (pv[u].w >> 31) == par);
+      if (!ok) continue;
+      pending &= ~(1u << u);
+      for (int e = 0; e < (two ? 2 : 1); ++e) {
+        const float v = __uint_as_float(e ? pv[u].z : pv[u].x);
+        const int ix = (int)((e ? pv[u].w : pv[u].y) & 0x7fffffffu);
+        if (v > best || (v == best && ix < bidx)) {
+          best = v;
+          bidx = ix;
+        }
+      }
+    }
+    if (__all(pending == 0)) break;
+    if (watch_tick(a, spins, lane)) return true;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bidx, off);
+    if (ov > best || (ov == best && oi < bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+  if (bidx < 0 || bidx >= a.V) bidx = 0;  // only reachable with non-finite logits
+  tok = bidx;
+  return false;
+}
 
 // ---------------------------------------------------------------------------
 // compute wave: weight streaming.  Each compute wave reads its share of a GEMV block (a
 // contiguous chunk range) with 16-byte loads into registers, double-buffered in batches of
 // STREAM_BATCH chunks.  Before a tile's last batch is consumed, the wave issues the loads of
 // the first PREFETCH_CHUNKS chunks of its next GEMV tile, so those bytes arrive while the
-// workgroup goes through the epilogue, the grid barrier and the next prologue.
+// workgroup publishes this tile's outputs and gathers the next inputs.
 // ---------------------------------------------------------------------------
 
 constexpr int STREAM_BATCH = 4;
 constexpr int PREFETCH_CHUNKS = 12;  // register budget: 8 are used when a KV head serves 3-4 query heads
 
-__device__ inline float dot8(const u32x4 w, const float* v) {
+__device__ __forceinline__ float dot8(const u32x4 w, const float* v) {
   const f32x4 v0 = *reinterpret_cast<const f32x4*>(v);
   const f32x4 v1 = *reinterpret_cast<const f32x4*>(v + 4);
   float s0 = bf16_lo(w.x) * v0.x;
@@ -186,7 +381,7 @@ struct Range {
   int64_t base;  // byte offset of the block's first chunk
 };
 
-__device__ inline Range block_range(const SegDesc& s, int k, int r0, int block_rows, int c) {
+__device__ __forceinline__ Range block_range(const SegDesc& s, int k, int r0, int block_rows, int c) {
   Range r;
   r.k = k;
   r.C = s.chunks_per_row;
@@ -200,7 +395,7 @@ __device__ inline Range block_range(const SegDesc& s, int k, int r0, int block_r
 
 // First block of the next GEMV wave after `k` (wrapping into the next step) in which compute
 // wave c has chunks; k = -1 when there is none.
-__device__ inline Range next_gemv(const SegDesc* segs, int n_waves, int k, int block_rows, int c) {
+__device__ __forceinline__ Range next_gemv(const SegDesc* segs, int n_waves, int k, int block_rows, int c) {
   for (int d = 1; d <= n_waves; ++d) {
     const int kk = (k + d) % n_waves;
     if (segs[kk].rows == 0) continue;
@@ -223,7 +418,7 @@ struct Prefetch {
 };
 
 template <int PF>
-__device__ inline void issue_prefetch(Prefetch<PF>& pf, const Range& r, const uint8_t* packed, int lane) {
+__device__ __forceinline__ void issue_prefetch(Prefetch<PF>& pf, const Range& r, const uint8_t* packed, int lane) {
   pf.k = r.k;
   pf.n = r.k < 0 ? 0 : min(PF, r.ihi - r.i);
   const u32x4* g = reinterpret_cast<const u32x4*>(packed + r.base) + (int64_t)r.i * 64 + lane;
@@ -236,7 +431,7 @@ __device__ inline void issue_prefetch(Prefetch<PF>& pf, const Range& r, const ui
 // Per-row partial sums go to part[row * NCOMP + c].  When `refill` is set, the loads of the next
 // tile's prefetch are issued as early as the current tile allows.
 template <int PF>
-__device__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane, Prefetch<PF>& pf,
+__device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane, Prefetch<PF>& pf,
                              bool use_pf, bool refill, const Range& nxt) {
   const int C = r.C;
   int i = r.i;
@@ -296,7 +491,7 @@ __device__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r
 }
 
 // total of row r of a block: partials of the compute waves whose ranges touch it, in order
-__device__ inline float row_total(const Lds& L, int nr, int C, int r) {
+__device__ __forceinline__ float row_total(const Lds& L, int nr, int C, int r) {
   const int n = nr * C;
   const int first = r * C, last = r * C + C - 1;
   float s = 0.f;
@@ -309,81 +504,23 @@ __device__ inline float row_total(const Lds& L, int nr, int C, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// control wave: prologues
+// attention
 // ---------------------------------------------------------------------------
 
-// Coherent copy of n floats (n % 4 == 0) from a scratch vector into LDS, zero-padded to npad;
-// loads are issued in batches of 16 per lane before any is consumed.
-__device__ void cw_load_vec(float* dst, const float* src, int n, int npad, int lane) {
-  constexpr int B = 16;
-  const __amdgpu_buffer_rsrc_t r = rsrc(src);
-  COMPILER_FENCE();
-  for (int base = 0; base < npad; base += B * 256) {
-    u32x4 v[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + lane * 4;
-      v[u] = i < n ? cld4(r, (uint32_t)i * 4) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + lane * 4;
-      if (i < npad) *reinterpret_cast<f32x4*>(dst + i) = as_f32x4(v[u]);
-    }
-  }
-  COMPILER_FENCE();
-}
+// Split partial record of one query head: m, l, acc[HD], two pad words (16-byte units).
+template <int HD>
+constexpr int pstride() { return HD + 4; }
 
-// RMSNorm prologue with the scale folded out: vec[i] = src[i] * gain[i] (i < n), vec[n..npad) = 0,
-// and the return value rs = 1 / sqrt(mean(src^2) + eps) multiplies the GEMV results instead
-// (W (rs x * g) = rs W (x * g)).  src is an FP32 device-coherent vector or a BF16 embedding
-// row; the source and gain loads of a batch are issued together.
-__device__ float cw_norm(const Lds& L, int lane, const float* src_f32, const uint16_t* src_bf16, const uint16_t* gain,
-                         int n, int npad, float eps) {
-  constexpr int B = 8;
-  const __amdgpu_buffer_rsrc_t r = rsrc(src_f32 ? (const void*)src_f32 : (const void*)src_bf16);
-  float ss = 0.f;
-  COMPILER_FENCE();
-  for (int base = 0; base < npad; base += B * 256) {
-    u32x4 xv[B];
-    uint2 gv[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + lane * 4;
-      xv[u] = u32x4{0u, 0u, 0u, 0u};
-      gv[u] = uint2{0u, 0u};
-      if (i < n) {
-        if (src_f32) {
-          xv[u] = cld4(r, (uint32_t)i * 4);
-        } else {
-          const uint2 e = *reinterpret_cast<const uint2*>(src_bf16 + i);
-          xv[u] = u32x4{e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
-        }
-        gv[u] = *reinterpret_cast<const uint2*>(gain + i);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int i = base + u * 256 + lane * 4;
-      const f32x4 x = as_f32x4(xv[u]);
-      ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-      const f32x4 v = {x.x * bf16_lo(gv[u].x), x.y * bf16_hi(gv[u].x), x.z * bf16_lo(gv[u].y), x.w * bf16_hi(gv[u].y)};
-      if (i < npad) *reinterpret_cast<f32x4*>(L.vec + i) = v;
-    }
-  }
-  COMPILER_FENCE();
-  const float tot = wave_sum(ss);
-  return 1.0f / sqrtf(tot / (float)n + eps);
-}
-
-// merge the S splits of one query head (Ph -> [S][HD + 2]) for output dim d, fixed split order
-__device__ inline float merge_splits(const float* Ph, int S, int HD, int d) {
+// merge the S splits of one query head (Ph -> [S][HD + 4]) for output dim d, fixed split order
+template <int HD>
+__device__ __forceinline__ float merge_splits(const float* Ph, int S, int d) {
+  constexpr int PS = pstride<HD>();
   float mm = -INFINITY;
-  for (int s = 0; s < S; ++s) mm = fmaxf(mm, Ph[s * (HD + 2)]);
+  for (int s = 0; s < S; ++s) mm = fmaxf(mm, Ph[s * PS]);
   if (mm == -INFINITY) return 0.f;
   float ll = 0.f, aa = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float* st = Ph + s * (HD + 2);
+    const float* st = Ph + s * PS;
     if (st[1] == 0.f) continue;
     const float f = __builtin_amdgcn_exp2f(st[0] - mm);
     ll += f * st[1];
@@ -394,41 +531,30 @@ __device__ inline float merge_splits(const float* Ph, int S, int HD, int d) {
 
 // Attention tile LDS layout (inside `part`): q[G][HD] (normed, roped, scaled to the base-2
 // domain) | kc[HD] (normed, roped, BF16-rounded) | vc[HD] (BF16-rounded) | compute-wave states
-// [NCOMP][G][HD + 2] | merged partial [G][HD + 2].  The raw q/k/v are staged in `vec`.
+// [NCOMP][G][HD + 4] | merged partial [G][HD + 4].  The raw q/k/v are gathered into `vec`.
 template <int HD, int G>
-__device__ inline float* attn_ws(const Lds& L) { return L.part + G * HD + 2 * HD; }
+__device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + G * HD + 2 * HD; }
 template <int HD, int G>
-__device__ inline float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * (HD + 2); }
+__device__ __forceinline__ float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * pstride<HD>(); }
 
-// control wave, before barrier P: raw q (G heads), k, v of KV group g into vec (one batch of loads)
+// all wavefronts: raw q (G heads), k, v of KV group g into vec from the QKV wave's output
 template <int HD, int G>
-__device__ void cw_attn_load(const KernelArgs& a, const Lds& L, int lane, int g) {
-  constexpr int N = (G + 2) * HD;
-  constexpr int B = (N + 255) / 256;
-  const __amdgpu_buffer_rsrc_t r = rsrc(a.qkv);
-  const int qbase = g * G * HD;
-  const int kbase = a.n_heads * HD + g * HD;
-  const int vbase = a.n_heads * HD + a.n_kv * HD + g * HD;
-  COMPILER_FENCE();
-  u32x4 v[B];
-#pragma unroll
-  for (int u = 0; u < B; ++u) {
-    const int i = u * 256 + lane * 4;
-    const int src = i < G * HD ? qbase + i : i < (G + 1) * HD ? kbase + (i - G * HD) : vbase + (i - (G + 1) * HD);
-    v[u] = i < N ? cld4(r, (uint32_t)src * 4) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int u = 0; u < B; ++u) {
-    const int i = u * 256 + lane * 4;
-    if (i < N) *reinterpret_cast<f32x4*>(L.vec + i) = as_f32x4(v[u]);
-  }
-  COMPILER_FENCE();
+__device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, const uint32_t* src, int g, int slot, int lane,
+                           uint32_t par) {
+  constexpr int NQ = G * HD / 4, NK = HD / 4;
+  const int q0 = g * G * HD / 4;
+  const int k0 = (a.n_heads * HD + g * HD) / 4;
+  const int v0 = (a.n_heads * HD + a.n_kv * HD + g * HD) / 4;
+  return gather<2>(
+      a, src, NQ + 2 * NK, slot, NWAVES, par, lane,
+      [&](int u) { return u < NQ ? q0 + u : u < NQ + NK ? k0 + (u - NQ) : v0 + (u - NQ - NK); }, NoPrep{},
+      [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(L.vec + u * 4) = x; });
 }
 
 // all wavefronts, between barriers P and A: wave u < G normalises (optional) and rotates query
 // head u, wave G the key; wave G + 1 rounds the value.  LDS only (plus read-only tables).
 template <int HD, int G>
-__device__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos) {
+__device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos) {
   constexpr int HALF = HD / 2;
   float* q = L.part;
   float* kc = q + G * HD;
@@ -471,7 +597,7 @@ __device__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index,
 
 // control wave, after barrier A: the split holding the current position writes its K/V row
 template <int HD, int G>
-__device__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
+__device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
                                  int64_t L_att) {
   const float* kc = L.part + G * HD;
   const float* vc = kc + HD;
@@ -488,19 +614,17 @@ __device__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, in
   }
 }
 
-// ---------------------------------------------------------------------------
-// compute wave: one share of an attention split
-// ---------------------------------------------------------------------------
-
 template <int HD>
-__device__ inline void unpack8(const u32x4 w, float* f) {
+__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
   f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
+// compute wave: one share of an attention split
 template <int HD, int G>
-__device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int lane, int layer, int g, int sp,
+__device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int lane, int layer, int g, int sp,
                                   int64_t L_att) {
+  constexpr int PS = pstride<HD>();
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
@@ -623,7 +747,7 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
   if (pp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* st = ws + (c * G + h) * (HD + 2);
+      float* st = ws + (c * G + h) * PS;
       if (dseg == 0) {
         st[0] = m[h];
         st[1] = l[h];
@@ -635,16 +759,17 @@ __device__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int 
 }
 
 // all wavefronts, between barriers B and E: merge the compute waves' states in wave order into
-// the tile's partial (m, l, acc) per query head
+// the tile's partial (m, l, acc, pad) per query head
 template <int HD, int G>
-__device__ void attn_merge_phase(const Lds& L, int wave_index, int lane) {
+__device__ __forceinline__ void attn_merge_phase(const Lds& L, int wave_index, int lane) {
+  constexpr int PS = pstride<HD>();
   const float* ws = attn_ws<HD, G>(L);
   float* mrg = attn_merged<HD, G>(L);
   for (int idx = wave_index * 64 + lane; idx < G * HD; idx += BLOCK_THREADS) {
     const int h = idx / HD, d = idx % HD;
     float mm = -INFINITY, ll = 0.f, aa = 0.f;
     for (int c = 0; c < NCOMP; ++c) {
-      const float* st = ws + (c * G + h) * (HD + 2);
+      const float* st = ws + (c * G + h) * PS;
       const float m2 = st[0];
       const float mn = fmaxf(mm, m2);
       if (mn == -INFINITY) continue;
@@ -653,229 +778,211 @@ __device__ void attn_merge_phase(const Lds& L, int wave_index, int lane) {
       aa = aa * f1 + st[2 + d] * f2;
       mm = mn;
     }
-    float* dst = mrg + h * (HD + 2);
+    float* dst = mrg + h * PS;
     if (d == 0) {
       dst[0] = mm;
       dst[1] = ll;
+      dst[HD + 2] = 0.f;
+      dst[HD + 3] = 0.f;
     }
     dst[2 + d] = aa;
   }
 }
 
-// control wave, after barrier E: store the merged partials of query heads g*G .. g*G+G-1, split sp
+// control wave, after barrier E: publish the merged partials of query heads g*G .. g*G+G-1, split sp
 template <int HD, int G>
-__device__ void cw_attn_store(const KernelArgs& a, const Lds& L, int lane, int g, int sp) {
+__device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& L, uint32_t* out, int lane, int g, int sp,
+                                uint32_t par) {
+  constexpr int PS = pstride<HD>();
   const float* mrg = attn_merged<HD, G>(L);
-  for (int idx = lane; idx < G * (HD + 2); idx += 64) {
-    const int h = idx / (HD + 2), e = idx % (HD + 2);
-    st_f32(a.part + ((int64_t)(g * G + h) * a.S + sp) * (HD + 2) + e, mrg[idx]);
-  }
-}
-
-// LDS-only prologue work shared by all eight wavefronts between barriers P and A:
-// merging the split partials into the o_proj input vector.  wave_index in [0, NWAVES).
-template <int HD, int G>
-__device__ inline void prologue_lds_phase(const KernelArgs& a, const Lds& L, int kind, int wave_index, int lane,
-                                          int layer, int pos) {
-  if (kind == KIND_ATTN) {
-    attn_lds_prep<HD, G>(a, L, wave_index, lane, layer, pos);
-  } else if (kind == KIND_O && a.combine_in_o) {
-    const int nq = a.n_heads * HD;
-    for (int i = wave_index * 64 + lane; i < nq; i += BLOCK_THREADS)
-      L.vec[i] = merge_splits(L.part + (i / HD) * a.S * (HD + 2), a.S, HD, i % HD);
+  for (int idx = lane; idx < G * PS; idx += 64) {
+    const int h = idx / PS, e = idx % PS;
+    publish(out, ((int64_t)(g * G + h) * a.S + sp) * PS + e, mrg[idx], par);
   }
 }
 
 // ---------------------------------------------------------------------------
-// grid barrier (control wave): every worker publishes its generation on its own
-// 64-byte line and polls all lines.  A watchdog bounds every wait.
-// ---------------------------------------------------------------------------
-
-// Spin until every lane's predicate holds; false = released, true = aborted (watchdog or peer abort).
-template <typename Ready>
-__device__ inline bool cw_spin(const KernelArgs& a, int lane, Ready ready) {
-  uint32_t spins = 0;
-  for (;;) {
-    if (__all(ready())) return false;
-    if ((++spins & 63) == 0) {
-      if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) return true;
-      if (spins > a.spin_limit) {
-        if (lane == 0) {
-          st_u32(a.sync + SYNC_STATUS_WORD, 1u);
-          st_u32(a.sync + SYNC_ABORT_WORD, 1u);
-        }
-        return true;
-      }
-    }
-  }
-}
-
-__device__ bool cw_grid_barrier(const KernelArgs& a, int bid, int lane, uint32_t gen) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
-  uint32_t* arrive = a.sync + SYNC_ARRIVE_BASE;
-  uint32_t* release = arrive + (int64_t)a.W * SYNC_LINE_WORDS;
-  if (lane == 0) st_u32(arrive + bid * SYNC_LINE_WORDS, gen);
-  auto all_arrived = [&]() {
-    bool ok = true;
-    for (int w = lane; w < a.W; w += 64) ok &= (int32_t)(ld_u32(arrive + w * SYNC_LINE_WORDS) - gen) >= 0;
-    return ok;
-  };
-  if (a.barrier_mode == 0) return cw_spin(a, lane, all_arrived);
-  // gather/release: worker 0 waits for every arrival, then writes each worker's release line
-  if (bid == 0) {
-    if (cw_spin(a, lane, all_arrived)) return true;
-    for (int w = lane; w < a.W; w += 64) st_u32(release + w * SYNC_LINE_WORDS, gen);
-  }
-  return cw_spin(a, lane, [&]() { return (int32_t)(ld_u32(release + bid * SYNC_LINE_WORDS) - gen) >= 0; });
-}
-
-// ---------------------------------------------------------------------------
-// control wave main loop
+// the worker loop (all eight wavefronts)
 // ---------------------------------------------------------------------------
 
 template <int HD, int G>
-__device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
-  int* smi = reinterpret_cast<int*>(L.small);
-  uint32_t gen = 0;
+__device__ __forceinline__ void worker_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int block_rows) {
+  constexpr int PS = pstride<HD>();
+  const bool ctl = wave == 0;
+  const int c = wave - 1;  // compute-wave index (compute waves only)
+  volatile int* smi = reinterpret_cast<volatile int*>(L.small);
+  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
+  pf.n = 0;
+  pf.k = -1;
+  if (!ctl) issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
   int tok = a.token0;
-  bool aborted = false;
   const int H = a.H;
-  for (int step = 0; step < a.n_steps && !aborted; ++step) {
+  bool stop = false;
+  for (int step = 0; step < a.n_steps && !stop; ++step) {
+    const uint32_t par = step_parity(step);
     const int pos = a.pos0 + step;
     const int64_t L_att = (int64_t)pos + 1;
-    const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)tok * a.embed_stride);
-    if (a.poison) {
-      const float nan = __uint_as_float(0x7fc00000u);
-      const int64_t gid = (int64_t)bid * 64 + lane, gsz = (int64_t)a.W * 64;
-      for (int64_t i = gid; i < a.qkv_rows; i += gsz) st_f32(a.qkv + i, nan);
-      for (int64_t i = gid; i < (int64_t)a.n_heads * a.S * (HD + 2); i += gsz) st_f32(a.part + i, nan);
-      for (int64_t i = gid; i < (int64_t)a.n_heads * HD; i += gsz) st_f32(a.attn + i, nan);
-      for (int64_t i = gid; i < a.F; i += gsz) st_f32(a.act + i, nan);
-      aborted = cw_grid_barrier(a, bid, lane, ++gen);
-      if (aborted) break;
-    }
     float lm_best = -INFINITY;
     int lm_idx = 0x7fffffff;
-    for (int wv = 0; wv < a.n_waves; ++wv) {
-      const TileDesc t = a.tiles[(int64_t)wv * a.W + bid];
-      const int layer = a.waves[wv].layer;
-      uint64_t t0 = 0;
-      if (a.trace) t0 = wall_clock64();
-      // ---- prologue (global loads by the control wave) ----
-      float rs = 1.0f;  // RMSNorm scale folded out of the input vector, applied to the GEMV results
-      switch (t.kind) {
+    for (int k = 0; k < a.n_waves; ++k) {
+      const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
+      const WaveDesc wd = a.waves[k];
+      const int layer = wd.layer;
+      const uint32_t* in = a.ll + (k > 0 ? a.waves[k - 1].ll_off : 0);
+      uint32_t* out = a.ll + (wd.ll_off >= 0 ? wd.ll_off : 0);
+      uint64_t t0 = 0, t_pro = 0, t_cmp = 0;
+      if (ctl && a.trace) t0 = wall_clock64();
+      // ---- inputs: every wavefront gathers its share ----
+      // Every worker gathers x in the QKV and gate/up waves, tile or not: the o_proj and down
+      // epilogues add their rows to the residual staged there.
+      const int gk = (wd.kind == KIND_QKV || wd.kind == KIND_GU) ? wd.kind : t.kind;
+      bool ab = false;
+      switch (gk) {
         case KIND_QKV:
-          rs = cw_norm(L, lane, layer == 0 ? nullptr : a.x, layer == 0 ? erow : nullptr,
-                       reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].attn_norm), H, t.kpad, a.eps);
-          break;
         case KIND_GU:
-          rs = cw_norm(L, lane, a.x, nullptr, reinterpret_cast<const uint16_t*>(a.packed + a.small[layer].mlp_norm), H,
-                       t.kpad, a.eps);
-          break;
-        case KIND_LM:
-          rs = cw_norm(L, lane, a.x, nullptr, reinterpret_cast<const uint16_t*>(a.packed + a.final_norm_off), H, t.kpad,
-                       a.eps);
-          break;
-        case KIND_O: {
-          const int nq = a.n_heads * HD;
-          if (a.combine_in_o) {
-            // stage all split partials; all wavefronts merge them after barrier P
-            const int np = a.n_heads * a.S * (HD + 2);  // even
-            cw_load_vec(L.part, a.part, np & ~3, np & ~3, lane);
-            for (int i = (np & ~3) + lane; i < np; i += 64) L.part[i] = ld_f32(a.part + i);
-            for (int i = nq + lane; i < t.kpad; i += 64) L.vec[i] = 0.f;
+        case KIND_LM: {
+          const int64_t goff = gk == KIND_QKV ? a.small[layer].attn_norm
+                               : gk == KIND_GU ? a.small[layer].mlp_norm
+                                               : a.final_norm_off;
+          const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
+          float ss = 0.f;
+          if (gk == KIND_QKV && layer == 0) {
+            if (ctl) {
+              if (step > 0) {
+                ab = gather_token(a, lane, step_parity(step - 1), tok);
+                if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+              }
+              if (!ab) ss = stage_embedding(a, L, tok, gain, lane);
+            }
           } else {
-            cw_load_vec(L.vec, a.attn, nq, t.kpad, lane);
+            ab = gather_norm(a, L, in, H, gain, wave, lane, par, ss);
           }
+          for (int i = H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+          if (lane == 0) L.small[SM_SS + wave] = ss;
           break;
         }
+        case KIND_O:
+          if (a.combine_in_o) ab = gather_plain(a, L.part, in, a.n_heads * a.S * PS, wave, lane, par);
+          else ab = gather_plain(a, L.vec, in, a.n_heads * HD, wave, lane, par);
+          for (int i = a.n_heads * HD + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+          break;
         case KIND_DOWN:
-          cw_load_vec(L.vec, a.act, a.F, t.kpad, lane);
+          ab = gather_plain(a, L.vec, in, a.F, wave, lane, par);
+          for (int i = a.F + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
           break;
         case KIND_ATTN:
-          cw_attn_load<HD, G>(a, L, lane, t.row0);
+          ab = gather_qkv<HD, G>(a, L, in, t.row0, wave, lane, par);
+          break;
+        case KIND_COMBINE:
+          ab = gather_plain(a, L.part, in + (int64_t)t.row0 * a.S * PS, a.S * PS, wave, lane, par);
           break;
         default:
           break;
       }
-      uint64_t t_pro = 0, t_cmp = 0;
-      if (a.trace) t_pro = wall_clock64();
-      if (lane == 0) {
-        smi[SM_KIND] = t.kind;
-        smi[SM_ROW0] = t.row0;
-        smi[SM_NROWS] = t.nrows;
-        smi[SM_LAYER] = layer;
-        smi[SM_C] = t.kpad / CHUNK_COLS;
-        smi[SM_POS] = pos;
+      if (ab) smi[SM_ABORT] = 1;
+      __syncthreads();  // P: inputs staged in LDS
+      if (smi[SM_ABORT]) {
+        stop = true;
+        break;
       }
-      __syncthreads();  // P: global inputs staged in LDS
-      prologue_lds_phase<HD, G>(a, L, t.kind, 0, lane, layer, pos);
+      if (ctl && a.trace) t_pro = wall_clock64();
+      // ---- LDS-only prologue work ----
+      float rs = 1.0f;  // RMSNorm scale folded out of the input vector, applied to the GEMV results
+      if (t.kind == KIND_QKV || t.kind == KIND_GU || t.kind == KIND_LM) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) tot += L.small[SM_SS + w];
+        rs = 1.0f / sqrtf(tot / (float)H + a.eps);
+      } else if (t.kind == KIND_ATTN) {
+        attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
+      } else if (t.kind == KIND_O && a.combine_in_o) {
+        const int nq = a.n_heads * HD;
+        for (int i = wave * 64 + lane; i < nq; i += BLOCK_THREADS)
+          L.vec[i] = merge_splits<HD>(L.part + (i / HD) * a.S * PS, a.S, i % HD);
+      } else if (t.kind == KIND_COMBINE) {
+        for (int d = wave * 64 + lane; d < HD; d += BLOCK_THREADS) L.vec[d] = merge_splits<HD>(L.part, a.S, d);
+      }
       __syncthreads();  // A: inputs ready
-      if (t.kind == KIND_ATTN) cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
-      // ---- compute waves run; epilogues ----
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
         const int C = t.kpad / CHUNK_COLS;
+        if (ctl && t.kind == KIND_O) {
+          // KV rows written by this worker earlier in the step must be complete before any
+          // output of this wave is published: later readers of those rows depend on it.
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const SegDesc sd = L.segs[k];
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const int nr = min(block_rows, rows - r0);
+          if (!ctl) {
+            const Range r = block_range(sd, k, r0, block_rows, c);
+            const bool last_block = r0 + block_rows >= rows;
+            const Range nxt = last_block ? next_gemv(L.segs, a.n_waves, k, block_rows, c) : r;
+            if (r.i < r.ihi) {
+              stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, last_block, nxt);
+            } else if (last_block) {
+              issue_prefetch(pf, nxt, a.packed, lane);
+            }
+          }
           __syncthreads();  // B: partials of this block ready
-          if (a.trace && r0 == 0) t_cmp = wall_clock64();
-          switch (t.kind) {
-            case KIND_QKV:
-              for (int r = lane; r < nr; r += 64) st_f32(a.qkv + t.row0 + r0 + r, rs * row_total(L, nr, C, r));
-              break;
-            case KIND_O:
-              for (int r = lane; r < nr; r += 64) {
-                const int j = t.row0 + r0 + r;
-                const float old = layer == 0 ? bf16_to_f32(erow[j]) : ld_f32(a.x + j);
-                st_f32(a.x + j, old + row_total(L, nr, C, r));
-              }
-              break;
-            case KIND_GU:  // interleaved gate/up rows
-              for (int p = lane; p < nr / 2; p += 64) {
-                const float gt = rs * row_total(L, nr, C, 2 * p);
-                const float up = rs * row_total(L, nr, C, 2 * p + 1);
-                st_f32(a.act + t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up);
-              }
-              break;
-            case KIND_DOWN:
-              for (int r = lane; r < nr; r += 64) {
-                const int j = t.row0 + r0 + r;
-                const float nx = ld_f32(a.x + j) + row_total(L, nr, C, r);
-                st_f32(a.x + j, nx);
-                if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = nx;
-              }
-              break;
-            case KIND_LM:
-              for (int r = lane; r < nr; r += 64) {
-                const float v = rs * row_total(L, nr, C, r);
-                const int idx = t.row0 + r0 + r;
-                if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
-                if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
-                  lm_best = v;
-                  lm_idx = idx;
+          if (ctl) {
+            if (a.trace && r0 == 0) t_cmp = wall_clock64();
+            switch (t.kind) {
+              case KIND_QKV:
+                for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * row_total(L, nr, C, r), par);
+                break;
+              case KIND_O:
+                for (int r = lane; r < nr; r += 64) {
+                  const int j = t.row0 + r0 + r;
+                  publish(out, j, L.xres[j] + row_total(L, nr, C, r), par);
                 }
-              }
-              break;
+                break;
+              case KIND_GU:  // interleaved gate/up rows
+                for (int p = lane; p < nr / 2; p += 64) {
+                  const float gt = rs * row_total(L, nr, C, 2 * p);
+                  const float up = rs * row_total(L, nr, C, 2 * p + 1);
+                  publish(out, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
+                }
+                break;
+              case KIND_DOWN:
+                for (int r = lane; r < nr; r += 64) {
+                  const int j = t.row0 + r0 + r;
+                  const float nx = L.xres[j] + row_total(L, nr, C, r);
+                  publish(out, j, nx, par);
+                  if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = tag_clear(nx);
+                }
+                break;
+              case KIND_LM:
+                for (int r = lane; r < nr; r += 64) {
+                  const float v = rs * row_total(L, nr, C, r);
+                  const int idx = t.row0 + r0 + r;
+                  if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
+                  if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
+                    lm_best = v;
+                    lm_idx = idx;
+                  }
+                }
+                break;
+            }
           }
           if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
         }
-      } else {
-        __syncthreads();  // B
-        if (a.trace) t_cmp = wall_clock64();
-        if (t.kind == KIND_ATTN) {
-          attn_merge_phase<HD, G>(L, 0, lane);
-          __syncthreads();  // E: merged partial ready
-          cw_attn_store<HD, G>(a, L, lane, t.row0, t.nrows);
-        } else if (t.kind == KIND_COMBINE) {
-          float* P = L.part;
-          const int np = a.S * (HD + 2);
-          for (int i = lane; i < np; i += 64) P[i] = ld_f32(a.part + (int64_t)t.row0 * np + i);
-          for (int d = lane; d < HD; d += 64) st_f32(a.attn + (int64_t)t.row0 * HD + d, merge_splits(P, a.S, HD, d));
+      } else if (t.kind == KIND_ATTN) {
+        if (ctl) cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
+        else compute_attention<HD, G>(a, L, c, lane, layer, t.row0, t.nrows, L_att);
+        __syncthreads();  // B: compute-wave states ready
+        if (ctl && a.trace) t_cmp = wall_clock64();
+        attn_merge_phase<HD, G>(L, wave, lane);
+        __syncthreads();  // E: merged partial ready
+        if (ctl) cw_attn_publish<HD, G>(a, L, out, lane, t.row0, t.nrows, par);
+      } else if (t.kind == KIND_COMBINE) {
+        if (ctl) {
+          if (a.trace) t_cmp = wall_clock64();
+          for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);
         }
       }
-      if (a.waves[wv].kind == KIND_LM) {
-        // worker partial (max, lowest index); also written by workers without vocabulary rows
+      if (ctl && wd.kind == KIND_LM) {
+        // worker partial (max, lowest index); also published by workers without vocabulary rows
         for (int off = 32; off >= 1; off >>= 1) {
           const float ov = __shfl_xor(lm_best, off);
           const int oi = __shfl_xor(lm_idx, off);
@@ -886,113 +993,23 @@ __device__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lan
         }
         if (lane == 0)
           st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
-                 (uint64_t)__float_as_uint(lm_best) | ((uint64_t)(uint32_t)lm_idx << 32));
+                 (uint64_t)__float_as_uint(lm_best) | ((uint64_t)((uint32_t)lm_idx | (par << 31)) << 32));
       }
-      uint64_t t1 = 0;
-      if (a.trace) t1 = wall_clock64();
-      aborted = cw_grid_barrier(a, bid, lane, ++gen);
-      if (a.trace && lane == 0) {
-        uint64_t* tr = a.trace + (((int64_t)step * a.n_waves + wv) * a.W + bid) * TRACE_WORDS;
+      if (ctl && a.trace && lane == 0) {
+        const uint64_t t1 = wall_clock64();
+        uint64_t* tr = a.trace + (((int64_t)step * a.n_waves + k) * a.W + bid) * TRACE_WORDS;
         tr[0] = t0;
         tr[1] = t_pro;
-        tr[2] = t_cmp;
+        tr[2] = t_cmp ? t_cmp : t_pro;
         tr[3] = t1;
-        tr[4] = wall_clock64();
-      }
-      if (aborted) break;
-    }
-    if (aborted) break;
-    // next token: argmax over all workers' partials, in worker order
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
-    {
-      const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
-      COMPILER_FENCE();
-      for (int base = 0; base < a.W; base += 4 * 128) {  // 2 partials per 16-byte load, 4 loads in flight
-        u32x4 pv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int w = base + u * 128 + lane * 2;
-          pv[u] = w < a.W ? cld4(r, (uint32_t)w * 8) : u32x4{0xff800000u, 0x7fffffffu, 0xff800000u, 0x7fffffffu};
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int w = base + u * 128 + lane * 2;
-          for (int e = 0; e < 2; ++e) {
-            const float v = __uint_as_float(e ? pv[u].z : pv[u].x);
-            const int ix = (int)(e ? pv[u].w : pv[u].y);
-            if (w + e < a.W && (v > best || (v == best && ix < bidx))) {
-              best = v;
-              bidx = ix;
-            }
-          }
-        }
-      }
-      COMPILER_FENCE();
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bidx, off);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
+        tr[4] = t1;
       }
     }
-    if (bidx < 0 || bidx >= a.V) bidx = 0;  // only reachable with non-finite logits
-    tok = bidx;
-    if (bid == 0 && lane == 0) a.out_tokens[step] = bidx;
   }
-  // release the compute waves: one more barrier (their P) with the done flag set
-  if (lane == 0) smi[SM_DONE] = 1;
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// compute wave main loop
-// ---------------------------------------------------------------------------
-
-template <int HD, int G>
-__device__ void compute_loop(const KernelArgs& a, const Lds& L, int c, int lane, int block_rows) {
-  const volatile int* smi = reinterpret_cast<const volatile int*>(L.small);
-  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
-  issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
-  int k = -1;  // schedule wave being executed
-  for (;;) {   // one iteration per wave of every step, until the control wave raises the done flag
-    __syncthreads();  // P
-    if (smi[SM_DONE]) break;
-    k = k + 1 == a.n_waves ? 0 : k + 1;
-    prologue_lds_phase<HD, G>(a, L, smi[SM_KIND], c + 1, lane, smi[SM_LAYER], smi[SM_POS]);
-    __syncthreads();  // A
-    const int kind = smi[SM_KIND];
-    const int row0 = smi[SM_ROW0];
-    const int nrows = smi[SM_NROWS];
-    const int layer = smi[SM_LAYER];
-    const int pos = smi[SM_POS];
-    if (is_gemv(kind)) {
-      const SegDesc sd = L.segs[k];
-      const int rows = sd.rows;
-      for (int r0 = 0; r0 < rows; r0 += block_rows) {
-        const Range r = block_range(sd, k, r0, block_rows, c);
-        const bool last_block = r0 + block_rows >= rows;
-        const Range nxt = last_block ? next_gemv(L.segs, a.n_waves, k, block_rows, c) : r;
-        if (r.i < r.ihi) {
-          stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, last_block, nxt);
-        } else if (last_block) {
-          issue_prefetch(pf, nxt, a.packed, lane);
-        }
-        __syncthreads();                              // B
-        if (r0 + block_rows < rows) __syncthreads();  // C
-      }
-    } else {
-      if (kind == KIND_ATTN) {
-        compute_attention<HD, G>(a, L, c, lane, layer, row0, nrows, (int64_t)pos + 1);
-        __syncthreads();  // B
-        attn_merge_phase<HD, G>(L, c + 1, lane);
-        __syncthreads();  // E
-      } else {
-        __syncthreads();  // B
-      }
-    }
+  // the last step's token
+  if (!stop && ctl && bid == 0) {
+    int last = 0;
+    if (!gather_token(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
   }
 }
 
@@ -1003,7 +1020,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   Lds L;
   L.vec = reinterpret_cast<float*>(lds_raw);
   L.part = L.vec + a.lds_vec_floats;
-  L.small = L.part + a.lds_part_floats;
+  L.xres = L.part + a.lds_part_floats;
+  L.small = L.xres + a.lds_xres_floats;
   L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, bid = blockIdx.x;
   for (int k = tid; k < a.n_waves; k += BLOCK_THREADS) {
@@ -1014,18 +1032,41 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
     s.rows = is_gemv(t.kind) ? (t.kind == KIND_GU ? 2 * t.nrows : t.nrows) : 0;
     L.segs[k] = s;
   }
-  if (tid == 0) reinterpret_cast<int*>(L.small)[SM_DONE] = 0;
+  if (tid == 0) reinterpret_cast<int*>(L.small)[SM_ABORT] = 0;
   __syncthreads();
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G>(a, L, wave - 1, lane, block_rows);
+  worker_loop<HD, G>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
-// weight packing (plan creation): one launch copies every segment.  Rows whose byte counts
-// and addresses are 16-byte multiples move with 16-byte accesses, others with 2-byte ones.
+// launch helpers: buffer fill (before every decode launch) and weight packing (plan creation)
 // ---------------------------------------------------------------------------
 
+__global__ void __launch_bounds__(256) fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream) {
+  const int64_t blocks = (n + 255) / 256;
+  const int grid = blocks < 1024 ? (blocks > 0 ? (int)blocks : 1) : 1024;
+  hipLaunchKernelGGL(fill_u32, dim3(grid), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
+// `nblk` blocks of `count` 16-bit words, `stride` words apart (debug poison of KV rows).
+__global__ void __launch_bounds__(256) fill_u16_blocks(uint16_t* __restrict__ p, int64_t stride, int64_t count, uint16_t v) {
+  uint16_t* b = p + (int64_t)blockIdx.x * stride;
+  for (int64_t i = threadIdx.x; i < count; i += 256) b[i] = v;
+}
+
+hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream) {
+  if (nblk < 1 || count < 1) return hipSuccess;
+  hipLaunchKernelGGL(fill_u16_blocks, dim3(nblk), dim3(256), 0, stream, p, stride, count, v);
+  return hipGetLastError();
+}
+
+// One launch copies every segment.  Rows whose byte counts and addresses are 16-byte multiples
+// move with 16-byte accesses, others with 2-byte ones.
 __global__ void __launch_bounds__(256) pack_weights(const PackSeg* __restrict__ segs, int nseg, uint8_t* __restrict__ dst) {
   for (int sidx = blockIdx.x; sidx < nseg; sidx += gridDim.x) {
     const PackSeg g = segs[sidx];

@@ -27,8 +27,8 @@ constexpr int CHUNK_COLS = 512;
 constexpr int CHUNK_BYTES = 1024;
 constexpr int BLOCK_THREADS = 512;
 constexpr int NWAVES = BLOCK_THREADS / 64;
-// Wavefront 0 of every workgroup is the control wave (prologues, epilogues, stores, grid
-// barrier); wavefronts 1..NCOMP stream weights into registers and compute.
+// Wavefront 0 of every workgroup is the control wave (epilogues and global stores);
+// wavefronts 1..NCOMP stream weights into registers and compute.  All eight gather inputs.
 constexpr int NCOMP = NWAVES - 1;
 constexpr int SMALL_FLOATS = 1024;                          // LDS scratch for reductions / broadcasts
 struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the weight prefetch)
@@ -53,7 +53,7 @@ struct WaveDesc {   // 16 bytes
   int32_t kind;
   int32_t layer;    // -1 for the LM head
   int32_t max_rows; // largest GEMV row count of any tile in the wave (sizes the LDS partial area)
-  int32_t pad;
+  int32_t ll_off;   // first word of the wave's tagged output buffer (-1: the LM head, see lmpart)
 };
 
 // Offsets (bytes) of the per-layer norm gains inside the packed buffer.
@@ -61,18 +61,18 @@ struct LayerSmall {
   int64_t attn_norm, mlp_norm, q_norm, k_norm;
 };
 
-// Sync area layout (uint32 words).  Each worker owns one 64-byte line of arrivals.
-constexpr int SYNC_LINE_WORDS = 16;
-constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = barrier watchdog)
+// Sync area layout (uint32 words, one 64-byte line each).
+constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = a wait's watchdog expired)
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
-constexpr int SYNC_ARRIVE_BASE = 64;     // arrive[w] at SYNC_ARRIVE_BASE + w * SYNC_LINE_WORDS
-// release[w] (gather/release barrier) at SYNC_ARRIVE_BASE + (W + w) * SYNC_LINE_WORDS
+constexpr int SYNC_WORDS = 32;
 
-// In-kernel trace record per (step, wave, worker): wave start, input staged, compute done,
-// barrier arrival, barrier release (100 MHz wall clock).
+// In-kernel trace record per (step, wave, worker): wave start, inputs staged, compute done,
+// outputs published, (same again; kept for the record layout) -- 100 MHz wall clock.
 constexpr int TRACE_WORDS = 5;
 
-inline int64_t sync_words(int W) { return SYNC_ARRIVE_BASE + 2 * (int64_t)W * SYNC_LINE_WORDS; }
+// Tagged-data buffers are filled with this word before every launch: a quiet NaN whose
+// parity bit (bit 0) is 0, so that step 0 (parity 1) never mistakes it for a value.
+constexpr uint32_t TAG_FILL = 0x7fc00000u;
 
 // One weight-packing copy executed on the device: `rows` rows of `row_bytes` bytes from
 // `src` (rows `src_pitch` apart) to packed + dst_off (rows `dst_pitch` apart).
@@ -94,31 +94,26 @@ struct KernelArgs {
   int64_t final_norm_off;    // bytes into packed
   int64_t embed_off;         // bytes into packed: embedding row 0
   int64_t embed_stride;      // bytes between embedding rows
-  // per-step scratch (FP32 unless noted)
-  float* x;                  // [H] residual stream
-  float* qkv;                // [(n_heads + 2 n_kv_heads) * head_dim]
-  float* part;               // [n_heads][S][head_dim + 2] split partials (m, l, acc...)
-  float* attn;               // [n_heads * head_dim] combined attention output
-  float* act;                // [F] SwiGLU output
-  uint32_t* lmpart;          // [W][2] (max logit bits, index)
-  uint32_t* sync;            // sync words
+  // tagged-data buffers (see the kernel): one per wave, and the LM-head partials
+  uint32_t* ll;              // FP32 values, parity in bit 0; wave k's output at ll + waves[k].ll_off
+  uint32_t* lmpart;          // [W][2] (max logit bits, index | parity << 31)
+  uint32_t* sync;            // SYNC_WORDS status / abort words
   uint16_t* kv_k;            // BF16 cache
   uint16_t* kv_v;
   int64_t kv_cap;
   int32_t* out_tokens;
   float* out_logits;         // may be null
   float* dbg_hidden;         // [n_steps][n_layers][H] or null
-  uint64_t* trace;           // [n_steps][n_waves][W][3] or null
+  uint64_t* trace;           // [n_steps][n_waves][W][TRACE_WORDS] or null
   int32_t token0, pos0, n_steps, n_waves;
   int32_t W, n_layers, H, Hpad, n_heads, n_kv, head_dim, F, Fpad, V, qkv_rows, Qpad, S;
   int32_t combine_in_o;      // 1: the o_proj prologue merges the splits
-  int32_t poison;
-  int32_t barrier_mode;      // 0: every worker polls every arrival line; 1: worker 0 gathers, then releases each worker
   float eps;
   float qscale;              // log2(e) / sqrt(head_dim): scores in the base-2 domain
-  uint32_t spin_limit;       // barrier watchdog (polls)
+  uint32_t spin_limit;       // watchdog of every wait (polls)
   int32_t lds_vec_floats;    // LDS layout
   int32_t lds_part_floats;
+  int32_t lds_xres_floats;
 };
 
 }  // namespace tiles

@@ -5,8 +5,9 @@
 // The planning rules follow "Tiles: Scheduling LLM Decoding as a Graph of Tiles" (intro):
 // a tile is a small range of output rows plus the work that produces it; small operations
 // fold into neighbouring tiles; each tile has a fixed worker, one worker per compute unit;
-// the planner balances the bytes each worker streams and groups tiles into waves separated
-// by grid barriers; the schedule is validated before launch.  The fusions are those of the
+// the planner balances the bytes each worker streams and groups tiles into waves (the pages
+// separate them with grid barriers; here each wave's tagged outputs carry the dependency);
+// the schedule is validated before launch.  The fusions are those of the
 // "M8 so far" table of the TileInfer.jl roadmap (residual add + RMSNorm, SwiGLU in the GEMV,
 // q/k norm + RoPE + KV write), and attention is split over KV positions as in its "Milestones"
 // table (M5, split-KV decode kernel); the roadmap's "Tried and not kept" table found a
@@ -76,7 +77,7 @@ uint64_t plan_checksum(const HostPlan& p) {
   const int64_t dims[] = {s.n_layers, s.H, s.n_heads, s.n_kv, s.hd, s.F, s.V, s.G, s.qkv_rows, s.Hpad, s.Qpad, s.Fpad,
                           s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
-                          p.lds_part_floats, p.lds_bytes};
+                          p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -119,7 +120,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // split-KV and combine placement
   p.S = cfg.kv_splits > 0 ? cfg.kv_splits : choose_splits(s, W);
   if (p.S < 1 || (int64_t)p.S * s.n_kv > W) return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads exceeds workers");
-  const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 2) * 4;
+  const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
   else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= 40 * 1024 ? 1 : 0;
@@ -157,7 +158,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   wbytes += (int64_t)s.H * 2;  // final norm
 
   auto new_wave = [&](int32_t kind, int32_t layer) {
-    p.waves.push_back({kind, layer, 0, 0});
+    p.waves.push_back({kind, layer, 0, -1});
     p.tiles.resize(p.waves.size() * (size_t)W);
     for (int w = 0; w < W; ++w) {
       TileDesc& t = p.tiles[(p.waves.size() - 1) * W + w];
@@ -252,6 +253,21 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.packed_bytes = round_up(off, 4096);
   p.weight_bytes_per_step = wbytes;
 
+  // ---- tagged output buffers, one per wave (64-word aligned) ----
+  {
+    int64_t w_off = 0;
+    for (WaveDesc& wd : p.waves) {
+      const int64_t n = wave_out_words(s, p.S, wd.kind);
+      if (n == 0) {
+        wd.ll_off = -1;
+        continue;
+      }
+      wd.ll_off = (int32_t)w_off;
+      w_off = round_up(w_off + n, 64);
+    }
+    p.ll_words = w_off;
+  }
+
   // ---- per-wave bytes and balance ----
   const int nw = (int)p.waves.size();
   p.wave_bytes.assign(nw, 0);
@@ -291,13 +307,15 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS)
   int32_t part = 0;
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
-  // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 2] and the merged partial
-  part = std::max(part, s.G * s.hd + 2 * s.hd + (NCOMP + 1) * s.G * (s.hd + 2));
-  part = std::max(part, p.S * (s.hd + 2));                                  // one head's splits (combine tile)
-  if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * (s.hd + 2));  // all splits (o_proj prologue)
+  // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
+  const int32_t ps = s.hd + 4;
+  part = std::max(part, s.G * s.hd + 2 * s.hd + (NCOMP + 1) * s.G * ps);
+  part = std::max(part, p.S * ps);                                  // one head's splits (combine tile)
+  if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
-  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + SMALL_FLOATS) * 4 +
+  p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64);
+  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
                 (int32_t)round_up((int64_t)p.waves.size() * (int64_t)sizeof(SegDesc), 256);
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
@@ -364,23 +382,22 @@ int validate_plan(const HostPlan& p, std::string& err) {
             return fail(err, TILES_E_PLAN, "packed weights out of bounds or misaligned");
           packed_ranges.push_back({t.woff, t.woff + bytes});
           const int64_t lo = t.row0, hi = t.row0 + t.nrows;
+          const int32_t in_buf = wv > 0 ? BUF_WAVE + wv - 1 : BUF_EMBED;
+          const int32_t out_buf = BUF_WAVE + wv;
           if (kind == KIND_QKV) {
-            x.reads.push_back({BUF_X, 0, s.H});
-            x.writes.push_back({BUF_QKV, lo, hi});
+            x.reads.push_back({layer == 0 ? BUF_EMBED : in_buf, 0, s.H});
+            x.writes.push_back({out_buf, lo, hi});
           } else if (kind == KIND_O) {
-            if (p.combine_in_o) x.reads.push_back({BUF_PART, 0, (int64_t)s.n_heads * p.S});
-            else x.reads.push_back({BUF_ATTN, 0, (int64_t)s.n_heads * s.hd});
-            x.reads.push_back({BUF_X, lo, hi});
-            x.writes.push_back({BUF_X, lo, hi});
+            x.reads.push_back({in_buf, 0, wave_out_words(s, p.S, p.waves[wv - 1].kind)});
+            x.writes.push_back({out_buf, lo, hi});
           } else if (kind == KIND_GU) {
-            x.reads.push_back({BUF_X, 0, s.H});
-            x.writes.push_back({BUF_ACT, lo, hi});
+            x.reads.push_back({in_buf, 0, s.H});
+            x.writes.push_back({out_buf, lo, hi});
           } else if (kind == KIND_DOWN) {
-            x.reads.push_back({BUF_ACT, 0, s.F});
-            x.reads.push_back({BUF_X, lo, hi});
-            x.writes.push_back({BUF_X, lo, hi});
+            x.reads.push_back({in_buf, 0, s.F});
+            x.writes.push_back({out_buf, lo, hi});
           } else {
-            x.reads.push_back({BUF_X, 0, s.H});
+            x.reads.push_back({in_buf, 0, s.H});
             x.writes.push_back({BUF_LMPART, w, w + 1});
             x.writes.push_back({BUF_LOGITS, lo, hi});
           }
@@ -390,24 +407,24 @@ int validate_plan(const HostPlan& p, std::string& err) {
           if (t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S)
             return fail(err, TILES_E_PLAN, "attention tile out of range");
           seen.push_back(t.row0 * p.S + t.nrows);
-          x.reads.push_back({BUF_QKV, 0, s.qkv_rows});
+          x.reads.push_back({BUF_WAVE + wv - 1, 0, s.qkv_rows});
           // cached positions of this KV head (all positions before the current one)
           const int64_t kvbase = ((int64_t)layer * s.n_kv + t.row0) * s.max_positions;
           x.reads.push_back({BUF_KV, kvbase, kvbase + s.max_positions - 1});
           // The current position is written by exactly one split (the one holding L-1, checked
           // for every L below); the model gives that write to split 0 and a slot past every read.
           if (t.nrows == 0) x.writes.push_back({BUF_KV, kvbase + s.max_positions - 1, kvbase + s.max_positions});
-          for (int g2 = 0; g2 < s.G; ++g2) {
-            int64_t h = (int64_t)t.row0 * s.G + g2;
-            x.writes.push_back({BUF_PART, h * p.S + t.nrows, h * p.S + t.nrows + 1});
+          for (int g2 = 0; g2 < s.G; ++g2) {  // one (hd + 4)-word record per query head
+            const int64_t h = (int64_t)t.row0 * s.G + g2, rec = (h * p.S + t.nrows) * (s.hd + 4);
+            x.writes.push_back({BUF_WAVE + wv, rec, rec + s.hd + 4});
           }
           break;
         }
         case KIND_COMBINE: {
           if (t.row0 < 0 || t.row0 >= s.n_heads) return fail(err, TILES_E_PLAN, "combine tile out of range");
           seen.push_back(t.row0);
-          x.reads.push_back({BUF_PART, (int64_t)t.row0 * p.S, (int64_t)(t.row0 + 1) * p.S});
-          x.writes.push_back({BUF_ATTN, (int64_t)t.row0 * s.hd, (int64_t)(t.row0 + 1) * s.hd});
+          x.reads.push_back({BUF_WAVE + wv - 1, (int64_t)t.row0 * p.S * (s.hd + 4), (int64_t)(t.row0 + 1) * p.S * (s.hd + 4)});
+          x.writes.push_back({BUF_WAVE + wv, (int64_t)t.row0 * s.hd, (int64_t)(t.row0 + 1) * s.hd});
           break;
         }
         default:
@@ -475,11 +492,32 @@ int validate_plan(const HostPlan& p, std::string& err) {
     if ((double)p.wave_max_bytes[wv] > mean + row_bytes + 0.5) return fail(err, TILES_E_PLAN, "worker bytes unbalanced");
   }
 
+  // tagged buffers: every wave but the LM head owns a 4-word aligned buffer, disjoint from the others
+  {
+    std::vector<std::pair<int64_t, int64_t>> bufs;
+    for (int wv = 0; wv < nw; ++wv) {
+      const int64_t n = wave_out_words(s, p.S, p.waves[wv].kind);
+      const int32_t off = p.waves[wv].ll_off;
+      if (n == 0) {
+        if (off != -1) return fail(err, TILES_E_PLAN, "LM-head wave with a tagged buffer");
+        continue;
+      }
+      if (off < 0 || off % 4 != 0 || n % 4 != 0 || off + n > p.ll_words)
+        return fail(err, TILES_E_PLAN, "tagged buffer misaligned or out of bounds");
+      bufs.push_back({off, off + n});
+    }
+    std::sort(bufs.begin(), bufs.end());
+    for (size_t i = 1; i < bufs.size(); ++i)
+      if (bufs[i].first < bufs[i - 1].second) return fail(err, TILES_E_PLAN, "tagged buffers overlap");
+  }
+
   // LDS capacity for every wave's staging
   if (p.lds_part_floats / NCOMP < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
-  if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 2) > p.lds_part_floats)
+  if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
+  if ((int64_t)p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
+  if (p.lds_xres_floats < s.Hpad) return fail(err, TILES_E_PLAN, "LDS residual area too small");
   return TILES_OK;
 }
 

@@ -30,7 +30,8 @@ struct CopySeg {
 };
 
 // Buffers named by the hazard check.
-enum BufId : int32_t { BUF_X, BUF_QKV, BUF_PART, BUF_ATTN, BUF_ACT, BUF_LMPART, BUF_KV, BUF_LOGITS, BUF_COUNT };
+// Tagged output buffer of wave k: BUF_WAVE + k.
+enum BufId : int32_t { BUF_EMBED, BUF_LMPART, BUF_KV, BUF_LOGITS, BUF_WAVE = 16 };
 
 struct Interval {
   int32_t buf;
@@ -61,7 +62,8 @@ struct HostPlan {
   std::vector<int64_t> wave_bytes, wave_max_bytes;  // padded bytes streamed per wave (all / max worker)
   std::vector<int32_t> wave_busy;
   double max_over_mean = 1.0;
-  int32_t lds_vec_floats = 0, lds_part_floats = 0, lds_bytes = 0;
+  int32_t lds_vec_floats = 0, lds_part_floats = 0, lds_xres_floats = 0, lds_bytes = 0;
+  int64_t ll_words = 0;        // tagged-data buffers of all waves (uint32 words)
   uint64_t checksum = 0;
 };
 
@@ -73,6 +75,19 @@ int validate_plan(const HostPlan& plan, std::string& err);
 
 // 64-bit FNV-1a over the schedule and its geometry.
 uint64_t plan_checksum(const HostPlan& plan);
+
+// Words of wave `kind`'s tagged output buffer (0 for the LM head, whose partials live apart).
+inline int64_t wave_out_words(const Shape& s, int32_t S, int32_t kind) {
+  switch (kind) {
+    case KIND_QKV: return s.qkv_rows;
+    case KIND_ATTN: return (int64_t)s.n_heads * S * (s.hd + 4);  // records (m, l, acc[hd], 2 pad)
+    case KIND_COMBINE: return (int64_t)s.n_heads * s.hd;
+    case KIND_O: return s.H;
+    case KIND_GU: return s.F;
+    case KIND_DOWN: return s.H;
+    default: return 0;
+  }
+}
 
 // The split [lo, hi) of KV positions that split `s` of `S` covers when `L` positions are attended.
 inline void split_range(int64_t L, int32_t S, int32_t s, int64_t& lo, int64_t& hi) {

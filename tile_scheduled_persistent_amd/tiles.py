@@ -31,7 +31,6 @@ TILES_E_KERNEL = -6
 TILES_DEBUG_HIDDEN = 0x1
 TILES_TRACE = 0x2
 TILES_POISON = 0x4
-TILES_BARRIER_GATHER = 0x8
 
 WAVE_KINDS = {1: "qkv", 2: "attn", 3: "combine", 4: "o_proj", 5: "gate_up", 6: "down", 7: "lm_head"}
 
