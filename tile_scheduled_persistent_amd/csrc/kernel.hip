@@ -77,6 +77,12 @@ __device__ __forceinline__ u32x4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_of
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, SC1);
 }
 #define COMPILER_FENCE() asm volatile("" ::: "memory")
+constexpr int NT = 2;    // buffer-instruction cache policy bit: non-temporal (streamed once)
+// Streaming 16-byte load: base in scalar registers (the descriptor), one per-lane byte offset
+// shared by every load of a wave, and a wave-uniform chunk offset.
+__device__ __forceinline__ u32x4 nt_load(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, NT);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -381,15 +387,20 @@ struct Range {
   int64_t base;  // byte offset of the block's first chunk
 };
 
+// (Values read from LDS are per-lane to the compiler; readfirstlane makes the bounds scalar.)
 __device__ __forceinline__ Range block_range(const SegDesc& s, int k, int r0, int block_rows, int c) {
   Range r;
   r.k = k;
-  r.C = s.chunks_per_row;
-  const int nr = min(block_rows, s.rows - r0);
-  const int n = nr * s.chunks_per_row;
+  const int cpr = __builtin_amdgcn_readfirstlane(s.chunks_per_row);
+  const int rows = __builtin_amdgcn_readfirstlane(s.rows);
+  const int64_t woff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s.woff >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s.woff);
+  r.C = cpr;
+  const int nr = min(block_rows, rows - r0);
+  const int n = nr * cpr;
   r.i = chunk_lo(n, c);
   r.ihi = chunk_lo(n, c + 1);
-  r.base = s.woff + (int64_t)r0 * s.chunks_per_row * CHUNK_BYTES;
+  r.base = woff + (int64_t)r0 * cpr * CHUNK_BYTES;
   return r;
 }
 
@@ -417,29 +428,39 @@ struct Prefetch {
   int k;  // schedule wave they belong to (-1: none)
 };
 
+// Every prefetch slot is loaded unconditionally: a slot past the end of the range re-reads its
+// last chunk (or the first KB of the packed buffer when there is no next tile).  Loads behind
+// per-slot branches make the compiler wait for every outstanding load before the first use.
 template <int PF>
 __device__ __forceinline__ void issue_prefetch(Prefetch<PF>& pf, const Range& r, const uint8_t* packed, int lane) {
   pf.k = r.k;
   pf.n = r.k < 0 ? 0 : min(PF, r.ihi - r.i);
-  const u32x4* g = reinterpret_cast<const u32x4*>(packed + r.base) + (int64_t)r.i * 64 + lane;
+  const int64_t base = pf.n > 0 ? r.base + (int64_t)r.i * CHUNK_BYTES : 0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(packed + base);
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (u < pf.n) pf.v[u] = __builtin_nontemporal_load(g + u * 64);
+  for (int u = 0; u < PF; ++u) {
+    const int uc = u < pf.n ? u : (pf.n > 0 ? pf.n - 1 : 0);
+    pf.v[u] = nt_load(rs, (uint32_t)lane * 16u, (uint32_t)uc * CHUNK_BYTES);
+  }
 }
 
-// Consume chunks [r.i, r.ihi): the first `npf` come from pf (when use_pf), the rest are streamed.
-// Per-row partial sums go to part[row * NCOMP + c].  When `refill` is set, the loads of the next
-// tile's prefetch are issued as early as the current tile allows.
-template <int PF>
-__device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane, Prefetch<PF>& pf,
-                             bool use_pf, bool refill, const Range& nxt) {
+// Consume chunks [r.i, r.ihi): the first `npf` come from pf (when use_pf), the rest are streamed
+// in batches of STREAM_BATCH that ping-pong between two register sets, so one batch is always
+// in flight while the other is consumed.  Per-row partial sums go to part[row * NCOMP + c].
+// refill() (which reloads pf for the next tile, or does nothing) runs as soon as the last
+// batch is in flight.  The bounds are wave-uniform and every load inside the loop is issued
+// unconditionally (addresses clamped to the last chunk of the range), which lets the compiler
+// count outstanding loads exactly instead of waiting for all of them.
+template <int PF, typename Refill>
+__device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
+                                             Prefetch<PF>& pf, bool use_pf, Refill refill) {
+  constexpr int B = STREAM_BATCH;
   const int C = r.C;
-  int i = r.i;
+  const int i = r.i;
   const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
   float acc = 0.f;
   const float* vlane = L.vec + lane * 8;
-  const u32x4* g = reinterpret_cast<const u32x4*>(packed + r.base) + lane;
   const int npf = use_pf ? pf.n : 0;
   auto consume = [&](const u32x4& w) {
     acc += dot8(w, vlane + seg * CHUNK_COLS);
@@ -451,38 +472,52 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
       ++row;
     }
   };
-  // first streamed batch is issued before the prefetched chunks are consumed
-  u32x4 wa[STREAM_BATCH], wb[STREAM_BATCH];
-  int j = i + npf;
-  int na = min(STREAM_BATCH, ihi - j);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(packed + r.base);  // block base; offsets stay below 4 GB
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+  auto load_batch = [&](u32x4* w, int jb) {
 #pragma unroll
-  for (int u = 0; u < STREAM_BATCH; ++u)
-    if (u < na) wa[u] = __builtin_nontemporal_load(g + (int64_t)(j + u) * 64);
-#pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (u < npf) consume(pf.v[u]);
-  bool refilled = false;
-  if (na <= 0) {
-    if (refill) issue_prefetch(pf, nxt, packed, lane);
-    refilled = true;
-  }
-  while (na > 0) {
-    const int jn = j + na;
-    const int nb = min(STREAM_BATCH, ihi - jn);
-#pragma unroll
-    for (int u = 0; u < STREAM_BATCH; ++u)
-      if (u < nb) wb[u] = __builtin_nontemporal_load(g + (int64_t)(jn + u) * 64);
-    if (nb <= 0 && !refilled) {  // last batch in flight: start the next tile's loads now
-      if (refill) issue_prefetch(pf, nxt, packed, lane);
-      refilled = true;
+    for (int u = 0; u < B; ++u) {
+      const int jc = jb + u < ihi ? jb + u : ihi - 1;
+      w[u] = nt_load(rs, lane_off, (uint32_t)jc * CHUNK_BYTES);
     }
+  };
+  auto consume_batch = [&](const u32x4* w, int jb) {
 #pragma unroll
-    for (int u = 0; u < STREAM_BATCH; ++u)
-      if (u < na) consume(wa[u]);
-    j = jn;
-    na = nb;
+    for (int u = 0; u < B; ++u)
+      if (jb + u < ihi) consume(w[u]);
+  };
+  const int j0 = i + npf;
+  const int nbatch = ihi > j0 ? (ihi - j0 + B - 1) / B : 0;
+  if (nbatch == 0) {
 #pragma unroll
-    for (int u = 0; u < STREAM_BATCH; ++u) wa[u] = wb[u];
+    for (int u = 0; u < PF; ++u)
+      if (u < npf) consume(pf.v[u]);
+    refill();
+  } else {
+    u32x4 wa[B], wb[B];
+    load_batch(wa, j0);  // first streamed batch, issued before the prefetched chunks are consumed
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < npf) consume(pf.v[u]);
+    int jb = j0;
+    for (int b = 0;; b += 2) {
+      if (b + 1 >= nbatch) {  // wa holds the last batch
+        refill();
+        consume_batch(wa, jb);
+        break;
+      }
+      load_batch(wb, jb + B);
+      consume_batch(wa, jb);
+      jb += B;
+      if (b + 2 >= nbatch) {  // wb holds the last batch
+        refill();
+        consume_batch(wb, jb);
+        break;
+      }
+      load_batch(wa, jb + B);
+      consume_batch(wb, jb);
+      jb += B;
+    }
   }
   if (seg != 0) {
     const float s = wave_sum(acc);
@@ -614,34 +649,92 @@ __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds&
   }
 }
 
+// Positions [wlo, whi) of a split that compute wave c handles at attended length L_att.
+struct AttnRange {
+  int64_t wlo, whi;
+};
+__device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int c, int64_t L_att) {
+  const int64_t ch = (L_att + a.S - 1) / a.S;
+  int64_t lo = (int64_t)sp * ch;
+  const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
+  if (lo > L_att) lo = L_att;
+  const int64_t n = hi > lo ? hi - lo : 0;
+  AttnRange r;
+  r.wlo = lo + (n * c) / NCOMP;
+  r.whi = lo + (n * (c + 1)) / NCOMP;
+  return r;
+}
+
+// K and V of position j of KV head (layer, g) for this lane's 16-byte segment; zero for the
+// current position (taken from LDS) and past the range.  Every row is read with a
+// device-coherent load: rows written earlier in this launch by other workers need it, and one
+// load form for all lanes keeps the loads of a batch independent (a per-lane choice between two
+// forms writing the same registers makes the compiler wait for all outstanding loads).
+// (Positions past the range or at the current position load row 0 instead; the consumer
+// ignores those values, and the loads stay unconditional for the reason given at issue_prefetch.)
+template <int HD>
+__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t j, int64_t whi,
+                                        int64_t cur, int dseg, u32x4& kw, u32x4& vw) {
+  constexpr int LPP = HD / 8;
+  const int64_t jj = (j < whi && j != cur) ? j : 0;
+  const uint32_t off = (uint32_t)((jj * LPP + dseg) * 16);
+  kw = cld4(rk, off);
+  vw = cld4(rv, off);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache, int64_t kvrow0, int hd) {
+  return rsrc(cache + kvrow0 * hd);
+}
+
+// Prefetch of an attention tile (wave k): K and V of this wave's first PF/2 position groups
+// (the ring compute_attention runs on), issued while the previous tile (QKV) streams.  The
+// cache rows do not depend on this step's q; the current position's row is never loaded (it
+// comes from LDS).  pf.n is the number of groups of the wave's range.
+template <int HD, int PF>
+__device__ __forceinline__ void issue_kv_prefetch(Prefetch<PF>& pf, const KernelArgs& a, int k, int layer, int g,
+                                                  int sp, int64_t L_att, int c, int lane) {
+  constexpr int LPP = HD / 8, P = 64 / LPP;
+  const AttnRange r = attn_range(a, sp, c, L_att);
+  pf.k = k;
+  pf.n = r.whi > r.wlo ? (int)((r.whi - r.wlo + P - 1) / P) : 0;
+  const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
+  const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
+  const int pp = lane / LPP, dseg = lane % LPP;
+#pragma unroll
+  for (int j = 0; j < PF / 2; ++j)
+    load_kv<HD>(rk, rv, r.wlo + j * P + pp, r.whi, L_att - 1, dseg, pf.v[2 * j], pf.v[2 * j + 1]);
+}
+
 template <int HD>
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
   f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
-// compute wave: one share of an attention split
-template <int HD, int G>
-__device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int c, int lane, int layer, int g, int sp,
-                                  int64_t L_att) {
+// compute wave: one share of an attention split.  The position groups run through a ring of
+// D = PF/2 (K, V) register pairs -- the prefetch registers themselves, filled with the first D
+// groups while the previous tile streamed: each step consumes one slot and reloads it with the
+// group D steps ahead (past the range the reload re-reads row 0, a cached dummy; every load is
+// unconditional for the reason given at issue_prefetch).  after() then reuses the registers for
+// the next tile's prefetch.
+template <int HD, int G, int PF, typename After>
+__device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
+                                                  int g, int sp, int64_t L_att, Prefetch<PF>& pf, After after) {
   constexpr int PS = pstride<HD>();
+  constexpr int D = PF / 2;
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
   float* ws = attn_ws<HD, G>(L);
-  const int64_t ch = (L_att + a.S - 1) / a.S;
-  int64_t lo = (int64_t)sp * ch;
-  const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
-  if (lo > L_att) lo = L_att;
   const int64_t cur = L_att - 1;
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   constexpr int LPP = HD / 8;  // lanes per position
   constexpr int P = 64 / LPP;  // positions per load
-  constexpr int U = 2;         // position groups per batch (two batches in flight)
-  const int64_t n = hi > lo ? hi - lo : 0;
-  const int64_t wlo = lo + (n * c) / NCOMP, whi = lo + (n * (c + 1)) / NCOMP;
+  const AttnRange rg = attn_range(a, sp, c, L_att);
+  const int64_t wlo = rg.wlo, whi = rg.whi;
+  const int ngroups = whi > wlo ? (int)((whi - wlo + P - 1) / P) : 0;
   const int pp = lane / LPP, dseg = lane % LPP;
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
+  const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -650,80 +743,57 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const u32x4* kbase_p = reinterpret_cast<const u32x4*>(a.kv_k + kvrow0 * HD);
-  const u32x4* vbase_p = reinterpret_cast<const u32x4*>(a.kv_v + kvrow0 * HD);
-  const __amdgpu_buffer_rsrc_t rk = rsrc(kbase_p), rv = rsrc(vbase_p);
-  auto load = [&](int64_t jb, u32x4* kw, u32x4* vw) {
+  auto consume1 = [&](int64_t jb, const u32x4& kw, const u32x4& vw) {
+    const int64_t j = jb + pp;
+    const bool valid = j < whi;
+    float kf[8], vf[8];
+    if (j == cur) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = jb + u * P + pp;
-      kw[u] = u32x4{0u, 0u, 0u, 0u};
-      vw[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < whi && j != cur) {
-        if (j < a.pos0) {  // cached before this launch: streaming loads
-          kw[u] = __builtin_nontemporal_load(kbase_p + j * LPP + dseg);
-          vw[u] = __builtin_nontemporal_load(vbase_p + j * LPP + dseg);
-        } else {           // written by another worker during this launch: device-coherent loads
-          kw[u] = cld4(rk, (uint32_t)((j * LPP + dseg) * 16));
-          vw[u] = cld4(rv, (uint32_t)((j * LPP + dseg) * 16));
-        }
+      for (int e = 0; e < 8; ++e) {
+        kf[e] = kc[dseg * 8 + e];
+        vf[e] = vc[dseg * 8 + e];
+      }
+    } else {
+      unpack8<HD>(kw, kf);
+      unpack8<HD>(vw, vf);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlane + h * HD + 4);
+      float d0 = q0.x * kf[0], d1 = q0.y * kf[1];
+      d0 = fmaf(q0.z, kf[2], d0);
+      d1 = fmaf(q0.w, kf[3], d1);
+      d0 = fmaf(q1.x, kf[4], d0);
+      d1 = fmaf(q1.y, kf[5], d1);
+      d0 = fmaf(q1.z, kf[6], d0);
+      d1 = fmaf(q1.w, kf[7], d1);
+      float s = d0 + d1;
+      s = LPP == 8 ? sum8(s) : sum16(s);
+      if (valid) {
+        const float mn = fmaxf(m[h], s);
+        const float al = __builtin_amdgcn_exp2f(m[h] - mn);
+        const float p = __builtin_amdgcn_exp2f(s - mn);
+        l[h] = l[h] * al + p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
+        m[h] = mn;
       }
     }
   };
-  auto consume = [&](int64_t jb, const u32x4* kw, const u32x4* vw) {
+  if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = jb + u * P + pp;
-      const bool valid = j < whi;
-      float kf[8], vf[8];
-      if (j == cur) {
+    for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+  }
+  for (int g0 = 0; g0 < ngroups; g0 += D) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[e] = kc[dseg * 8 + e];
-          vf[e] = vc[dseg * 8 + e];
-        }
-      } else {
-        unpack8<HD>(kw[u], kf);
-        unpack8<HD>(vw[u], vf);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlane + h * HD + 4);
-        float d0 = q0.x * kf[0], d1 = q0.y * kf[1];
-        d0 = fmaf(q0.z, kf[2], d0);
-        d1 = fmaf(q0.w, kf[3], d1);
-        d0 = fmaf(q1.x, kf[4], d0);
-        d1 = fmaf(q1.y, kf[5], d1);
-        d0 = fmaf(q1.z, kf[6], d0);
-        d1 = fmaf(q1.w, kf[7], d1);
-        float s = d0 + d1;
-        s = LPP == 8 ? sum8(s) : sum16(s);
-        if (valid) {
-          const float mn = fmaxf(m[h], s);
-          const float al = __builtin_amdgcn_exp2f(m[h] - mn);
-          const float p = __builtin_amdgcn_exp2f(s - mn);
-          l[h] = l[h] * al + p;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
-          m[h] = mn;
-        }
-      }
-    }
-  };
-  if (wlo < whi) {
-    u32x4 ka[U], va[U], kb[U], vb[U];
-    load(wlo, ka, va);
-    for (int64_t jb = wlo; jb < whi; jb += 2 * U * P) {
-      const int64_t jn = jb + U * P;
-      if (jn < whi) load(jn, kb, vb);
-      consume(jb, ka, va);
-      if (jn >= whi) break;
-      const int64_t jnn = jn + U * P;
-      if (jnn < whi) load(jnn, ka, va);
-      consume(jn, kb, vb);
+    for (int s = 0; s < D; ++s) {
+      const int gi = g0 + s;
+      if (gi < ngroups) consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);
+      load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
     }
   }
+  after();
   // merge the P position groups of this wave (lanes differing by multiples of LPP)
 #pragma unroll
   for (int off = LPP; off < 64; off <<= 1) {
@@ -802,19 +872,100 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 }
 
 // ---------------------------------------------------------------------------
-// the worker loop (all eight wavefronts)
+// per-wave phases shared by all wavefronts.  The control wave (0) and the compute waves
+// (1..7) run separate loops (so that each keeps only its own values in registers) with the
+// same barrier sequence per wave: P (inputs staged), A (LDS prologue done), then for GEMV
+// tiles B per row block (and C between blocks), for attention tiles B and E.
+// ---------------------------------------------------------------------------
+
+// Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
+// abandoned.  The control wave also reduces the previous step's token (tok).
+template <int HD, int G>
+__device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
+                                              const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
+                                              int& tok) {
+  constexpr int PS = pstride<HD>();
+  const int layer = wd.layer;
+  const uint32_t* in = a.ll + (k > 0 ? a.waves[k - 1].ll_off : 0);
+  // Every worker gathers x in the QKV and gate/up waves, tile or not: the o_proj and down
+  // epilogues add their rows to the residual staged there.
+  const int gk = (wd.kind == KIND_QKV || wd.kind == KIND_GU) ? wd.kind : t.kind;
+  bool ab = false;
+  switch (gk) {
+    case KIND_QKV:
+    case KIND_GU:
+    case KIND_LM: {
+      const int64_t goff = gk == KIND_QKV ? a.small[layer].attn_norm
+                           : gk == KIND_GU ? a.small[layer].mlp_norm
+                                           : a.final_norm_off;
+      const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
+      float ss = 0.f;
+      if (gk == KIND_QKV && layer == 0) {
+        if (wave == 0) {
+          if (step > 0) {
+            ab = gather_token(a, lane, step_parity(step - 1), tok);
+            if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+          }
+          if (!ab) ss = stage_embedding(a, L, tok, gain, lane);
+        }
+      } else {
+        ab = gather_norm(a, L, in, a.H, gain, wave, lane, par, ss);
+      }
+      for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+      if (lane == 0) L.small[SM_SS + wave] = ss;
+      break;
+    }
+    case KIND_O:
+      if (a.combine_in_o) ab = gather_plain(a, L.part, in, a.n_heads * a.S * PS, wave, lane, par);
+      else ab = gather_plain(a, L.vec, in, a.n_heads * HD, wave, lane, par);
+      for (int i = a.n_heads * HD + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+      break;
+    case KIND_DOWN:
+      ab = gather_plain(a, L.vec, in, a.F, wave, lane, par);
+      for (int i = a.F + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+      break;
+    case KIND_ATTN:
+      ab = gather_qkv<HD, G>(a, L, in, t.row0, wave, lane, par);
+      break;
+    case KIND_COMBINE:
+      ab = gather_plain(a, L.part, in + (int64_t)t.row0 * a.S * PS, a.S * PS, wave, lane, par);
+      break;
+    default:
+      break;
+  }
+  return ab;
+}
+
+// LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale.
+template <int HD, int G>
+__device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
+                                              const TileDesc& t, int layer, int pos) {
+  constexpr int PS = pstride<HD>();
+  float rs = 1.0f;
+  if (t.kind == KIND_QKV || t.kind == KIND_GU || t.kind == KIND_LM) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) tot += L.small[SM_SS + w];
+    rs = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+  } else if (t.kind == KIND_ATTN) {
+    attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
+  } else if (t.kind == KIND_O && a.combine_in_o) {
+    const int nq = a.n_heads * HD;
+    for (int i = wave * 64 + lane; i < nq; i += BLOCK_THREADS)
+      L.vec[i] = merge_splits<HD>(L.part + (i / HD) * a.S * PS, a.S, i % HD);
+  } else if (t.kind == KIND_COMBINE) {
+    for (int d = wave * 64 + lane; d < HD; d += BLOCK_THREADS) L.vec[d] = merge_splits<HD>(L.part, a.S, d);
+  }
+  return rs;
+}
+
+// ---------------------------------------------------------------------------
+// control wave loop
 // ---------------------------------------------------------------------------
 
 template <int HD, int G>
-__device__ __forceinline__ void worker_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int block_rows) {
-  constexpr int PS = pstride<HD>();
-  const bool ctl = wave == 0;
-  const int c = wave - 1;  // compute-wave index (compute waves only)
+__device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   volatile int* smi = reinterpret_cast<volatile int*>(L.small);
-  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
-  pf.n = 0;
-  pf.k = -1;
-  if (!ctl) issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
   int tok = a.token0;
   const int H = a.H;
   bool stop = false;
@@ -828,160 +979,79 @@ __device__ __forceinline__ void worker_loop(const KernelArgs& a, const Lds& L, i
       const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
       const WaveDesc wd = a.waves[k];
       const int layer = wd.layer;
-      const uint32_t* in = a.ll + (k > 0 ? a.waves[k - 1].ll_off : 0);
       uint32_t* out = a.ll + (wd.ll_off >= 0 ? wd.ll_off : 0);
       uint64_t t0 = 0, t_pro = 0, t_cmp = 0;
-      if (ctl && a.trace) t0 = wall_clock64();
-      // ---- inputs: every wavefront gathers its share ----
-      // Every worker gathers x in the QKV and gate/up waves, tile or not: the o_proj and down
-      // epilogues add their rows to the residual staged there.
-      const int gk = (wd.kind == KIND_QKV || wd.kind == KIND_GU) ? wd.kind : t.kind;
-      bool ab = false;
-      switch (gk) {
-        case KIND_QKV:
-        case KIND_GU:
-        case KIND_LM: {
-          const int64_t goff = gk == KIND_QKV ? a.small[layer].attn_norm
-                               : gk == KIND_GU ? a.small[layer].mlp_norm
-                                               : a.final_norm_off;
-          const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
-          float ss = 0.f;
-          if (gk == KIND_QKV && layer == 0) {
-            if (ctl) {
-              if (step > 0) {
-                ab = gather_token(a, lane, step_parity(step - 1), tok);
-                if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
-              }
-              if (!ab) ss = stage_embedding(a, L, tok, gain, lane);
-            }
-          } else {
-            ab = gather_norm(a, L, in, H, gain, wave, lane, par, ss);
-          }
-          for (int i = H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
-          if (lane == 0) L.small[SM_SS + wave] = ss;
-          break;
-        }
-        case KIND_O:
-          if (a.combine_in_o) ab = gather_plain(a, L.part, in, a.n_heads * a.S * PS, wave, lane, par);
-          else ab = gather_plain(a, L.vec, in, a.n_heads * HD, wave, lane, par);
-          for (int i = a.n_heads * HD + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
-          break;
-        case KIND_DOWN:
-          ab = gather_plain(a, L.vec, in, a.F, wave, lane, par);
-          for (int i = a.F + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
-          break;
-        case KIND_ATTN:
-          ab = gather_qkv<HD, G>(a, L, in, t.row0, wave, lane, par);
-          break;
-        case KIND_COMBINE:
-          ab = gather_plain(a, L.part, in + (int64_t)t.row0 * a.S * PS, a.S * PS, wave, lane, par);
-          break;
-        default:
-          break;
-      }
-      if (ab) smi[SM_ABORT] = 1;
+      if (a.trace) t0 = wall_clock64();
+      if (gather_inputs<HD, G>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
         break;
       }
-      if (ctl && a.trace) t_pro = wall_clock64();
-      // ---- LDS-only prologue work ----
-      float rs = 1.0f;  // RMSNorm scale folded out of the input vector, applied to the GEMV results
-      if (t.kind == KIND_QKV || t.kind == KIND_GU || t.kind == KIND_LM) {
-        float tot = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) tot += L.small[SM_SS + w];
-        rs = 1.0f / sqrtf(tot / (float)H + a.eps);
-      } else if (t.kind == KIND_ATTN) {
-        attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
-      } else if (t.kind == KIND_O && a.combine_in_o) {
-        const int nq = a.n_heads * HD;
-        for (int i = wave * 64 + lane; i < nq; i += BLOCK_THREADS)
-          L.vec[i] = merge_splits<HD>(L.part + (i / HD) * a.S * PS, a.S, i % HD);
-      } else if (t.kind == KIND_COMBINE) {
-        for (int d = wave * 64 + lane; d < HD; d += BLOCK_THREADS) L.vec[d] = merge_splits<HD>(L.part, a.S, d);
-      }
+      if (a.trace) t_pro = wall_clock64();
+      const float rs = lds_prologue<HD, G>(a, L, 0, lane, t, layer, pos);
       __syncthreads();  // A: inputs ready
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
         const int C = t.kpad / CHUNK_COLS;
-        if (ctl && t.kind == KIND_O) {
-          // KV rows written by this worker earlier in the step must be complete before any
-          // output of this wave is published: later readers of those rows depend on it.
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        const SegDesc sd = L.segs[k];
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const int nr = min(block_rows, rows - r0);
-          if (!ctl) {
-            const Range r = block_range(sd, k, r0, block_rows, c);
-            const bool last_block = r0 + block_rows >= rows;
-            const Range nxt = last_block ? next_gemv(L.segs, a.n_waves, k, block_rows, c) : r;
-            if (r.i < r.ihi) {
-              stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, last_block, nxt);
-            } else if (last_block) {
-              issue_prefetch(pf, nxt, a.packed, lane);
-            }
-          }
           __syncthreads();  // B: partials of this block ready
-          if (ctl) {
-            if (a.trace && r0 == 0) t_cmp = wall_clock64();
-            switch (t.kind) {
-              case KIND_QKV:
-                for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * row_total(L, nr, C, r), par);
-                break;
-              case KIND_O:
-                for (int r = lane; r < nr; r += 64) {
-                  const int j = t.row0 + r0 + r;
-                  publish(out, j, L.xres[j] + row_total(L, nr, C, r), par);
+          if (a.trace && r0 == 0) t_cmp = wall_clock64();
+          switch (t.kind) {
+            case KIND_QKV:
+              for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * row_total(L, nr, C, r), par);
+              break;
+            case KIND_O:
+              for (int r = lane; r < nr; r += 64) {
+                const int j = t.row0 + r0 + r;
+                publish(out, j, L.xres[j] + row_total(L, nr, C, r), par);
+              }
+              break;
+            case KIND_GU:  // interleaved gate/up rows
+              for (int p = lane; p < nr / 2; p += 64) {
+                const float gt = rs * row_total(L, nr, C, 2 * p);
+                const float up = rs * row_total(L, nr, C, 2 * p + 1);
+                publish(out, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
+              }
+              break;
+            case KIND_DOWN:
+              for (int r = lane; r < nr; r += 64) {
+                const int j = t.row0 + r0 + r;
+                const float nx = L.xres[j] + row_total(L, nr, C, r);
+                publish(out, j, nx, par);
+                if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = tag_clear(nx);
+              }
+              break;
+            case KIND_LM:
+              for (int r = lane; r < nr; r += 64) {
+                const float v = rs * row_total(L, nr, C, r);
+                const int idx = t.row0 + r0 + r;
+                if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
+                if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
+                  lm_best = v;
+                  lm_idx = idx;
                 }
-                break;
-              case KIND_GU:  // interleaved gate/up rows
-                for (int p = lane; p < nr / 2; p += 64) {
-                  const float gt = rs * row_total(L, nr, C, 2 * p);
-                  const float up = rs * row_total(L, nr, C, 2 * p + 1);
-                  publish(out, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
-                }
-                break;
-              case KIND_DOWN:
-                for (int r = lane; r < nr; r += 64) {
-                  const int j = t.row0 + r0 + r;
-                  const float nx = L.xres[j] + row_total(L, nr, C, r);
-                  publish(out, j, nx, par);
-                  if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = tag_clear(nx);
-                }
-                break;
-              case KIND_LM:
-                for (int r = lane; r < nr; r += 64) {
-                  const float v = rs * row_total(L, nr, C, r);
-                  const int idx = t.row0 + r0 + r;
-                  if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
-                  if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
-                    lm_best = v;
-                    lm_idx = idx;
-                  }
-                }
-                break;
-            }
+              }
+              break;
           }
           if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
         }
       } else if (t.kind == KIND_ATTN) {
-        if (ctl) cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
-        else compute_attention<HD, G>(a, L, c, lane, layer, t.row0, t.nrows, L_att);
+        cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
+        // The KV row must be complete before this worker publishes anything later readers of
+        // the row depend on (its split partial, below); the wait overlaps the compute waves.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // B: compute-wave states ready
-        if (ctl && a.trace) t_cmp = wall_clock64();
-        attn_merge_phase<HD, G>(L, wave, lane);
+        if (a.trace) t_cmp = wall_clock64();
+        attn_merge_phase<HD, G>(L, 0, lane);
         __syncthreads();  // E: merged partial ready
-        if (ctl) cw_attn_publish<HD, G>(a, L, out, lane, t.row0, t.nrows, par);
+        cw_attn_publish<HD, G>(a, L, out, lane, t.row0, t.nrows, par);
       } else if (t.kind == KIND_COMBINE) {
-        if (ctl) {
-          if (a.trace) t_cmp = wall_clock64();
-          for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);
-        }
+        if (a.trace) t_cmp = wall_clock64();
+        for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);
       }
-      if (ctl && wd.kind == KIND_LM) {
+      if (wd.kind == KIND_LM) {
         // worker partial (max, lowest index); also published by workers without vocabulary rows
         for (int off = 32; off >= 1; off >>= 1) {
           const float ov = __shfl_xor(lm_best, off);
@@ -995,7 +1065,7 @@ __device__ __forceinline__ void worker_loop(const KernelArgs& a, const Lds& L, i
           st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
                  (uint64_t)__float_as_uint(lm_best) | ((uint64_t)((uint32_t)lm_idx | (par << 31)) << 32));
       }
-      if (ctl && a.trace && lane == 0) {
+      if (a.trace && lane == 0) {
         const uint64_t t1 = wall_clock64();
         uint64_t* tr = a.trace + (((int64_t)step * a.n_waves + k) * a.W + bid) * TRACE_WORDS;
         tr[0] = t0;
@@ -1007,9 +1077,73 @@ __device__ __forceinline__ void worker_loop(const KernelArgs& a, const Lds& L, i
     }
   }
   // the last step's token
-  if (!stop && ctl && bid == 0) {
+  if (!stop && bid == 0) {
     int last = 0;
     if (!gather_token(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// compute wave loop
+// ---------------------------------------------------------------------------
+
+template <int HD, int G>
+__device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
+                                             int block_rows) {
+  const int c = wave - 1;
+  volatile int* smi = reinterpret_cast<volatile int*>(L.small);
+  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
+  issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
+  int tok_unused = 0;
+  bool stop = false;
+  for (int step = 0; step < a.n_steps && !stop; ++step) {
+    const uint32_t par = step_parity(step);
+    const int pos = a.pos0 + step;
+    const int64_t L_att = (int64_t)pos + 1;
+    for (int k = 0; k < a.n_waves; ++k) {
+      const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
+      const WaveDesc wd = a.waves[k];
+      const int layer = wd.layer;
+      if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      __syncthreads();  // P
+      if (smi[SM_ABORT]) {
+        stop = true;
+        break;
+      }
+      lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
+      __syncthreads();  // A
+      if (is_gemv(t.kind)) {
+        const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
+        const SegDesc sd = L.segs[k];
+        // the prefetch issued at the end of this tile: KV rows when this worker's next tile
+        // is an attention split, else the weights of its next GEMV tile
+        const TileDesc tn = a.tiles[(int64_t)(k + 1 < a.n_waves ? k + 1 : 0) * a.W + bid];
+        const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
+        auto refill_next = [&]() {
+          if (next_attn) issue_kv_prefetch<HD>(pf, a, k + 1, layer, tn.row0, tn.nrows, L_att, c, lane);
+          else issue_prefetch(pf, next_gemv(L.segs, a.n_waves, k, block_rows, c), a.packed, lane);
+        };
+        for (int r0 = 0; r0 < rows; r0 += block_rows) {
+          const Range r = block_range(sd, k, r0, block_rows, c);
+          const bool last_block = r0 + block_rows >= rows;
+          if (r.i < r.ihi) {
+            if (last_block) stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, refill_next);
+            else stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, []() {});
+          } else if (last_block) {
+            refill_next();
+          }
+          __syncthreads();                              // B
+          if (r0 + block_rows < rows) __syncthreads();  // C
+        }
+      } else if (t.kind == KIND_ATTN) {
+        compute_attention<HD, G>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, pf, [&]() {
+          issue_prefetch(pf, next_gemv(L.segs, a.n_waves, k, block_rows, c), a.packed, lane);
+        });
+        __syncthreads();  // B
+        attn_merge_phase<HD, G>(L, wave, lane);
+        __syncthreads();  // E
+      }
+    }
   }
 }
 
@@ -1023,7 +1157,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   L.xres = L.part + a.lds_part_floats;
   L.small = L.xres + a.lds_xres_floats;
   L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, bid = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, bid = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int k = tid; k < a.n_waves; k += BLOCK_THREADS) {
     const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
     SegDesc s;
@@ -1035,7 +1170,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   if (tid == 0) reinterpret_cast<int*>(L.small)[SM_ABORT] = 0;
   __syncthreads();
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  worker_loop<HD, G>(a, L, bid, wave, lane, block_rows);
+  if (wave == 0) control_loop<HD, G>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
