@@ -234,7 +234,7 @@ __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src,
   return false;
 }
 
-constexpr int GATHER_UNITS = 8;  // units per lane per polling pass (8 wavefronts x 64 lanes x 8 = 16384 floats)
+constexpr int GATHER_UNITS = 4;  // units per lane per polling pass (8 wavefronts x 64 lanes x 4 = 8192 floats)
 
 struct Identity {
   __device__ int operator()(int u) const { return u; }
@@ -356,14 +356,22 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
 
 // ---------------------------------------------------------------------------
 // compute wave: weight streaming.  Each compute wave reads its share of a GEMV block (a
-// contiguous chunk range) with 16-byte loads into registers, double-buffered in batches of
-// STREAM_BATCH chunks.  Before a tile's last batch is consumed, the wave issues the loads of
-// the first PREFETCH_CHUNKS chunks of its next GEMV tile, so those bytes arrive while the
-// workgroup publishes this tile's outputs and gathers the next inputs.
+// contiguous chunk range) with 16-byte loads into registers, in batches of STREAM_BATCH
+// chunks that ping-pong between two register sets X and Y: while one batch is consumed the
+// other is in flight.  The reloads issued after a range's last batches fetch the first two
+// batches of the wave's next range -- the next block, the next GEMV tile or the (K, V) rows of
+// its next attention split -- so those bytes arrive while the workgroup publishes this tile's
+// outputs and gathers the next inputs: weights (and cached KV rows) do not depend on
+// activations, only the dot products do (the Tiles page credits this prefetch idea to the
+// megakernel it builds on).
+//
+// Every load of these loops is issued unconditionally (addresses clamped into the range, or a
+// dummy chunk when there is nothing to fetch) and the bounds are wave-uniform: that lets the
+// compiler count outstanding loads exactly; loads behind per-slot branches make it wait for
+// all of them before the first use.
 // ---------------------------------------------------------------------------
 
 constexpr int STREAM_BATCH = 4;
-constexpr int PREFETCH_CHUNKS = 12;  // register budget: 8 are used when a KV head serves 3-4 query heads
 
 __device__ __forceinline__ float dot8(const u32x4 w, const float* v) {
   const f32x4 v0 = *reinterpret_cast<const f32x4*>(v);
@@ -382,6 +390,7 @@ __device__ __forceinline__ float dot8(const u32x4 w, const float* v) {
 // Chunk range [i, ihi) of compute wave c in block r0 of a GEMV segment.
 struct Range {
   int k;         // schedule wave (-1: none)
+  int r0;        // first row of the block
   int C;         // chunks per row
   int i, ihi;
   int64_t base;  // byte offset of the block's first chunk
@@ -391,6 +400,7 @@ struct Range {
 __device__ __forceinline__ Range block_range(const SegDesc& s, int k, int r0, int block_rows, int c) {
   Range r;
   r.k = k;
+  r.r0 = r0;
   const int cpr = __builtin_amdgcn_readfirstlane(s.chunks_per_row);
   const int rows = __builtin_amdgcn_readfirstlane(s.rows);
   const int64_t woff = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s.woff >> 32)) << 32) |
@@ -404,6 +414,16 @@ __device__ __forceinline__ Range block_range(const SegDesc& s, int k, int r0, in
   return r;
 }
 
+__device__ __forceinline__ Range no_range() {
+  Range r;
+  r.k = -1;
+  r.r0 = 0;
+  r.C = 1;
+  r.i = r.ihi = 0;
+  r.base = 0;
+  return r;
+}
+
 // First block of the next GEMV wave after `k` (wrapping into the next step) in which compute
 // wave c has chunks; k = -1 when there is none.
 __device__ __forceinline__ Range next_gemv(const SegDesc* segs, int n_waves, int k, int block_rows, int c) {
@@ -413,58 +433,50 @@ __device__ __forceinline__ Range next_gemv(const SegDesc* segs, int n_waves, int
     const Range r = block_range(segs[kk], kk, 0, block_rows, c);
     if (r.i < r.ihi) return r;
   }
-  Range none;
-  none.k = -1;
-  none.C = 1;
-  none.i = none.ihi = 0;
-  none.base = 0;
-  return none;
+  return no_range();
 }
 
-template <int PF>
-struct Prefetch {
-  u32x4 v[PF];
-  int n;  // valid entries
-  int k;  // schedule wave they belong to (-1: none)
+// The two batch register sets of a compute wave: X = v[0, B), Y = v[B, 2B).
+template <int B>
+struct Stream {
+  u32x4 v[2 * B];
+  int k;   // wave whose data the registers hold (-1: none)
+  int r0;  // GEMV block of that wave
 };
 
-// Every prefetch slot is loaded unconditionally: a slot past the end of the range re-reads its
-// last chunk (or the first KB of the packed buffer when there is no next tile).  Loads behind
-// per-slot branches make the compiler wait for every outstanding load before the first use.
-template <int PF>
-__device__ __forceinline__ void issue_prefetch(Prefetch<PF>& pf, const Range& r, const uint8_t* packed, int lane) {
-  pf.k = r.k;
-  pf.n = r.k < 0 ? 0 : min(PF, r.ihi - r.i);
-  const int64_t base = pf.n > 0 ? r.base + (int64_t)r.i * CHUNK_BYTES : 0;
-  const __amdgpu_buffer_rsrc_t rs = rsrc(packed + base);
+// Batch q of GEMV range r into w[0, B): chunks r.i + q*B + u, clamped to the range's last chunk
+// (a range with no chunks reads the first KB of the packed buffer).
+template <int B>
+__device__ __forceinline__ void load_gemv_batch(u32x4* w, const uint8_t* packed, const Range& r, int q, int lane) {
+  const bool any = r.i < r.ihi;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(packed + (any ? r.base : 0));
 #pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    const int uc = u < pf.n ? u : (pf.n > 0 ? pf.n - 1 : 0);
-    pf.v[u] = nt_load(rs, (uint32_t)lane * 16u, (uint32_t)uc * CHUNK_BYTES);
+  for (int u = 0; u < B; ++u) {
+    const int j = r.i + q * B + u;
+    const int jc = any ? (j < r.ihi ? j : r.ihi - 1) : 0;
+    w[u] = nt_load(rs, (uint32_t)lane * 16u, (uint32_t)jc * CHUNK_BYTES);
   }
 }
 
-// Consume chunks [r.i, r.ihi): the first `npf` come from pf (when use_pf), the rest are streamed
-// in batches of STREAM_BATCH that ping-pong between two register sets, so one batch is always
-// in flight while the other is consumed.  Per-row partial sums go to part[row * NCOMP + c].
-// refill() (which reloads pf for the next tile, or does nothing) runs as soon as the last
-// batch is in flight.  The bounds are wave-uniform and every load inside the loop is issued
-// unconditionally (addresses clamped to the last chunk of the range), which lets the compiler
-// count outstanding loads exactly instead of waiting for all of them.
-template <int PF, typename Refill>
+// Consume chunks [r.i, r.ihi) in batches; st holds batches 0 and 1 when `have` (else they are
+// loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the last
+// batches run next_load(w, 0) into X and next_load(w, 1) into Y.
+template <int B, typename NextLoad>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
-                                             Prefetch<PF>& pf, bool use_pf, Refill refill) {
-  constexpr int B = STREAM_BATCH;
+                                             Stream<B>& st, bool have, NextLoad next_load) {
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
   float acc = 0.f;
   const float* vlane = L.vec + lane * 8;
-  const int npf = use_pf ? pf.n : 0;
-  auto consume = [&](const u32x4& w) {
-    acc += dot8(w, vlane + seg * CHUNK_COLS);
-    if (++seg == C) {
+  // Every slot is consumed (a slot past the range contributes zero and does not advance the
+  // row), so no branch sits between a load and the use of its registers.
+  auto consume = [&](const u32x4& w, bool valid) {
+    const float d = dot8(w, vlane + seg * CHUNK_COLS);
+    acc += valid ? d : 0.f;
+    seg += valid ? 1 : 0;
+    if (seg == C) {
       const float s = wave_sum(acc);
       if (lane == 0) L.part[row * NCOMP + c] = s;
       acc = 0.f;
@@ -472,52 +484,25 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
       ++row;
     }
   };
-  const __amdgpu_buffer_rsrc_t rs = rsrc(packed + r.base);  // block base; offsets stay below 4 GB
-  const uint32_t lane_off = (uint32_t)lane * 16u;
-  auto load_batch = [&](u32x4* w, int jb) {
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const int jc = jb + u < ihi ? jb + u : ihi - 1;
-      w[u] = nt_load(rs, lane_off, (uint32_t)jc * CHUNK_BYTES);
-    }
-  };
   auto consume_batch = [&](const u32x4* w, int jb) {
 #pragma unroll
-    for (int u = 0; u < B; ++u)
-      if (jb + u < ihi) consume(w[u]);
+    for (int u = 0; u < B; ++u) consume(w[u], jb + u < ihi);
   };
-  const int j0 = i + npf;
-  const int nbatch = ihi > j0 ? (ihi - j0 + B - 1) / B : 0;
-  if (nbatch == 0) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (u < npf) consume(pf.v[u]);
-    refill();
-  } else {
-    u32x4 wa[B], wb[B];
-    load_batch(wa, j0);  // first streamed batch, issued before the prefetched chunks are consumed
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (u < npf) consume(pf.v[u]);
-    int jb = j0;
-    for (int b = 0;; b += 2) {
-      if (b + 1 >= nbatch) {  // wa holds the last batch
-        refill();
-        consume_batch(wa, jb);
-        break;
-      }
-      load_batch(wb, jb + B);
-      consume_batch(wa, jb);
-      jb += B;
-      if (b + 2 >= nbatch) {  // wb holds the last batch
-        refill();
-        consume_batch(wb, jb);
-        break;
-      }
-      load_batch(wa, jb + B);
-      consume_batch(wb, jb);
-      jb += B;
-    }
+  u32x4* X = st.v;
+  u32x4* Y = st.v + B;
+  const int nb = (ihi - i + B - 1) / B;
+  const int nbe = nb + (nb & 1);  // an even batch count: the last reloads always go to X, then Y
+  if (!have) {
+    load_gemv_batch<B>(X, packed, r, 0, lane);
+    load_gemv_batch<B>(Y, packed, r, 1, lane);
+  }
+  for (int b = 0; b < nbe; b += 2) {
+    consume_batch(X, i + b * B);
+    if (b + 2 < nbe) load_gemv_batch<B>(X, packed, r, b + 2, lane);
+    else next_load(X, 0);
+    consume_batch(Y, i + (b + 1) * B);
+    if (b + 2 < nbe) load_gemv_batch<B>(Y, packed, r, b + 3, lane);
+    else next_load(Y, 1);
   }
   if (seg != 0) {
     const float s = wave_sum(acc);
@@ -671,7 +656,7 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
 // load form for all lanes keeps the loads of a batch independent (a per-lane choice between two
 // forms writing the same registers makes the compiler wait for all outstanding loads).
 // (Positions past the range or at the current position load row 0 instead; the consumer
-// ignores those values, and the loads stay unconditional for the reason given at issue_prefetch.)
+// ignores those values, and the loads stay unconditional, see the weight streaming above.)
 template <int HD>
 __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t j, int64_t whi,
                                         int64_t cur, int dseg, u32x4& kw, u32x4& vw) {
@@ -685,23 +670,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache,
   return rsrc(cache + kvrow0 * hd);
 }
 
-// Prefetch of an attention tile (wave k): K and V of this wave's first PF/2 position groups
-// (the ring compute_attention runs on), issued while the previous tile (QKV) streams.  The
-// cache rows do not depend on this step's q; the current position's row is never loaded (it
-// comes from LDS).  pf.n is the number of groups of the wave's range.
-template <int HD, int PF>
-__device__ __forceinline__ void issue_kv_prefetch(Prefetch<PF>& pf, const KernelArgs& a, int k, int layer, int g,
-                                                  int sp, int64_t L_att, int c, int lane) {
+// Half h of the first B (K, V) position-group pairs of an attention split (pairs h*B/2 ..
+// h*B/2 + B/2 - 1) into w[0, B): the opening of the ring compute_attention runs on, loaded while
+// the previous tile (QKV) streams.  The cache rows do not depend on this step's q; the current
+// position's row is never loaded (it comes from LDS).
+template <int HD, int B>
+__device__ __forceinline__ void load_kv_half(u32x4* w, const KernelArgs& a, int layer, int g, int sp, int64_t L_att,
+                                             int h, int c, int lane) {
   constexpr int LPP = HD / 8, P = 64 / LPP;
   const AttnRange r = attn_range(a, sp, c, L_att);
-  pf.k = k;
-  pf.n = r.whi > r.wlo ? (int)((r.whi - r.wlo + P - 1) / P) : 0;
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
   const int pp = lane / LPP, dseg = lane % LPP;
 #pragma unroll
-  for (int j = 0; j < PF / 2; ++j)
-    load_kv<HD>(rk, rv, r.wlo + j * P + pp, r.whi, L_att - 1, dseg, pf.v[2 * j], pf.v[2 * j + 1]);
+  for (int s = 0; s < B / 2; ++s)
+    load_kv<HD>(rk, rv, r.wlo + (int64_t)(h * (B / 2) + s) * P + pp, r.whi, L_att - 1, dseg, w[2 * s], w[2 * s + 1]);
 }
 
 template <int HD>
@@ -711,16 +694,16 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 }
 
 // compute wave: one share of an attention split.  The position groups run through a ring of
-// D = PF/2 (K, V) register pairs -- the prefetch registers themselves, filled with the first D
-// groups while the previous tile streamed: each step consumes one slot and reloads it with the
-// group D steps ahead (past the range the reload re-reads row 0, a cached dummy; every load is
-// unconditional for the reason given at issue_prefetch).  after() then reuses the registers for
-// the next tile's prefetch.
-template <int HD, int G, int PF, typename After>
+// D = B (K, V) register pairs -- the stream registers themselves, filled with the first D groups
+// while the previous tile streamed: each step consumes one slot and reloads it with the group D
+// steps ahead (past the range the reload re-reads row 0, a cached dummy; every load is
+// unconditional, see the weight streaming above).  after() then reuses the registers to fetch
+// the next GEMV tile's first batches.
+template <int HD, int G, int B, typename After>
 __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
-                                                  int g, int sp, int64_t L_att, Prefetch<PF>& pf, After after) {
+                                                  int g, int sp, int64_t L_att, Stream<B>& pf, After after) {
   constexpr int PS = pstride<HD>();
-  constexpr int D = PF / 2;
+  constexpr int D = B;  // ring slots: (K, V) pairs in the 2B stream registers
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
@@ -743,19 +726,19 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
+  // branch-free with respect to the loaded registers: the current position's row is selected
+  // from LDS, positions past the range are masked in the softmax update
   auto consume1 = [&](int64_t jb, const u32x4& kw, const u32x4& vw) {
     const int64_t j = jb + pp;
     const bool valid = j < whi;
+    const bool is_cur = j == cur;
     float kf[8], vf[8];
-    if (j == cur) {
+    unpack8<HD>(kw, kf);
+    unpack8<HD>(vw, vf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kf[e] = kc[dseg * 8 + e];
-        vf[e] = vc[dseg * 8 + e];
-      }
-    } else {
-      unpack8<HD>(kw, kf);
-      unpack8<HD>(vw, vf);
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = is_cur ? kc[dseg * 8 + e] : kf[e];
+      vf[e] = is_cur ? vc[dseg * 8 + e] : vf[e];
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -770,15 +753,14 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       d1 = fmaf(q1.w, kf[7], d1);
       float s = d0 + d1;
       s = LPP == 8 ? sum8(s) : sum16(s);
-      if (valid) {
-        const float mn = fmaxf(m[h], s);
-        const float al = __builtin_amdgcn_exp2f(m[h] - mn);
-        const float p = __builtin_amdgcn_exp2f(s - mn);
-        l[h] = l[h] * al + p;
+      // online-softmax update; a masked position leaves the state unchanged (al = 1, p = 0)
+      const float mn = valid ? fmaxf(m[h], s) : m[h];
+      const float al = valid ? __builtin_amdgcn_exp2f(m[h] - mn) : 1.0f;
+      const float p = valid ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
+      l[h] = l[h] * al + p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
-        m[h] = mn;
-      }
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
+      m[h] = mn;
     }
   };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
@@ -789,7 +771,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int gi = g0 + s;
-      if (gi < ngroups) consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);
+      consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
       load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
     }
   }
@@ -959,6 +941,11 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
   return rs;
 }
 
+// one trace word of (step, wave k, worker bid)
+__device__ __forceinline__ void trace_word(const KernelArgs& a, int step, int k, int bid, int word) {
+  a.trace[(((int64_t)step * a.n_waves + k) * a.W + bid) * TRACE_WORDS + word] = wall_clock64();
+}
+
 // ---------------------------------------------------------------------------
 // control wave loop
 // ---------------------------------------------------------------------------
@@ -991,6 +978,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       if (a.trace) t_pro = wall_clock64();
       const float rs = lds_prologue<HD, G>(a, L, 0, lane, t, layer, pos);
       __syncthreads();  // A: inputs ready
+      if (a.trace && lane == 0) trace_word(a, step, k, bid, 7);
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
         const int C = t.kpad / CHUNK_COLS;
@@ -1072,7 +1060,6 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         tr[1] = t_pro;
         tr[2] = t_cmp ? t_cmp : t_pro;
         tr[3] = t1;
-        tr[4] = t1;
       }
     }
   }
@@ -1090,10 +1077,17 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
 template <int HD, int G>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
+  constexpr int B = STREAM_BATCH;
   const int c = wave - 1;
   volatile int* smi = reinterpret_cast<volatile int*>(L.small);
-  Prefetch<(G >= 3 ? 8 : PREFETCH_CHUNKS)> pf;
-  issue_prefetch(pf, next_gemv(L.segs, a.n_waves, -1, block_rows, c), a.packed, lane);
+  Stream<B> st;
+  {
+    const Range r = next_gemv(L.segs, a.n_waves, -1, block_rows, c);
+    load_gemv_batch<B>(st.v, a.packed, r, 0, lane);
+    load_gemv_batch<B>(st.v + B, a.packed, r, 1, lane);
+    st.k = r.k;
+    st.r0 = r.r0;
+  }
   int tok_unused = 0;
   bool stop = false;
   for (int step = 0; step < a.n_steps && !stop; ++step) {
@@ -1105,6 +1099,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const WaveDesc wd = a.waves[k];
       const int layer = wd.layer;
       if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 5);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1112,33 +1107,43 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       }
       lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
       __syncthreads();  // A
+      if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 6);
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
         const SegDesc sd = L.segs[k];
-        // the prefetch issued at the end of this tile: KV rows when this worker's next tile
-        // is an attention split, else the weights of its next GEMV tile
+        // what the registers fetch once this block's last batches are in flight: the next block,
+        // the KV rows of this worker's attention split when that is its next tile, or the next
+        // GEMV tile
         const TileDesc tn = a.tiles[(int64_t)(k + 1 < a.n_waves ? k + 1 : 0) * a.W + bid];
         const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
-        auto refill_next = [&]() {
-          if (next_attn) issue_kv_prefetch<HD>(pf, a, k + 1, layer, tn.row0, tn.nrows, L_att, c, lane);
-          else issue_prefetch(pf, next_gemv(L.segs, a.n_waves, k, block_rows, c), a.packed, lane);
-        };
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const Range r = block_range(sd, k, r0, block_rows, c);
           const bool last_block = r0 + block_rows >= rows;
           if (r.i < r.ihi) {
-            if (last_block) stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, refill_next);
-            else stream_range(L, a.packed, r, c, lane, pf, r0 == 0 && pf.k == k, []() {});
-          } else if (last_block) {
-            refill_next();
+            const Range nr = !last_block ? block_range(sd, k, r0 + block_rows, block_rows, c)
+                             : next_attn ? no_range()
+                                         : next_gemv(L.segs, a.n_waves, k, block_rows, c);
+            const bool kv_next = last_block && next_attn;
+            stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](u32x4* w, int h) {
+              if (kv_next) load_kv_half<HD, B>(w, a, layer, tn.row0, tn.nrows, L_att, h, c, lane);
+              else load_gemv_batch<B>(w, a.packed, nr, h, lane);
+            });
+            st.k = kv_next ? k + 1 : nr.k;
+            st.r0 = kv_next ? 0 : nr.r0;
           }
+          if (a.trace && c == 0 && r0 == 0 && lane == 0) trace_word(a, step, k, bid, 4);
           __syncthreads();                              // B
           if (r0 + block_rows < rows) __syncthreads();  // C
         }
       } else if (t.kind == KIND_ATTN) {
-        compute_attention<HD, G>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, pf, [&]() {
-          issue_prefetch(pf, next_gemv(L.segs, a.n_waves, k, block_rows, c), a.packed, lane);
+        compute_attention<HD, G, B>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&]() {
+          const Range nr = next_gemv(L.segs, a.n_waves, k, block_rows, c);
+          load_gemv_batch<B>(st.v, a.packed, nr, 0, lane);
+          load_gemv_batch<B>(st.v + B, a.packed, nr, 1, lane);
+          st.k = nr.k;
+          st.r0 = nr.r0;
         });
+        if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 4);
         __syncthreads();  // B
         attn_merge_phase<HD, G>(L, wave, lane);
         __syncthreads();  // E

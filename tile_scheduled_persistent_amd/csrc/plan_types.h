@@ -66,9 +66,12 @@ constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = a wait's wat
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
 constexpr int SYNC_WORDS = 32;
 
-// In-kernel trace record per (step, wave, worker): wave start, inputs staged, compute done,
-// outputs published, (same again; kept for the record layout) -- 100 MHz wall clock.
-constexpr int TRACE_WORDS = 5;
+// In-kernel trace record per (step, wave, worker), 100 MHz wall clock:
+//   0 wave start, 1 inputs staged (after barrier P), 2 compute done (after barrier B),
+//   3 outputs published, 7 after barrier A  -- all taken by the control wave;
+//   5 own gather done (before P), 6 after barrier A, 4 own share of the tile done (before B)
+//   -- taken by the first compute wave (4 stays 0 when it had no share).
+constexpr int TRACE_WORDS = 8;
 
 // Tagged-data buffers are filled with this word before every launch: a quiet NaN whose
 // parity bit (bit 0) is 0, so that step 0 (parity 1) never mistakes it for a value.

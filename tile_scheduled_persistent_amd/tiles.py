@@ -30,6 +30,7 @@ TILES_E_KERNEL = -6
 
 TILES_DEBUG_HIDDEN = 0x1
 TILES_TRACE = 0x2
+TRACE_WORDS = 8  # see tiles_read_debug in include/tiles.h
 TILES_POISON = 0x4
 
 WAVE_KINDS = {1: "qkv", 2: "attn", 3: "combine", 4: "o_proj", 5: "gate_up", 6: "down", 7: "lm_head"}
@@ -243,7 +244,7 @@ class Plan:
         return out
 
     def read_debug(self, hidden: bool = True, trace: bool = False):
-        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, 5] uint64 or None)."""
+        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, TRACE_WORDS] uint64 or None)."""
         info = self.info()
         n = ctypes.c_int32(0)
         _check(lib().tiles_read_debug(self._h, None, None, ctypes.byref(n)))
@@ -253,7 +254,7 @@ class Plan:
             hid = np.zeros((n.value, self.model.n_layers, self.model.hidden), dtype=np.float32)
             hp = hid.ctypes.data
         if trace:
-            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, 5), dtype=np.uint64)
+            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, TRACE_WORDS), dtype=np.uint64)
             tp = tr.ctypes.data
         _check(lib().tiles_read_debug(self._h, hp, tp, None))
         return hid, tr
