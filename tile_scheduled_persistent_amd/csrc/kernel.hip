@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan_types.h"
 
 namespace tiles {
@@ -139,6 +141,25 @@ __device__ __forceinline__ float sum16(float v) {
   v += dpp<DPP_MIRROR>(v);
   return v;
 }
+// Lane exchanges across 8, 16 and 32 lanes without the LDS crossbar: a DPP rotation by 8
+// within each 16-lane row, and the gfx950 permlane swaps of 16-lane rows and 32-lane halves.
+__device__ __forceinline__ float xor8(float v) { return dpp<0x128>(v); }  // row_ror:8
+__device__ __forceinline__ float xor16(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(lane >= 32 ? r[0] : r[1]);
+}
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane_xor offsets: 8, 16, 32");
+  if constexpr (OFF == 8) return xor8(v);
+  else if constexpr (OFF == 16) return xor16(v, lane);
+  else return xor32(v, lane);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v = sum16(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -726,20 +747,10 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  // branch-free with respect to the loaded registers: the current position's row is selected
-  // from LDS, positions past the range are masked in the softmax update
-  auto consume1 = [&](int64_t jb, const u32x4& kw, const u32x4& vw) {
-    const int64_t j = jb + pp;
-    const bool valid = j < whi;
-    const bool is_cur = j == cur;
-    float kf[8], vf[8];
-    unpack8<HD>(kw, kf);
-    unpack8<HD>(vw, vf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kf[e] = is_cur ? kc[dseg * 8 + e] : kf[e];
-      vf[e] = is_cur ? vc[dseg * 8 + e] : vf[e];
-    }
+  // One position group (this lane's position j, 8 dims) into the online softmax of every query
+  // head; branch-free with respect to the loaded registers: an invalid position (past the
+  // range, or the current one, which is handled apart from LDS) is masked in the update.
+  auto update = [&](bool valid, const float* kf, const float* vf) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
@@ -763,6 +774,13 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       m[h] = mn;
     }
   };
+  auto consume1 = [&](int64_t jb, const u32x4& kw, const u32x4& vw) {
+    const int64_t j = jb + pp;
+    float kf[8], vf[8];
+    unpack8<HD>(kw, kf);
+    unpack8<HD>(vw, vf);
+    update(j < whi && j != cur, kf, vf);
+  };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
     for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
@@ -776,26 +794,38 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
     }
   }
   after();
-  // merge the P position groups of this wave (lanes differing by multiples of LPP)
+  if (wlo <= cur && cur < whi) {  // the current position (its K/V row is in LDS): lane group 0
+    float kf[8], vf[8];
 #pragma unroll
-  for (int off = LPP; off < 64; off <<= 1) {
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = kc[dseg * 8 + e];
+      vf[e] = vc[dseg * 8 + e];
+    }
+    update(pp == 0, kf, vf);
+  }
+  // merge the P position groups of this wave (lanes differing by multiples of LPP)
+  auto merge_lanes = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(m[h], off);
-      const float l2 = __shfl_xor(l[h], off);
+      const float m2 = lane_xor<OFF>(m[h], lane);
+      const float l2 = lane_xor<OFF>(l[h], lane);
       float a2[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[h][e], off);
+      for (int e = 0; e < 8; ++e) a2[e] = lane_xor<OFF>(acc[h][e], lane);
       const float mn = fmaxf(m[h], m2);
-      if (mn != -INFINITY) {
-        const float f1 = __builtin_amdgcn_exp2f(m[h] - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);
-        l[h] = l[h] * f1 + l2 * f2;
+      const bool live = mn != -INFINITY;
+      const float f1 = live ? __builtin_amdgcn_exp2f(m[h] - mn) : 0.f;
+      const float f2 = live ? __builtin_amdgcn_exp2f(m2 - mn) : 0.f;
+      l[h] = l[h] * f1 + l2 * f2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * f1 + a2[e] * f2;
-        m[h] = mn;
-      }
+      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * f1 + a2[e] * f2;
+      m[h] = mn;
     }
-  }
+  };
+  if constexpr (LPP == 8) merge_lanes(std::integral_constant<int, 8>{});
+  merge_lanes(std::integral_constant<int, 16>{});
+  merge_lanes(std::integral_constant<int, 32>{});
   if (pp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
