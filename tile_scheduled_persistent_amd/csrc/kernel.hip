@@ -56,6 +56,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SC1 = 16;  // buffer-instruction cache policy bit: device-coherent access
+constexpr int NT = 2;    // buffer-instruction cache policy bit: non-temporal (streamed once)
 
 // ---------------------------------------------------------------------------
 // coherent memory helpers
@@ -79,12 +80,7 @@ __device__ __forceinline__ u32x4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_of
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, SC1);
 }
 #define COMPILER_FENCE() asm volatile("" ::: "memory")
-constexpr int NT = 2;    // buffer-instruction cache policy bit: non-temporal (streamed once)
-// Streaming 16-byte load: base in scalar registers (the descriptor), one per-lane byte offset
-// shared by every load of a wave, and a wave-uniform chunk offset.
-__device__ __forceinline__ u32x4 nt_load(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, uniform_off, NT);
-}
+
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -465,26 +461,65 @@ struct Stream {
   int r0;  // GEMV block of that wave
 };
 
-// Batch q of GEMV range r into w[0, B): chunks r.i + q*B + u, clamped to the range's last chunk
-// (a range with no chunks reads the first KB of the packed buffer).
+// Source of the B loads of one batch: per slot a buffer descriptor, a per-lane byte offset and a
+// wave-uniform byte offset.  The loads themselves are always the same instruction sequence;
+// only these operands are selected (uniformly, without branches) between the sources.
 template <int B>
-__device__ __forceinline__ void load_gemv_batch(u32x4* w, const uint8_t* packed, const Range& r, int q, int lane) {
+struct BatchSrc {
+  __amdgpu_buffer_rsrc_t d[B];
+  uint32_t vo[B];
+  uint32_t so[B];
+};
+
+// Batch q of GEMV range r: chunks r.i + q*B + u, clamped to the range's last chunk (a range
+// with no chunks reads the first KB of the packed buffer).
+template <int B>
+__device__ __forceinline__ BatchSrc<B> gemv_src(const uint8_t* packed, const Range& r, int q, int lane) {
+  BatchSrc<B> b;
   const bool any = r.i < r.ihi;
   const __amdgpu_buffer_rsrc_t rs = rsrc(packed + (any ? r.base : 0));
 #pragma unroll
   for (int u = 0; u < B; ++u) {
     const int j = r.i + q * B + u;
     const int jc = any ? (j < r.ihi ? j : r.ihi - 1) : 0;
-    w[u] = nt_load(rs, (uint32_t)lane * 16u, (uint32_t)jc * CHUNK_BYTES);
+    b.d[u] = rs;
+    b.vo[u] = (uint32_t)lane * 16u;
+    b.so[u] = (uint32_t)jc * CHUNK_BYTES;
   }
+  return b;
+}
+
+template <int B>
+__device__ __forceinline__ BatchSrc<B> select_src(bool first, const BatchSrc<B>& x, const BatchSrc<B>& y) {
+  BatchSrc<B> b;
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    b.d[u] = first ? x.d[u] : y.d[u];
+    b.vo[u] = first ? x.vo[u] : y.vo[u];
+    b.so[u] = first ? x.so[u] : y.so[u];
+  }
+  return b;
+}
+
+// Non-temporal 16-byte loads for every stream (weights and KV rows alike; see load_kv for why
+// that is coherent for KV rows): one load form for all sources.
+template <int B>
+__device__ __forceinline__ void load_batch(u32x4* w, const BatchSrc<B>& b) {
+#pragma unroll
+  for (int u = 0; u < B; ++u) w[u] = __builtin_amdgcn_raw_buffer_load_b128(b.d[u], b.vo[u], b.so[u], NT);
+}
+
+template <int B>
+__device__ __forceinline__ void load_gemv_batch(u32x4* w, const uint8_t* packed, const Range& r, int q, int lane) {
+  load_batch<B>(w, gemv_src<B>(packed, r, q, lane));
 }
 
 // Consume chunks [r.i, r.ihi) in batches; st holds batches 0 and 1 when `have` (else they are
 // loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the last
-// batches run next_load(w, 0) into X and next_load(w, 1) into Y.
-template <int B, typename NextLoad>
+// batches fetch next_src(0) into X and next_src(1) into Y.
+template <int B, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
-                                             Stream<B>& st, bool have, NextLoad next_load) {
+                                             Stream<B>& st, bool have, NextSrc next_src) {
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
@@ -518,12 +553,13 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
     load_gemv_batch<B>(Y, packed, r, 1, lane);
   }
   for (int b = 0; b < nbe; b += 2) {
+    const bool more = b + 2 < nbe;
     consume_batch(X, i + b * B);
-    if (b + 2 < nbe) load_gemv_batch<B>(X, packed, r, b + 2, lane);
-    else next_load(X, 0);
+    load_batch<B>(X, select_src<B>(more, gemv_src<B>(packed, r, b + 2, lane), next_src(0)));
+    __builtin_amdgcn_sched_barrier(0);  // keep the reload of X ahead of the consumption of Y
     consume_batch(Y, i + (b + 1) * B);
-    if (b + 2 < nbe) load_gemv_batch<B>(Y, packed, r, b + 3, lane);
-    else next_load(Y, 1);
+    load_batch<B>(Y, select_src<B>(more, gemv_src<B>(packed, r, b + 3, lane), next_src(1)));
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (seg != 0) {
     const float s = wave_sum(acc);
@@ -671,24 +707,47 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
   return r;
 }
 
-// K and V of position j of KV head (layer, g) for this lane's 16-byte segment; zero for the
-// current position (taken from LDS) and past the range.  Every row is read with a
-// device-coherent load: rows written earlier in this launch by other workers need it, and one
-// load form for all lanes keeps the loads of a batch independent (a per-lane choice between two
-// forms writing the same registers makes the compiler wait for all outstanding loads).
-// (Positions past the range or at the current position load row 0 instead; the consumer
-// ignores those values, and the loads stay unconditional, see the weight streaming above.)
+// K and V of position j of KV head (layer, g) for this lane's 16-byte segment.  Every stream
+// of the compute waves (weights and KV rows alike) uses the same non-temporal 16-byte load, so
+// that one instruction sequence serves whichever source a batch comes from.  That is coherent
+// for KV rows because, within a launch, no row is read before this launch writes it: real
+// reads only touch positions before the current one (written in earlier steps, completed
+// before any output this worker's readers depend on), and a slot that has no position -- past
+// the range, or the current position, taken from LDS -- reads the cache's last row
+// (capacity - 1) instead, which is never read for real (a position is read only in later
+// steps, and none follows the last one); rows from earlier launches are covered by the cache
+// maintenance at kernel boundaries.  The consumer masks those slots.
 template <int HD>
 __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t j, int64_t whi,
-                                        int64_t cur, int dseg, u32x4& kw, u32x4& vw) {
+                                        int64_t cur, int64_t dummy, int dseg, u32x4& kw, u32x4& vw) {
   constexpr int LPP = HD / 8;
-  const int64_t jj = (j < whi && j != cur) ? j : 0;
+  const int64_t jj = (j < whi && j != cur) ? j : dummy;
   const uint32_t off = (uint32_t)((jj * LPP + dseg) * 16);
-  kw = cld4(rk, off);
-  vw = cld4(rv, off);
+  kw = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, NT);
+  vw = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, NT);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache, int64_t kvrow0, int hd) {
   return rsrc(cache + kvrow0 * hd);
+}
+
+// Where an attention split's opening loads come from: descriptors of the KV head and this
+// wave's position range, computed once (outside the streaming loop that issues the loads).
+struct KvOpen {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int64_t wlo, whi, cur, dummy;
+};
+template <int HD>
+__device__ __forceinline__ KvOpen kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c) {
+  KvOpen o;
+  const AttnRange r = attn_range(a, sp, c, L_att);
+  const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
+  o.rk = kv_rsrc(a.kv_k, kvrow0, HD);
+  o.rv = kv_rsrc(a.kv_v, kvrow0, HD);
+  o.wlo = r.wlo;
+  o.whi = r.whi;
+  o.cur = L_att - 1;
+  o.dummy = a.kv_cap - 1;
+  return o;
 }
 
 // Half h of the first B (K, V) position-group pairs of an attention split (pairs h*B/2 ..
@@ -696,16 +755,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache,
 // the previous tile (QKV) streams.  The cache rows do not depend on this step's q; the current
 // position's row is never loaded (it comes from LDS).
 template <int HD, int B>
-__device__ __forceinline__ void load_kv_half(u32x4* w, const KernelArgs& a, int layer, int g, int sp, int64_t L_att,
-                                             int h, int c, int lane) {
+__device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen& o, int h, int lane) {
   constexpr int LPP = HD / 8, P = 64 / LPP;
-  const AttnRange r = attn_range(a, sp, c, L_att);
-  const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
-  const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
   const int pp = lane / LPP, dseg = lane % LPP;
+  BatchSrc<B> b;
 #pragma unroll
-  for (int s = 0; s < B / 2; ++s)
-    load_kv<HD>(rk, rv, r.wlo + (int64_t)(h * (B / 2) + s) * P + pp, r.whi, L_att - 1, dseg, w[2 * s], w[2 * s + 1]);
+  for (int s = 0; s < B / 2; ++s) {
+    const int64_t j = o.wlo + (int64_t)(h * (B / 2) + s) * P + pp;
+    const int64_t jj = (j < o.whi && j != o.cur) ? j : o.dummy;
+    const uint32_t off = (uint32_t)((jj * LPP + dseg) * 16);
+    b.d[2 * s] = o.rk;
+    b.d[2 * s + 1] = o.rv;
+    b.vo[2 * s] = b.vo[2 * s + 1] = off;
+    b.so[2 * s] = b.so[2 * s + 1] = 0;
+  }
+  return b;
 }
 
 template <int HD>
@@ -739,6 +803,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const int pp = lane / LPP, dseg = lane % LPP;
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
+  const int64_t dummy = a.kv_cap - 1;
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -783,14 +848,15 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+    for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
   }
   for (int g0 = 0; g0 < ngroups; g0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int gi = g0 + s;
       consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
-      load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+      load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
     }
   }
   after();
@@ -1154,9 +1220,9 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                              : next_attn ? no_range()
                                          : next_gemv(L.segs, a.n_waves, k, block_rows, c);
             const bool kv_next = last_block && next_attn;
-            stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](u32x4* w, int h) {
-              if (kv_next) load_kv_half<HD, B>(w, a, layer, tn.row0, tn.nrows, L_att, h, c, lane);
-              else load_gemv_batch<B>(w, a.packed, nr, h, lane);
+            const KvOpen ko = kv_open<HD>(a, layer, tn.row0, tn.nrows, L_att, c);
+            stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](int h) {
+              return select_src<B>(kv_next, kv_half_src<HD, B>(ko, h, lane), gemv_src<B>(a.packed, nr, h, lane));
             });
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
