@@ -174,6 +174,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 constexpr int SM_ABORT = 0;  // int: some wavefront gave up waiting (all leave after barrier P)
 constexpr int SM_SS = 8;     // float[NWAVES]: sums of squares of each wavefront's share of x
+constexpr int SM_ROPE = 256;   // float[head_dim]: (cos, sin) pairs of the current position (attention tiles)
+constexpr int SM_QGAIN = 512;  // float[head_dim]: q-norm gains (attention tiles with q/k norm)
+constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
 
 struct Lds {
   float* vec;
@@ -181,7 +184,44 @@ struct Lds {
   float* xres;
   float* small;
   SegDesc* segs;
+  TileDesc* tiles;      // this worker's tile of every wave
+  WaveDesc* waves;      // every wave's descriptor
+  LayerSmall* lsmall;   // per-layer gain offsets
 };
+
+// The schedule tables live in LDS for the whole launch: read from global memory they are cold
+// every time (each entry is used once per token) and each read would wait behind the weight
+// stream.  Values read from LDS are per-lane to the compiler; readfirstlane makes them scalar.
+__device__ __forceinline__ int sc(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t sc64(int64_t v) {
+  return ((int64_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+__device__ __forceinline__ TileDesc tile_of(const Lds& L, int k) {
+  const TileDesc x = L.tiles[k];
+  TileDesc t;
+  t.kind = sc(x.kind);
+  t.row0 = sc(x.row0);
+  t.nrows = sc(x.nrows);
+  t.kpad = sc(x.kpad);
+  t.woff = sc64(x.woff);
+  t.aux0 = 0;
+  t.aux1 = 0;
+  return t;
+}
+__device__ __forceinline__ WaveDesc wave_of(const Lds& L, int k) {
+  const WaveDesc x = L.waves[k];
+  WaveDesc w;
+  w.kind = sc(x.kind);
+  w.layer = sc(x.layer);
+  w.max_rows = sc(x.max_rows);
+  w.ll_off = sc(x.ll_off);
+  return w;
+}
+__device__ __forceinline__ int64_t gain_off(const Lds& L, int layer, int which) {  // 0 attn, 1 mlp, 2 q, 3 k
+  const LayerSmall& x = L.lsmall[layer];
+  return sc64(which == 0 ? x.attn_norm : which == 1 ? x.mlp_norm : which == 2 ? x.q_norm : x.k_norm);
+}
 
 __device__ __forceinline__ bool is_gemv(int kind) {
   return kind == KIND_QKV || kind == KIND_O || kind == KIND_GU || kind == KIND_DOWN || kind == KIND_LM;
@@ -644,18 +684,17 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
       u0 = raw[u * HD + lane];
       u1 = raw[u * HD + lane + HALF];
     }
-    if (a.small[layer].q_norm >= 0) {
+    if (gain_off(L, layer, 2) >= 0) {
       const float ss = wave_sum(u0 * u0 + u1 * u1);
       const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
-      const uint16_t* gn =
-          reinterpret_cast<const uint16_t*>(a.packed + (u < G ? a.small[layer].q_norm : a.small[layer].k_norm));
+      const float* gn = L.small + (u < G ? SM_QGAIN : SM_KGAIN);
       if (lane < HALF) {
-        u0 = u0 * rs * bf16_to_f32(gn[lane]);
-        u1 = u1 * rs * bf16_to_f32(gn[lane + HALF]);
+        u0 = u0 * rs * gn[lane];
+        u1 = u1 * rs * gn[lane + HALF];
       }
     }
     if (lane < HALF) {
-      const float* cs = a.rope + ((int64_t)pos * HALF + lane) * 2;
+      const float* cs = L.small + SM_ROPE + lane * 2;
       const float co = cs[0], si = cs[1];
       const float r0 = u0 * co - u1 * si;
       const float r1 = u1 * co + u0 * si;
@@ -964,7 +1003,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
                                               int& tok) {
   constexpr int PS = pstride<HD>();
   const int layer = wd.layer;
-  const uint32_t* in = a.ll + (k > 0 ? a.waves[k - 1].ll_off : 0);
+  const uint32_t* in = a.ll + (k > 0 ? wave_of(L, k - 1).ll_off : 0);
   // Every worker gathers x in the QKV and gate/up waves, tile or not: the o_proj and down
   // epilogues add their rows to the residual staged there.
   const int gk = (wd.kind == KIND_QKV || wd.kind == KIND_GU) ? wd.kind : t.kind;
@@ -973,8 +1012,8 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
     case KIND_QKV:
     case KIND_GU:
     case KIND_LM: {
-      const int64_t goff = gk == KIND_QKV ? a.small[layer].attn_norm
-                           : gk == KIND_GU ? a.small[layer].mlp_norm
+      const int64_t goff = gk == KIND_QKV ? gain_off(L, layer, 0)
+                           : gk == KIND_GU ? gain_off(L, layer, 1)
                                            : a.final_norm_off;
       const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
       float ss = 0.f;
@@ -1002,9 +1041,35 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       ab = gather_plain(a, L.vec, in, a.F, wave, lane, par);
       for (int i = a.F + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
       break;
-    case KIND_ATTN:
+    case KIND_ATTN: {
+      // the control wave also stages the current position's RoPE row and the q/k-norm gains;
+      // the loads are issued before the poll and complete while it waits for the producers
+      constexpr int HALF = HD / 2;
+      float2 cs = {0.f, 0.f};
+      float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;
+      const int64_t qoff = gain_off(L, layer, 2);
+      if (wave == 0 && lane < HALF) {
+        cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(a.pos0 + step) * HALF + lane) * 2);
+        if (qoff >= 0) {
+          const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.packed + qoff);
+          const uint16_t* gkk = reinterpret_cast<const uint16_t*>(a.packed + gain_off(L, layer, 3));
+          gq0 = bf16_to_f32(gq[lane]);
+          gq1 = bf16_to_f32(gq[lane + HALF]);
+          gk0 = bf16_to_f32(gkk[lane]);
+          gk1 = bf16_to_f32(gkk[lane + HALF]);
+        }
+      }
       ab = gather_qkv<HD, G>(a, L, in, t.row0, wave, lane, par);
+      if (wave == 0 && lane < HALF) {
+        L.small[SM_ROPE + 2 * lane] = cs.x;
+        L.small[SM_ROPE + 2 * lane + 1] = cs.y;
+        L.small[SM_QGAIN + lane] = gq0;
+        L.small[SM_QGAIN + lane + HALF] = gq1;
+        L.small[SM_KGAIN + lane] = gk0;
+        L.small[SM_KGAIN + lane + HALF] = gk1;
+      }
       break;
+    }
     case KIND_COMBINE:
       ab = gather_plain(a, L.part, in + (int64_t)t.row0 * a.S * PS, a.S * PS, wave, lane, par);
       break;
@@ -1059,8 +1124,8 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
     float lm_best = -INFINITY;
     int lm_idx = 0x7fffffff;
     for (int k = 0; k < a.n_waves; ++k) {
-      const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
-      const WaveDesc wd = a.waves[k];
+      const TileDesc t = tile_of(L, k);
+      const WaveDesc wd = wave_of(L, k);
       const int layer = wd.layer;
       uint32_t* out = a.ll + (wd.ll_off >= 0 ? wd.ll_off : 0);
       uint64_t t0 = 0, t_pro = 0, t_cmp = 0;
@@ -1191,8 +1256,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
     const int pos = a.pos0 + step;
     const int64_t L_att = (int64_t)pos + 1;
     for (int k = 0; k < a.n_waves; ++k) {
-      const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
-      const WaveDesc wd = a.waves[k];
+      const TileDesc t = tile_of(L, k);
+      const WaveDesc wd = wave_of(L, k);
       const int layer = wd.layer;
       if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 5);
@@ -1210,7 +1275,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         // what the registers fetch once this block's last batches are in flight: the next block,
         // the KV rows of this worker's attention split when that is its next tile, or the next
         // GEMV tile
-        const TileDesc tn = a.tiles[(int64_t)(k + 1 < a.n_waves ? k + 1 : 0) * a.W + bid];
+        const TileDesc tn = tile_of(L, k + 1 < a.n_waves ? k + 1 : 0);
         const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const Range r = block_range(sd, k, r0, block_rows, c);
@@ -1258,6 +1323,9 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   L.xres = L.part + a.lds_part_floats;
   L.small = L.xres + a.lds_xres_floats;
   L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
+  L.tiles = reinterpret_cast<TileDesc*>(L.segs + a.n_waves);
+  L.waves = reinterpret_cast<WaveDesc*>(L.tiles + a.n_waves);
+  L.lsmall = reinterpret_cast<LayerSmall*>(L.waves + a.n_waves);
   const int tid = threadIdx.x, lane = tid & 63, bid = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int k = tid; k < a.n_waves; k += BLOCK_THREADS) {
@@ -1267,7 +1335,10 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
     s.chunks_per_row = t.kpad / CHUNK_COLS;
     s.rows = is_gemv(t.kind) ? (t.kind == KIND_GU ? 2 * t.nrows : t.nrows) : 0;
     L.segs[k] = s;
+    L.tiles[k] = t;
+    L.waves[k] = a.waves[k];
   }
+  for (int l = tid; l < a.n_layers; l += BLOCK_THREADS) L.lsmall[l] = a.small[l];
   if (tid == 0) reinterpret_cast<int*>(L.small)[SM_ABORT] = 0;
   __syncthreads();
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;

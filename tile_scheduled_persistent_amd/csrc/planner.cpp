@@ -315,8 +315,10 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
   p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64);
+  // schedule tables: per wave a SegDesc, this worker's TileDesc and the WaveDesc; per layer a LayerSmall
   p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
-                (int32_t)round_up((int64_t)p.waves.size() * (int64_t)sizeof(SegDesc), 256);
+                (int32_t)round_up((int64_t)p.waves.size() * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
+                                      (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
   if (p.lds_bytes > 160 * 1024) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
