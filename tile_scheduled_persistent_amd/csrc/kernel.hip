@@ -174,6 +174,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 constexpr int SM_ABORT = 0;  // int: some wavefront gave up waiting (all leave after barrier P)
 constexpr int SM_SS = 8;     // float[NWAVES]: sums of squares of each wavefront's share of x
+constexpr int SM_CTRACE = 32;  // uint64[2][8]: first compute wavefront's timestamps of a tile (set = tile parity)
 constexpr int SM_ROPE = 256;   // float[head_dim]: (cos, sin) pairs of the current position (attention tiles)
 constexpr int SM_QGAIN = 512;  // float[head_dim]: q-norm gains (attention tiles with q/k norm)
 constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
@@ -430,6 +431,14 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
 
 constexpr int STREAM_BATCH = 4;
 
+// Trace stamps of the first compute wavefront, kept in LDS (a global store would hold up the
+// wavefront's next wait on its loads, which counts stores too) and written out by the control
+// wavefront after barrier B.
+enum { TS_GATHERED, TS_AFTER_A, TS_ENTRY, TS_FIRST, TS_DONE, TS_COUNT };
+__device__ __forceinline__ void stamp(uint64_t* ts, int i, int lane) {
+  if (ts && lane == 0) ts[i] = wall_clock64();
+}
+
 __device__ __forceinline__ float dot8(const u32x4 w, const float* v) {
   const f32x4 v0 = *reinterpret_cast<const f32x4*>(v);
   const f32x4 v1 = *reinterpret_cast<const f32x4*>(v + 4);
@@ -559,7 +568,7 @@ __device__ __forceinline__ void load_gemv_batch(u32x4* w, const uint8_t* packed,
 // batches fetch next_src(0) into X and next_src(1) into Y.
 template <int B, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
-                                             Stream<B>& st, bool have, NextSrc next_src) {
+                                             Stream<B>& st, bool have, NextSrc next_src, uint64_t* ts) {
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
@@ -568,8 +577,8 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   const float* vlane = L.vec + lane * 8;
   // Every slot is consumed (a slot past the range contributes zero and does not advance the
   // row), so no branch sits between a load and the use of its registers.
-  auto consume = [&](const u32x4& w, bool valid) {
-    const float d = dot8(w, vlane + seg * CHUNK_COLS);
+  auto consume = [&](const u32x4& w, bool valid, const float* xv) {
+    const float d = dot8(w, xv);
     acc += valid ? d : 0.f;
     seg += valid ? 1 : 0;
     if (seg == C) {
@@ -580,9 +589,22 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
       ++row;
     }
   };
+  // The input-vector slices of a batch's chunks are read from LDS before any of them is used,
+  // so their latencies overlap (the row-end branches would otherwise serialise them).  A slot
+  // past the range reads a slice too (in bounds, masked).
   auto consume_batch = [&](const u32x4* w, int jb) {
+    float xv[B][8];
+    int s = seg;
 #pragma unroll
-    for (int u = 0; u < B; ++u) consume(w[u], jb + u < ihi);
+    for (int u = 0; u < B; ++u) {
+      const f32x4* px = reinterpret_cast<const f32x4*>(vlane + s * CHUNK_COLS);
+      const f32x4 x0 = px[0], x1 = px[1];
+      xv[u][0] = x0.x; xv[u][1] = x0.y; xv[u][2] = x0.z; xv[u][3] = x0.w;
+      xv[u][4] = x1.x; xv[u][5] = x1.y; xv[u][6] = x1.z; xv[u][7] = x1.w;
+      s = s + 1 == C ? 0 : s + 1;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) consume(w[u], jb + u < ihi, xv[u]);
   };
   u32x4* X = st.v;
   u32x4* Y = st.v + B;
@@ -592,11 +614,13 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
     load_gemv_batch<B>(X, packed, r, 0, lane);
     load_gemv_batch<B>(Y, packed, r, 1, lane);
   }
+  stamp(ts, TS_ENTRY, lane);
   for (int b = 0; b < nbe; b += 2) {
     const bool more = b + 2 < nbe;
     consume_batch(X, i + b * B);
     load_batch<B>(X, select_src<B>(more, gemv_src<B>(packed, r, b + 2, lane), next_src(0)));
     __builtin_amdgcn_sched_barrier(0);  // keep the reload of X ahead of the consumption of Y
+    if (b == 0) stamp(ts, TS_FIRST, lane);
     consume_batch(Y, i + (b + 1) * B);
     load_batch<B>(Y, select_src<B>(more, gemv_src<B>(packed, r, b + 3, lane), next_src(1)));
     __builtin_amdgcn_sched_barrier(0);
@@ -825,7 +849,8 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // the next GEMV tile's first batches.
 template <int HD, int G, int B, typename After>
 __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
-                                                  int g, int sp, int64_t L_att, Stream<B>& pf, After after) {
+                                                  int g, int sp, int64_t L_att, Stream<B>& pf, After after,
+                                                  uint64_t* ts) {
   constexpr int PS = pstride<HD>();
   constexpr int D = B;  // ring slots: (K, V) pairs in the 2B stream registers
   const float* q = L.part;
@@ -889,6 +914,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
   }
+  stamp(ts, TS_ENTRY, lane);
   for (int g0 = 0; g0 < ngroups; g0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -896,6 +922,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
       load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
+      if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
     }
   }
   after();
@@ -1102,10 +1129,6 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
   return rs;
 }
 
-// one trace word of (step, wave k, worker bid)
-__device__ __forceinline__ void trace_word(const KernelArgs& a, int step, int k, int bid, int word) {
-  a.trace[(((int64_t)step * a.n_waves + k) * a.W + bid) * TRACE_WORDS + word] = wall_clock64();
-}
 
 // ---------------------------------------------------------------------------
 // control wave loop
@@ -1129,6 +1152,8 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const int layer = wd.layer;
       uint32_t* out = a.ll + (wd.ll_off >= 0 ? wd.ll_off : 0);
       uint64_t t0 = 0, t_pro = 0, t_cmp = 0;
+      uint64_t cw[TS_COUNT] = {};  // the first compute wavefront's stamps, read after barrier B
+      const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
       if (gather_inputs<HD, G>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
@@ -1139,14 +1164,17 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       if (a.trace) t_pro = wall_clock64();
       const float rs = lds_prologue<HD, G>(a, L, 0, lane, t, layer, pos);
       __syncthreads();  // A: inputs ready
-      if (a.trace && lane == 0) trace_word(a, step, k, bid, 7);
+      const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
         const int C = t.kpad / CHUNK_COLS;
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const int nr = min(block_rows, rows - r0);
           __syncthreads();  // B: partials of this block ready
-          if (a.trace && r0 == 0) t_cmp = wall_clock64();
+          if (a.trace && r0 == 0) {
+            t_cmp = wall_clock64();
+            for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
+          }
           switch (t.kind) {
             case KIND_QKV:
               for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * row_total(L, nr, C, r), par);
@@ -1192,7 +1220,10 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         // the row depend on (its split partial, below); the wait overlaps the compute waves.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // B: compute-wave states ready
-        if (a.trace) t_cmp = wall_clock64();
+        if (a.trace) {
+          t_cmp = wall_clock64();
+          for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
+        }
         attn_merge_phase<HD, G>(L, 0, lane);
         __syncthreads();  // E: merged partial ready
         cw_attn_publish<HD, G>(a, L, out, lane, t.row0, t.nrows, par);
@@ -1221,6 +1252,12 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         tr[1] = t_pro;
         tr[2] = t_cmp ? t_cmp : t_pro;
         tr[3] = t1;
+        tr[7] = t_a;
+        tr[4] = cw[TS_DONE];
+        tr[5] = cw[TS_GATHERED];
+        tr[6] = cw[TS_AFTER_A];
+        tr[8] = cw[TS_FIRST];
+        tr[9] = cw[TS_ENTRY];
       }
     }
   }
@@ -1259,8 +1296,24 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const TileDesc t = tile_of(L, k);
       const WaveDesc wd = wave_of(L, k);
       const int layer = wd.layer;
+      uint64_t* ts = a.trace && c == 0 ? reinterpret_cast<uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8 : nullptr;
+      if (ts && lane < TS_COUNT) ts[lane] = 0;
+      // The stream plan of the tile's first block -- its chunk range and what the registers
+      // fetch once its last batches are in flight: the next block, the KV rows of this worker's
+      // attention split when that is its next tile, or the next GEMV tile -- worked out before
+      // the inputs arrive, so that streaming starts right after barrier A.
+      const SegDesc sd = L.segs[k];
+      const TileDesc tn = tile_of(L, k + 1 < a.n_waves ? k + 1 : 0);
+      const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
+      const Range ng = next_gemv(L.segs, a.n_waves, k, block_rows, c);
+      const Range r_first = block_range(sd, k, 0, block_rows, c);
+      const int rows = sc(sd.rows);
+      const bool one_block = block_rows >= rows;
+      const Range nr_first = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng;
+      const bool kv_first = one_block && next_attn;
+      const KvOpen ko = kv_open<HD>(a, layer, tn.row0, tn.nrows, L_att, c);
       if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
-      if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 5);
+      stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1268,43 +1321,35 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       }
       lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
       __syncthreads();  // A
-      if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 6);
+      stamp(ts, TS_AFTER_A, lane);
       if (is_gemv(t.kind)) {
-        const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
-        const SegDesc sd = L.segs[k];
-        // what the registers fetch once this block's last batches are in flight: the next block,
-        // the KV rows of this worker's attention split when that is its next tile, or the next
-        // GEMV tile
-        const TileDesc tn = tile_of(L, k + 1 < a.n_waves ? k + 1 : 0);
-        const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
-          const Range r = block_range(sd, k, r0, block_rows, c);
           const bool last_block = r0 + block_rows >= rows;
+          const Range r = r0 == 0 ? r_first : block_range(sd, k, r0, block_rows, c);
           if (r.i < r.ihi) {
-            const Range nr = !last_block ? block_range(sd, k, r0 + block_rows, block_rows, c)
+            const Range nr = r0 == 0 ? nr_first
+                             : !last_block ? block_range(sd, k, r0 + block_rows, block_rows, c)
                              : next_attn ? no_range()
-                                         : next_gemv(L.segs, a.n_waves, k, block_rows, c);
-            const bool kv_next = last_block && next_attn;
-            const KvOpen ko = kv_open<HD>(a, layer, tn.row0, tn.nrows, L_att, c);
+                                         : ng;
+            const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
             stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](int h) {
               return select_src<B>(kv_next, kv_half_src<HD, B>(ko, h, lane), gemv_src<B>(a.packed, nr, h, lane));
-            });
+            }, r0 == 0 ? ts : nullptr);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
+            if (r0 == 0) stamp(ts, TS_DONE, lane);
           }
-          if (a.trace && c == 0 && r0 == 0 && lane == 0) trace_word(a, step, k, bid, 4);
           __syncthreads();                              // B
           if (r0 + block_rows < rows) __syncthreads();  // C
         }
       } else if (t.kind == KIND_ATTN) {
         compute_attention<HD, G, B>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&]() {
-          const Range nr = next_gemv(L.segs, a.n_waves, k, block_rows, c);
-          load_gemv_batch<B>(st.v, a.packed, nr, 0, lane);
-          load_gemv_batch<B>(st.v + B, a.packed, nr, 1, lane);
-          st.k = nr.k;
-          st.r0 = nr.r0;
-        });
-        if (a.trace && c == 0 && lane == 0) trace_word(a, step, k, bid, 4);
+          load_gemv_batch<B>(st.v, a.packed, ng, 0, lane);
+          load_gemv_batch<B>(st.v + B, a.packed, ng, 1, lane);
+          st.k = ng.k;
+          st.r0 = ng.r0;
+        }, ts);
+        stamp(ts, TS_DONE, lane);
         __syncthreads();  // B
         attn_merge_phase<HD, G>(L, wave, lane);
         __syncthreads();  // E
