@@ -69,7 +69,7 @@ typedef struct tiles_config {
   float rms_eps;          /* RMSNorm epsilon (also used for the q/k norms) */
   int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
   int32_t tie_embeddings; /* 1: the LM head is the embedding matrix */
-  int32_t max_positions;  /* largest KV length (cached + decoded) the plan supports */
+  int32_t max_positions;  /* largest KV length (cached + decoded) the plan supports, 1 .. 2^23 */
   uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON */
   int32_t kv_splits;      /* split-KV count per KV head; 0 lets the planner choose */
   int32_t combine_mode;   /* 0 planner choice, 1 combine splits in the o_proj prologue, 2 own wave */

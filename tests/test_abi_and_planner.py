@@ -90,6 +90,13 @@ def test_untileable_shapes_are_rejected(bad, code):
     assert e.value.code == code
 
 
+def test_kv_capacity_limit():
+    tiles.dry_run(TINY, 1 << 23)
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(TINY, (1 << 23) + 1)
+    assert e.value.code == tiles.TILES_E_CONFIG
+
+
 def test_too_many_splits_rejected():
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(LLAMA_1B, 1087, kv_splits=33)

@@ -228,7 +228,7 @@ __device__ __forceinline__ bool is_gemv(int kind) {
   return kind == KIND_QKV || kind == KIND_O || kind == KIND_GU || kind == KIND_DOWN || kind == KIND_LM;
 }
 // chunk range of compute wave c over n chunks
-__device__ __forceinline__ int chunk_lo(int n, int c) { return (int)(((int64_t)n * c) / NCOMP); }
+__device__ __forceinline__ int chunk_lo(int n, int c) { return (int)((uint32_t)(n * c) / NCOMP); }
 
 // ---------------------------------------------------------------------------
 // waiting: every poll loop is bounded (watchdog) and leaves when any worker has aborted
@@ -615,16 +615,24 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
     load_gemv_batch<B>(Y, packed, r, 1, lane);
   }
   stamp(ts, TS_ENTRY, lane);
-  for (int b = 0; b < nbe; b += 2) {
-    const bool more = b + 2 < nbe;
+  int b = 0;
+  for (; b + 2 < nbe; b += 2) {
     consume_batch(X, i + b * B);
-    load_batch<B>(X, select_src<B>(more, gemv_src<B>(packed, r, b + 2, lane), next_src(0)));
+    load_gemv_batch<B>(X, packed, r, b + 2, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the reload of X ahead of the consumption of Y
     if (b == 0) stamp(ts, TS_FIRST, lane);
     consume_batch(Y, i + (b + 1) * B);
-    load_batch<B>(Y, select_src<B>(more, gemv_src<B>(packed, r, b + 3, lane), next_src(1)));
+    load_gemv_batch<B>(Y, packed, r, b + 3, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the last two batches: their reloads fetch what follows the range
+  consume_batch(X, i + b * B);
+  load_batch<B>(X, next_src(0));
+  __builtin_amdgcn_sched_barrier(0);
+  if (b == 0) stamp(ts, TS_FIRST, lane);
+  consume_batch(Y, i + (b + 1) * B);
+  load_batch<B>(Y, next_src(1));
+  __builtin_amdgcn_sched_barrier(0);
   if (seg != 0) {
     const float s = wave_sum(acc);
     if (lane == 0) L.part[row * NCOMP + c] = s;
@@ -755,18 +763,21 @@ __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds&
 }
 
 // Positions [wlo, whi) of a split that compute wave c handles at attended length L_att.
+// Positions are below 2^31 (the planner bounds the cache capacity), so 32-bit arithmetic.
 struct AttnRange {
-  int64_t wlo, whi;
+  int wlo, whi;
 };
-__device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int c, int64_t L_att) {
-  const int64_t ch = (L_att + a.S - 1) / a.S;
-  int64_t lo = (int64_t)sp * ch;
-  const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
+__device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int c, int64_t L_att64) {
+  const int L_att = (int)L_att64;
+  const int S = a.S;
+  const int ch = (int)((uint32_t)(L_att + S - 1) / (uint32_t)S);
+  int lo = sp * ch;
+  const int hi = lo + ch < L_att ? lo + ch : L_att;
   if (lo > L_att) lo = L_att;
-  const int64_t n = hi > lo ? hi - lo : 0;
+  const int n = hi > lo ? hi - lo : 0;
   AttnRange r;
-  r.wlo = lo + (n * c) / NCOMP;
-  r.whi = lo + (n * (c + 1)) / NCOMP;
+  r.wlo = lo + (int)((uint32_t)(n * c) / NCOMP);
+  r.whi = lo + (int)((uint32_t)(n * (c + 1)) / NCOMP);
   return r;
 }
 
@@ -781,11 +792,11 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
 // steps, and none follows the last one); rows from earlier launches are covered by the cache
 // maintenance at kernel boundaries.  The consumer masks those slots.
 template <int HD>
-__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int64_t j, int64_t whi,
-                                        int64_t cur, int64_t dummy, int dseg, u32x4& kw, u32x4& vw) {
+__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j, int whi,
+                                        int cur, int dummy, int dseg, u32x4& kw, u32x4& vw) {
   constexpr int LPP = HD / 8;
-  const int64_t jj = (j < whi && j != cur) ? j : dummy;
-  const uint32_t off = (uint32_t)((jj * LPP + dseg) * 16);
+  const int jj = (j < whi && j != cur) ? j : dummy;
+  const uint32_t off = ((uint32_t)jj * LPP + dseg) * 16u;
   kw = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, NT);
   vw = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, NT);
 }
@@ -793,46 +804,73 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache,
   return rsrc(cache + kvrow0 * hd);
 }
 
-// Where an attention split's opening loads come from: descriptors of the KV head and this
-// wave's position range, computed once (outside the streaming loop that issues the loads).
+// The opening loads of an attention split -- the first B (K, V) position-group pairs of this
+// wave's range -- prepared ahead: the KV head's row bases and each pair's per-lane byte offset
+// (a slot without a position reads the dummy row, as in load_kv).
+template <int B>
 struct KvOpen {
-  __amdgpu_buffer_rsrc_t rk, rv;
-  int64_t wlo, whi, cur, dummy;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  uint32_t off[B];
 };
-template <int HD>
-__device__ __forceinline__ KvOpen kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c) {
-  KvOpen o;
+template <int HD, int B>
+__device__ __forceinline__ KvOpen<B> kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c,
+                                             int lane) {
+  constexpr int LPP = HD / 8, P = 64 / LPP;
+  const int pp = lane / LPP, dseg = lane % LPP;
+  KvOpen<B> o;
   const AttnRange r = attn_range(a, sp, c, L_att);
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
-  o.rk = kv_rsrc(a.kv_k, kvrow0, HD);
-  o.rv = kv_rsrc(a.kv_v, kvrow0, HD);
-  o.wlo = r.wlo;
-  o.whi = r.whi;
-  o.cur = L_att - 1;
-  o.dummy = a.kv_cap - 1;
+  o.kbase = a.kv_k + kvrow0 * HD;
+  o.vbase = a.kv_v + kvrow0 * HD;
+  const int cur = (int)L_att - 1, dummy = (int)a.kv_cap - 1;
+#pragma unroll
+  for (int s = 0; s < B; ++s) {
+    const int j = r.wlo + s * P + pp;
+    const int jj = (j < r.whi && j != cur) ? j : dummy;
+    o.off[s] = ((uint32_t)jj * LPP + dseg) * 16u;
+  }
   return o;
 }
 
-// Half h of the first B (K, V) position-group pairs of an attention split (pairs h*B/2 ..
-// h*B/2 + B/2 - 1) into w[0, B): the opening of the ring compute_attention runs on, loaded while
-// the previous tile (QKV) streams.  The cache rows do not depend on this step's q; the current
-// position's row is never loaded (it comes from LDS).
-template <int HD, int B>
-__device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen& o, int h, int lane) {
-  constexpr int LPP = HD / 8, P = 64 / LPP;
-  const int pp = lane / LPP, dseg = lane % LPP;
+// Half h of the opening (pairs h*B/2 .. h*B/2 + B/2 - 1) into w[0, B): the start of the ring
+// compute_attention runs on, loaded while the previous tile (QKV) streams.  The cache rows do
+// not depend on this step's q; the current position's row is never loaded (it comes from LDS).
+template <int B>
+__device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen<B>& o, int h) {
   BatchSrc<B> b;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(o.kbase), rv = rsrc(o.vbase);
 #pragma unroll
   for (int s = 0; s < B / 2; ++s) {
-    const int64_t j = o.wlo + (int64_t)(h * (B / 2) + s) * P + pp;
-    const int64_t jj = (j < o.whi && j != o.cur) ? j : o.dummy;
-    const uint32_t off = (uint32_t)((jj * LPP + dseg) * 16);
-    b.d[2 * s] = o.rk;
-    b.d[2 * s + 1] = o.rv;
-    b.vo[2 * s] = b.vo[2 * s + 1] = off;
+    b.d[2 * s] = rk;
+    b.d[2 * s + 1] = rv;
+    b.vo[2 * s] = b.vo[2 * s + 1] = o.off[h * (B / 2) + s];
     b.so[2 * s] = b.so[2 * s + 1] = 0;
   }
   return b;
+}
+
+// Values prepared before a wait are passed through an empty asm statement so that they are
+// computed there (the compiler would otherwise sink the arithmetic to the first use, after the
+// barrier that ends the wait).
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+s"(x)); }
+__device__ __forceinline__ void pin(int64_t& x) { asm volatile("" : "+s"(x)); }
+__device__ __forceinline__ void pin(const uint16_t*& p) { asm volatile("" : "+s"(p)); }
+__device__ __forceinline__ void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(Range& r) {
+  pin(r.k);
+  pin(r.r0);
+  pin(r.C);
+  pin(r.i);
+  pin(r.ihi);
+  pin(r.base);
+}
+template <int B>
+__device__ __forceinline__ void pin(KvOpen<B>& o) {
+  pin(o.kbase);
+  pin(o.vbase);
+#pragma unroll
+  for (int s = 0; s < B; ++s) pin_v(o.off[s]);
 }
 
 template <int HD>
@@ -857,17 +895,17 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
   float* ws = attn_ws<HD, G>(L);
-  const int64_t cur = L_att - 1;
+  const int cur = (int)L_att - 1;
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   constexpr int LPP = HD / 8;  // lanes per position
   constexpr int P = 64 / LPP;  // positions per load
   const AttnRange rg = attn_range(a, sp, c, L_att);
-  const int64_t wlo = rg.wlo, whi = rg.whi;
-  const int ngroups = whi > wlo ? (int)((whi - wlo + P - 1) / P) : 0;
+  const int wlo = rg.wlo, whi = rg.whi;
+  const int ngroups = whi > wlo ? (whi - wlo + P - 1) / P : 0;
   const int pp = lane / LPP, dseg = lane % LPP;
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
-  const int64_t dummy = a.kv_cap - 1;
+  const int dummy = (int)a.kv_cap - 1;
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -903,8 +941,8 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       m[h] = mn;
     }
   };
-  auto consume1 = [&](int64_t jb, const u32x4& kw, const u32x4& vw) {
-    const int64_t j = jb + pp;
+  auto consume1 = [&](int jb, const u32x4& kw, const u32x4& vw) {
+    const int j = jb + pp;
     float kf[8], vf[8];
     unpack8<HD>(kw, kf);
     unpack8<HD>(vw, vf);
@@ -919,8 +957,8 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int gi = g0 + s;
-      consume1(wlo + (int64_t)gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
-      load_kv<HD>(rk, rv, wlo + (int64_t)(gi + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+      consume1(wlo + gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
+      load_kv<HD>(rk, rv, wlo + (gi + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
       if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
     }
@@ -1305,13 +1343,20 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const SegDesc sd = L.segs[k];
       const TileDesc tn = tile_of(L, k + 1 < a.n_waves ? k + 1 : 0);
       const bool next_attn = k + 1 < a.n_waves && tn.kind == KIND_ATTN;
-      const Range ng = next_gemv(L.segs, a.n_waves, k, block_rows, c);
-      const Range r_first = block_range(sd, k, 0, block_rows, c);
+      const Range ng0 = next_gemv(L.segs, a.n_waves, k, block_rows, c);
+      const Range r_first0 = block_range(sd, k, 0, block_rows, c);
       const int rows = sc(sd.rows);
       const bool one_block = block_rows >= rows;
-      const Range nr_first = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng;
-      const bool kv_first = one_block && next_attn;
-      const KvOpen ko = kv_open<HD>(a, layer, tn.row0, tn.nrows, L_att, c);
+      const Range nr_first0 = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng0;
+      const bool kv_first0 = one_block && next_attn;
+      KvOpen<B> ko = kv_open<HD, B>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
+      Range ng = ng0, r_first = r_first0, nr_first = nr_first0;
+      int kv_first = kv_first0;
+      pin(ng);
+      pin(r_first);
+      pin(nr_first);
+      pin(kv_first);
+      pin(ko);
       if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
@@ -1333,7 +1378,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                                          : ng;
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
             stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](int h) {
-              return select_src<B>(kv_next, kv_half_src<HD, B>(ko, h, lane), gemv_src<B>(a.packed, nr, h, lane));
+              return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane));
             }, r0 == 0 ? ts : nullptr);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;

@@ -37,7 +37,8 @@ struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the 
   int32_t rows;  // weight rows of the tile (0: no GEMV tile in this wave)
 };
 constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
-constexpr int MAX_BLOCK_ROWS = 640;  // GEMV rows staged per LDS block
+constexpr int MAX_BLOCK_ROWS = 640;
+constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit  // GEMV rows staged per LDS block
 
 struct TileDesc {   // 32 bytes
   int32_t kind;

@@ -105,6 +105,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   s.G = s.n_heads / s.n_kv;
   if (s.G > MAX_GROUP) return fail(err, TILES_E_CONFIG, "more than 4 query heads per KV head");
   if (s.max_positions < 1) return fail(err, TILES_E_CONFIG, "max_positions must be >= 1");
+  // positions and byte offsets within one KV head's cache rows are 32-bit in the kernel
+  if (s.max_positions > MAX_POSITIONS) return fail(err, TILES_E_CONFIG, "max_positions above 2^23");
   if (!(cfg.rms_eps > 0.0f) || !(cfg.rope_theta > 1.0f)) return fail(err, TILES_E_CONFIG, "bad rms_eps or rope_theta");
   if (n_workers < 1) return fail(err, TILES_E_CONFIG, "n_workers must be >= 1");
   if (n_workers < s.n_heads || n_workers < s.n_kv) return fail(err, TILES_E_CONFIG, "fewer workers than attention heads");
