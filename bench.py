@@ -204,7 +204,7 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     _, tr = plan.read_debug(hidden=False, trace=True)
     waves = plan.waves()
     plan.close()
-    # [steps, waves, W, 10] 100 MHz ticks (see tiles_read_debug in include/tiles.h)
+    # [steps, waves, W, 12] 100 MHz ticks (see tiles_read_debug in include/tiles.h)
     tr = tr.astype(np.int64)
     steps, nw = tr.shape[0], tr.shape[1]
     names = tiles.WAVE_KINDS
@@ -220,13 +220,18 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     cw = (np.where(has, tr[:, :, :, 4] - tr[:, :, :, 6], 0)).max(axis=2) * 0.01  # first compute wave, A -> done
     setup = (np.where(has, tr[:, :, :, 9] - tr[:, :, :, 6], 0)).max(axis=2) * 0.01  # A -> streaming loop entered
     first = (np.where(has, tr[:, :, :, 8] - tr[:, :, :, 9], 0)).max(axis=2) * 0.01  # entry -> first batch consumed
+    hasl = tr[:, :, :, 11] != 0
+    lastw = (np.where(hasl, tr[:, :, :, 11] - tr[:, :, :, 7], 0)).max(axis=2) * 0.01  # A -> last compute wave done
+    hasb = tr[:, :, :, 10] != 0
+    ctlb = (np.where(hasb, tr[:, :, :, 10] - tr[:, :, :, 7], 0)).max(axis=2) * 0.01  # A -> control ready for B
     lines = ["# per-wave timing from the in-kernel trace (wall clock 100 MHz).  dur = last publish of this wave",
              "# minus last publish of the previous one; edge = last worker's inputs staged minus the previous",
              "# wave's last publish; wait / compute / publish = max over workers of each phase (control wave);",
              "# prologue = LDS prologue (P -> A); cw1 = first compute wavefront's own work after A (max over workers);",
-             "# setup = its A -> streaming loop entry; first = loop entry -> first batch consumed (max over workers)",
+             "# setup = its A -> streaming loop entry; first = loop entry -> first batch consumed (max over workers);",
+             "# lastw = A -> last compute wavefront done; ctlB = A -> control wavefront ready for B (attention)",
              f"# workload: {wl.description}; steps traced: {steps}; waves per step: {nw}",
-             "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tedge_us\twait_us\tcompute_us\tpublish_us\tprologue_us\tcw1_us\tsetup_us\tfirst_us"]
+             "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tedge_us\twait_us\tcompute_us\tpublish_us\tprologue_us\tcw1_us\tsetup_us\tfirst_us\tlastw_us\tctlB_us"]
     sl = slice(1, None) if steps > 2 else slice(None)  # the first step includes the launch ramp
     tot = 0.0
     per_kind = {}
@@ -235,18 +240,20 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
         tot += d_us
         gbs = (wv.weight_bytes / 1e9) / (d_us * 1e-6) if d_us > 0 else 0.0
         k = names.get(wv.kind, str(wv.kind))
-        ph = [float(np.median(x[sl, i])) for x in (edge, wait, cmp_, pub, pro, cw, setup, first)]
-        acc = per_kind.setdefault(k, [0.0] * 10)
+        ph = [float(np.median(x[sl, i])) for x in (edge, wait, cmp_, pub, pro, cw, setup, first, lastw, ctlb)]
+        acc = per_kind.setdefault(k, [0.0] * 12)
         acc[0] += d_us
         acc[1] += wv.weight_bytes
-        for j in range(8):
+        for j in range(10):
             acc[2 + j] += ph[j]
         lines.append(f"{i}\t{k}\t{wv.layer}\t{wv.weight_bytes / 1e6:.2f}\t{d_us:.2f}\t{gbs:.0f}\t" +
                      "\t".join(f"{x:.2f}" for x in ph))
-    lines.append("# per kind (us per token): total | GB/s | edge | wait | compute | publish | prologue | cw1 | setup | first")
+    lines.append("# per kind (us per token): total | GB/s | edge | wait | compute | publish | prologue | cw1 | setup | first"
+                 " | lastw | ctlB")
     for k, d in per_kind.items():
         lines.append(f"# {k}\t{d[0]:.1f}\t{d[1] / 1e9 / (d[0] * 1e-6) if d[0] else 0:.0f} GB/s\t"
-                     f"{d[2]:.1f}\t{d[3]:.1f}\t{d[4]:.1f}\t{d[5]:.1f}\t{d[6]:.1f}\t{d[7]:.1f}\t{d[8]:.1f}\t{d[9]:.1f}")
+                     f"{d[2]:.1f}\t{d[3]:.1f}\t{d[4]:.1f}\t{d[5]:.1f}\t{d[6]:.1f}\t{d[7]:.1f}\t{d[8]:.1f}\t{d[9]:.1f}\t"
+                     f"{d[10]:.1f}\t{d[11]:.1f}")
     step_us = float(np.median(np.diff(end[:, -1]))) * 0.01 if steps > 1 else tot
     lines.append(f"# token time (median step-to-step) {step_us:.1f} us; sum of wave medians {tot:.1f} us")
     with open(path, "w") as f:

@@ -178,13 +178,15 @@ int tiles_plan_status(tiles_plan_t *plan);
 
 /* Copy debug buffers to host memory after synchronizing the plan's stream.
  *   hidden : host float [n_steps_of_last_decode][n_layers][H] or NULL (needs TILES_DEBUG_HIDDEN);
- *   trace  : host uint64 [n_steps][waves_per_step][n_workers][10] or NULL (needs TILES_TRACE),
+ *   trace  : host uint64 [n_steps][waves_per_step][n_workers][12] or NULL (needs TILES_TRACE),
  *            100 MHz wall-clock ticks per (step, wave, worker): 0 wave start, 1 inputs staged,
  *            2 compute done, 3 outputs published, 7 after the LDS prologue (control wavefront);
  *            5 own gather done, 6 after the LDS prologue, 9 streaming loop entered, 8 first
  *            batch consumed, 4 own share of the tile done (first compute wavefront, GEMV and
  *            attention tiles; 4, 8 and 9 are 0 when it had no share, all five are 0 for other
- *            tiles).
+ *            tiles); 11 the last compute wavefront's share done (GEMV and attention tiles),
+ *            10 the control wavefront ready for barrier B after its KV-row write (attention
+ *            tiles, else 0).
  *   *n_steps_out receives the step count of the last decode. */
 int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t *n_steps_out);
 

@@ -175,6 +175,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 constexpr int SM_ABORT = 0;  // int: some wavefront gave up waiting (all leave after barrier P)
 constexpr int SM_SS = 8;     // float[NWAVES]: sums of squares of each wavefront's share of x
 constexpr int SM_CTRACE = 32;  // uint64[2][8]: first compute wavefront's timestamps of a tile (set = tile parity)
+constexpr int SM_WDONE = 64;   // uint64[2][8]: each compute wavefront's done stamp of a tile (set = tile parity)
 constexpr int SM_ROPE = 256;   // float[head_dim]: (cos, sin) pairs of the current position (attention tiles)
 constexpr int SM_QGAIN = 512;  // float[head_dim]: q-norm gains (attention tiles with q/k norm)
 constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
@@ -661,21 +662,39 @@ template <int HD>
 constexpr int pstride() { return HD + 4; }
 
 // merge the S splits of one query head (Ph -> [S][HD + 4]) for output dim d, fixed split order
+// Merge the S split partials (m, l, acc[HD], pad) of heads [0, nh) -- head h's at
+// part + h * S * (HD + 4) -- into out[h * HD + d]: acc weighted by 2^(m_s - max m) over the
+// weighted l ("Tiles", split-KV attention combine).  Each thread takes four consecutive
+// dimensions of one head; a split's (m, l) pair and accumulator slice are read with
+// independent loads, so their latencies overlap.  Empty splits (l = 0) carry no weight; a head
+// with no positions gives 0.
 template <int HD>
-__device__ __forceinline__ float merge_splits(const float* Ph, int S, int d) {
+__device__ __forceinline__ void merge_heads(const float* part, int nh, int S, int tid, float* out) {
   constexpr int PS = pstride<HD>();
-  float mm = -INFINITY;
-  for (int s = 0; s < S; ++s) mm = fmaxf(mm, Ph[s * PS]);
-  if (mm == -INFINITY) return 0.f;
-  float ll = 0.f, aa = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* st = Ph + s * PS;
-    if (st[1] == 0.f) continue;
-    const float f = __builtin_amdgcn_exp2f(st[0] - mm);
-    ll += f * st[1];
-    aa += f * st[2 + d];
+  for (int o = tid * 4; o < nh * HD; o += BLOCK_THREADS * 4) {
+    const int h = o / HD, d = o % HD;
+    const float* P = part + h * S * PS;
+    float mm = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(P + sp * PS);
+      mm = ml.y > 0.f ? fmaxf(mm, ml.x) : mm;
+    }
+    float ll = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float* st = P + sp * PS;
+      const float2 ml = *reinterpret_cast<const float2*>(st);
+      const float2 v01 = *reinterpret_cast<const float2*>(st + 2 + d);
+      const float2 v23 = *reinterpret_cast<const float2*>(st + 4 + d);
+      const float f = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mm) : 0.f;
+      ll = fmaf(f, ml.y, ll);
+      a0 = fmaf(f, v01.x, a0);
+      a1 = fmaf(f, v01.y, a1);
+      a2 = fmaf(f, v23.x, a2);
+      a3 = fmaf(f, v23.y, a3);
+    }
+    const float inv = ll > 0.f ? 1.0f / ll : 0.f;
+    *reinterpret_cast<f32x4*>(out + o) = f32x4{a0 * inv, a1 * inv, a2 * inv, a3 * inv};
   }
-  return aa / ll;
 }
 
 // Attention tile LDS layout (inside `part`): q[G][HD] (normed, roped, scaled to the base-2
@@ -1148,7 +1167,6 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
 template <int HD, int G>
 __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
                                               const TileDesc& t, int layer, int pos) {
-  constexpr int PS = pstride<HD>();
   float rs = 1.0f;
   if (t.kind == KIND_QKV || t.kind == KIND_GU || t.kind == KIND_LM) {
     float tot = 0.f;
@@ -1158,11 +1176,9 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
   } else if (t.kind == KIND_ATTN) {
     attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
   } else if (t.kind == KIND_O && a.combine_in_o) {
-    const int nq = a.n_heads * HD;
-    for (int i = wave * 64 + lane; i < nq; i += BLOCK_THREADS)
-      L.vec[i] = merge_splits<HD>(L.part + (i / HD) * a.S * PS, a.S, i % HD);
+    merge_heads<HD>(L.part, a.n_heads, a.S, wave * 64 + lane, L.vec);
   } else if (t.kind == KIND_COMBINE) {
-    for (int d = wave * 64 + lane; d < HD; d += BLOCK_THREADS) L.vec[d] = merge_splits<HD>(L.part, a.S, d);
+    merge_heads<HD>(L.part, 1, a.S, wave * 64 + lane, L.vec);
   }
   return rs;
 }
@@ -1191,6 +1207,8 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       uint32_t* out = a.ll + (wd.ll_off >= 0 ? wd.ll_off : 0);
       uint64_t t0 = 0, t_pro = 0, t_cmp = 0;
       uint64_t cw[TS_COUNT] = {};  // the first compute wavefront's stamps, read after barrier B
+      uint64_t t_preb = 0, t_last = 0;  // control wave ready for B; last compute wavefront done
+      const uint64_t* wds = reinterpret_cast<const uint64_t*>(L.small + SM_WDONE) + (k & 1) * 8;
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
       if (gather_inputs<HD, G>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
@@ -1212,6 +1230,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           if (a.trace && r0 == 0) {
             t_cmp = wall_clock64();
             for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
+            for (int w = 1; w < NWAVES; ++w) t_last = wds[w] > t_last ? wds[w] : t_last;
           }
           switch (t.kind) {
             case KIND_QKV:
@@ -1257,10 +1276,12 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         // The KV row must be complete before this worker publishes anything later readers of
         // the row depend on (its split partial, below); the wait overlaps the compute waves.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (a.trace) t_preb = wall_clock64();
         __syncthreads();  // B: compute-wave states ready
         if (a.trace) {
           t_cmp = wall_clock64();
           for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
+          for (int w = 1; w < NWAVES; ++w) t_last = wds[w] > t_last ? wds[w] : t_last;
         }
         attn_merge_phase<HD, G>(L, 0, lane);
         __syncthreads();  // E: merged partial ready
@@ -1296,6 +1317,8 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         tr[6] = cw[TS_AFTER_A];
         tr[8] = cw[TS_FIRST];
         tr[9] = cw[TS_ENTRY];
+        tr[10] = t_preb;
+        tr[11] = t_last;
       }
     }
   }
@@ -1336,6 +1359,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const int layer = wd.layer;
       uint64_t* ts = a.trace && c == 0 ? reinterpret_cast<uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8 : nullptr;
       if (ts && lane < TS_COUNT) ts[lane] = 0;
+      uint64_t* wdone = a.trace ? reinterpret_cast<uint64_t*>(L.small + SM_WDONE) + (k & 1) * 8 + wave : nullptr;
+      if (wdone && lane == 0) *wdone = 0;
       // The stream plan of the tile's first block -- its chunk range and what the registers
       // fetch once its last batches are in flight: the next block, the KV rows of this worker's
       // attention split when that is its next tile, or the next GEMV tile -- worked out before
@@ -1383,6 +1408,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
             if (r0 == 0) stamp(ts, TS_DONE, lane);
+            if (r0 == 0 && wdone && lane == 0) *wdone = wall_clock64();
           }
           __syncthreads();                              // B
           if (r0 + block_rows < rows) __syncthreads();  // C
@@ -1395,6 +1421,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.r0 = ng.r0;
         }, ts);
         stamp(ts, TS_DONE, lane);
+        if (wdone && lane == 0) *wdone = wall_clock64();
         __syncthreads();  // B
         attn_merge_phase<HD, G>(L, wave, lane);
         __syncthreads();  // E

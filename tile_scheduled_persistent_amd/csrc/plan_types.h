@@ -72,7 +72,7 @@ constexpr int SYNC_WORDS = 32;
 //   3 outputs published, 7 after barrier A  -- all taken by the control wave;
 //   5 own gather done (before P), 6 after barrier A, 4 own share of the tile done (before B)
 //   -- taken by the first compute wave (4 stays 0 when it had no share).
-constexpr int TRACE_WORDS = 10;
+constexpr int TRACE_WORDS = 12;
 
 // Tagged-data buffers are filled with this word before every launch: a quiet NaN whose
 // parity bit (bit 0) is 0, so that step 0 (parity 1) never mistakes it for a value.

@@ -30,7 +30,7 @@ TILES_E_KERNEL = -6
 
 TILES_DEBUG_HIDDEN = 0x1
 TILES_TRACE = 0x2
-TRACE_WORDS = 10  # see tiles_read_debug in include/tiles.h
+TRACE_WORDS = 12  # see tiles_read_debug in include/tiles.h
 TILES_POISON = 0x4
 
 WAVE_KINDS = {1: "qkv", 2: "attn", 3: "combine", 4: "o_proj", 5: "gate_up", 6: "down", 7: "lm_head"}
