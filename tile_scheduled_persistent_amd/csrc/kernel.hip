@@ -430,7 +430,6 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
 // all of them before the first use.
 // ---------------------------------------------------------------------------
 
-constexpr int STREAM_BATCH = 4;
 
 // Trace stamps of the first compute wavefront, kept in LDS (a global store would hold up the
 // wavefront's next wait on its loads, which counts stores too) and written out by the control

@@ -38,6 +38,10 @@ struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the 
 };
 constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
 constexpr int MAX_BLOCK_ROWS = 640;
+// Register streaming of the compute wavefronts: two batches of STREAM_BATCH 16-byte loads per
+// lane in flight (STREAM_DEPTH), for weight chunks and K/V rows alike.
+constexpr int STREAM_BATCH = 4;
+constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit  // GEMV rows staged per LDS block
 
 struct TileDesc {   // 32 bytes

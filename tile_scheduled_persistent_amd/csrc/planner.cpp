@@ -43,10 +43,21 @@ int fail(std::string& err, int code, const std::string& msg) {
 
 // Split count: about `target` bytes of K+V per split tile at the largest attended
 // length, at least 1, at most as many tiles as workers.
+// Split partials of all heads up to this size are merged in the o_proj prologue (combine mode 0).
+constexpr int64_t COMBINE_IN_O_BYTES = 64 * 1024;
+
 int32_t choose_splits(const Shape& s, int32_t W) {
+  // Preferably a split's K/V rows fit the compute wavefronts' register prefetch (STREAM_DEPTH
+  // 16-byte loads per lane, NCOMP wavefronts), so that its attention runs in one pass, as long
+  // as the partials still merge in the o_proj prologue; else about 96 KB of K/V per split.
   const int64_t kv_head_bytes = (int64_t)s.max_positions * s.hd * 2 /*K,V*/ * 2 /*bf16*/;
-  const int64_t target = 96 * 1024;
-  int64_t S = (kv_head_bytes + target / 2) / target;
+  const int64_t one_pass = (int64_t)NCOMP * STREAM_DEPTH * 64 * 16;
+  const int64_t split_record_bytes = (int64_t)s.n_heads * (s.hd + 4) * 4;
+  int64_t S = (kv_head_bytes + one_pass - 1) / one_pass;
+  if (S * split_record_bytes > COMBINE_IN_O_BYTES) {
+    const int64_t target = 96 * 1024;
+    S = (kv_head_bytes + target / 2) / target;
+  }
   S = std::max<int64_t>(1, std::min<int64_t>(S, W / s.n_kv));
   return (int32_t)S;
 }
@@ -125,7 +136,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
-  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= 40 * 1024 ? 1 : 0;
+  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES ? 1 : 0;
   else return fail(err, TILES_E_CONFIG, "combine_mode must be 0, 1 or 2");
 
   // ---- packed layout: norm gains first, then the GEMV waves in execution order ----
