@@ -924,6 +924,9 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
   const int dummy = (int)a.kv_cap - 1;
+  // Running state per query head: m[h] is the same in every lane (the largest score the wave has
+  // seen so far, base 2); l[h] and acc[h][] are this lane's sums over its positions, weighted
+  // by 2^(score - m[h]).
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -932,88 +935,115 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  // One position group (this lane's position j, 8 dims) into the online softmax of every query
-  // head; branch-free with respect to the loaded registers: an invalid position (past the
-  // range, or the current one, which is handled apart from LDS) is masked in the update.
-  auto update = [&](bool valid, const float* kf, const float* vf) {
+  // score of this lane's position for head h (its 8 dimensions, summed over the LPP lanes)
+  auto score = [&](const float* kf, int h) -> float {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlane + h * HD + 4);
+    float d0 = q0.x * kf[0], d1 = q0.y * kf[1];
+    d0 = fmaf(q0.z, kf[2], d0);
+    d1 = fmaf(q0.w, kf[3], d1);
+    d0 = fmaf(q1.x, kf[4], d0);
+    d1 = fmaf(q1.y, kf[5], d1);
+    d0 = fmaf(q1.z, kf[6], d0);
+    d1 = fmaf(q1.w, kf[7], d1);
+    const float sc = d0 + d1;
+    return LPP == 8 ? sum8(sc) : sum16(sc);
+  };
+  // maximum over the wave's positions (lanes differing by multiples of LPP)
+  auto pos_max = [&](float v) -> float {
+    if constexpr (LPP == 8) v = fmaxf(v, lane_xor<8>(v, lane));
+    v = fmaxf(v, lane_xor<16>(v, lane));
+    return fmaxf(v, lane_xor<32>(v, lane));
+  };
+  // raise each head's running maximum to cover bm (this lane's candidates, -inf for none) and
+  // rescale the sums to it
+  auto raise = [&](const float* bm) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qlane + h * HD);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qlane + h * HD + 4);
-      float d0 = q0.x * kf[0], d1 = q0.y * kf[1];
-      d0 = fmaf(q0.z, kf[2], d0);
-      d1 = fmaf(q0.w, kf[3], d1);
-      d0 = fmaf(q1.x, kf[4], d0);
-      d1 = fmaf(q1.y, kf[5], d1);
-      d0 = fmaf(q1.z, kf[6], d0);
-      d1 = fmaf(q1.w, kf[7], d1);
-      float s = d0 + d1;
-      s = LPP == 8 ? sum8(s) : sum16(s);
-      // online-softmax update; a masked position leaves the state unchanged (al = 1, p = 0)
-      const float mn = valid ? fmaxf(m[h], s) : m[h];
-      const float al = valid ? __builtin_amdgcn_exp2f(m[h] - mn) : 1.0f;
-      const float p = valid ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
-      l[h] = l[h] * al + p;
+      const float mn = fmaxf(m[h], pos_max(bm[h]));
+      const float al = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[h] - mn);
+      l[h] *= al;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], al, p * vf[e]);
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
       m[h] = mn;
     }
   };
-  auto consume1 = [&](int jb, const u32x4& kw, const u32x4& vw) {
-    const int j = jb + pp;
-    float kf[8], vf[8];
-    unpack8<HD>(kw, kf);
-    unpack8<HD>(vw, vf);
-    update(j < whi && j != cur, kf, vf);
+  // weighted V of one position (p = 0 for a slot without one)
+  auto accumulate = [&](bool valid, const float* sc, const float* vf) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = valid ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
+      l[h] += p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+    }
   };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
     for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
   }
   stamp(ts, TS_ENTRY, lane);
+  // One pass per D position groups (the ring): scores of every slot from its K row, one raise of
+  // the running maximum, then the weighted V rows; each slot is reloaded (group + D) as soon as
+  // its V row is used.  Slots past the range, or holding the current position (taken from LDS
+  // below), are masked.
   for (int g0 = 0; g0 < ngroups; g0 += D) {
+    float sc[D][G], bm[G];
+    bool valid[D];
+#pragma unroll
+    for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      const int gi = g0 + s;
-      consume1(wlo + gi * P, pf.v[2 * s], pf.v[2 * s + 1]);  // groups past the range are masked
-      load_kv<HD>(rk, rv, wlo + (gi + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+      const int j = wlo + (g0 + s) * P + pp;
+      valid[s] = j < whi && j != cur;
+      float kf[8];
+      unpack8<HD>(pf.v[2 * s], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sc[s][h] = score(kf, h);
+        bm[h] = valid[s] ? fmaxf(bm[h], sc[s][h]) : bm[h];
+      }
+    }
+    raise(bm);
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      float vf[8];
+      unpack8<HD>(pf.v[2 * s + 1], vf);
+      accumulate(valid[s], sc[s], vf);
+      load_kv<HD>(rk, rv, wlo + (g0 + s + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
       if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
     }
   }
   after();
   if (wlo <= cur && cur < whi) {  // the current position (its K/V row is in LDS): lane group 0
-    float kf[8], vf[8];
+    float kf[8], vf[8], sc[G], bm[G];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kf[e] = kc[dseg * 8 + e];
       vf[e] = vc[dseg * 8 + e];
     }
-    update(pp == 0, kf, vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sc[h] = score(kf, h);
+      bm[h] = pp == 0 ? sc[h] : -INFINITY;
+    }
+    raise(bm);
+    accumulate(pp == 0, sc, vf);
   }
-  // merge the P position groups of this wave (lanes differing by multiples of LPP)
-  auto merge_lanes = [&](auto off_tag) {
+  // every lane's sums are relative to the same maximum: add up the lanes of equal dimensions
+  auto sum_lanes = [&](auto off_tag) {
     constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float m2 = lane_xor<OFF>(m[h], lane);
-      const float l2 = lane_xor<OFF>(l[h], lane);
-      float a2[8];
+      l[h] += lane_xor<OFF>(l[h], lane);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a2[e] = lane_xor<OFF>(acc[h][e], lane);
-      const float mn = fmaxf(m[h], m2);
-      const bool live = mn != -INFINITY;
-      const float f1 = live ? __builtin_amdgcn_exp2f(m[h] - mn) : 0.f;
-      const float f2 = live ? __builtin_amdgcn_exp2f(m2 - mn) : 0.f;
-      l[h] = l[h] * f1 + l2 * f2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * f1 + a2[e] * f2;
-      m[h] = mn;
+      for (int e = 0; e < 8; ++e) acc[h][e] += lane_xor<OFF>(acc[h][e], lane);
     }
   };
-  if constexpr (LPP == 8) merge_lanes(std::integral_constant<int, 8>{});
-  merge_lanes(std::integral_constant<int, 16>{});
-  merge_lanes(std::integral_constant<int, 32>{});
+  if constexpr (LPP == 8) sum_lanes(std::integral_constant<int, 8>{});
+  sum_lanes(std::integral_constant<int, 16>{});
+  sum_lanes(std::integral_constant<int, 32>{});
   if (pp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
