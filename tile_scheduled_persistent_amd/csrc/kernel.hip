@@ -639,15 +639,20 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   }
 }
 
-// total of row r of a block: partials of the compute waves whose ranges touch it, in order
+// total of row r of a block: partials of the compute waves whose ranges touch it, in order.
+// Every slot of the row is read (independent loads); those of waves that did not write it are
+// dropped by a select.
 __device__ __forceinline__ float row_total(const Lds& L, int nr, int C, int r) {
   const int n = nr * C;
   const int first = r * C, last = r * C + C - 1;
+  float v[NCOMP];
+#pragma unroll
+  for (int c = 0; c < NCOMP; ++c) v[c] = L.part[r * NCOMP + c];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < NCOMP; ++c) {
     const int lo = chunk_lo(n, c), hi = chunk_lo(n, c + 1);
-    if (lo < hi && lo <= last && first < hi) s += L.part[r * NCOMP + c];
+    s += (lo < hi && lo <= last && first < hi) ? v[c] : 0.f;
   }
   return s;
 }
@@ -1067,16 +1072,24 @@ __device__ __forceinline__ void attn_merge_phase(const Lds& L, int wave_index, i
   float* mrg = attn_merged<HD, G>(L);
   for (int idx = wave_index * 64 + lane; idx < G * HD; idx += BLOCK_THREADS) {
     const int h = idx / HD, d = idx % HD;
-    float mm = -INFINITY, ll = 0.f, aa = 0.f;
+    // every compute wave's state of head h (independent loads), then one common maximum
+    float mv[NCOMP], lv[NCOMP], av[NCOMP];
+#pragma unroll
     for (int c = 0; c < NCOMP; ++c) {
       const float* st = ws + (c * G + h) * PS;
-      const float m2 = st[0];
-      const float mn = fmaxf(mm, m2);
-      if (mn == -INFINITY) continue;
-      const float f1 = __builtin_amdgcn_exp2f(mm - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);
-      ll = ll * f1 + st[1] * f2;
-      aa = aa * f1 + st[2 + d] * f2;
-      mm = mn;
+      mv[c] = st[0];
+      lv[c] = st[1];
+      av[c] = st[2 + d];
+    }
+    float mm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NCOMP; ++c) mm = fmaxf(mm, mv[c]);
+    float ll = 0.f, aa = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCOMP; ++c) {
+      const float f = mv[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[c] - mm);  // a wave without positions: weight 0
+      ll = fmaf(f, lv[c], ll);
+      aa = fmaf(f, av[c], aa);
     }
     float* dst = mrg + h * PS;
     if (d == 0) {
@@ -1094,10 +1107,15 @@ template <int HD, int G>
 __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& L, uint32_t* out, int lane, int g, int sp,
                                 uint32_t par) {
   constexpr int PS = pstride<HD>();
+  constexpr int N = (G * PS + 63) / 64;  // values per lane
   const float* mrg = attn_merged<HD, G>(L);
-  for (int idx = lane; idx < G * PS; idx += 64) {
-    const int h = idx / PS, e = idx % PS;
-    publish(out, ((int64_t)(g * G + h) * a.S + sp) * PS + e, mrg[idx], par);
+  float v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = lane + 64 * i < G * PS ? mrg[lane + 64 * i] : 0.f;  // reads first, then the stores
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int idx = lane + 64 * i;
+    if (idx < G * PS) publish(out, ((int64_t)(g * G + idx / PS) * a.S + sp) * PS + idx % PS, v[i], par);
   }
 }
 
