@@ -294,6 +294,9 @@ __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src,
 }
 
 constexpr int GATHER_UNITS = 4;  // units per lane per polling pass (8 wavefronts x 64 lanes x 4 = 8192 floats)
+// Plain gathers (split partials into the o_proj prologue, the down input) poll twice as many
+// units per pass: the partials of 32 heads x 5 splits then arrive in one round trip.
+constexpr int GATHER_UNITS_PLAIN = 2 * GATHER_UNITS;
 
 struct Identity {
   __device__ int operator()(int u) const { return u; }
@@ -323,7 +326,7 @@ __device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, c
 // plain tagged vector -> dst
 __device__ __forceinline__ bool gather_plain(const KernelArgs& a, float* dst, const uint32_t* src, int n, int slot, int lane,
                              uint32_t par) {
-  return gather<GATHER_UNITS>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
+  return gather<GATHER_UNITS_PLAIN>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
                               [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(dst + u * 4) = x; });
 }
 
