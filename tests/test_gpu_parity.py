@@ -79,7 +79,7 @@ def test_tiny_workload_as_specified_free_running():
 def _full_run(s: Setup, token, n, flags=tiles.TILES_DEBUG_HIDDEN):
     kv = s.fresh_kv()
     with s.plan(flags=flags) as plan:
-        g_t, g_l, g_h = run_gpu(plan, kv, token, n)
+        g_t, g_l, g_h = run_gpu(plan, kv, token, n, want_hidden=bool(flags & tiles.TILES_DEBUG_HIDDEN))
     return g_t, g_l, g_h, kv
 
 
@@ -198,6 +198,7 @@ def test_full_size_workload(key, n_check):
     kv = s.fresh_kv()
     with s.plan() as plan:
         g_t, g_l, g_h = run_gpu(plan, kv, tok, wl.n_steps)
+    print(f"{key}: GPU launch of {wl.n_steps} steps done; oracle for {n_check} steps", flush=True)
     o_res = s.oracle().decode(s.oracle_kv(), tok, wl.n_cached, n_check)
     n = compare_free_running(key, g_t, g_l, g_h, o_res, n_check)
     assert n >= 1
