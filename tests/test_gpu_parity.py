@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 RAGGED = scaled(TINY, name="ragged", n_layers=3, hidden=384, n_heads=6, n_kv_heads=2, ffn=1000, vocab=1000)
 QK128 = scaled(TINY, name="tiny-qk128", head_dim=128, n_heads=4, n_kv_heads=1, qk_norm=True, rms_eps=1e-6,
                rope_theta=1e6)
+# Llama-3.2-1B widths on two layers: a compute wavefront's share of a gate/up or down tile spans
+# more than two batches, so the staged (direct-to-LDS) part of the weight prefetch runs
+WIDE = scaled(TINY, name="wide-2layer", n_layers=2, hidden=2048, n_heads=32, n_kv_heads=8, head_dim=64, ffn=8192,
+              vocab=4096, rms_eps=1e-5, rope_theta=5e5)
 
 
 def _oracle_forced(setup: Setup, inputs_prefix, n_steps, plan, pos0=None, tag=""):
@@ -127,6 +131,13 @@ def test_ragged_shapes_group3_padding():
     toks = synth.make_tokens(RAGGED, 1)
     with s.plan() as plan:
         _oracle_forced(s, toks, 12, plan, tag="ragged")
+
+
+def test_wide_layers_staged_prefetch():
+    s = Setup(WIDE, 96, 70)
+    toks = synth.make_tokens(WIDE, 1)
+    with s.plan() as plan:
+        _oracle_forced(s, toks, 6, plan, tag="wide")
 
 
 def test_qk_norm_head_dim_128():

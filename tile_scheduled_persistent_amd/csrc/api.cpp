@@ -358,6 +358,8 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.lds_vec_floats = hp.lds_vec_floats;
   a.lds_part_floats = hp.lds_part_floats;
   a.lds_xres_floats = hp.lds_xres_floats;
+  a.lds_stage_floats = hp.lds_stage_floats;
+  a.stage_batches = hp.stage_batches;
 
   // Kernels rather than memsets, so that the launch sequence can be captured in a graph.
   HIP_TRY(launch_fill(p->ll, p->fill_words, TAG_FILL, p->stream));

@@ -166,7 +166,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout (dynamic): vec | part | xres | small | segs.
+// LDS layout (dynamic, from LDS address 0): stage | vec | part | xres | small | segs | tiles |
+// waves | lsmall.
+//   stage per compute wavefront, staged chunks of its next GEMV range (direct-to-LDS loads; first,
+//         so that their LDS addresses stay below 64 KB)
 //   vec   GEMV input vector (or the raw q/k/v of an attention tile)
 //   part  GEMV row partials, attention work areas, gathered split partials
 //   xres  the residual stream x as last gathered (read by the o_proj / down epilogues)
@@ -184,6 +187,7 @@ struct Lds {
   float* vec;
   float* part;
   float* xres;
+  float* stage;
   float* small;
   SegDesc* segs;
   TileDesc* tiles;      // this worker's tile of every wave
@@ -511,6 +515,8 @@ struct Stream {
   u32x4 v[2 * B];
   int k;   // wave whose data the registers hold (-1: none)
   int r0;  // GEMV block of that wave
+  int sk;  // wave whose first block has batches 2 .. 2 + ls staged in the wave's LDS area (-1: none)
+  int ls;
 };
 
 // Source of the B loads of one batch: per slot a buffer descriptor, a per-lane byte offset and a
@@ -566,12 +572,48 @@ __device__ __forceinline__ void load_gemv_batch(u32x4* w, const uint8_t* packed,
   load_batch<B>(w, gemv_src<B>(packed, r, q, lane));
 }
 
+// Batch q of GEMV range r (chunks clamped into the range, as in gemv_src) straight into LDS at
+// byte address lds + u * CHUNK_BYTES for slot u: gfx950's 16-byte direct-to-LDS load puts lane i's
+// 16 bytes at M0 + 16 i, so a staged chunk has the same lane layout as a register batch.  The
+// compiler does not see these loads: a consumer waits for them explicitly (they complete in issue
+// order with the wavefront's other vector-memory loads).
+template <int B>
+__device__ __forceinline__ void stage_batch(const uint8_t* packed, const Range& r, int q, int lane, uint32_t lds) {
+  const uint8_t* base = packed + r.base + (uint32_t)lane * 16u;
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int j = r.i + q * B + u;
+    const int jc = j < r.ihi ? j : r.ihi - 1;
+    const uint8_t* g = base + (int64_t)jc * CHUNK_BYTES;
+    const uint32_t dst = lds + u * CHUNK_BYTES;
+    uint32_t saved;  // M0 is the compiler's: kept across the statement
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(dst)
+        : "memory");
+  }
+}
+// Stage batches 2 .. 2 + n of GEMV range r (n = what the range has beyond its first two
+// batches, at most `limit`); returns n.  The area's previous contents must have been read.
+template <int B>
+__device__ __forceinline__ int stage_range(const uint8_t* packed, const Range& r, int limit, int lane, uint32_t lds) {
+  if (limit <= 0 || r.i >= r.ihi) return 0;
+  const int nb = (r.ihi - r.i + B - 1) / B;
+  const int n = nb - 2 < limit ? (nb - 2 > 0 ? nb - 2 : 0) : limit;
+  if (n > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the area have completed
+  for (int t = 0; t < n; ++t) stage_batch<B>(packed, r, 2 + t, lane, lds + t * B * CHUNK_BYTES);
+  return n;
+}
+
 // Consume chunks [r.i, r.ihi) in batches; st holds batches 0 and 1 when `have` (else they are
 // loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the last
 // batches fetch next_src(0) into X and next_src(1) into Y.
 template <int B, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
-                                             Stream<B>& st, bool have, NextSrc next_src, uint64_t* ts) {
+                                             Stream<B>& st, bool have, NextSrc next_src, const float* stage,
+                                             uint64_t* ts) {
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
@@ -611,8 +653,29 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   };
   u32x4* X = st.v;
   u32x4* Y = st.v + B;
+  // Batches 0 and 1 come from X and Y, batches 2 .. 2 + ls from the wave's LDS area (staged while
+  // the tile's inputs were outstanding), the rest stream through X and Y again: register batch q is
+  // batch rb(q).
+  const int ls = st.sk == r.k && r.r0 == 0 ? st.ls : 0;
   const int nb = (ihi - i + B - 1) / B;
-  const int nbe = nb + (nb & 1);  // an even batch count: the last reloads always go to X, then Y
+  const int nrb = nb - ls;
+  const int nbe = nrb + (nrb & 1);  // an even register batch count: the last reloads go to X, then Y
+  auto rb = [&](int q) { return q < 2 ? q : q + ls; };
+  const float* stg = stage + lane * 4;
+  auto consume_staged = [&]() {
+    if (ls > 0) {
+      // the staging loads were issued before the 2B register loads of the first pair, the last
+      // vector-memory instructions: once at most 2B are outstanding, they have landed
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      static_assert(2 * B == 8, "the wait above counts the first pair's reloads");
+      for (int t = 0; t < ls; ++t) {
+        u32x4 w[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) w[u] = *reinterpret_cast<const u32x4*>(stg + (t * B + u) * (CHUNK_BYTES / 4));
+        consume_batch(w, i + (2 + t) * B);
+      }
+    }
+  };
   if (!have) {
     load_gemv_batch<B>(X, packed, r, 0, lane);
     load_gemv_batch<B>(Y, packed, r, 1, lane);
@@ -620,22 +683,25 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   stamp(ts, TS_ENTRY, lane);
   int b = 0;
   for (; b + 2 < nbe; b += 2) {
-    consume_batch(X, i + b * B);
-    load_gemv_batch<B>(X, packed, r, b + 2, lane);
+    consume_batch(X, i + rb(b) * B);
+    load_gemv_batch<B>(X, packed, r, rb(b + 2), lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the reload of X ahead of the consumption of Y
     if (b == 0) stamp(ts, TS_FIRST, lane);
-    consume_batch(Y, i + (b + 1) * B);
-    load_gemv_batch<B>(Y, packed, r, b + 3, lane);
+    consume_batch(Y, i + rb(b + 1) * B);
+    load_gemv_batch<B>(Y, packed, r, rb(b + 3), lane);
     __builtin_amdgcn_sched_barrier(0);
+    if (b == 0) consume_staged();
   }
-  // the last two batches: their reloads fetch what follows the range
-  consume_batch(X, i + b * B);
+  // the last two register batches: their reloads fetch what follows the range
+  consume_batch(X, i + rb(b) * B);
   load_batch<B>(X, next_src(0));
   __builtin_amdgcn_sched_barrier(0);
   if (b == 0) stamp(ts, TS_FIRST, lane);
-  consume_batch(Y, i + (b + 1) * B);
+  consume_batch(Y, i + rb(b + 1) * B);
   load_batch<B>(Y, next_src(1));
   __builtin_amdgcn_sched_barrier(0);
+  if (b == 0) consume_staged();
+  if (ls > 0) st.sk = -1;
   if (seg != 0) {
     const float s = wave_sum(acc);
     if (lane == 0) L.part[row * NCOMP + c] = s;
@@ -1396,7 +1462,12 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
     load_gemv_batch<B>(st.v + B, a.packed, r, 1, lane);
     st.k = r.k;
     st.r0 = r.r0;
+    st.sk = -1;
+    st.ls = 0;
   }
+  // this wave's staging area: LDS pointer (reads) and LDS byte address (direct-to-LDS loads)
+  const float* stage_w = L.stage + c * (a.stage_batches * B * (CHUNK_BYTES / 4));
+  const uint32_t stage_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)stage_w;
   int tok_unused = 0;
   bool stop = false;
   for (int step = 0; step < a.n_steps && !stop; ++step) {
@@ -1432,6 +1503,20 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       pin(nr_first);
       pin(kv_first);
       pin(ko);
+      // Batches 2 .. of a first block into the LDS area while this tile's inputs are outstanding
+      // (range tails prefetch batches 0 and 1 into registers): a tile whose share streams beyond
+      // its register prefetch stages its own; one whose share fits the registers stages the next
+      // GEMV tile's, so that the staging lands during a wait that is already there (its own
+      // inputs) instead of lengthening the next tile's.  Not issued with the tail prefetch: a
+      // wavefront's outstanding loads are bounded, and the issue would stall the tile's end.
+      if (is_gemv(t.kind) && st.sk != k) {
+        const int own = r_first.i < r_first.ihi ? (r_first.ihi - r_first.i + B - 1) / B : 0;
+        const Range& sr = own > 2 ? r_first : ng;
+        if (own > 2 || (ng.k >= 0 && ng.k != k && ng.r0 == 0)) {
+          st.ls = stage_range<B>(a.packed, sr, a.stage_batches, lane, stage_lds);
+          st.sk = st.ls > 0 ? sr.k : -1;
+        }
+      }
       if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
@@ -1452,9 +1537,10 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                              : next_attn ? no_range()
                                          : ng;
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
-            stream_range<B>(L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0, [&](int h) {
-              return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane));
-            }, r0 == 0 ? ts : nullptr);
+            stream_range<B>(
+                L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
+                [&](int h) { return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
+                stage_w, r0 == 0 ? ts : nullptr);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
             if (r0 == 0) stamp(ts, TS_DONE, lane);
@@ -1478,6 +1564,9 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       }
     }
   }
+  // the last range's tail prefetched (into registers and the LDS area) for a range that does not
+  // come: let those loads land before the wavefront ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int HD, int G>
@@ -1485,7 +1574,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
   Lds L;
-  L.vec = reinterpret_cast<float*>(lds_raw);
+  L.stage = reinterpret_cast<float*>(lds_raw);
+  L.vec = L.stage + a.lds_stage_floats;
   L.part = L.vec + a.lds_vec_floats;
   L.xres = L.part + a.lds_part_floats;
   L.small = L.xres + a.lds_xres_floats;

@@ -38,10 +38,14 @@ struct SegDesc {  // per-wave GEMV geometry of one worker (LDS copy used by the 
 };
 constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
 constexpr int MAX_BLOCK_ROWS = 640;
+constexpr int32_t LDS_LIMIT = 160 * 1024;  // LDS of one CU (gfx950)
 // Register streaming of the compute wavefronts: two batches of STREAM_BATCH 16-byte loads per
 // lane in flight (STREAM_DEPTH), for weight chunks and K/V rows alike.
 constexpr int STREAM_BATCH = 4;
 constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
+// Up to this many further batches of a compute wavefront's next GEMV range are staged in its LDS
+// area by direct-to-LDS loads issued with the register prefetch (as many as the LDS holds).
+constexpr int MAX_STAGE_BATCHES = 2;
 constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit  // GEMV rows staged per LDS block
 
 struct TileDesc {   // 32 bytes
@@ -122,6 +126,8 @@ struct KernelArgs {
   int32_t lds_vec_floats;    // LDS layout
   int32_t lds_part_floats;
   int32_t lds_xres_floats;
+  int32_t lds_stage_floats;  // NCOMP staging areas of stage_batches batches
+  int32_t stage_batches;
 };
 
 }  // namespace tiles

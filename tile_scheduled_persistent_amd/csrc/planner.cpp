@@ -88,7 +88,8 @@ uint64_t plan_checksum(const HostPlan& p) {
   const int64_t dims[] = {s.n_layers, s.H, s.n_heads, s.n_kv, s.hd, s.F, s.V, s.G, s.qkv_rows, s.Hpad, s.Qpad, s.Fpad,
                           s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
-                          p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words};
+                          p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
+                          p.stage_batches};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -332,9 +333,16 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
                 (int32_t)round_up((int64_t)p.waves.size() * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
                                       (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
+  if (p.lds_bytes > LDS_LIMIT) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
+  // staging areas for the next GEMV range's chunks, as many batches per compute wave as fit
+  const int32_t stage_batch_bytes = NCOMP * STREAM_BATCH * CHUNK_BYTES;
+  // (the area sits at LDS address 0 and must end below 64 KB: the load's LDS address is 16 bits)
+  p.stage_batches = std::min<int32_t>({MAX_STAGE_BATCHES, (LDS_LIMIT - p.lds_bytes) / stage_batch_bytes,
+                                       65536 / stage_batch_bytes});
+  p.lds_stage_floats = p.stage_batches * stage_batch_bytes / 4;
+  p.lds_bytes += p.lds_stage_floats * 4;
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
-  if (p.lds_bytes > 160 * 1024) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
 
   int rc = validate_plan(p, err);
   if (rc != TILES_OK) return rc;
@@ -528,6 +536,9 @@ int validate_plan(const HostPlan& p, std::string& err) {
 
   // LDS capacity for every wave's staging
   if (p.lds_part_floats / NCOMP < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
+  if (p.stage_batches < 0 || p.stage_batches > MAX_STAGE_BATCHES ||
+      p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT)
+    return fail(err, TILES_E_PLAN, "bad LDS staging area");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
   if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");

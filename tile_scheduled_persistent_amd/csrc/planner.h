@@ -63,6 +63,7 @@ struct HostPlan {
   std::vector<int32_t> wave_busy;
   double max_over_mean = 1.0;
   int32_t lds_vec_floats = 0, lds_part_floats = 0, lds_xres_floats = 0, lds_bytes = 0;
+  int32_t lds_stage_floats = 0, stage_batches = 0;  // staging of the next GEMV range's chunks
   int64_t ll_words = 0;        // tagged-data buffers of all waves (uint32 words)
   uint64_t checksum = 0;
 };
