@@ -73,6 +73,7 @@ typedef struct tiles_config {
   uint32_t flags;         /* TILES_DEBUG_HIDDEN | TILES_TRACE | TILES_POISON */
   int32_t kv_splits;      /* split-KV count per KV head; 0 lets the planner choose */
   int32_t combine_mode;   /* 0 planner choice, 1 combine splits in the o_proj prologue, 2 own wave */
+  int32_t attn_heads;     /* query heads per attention tile (divides n_heads / n_kv_heads); 0 planner choice */
   int32_t n_workers;      /* 0 = one workgroup per compute unit (required on the GPU) */
   void *stream;           /* hipStream_t used by create (copies) and by every decode; NULL = null stream */
 } tiles_config_t;
@@ -119,6 +120,8 @@ typedef struct tiles_plan_info {
   double max_over_mean;       /* worst per-wave worker byte imbalance (max / mean over busy waves) */
   uint64_t checksum;          /* schedule checksum (re-checked at every decode) */
   uint64_t build_id;          /* worker-kernel build id the plan was made for */
+  int32_t attn_heads;         /* query heads per attention tile */
+  int32_t reserved;
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */

@@ -90,6 +90,20 @@ def test_untileable_shapes_are_rejected(bad, code):
     assert e.value.code == code
 
 
+def test_attention_heads_per_tile():
+    # planner choice: the group's query heads spread over as many tiles as the workers allow
+    assert tiles.dry_run(LLAMA_1B, 1087).attn_heads == 1
+    for t in (1, 2, 4):
+        info = tiles.dry_run(LLAMA_1B, 1087, attn_heads=t)
+        assert info.attn_heads == t
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(LLAMA_1B, 1087, attn_heads=3)  # does not divide the 4 query heads per KV head
+    assert e.value.code == tiles.TILES_E_CONFIG
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(LLAMA_1B, 1087, kv_splits=16, attn_heads=1)  # 8 x 4 x 16 tiles > 256 workers
+    assert e.value.code == tiles.TILES_E_CONFIG
+
+
 def test_kv_capacity_limit():
     tiles.dry_run(TINY, 1 << 23)
     with pytest.raises(tiles.TilesError) as e:

@@ -140,11 +140,13 @@ def test_wide_layers_staged_prefetch():
         _oracle_forced(s, toks, 6, plan, tag="wide")
 
 
-def test_qk_norm_head_dim_128():
+@pytest.mark.parametrize("heads", [0, 2, 4])
+def test_qk_norm_head_dim_128(heads):
     s = Setup(QK128, 64, 29)
     toks = synth.make_tokens(QK128, 1)
-    with s.plan() as plan:
-        _oracle_forced(s, toks, 10, plan, tag="qk128")
+    with s.plan(attn_heads=heads) as plan:
+        assert heads == 0 or plan.info().attn_heads == heads
+        _oracle_forced(s, toks, 10, plan, tag=f"qk128 heads/tile={heads}")
 
 
 @pytest.mark.parametrize("splits,mode", [(1, 1), (3, 1), (3, 2), (7, 2), (16, 2)])

@@ -157,7 +157,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.s.G);
+  p->kernel = worker_kernel(hp.s.hd, hp.T);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -393,6 +393,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->n_tiles = n;
   info->kv_splits = hp.S;
   info->combine_mode = hp.combine_in_o ? 1 : 2;
+  info->attn_heads = hp.T;
   info->occupancy = occupancy;
   info->packed_bytes = hp.packed_bytes;
   info->weight_bytes_per_step = hp.weight_bytes_per_step;

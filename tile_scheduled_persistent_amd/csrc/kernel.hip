@@ -211,7 +211,7 @@ __device__ __forceinline__ TileDesc tile_of(const Lds& L, int k) {
   t.nrows = sc(x.nrows);
   t.kpad = sc(x.kpad);
   t.woff = sc64(x.woff);
-  t.aux0 = 0;
+  t.aux0 = sc(x.aux0);  // attention: first query head of the tile
   t.aux1 = 0;
   return t;
 }
@@ -778,12 +778,13 @@ __device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + G * HD
 template <int HD, int G>
 __device__ __forceinline__ float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * pstride<HD>(); }
 
-// all wavefronts: raw q (G heads), k, v of KV group g into vec from the QKV wave's output
+// all wavefronts: raw q (the tile's G query heads, from head qa), k, v of KV head g into vec from
+// the QKV wave's output
 template <int HD, int G>
-__device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, const uint32_t* src, int g, int slot, int lane,
-                           uint32_t par) {
+__device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, const uint32_t* src, int g, int qa, int slot,
+                                           int lane, uint32_t par) {
   constexpr int NQ = G * HD / 4, NK = HD / 4;
-  const int q0 = g * G * HD / 4;
+  const int q0 = qa * HD / 4;
   const int k0 = (a.n_heads * HD + g * HD) / 4;
   const int v0 = (a.n_heads * HD + a.n_kv * HD + g * HD) / 4;
   return gather<2>(
@@ -835,10 +836,12 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
   }
 }
 
-// control wave, after barrier A: the split holding the current position writes its K/V row
+// control wave, after barrier A: the split holding the current position writes its K/V row (the
+// tile of the KV head's first query heads, when the heads are spread over several tiles)
 template <int HD, int G>
 __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
-                                 int64_t L_att) {
+                                 int qa, int64_t L_att) {
+  if (qa != g * (a.n_heads / a.n_kv)) return;
   const float* kc = L.part + G * HD;
   const float* vc = kc + HD;
   const int64_t ch = (L_att + a.S - 1) / a.S;
@@ -1171,9 +1174,9 @@ __device__ __forceinline__ void attn_merge_phase(const Lds& L, int wave_index, i
   }
 }
 
-// control wave, after barrier E: publish the merged partials of query heads g*G .. g*G+G-1, split sp
+// control wave, after barrier E: publish the merged partials of query heads qa .. qa + G - 1, split sp
 template <int HD, int G>
-__device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& L, uint32_t* out, int lane, int g, int sp,
+__device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& L, uint32_t* out, int lane, int qa, int sp,
                                 uint32_t par) {
   constexpr int PS = pstride<HD>();
   constexpr int N = (G * PS + 63) / 64;  // values per lane
@@ -1184,7 +1187,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int idx = lane + 64 * i;
-    if (idx < G * PS) publish(out, ((int64_t)(g * G + idx / PS) * a.S + sp) * PS + idx % PS, v[i], par);
+    if (idx < G * PS) publish(out, ((int64_t)(qa + idx / PS) * a.S + sp) * PS + idx % PS, v[i], par);
   }
 }
 
@@ -1259,7 +1262,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           gk1 = bf16_to_f32(gkk[lane + HALF]);
         }
       }
-      ab = gather_qkv<HD, G>(a, L, in, t.row0, wave, lane, par);
+      ab = gather_qkv<HD, G>(a, L, in, t.row0, t.aux0, wave, lane, par);
       if (wave == 0 && lane < HALF) {
         L.small[SM_ROPE + 2 * lane] = cs.x;
         L.small[SM_ROPE + 2 * lane + 1] = cs.y;
@@ -1388,7 +1391,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
         }
       } else if (t.kind == KIND_ATTN) {
-        cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, L_att);
+        cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, t.aux0, L_att);
         // The KV row must be complete before this worker publishes anything later readers of
         // the row depend on (its split partial, below); the wait overlaps the compute waves.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1401,7 +1404,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         }
         attn_merge_phase<HD, G>(L, 0, lane);
         __syncthreads();  // E: merged partial ready
-        cw_attn_publish<HD, G>(a, L, out, lane, t.row0, t.nrows, par);
+        cw_attn_publish<HD, G>(a, L, out, lane, t.aux0, t.nrows, par);
       } else if (t.kind == KIND_COMBINE) {
         if (a.trace) t_cmp = wall_clock64();
         for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);

@@ -46,7 +46,7 @@ constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 // Up to this many further batches of a compute wavefront's next GEMV range are staged in its LDS
 // area by direct-to-LDS loads issued with the register prefetch (as many as the LDS holds).
 constexpr int MAX_STAGE_BATCHES = 2;
-constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit  // GEMV rows staged per LDS block
+constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit
 
 struct TileDesc {   // 32 bytes
   int32_t kind;

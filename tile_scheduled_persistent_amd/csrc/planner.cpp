@@ -86,7 +86,7 @@ uint64_t plan_checksum(const HostPlan& p) {
   };
   const Shape& s = p.s;
   const int64_t dims[] = {s.n_layers, s.H, s.n_heads, s.n_kv, s.hd, s.F, s.V, s.G, s.qkv_rows, s.Hpad, s.Qpad, s.Fpad,
-                          s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o,
+                          s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o, p.T,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
                           p.stage_batches};
@@ -133,7 +133,21 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
 
   // split-KV and combine placement
   p.S = cfg.kv_splits > 0 ? cfg.kv_splits : choose_splits(s, W);
-  if (p.S < 1 || (int64_t)p.S * s.n_kv > W) return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads exceeds workers");
+  // query heads per attention tile: the group's heads spread over as many tiles as the workers
+  // allow (each re-reads the split's K/V rows; attention is bound by arithmetic per head)
+  if (cfg.attn_heads > 0) {
+    p.T = cfg.attn_heads;
+    if (s.G % p.T != 0) return fail(err, TILES_E_CONFIG, "attn_heads must divide n_heads / n_kv_heads");
+  } else {
+    p.T = s.G;
+    for (int32_t t = 1; t <= s.G; ++t)
+      if (s.G % t == 0 && (int64_t)s.n_kv * (s.G / t) * std::max(p.S, 1) <= W) {
+        p.T = t;
+        break;
+      }
+  }
+  if (p.S < 1 || (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
+    return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads * (query heads per KV head / attn_heads) exceeds workers");
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
@@ -220,16 +234,19 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
         if (b > a) p.copies.push_back({src[m], l, a - bounds[m], b - a, s.H, dst + (a - lo) * s.Hpad * 2, (int64_t)s.Hpad * 2});
       }
     });
-    // attention: one tile per (KV head, split)
+    // attention: one tile per (KV head, group of T query heads, split)
     {
       int32_t wv = new_wave(KIND_ATTN, l);
+      const int32_t nhs = s.G / p.T;
       for (int g = 0; g < s.n_kv; ++g)
-        for (int sp = 0; sp < p.S; ++sp) {
-          TileDesc& t = tile_at(wv, g * p.S + sp);
-          t.kind = KIND_ATTN;
-          t.row0 = g;
-          t.nrows = sp;
-        }
+        for (int hs = 0; hs < nhs; ++hs)
+          for (int sp = 0; sp < p.S; ++sp) {
+            TileDesc& t = tile_at(wv, (g * nhs + hs) * p.S + sp);
+            t.kind = KIND_ATTN;
+            t.row0 = g;
+            t.nrows = sp;
+            t.aux0 = g * s.G + hs * p.T;  // first query head
+          }
     }
     if (!p.combine_in_o) {
       int32_t wv = new_wave(KIND_COMBINE, l);
@@ -323,7 +340,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
   // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
   const int32_t ps = s.hd + 4;
-  part = std::max(part, s.G * s.hd + 2 * s.hd + (NCOMP + 1) * s.G * ps);
+  part = std::max(part, p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * ps);
   part = std::max(part, p.S * ps);                                  // one head's splits (combine tile)
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
@@ -427,18 +444,21 @@ int validate_plan(const HostPlan& p, std::string& err) {
           break;
         }
         case KIND_ATTN: {
-          if (t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S)
+          const int32_t hs = (t.aux0 - t.row0 * s.G) / p.T;
+          if (t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S || t.aux0 < t.row0 * s.G ||
+              (t.aux0 - t.row0 * s.G) % p.T != 0 || hs >= s.G / p.T)
             return fail(err, TILES_E_PLAN, "attention tile out of range");
-          seen.push_back(t.row0 * p.S + t.nrows);
+          seen.push_back((t.row0 * (s.G / p.T) + hs) * p.S + t.nrows);
           x.reads.push_back({BUF_WAVE + wv - 1, 0, s.qkv_rows});
           // cached positions of this KV head (all positions before the current one)
           const int64_t kvbase = ((int64_t)layer * s.n_kv + t.row0) * s.max_positions;
           x.reads.push_back({BUF_KV, kvbase, kvbase + s.max_positions - 1});
           // The current position is written by exactly one split (the one holding L-1, checked
-          // for every L below); the model gives that write to split 0 and a slot past every read.
-          if (t.nrows == 0) x.writes.push_back({BUF_KV, kvbase + s.max_positions - 1, kvbase + s.max_positions});
-          for (int g2 = 0; g2 < s.G; ++g2) {  // one (hd + 4)-word record per query head
-            const int64_t h = (int64_t)t.row0 * s.G + g2, rec = (h * p.S + t.nrows) * (s.hd + 4);
+          // for every L below) of the KV head's first query-head group; the model gives that write
+          // to split 0 and a slot past every read.
+          if (t.nrows == 0 && hs == 0) x.writes.push_back({BUF_KV, kvbase + s.max_positions - 1, kvbase + s.max_positions});
+          for (int g2 = 0; g2 < p.T; ++g2) {  // one (hd + 4)-word record per query head
+            const int64_t h = (int64_t)t.aux0 + g2, rec = (h * p.S + t.nrows) * (s.hd + 4);
             x.writes.push_back({BUF_WAVE + wv, rec, rec + s.hd + 4});
           }
           break;
@@ -456,7 +476,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
     }
     if (kind == KIND_ATTN || kind == KIND_COMBINE) {
       std::sort(seen.begin(), seen.end());
-      const int want_n = kind == KIND_ATTN ? s.n_kv * p.S : s.n_heads;
+      const int want_n = kind == KIND_ATTN ? s.n_kv * (s.G / p.T) * p.S : s.n_heads;
       if ((int)seen.size() != want_n) return fail(err, TILES_E_PLAN, "attention/combine tiles do not cover every head");
       for (int i = 0; i < want_n; ++i)
         if (seen[i] != i) return fail(err, TILES_E_PLAN, "attention/combine tile duplicated or missing");

@@ -52,6 +52,7 @@ struct HostPlan {
   int32_t W = 0;               // workers
   int32_t S = 1;               // KV splits
   int32_t combine_in_o = 1;    // 1 prologue, 0 own wave
+  int32_t T = 1;               // query heads per attention tile (divides G)
   std::vector<WaveDesc> waves;
   std::vector<TileDesc> tiles; // [n_waves][W]
   std::vector<LayerSmall> small;
