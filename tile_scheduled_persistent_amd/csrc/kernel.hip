@@ -1516,7 +1516,9 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         const int own = r_first.i < r_first.ihi ? (r_first.ihi - r_first.i + B - 1) / B : 0;
         const Range& sr = own > 2 ? r_first : ng;
         if (own > 2 || (ng.k >= 0 && ng.k != k && ng.r0 == 0)) {
-          st.ls = stage_range<B>(a.packed, sr, a.stage_batches, lane, stage_lds);
+          // own staging lands during this tile's input wait and delays its end: one batch, which
+          // arrives within that wait; the next tile's staging may take the whole area
+          st.ls = stage_range<B>(a.packed, sr, own > 2 ? 1 : a.stage_batches, lane, stage_lds);
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
