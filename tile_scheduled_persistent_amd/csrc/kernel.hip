@@ -292,6 +292,8 @@ __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src,
       }
       if (__all(pending == 0)) break;
       if (watch_tick(a, spins, lane)) return true;
+      // a long wait polls less often: less polling traffic on the fabric for the other workers
+      if (spins > 4) __builtin_amdgcn_s_sleep(8);
     }
   }
   return false;
