@@ -741,7 +741,7 @@ constexpr int pstride() { return HD + 4; }
 // part + h * S * (HD + 4) -- into out[h * HD + d]: acc weighted by 2^(m_s - max m) over the
 // weighted l ("Tiles", split-KV attention combine).  Each thread takes four consecutive
 // dimensions of one head; a split's (m, l) pair and accumulator slice are read with
-// independent loads, so their latencies overlap.  Empty splits (l = 0) carry no weight; a head
+// independent loads, and both loops over the splits are unrolled, so the LDS latencies overlap.  Empty splits (l = 0) carry no weight; a head
 // with no positions gives 0.
 template <int HD>
 __device__ __forceinline__ void merge_heads(const float* part, int nh, int S, int tid, float* out) {
@@ -750,11 +750,14 @@ __device__ __forceinline__ void merge_heads(const float* part, int nh, int S, in
     const int h = o / HD, d = o % HD;
     const float* P = part + h * S * PS;
     float mm = -INFINITY;
+#pragma unroll 4
     for (int sp = 0; sp < S; ++sp) {
-      const float2 ml = *reinterpret_cast<const float2*>(P + sp * PS);
-      mm = ml.y > 0.f ? fmaxf(mm, ml.x) : mm;
+      // (m, l) as one 8-byte read (the compiler would read l, branch, then read m)
+      const uint2 ml = *reinterpret_cast<const uint2*>(P + sp * PS);
+      mm = __uint_as_float(ml.y) > 0.f ? fmaxf(mm, __uint_as_float(ml.x)) : mm;
     }
     float ll = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 4
     for (int sp = 0; sp < S; ++sp) {
       const float* st = P + sp * PS;
       const float2 ml = *reinterpret_cast<const float2*>(st);
