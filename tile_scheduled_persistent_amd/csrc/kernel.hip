@@ -425,9 +425,11 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
 // ---------------------------------------------------------------------------
 // compute wave: weight streaming.  Each compute wave reads its share of a GEMV block (a
 // contiguous chunk range) with 16-byte loads into registers, in batches of STREAM_BATCH
-// chunks that ping-pong between two register sets X and Y: while one batch is consumed the
-// other is in flight.  The reloads issued after a range's last batches fetch the first two
-// batches of the wave's next range -- the next block, the next GEMV tile or the (K, V) rows of
+// chunks that rotate through a ring of NB register sets: while one batch is consumed the
+// other NB - 1 are in flight (the per-wave depth sets how many bytes a compute unit keeps in
+// flight, and so its share of the HBM bandwidth).  The reloads issued after a range's last
+// batches fetch the first NB batches of the wave's next range -- the next block, the next GEMV
+// tile or the (K, V) rows of
 // its next attention split -- so those bytes arrive while the workgroup publishes this tile's
 // outputs and gathers the next inputs: weights (and cached KV rows) do not depend on
 // activations, only the dot products do (the Tiles page credits this prefetch idea to the
@@ -511,13 +513,13 @@ __device__ __forceinline__ Range next_gemv(const SegDesc* segs, int n_waves, int
   return no_range();
 }
 
-// The two batch register sets of a compute wave: X = v[0, B), Y = v[B, 2B).
-template <int B>
+// The NB batch register sets of a compute wave: batch slot h = v[h * B, (h + 1) * B).
+template <int B, int NB>
 struct Stream {
-  u32x4 v[2 * B];
+  u32x4 v[NB * B];
   int k;   // wave whose data the registers hold (-1: none)
   int r0;  // GEMV block of that wave
-  int sk;  // wave whose first block has batches 2 .. 2 + ls staged in the wave's LDS area (-1: none)
+  int sk;  // wave whose first block has batches NB .. NB + ls staged in the wave's LDS area (-1: none)
   int ls;
 };
 
@@ -597,24 +599,32 @@ __device__ __forceinline__ void stage_batch(const uint8_t* packed, const Range& 
         : "memory");
   }
 }
-// Stage batches 2 .. 2 + n of GEMV range r (n = what the range has beyond its first two
+// Stage batches NB .. NB + n of GEMV range r (n = what the range has beyond its first NB
 // batches, at most `limit`); returns n.  The area's previous contents must have been read.
-template <int B>
+template <int B, int NB>
 __device__ __forceinline__ int stage_range(const uint8_t* packed, const Range& r, int limit, int lane, uint32_t lds) {
   if (limit <= 0 || r.i >= r.ihi) return 0;
   const int nb = (r.ihi - r.i + B - 1) / B;
-  const int n = nb - 2 < limit ? (nb - 2 > 0 ? nb - 2 : 0) : limit;
+  const int n = nb - NB < limit ? (nb - NB > 0 ? nb - NB : 0) : limit;
   if (n > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the area have completed
-  for (int t = 0; t < n; ++t) stage_batch<B>(packed, r, 2 + t, lane, lds + t * B * CHUNK_BYTES);
+  for (int t = 0; t < n; ++t) stage_batch<B>(packed, r, NB + t, lane, lds + t * B * CHUNK_BYTES);
   return n;
 }
 
-// Consume chunks [r.i, r.ihi) in batches; st holds batches 0 and 1 when `have` (else they are
-// loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the last
-// batches fetch next_src(0) into X and next_src(1) into Y.
-template <int B, typename NextSrc>
+// s_waitcnt with only the vector-memory count N enforced (gfx9 encoding: vmcnt[3:0] in bits
+// 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Consume chunks [r.i, r.ihi) in batches; st holds batches 0 .. NB - 1 when `have` (else they
+// are loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the
+// last NB batches fetch next_src(0) .. next_src(NB - 1) into the NB register sets.
+template <int B, int NB, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
-                                             Stream<B>& st, bool have, NextSrc next_src, const float* stage,
+                                             Stream<B, NB>& st, bool have, NextSrc next_src, const float* stage,
                                              uint64_t* ts) {
   const int C = r.C;
   const int i = r.i;
@@ -653,55 +663,52 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
 #pragma unroll
     for (int u = 0; u < B; ++u) consume(w[u], jb + u < ihi, xv[u]);
   };
-  u32x4* X = st.v;
-  u32x4* Y = st.v + B;
-  // Batches 0 and 1 come from X and Y, batches 2 .. 2 + ls from the wave's LDS area (staged while
-  // the tile's inputs were outstanding), the rest stream through X and Y again: register batch q is
-  // batch rb(q).
+  // Batches 0 .. NB - 1 come from the register sets, batches NB .. NB + ls from the wave's LDS
+  // area (staged while the tile's inputs were outstanding), the rest stream through the register
+  // sets again: register batch q is batch rb(q).
   const int ls = st.sk == r.k && r.r0 == 0 ? st.ls : 0;
   const int nb = (ihi - i + B - 1) / B;
   const int nrb = nb - ls;
-  const int nbe = nrb + (nrb & 1);  // an even register batch count: the last reloads go to X, then Y
-  auto rb = [&](int q) { return q < 2 ? q : q + ls; };
+  const int nbe = (nrb + NB - 1) / NB * NB;  // whole ring passes: the last NB reloads fetch what follows
+  auto rb = [&](int q) { return q < NB ? q : q + ls; };
   const float* stg = stage + lane * 4;
   auto consume_staged = [&]() {
     if (ls > 0) {
-      // the staging loads were issued before the 2B register loads of the first pair, the last
-      // vector-memory instructions: once at most 2B are outstanding, they have landed
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      static_assert(2 * B == 8, "the wait above counts the first pair's reloads");
+      // the staging loads were issued before the NB * B reloads of the first ring pass, the last
+      // vector-memory instructions: once at most NB * B are outstanding, they have landed
+      wait_vmcnt<NB * B>();
       for (int t = 0; t < ls; ++t) {
         u32x4 w[B];
 #pragma unroll
         for (int u = 0; u < B; ++u) w[u] = *reinterpret_cast<const u32x4*>(stg + (t * B + u) * (CHUNK_BYTES / 4));
-        consume_batch(w, i + (2 + t) * B);
+        consume_batch(w, i + (NB + t) * B);
       }
     }
   };
   if (!have) {
-    load_gemv_batch<B>(X, packed, r, 0, lane);
-    load_gemv_batch<B>(Y, packed, r, 1, lane);
+#pragma unroll
+    for (int h = 0; h < NB; ++h) load_gemv_batch<B>(st.v + h * B, packed, r, h, lane);
   }
   stamp(ts, TS_ENTRY, lane);
   int b = 0;
-  for (; b + 2 < nbe; b += 2) {
-    consume_batch(X, i + rb(b) * B);
-    load_gemv_batch<B>(X, packed, r, rb(b + 2), lane);
-    __builtin_amdgcn_sched_barrier(0);  // keep the reload of X ahead of the consumption of Y
-    if (b == 0) stamp(ts, TS_FIRST, lane);
-    consume_batch(Y, i + rb(b + 1) * B);
-    load_gemv_batch<B>(Y, packed, r, rb(b + 3), lane);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; b + NB < nbe; b += NB) {
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      consume_batch(st.v + h * B, i + rb(b + h) * B);
+      load_gemv_batch<B>(st.v + h * B, packed, r, rb(b + h + NB), lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep each reload ahead of the next slot's consumption
+      if (b == 0 && h == 0) stamp(ts, TS_FIRST, lane);
+    }
     if (b == 0) consume_staged();
   }
-  // the last two register batches: their reloads fetch what follows the range
-  consume_batch(X, i + rb(b) * B);
-  load_batch<B>(X, next_src(0));
-  __builtin_amdgcn_sched_barrier(0);
-  if (b == 0) stamp(ts, TS_FIRST, lane);
-  consume_batch(Y, i + rb(b + 1) * B);
-  load_batch<B>(Y, next_src(1));
-  __builtin_amdgcn_sched_barrier(0);
+  // the last ring pass: its reloads fetch what follows the range
+#pragma unroll
+  for (int h = 0; h < NB; ++h) {
+    consume_batch(st.v + h * B, i + rb(b + h) * B);
+    load_batch<B>(st.v + h * B, next_src(h));
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == 0 && h == 0) stamp(ts, TS_FIRST, lane);
+  }
   if (b == 0) consume_staged();
   if (ls > 0) st.sk = -1;
   if (seg != 0) {
@@ -904,28 +911,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache,
   return rsrc(cache + kvrow0 * hd);
 }
 
-// The opening loads of an attention split -- the first B (K, V) position-group pairs of this
-// wave's range -- prepared ahead: the KV head's row bases and each pair's per-lane byte offset
-// (a slot without a position reads the dummy row, as in load_kv).
-template <int B>
+// The opening loads of an attention split -- the first NP (K, V) position-group pairs of this
+// wave's range, one per ring slot -- prepared ahead: the KV head's row bases and each pair's
+// per-lane byte offset (a slot without a position reads the dummy row, as in load_kv).
+template <int NP>
 struct KvOpen {
   const uint16_t* kbase;
   const uint16_t* vbase;
-  uint32_t off[B];
+  uint32_t off[NP];
 };
-template <int HD, int B>
-__device__ __forceinline__ KvOpen<B> kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c,
+template <int HD, int NP>
+__device__ __forceinline__ KvOpen<NP> kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c,
                                              int lane) {
   constexpr int LPP = HD / 8, P = 64 / LPP;
   const int pp = lane / LPP, dseg = lane % LPP;
-  KvOpen<B> o;
+  KvOpen<NP> o;
   const AttnRange r = attn_range(a, sp, c, L_att);
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   o.kbase = a.kv_k + kvrow0 * HD;
   o.vbase = a.kv_v + kvrow0 * HD;
   const int cur = (int)L_att - 1, dummy = (int)a.kv_cap - 1;
 #pragma unroll
-  for (int s = 0; s < B; ++s) {
+  for (int s = 0; s < NP; ++s) {
     const int j = r.wlo + s * P + pp;
     const int jj = (j < r.whi && j != cur) ? j : dummy;
     o.off[s] = ((uint32_t)jj * LPP + dseg) * 16u;
@@ -933,11 +940,12 @@ __device__ __forceinline__ KvOpen<B> kv_open(const KernelArgs& a, int layer, int
   return o;
 }
 
-// Half h of the opening (pairs h*B/2 .. h*B/2 + B/2 - 1) into w[0, B): the start of the ring
-// compute_attention runs on, loaded while the previous tile (QKV) streams.  The cache rows do
-// not depend on this step's q; the current position's row is never loaded (it comes from LDS).
-template <int B>
-__device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen<B>& o, int h) {
+// Part h of the opening (pairs h*B/2 .. h*B/2 + B/2 - 1) as one batch of B loads: the start of
+// the ring compute_attention runs on, loaded while the previous tile (QKV) streams.  The cache
+// rows do not depend on this step's q; the current position's row is never loaded (it comes
+// from LDS).
+template <int B, int NP>
+__device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen<NP>& o, int h) {
   BatchSrc<B> b;
   const __amdgpu_buffer_rsrc_t rk = rsrc(o.kbase), rv = rsrc(o.vbase);
 #pragma unroll
@@ -965,12 +973,12 @@ __device__ __forceinline__ void pin(Range& r) {
   pin(r.ihi);
   pin(r.base);
 }
-template <int B>
-__device__ __forceinline__ void pin(KvOpen<B>& o) {
+template <int NP>
+__device__ __forceinline__ void pin(KvOpen<NP>& o) {
   pin(o.kbase);
   pin(o.vbase);
 #pragma unroll
-  for (int s = 0; s < B; ++s) pin_v(o.off[s]);
+  for (int s = 0; s < NP; ++s) pin_v(o.off[s]);
 }
 
 template <int HD>
@@ -980,17 +988,17 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 }
 
 // compute wave: one share of an attention split.  The position groups run through a ring of
-// D = B (K, V) register pairs -- the stream registers themselves, filled with the first D groups
+// D = NB * B / 2 (K, V) register pairs -- the stream registers themselves, filled with the first D groups
 // while the previous tile streamed: each step consumes one slot and reloads it with the group D
-// steps ahead (past the range the reload re-reads row 0, a cached dummy; every load is
-// unconditional, see the weight streaming above).  after() then reuses the registers to fetch
-// the next GEMV tile's first batches.
-template <int HD, int G, int B, typename After>
+// steps ahead (past the range the reload reads the dummy row; every load is unconditional, see
+// the weight streaming above).  after(h) reuses the registers of batch slot h to fetch batch h
+// of the next GEMV tile.
+template <int HD, int G, int B, int NB, typename After>
 __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
-                                                  int g, int sp, int64_t L_att, Stream<B>& pf, After after,
+                                                  int g, int sp, int64_t L_att, Stream<B, NB>& pf, After after,
                                                   uint64_t* ts) {
   constexpr int PS = pstride<HD>();
-  constexpr int D = B;  // ring slots: (K, V) pairs in the 2B stream registers
+  constexpr int D = NB * B / 2;  // ring slots: (K, V) pairs in the NB * B stream registers
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
@@ -1066,10 +1074,11 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   }
   stamp(ts, TS_ENTRY, lane);
   // One pass per D position groups (the ring): scores of every slot from its K row, one raise of
-  // the running maximum, then the weighted V rows; each slot is reloaded (group + D) as soon as
-  // its V row is used.  Slots past the range, or holding the current position (taken from LDS
-  // below), are masked.
-  for (int g0 = 0; g0 < ngroups; g0 += D) {
+  // the running maximum, then the weighted V rows.  Slots past the range, or holding the current
+  // position (taken from LDS below), are masked.  In every pass but the last each slot is
+  // reloaded (group + D) as soon as its V row is used; in the last pass each batch of B / 2
+  // slots, once used, fetches batch h of the next GEMV tile instead (after(h)).
+  auto pass = [&](int g0, bool last) {
     float sc[D][G], bm[G];
     bool valid[D];
 #pragma unroll
@@ -1092,12 +1101,19 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       float vf[8];
       unpack8<HD>(pf.v[2 * s + 1], vf);
       accumulate(valid[s], sc[s], vf);
-      load_kv<HD>(rk, rv, wlo + (g0 + s + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
-      __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
+      if (!last) {
+        load_kv<HD>(rk, rv, wlo + (g0 + s + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+        __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
+      } else if (s % (B / 2) == B / 2 - 1) {
+        after(s / (B / 2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
     }
-  }
-  after();
+  };
+  int g0 = 0;
+  for (; g0 + D < ngroups; g0 += D) pass(g0, false);
+  pass(g0, true);
   if (wlo <= cur && cur < whi) {  // the current position (its K/V row is in LDS): lane group 0
     float kf[8], vf[8], sc[G], bm[G];
 #pragma unroll
@@ -1457,17 +1473,27 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
 // compute wave loop
 // ---------------------------------------------------------------------------
 
+
+// 16 KB per wave, 112 KB per compute unit in flight; the variants holding 3 or 4 query heads per
+// attention tile keep two (their attention state leaves no room for more within 256 VGPRs).
+template <int HD, int G>
+constexpr int stream_sets() {
+  return 2;
+}
+
 template <int HD, int G>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
+  constexpr int NB = stream_sets<HD, G>();
+  constexpr int NP = NB * B / 2;  // (K, V) pairs of the attention ring
   const int c = wave - 1;
   volatile int* smi = reinterpret_cast<volatile int*>(L.small);
-  Stream<B> st;
+  Stream<B, NB> st;
   {
     const Range r = next_gemv(L.segs, a.n_waves, -1, block_rows, c);
-    load_gemv_batch<B>(st.v, a.packed, r, 0, lane);
-    load_gemv_batch<B>(st.v + B, a.packed, r, 1, lane);
+#pragma unroll
+    for (int h = 0; h < NB; ++h) load_gemv_batch<B>(st.v + h * B, a.packed, r, h, lane);
     st.k = r.k;
     st.r0 = r.r0;
     st.sk = -1;
@@ -1503,7 +1529,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const bool one_block = block_rows >= rows;
       const Range nr_first0 = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng0;
       const bool kv_first0 = one_block && next_attn;
-      KvOpen<B> ko = kv_open<HD, B>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
+      KvOpen<NP> ko = kv_open<HD, NP>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
       Range ng = ng0, r_first = r_first0, nr_first = nr_first0;
       int kv_first = kv_first0;
       pin(ng);
@@ -1519,11 +1545,11 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       // wavefront's outstanding loads are bounded, and the issue would stall the tile's end.
       if (is_gemv(t.kind) && st.sk != k) {
         const int own = r_first.i < r_first.ihi ? (r_first.ihi - r_first.i + B - 1) / B : 0;
-        const Range& sr = own > 2 ? r_first : ng;
-        if (own > 2 || (ng.k >= 0 && ng.k != k && ng.r0 == 0)) {
+        const Range& sr = own > NB ? r_first : ng;
+        if (own > NB || (ng.k >= 0 && ng.k != k && ng.r0 == 0)) {
           // own staging lands during this tile's input wait and delays its end: one batch, which
           // arrives within that wait; the next tile's staging may take the whole area
-          st.ls = stage_range<B>(a.packed, sr, own > 2 ? 1 : a.stage_batches, lane, stage_lds);
+          st.ls = stage_range<B, NB>(a.packed, sr, own > NB ? 1 : a.stage_batches, lane, stage_lds);
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
@@ -1547,7 +1573,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                              : next_attn ? no_range()
                                          : ng;
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
-            stream_range<B>(
+            stream_range<B, NB>(
                 L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
                 [&](int h) { return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
                 stage_w, r0 == 0 ? ts : nullptr);
@@ -1560,12 +1586,11 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           if (r0 + block_rows < rows) __syncthreads();  // C
         }
       } else if (t.kind == KIND_ATTN) {
-        compute_attention<HD, G, B>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&]() {
-          load_gemv_batch<B>(st.v, a.packed, ng, 0, lane);
-          load_gemv_batch<B>(st.v + B, a.packed, ng, 1, lane);
-          st.k = ng.k;
-          st.r0 = ng.r0;
+        compute_attention<HD, G, B, NB>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&](int h) {
+          load_gemv_batch<B>(st.v + h * B, a.packed, ng, h, lane);
         }, ts);
+        st.k = ng.k;
+        st.r0 = ng.r0;
         stamp(ts, TS_DONE, lane);
         if (wdone && lane == 0) *wdone = wall_clock64();
         __syncthreads();  // B
