@@ -1473,9 +1473,11 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
 // compute wave loop
 // ---------------------------------------------------------------------------
 
-
-// 16 KB per wave, 112 KB per compute unit in flight; the variants holding 3 or 4 query heads per
-// attention tile keep two (their attention state leaves no room for more within 256 VGPRs).
+// Register sets of the compute waves' stream ring (batches in flight per wave).  Two sets keep
+// 8 KB per wave, 56 KB per compute unit in flight.  Four sets (112 KB per compute unit) were
+// measured slower on the 1B-parameter Llama shape: the long streams (LM head, gate/up) did not
+// speed up -- they already run near what the HBM delivers to a stream of 16-byte loads -- while
+// the small tiles paid for padded ring passes and a longer in-order wait before each gather.
 template <int HD, int G>
 constexpr int stream_sets() {
   return 2;
