@@ -1221,7 +1221,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G>
+template <int HD, int G, bool CTRL>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
@@ -1242,7 +1242,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
       float ss = 0.f;
       if (gk == KIND_QKV && layer == 0) {
-        if (wave == 0) {
+        if (CTRL) {
           if (step > 0) {
             ab = gather_token(a, lane, step_parity(step - 1), tok);
             if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
@@ -1257,14 +1257,27 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       break;
     }
     case KIND_O:
-      if (a.combine_in_o) ab = gather_plain(a, L.part, in, a.n_heads * a.S * PS, wave, lane, par);
-      else ab = gather_plain(a, L.vec, in, a.n_heads * HD, wave, lane, par);
-      for (int i = a.n_heads * HD + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
-      break;
     case KIND_DOWN:
-      ab = gather_plain(a, L.vec, in, a.F, wave, lane, par);
-      for (int i = a.F + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+    case KIND_COMBINE: {
+      // one plain gather for all three (a single copy of the polling loop in the code): the
+      // o_proj input (split partials, or merged heads), the SwiGLU rows, or one head's partials
+      float* dst = L.vec;
+      const uint32_t* src = in;
+      int n = a.F, nz = a.F;
+      if (gk == KIND_O) {
+        dst = a.combine_in_o ? L.part : L.vec;
+        n = a.combine_in_o ? a.n_heads * a.S * PS : a.n_heads * HD;
+        nz = a.n_heads * HD;
+      } else if (gk == KIND_COMBINE) {
+        dst = L.part;
+        src = in + (int64_t)t.row0 * a.S * PS;
+        n = a.S * PS;
+        nz = t.kpad;  // no GEMV input to pad
+      }
+      ab = gather_plain(a, dst, src, n, wave, lane, par);
+      for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
       break;
+    }
     case KIND_ATTN: {
       // the control wave also stages the current position's RoPE row and the q/k-norm gains;
       // the loads are issued before the poll and complete while it waits for the producers
@@ -1272,7 +1285,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       float2 cs = {0.f, 0.f};
       float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;
       const int64_t qoff = gain_off(L, layer, 2);
-      if (wave == 0 && lane < HALF) {
+      if (CTRL && lane < HALF) {
         cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(a.pos0 + step) * HALF + lane) * 2);
         if (qoff >= 0) {
           const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.packed + qoff);
@@ -1284,7 +1297,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         }
       }
       ab = gather_qkv<HD, G>(a, L, in, t.row0, t.aux0, wave, lane, par);
-      if (wave == 0 && lane < HALF) {
+      if (CTRL && lane < HALF) {
         L.small[SM_ROPE + 2 * lane] = cs.x;
         L.small[SM_ROPE + 2 * lane + 1] = cs.y;
         L.small[SM_QGAIN + lane] = gq0;
@@ -1294,9 +1307,6 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       }
       break;
     }
-    case KIND_COMBINE:
-      ab = gather_plain(a, L.part, in + (int64_t)t.row0 * a.S * PS, a.S * PS, wave, lane, par);
-      break;
     default:
       break;
   }
@@ -1315,10 +1325,9 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     rs = 1.0f / sqrtf(tot / (float)a.H + a.eps);
   } else if (t.kind == KIND_ATTN) {
     attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
-  } else if (t.kind == KIND_O && a.combine_in_o) {
-    merge_heads<HD>(L.part, a.n_heads, a.S, wave * 64 + lane, L.vec);
-  } else if (t.kind == KIND_COMBINE) {
-    merge_heads<HD>(L.part, 1, a.S, wave * 64 + lane, L.vec);
+  } else if ((t.kind == KIND_O && a.combine_in_o) || t.kind == KIND_COMBINE) {
+    // all heads' splits (o_proj prologue) or one head's (combine tile): one copy of the merge
+    merge_heads<HD>(L.part, t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane, L.vec);
   }
   return rs;
 }
@@ -1351,7 +1360,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* wds = reinterpret_cast<const uint64_t*>(L.small + SM_WDONE) + (k & 1) * 8;
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
-      if (gather_inputs<HD, G>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1555,7 +1564,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
