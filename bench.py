@@ -69,6 +69,38 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
                       f"({el:.1f} s timed; warm-up incl. BF16->FP32 widening {prep:.1f} s), NumPy FP32"}
 
 
+def _read_ceiling(n_workers: int, stream) -> dict:
+    """Measured stream-read ceiling of this GPU, same run: the library's stream-read kernel (the decode
+    kernel's 16-byte non-temporal load form) over 2 GiB, one and two 512-thread workgroups per CU;
+    the better median of 5 timed launches (HIP events on the launch stream)."""
+    import numpy as np
+    import torch
+
+    from tile_scheduled_persistent_amd import tiles
+
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best, how = 0.0, ""
+    for per_cu in (1, 2):
+        groups = n_workers * per_cu
+        for _ in range(2):
+            tiles.stream_read(buf, groups, sink, stream)
+        ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            tiles.stream_read(buf, groups, sink, stream)
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        gbs = buf.numel() / (float(np.median(ms)) * 1e-3) / 1e9
+        if gbs > best:
+            best, how = gbs, (f"tiles_stream_read over 2 GiB, {groups} workgroups x 512 threads, 16-byte "
+                              f"non-temporal loads, median of 5 launches")
+    del buf
+    return {"gbs": best, "how": how}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +177,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     avg_ms = float(np.mean(launch_ms))
+    ceiling = _read_ceiling(info.n_workers, stream)
 
     bpt = wl.bytes_per_token()
     tok_s = args.steps * n_tok / wall
@@ -176,6 +209,8 @@ def main():
                  "workers": info.n_workers, "block_threads": info.block_threads},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "read_ceiling": {"gbs": round(ceiling["gbs"], 1), "frac": round(achieved / ceiling["gbs"], 4),
+                         "how": ceiling["how"]},
     }
 
     if args.trace_report:

@@ -197,6 +197,19 @@ int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t
  * decode must fail its checksum (TILES_E_PLAN).  Does not touch the device. */
 int tiles_plan_debug_corrupt(tiles_plan_t *plan);
 
+/* Measurement helper, not part of the decode path: the stream-read ceiling against which the
+ * decode kernel's HBM rate is compared ("History and roadmap" page, "Where it stands": decode
+ * speed is stated as a fraction of what memory bandwidth allows).  Reads `bytes` of device
+ * memory at `buf` with the decode kernel's load form -- 16-byte non-temporal loads, one 1 KB
+ * chunk per wavefront instruction, 8 chunks in flight per wavefront -- in `n_groups`
+ * workgroups of 512 threads, each wavefront one contiguous share, and XORs every word read
+ * into the device word *sink (so the loads cannot be dropped; the caller zeroes it first if
+ * it wants the checksum).  Asynchronous on `stream` (hipStream_t, NULL = null stream); the
+ * caller times it.  buf and sink are caller-owned device memory.  Errors: TILES_E_ARG for a
+ * null pointer, n_groups outside [1, 65536], or bytes not a positive multiple of
+ * n_groups * 8 * 8192 (or above 4 GB per wavefront); TILES_E_HIP for a launch error. */
+int tiles_stream_read(const void *buf, int64_t bytes, int32_t n_groups, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -239,3 +239,23 @@ def test_llama_full_size_repeatable_and_chunk_invariant():
             assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
             t = int(t1[0])
     assert torch.equal(kv.k, a[3].k) and torch.equal(kv.v, a[3].v)
+
+
+# ---------------------------------------------------------------------------
+# the stream-read ceiling kernel (measurement helper): it reads every byte it is given
+# ---------------------------------------------------------------------------
+
+def test_stream_read_reads_every_word():
+    g = torch.Generator().manual_seed(5)
+    n_groups = 4
+    unit = n_groups * 8 * 8 * 1024
+    host = torch.randint(-2**31, 2**31 - 1, (3 * unit // 4,), dtype=torch.int64, generator=g).to(torch.int32)
+    expect = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    buf = host.cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tiles.stream_read(buf, n_groups, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == expect
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.stream_read(buf[: unit // 4 - 4], n_groups, sink)  # not a multiple of the per-launch unit
+    assert e.value.code == tiles.TILES_E_ARG

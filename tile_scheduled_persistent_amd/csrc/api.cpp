@@ -27,6 +27,7 @@ const void* worker_kernel(int head_dim, int group);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
+hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, int n_groups, uint32_t* sink, hipStream_t stream);
 }
 
 using namespace tiles;
@@ -470,6 +471,18 @@ int tiles_plan_debug_corrupt(tiles_plan_t* p) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   if (p->hp.tiles.empty()) return set_err(TILES_E_PLAN, "empty plan");
   p->hp.tiles[p->hp.tiles.size() / 2].woff ^= 0x400;
+  return TILES_OK;
+}
+
+int tiles_stream_read(const void* buf, int64_t bytes, int32_t n_groups, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return set_err(TILES_E_ARG, "null buffer or sink");
+  if (n_groups < 1 || n_groups > 65536) return set_err(TILES_E_ARG, "n_groups out of range [1, 65536]");
+  const int64_t unit = (int64_t)n_groups * NWAVES * STREAM_DEPTH * CHUNK_BYTES;
+  if (bytes <= 0 || bytes % unit != 0)
+    return set_err(TILES_E_ARG, "bytes must be a positive multiple of n_groups * 8 wavefronts * 8 KB");
+  if (bytes / ((int64_t)n_groups * NWAVES) > (int64_t)0xffffffffll)
+    return set_err(TILES_E_ARG, "more than 4 GB per wavefront");
+  HIP_TRY(launch_stream_read(static_cast<const uint8_t*>(buf), bytes, n_groups, sink, static_cast<hipStream_t>(stream)));
   return TILES_OK;
 }
 

@@ -1650,6 +1650,36 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
 }
 
 // ---------------------------------------------------------------------------
+// stream-read ceiling: what HBM delivers to streams of the decode kernel's load form (16-byte
+// non-temporal loads, one 1 KB chunk per wavefront instruction), each wavefront reading one
+// contiguous share with STREAM_DEPTH chunks in flight; an XOR of everything read goes to `sink`
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(BLOCK_THREADS) stream_read(const uint8_t* __restrict__ p, int64_t chunks_per_wave,
+                                                            uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t r = rsrc(p + w * chunks_per_wave * CHUNK_BYTES);
+  uint32_t x = 0;
+  for (int64_t i = 0; i < chunks_per_wave; i += STREAM_DEPTH) {
+    u32x4 v[STREAM_DEPTH];
+#pragma unroll
+    for (int u = 0; u < STREAM_DEPTH; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)lane * 16u, (uint32_t)(i + u) * CHUNK_BYTES, NT);
+#pragma unroll
+    for (int u = 0; u < STREAM_DEPTH; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+  if (lane == 0) atomicXor(sink, x);
+}
+
+hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, int n_groups, uint32_t* sink, hipStream_t stream) {
+  const int64_t per_wave = bytes / CHUNK_BYTES / ((int64_t)n_groups * NWAVES);
+  hipLaunchKernelGGL(stream_read, dim3(n_groups), dim3(BLOCK_THREADS), 0, stream, p, per_wave, sink);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launch helpers: buffer fill (before every decode launch) and weight packing (plan creation)
 // ---------------------------------------------------------------------------
 

@@ -118,6 +118,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_int32)]
         L.tiles_plan_debug_corrupt.restype = ctypes.c_int
         L.tiles_plan_debug_corrupt.argtypes = [ctypes.c_void_p]
+        L.tiles_stream_read.restype = ctypes.c_int
+        L.tiles_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -152,6 +155,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr()
+
+
+def stream_read(buf: torch.Tensor, n_groups: int, sink: torch.Tensor, stream=None) -> None:
+    """Launch the stream-read ceiling kernel over the bytes of a device tensor (tiles_stream_read):
+    XORs every word into sink (an int32/uint32 device tensor of one element).  Asynchronous."""
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib().tiles_stream_read(ctypes.c_void_p(_ptr(buf)), buf.numel() * buf.element_size(), n_groups,
+                                   ctypes.c_void_p(_ptr(sink)), ctypes.c_void_p(s.cuda_stream)))
 
 
 @dataclass
