@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")
+    ap.add_argument("--o-placement", type=int, default=0,
+                    help="o_proj workers: 0 planner choice, 1 all, 2 those without an attention tile")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed launches, run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -138,7 +140,7 @@ def main():
     token = synth.make_tokens(m, 1)[0]
     stream = torch.cuda.current_stream()
     plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
-                      attn_heads=args.attn_heads,
+                      attn_heads=args.attn_heads, o_placement=args.o_placement,
                       stream=stream)
     info = plan.info()
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
@@ -205,7 +207,7 @@ def main():
         "plan": {"waves_per_token": info.waves_per_step, "kv_splits": info.kv_splits,
                  "sync": "tagged data (parity bit), no grid barrier",
                  "combine": "o_proj prologue" if info.combine_mode == 1 else "own wave",
-                 "attn_heads_per_tile": info.attn_heads,
+                 "attn_heads_per_tile": info.attn_heads, "o_proj_workers": info.o_workers,
                  "workers": info.n_workers, "block_threads": info.block_threads},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
@@ -235,7 +237,7 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     from tile_scheduled_persistent_amd import tiles
 
     plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits, attn_heads=args.attn_heads,
-                      combine_mode=args.combine_mode)
+                      combine_mode=args.combine_mode, o_placement=args.o_placement)
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
     plan.decode(kv, token, wl.n_steps, out_t, None)

@@ -76,6 +76,9 @@ typedef struct tiles_config {
   int32_t attn_heads;     /* query heads per attention tile (divides n_heads / n_kv_heads); 0 planner choice */
   int32_t n_workers;      /* 0 = one workgroup per compute unit (required on the GPU) */
   void *stream;           /* hipStream_t used by create (copies) and by every decode; NULL = null stream */
+  int32_t o_placement;    /* workers of the o_proj tiles: 0 planner choice (all), 1 all workers, 2 those
+                             without an attention tile, when there are any and the splits merge in the
+                             o_proj prologue */
 } tiles_config_t;
 
 /* Per-layer weights, BF16, row-major [out, in]:
@@ -117,11 +120,11 @@ typedef struct tiles_plan_info {
   int32_t occupancy;          /* workgroups per CU the kernel can hold (0 in a dry run) */
   int64_t packed_bytes;       /* device bytes of the packed weights */
   int64_t weight_bytes_per_step; /* weight bytes one token streams (algorithmic) */
-  double max_over_mean;       /* worst per-wave worker byte imbalance (max / mean over busy waves) */
+  double max_over_mean;       /* worst per-wave worker byte imbalance (max / mean over the busy workers of a GEMV wave) */
   uint64_t checksum;          /* schedule checksum (re-checked at every decode) */
   uint64_t build_id;          /* worker-kernel build id the plan was made for */
   int32_t attn_heads;         /* query heads per attention tile */
-  int32_t reserved;
+  int32_t o_workers;          /* workers holding o_proj tiles (all, or those without an attention tile) */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */

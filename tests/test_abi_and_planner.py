@@ -50,8 +50,9 @@ def test_dry_run_every_workload(key):
     assert info.n_workers == 256 and info.block_threads == 512
     assert 84 * 1024 <= info.lds_bytes <= 160 * 1024
     assert info.weight_bytes_per_step == m.weight_bytes_per_token()
-    # balanced to within one row of a perfect split
-    assert info.max_over_mean < 1.05
+    # balanced over each GEMV wave's busy workers (the planner's validator enforces "within one row
+    # of a perfect split" itself; o_proj tiles may hold ~6 rows each, so one row is up to ~17 %)
+    assert info.max_over_mean < 1.2
     assert info.kv_splits >= 1 and info.kv_splits * m.n_kv_heads <= 256
 
 
@@ -127,3 +128,18 @@ def test_small_worker_counts_plan():
     for W in [16, 37, 100]:
         info = tiles.dry_run(QWEN3_06B, 200, n_workers=W)
         assert info.n_workers == W
+
+
+def test_o_proj_placement():
+    # planner choice and 1: all workers; 2: exactly the workers without an attention tile
+    wl = WORKLOADS["llama1b"]
+    for op in (0, 1):
+        assert tiles.dry_run(wl.model, wl.capacity, o_placement=op).o_workers == 256
+    info = tiles.dry_run(wl.model, wl.capacity, o_placement=2)
+    n_attn = wl.model.n_kv_heads * (wl.model.n_heads // wl.model.n_kv_heads // info.attn_heads) * info.kv_splits
+    assert info.o_workers == 256 - n_attn == 96
+    # a separate combine wave keeps o_proj on all workers
+    assert tiles.dry_run(wl.model, wl.capacity, o_placement=2, combine_mode=2).o_workers == 256
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(wl.model, wl.capacity, o_placement=3)
+    assert e.value.code == tiles.TILES_E_CONFIG

@@ -133,11 +133,16 @@ def test_ragged_shapes_group3_padding():
         _oracle_forced(s, toks, 12, plan, tag="ragged")
 
 
-def test_wide_layers_staged_prefetch():
+@pytest.mark.parametrize("o_placement", [0, 2])
+def test_wide_layers_staged_prefetch(o_placement):
+    # o_placement 2: o_proj tiles only on the workers without an attention tile (they stage their
+    # o_proj share in the attention wave, the attention workers stage gate/up in the o_proj wave)
     s = Setup(WIDE, 96, 70)
     toks = synth.make_tokens(WIDE, 1)
-    with s.plan() as plan:
-        _oracle_forced(s, toks, 6, plan, tag="wide")
+    with s.plan(o_placement=o_placement) as plan:
+        info = plan.info()
+        assert o_placement == 0 or 0 < info.o_workers < info.n_workers
+        _oracle_forced(s, toks, 6, plan, tag=f"wide o_placement={o_placement}")
 
 
 @pytest.mark.parametrize("heads", [0, 2, 4])

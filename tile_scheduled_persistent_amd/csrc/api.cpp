@@ -395,6 +395,11 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->kv_splits = hp.S;
   info->combine_mode = hp.combine_in_o ? 1 : 2;
   info->attn_heads = hp.T;
+  for (size_t wv = 0; wv < hp.waves.size(); ++wv)
+    if (hp.waves[wv].kind == KIND_O) {
+      info->o_workers = hp.wave_busy[wv];
+      break;
+    }
   info->occupancy = occupancy;
   info->packed_bytes = hp.packed_bytes;
   info->weight_bytes_per_step = hp.weight_bytes_per_step;

@@ -1554,10 +1554,14 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       // GEMV tile's, so that the staging lands during a wait that is already there (its own
       // inputs) instead of lengthening the next tile's.  Not issued with the tail prefetch: a
       // wavefront's outstanding loads are bounded, and the issue would stall the tile's end.
-      if (is_gemv(t.kind) && st.sk != k) {
-        const int own = r_first.i < r_first.ihi ? (r_first.ihi - r_first.i + B - 1) / B : 0;
+      // The next tile's batches are staged only in the wave right before it, by a GEMV tile that
+      // fits the registers or by a worker without a tile in this wave (no input gather there: the
+      // staging lands while the worker waits for the next tile's inputs).  The area holds one
+      // tile's batches at a time (st.sk = -1 once they are consumed).
+      if ((is_gemv(t.kind) || t.kind == KIND_NONE) && st.sk < 0) {
+        const int own = is_gemv(t.kind) && r_first.i < r_first.ihi ? (r_first.ihi - r_first.i + B - 1) / B : 0;
         const Range& sr = own > NB ? r_first : ng;
-        if (own > NB || (ng.k >= 0 && ng.k != k && ng.r0 == 0)) {
+        if (own > NB || (ng.k == k + 1 && ng.r0 == 0)) {
           // own staging lands during this tile's input wait and delays its end: one batch, which
           // arrives within that wait; the next tile's staging may take the whole area
           st.ls = stage_range<B, NB>(a.packed, sr, own > NB ? 1 : a.stage_batches, lane, stage_lds);

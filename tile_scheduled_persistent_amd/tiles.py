@@ -50,6 +50,7 @@ class Config(ctypes.Structure):
         ("qk_norm", ctypes.c_int32), ("tie_embeddings", ctypes.c_int32), ("max_positions", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("kv_splits", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
         ("attn_heads", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
+        ("o_placement", ctypes.c_int32),
     ]
 
 
@@ -75,7 +76,7 @@ class PlanInfo(ctypes.Structure):
         ("combine_mode", ctypes.c_int32), ("occupancy", ctypes.c_int32), ("packed_bytes", ctypes.c_int64),
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("o_workers", ctypes.c_int32),
     ]
 
 
@@ -135,10 +136,10 @@ def _check(rc: int):
 
 
 def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
-                n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0) -> Config:
+                n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0) -> Config:
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
                   float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
-                  int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream)
+                  int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement))
 
 
 def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
@@ -181,11 +182,12 @@ class Plan:
     """A tile plan for one model on the current device (owns a packed copy of the weights)."""
 
     def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
-                 combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0):
+                 combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0,
+                 o_placement: int = 0):
         self.model = m
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream,
-                                attn_heads)
+                                attn_heads, o_placement)
         on_device = weights["embed"].is_cuda
         layers = (LayerWeights * m.n_layers)()
         for i, d in enumerate(weights["layers"]):
