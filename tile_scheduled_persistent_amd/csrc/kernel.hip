@@ -1215,8 +1215,9 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 // ---------------------------------------------------------------------------
 // per-wave phases shared by all wavefronts.  The control wave (0) and the compute waves
 // (1..7) run separate loops (so that each keeps only its own values in registers) with the
-// same barrier sequence per wave: P (inputs staged), A (LDS prologue done), then for GEMV
-// tiles B per row block (and C between blocks), for attention tiles B and E.
+// same barrier sequence per wave: P (inputs staged), A (LDS prologue done; only for tiles whose
+// prologue writes LDS the compute waves read), then for GEMV tiles B per row block (and C
+// between blocks), for attention tiles B and E.
 // ---------------------------------------------------------------------------
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
@@ -1313,6 +1314,13 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
   return ab;
 }
 
+// Barrier A is needed only where the prologue writes LDS the compute waves read (attention prep,
+// split merges).  For the other tiles the prologue only forms the folded RMSNorm scale, which only
+// the control wave's epilogue uses: their compute waves start streaming right after barrier P.
+__device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileDesc& t) {
+  return t.kind == KIND_ATTN || t.kind == KIND_COMBINE || (t.kind == KIND_O && a.combine_in_o);
+}
+
 // LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale.
 template <int HD, int G>
 __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
@@ -1368,7 +1376,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       }
       if (a.trace) t_pro = wall_clock64();
       const float rs = lds_prologue<HD, G>(a, L, 0, lane, t, layer, pos);
-      __syncthreads();  // A: inputs ready
+      if (needs_barrier_a(a, t)) __syncthreads();  // A: inputs ready
       const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
@@ -1575,8 +1583,10 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         stop = true;
         break;
       }
-      lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
-      __syncthreads();  // A
+      if (needs_barrier_a(a, t)) {
+        lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
+        __syncthreads();  // A
+      }
       stamp(ts, TS_AFTER_A, lane);
       if (is_gemv(t.kind)) {
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
