@@ -40,7 +40,8 @@ constexpr int MAX_GROUP = 4;  // query heads per KV head the kernel supports
 constexpr int MAX_BLOCK_ROWS = 640;
 constexpr int32_t LDS_LIMIT = 160 * 1024;  // LDS of one CU (gfx950)
 // Register streaming of the compute wavefronts: two batches of STREAM_BATCH 16-byte loads per
-// lane in flight (STREAM_DEPTH), for weight chunks and K/V rows alike.
+// lane in flight (STREAM_DEPTH; the kernel's ring has two register sets), for weight chunks and
+// K/V rows alike.
 constexpr int STREAM_BATCH = 4;
 constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 // Up to this many further batches of a compute wavefront's next GEMV range are staged in its LDS
