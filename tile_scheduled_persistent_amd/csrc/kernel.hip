@@ -1347,7 +1347,11 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
 
 template <int HD, int G>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
-  volatile int* smi = reinterpret_cast<volatile int*>(L.small);
+  // The abort word lives in LDS and is written and read only on either side of a barrier (which
+  // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
+  // through this generic pointer would be a FLAT access, whose wait also drains every outstanding
+  // global load and store of the wavefront (its prefetch, its last publish).
+  int* smi = reinterpret_cast<int*>(L.small);
   int tok = a.token0;
   const int H = a.H;
   bool stop = false;
@@ -1507,7 +1511,11 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
   constexpr int NB = stream_sets<HD, G>();
   constexpr int NP = NB * B / 2;  // (K, V) pairs of the attention ring
   const int c = wave - 1;
-  volatile int* smi = reinterpret_cast<volatile int*>(L.small);
+  // The abort word lives in LDS and is written and read only on either side of a barrier (which
+  // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
+  // through this generic pointer would be a FLAT access, whose wait also drains every outstanding
+  // global load and store of the wavefront (its prefetch, its last publish).
+  int* smi = reinterpret_cast<int*>(L.small);
   Stream<B, NB> st;
   {
     const Range r = next_gemv(L.segs, a.n_waves, -1, block_rows, c);
