@@ -200,6 +200,15 @@ int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t
  * decode must fail its checksum (TILES_E_PLAN).  Does not touch the device. */
 int tiles_plan_debug_corrupt(tiles_plan_t *plan);
 
+/* Test hook: the watchdog of every wait in later decodes of this plan -- after `rounds`
+ * unanswered polling rounds a wait gives up, the launch ends early (every worker leaves after
+ * its next input barrier) and tiles_plan_status reports TILES_E_KERNEL.  0 restores the default
+ * (2^22 rounds, seconds).  A small value makes ordinary waits give up, which exercises that path
+ * without any fault; under 32 rounds the plan launches a test instantiation of the worker that
+ * checks its watchdog every round (one query head per attention tile only: TILES_E_CONFIG
+ * otherwise).  Host only (plus an occupancy query of that instantiation). */
+int tiles_plan_debug_spin_limit(tiles_plan_t *plan, uint32_t rounds);
+
 /* Measurement helper, not part of the decode path: the stream-read ceiling against which the
  * decode kernel's HBM rate is compared ("History and roadmap" page, "Where it stands": decode
  * speed is stated as a fraction of what memory bandwidth allows).  Reads `bytes` of device

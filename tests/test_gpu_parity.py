@@ -246,6 +246,28 @@ def test_llama_full_size_repeatable_and_chunk_invariant():
     assert torch.equal(kv.k, a[3].k) and torch.equal(kv.v, a[3].v)
 
 
+def test_watchdog_gives_up_and_the_plan_recovers():
+    # A one-round watchdog (set from the host) makes ordinary waits give up: the launch ends early
+    # with every worker leaving after its next input barrier, the status reports it, and once the
+    # default is back the same plan decodes bit-identically to a fresh plan.
+    s = Setup(WIDE, 96, 70)
+    tok = synth.make_tokens(WIDE, 1)[0]
+    n = 8
+    with s.plan() as plan:
+        plan.debug_spin_limit(1)
+        out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+        plan.decode(s.fresh_kv(), tok, n, out_t)
+        assert plan.status() == tiles.TILES_E_KERNEL
+        assert plan.status() == tiles.TILES_OK  # the fault word was cleared
+        plan.debug_spin_limit(0)
+        g_t, g_l, g_h = run_gpu(plan, s.fresh_kv(), tok, n)
+    with s.plan() as fresh:
+        r_t, r_l, r_h = run_gpu(fresh, s.fresh_kv(), tok, n)
+    assert np.array_equal(g_t, r_t)
+    assert np.array_equal(g_l.view(np.uint32), r_l.view(np.uint32))
+    assert np.array_equal(g_h.view(np.uint32), r_h.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # the stream-read ceiling kernel (measurement helper): it reads every byte it is given
 # ---------------------------------------------------------------------------

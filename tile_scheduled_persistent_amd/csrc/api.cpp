@@ -23,7 +23,7 @@
 #endif
 
 namespace tiles {
-const void* worker_kernel(int head_dim, int group);
+const void* worker_kernel(int head_dim, int group, bool short_watchdog);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
@@ -63,6 +63,8 @@ struct tiles_plan {
   uint64_t build_id = TILES_BUILD_ID;
   const void* kernel = nullptr;
   int occupancy = 0;
+  uint32_t spin_limit = DEFAULT_SPIN_LIMIT;  // polling rounds before a wait gives up (watchdog)
+  const void* kernel_wd = nullptr;            // test instantiation checking the watchdog every round
   hipStream_t stream = nullptr;
   // device memory
   uint8_t* packed = nullptr;
@@ -158,7 +160,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.T);
+  p->kernel = worker_kernel(hp.s.hd, hp.T, false);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -355,7 +357,7 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.combine_in_o = hp.combine_in_o;
   a.eps = p->cfg.rms_eps;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)hp.s.hd));
-  a.spin_limit = 1u << 22;
+  a.spin_limit = p->spin_limit;
   a.lds_vec_floats = hp.lds_vec_floats;
   a.lds_part_floats = hp.lds_part_floats;
   a.lds_xres_floats = hp.lds_xres_floats;
@@ -373,7 +375,10 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
     HIP_TRY(launch_fill_blocks(a.kv_v + first, nblk, stride, count, 0x7fc0, p->stream));
   }
   void* args[] = {&a};
-  HIP_TRY(hipLaunchCooperativeKernel(p->kernel, dim3(hp.W), dim3(BLOCK_THREADS), args, hp.lds_bytes, p->stream));
+  // (the worker checks its watchdog every 32 polling rounds; a short test watchdog runs the test
+  // instantiation, which checks every round)
+  const void* kern = p->spin_limit < 32 ? p->kernel_wd : p->kernel;
+  HIP_TRY(hipLaunchCooperativeKernel(kern, dim3(hp.W), dim3(BLOCK_THREADS), args, hp.lds_bytes, p->stream));
   kv->length += n_steps;
   p->last_steps = n_steps;
   return TILES_OK;
@@ -469,6 +474,22 @@ int tiles_read_debug(tiles_plan_t* p, float* hidden, uint64_t* trace, int32_t* n
     HIP_TRY(hipMemcpy(trace, p->trace, (size_t)p->last_steps * hp.waves.size() * hp.W * TRACE_WORDS * sizeof(uint64_t),
                       hipMemcpyDeviceToHost));
   }
+  return TILES_OK;
+}
+
+int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  const uint32_t limit = rounds ? rounds : DEFAULT_SPIN_LIMIT;
+  if (limit < 32 && !p->kernel_wd) {
+    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true);
+    if (!k) return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs one query head per attention tile");
+    HIP_TRY(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p->hp.lds_bytes));
+    int occ = 0;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, BLOCK_THREADS, p->hp.lds_bytes));
+    if (occ < 1) return set_err(TILES_E_DEVICE, "test worker kernel cannot be resident (occupancy < 1)");
+    p->kernel_wd = k;
+  }
+  p->spin_limit = limit;
   return TILES_OK;
 }
 

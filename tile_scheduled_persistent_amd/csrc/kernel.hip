@@ -239,9 +239,12 @@ __device__ __forceinline__ int chunk_lo(int n, int c) { return (int)((uint32_t)(
 // waiting: every poll loop is bounded (watchdog) and leaves when any worker has aborted
 // ---------------------------------------------------------------------------
 
+// WD: the test instantiation of the worker, whose waits check every round (a short watchdog set
+// from the host then makes ordinary waits give up); the worker proper checks every 32 rounds.
+template <bool WD>
 __device__ __forceinline__ bool watch_tick(const KernelArgs& a, uint32_t& spins, int lane) {
   ++spins;
-  if ((spins & 31) == 0) {
+  if ((spins & (WD ? 0u : 31u)) == 0) {
     if (ld_u32(a.sync + SYNC_ABORT_WORD) != 0) return true;
     if (spins > a.spin_limit) {
       if (lane == 0) {
@@ -259,7 +262,7 @@ __device__ __forceinline__ bool watch_tick(const KernelArgs& a, uint32_t& spins,
 // u = (i * nslots + slot) * 64 + lane.  prep(i, u) runs once per owned unit before polling
 // (to issue independent loads early), sink(i, u, x) once the unit shows parity `par`.
 // Only units not yet seen are re-read.  Returns true when the wait was abandoned.
-template <int GB, typename Map, typename Prep, typename Sink>
+template <int GB, bool WD, typename Map, typename Prep, typename Sink>
 __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src, int nunits, int slot, int nslots, uint32_t par,
                        int lane, Map map, Prep prep, Sink sink) {
   const __amdgpu_buffer_rsrc_t r = rsrc(src);
@@ -291,7 +294,7 @@ __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src,
         }
       }
       if (__all(pending == 0)) break;
-      if (watch_tick(a, spins, lane)) return true;
+      if (watch_tick<WD>(a, spins, lane)) return true;
       // a long wait polls less often: less polling traffic on the fabric for the other workers
       if (spins > 4) __builtin_amdgcn_s_sleep(8);
     }
@@ -312,11 +315,12 @@ struct NoPrep {
 };
 
 // x (n floats, tagged) -> xres = x, vec = x * gain, and this wavefront's sum of squares of its share
+template <bool WD>
 __device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, const uint32_t* src, int n, const uint16_t* gain,
                             int slot, int lane, uint32_t par, float& ss) {
   uint2 gv[GATHER_UNITS];
   float s = 0.f;
-  const bool ab = gather<GATHER_UNITS>(
+  const bool ab = gather<GATHER_UNITS, WD>(
       a, src, n / 4, slot, NWAVES, par, lane, Identity{},
       [&](int i, int u) { gv[i] = *reinterpret_cast<const uint2*>(gain + u * 4); },
       [&](int i, int u, const f32x4 x) {
@@ -330,9 +334,10 @@ __device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, c
 }
 
 // plain tagged vector -> dst
+template <bool WD>
 __device__ __forceinline__ bool gather_plain(const KernelArgs& a, float* dst, const uint32_t* src, int n, int slot, int lane,
                              uint32_t par) {
-  return gather<GATHER_UNITS_PLAIN>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
+  return gather<GATHER_UNITS_PLAIN, WD>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
                               [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(dst + u * 4) = x; });
 }
 
@@ -370,6 +375,7 @@ __device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds&
 
 // Next token: reduce the W LM-head partials (value, index | parity << 31) of the step with
 // parity `par`, greater value first, lower index on ties.  Returns true when abandoned.
+template <bool WD>
 __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint32_t par, int& tok) {
   constexpr int B = 4;  // up to 4 x 128 workers
   const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
@@ -407,7 +413,7 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
       }
     }
     if (__all(pending == 0)) break;
-    if (watch_tick(a, spins, lane)) return true;
+    if (watch_tick<WD>(a, spins, lane)) return true;
   }
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(best, off);
@@ -792,14 +798,14 @@ __device__ __forceinline__ float* attn_merged(const Lds& L) { return L.part + G 
 
 // all wavefronts: raw q (the tile's G query heads, from head qa), k, v of KV head g into vec from
 // the QKV wave's output
-template <int HD, int G>
+template <int HD, int G, bool WD>
 __device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, const uint32_t* src, int g, int qa, int slot,
                                            int lane, uint32_t par) {
   constexpr int NQ = G * HD / 4, NK = HD / 4;
   const int q0 = qa * HD / 4;
   const int k0 = (a.n_heads * HD + g * HD) / 4;
   const int v0 = (a.n_heads * HD + a.n_kv * HD + g * HD) / 4;
-  return gather<2>(
+  return gather<2, WD>(
       a, src, NQ + 2 * NK, slot, NWAVES, par, lane,
       [&](int u) { return u < NQ ? q0 + u : u < NQ + NK ? k0 + (u - NQ) : v0 + (u - NQ - NK); }, NoPrep{},
       [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(L.vec + u * 4) = x; });
@@ -1222,7 +1228,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G, bool CTRL>
+template <int HD, int G, bool CTRL, bool WD>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
@@ -1245,13 +1251,13 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       if (gk == KIND_QKV && layer == 0) {
         if (CTRL) {
           if (step > 0) {
-            ab = gather_token(a, lane, step_parity(step - 1), tok);
+            ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
             if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
           }
           if (!ab) ss = stage_embedding(a, L, tok, gain, lane);
         }
       } else {
-        ab = gather_norm(a, L, in, a.H, gain, wave, lane, par, ss);
+        ab = gather_norm<WD>(a, L, in, a.H, gain, wave, lane, par, ss);
       }
       for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
       if (lane == 0) L.small[SM_SS + wave] = ss;
@@ -1275,7 +1281,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         n = a.S * PS;
         nz = t.kpad;  // no GEMV input to pad
       }
-      ab = gather_plain(a, dst, src, n, wave, lane, par);
+      ab = gather_plain<WD>(a, dst, src, n, wave, lane, par);
       for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
       break;
     }
@@ -1297,7 +1303,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           gk1 = bf16_to_f32(gkk[lane + HALF]);
         }
       }
-      ab = gather_qkv<HD, G>(a, L, in, t.row0, t.aux0, wave, lane, par);
+      ab = gather_qkv<HD, G, WD>(a, L, in, t.row0, t.aux0, wave, lane, par);
       if (CTRL && lane < HALF) {
         L.small[SM_ROPE + 2 * lane] = cs.x;
         L.small[SM_ROPE + 2 * lane + 1] = cs.y;
@@ -1345,7 +1351,7 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
 // control wave loop
 // ---------------------------------------------------------------------------
 
-template <int HD, int G>
+template <int HD, int G, bool WD>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1372,7 +1378,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* wds = reinterpret_cast<const uint64_t*>(L.small + SM_WDONE) + (k & 1) * 8;
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
-      if (gather_inputs<HD, G, true>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true, WD>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1486,7 +1492,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
   // the last step's token
   if (!stop && bid == 0) {
     int last = 0;
-    if (!gather_token(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
+    if (!gather_token<WD>(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
   }
 }
 
@@ -1504,7 +1510,7 @@ constexpr int stream_sets() {
   return 2;
 }
 
-template <int HD, int G>
+template <int HD, int G, bool WD>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
@@ -1584,7 +1590,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G, false>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false, WD>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
@@ -1637,7 +1643,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int HD, int G>
+template <int HD, int G, bool WD>
 __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
@@ -1667,8 +1673,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   if (tid == 0) reinterpret_cast<int*>(L.small)[SM_ABORT] = 0;
   __syncthreads();
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G>(a, L, bid, wave, lane, block_rows);
+  if (wave == 0) control_loop<HD, G, WD>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G, WD>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -1758,20 +1764,28 @@ hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t 
 // host-visible handles of the instantiations
 // ---------------------------------------------------------------------------
 
-const void* worker_kernel(int head_dim, int group) {
+// The worker for a head size and query heads per attention tile; `short_watchdog` selects the test
+// instantiation whose waits check their watchdog every polling round (one query head per tile only).
+const void* worker_kernel(int head_dim, int group, bool short_watchdog) {
+  if (short_watchdog) {
+    if (group != 1) return nullptr;
+    if (head_dim == 64) return reinterpret_cast<const void*>(&tiles_worker<64, 1, true>);
+    if (head_dim == 128) return reinterpret_cast<const void*>(&tiles_worker<128, 1, true>);
+    return nullptr;
+  }
   if (head_dim == 64) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false>);
     }
   } else if (head_dim == 128) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false>);
     }
   }
   return nullptr;

@@ -47,6 +47,7 @@ constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 // Up to this many further batches of a compute wavefront's next GEMV range are staged in its LDS
 // area by direct-to-LDS loads issued with the register prefetch (as many as the LDS holds).
 constexpr int MAX_STAGE_BATCHES = 2;
+constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;  // polling rounds before a wait gives up (watchdog)
 constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit
 
 struct TileDesc {   // 32 bytes

@@ -119,6 +119,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_int32)]
         L.tiles_plan_debug_corrupt.restype = ctypes.c_int
         L.tiles_plan_debug_corrupt.argtypes = [ctypes.c_void_p]
+        L.tiles_plan_debug_spin_limit.restype = ctypes.c_int
+        L.tiles_plan_debug_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
         L.tiles_stream_read.restype = ctypes.c_int
         L.tiles_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
@@ -280,3 +282,7 @@ class Plan:
 
     def debug_corrupt(self):
         _check(lib().tiles_plan_debug_corrupt(self._h))
+
+    def debug_spin_limit(self, rounds: int):
+        """Watchdog of every wait in later decodes (0 restores the default)."""
+        _check(lib().tiles_plan_debug_spin_limit(self._h, int(rounds)))
