@@ -38,6 +38,13 @@ def test_null_arguments_are_rejected_without_a_gpu():
     assert L.tiles_plan_create(None, None) is None
     L.tiles_plan_destroy(None)  # NULL-safe
     assert L.tiles_plan_status(None) == tiles.TILES_E_ARG
+    assert L.tiles_plan_debug_spin_limit(None, 1) == tiles.TILES_E_ARG
+    assert L.tiles_plan_debug_corrupt(None) == tiles.TILES_E_ARG
+    # the stream-read helper checks its arguments before touching the device
+    assert L.tiles_stream_read(None, 1 << 20, 1, None, None) == tiles.TILES_E_ARG
+    assert L.tiles_stream_read(1, 1 << 20, 0, 1, None) == tiles.TILES_E_ARG      # no workgroups
+    assert L.tiles_stream_read(1, 1000, 1, 1, None) == tiles.TILES_E_ARG         # not whole 8 KB per wavefront
+    assert "multiple" in tiles.last_error()
 
 
 @pytest.mark.parametrize("key", list(WORKLOADS))
