@@ -69,6 +69,37 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
                       f"({el:.1f} s timed; warm-up incl. BF16->FP32 widening {prep:.1f} s), NumPy FP32"}
 
 
+def _edge_floor(stream) -> dict:
+    """Latency floor of one dependency edge on this GPU, same run: the library's ping-pong
+    (tiles_edge_latency, the decode kernel's publish and poll forms) between workgroup 0 and a peer
+    on the same XCD (8, 16) or on another (1, 2, 5); median round trip over 3 runs of 2000 each."""
+    import numpy as np
+    import torch
+
+    from tile_scheduled_persistent_amd import tiles
+
+    words = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    iters = 2000
+    res = {}
+    for name, peers in (("same_xcd", (8, 16)), ("cross_xcd", (1, 2, 5))):
+        rt = []
+        for peer in peers:
+            for _ in range(3):
+                words.zero_()
+                out.zero_()
+                torch.cuda.synchronize()
+                tiles.edge_latency(words, peer, iters, out, stream=stream)
+                stream.synchronize()
+                ticks, gave_up_peer, gave_up_0 = (int(x) for x in out.cpu())
+                if gave_up_peer or gave_up_0:
+                    continue
+                rt.append(ticks * 0.01 / iters)  # 100 MHz wall clock
+        res["round_trip_us_" + name] = round(float(np.median(rt)), 3) if rt else None
+    res["how"] = "one lane each of workgroup 0 and a peer pass a counter through two words, agent-scope stores and device-coherent polls"
+    return res
+
+
 def _read_ceiling(n_workers: int, stream) -> dict:
     """Measured stream-read ceiling of this GPU, same run: the library's stream-read kernel (the decode
     kernel's 16-byte non-temporal load form) over 2 GiB, one and two 512-thread workgroups per CU;
@@ -180,6 +211,7 @@ def main():
         del src, dst
     avg_ms = float(np.mean(launch_ms))
     ceiling = _read_ceiling(info.n_workers, stream)
+    edge = _edge_floor(stream)
 
     bpt = wl.bytes_per_token()
     tok_s = args.steps * n_tok / wall
@@ -213,6 +245,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "read_ceiling": {"gbs": round(ceiling["gbs"], 1), "frac": round(achieved / ceiling["gbs"], 4),
                          "how": ceiling["how"]},
+        "edge_floor": edge,
     }
 
     if args.trace_report:

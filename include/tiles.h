@@ -222,6 +222,21 @@ int tiles_plan_debug_spin_limit(tiles_plan_t *plan, uint32_t rounds);
  * n_groups * 8 * 8192 (or above 4 GB per wavefront); TILES_E_HIP for a launch error. */
 int tiles_stream_read(const void *buf, int64_t bytes, int32_t n_groups, uint32_t *sink, void *stream);
 
+/* Measurement helper, not part of the decode path: the latency floor of one dependency edge
+ * (Tiles page, introduction: what the synchronisation between waves costs decides whether a
+ * static schedule pays).  Workgroups 0 and `peer` of a (peer + 1)-workgroup launch, one lane
+ * each, pass a counter 1, 2, ..., iters back and forth through words[0] and words[16] with the
+ * decode kernel's publish (agent-scope store) and poll (device-coherent load) forms.  Workgroups
+ * are dealt to the 8 XCDs in turn, so a peer that is a multiple of 8 shares workgroup 0's XCD.
+ * out[0] receives the wall-clock ticks (100 MHz) workgroup 0 spent on the whole exchange
+ * (iters round trips); out[1] / out[2] become nonzero if the peer / workgroup 0 gave up a wait
+ * after `spin_limit` polls (the exchange then ends early, no wait is unbounded).  words (at
+ * least 17 words, zeroed by the caller before every call) and out (3 words) are caller-owned
+ * device memory.  Asynchronous on `stream` (hipStream_t, NULL = null stream).  Errors:
+ * TILES_E_ARG for a null pointer, peer outside [1, 255], iters outside [1, 2^20] or a zero
+ * spin_limit; TILES_E_HIP for a launch error. */
+int tiles_edge_latency(uint32_t *words, int32_t peer, int32_t iters, uint32_t spin_limit, uint64_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,13 @@ def test_null_arguments_are_rejected_without_a_gpu():
     assert L.tiles_stream_read(1, 1 << 20, 0, 1, None) == tiles.TILES_E_ARG      # no workgroups
     assert L.tiles_stream_read(1, 1000, 1, 1, None) == tiles.TILES_E_ARG         # not whole 8 KB per wavefront
     assert "multiple" in tiles.last_error()
+    # the edge-latency helper too
+    assert L.tiles_edge_latency(None, 1, 10, 100, None, None) == tiles.TILES_E_ARG
+    assert L.tiles_edge_latency(1, 0, 10, 100, 1, None) == tiles.TILES_E_ARG       # peer is not workgroup 0
+    assert L.tiles_edge_latency(1, 256, 10, 100, 1, None) == tiles.TILES_E_ARG
+    assert L.tiles_edge_latency(1, 8, 0, 100, 1, None) == tiles.TILES_E_ARG        # no round trips
+    assert L.tiles_edge_latency(1, 8, 10, 0, 1, None) == tiles.TILES_E_ARG         # no polls allowed
+    assert "spin_limit" in tiles.last_error()
 
 
 @pytest.mark.parametrize("key", list(WORKLOADS))

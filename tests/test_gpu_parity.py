@@ -286,3 +286,34 @@ def test_stream_read_reads_every_word():
     with pytest.raises(tiles.TilesError) as e:
         tiles.stream_read(buf[: unit // 4 - 4], n_groups, sink)  # not a multiple of the per-launch unit
     assert e.value.code == tiles.TILES_E_ARG
+
+
+# ---------------------------------------------------------------------------
+# the edge-latency helper: every round trip completes, at a plausible cost, and a one-poll limit
+# ends the exchange early instead of waiting
+# ---------------------------------------------------------------------------
+
+def test_edge_latency_round_trips_complete():
+    words = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    for peer in (1, 8):
+        words.zero_()
+        out.zero_()
+        tiles.edge_latency(words, peer, 500, out)
+        torch.cuda.synchronize()
+        ticks, gave_up_peer, gave_up_0 = (int(x) for x in out.cpu())
+        assert gave_up_peer == 0 and gave_up_0 == 0
+        # both words hold the last count: every one of the 500 round trips happened
+        w = words.cpu()
+        assert int(w[0]) == 500 and int(w[16]) == 500
+        us = ticks * 0.01 / 500
+        assert 0.05 < us < 50.0, us
+    # a limit of one poll: the first wait that is not answered at once gives up; the launch ends
+    words.zero_()
+    out.zero_()
+    tiles.edge_latency(words, 8, 1000, out, spin_limit=1)
+    torch.cuda.synchronize()
+    assert int(out[1]) != 0 or int(out[2]) != 0
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.edge_latency(words[:8], 8, 10, out)
+    assert e.value.code == tiles.TILES_E_ARG

@@ -28,6 +28,8 @@ hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t 
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
 hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, int n_groups, uint32_t* sink, hipStream_t stream);
+hipError_t launch_edge_latency(uint32_t* words, int peer, int iters, uint32_t spin_limit, uint64_t* out,
+                               hipStream_t stream);
 }
 
 using namespace tiles;
@@ -509,6 +511,16 @@ int tiles_stream_read(const void* buf, int64_t bytes, int32_t n_groups, uint32_t
   if (bytes / ((int64_t)n_groups * NWAVES) > (int64_t)0xffffffffll)
     return set_err(TILES_E_ARG, "more than 4 GB per wavefront");
   HIP_TRY(launch_stream_read(static_cast<const uint8_t*>(buf), bytes, n_groups, sink, static_cast<hipStream_t>(stream)));
+  return TILES_OK;
+}
+
+int tiles_edge_latency(uint32_t* words, int32_t peer, int32_t iters, uint32_t spin_limit, uint64_t* out,
+                       void* stream) {
+  if (!words || !out) return set_err(TILES_E_ARG, "null words or out");
+  if (peer < 1 || peer > 255) return set_err(TILES_E_ARG, "peer out of range [1, 255]");
+  if (iters < 1 || iters > (1 << 20)) return set_err(TILES_E_ARG, "iters out of range [1, 2^20]");
+  if (spin_limit == 0) return set_err(TILES_E_ARG, "spin_limit must be positive");
+  HIP_TRY(launch_edge_latency(words, peer, iters, spin_limit, out, static_cast<hipStream_t>(stream)));
   return TILES_OK;
 }
 

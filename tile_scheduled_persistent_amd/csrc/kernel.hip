@@ -1708,6 +1708,54 @@ hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, int n_groups, uin
 }
 
 // ---------------------------------------------------------------------------
+// edge latency floor: workgroup 0 and workgroup `peer` (one lane each) pass a counter back and
+// forth through two words, with the decode kernel's publish (agent-scope store) and poll
+// (device-coherent load) forms.  Every wait is bounded by `spin_limit` polls; a wait that gives
+// up ends the exchange and sets out[1] (peer) or out[2] (workgroup 0).  The other workgroups of
+// the grid leave at once.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(64) edge_pingpong(uint32_t* words, int peer, int iters, uint32_t spin_limit,
+                                                    uint64_t* __restrict__ out) {
+  const int b = blockIdx.x;
+  if ((b != 0 && b != peer) || threadIdx.x != 0) return;
+  const __amdgpu_buffer_rsrc_t r = rsrc(words);
+  // workgroup 0 writes word 0 and polls word 16 (a separate 64-byte line); the peer the reverse
+  const uint32_t in_off = b == 0 ? 64u : 0u;
+  uint32_t* mine = b == 0 ? words : words + 16;
+  const uint64_t t0 = wall_clock64();
+  bool gave_up = false;
+  for (int i = 1; i <= iters && !gave_up; ++i) {
+    if (b == 0) st_u32(mine, (uint32_t)i);
+    uint32_t spins = 0;
+    for (;;) {
+      // the fence keeps every round's load: the compiler sees no writer of the word, and would
+      // otherwise read it once and fold the wait into a single test
+      COMPILER_FENCE();
+      if (__builtin_amdgcn_raw_buffer_load_b32(r, in_off, 0, SC1) == (uint32_t)i) break;
+      if (++spins >= spin_limit) {
+        gave_up = true;
+        break;
+      }
+    }
+    if (b != 0 && !gave_up) st_u32(mine, (uint32_t)i);
+  }
+  const uint64_t t1 = wall_clock64();
+  if (b == 0) {
+    out[0] = t1 - t0;
+    out[2] = gave_up;
+  } else {
+    out[1] = gave_up;
+  }
+}
+
+hipError_t launch_edge_latency(uint32_t* words, int peer, int iters, uint32_t spin_limit, uint64_t* out,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(edge_pingpong, dim3(peer + 1), dim3(64), 0, stream, words, peer, iters, spin_limit, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launch helpers: buffer fill (before every decode launch) and weight packing (plan creation)
 // ---------------------------------------------------------------------------
 

@@ -124,6 +124,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_stream_read.restype = ctypes.c_int
         L.tiles_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
+        L.tiles_edge_latency.restype = ctypes.c_int
+        L.tiles_edge_latency.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -166,6 +169,18 @@ def stream_read(buf: torch.Tensor, n_groups: int, sink: torch.Tensor, stream=Non
     s = stream if stream is not None else torch.cuda.current_stream()
     _check(lib().tiles_stream_read(ctypes.c_void_p(_ptr(buf)), buf.numel() * buf.element_size(), n_groups,
                                    ctypes.c_void_p(_ptr(sink)), ctypes.c_void_p(s.cuda_stream)))
+
+
+def edge_latency(words: torch.Tensor, peer: int, iters: int, out: torch.Tensor, spin_limit: int = 1 << 22,
+                 stream=None) -> None:
+    """Launch the edge-latency ping-pong (tiles_edge_latency): words is a zeroed int32 device tensor
+    of at least 17 elements, out an int64 device tensor of 3 (ticks, peer gave up, workgroup 0
+    gave up).  Asynchronous."""
+    if words.numel() * words.element_size() < 17 * 4 or out.numel() * out.element_size() < 3 * 8:
+        raise TilesError(TILES_E_ARG, "words needs 17 int32, out 3 int64")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib().tiles_edge_latency(ctypes.c_void_p(_ptr(words)), peer, iters, spin_limit, ctypes.c_void_p(_ptr(out)),
+                                    ctypes.c_void_p(s.cuda_stream)))
 
 
 @dataclass
