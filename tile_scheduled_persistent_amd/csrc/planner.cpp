@@ -44,7 +44,7 @@ int fail(std::string& err, int code, const std::string& msg) {
 // Split count: about `target` bytes of K+V per split tile at the largest attended
 // length, at least 1, at most as many tiles as workers.
 // Split partials of all heads up to this size are merged in the o_proj prologue (combine mode 0).
-constexpr int64_t COMBINE_IN_O_BYTES = 64 * 1024;
+constexpr int64_t COMBINE_IN_O_BYTES = 68 * 1024;
 
 int32_t choose_splits(const Shape& s, int32_t W) {
   // Preferably a split's K/V rows fit the compute wavefronts' register prefetch (STREAM_DEPTH
@@ -57,6 +57,11 @@ int32_t choose_splits(const Shape& s, int32_t W) {
   if (S * split_record_bytes > COMBINE_IN_O_BYTES) {
     const int64_t target = 96 * 1024;
     S = (kv_head_bytes + target / 2) / target;
+    // A merge wave of its own costs a dependency edge per layer: when at least two thirds of
+    // those splits still merge in the prologue, take that count instead (Qwen3-4B shape at 1K
+    // positions: 4 splits merged in o_proj measured faster than 6 with a merge wave).
+    const int64_t fit = COMBINE_IN_O_BYTES / split_record_bytes;
+    if (S * split_record_bytes > COMBINE_IN_O_BYTES && fit >= 1 && 3 * fit >= 2 * S) S = fit;
   }
   S = std::max<int64_t>(1, std::min<int64_t>(S, W / s.n_kv));
   return (int32_t)S;
