@@ -25,6 +25,7 @@ enum : int32_t {
 // columns of one row.  Every GEMV row is padded to a multiple of CHUNK_COLS.
 constexpr int CHUNK_COLS = 512;
 constexpr int CHUNK_BYTES = 1024;
+constexpr int XCDS = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2; workgroup i runs on XCD i % 8
 constexpr int BLOCK_THREADS = 512;
 constexpr int NWAVES = BLOCK_THREADS / 64;
 // Wavefront 0 of every workgroup is the control wave (epilogues and global stores);

@@ -243,15 +243,22 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
         if (b > a) p.copies.push_back({src[m], l, a - bounds[m], b - a, s.H, dst + (a - lo) * s.Hpad * 2, (int64_t)s.Hpad * 2});
       }
     });
-    // attention: one tile per (KV head, group of T query heads, split)
+    // attention: one tile per (KV head, group of T query heads, split).  The tiles that read the
+    // same K/V rows (one KV head and split, every query-head group) go to workers on one XCD:
+    // workgroups are dealt to the XCDs in turn, so workers with equal index mod XCDS share an L2,
+    // which then serves all but the first read of those rows (measured +0.2 to +0.6 %).
     int32_t attn_wv = -1;
     {
       int32_t wv = attn_wv = new_wave(KIND_ATTN, l);
       const int32_t nhs = s.G / p.T;
+      const int32_t units = s.n_kv * p.S;  // distinct K/V ranges
+      const bool xcd_groups = (int64_t)(units + XCDS - 1) / XCDS * XCDS * nhs <= W;
       for (int g = 0; g < s.n_kv; ++g)
         for (int hs = 0; hs < nhs; ++hs)
           for (int sp = 0; sp < p.S; ++sp) {
-            TileDesc& t = tile_at(wv, (g * nhs + hs) * p.S + sp);
+            const int32_t u = g * p.S + sp;
+            const int32_t w = xcd_groups ? (u / XCDS) * XCDS * nhs + hs * XCDS + u % XCDS : (g * nhs + hs) * p.S + sp;
+            TileDesc& t = tile_at(wv, w);
             t.kind = KIND_ATTN;
             t.row0 = g;
             t.nrows = sp;
