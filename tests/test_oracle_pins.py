@@ -456,3 +456,106 @@ def test_fp32_oracle_close_to_fp64_on_tiny_synthetic_model():
     rel = np.linalg.norm(r32["hidden"] - r64["hidden"], axis=-1) / np.linalg.norm(r64["hidden"], axis=-1)
     assert rel.max() < 1e-5
     assert np.abs(r32["logits"] - r64["logits"]).max() < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# Plumbing of the whole step: which weights and which gain each stage reads.
+# Every layer and every norm gets its own, non-unit gain, so that a stage
+# reading another stage's (or another layer's) tensors changes the result.
+# ---------------------------------------------------------------------------
+
+def test_step_layers_and_norm_gains_closed_form():
+    """Two layers with distinct weights and distinct, non-unit gains.  Layer 0 passes x through
+    (W_o = W_down = 0); layer 1 has attention off and an MLP W_gate = 2I, W_up = I, W_down = I.
+    Then hidden[0] = x0, hidden[1] = x0 + silu(2h) * h with h = x0 / rms(x0) * g_mlp[1], and
+    logits = E (x1 / rms(x1) * g_final).
+    Catches: a layer reading another layer's weights or gains, the MLP norm taking the attention
+    gain, the final-norm gain dropped."""
+    c = Cfg(n_layers=2, hidden=4, ffn=4, n_heads=1, n_kv_heads=1, head_dim=4, vocab=8)
+    rng = np.random.default_rng(16)
+    w = _zero_model(c, rng)
+    ga = [np.array([1.25, 0.75, 1.5, 0.5]), np.array([0.625, 1.75, 1.125, 0.875])]
+    gm = [np.array([0.5, 1.5, 0.75, 1.25]), np.array([1.375, 0.625, 0.25, 2.0])]
+    gf = np.array([0.75, 1.25, 2.0, 0.5])
+    for l in range(2):
+        w["layers"][l]["attn_norm"] = _b(ga[l])
+        w["layers"][l]["mlp_norm"] = _b(gm[l])
+    # layer 0's MLP is live up to W_down = 0, so reading its gate/up instead of layer 1's is not enough
+    w["layers"][0]["w_gate"] = _b(np.eye(4) * -3.0)
+    w["layers"][0]["w_up"] = _b(np.eye(4) * 0.5)
+    w["layers"][1]["w_gate"] = _b(np.eye(4) * 2.0)
+    w["layers"][1]["w_up"] = _b(np.eye(4))
+    w["layers"][1]["w_down"] = _b(np.eye(4))
+    w["final_norm"] = _b(gf)
+    x0 = np.array([0.5, -1.25, 0.75, 2.0])
+    w["embed"][3] = _b(x0)
+    logits, hidden = OracleModel(c, w, np.float64).step(_kv(c, 2), 3, 0)
+    assert np.array_equal(hidden[0], x0)
+    h = x0 / math.sqrt(np.mean(x0 * x0) + c.rms_eps) * gm[1]
+    x1 = x0 + (2.0 * h / (1.0 + np.exp(-2.0 * h))) * h
+    assert np.allclose(hidden[1], x1, rtol=1e-13, atol=0)
+    E = bf16_bits_to_float(w["embed"], np.float64)
+    hf = x1 / math.sqrt(np.mean(x1 * x1) + c.rms_eps) * gf
+    assert np.allclose(logits, E @ hf, rtol=1e-12, atol=1e-15)
+
+
+def test_step_qk_norm_before_rope_with_own_gains():
+    """Per-head q/k RMSNorm with distinct non-unit gains, then RoPE, on head_dim 2 (one frequency,
+    angle = position).  W_q, W_k pick the first normed input coordinate, so q_raw = [a, 0] and
+    k_raw = [b, 0]; normed: [g_q0 a / sqrt(a^2/2 + eps), 0] and [g_k0 b / sqrt(b^2/2 + eps), 0];
+    rotated by p.  The cached key is that vector rounded to BF16; the attention output over
+    (cached position 0, current position 1) is w0 V0 + w1 v1 with softmax weights of q.K / sqrt(2).
+    Catches: q/k norm after RoPE, the k norm taking the q gain (or the reverse)."""
+    c = Cfg(n_layers=1, hidden=2, ffn=2, n_heads=1, n_kv_heads=1, head_dim=2, vocab=4, qk_norm=True,
+            rms_eps=1e-6)
+    rng = np.random.default_rng(17)
+    w = _zero_model(c, rng)
+    ga = np.array([1.5, 0.5])
+    gq = np.array([0.25, 3.0])
+    gk = np.array([2.0, 0.5])
+    L0 = w["layers"][0]
+    L0["attn_norm"] = _b(ga)
+    L0["mlp_norm"] = _b([0.875, 1.625])
+    L0["q_norm"] = _b(gq)
+    L0["k_norm"] = _b(gk)
+    L0["wq"] = _b([[1.0, 0.0], [0.0, 0.0]])
+    L0["wk"] = _b([[0.75, 0.0], [0.0, 0.0]])
+    L0["wv"] = _b([[0.0, 0.0], [0.0, 1.0]])
+    L0["wo"] = _b(np.eye(2))
+    w["embed"][1] = _b([1.0, 1.0])
+    kv = _kv(c, 4)
+    kv["k"][0, 0, 0] = _b([1.0, 2.0])
+    kv["v"][0, 0, 0] = _b([1.0, 0.0])
+    p, eps = 1, c.rms_eps
+    _, hidden = OracleModel(c, w, np.float64).step(kv, 1, p)
+    h = np.array([1.0, 1.0]) / math.sqrt(1.0 + eps) * ga
+    a, b = h[0], 0.75 * h[0]
+    qa = gq[0] * a / math.sqrt(a * a / 2 + eps)
+    ka = gk[0] * b / math.sqrt(b * b / 2 + eps)
+    q = np.array([qa * math.cos(p), qa * math.sin(p)])
+    k_now = np.array([ka * math.cos(p), ka * math.sin(p)])
+    cached = bf16_bits_to_float(kv["k"][0, 0, p], np.float64)
+    assert np.allclose(cached, k_now, rtol=2.0 ** -8, atol=0)           # rounded to BF16 (half an ulp)
+    s0 = q @ np.array([1.0, 2.0]) / math.sqrt(2.0)
+    s1 = q @ cached / math.sqrt(2.0)
+    w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+    v1 = bf16_bits_to_float(kv["v"][0, 0, p], np.float64)
+    assert np.allclose(v1, [0.0, h[1]], rtol=2.0 ** -8, atol=0)
+    want = np.array([1.0, 1.0]) + (1.0 - w1) * np.array([1.0, 0.0]) + w1 * v1
+    assert np.allclose(hidden[0], want, rtol=1e-12, atol=0)
+
+
+def test_decode_argmax_ties_take_the_lowest_index():
+    """Two identical embedding rows (tied head) give exactly equal logits; with them dominant the
+    greedy token is the lower of the two indices, whatever the input.  Catches an argmax that
+    keeps the last maximum."""
+    c = Cfg(vocab=16)
+    rng = np.random.default_rng(18)
+    w = _zero_model(c, rng)
+    row = np.full(c.hidden, 2.0)
+    w["embed"][5] = _b(row)
+    w["embed"][11] = _b(row)
+    w["embed"][2] = _b(np.full(c.hidden, 0.5))
+    res = OracleModel(c, w, np.float64).decode(_kv(c, 4), 2, 0, 3)
+    assert res["logits"][0][5] == res["logits"][0][11] == res["logits"][0].max()
+    assert list(res["tokens"]) == [5, 5, 5]
