@@ -14,10 +14,10 @@
  * Sources: "Tiles: Scheduling LLM Decoding as a Graph of Tiles" (intro: tiles
  * as the unit of scheduled work, a fixed worker per tile, byte balancing,
  * waves separated by grid barriers, validation before launch, bit-identical
- * runs; "What the code contains": TilePlan probes occupancy, builds and
- * validates the tile graph and packs the weights; TileInfer re-validates the
- * plan, checks it against the worker binary and GPU, runs up to 64 tokens per
- * cooperative launch with greedy selection in the kernel).  The fused
+ * runs; "What the code contains": an offline plan builder that sizes the grid
+ * from the kernel's occupancy, validates the graph and packs the weights, and
+ * a runtime that checks the plan before using it and runs many tokens per
+ * cooperative launch with greedy selection on the GPU).  The fused
  * operations follow "History and roadmap" (TileInfer.jl), "M8 so far" table:
  * q/k norm + RoPE + KV write, residual add + RMSNorm, SwiGLU in the GEMV;
  * split-KV decode attention follows its "Milestones" table, M5.
@@ -98,7 +98,10 @@ typedef struct tiles_weights {
 } tiles_weights_t;
 
 /* KV cache, caller-owned device memory, BF16 [n_layers][n_kv_heads][capacity][head_dim].
- * Keys are stored after q/k norm and RoPE. */
+ * Keys are stored after q/k norm and RoPE.  A decode reads positions [0, length + i) at step i
+ * (position length + i itself from the values it has just computed) and writes position
+ * length + i; the contents of every other row -- the unused tail, NaN included -- never affect
+ * any result. */
 typedef struct tiles_kv {
   void *k;
   void *v;
@@ -175,11 +178,24 @@ int tiles_plan_wave(const tiles_plan_t *plan, int32_t wave, tiles_wave_info_t *o
  * touching any GPU (no device memory, no kernel).  Fills *info (occupancy = 0). */
 int tiles_plan_dry_run(const tiles_config_t *cfg, int32_t n_workers, tiles_plan_info_t *info);
 
+/* Test hook (host only, no GPU): build the schedule for `n_workers` workers as tiles_plan_dry_run does,
+ * plant mistake number `mutation` in it (0 none; 1 rows covered twice, 2 a row covered by nobody,
+ * 3 an attention tile duplicated, 4 one missing, 5 a split index out of range, 6 two waves' tagged
+ * buffers overlapping, 7 one out of bounds, 8 a worker streaming two rows more than the balance
+ * allows, 9 waves out of dependency order, 10 a step not ending with the LM head, 11 two tiles
+ * reading the same packed bytes, 12 two tiles' packed rows exchanged, 13 a packing copy dropped,
+ * 14 a norm gain misplaced, 15 more staging than the LDS layout holds) and run the plan validator
+ * on the result.  Returns what the validator returns (TILES_E_PLAN with its message for every planted
+ * mistake), or TILES_E_ARG for an unknown mutation or one the plan has no site for. */
+int tiles_plan_debug_validate(const tiles_config_t *cfg, int32_t n_workers, int32_t mutation);
+
 /* Change the stream used by subsequent decodes (hipStream_t, NULL = null stream). */
 int tiles_plan_set_stream(tiles_plan_t *plan, void *stream);
 
-/* Synchronize the plan's stream and report a device-side fault of the last launch:
- * TILES_OK or TILES_E_KERNEL (and clears the fault word). */
+/* Synchronize the plan's stream and report a device-side fault of the last launch, and clear it:
+ * TILES_OK, TILES_E_KERNEL (a wait's watchdog expired) or TILES_E_PLAN (a worker found that the
+ * schedule it loaded from device memory, or the build id stored with it, differs from what the plan
+ * recorded at creation; that launch did nothing). */
 int tiles_plan_status(tiles_plan_t *plan);
 
 /* Copy debug buffers to host memory after synchronizing the plan's stream.
@@ -199,6 +215,12 @@ int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t
 /* Test hook: corrupt one byte of the host copy of the schedule so that the next
  * decode must fail its checksum (TILES_E_PLAN).  Does not touch the device. */
 int tiles_plan_debug_corrupt(tiles_plan_t *plan);
+
+/* Test hook: flip one bit of the device-resident copy of the schedule (a tile's weight offset) and
+ * leave the host copy alone.  The next decode's launch detects it before the corrupted entry is used
+ * (the worker holding it re-hashes the schedule it loaded and leaves; the others leave at their next
+ * wait) and tiles_plan_status then reports TILES_E_PLAN.  The plan stays corrupted. */
+int tiles_plan_debug_corrupt_device(tiles_plan_t *plan);
 
 /* Test hook: the watchdog of every wait in later decodes of this plan -- after `rounds`
  * unanswered polling rounds a wait gives up, the launch ends early (every worker leaves after

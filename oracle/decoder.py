@@ -198,10 +198,14 @@ class OracleModel:
         return self._get(None, "lm_head")
 
     # one step ----------------------------------------------------------------
-    def step(self, kv: dict, token: int, pos: int):
+    def step(self, kv: dict, token: int, pos: int, kv_wide: Optional[dict] = None):
         """Run one decode step for ``token`` at position ``pos``.
 
         Returns (logits [V], hidden [n_layers, H]); writes K/V at ``pos``.
+        ``kv_wide`` (optional) holds the cache already widened to this model's dtype
+        (``k``/``v`` arrays shaped like the bit arrays, see :meth:`widen_kv`): attention then
+        reads the widened rows instead of widening them again, and the row written at
+        ``pos`` is written to both.  The values are the same either way.
         """
         c = self.cfg
         dt = self.dtype
@@ -230,11 +234,18 @@ class OracleModel:
             k = apply_rope(k, cos, sin)
             kv["k"][l, :, pos, :] = float_to_bf16_bits(k)        # R5
             kv["v"][l, :, pos, :] = float_to_bf16_bits(v)
+            if kv_wide is not None:
+                kv_wide["k"][l, :, pos, :] = bf16_bits_to_float(kv["k"][l, :, pos, :], dt)
+                kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)
             attn = np.empty((nq, hd), dtype=dt)
             for hh in range(nq):
                 g = hh // group                                    # R3
-                Kc = bf16_bits_to_float(kv["k"][l, g, : pos + 1], dt)
-                Vc = bf16_bits_to_float(kv["v"][l, g, : pos + 1], dt)
+                if kv_wide is not None:
+                    Kc = kv_wide["k"][l, g, : pos + 1]
+                    Vc = kv_wide["v"][l, g, : pos + 1]
+                else:
+                    Kc = bf16_bits_to_float(kv["k"][l, g, : pos + 1], dt)
+                    Vc = bf16_bits_to_float(kv["v"][l, g, : pos + 1], dt)
                 attn[hh] = attend(q[hh], Kc, Vc)
             x = x + self._get(l, "wo") @ attn.reshape(-1)
             h = rmsnorm(x, self._get(l, "mlp_norm"), eps)
@@ -248,24 +259,33 @@ class OracleModel:
         return logits, hidden
 
     # drivers -----------------------------------------------------------------
+    def widen_kv(self, kv: dict) -> dict:
+        """The whole cache widened (exactly) to this model's dtype, for :meth:`step`'s
+        ``kv_wide``: long caches are then widened once instead of at every step."""
+        return {"k": bf16_bits_to_float(kv["k"], self.dtype).copy(),
+                "v": bf16_bits_to_float(kv["v"], self.dtype).copy()}
+
     def decode(self, kv: dict, token: int, pos0: int, n_steps: int,
-               teacher: Optional[Sequence[int]] = None, keep_hidden: bool = True):
+               teacher: Optional[Sequence[int]] = None, keep_hidden: bool = True,
+               widen_kv_once: bool = False):
         """Greedy decode ``n_steps`` steps starting with ``token`` at ``pos0``.
 
         Step i consumes ``token`` (i = 0), else the previous step's argmax
         (free-running) or ``teacher[i - 1]`` (teacher-forced).  Returns a dict
         with ``tokens`` [n] (argmax of each step, R8), ``logits`` [n, V] and
-        ``hidden`` [n, n_layers, H] (or None).
+        ``hidden`` [n, n_layers, H] (or None).  ``widen_kv_once`` widens the cache
+        once up front (see :meth:`widen_kv`); the results are the same.
         """
         toks = np.empty(n_steps, dtype=np.int64)
         logits_all = np.empty((n_steps, self.cfg.vocab), dtype=self.dtype)
         hidden_all = (np.empty((n_steps, self.cfg.n_layers, self.cfg.hidden), dtype=self.dtype)
                       if keep_hidden else None)
         t = int(token)
+        kv_wide = self.widen_kv(kv) if widen_kv_once else None
         for i in range(n_steps):
             if i > 0:
                 t = int(teacher[i - 1]) if teacher is not None else int(toks[i - 1])
-            logits, hidden = self.step(kv, t, pos0 + i)
+            logits, hidden = self.step(kv, t, pos0 + i, kv_wide)
             toks[i] = int(np.argmax(logits))                       # R8: first max
             logits_all[i] = logits
             if keep_hidden:

@@ -89,6 +89,43 @@ def check_step(tag: str, g_logits, g_hidden, o_logits, o_hidden, g_tok: int, o_t
     return margin
 
 
+def compare_teacher_forced(tag, g_tokens, g_logits, g_hidden, o_res):
+    """Compare every step of a GPU launch with an oracle teacher-forced on the GPU's own inputs
+    (step i of both consumed the same token).  Asserts the bars at every step and returns the
+    observed errors: max per-layer hidden relative L2, max logit abs error, the number of steps
+    whose token was checked (oracle top-2 margin > MARGIN) and the smallest oracle margin."""
+    n = len(g_tokens)
+    assert o_res["logits"].shape[0] == n
+    worst_h, worst_l, checked, min_margin = 0.0, 0.0, 0, float("inf")
+    for i in range(n):
+        margin = check_step(f"{tag} step {i}", g_logits[i], None if g_hidden is None else g_hidden[i],
+                            o_res["logits"][i], o_res["hidden"][i], int(g_tokens[i]), int(o_res["tokens"][i]))
+        if g_hidden is not None:
+            num = np.linalg.norm((g_hidden[i] - o_res["hidden"][i]).astype(np.float64), axis=-1)
+            den = np.linalg.norm(o_res["hidden"][i].astype(np.float64), axis=-1)
+            worst_h = max(worst_h, float((num / den).max()))
+        worst_l = max(worst_l, float(np.abs(g_logits[i].astype(np.float64) - o_res["logits"][i]).max()))
+        checked += margin > MARGIN
+        min_margin = min(min_margin, margin)
+    return {"steps": n, "hidden_rel_l2_max": worst_h, "logit_abs_max": worst_l, "tokens_checked": checked,
+            "min_margin": min_margin}
+
+
+def kv_rows_close(tag, g_cache, o_bits, pos: int, n: int):
+    """The K or V rows a launch wrote (positions pos .. pos + n - 1) against the oracle's: the same
+    relative-L2 bar per (layer, head, position) row as the hidden states (entries near cancellation
+    may differ by a few BF16 ulps), and at most 1 % of the entries differing at all."""
+    gb = synth.bits(g_cache)[:, :, pos:pos + n]
+    ob = o_bits[:, :, pos:pos + n]
+    gf = (gb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    of = (ob.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rel = np.linalg.norm(gf - of, axis=-1) / np.linalg.norm(of, axis=-1)
+    assert rel.max() <= HIDDEN_REL_L2, f"{tag}: cached rows rel L2 {rel.max():.3e}"
+    frac = float(np.mean(gb != ob))
+    assert frac < 1e-2, f"{tag}: {frac:.3%} of cached entries differ"
+    return float(rel.max()), frac
+
+
 def compare_free_running(tag, g_tokens, g_logits, g_hidden, o_res, n_check: int):
     """Compare a free-running GPU launch with a free-running oracle for the first
     n_check steps while both consumed the same input token.  Returns the number

@@ -157,3 +157,43 @@ def test_o_proj_placement():
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(wl.model, wl.capacity, o_placement=3)
     assert e.value.code == tiles.TILES_E_CONFIG
+
+
+# ---------------------------------------------------------------------------
+# the plan validator rejects each planted mistake with the rule it breaks
+# ---------------------------------------------------------------------------
+
+VALIDATOR_MUTATIONS = [
+    (1, "GEMV rows not covered exactly once"),
+    (2, "GEMV rows not covered exactly once"),
+    (3, "attention/combine tile"),
+    (4, "attention/combine tiles do not cover every head"),
+    (5, "attention tile out of range"),
+    (6, "tagged buffers overlap"),
+    (7, "tagged buffer misaligned or out of bounds"),
+    (8, "worker bytes unbalanced"),
+    (9, "waves out of dependency order"),
+    (10, "waves out of dependency order"),
+    (11, "packed tiles overlap"),
+    (12, "is not its source row"),
+    (13, "source rows not packed exactly once"),
+    (14, "norm gains misplaced"),
+    (15, "bad LDS staging area"),
+]
+
+
+def test_validator_accepts_the_unmutated_plans():
+    for m, pos in ((LLAMA_1B, 1087), (QWEN3_06B, 1087), (TINY, 64)):
+        assert tiles.debug_validate(m, pos, 0) == tiles.TILES_OK, tiles.last_error()
+
+
+@pytest.mark.parametrize("mutation,message", VALIDATOR_MUTATIONS, ids=[str(m) for m, _ in VALIDATOR_MUTATIONS])
+def test_validator_rejects_planted_mistake(mutation, message):
+    rc = tiles.debug_validate(LLAMA_1B, 1087, mutation)
+    assert rc == tiles.TILES_E_PLAN, (rc, tiles.last_error())
+    assert message in tiles.last_error()
+
+
+def test_validator_mutation_hook_arguments():
+    assert tiles.debug_validate(TINY, 64, 99) == tiles.TILES_E_ARG
+    assert tiles.lib().tiles_plan_debug_validate(None, 256, 0) == tiles.TILES_E_ARG

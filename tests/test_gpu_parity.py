@@ -9,7 +9,8 @@ import torch
 from tile_scheduled_persistent_amd import synth, tiles
 from tile_scheduled_persistent_amd.configs import TINY, WORKLOADS, scaled
 
-from parity_util import HIDDEN_REL_L2, Setup, check_step, compare_free_running, run_gpu, top2_margin
+from parity_util import (HIDDEN_REL_L2, Setup, check_step, compare_free_running, compare_teacher_forced,
+                         kv_rows_close, run_gpu, top2_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +127,60 @@ def test_poison_mode_changes_nothing():
     assert np.array_equal(a[0], b[0])
 
 
+def _bits_equal(a, b):
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    assert torch.equal(a[3].k.view(torch.int16), b[3].k.view(torch.int16))
+    assert torch.equal(a[3].v.view(torch.int16), b[3].v.view(torch.int16))
+
+
+def test_poison_with_the_cache_filled_to_capacity():
+    """length + n_steps == capacity: the NaN-poisoned rows include the last row of every head, the
+    one masked attention slots read; masked slots must discard it (regression: they used to weigh
+    it by 0, and 0 * NaN poisoned the sums)."""
+    s = Setup(TINY, 32, 20)
+    a = _full_run(s, 7, 12)
+    b = _full_run(s, 7, 12, flags=tiles.TILES_DEBUG_HIDDEN | tiles.TILES_POISON)
+    _bits_equal(a, b)
+
+
+def test_nan_in_the_unused_cache_tail_changes_nothing():
+    """A cache whose rows past the launch's last position hold NaN gives bit-identical results."""
+    s = Setup(TINY, 48, 20)
+    a = _full_run(s, 7, 12)
+    kv = s.fresh_kv()
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device="cuda")
+    kv.k[:, :, 20:] = nan
+    kv.v[:, :, 20:] = nan
+    with s.plan() as plan:
+        g_t, g_l, g_h = run_gpu(plan, kv, 7, 12)
+    b = (g_t, g_l, g_h, kv)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    assert torch.equal(a[3].k[:, :, :32].view(torch.int16), kv.k[:, :, :32].view(torch.int16))
+    assert torch.equal(a[3].v[:, :, :32].view(torch.int16), kv.v[:, :, :32].view(torch.int16))
+
+
+def test_argmax_tie_takes_the_lowest_index():
+    """Embedding rows 100 and 3000 made identical and dominant (tied head): their logits are equal
+    bit for bit, and the greedy token is the lower index, on the GPU (the rows sit in the LM-head
+    tiles of different workers, so the cross-worker reduction decides) as in the oracle."""
+    s = Setup(TINY, 16, 0)
+    row = torch.full((TINY.hidden,), 0.5, dtype=torch.bfloat16)
+    for r in (100, 3000):
+        s.w_dev["embed"][r] = row.cuda()
+        s.w_bits["embed"][r] = synth.bits(row)
+    with s.plan() as plan:
+        g_t, g_l, _ = run_gpu(plan, s.fresh_kv(), 100, 3)
+    o = s.oracle().decode(s.oracle_kv(), 100, 0, 3)
+    for i in range(3):
+        assert g_l[i][100] == g_l[i][3000] == g_l[i].max()
+        assert o["logits"][i][100] == o["logits"][i][3000] == o["logits"][i].max()
+    assert list(g_t) == [100, 100, 100] and list(o["tokens"]) == [100, 100, 100]
+
+
 def test_ragged_shapes_group3_padding():
     s = Setup(RAGGED, 64, 37)
     toks = synth.make_tokens(RAGGED, 1)
@@ -199,29 +254,66 @@ def test_error_paths():
         assert e.value.code == tiles.TILES_E_PLAN
 
 
+def test_corrupted_device_schedule_is_detected_in_the_launch():
+    """A bit flipped in the device copy of the schedule (the host copy and its checksum intact): the
+    worker that loads it finds its hash changed and leaves before using it, the others leave at their
+    next wait, and the status reports TILES_E_PLAN; out_tokens stays untouched."""
+    s = Setup(TINY, 24, 8)
+    with s.plan() as plan:
+        run_gpu(plan, s.fresh_kv(), 3, 2)  # the intact plan decodes
+        plan.debug_corrupt_device()
+        out = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+        plan.decode(s.fresh_kv(), 3, 4, out)
+        assert plan.status() == tiles.TILES_E_PLAN
+        assert "schedule" in tiles.last_error()
+        assert plan.status() == tiles.TILES_OK  # the status word was cleared
+        assert out.cpu().tolist() == [-7, -7, -7, -7]
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads: the launch bench.py times (one launch of all steps)
 # ---------------------------------------------------------------------------
 
-FULL = [("llama1b", 3), ("qwen06b", 3), ("qwen4b", 2), ("qwen4b_32k", 2)]
+FULL = ["llama1b", "qwen06b", "qwen4b", "qwen4b_32k"]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("key,n_check", FULL)
-def test_full_size_workload(key, n_check):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", FULL)
+def test_full_size_workload_every_step(key):
+    """The launch bench.py times, every step: the oracle is teacher-forced on the GPU's own tokens
+    (step i of both consumes the same input), so every step is compared, the last one included.
+    The timed configuration itself (no debug buffers, no logits) gives the same tokens and the same
+    cache bytes as the checked one."""
     wl = WORKLOADS[key]
     m = wl.model
+    n = wl.n_steps
     s = Setup(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda")
     tok = synth.make_tokens(m, 1)[0]
+    kv_timed = s.fresh_kv()
+    with s.plan(flags=0) as plan:
+        out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+        plan.decode(kv_timed, tok, n, out_t, None)
+        assert plan.status() == tiles.TILES_OK, tiles.last_error()
+        timed_tokens = out_t.cpu().numpy().astype(np.int64)
     kv = s.fresh_kv()
     with s.plan() as plan:
-        g_t, g_l, g_h = run_gpu(plan, kv, tok, wl.n_steps)
-    print(f"{key}: GPU launch of {wl.n_steps} steps done; oracle for {n_check} steps", flush=True)
-    o_res = s.oracle().decode(s.oracle_kv(), tok, wl.n_cached, n_check)
-    n = compare_free_running(key, g_t, g_l, g_h, o_res, n_check)
-    assert n >= 1
-    print(f"{key}: compared {n} steps; oracle margins "
-          f"{[round(top2_margin(o_res['logits'][i]), 3) for i in range(n)]}", flush=True)
+        g_t, g_l, g_h = run_gpu(plan, kv, tok, n)
+    assert np.array_equal(timed_tokens, g_t), "timed configuration gives other tokens"
+    assert torch.equal(kv_timed.k.view(torch.int16), kv.k.view(torch.int16))
+    assert torch.equal(kv_timed.v.view(torch.int16), kv.v.view(torch.int16))
+    del kv_timed
+    print(f"{key}: GPU launch of {n} steps done; teacher-forced oracle for all {n} steps", flush=True)
+    okv = s.oracle_kv()
+    o_res = s.oracle().decode(okv, tok, wl.n_cached, n, teacher=[int(t) for t in g_t[:-1]], widen_kv_once=True)
+    stats = compare_teacher_forced(key, g_t, g_l, g_h, o_res)
+    assert stats["steps"] == n
+    k_rel, k_frac = kv_rows_close(f"{key} K", kv.k, okv["k"], wl.n_cached, n)
+    v_rel, v_frac = kv_rows_close(f"{key} V", kv.v, okv["v"], wl.n_cached, n)
+    print(f"{key}: {n} of {n} steps compared; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
+          f"{stats['logit_abs_max']:.2e}, tokens checked at margin > 0.1: {stats['tokens_checked']} "
+          f"(smallest oracle margin {stats['min_margin']:.3f}); cached K/V rows rel L2 {k_rel:.2e} / {v_rel:.2e}, "
+          f"entries differing {k_frac:.3%} / {v_frac:.3%}", flush=True)
 
 
 @pytest.mark.slow

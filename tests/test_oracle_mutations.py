@@ -57,6 +57,8 @@ MUTATIONS = [
     ("q norm takes the k gain", 'rmsnorm(q, self._get(l, "q_norm"), eps)', 'rmsnorm(q, self._get(l, "k_norm"), eps)', False),
     ("MLP norm takes the attention gain", 'rmsnorm(x, self._get(l, "mlp_norm"), eps)',
      'rmsnorm(x, self._get(l, "attn_norm"), eps)', False),
+    ("widened cache row written unrounded", 'kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)',
+     'kv_wide["v"][l, :, pos, :] = v', False),
     ("argmax keeps the last maximum", "toks[i] = int(np.argmax(logits))",
      "toks[i] = int(len(logits) - 1 - np.argmax(logits[::-1]))", False),
 ]

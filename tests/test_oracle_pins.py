@@ -559,3 +559,21 @@ def test_decode_argmax_ties_take_the_lowest_index():
     res = OracleModel(c, w, np.float64).decode(_kv(c, 4), 2, 0, 3)
     assert res["logits"][0][5] == res["logits"][0][11] == res["logits"][0].max()
     assert list(res["tokens"]) == [5, 5, 5]
+
+
+def test_widened_cache_path_equals_the_plain_path():
+    """The optional FP32 shadow of the cache (widened once, updated on every write) gives
+    exactly the plain path's tokens, logits, hidden states and cache bits."""
+    from tile_scheduled_persistent_amd import synth
+    from tile_scheduled_persistent_amd.configs import TINY
+    w = synth.weights_as_bits(synth.make_weights(TINY))
+    k, v = synth.make_kv(TINY, 24, 10)
+    kva = {"k": synth.bits(k), "v": synth.bits(v)}
+    kvb = {"k": kva["k"].copy(), "v": kva["v"].copy()}
+    toks = synth.make_tokens(TINY, 6)
+    m = OracleModel(TINY, w, np.float32)
+    a = m.decode(kva, toks[0], 10, 6, teacher=toks[1:])
+    b = m.decode(kvb, toks[0], 10, 6, teacher=toks[1:], widen_kv_once=True)
+    for key in ("tokens", "logits", "hidden"):
+        assert np.array_equal(a[key], b[key])
+    assert np.array_equal(kva["k"], kvb["k"]) and np.array_equal(kva["v"], kvb["v"])

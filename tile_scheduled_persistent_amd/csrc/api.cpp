@@ -1,14 +1,17 @@
 // C-ABI runtime: plan creation (device probe, planning, validation, weight packing,
 // uploads), cooperative launches of the persistent worker, status and debug read-back.
 //
-// "Tiles: Scheduling LLM Decoding as a Graph of Tiles", "What the code contains": the
-// planner probes the compiled worker kernel for occupancy, builds and validates the tile
-// graph and its schedule and packs the weights; the runtime re-validates the plan, checks
-// that it was made for this worker binary and GPU, and runs up to 64 tokens per
-// cooperative launch with greedy selection inside the kernel.
+// Follows "Tiles: Scheduling LLM Decoding as a Graph of Tiles", "What the code contains"
+// (the split between an offline plan builder and a runtime that checks a plan before each
+// use and runs many tokens per cooperative launch).  Here the checks are: before every
+// launch the host re-hashes its copy of the schedule and compares device and CU count; in
+// every launch each worker re-hashes the schedule it actually loaded from device memory and
+// compares it, and the build id stored with the plan, against what the plan recorded and
+// against its own compiled-in build id.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -81,6 +84,7 @@ struct tiles_plan {
   int64_t fill_words = 0;      // ll .. lmpart end, refilled before every launch
   uint32_t* sync = nullptr;
   size_t sync_bytes = 0;
+  uint64_t* d_table_check = nullptr;  // [W] per-worker schedule hashes, then the build id
   float* dbg_hidden = nullptr;
   uint64_t* trace = nullptr;
   int last_steps = 0;
@@ -125,7 +129,8 @@ const void* src_ptr(const tiles_weights_t* w, int32_t tensor, int32_t layer) {
 void release(tiles_plan* p) {
   if (!p) return;
   if (p->stream || p->device >= 0) (void)hipStreamSynchronize(p->stream);
-  void* bufs[] = {p->packed, p->d_tiles, p->d_waves, p->d_small, p->d_rope, p->scratch, p->dbg_hidden, p->trace};
+  void* bufs[] = {p->packed, p->d_tiles, p->d_waves, p->d_small, p->d_rope, p->scratch, p->dbg_hidden, p->trace,
+                  p->d_table_check};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   delete p;
@@ -233,6 +238,12 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   TRY(hipMemcpyAsync(p->d_waves, hp.waves.data(), hp.waves.size() * sizeof(WaveDesc), hipMemcpyHostToDevice, p->stream));
   TRY(hipMalloc(&p->d_small, hp.small.size() * sizeof(LayerSmall)));
   TRY(hipMemcpyAsync(p->d_small, hp.small.data(), hp.small.size() * sizeof(LayerSmall), hipMemcpyHostToDevice, p->stream));
+  {
+    std::vector<uint64_t> chk = worker_table_hashes(hp);
+    chk.push_back(p->build_id);
+    TRY(hipMalloc(&p->d_table_check, chk.size() * sizeof(uint64_t)));
+    TRY(hipMemcpy(p->d_table_check, chk.data(), chk.size() * sizeof(uint64_t), hipMemcpyHostToDevice));
+  }
   // RoPE table: angles p * theta^(-2i/hd) in double, cos/sin rounded to float
   {
     const int half = hp.s.hd / 2;
@@ -288,7 +299,6 @@ int check_identity(const tiles_plan* p) {
   int dev = -1;
   HIP_TRY(hipGetDevice(&dev));
   if (dev != p->device) return set_err(TILES_E_DEVICE, "plan was created for another device");
-  if (p->build_id != (uint64_t)TILES_BUILD_ID) return set_err(TILES_E_DEVICE, "plan was made for another worker binary");
   if (p->hp.W != p->cu_count) return set_err(TILES_E_DEVICE, "plan worker count differs from the CU count");
   if (plan_checksum(p->hp) != p->hp.checksum) return set_err(TILES_E_PLAN, "plan checksum mismatch (schedule modified)");
   return TILES_OK;
@@ -332,6 +342,7 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.ll = p->ll;
   a.lmpart = p->lmpart;
   a.sync = p->sync;
+  a.table_check = p->d_table_check;
   a.kv_k = static_cast<uint16_t*>(kv->k);
   a.kv_v = static_cast<uint16_t*>(kv->v);
   a.kv_cap = kv->capacity;
@@ -443,6 +454,20 @@ int tiles_plan_dry_run(const tiles_config_t* cfg, int32_t n_workers, tiles_plan_
   return TILES_OK;
 }
 
+int tiles_plan_debug_validate(const tiles_config_t* cfg, int32_t n_workers, int32_t mutation) {
+  if (!cfg) return set_err(TILES_E_ARG, "null config");
+  HostPlan hp;
+  std::string err;
+  int rc = build_plan(*cfg, n_workers, hp, err);
+  if (rc != TILES_OK) return set_err(rc, err);
+  rc = debug_mutate_plan(hp, mutation, err);
+  if (rc != TILES_OK) return set_err(rc, err);
+  rc = validate_plan(hp, err);
+  if (rc != TILES_OK) return set_err(rc, err);
+  g_err.clear();
+  return TILES_OK;
+}
+
 int tiles_plan_set_stream(tiles_plan_t* p, void* stream) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   p->stream = static_cast<hipStream_t>(stream);
@@ -456,6 +481,8 @@ int tiles_plan_status(tiles_plan_t* p) {
   HIP_TRY(hipMemcpy(&status, p->sync + SYNC_STATUS_WORD, 4, hipMemcpyDeviceToHost));
   if (status != 0) {
     HIP_TRY(hipMemset(p->sync, 0, p->sync_bytes));
+    if (status == STATUS_TABLES)
+      return set_err(TILES_E_PLAN, "a worker's device-resident schedule or build id failed its check in the last launch");
     return set_err(TILES_E_KERNEL, "a wait's watchdog expired in the last launch");
   }
   return TILES_OK;
@@ -499,6 +526,20 @@ int tiles_plan_debug_corrupt(tiles_plan_t* p) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   if (p->hp.tiles.empty()) return set_err(TILES_E_PLAN, "empty plan");
   p->hp.tiles[p->hp.tiles.size() / 2].woff ^= 0x400;
+  return TILES_OK;
+}
+
+int tiles_plan_debug_corrupt_device(tiles_plan_t* p) {
+  if (!p) return set_err(TILES_E_ARG, "null plan");
+  if (p->hp.tiles.empty() || !p->d_tiles) return set_err(TILES_E_PLAN, "empty plan");
+  // one bit of the woff field of a tile in the middle of the table (device copy only)
+  const size_t idx = p->hp.tiles.size() / 2;
+  uint8_t* byte = reinterpret_cast<uint8_t*>(p->d_tiles + idx) + offsetof(TileDesc, woff) + 1;
+  uint8_t v = 0;
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  HIP_TRY(hipMemcpy(&v, byte, 1, hipMemcpyDeviceToHost));
+  v ^= 0x04;
+  HIP_TRY(hipMemcpy(byte, &v, 1, hipMemcpyHostToDevice));
   return TILES_OK;
 }
 

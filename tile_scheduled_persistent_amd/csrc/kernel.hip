@@ -12,11 +12,15 @@
 // producer wave's output buffer with device-coherent 16-byte loads until every element
 // they need shows the current parity.  One memory round trip thus both signals and moves
 // the data: there is no grid barrier, no flag and no wait for store completion on the
-// critical path.  Each wave has its own output buffer, written once per step; a worker can
-// only write step s+1 of a buffer after every worker has consumed step s of it (every
-// wave's inputs depend on all workers' outputs of the previous waves), so one parity bit
-// separates the generations.  The buffers are filled with a quiet NaN of parity 0 before
-// every launch; step 0 publishes parity 1.
+// critical path.  Each wave has its own output buffer, written exactly once per step.  The
+// generations are separated by one all-to-all per step: every worker ends a step with a
+// release store of its LM-head partial, and every worker begins the next step by reading all
+// W partials (the token gather) followed by an acquire.  So when any worker starts step s + 1,
+// every worker has finished step s (each of its reads and writes), and every store of step s
+// is visible to it: a producer never overwrites a value a consumer still needs, and a consumer
+// polling at step s + 1 sees each buffer's step-s value (the other parity) until the
+// step-(s+1) value arrives, never an older one of its own parity.  The buffers are filled with
+// a quiet NaN of parity 0 before every launch; step 0 publishes parity 1.
 //
 // Workgroup organisation (512 threads = 8 wavefronts):
 //   * all eight wavefronts share the input gather of every wave (each polls its share of
@@ -50,6 +54,10 @@
 
 #include "plan_types.h"
 
+#ifndef TILES_BUILD_ID
+#define TILES_BUILD_ID 0x0ull
+#endif
+
 namespace tiles {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -68,8 +76,11 @@ __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
 __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The per-step LM-head partial is a release: every store this wavefront made earlier in the step
+// (all of the worker's published values and its KV rows: the control wavefront makes every global
+// store) is visible before the partial is.
+__device__ __forceinline__ void st_u64_release(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Buffer descriptor over a scratch array (byte offsets < 4 GB).  Device-coherent buffer
 // loads through it are plain (non-atomic) loads the compiler can issue back to back.
@@ -425,6 +436,11 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
   }
   if (bidx < 0 || bidx >= a.V) bidx = 0;  // only reachable with non-finite logits
   tok = bidx;
+  // Acquire: having seen every worker's (released) partial of the step, this worker sees every
+  // store any worker made in that step.  This is what lets one parity bit separate generations:
+  // when a consumer polls a buffer at step s + 2, the buffer already shows step s + 1's value (the
+  // other parity) or a newer one, never step s's (nor, at step 1, the fill value).
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return false;
 }
 
@@ -903,7 +919,9 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
 // the range, or the current position, taken from LDS -- reads the cache's last row
 // (capacity - 1) instead, which is never read for real (a position is read only in later
 // steps, and none follows the last one); rows from earlier launches are covered by the cache
-// maintenance at kernel boundaries.  The consumer masks those slots.
+// maintenance at kernel boundaries.  The consumer discards what such a slot read (its weight
+// and V values are selected away, not multiplied by 0), so that row's contents never matter:
+// it may hold anything, NaN included.
 template <int HD>
 __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j, int whi,
                                         int cur, int dummy, int dseg, u32x4& kw, u32x4& vw) {
@@ -1064,8 +1082,13 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       m[h] = mn;
     }
   };
-  // weighted V of one position (p = 0 for a slot without one)
-  auto accumulate = [&](bool valid, const float* sc, const float* vf) {
+  // weighted V of one position.  A slot without a position contributes exactly nothing: its
+  // weight is 0 and its V values are replaced by 0 (selects, not a multiplication by 0, so that
+  // whatever the masked load read -- a NaN in an unwritten cache row included -- cannot reach
+  // the sums).
+  auto accumulate = [&](bool valid, const float* sc, float* vf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.0f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = valid ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
@@ -1468,7 +1491,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           }
         }
         if (lane == 0)
-          st_u64(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
+          st_u64_release(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
                  (uint64_t)__float_as_uint(lm_best) | ((uint64_t)((uint32_t)lm_idx | (par << 31)) << 32));
       }
       if (a.trace && lane == 0) {
@@ -1672,6 +1695,28 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   for (int l = tid; l < a.n_layers; l += BLOCK_THREADS) L.lsmall[l] = a.small[l];
   if (tid == 0) reinterpret_cast<int*>(L.small)[SM_ABORT] = 0;
   __syncthreads();
+  // The schedule as loaded (this worker's tiles, every wave descriptor, every layer's gain offsets:
+  // one run of 32-bit words in LDS) must hash to what the host computed when it built the plan, and
+  // the plan must carry this kernel's build id; otherwise every wavefront of this worker leaves before
+  // using any of it, and the abort word makes the other workers leave at their next wait.
+  if (wave == 0) {
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(L.tiles);
+    const int nwords = a.n_waves * (int)((sizeof(TileDesc) + sizeof(WaveDesc)) / 4) + a.n_layers * (int)(sizeof(LayerSmall) / 4);
+    uint64_t hs = 0;
+    for (int i = lane; i < nwords; i += 64) hs += table_mix(((uint64_t)i << 32) | words[i]);
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)hs, off), hi = __shfl_xor((uint32_t)(hs >> 32), off);
+      hs += ((uint64_t)hi << 32) | lo;
+    }
+    const bool bad = hs != a.table_check[bid] || a.table_check[a.W] != (uint64_t)TILES_BUILD_ID;
+    if (bad && lane == 0) {
+      st_u32(a.sync + SYNC_STATUS_WORD, STATUS_TABLES);
+      st_u32(a.sync + SYNC_ABORT_WORD, 1u);
+      reinterpret_cast<int*>(L.small)[SM_ABORT] = 1;
+    }
+  }
+  __syncthreads();
+  if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
   if (wave == 0) control_loop<HD, G, WD>(a, L, bid, lane, block_rows);
   else compute_loop<HD, G, WD>(a, L, bid, wave, lane, block_rows);

@@ -74,7 +74,9 @@ struct LayerSmall {
 };
 
 // Sync area layout (uint32 words, one 64-byte line each).
-constexpr int SYNC_STATUS_WORD = 0;      // fault word (0 = ok, 1 = a wait's watchdog expired)
+constexpr int SYNC_STATUS_WORD = 0;      // fault word: 0 ok, STATUS_WATCHDOG or STATUS_TABLES
+constexpr uint32_t STATUS_WATCHDOG = 1;  // a wait's watchdog expired
+constexpr uint32_t STATUS_TABLES = 2;    // a worker's device-resident schedule failed its check
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
 constexpr int SYNC_WORDS = 32;
 
@@ -84,6 +86,20 @@ constexpr int SYNC_WORDS = 32;
 //   5 own gather done (before P), 6 after barrier A, 4 own share of the tile done (before B)
 //   -- taken by the first compute wave (4 stays 0 when it had no share).
 constexpr int TRACE_WORDS = 12;
+
+// Hash of the schedule bytes worker `w` loads: its TileDesc of every wave, every WaveDesc and
+// every LayerSmall, as 32-bit words; word i of the sequence contributes mix(i << 32 | word) and the
+// contributions are summed modulo 2^64 (so that lanes may add them up in any grouping).  The host
+// computes it at plan creation; the kernel recomputes it from the copies it loaded before using them.
+// (constexpr: callable from host and device code alike)
+constexpr uint64_t table_mix(uint64_t x) {  // the splitmix64 finaliser
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ull;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebull;
+  x ^= x >> 31;
+  return x;
+}
 
 // Tagged-data buffers are filled with this word before every launch: a quiet NaN whose
 // parity bit (bit 0) is 0, so that step 0 (parity 1) never mistakes it for a value.
@@ -113,6 +129,7 @@ struct KernelArgs {
   uint32_t* ll;              // FP32 values, parity in bit 0; wave k's output at ll + waves[k].ll_off
   uint32_t* lmpart;          // [W][2] (max logit bits, index | parity << 31)
   uint32_t* sync;            // SYNC_WORDS status / abort words
+  const uint64_t* table_check;  // [W + 1]: per-worker hash of the schedule it loads, then the build id
   uint16_t* kv_k;            // BF16 cache
   uint16_t* kv_v;
   int64_t kv_cap;

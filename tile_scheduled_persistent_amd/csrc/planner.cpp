@@ -18,7 +18,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <sstream>
+#include <unordered_map>
 
 namespace tiles {
 
@@ -100,6 +102,26 @@ uint64_t plan_checksum(const HostPlan& p) {
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
   if (!p.small.empty()) mix(p.small.data(), p.small.size() * sizeof(LayerSmall));
   return h;
+}
+
+std::vector<uint64_t> worker_table_hashes(const HostPlan& p) {
+  std::vector<uint64_t> out(p.W, 0);
+  const size_t nw = p.waves.size();
+  std::vector<uint32_t> common((nw * sizeof(WaveDesc) + p.small.size() * sizeof(LayerSmall)) / 4);
+  if (nw) std::memcpy(common.data(), p.waves.data(), nw * sizeof(WaveDesc));
+  if (!p.small.empty()) std::memcpy(common.data() + nw * sizeof(WaveDesc) / 4, p.small.data(), p.small.size() * sizeof(LayerSmall));
+  constexpr size_t TW = sizeof(TileDesc) / 4;
+  for (int32_t w = 0; w < p.W; ++w) {
+    uint64_t h = 0, i = 0;
+    for (size_t k = 0; k < nw; ++k) {
+      uint32_t t[TW];
+      std::memcpy(t, &p.tiles[k * p.W + w], sizeof(TileDesc));
+      for (size_t j = 0; j < TW; ++j, ++i) h += table_mix((i << 32) | t[j]);
+    }
+    for (uint32_t x : common) h += table_mix((i++ << 32) | x);
+    out[w] = h;
+  }
+  return out;
 }
 
 int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::string& err) {
@@ -424,14 +446,55 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   return TILES_OK;
 }
 
+namespace {
+
+// Rows of the source tensor a packing copy reads, and their width (BF16 values).
+bool source_geometry(const Shape& s, int32_t tensor, int64_t& rows, int64_t& cols) {
+  const int64_t q = (int64_t)s.n_heads * s.hd, kv = (int64_t)s.n_kv * s.hd;
+  switch (tensor) {
+    case SRC_EMBED: case SRC_LM_HEAD: rows = s.V; cols = s.H; return true;
+    case SRC_FINAL_NORM: case SRC_ATTN_NORM: case SRC_MLP_NORM: rows = 1; cols = s.H; return true;
+    case SRC_Q_NORM: case SRC_K_NORM: rows = 1; cols = s.hd; return true;
+    case SRC_WQ: rows = q; cols = s.H; return true;
+    case SRC_WK: case SRC_WV: rows = kv; cols = s.H; return true;
+    case SRC_WO: rows = s.H; cols = q; return true;
+    case SRC_WGATE: case SRC_WUP: rows = s.F; cols = s.H; return true;
+    case SRC_WDOWN: rows = s.H; cols = s.F; return true;
+  }
+  return false;
+}
+
+// The source row packed at output row r of a GEMV tile kind (GU rows interleave gate and up).
+void expected_source(const Shape& s, int32_t kind, int32_t layer, bool tied, int64_t out_row, int64_t r,
+                     int32_t& tensor, int32_t& src_layer, int64_t& src_row) {
+  const int64_t q = (int64_t)s.n_heads * s.hd, kv = (int64_t)s.n_kv * s.hd;
+  src_layer = layer;
+  switch (kind) {
+    case KIND_QKV:
+      if (out_row < q) { tensor = SRC_WQ; src_row = out_row; }
+      else if (out_row < q + kv) { tensor = SRC_WK; src_row = out_row - q; }
+      else { tensor = SRC_WV; src_row = out_row - q - kv; }
+      return;
+    case KIND_O: tensor = SRC_WO; src_row = out_row; return;
+    case KIND_GU: tensor = (r & 1) ? SRC_WUP : SRC_WGATE; src_row = out_row; return;
+    case KIND_DOWN: tensor = SRC_WDOWN; src_row = out_row; return;
+    default: tensor = tied ? SRC_EMBED : SRC_LM_HEAD; src_layer = -1; src_row = out_row; return;
+  }
+}
+
+}  // namespace
+
 int validate_plan(const HostPlan& p, std::string& err) {
   const Shape& s = p.s;
   const int32_t W = p.W;
   const int nw = (int)p.waves.size();
   std::ostringstream os;
-  if ((size_t)nw * W != p.tiles.size()) return fail(err, TILES_E_PLAN, "tile table size mismatch");
+  if (W < 1 || (size_t)nw * W != p.tiles.size()) return fail(err, TILES_E_PLAN, "tile table size mismatch");
 
-  // wave order: per layer QKV, ATTN, [COMBINE], O, GU, DOWN; then LM
+  // wave order: per layer QKV, ATTN, [COMBINE], O, GU, DOWN; then LM.  A step therefore starts with
+  // layer 0's QKV wave, in which every worker gathers all LM-head partials of the previous step (the
+  // token), and ends with the LM-head wave, in which every worker publishes its partial: this
+  // all-to-all once per step is what lets one parity bit tell a buffer's generations apart.
   {
     std::vector<int32_t> want;
     for (int l = 0; l < s.n_layers; ++l) {
@@ -452,7 +515,26 @@ int validate_plan(const HostPlan& p, std::string& err) {
     }
   }
 
-  // per-wave coverage, packing bounds and hazards
+  // tagged buffers: every wave but the LM head owns a 4-word aligned buffer, disjoint from the others
+  {
+    std::vector<std::pair<int64_t, int64_t>> bufs;
+    for (int wv = 0; wv < nw; ++wv) {
+      const int64_t n = wave_out_words(s, p.S, p.waves[wv].kind);
+      const int32_t off = p.waves[wv].ll_off;
+      if (n == 0) {
+        if (off != -1) return fail(err, TILES_E_PLAN, "LM-head wave with a tagged buffer");
+        continue;
+      }
+      if (off < 0 || off % 4 != 0 || n % 4 != 0 || off + n > p.ll_words)
+        return fail(err, TILES_E_PLAN, "tagged buffer misaligned or out of bounds");
+      bufs.push_back({off, off + n});
+    }
+    std::sort(bufs.begin(), bufs.end());
+    for (size_t i = 1; i < bufs.size(); ++i)
+      if (bufs[i].first < bufs[i - 1].second) return fail(err, TILES_E_PLAN, "tagged buffers overlap");
+  }
+
+  // per wave: tile ranges and coverage, the read and write sets, dataflow and hazards
   std::vector<std::pair<int64_t, int64_t>> packed_ranges;
   for (int wv = 0; wv < nw; ++wv) {
     const int32_t kind = p.waves[wv].kind;
@@ -461,11 +543,30 @@ int validate_plan(const HostPlan& p, std::string& err) {
     int64_t covered = 0;
     std::vector<std::pair<int64_t, int64_t>> spans;  // GEMV tiles' (row0, nrows), in any worker order
     std::vector<int> seen;
+    const int32_t in_buf = wv > 0 ? BUF_WAVE + wv - 1 : BUF_EMBED;
+    const int32_t out_buf = BUF_WAVE + wv;
     for (int w = 0; w < W; ++w) {
       const TileDesc& t = p.tiles[(size_t)wv * W + w];
+      TileIO& x = io[w];
+      // What every worker does in this wave, tile or not (the kernel's gathers and the LM partial):
+      // layer 0's QKV wave reads all LM partials of the previous step (the token) and an embedding
+      // row; every other QKV wave and every gate/up wave reads the residual stream x from the wave
+      // before (the o_proj and down epilogues add their rows to it); in the LM wave every worker
+      // publishes its (max, index) partial.
+      if (kind == KIND_QKV) {
+        if (layer == 0) {
+          x.reads.push_back({BUF_LMPART, 0, W});
+          x.reads.push_back({BUF_EMBED, 0, s.H});
+        } else {
+          x.reads.push_back({in_buf, 0, s.H});
+        }
+      } else if (kind == KIND_GU) {
+        x.reads.push_back({in_buf, 0, s.H});
+      } else if (kind == KIND_LM) {
+        x.writes.push_back({BUF_LMPART, w, w + 1});
+      }
       if (t.kind == KIND_NONE) continue;
       if (t.kind != kind) return fail(err, TILES_E_PLAN, "tile kind differs from its wave");
-      TileIO& x = io[w];
       switch (kind) {
         case KIND_QKV: case KIND_O: case KIND_GU: case KIND_DOWN: case KIND_LM: {
           int64_t R = kind == KIND_QKV ? s.qkv_rows : kind == KIND_GU ? s.F : kind == KIND_LM ? s.V : s.H;
@@ -480,34 +581,27 @@ int validate_plan(const HostPlan& p, std::string& err) {
             return fail(err, TILES_E_PLAN, "packed weights out of bounds or misaligned");
           packed_ranges.push_back({t.woff, t.woff + bytes});
           const int64_t lo = t.row0, hi = t.row0 + t.nrows;
-          const int32_t in_buf = wv > 0 ? BUF_WAVE + wv - 1 : BUF_EMBED;
-          const int32_t out_buf = BUF_WAVE + wv;
-          if (kind == KIND_QKV) {
-            x.reads.push_back({layer == 0 ? BUF_EMBED : in_buf, 0, s.H});
-            x.writes.push_back({out_buf, lo, hi});
-          } else if (kind == KIND_O) {
+          if (kind == KIND_O) {
             x.reads.push_back({in_buf, 0, wave_out_words(s, p.S, p.waves[wv - 1].kind)});
-            x.writes.push_back({out_buf, lo, hi});
-          } else if (kind == KIND_GU) {
-            x.reads.push_back({in_buf, 0, s.H});
             x.writes.push_back({out_buf, lo, hi});
           } else if (kind == KIND_DOWN) {
             x.reads.push_back({in_buf, 0, s.F});
             x.writes.push_back({out_buf, lo, hi});
-          } else {
+          } else if (kind == KIND_LM) {
             x.reads.push_back({in_buf, 0, s.H});
-            x.writes.push_back({BUF_LMPART, w, w + 1});
             x.writes.push_back({BUF_LOGITS, lo, hi});
+          } else {
+            x.writes.push_back({out_buf, lo, hi});  // QKV, GU: inputs listed above
           }
           break;
         }
         case KIND_ATTN: {
-          const int32_t hs = (t.aux0 - t.row0 * s.G) / p.T;
-          if (t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S || t.aux0 < t.row0 * s.G ||
+          const int32_t hs = p.T > 0 ? (t.aux0 - t.row0 * s.G) / p.T : -1;
+          if (p.T < 1 || t.row0 < 0 || t.row0 >= s.n_kv || t.nrows < 0 || t.nrows >= p.S || t.aux0 < t.row0 * s.G ||
               (t.aux0 - t.row0 * s.G) % p.T != 0 || hs >= s.G / p.T)
             return fail(err, TILES_E_PLAN, "attention tile out of range");
           seen.push_back((t.row0 * (s.G / p.T) + hs) * p.S + t.nrows);
-          x.reads.push_back({BUF_WAVE + wv - 1, 0, s.qkv_rows});
+          x.reads.push_back({in_buf, 0, s.qkv_rows});
           // cached positions of this KV head (all positions before the current one)
           const int64_t kvbase = ((int64_t)layer * s.n_kv + t.row0) * s.max_positions;
           x.reads.push_back({BUF_KV, kvbase, kvbase + s.max_positions - 1});
@@ -517,15 +611,15 @@ int validate_plan(const HostPlan& p, std::string& err) {
           if (t.nrows == 0 && hs == 0) x.writes.push_back({BUF_KV, kvbase + s.max_positions - 1, kvbase + s.max_positions});
           for (int g2 = 0; g2 < p.T; ++g2) {  // one (hd + 4)-word record per query head
             const int64_t h = (int64_t)t.aux0 + g2, rec = (h * p.S + t.nrows) * (s.hd + 4);
-            x.writes.push_back({BUF_WAVE + wv, rec, rec + s.hd + 4});
+            x.writes.push_back({out_buf, rec, rec + s.hd + 4});
           }
           break;
         }
         case KIND_COMBINE: {
           if (t.row0 < 0 || t.row0 >= s.n_heads) return fail(err, TILES_E_PLAN, "combine tile out of range");
           seen.push_back(t.row0);
-          x.reads.push_back({BUF_WAVE + wv - 1, (int64_t)t.row0 * p.S * (s.hd + 4), (int64_t)(t.row0 + 1) * p.S * (s.hd + 4)});
-          x.writes.push_back({BUF_WAVE + wv, (int64_t)t.row0 * s.hd, (int64_t)(t.row0 + 1) * s.hd});
+          x.reads.push_back({in_buf, (int64_t)t.row0 * p.S * (s.hd + 4), (int64_t)(t.row0 + 1) * p.S * (s.hd + 4)});
+          x.writes.push_back({out_buf, (int64_t)t.row0 * s.hd, (int64_t)(t.row0 + 1) * s.hd});
           break;
         }
         default:
@@ -548,6 +642,46 @@ int validate_plan(const HostPlan& p, std::string& err) {
       }
       if (covered != R || expect_next != R) return fail(err, TILES_E_PLAN, "GEMV rows not covered exactly once");
     }
+    // Dataflow: every tagged value a worker reads was published by the wave right before this one
+    // in the same step (the kernel's gathers poll that buffer and no other), inside that buffer; the
+    // LM partials of the previous step are read only at the start of a step.
+    for (int w = 0; w < W; ++w)
+      for (const Interval& r : io[w].reads) {
+        if (r.buf >= BUF_WAVE) {
+          const int j = r.buf - BUF_WAVE;
+          if (j != wv - 1) return fail(err, TILES_E_PLAN, "a tile reads a tagged buffer other than the previous wave's");
+          if (r.lo < 0 || r.hi > wave_out_words(s, p.S, p.waves[j].kind))
+            return fail(err, TILES_E_PLAN, "a read falls outside its producer's buffer");
+        } else if (r.buf == BUF_LMPART && wv != 0) {
+          return fail(err, TILES_E_PLAN, "LM-head partials read outside the first wave of a step");
+        }
+      }
+    // Every word of this wave's output buffer (the LM partials: every worker's slot) is written by
+    // exactly one tile per step: a word nobody writes would leave its consumers polling forever, a
+    // word written twice would race.
+    {
+      const int32_t target = kind == KIND_LM ? BUF_LMPART : out_buf;
+      const int64_t n = kind == KIND_LM ? W : wave_out_words(s, p.S, kind);
+      std::vector<std::pair<int64_t, int64_t>> ws;
+      for (int w = 0; w < W; ++w)
+        for (const Interval& x : io[w].writes) {
+          if (x.buf == target) ws.push_back({x.lo, x.hi});
+          else if (x.buf >= BUF_WAVE) return fail(err, TILES_E_PLAN, "a tile writes another wave's buffer");
+        }
+      std::sort(ws.begin(), ws.end());
+      int64_t next = 0;
+      for (const auto& iv : ws) {
+        if (iv.first != next) {
+          os << "output buffer of wave " << wv << " not written exactly once per step";
+          return fail(err, TILES_E_PLAN, os.str());
+        }
+        next = iv.second;
+      }
+      if (next != n) {
+        os << "output buffer of wave " << wv << " not written exactly once per step";
+        return fail(err, TILES_E_PLAN, os.str());
+      }
+    }
     // hazards: a write of one worker may not meet a read or write of another worker in the same wave
     for (int a = 0; a < W; ++a)
       for (const Interval& wr : io[a].writes)
@@ -565,10 +699,107 @@ int validate_plan(const HostPlan& p, std::string& err) {
             }
         }
   }
+
+  // byte balance: max/mean over the wave's busy workers within one row of a perfect split
+  for (int wv = 0; wv < nw; ++wv) {
+    int64_t tot = 0, mx = 0, row_bytes = 0;
+    int busy = 0;
+    for (int w = 0; w < W; ++w) {
+      const TileDesc& t = p.tiles[(size_t)wv * W + w];
+      if (t.kind == KIND_NONE || t.kind == KIND_ATTN || t.kind == KIND_COMBINE) continue;
+      const int64_t b = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1) * t.kpad * 2;
+      ++busy;
+      tot += b;
+      mx = std::max(mx, b);
+      row_bytes = std::max<int64_t>(row_bytes, (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1));
+    }
+    if (busy == 0) continue;
+    if ((double)mx > (double)tot / busy + row_bytes + 0.5) {
+      os << "worker bytes unbalanced in wave " << wv;
+      return fail(err, TILES_E_PLAN, os.str());
+    }
+  }
+
   // packed ranges of different tiles never overlap
   std::sort(packed_ranges.begin(), packed_ranges.end());
   for (size_t i = 1; i < packed_ranges.size(); ++i)
     if (packed_ranges[i].first < packed_ranges[i - 1].second) return fail(err, TILES_E_PLAN, "packed tiles overlap");
+
+  // Packing round trip: every row of every source tensor is copied exactly once, with its full
+  // width, inside the packed buffer, and every GEMV tile row finds there the source row it computes
+  // with (QKV rows from Wq, Wk, Wv in turn; gate/up rows alternating; LM-head rows from the embedding
+  // when tied), so that a packing mistake cannot go unnoticed until the numbers come out wrong.
+  {
+    struct Src { int32_t tensor, layer; int64_t row, cols; };
+    std::unordered_map<int64_t, Src> at;  // destination byte offset of a packed row -> its source
+    at.reserve(1 << 16);
+    std::map<std::pair<int32_t, int32_t>, std::vector<std::pair<int64_t, int64_t>>> rows_of;  // source rows copied
+    for (const CopySeg& c : p.copies) {
+      int64_t R = 0, C = 0;
+      if (!source_geometry(s, c.tensor, R, C) || c.cols != C || c.nrows < 1 || c.src_row < 0 || c.src_row + c.nrows > R ||
+          c.dst_off < 0 || c.dst_pitch < c.cols * 2 || c.dst_off + (c.nrows - 1) * c.dst_pitch + c.cols * 2 > p.packed_bytes)
+        return fail(err, TILES_E_PLAN, "packing copy out of range");
+      rows_of[{c.tensor, c.layer}].push_back({c.src_row, c.src_row + c.nrows});
+      for (int64_t r = 0; r < c.nrows; ++r)
+        if (!at.emplace(c.dst_off + r * c.dst_pitch, Src{c.tensor, c.layer, c.src_row + r, c.cols}).second)
+          return fail(err, TILES_E_PLAN, "two packing copies write the same packed row");
+    }
+    for (auto& kvp : rows_of) {
+      int64_t R = 0, C = 0;
+      source_geometry(s, kvp.first.first, R, C);
+      auto& v = kvp.second;
+      std::sort(v.begin(), v.end());
+      int64_t next = 0;
+      for (const auto& iv : v) {
+        if (iv.first != next) return fail(err, TILES_E_PLAN, "source rows not packed exactly once");
+        next = iv.second;
+      }
+      if (next != R) return fail(err, TILES_E_PLAN, "source rows not packed exactly once");
+    }
+    // every source tensor the model has is packed
+    const size_t per_layer = s.qk_norm ? 11 : 9;
+    const size_t want = (size_t)s.n_layers * per_layer + 2 /*final norm, embedding or LM head*/ + (s.tied ? 0 : 1);
+    if (rows_of.size() != want) return fail(err, TILES_E_PLAN, "source rows not packed exactly once");
+    for (int wv = 0; wv < nw; ++wv) {
+      const int32_t kind = p.waves[wv].kind;
+      if (kind == KIND_ATTN || kind == KIND_COMBINE) continue;
+      for (int w = 0; w < W; ++w) {
+        const TileDesc& t = p.tiles[(size_t)wv * W + w];
+        if (t.kind == KIND_NONE) continue;
+        const int64_t nr = (int64_t)t.nrows * (kind == KIND_GU ? 2 : 1);
+        for (int64_t r = 0; r < nr; ++r) {
+          int32_t tensor, layer;
+          int64_t srow;
+          expected_source(s, kind, p.waves[wv].layer, s.tied, t.row0 + (kind == KIND_GU ? r / 2 : r), r, tensor, layer, srow);
+          auto it = at.find(t.woff + r * t.kpad * 2);
+          if (it == at.end() || it->second.tensor != tensor || it->second.layer != layer || it->second.row != srow ||
+              it->second.cols * 2 > (int64_t)t.kpad * 2) {
+            os << "packed row " << r << " of worker " << w << "'s tile in wave " << wv << " is not its source row";
+            return fail(err, TILES_E_PLAN, os.str());
+          }
+        }
+      }
+    }
+    // the embedding rows the first wave reads, and the gains, are where the plan says
+    auto it = at.find(p.embed_off + (int64_t)(s.V - 1) * p.embed_stride);
+    if (it == at.end() || it->second.tensor != SRC_EMBED || it->second.row != s.V - 1)
+      return fail(err, TILES_E_PLAN, "embedding rows not where the plan reads them");
+    it = at.find(p.final_norm_off);
+    if (it == at.end() || it->second.tensor != SRC_FINAL_NORM) return fail(err, TILES_E_PLAN, "final-norm gain misplaced");
+    for (int l = 0; l < s.n_layers; ++l) {
+      const LayerSmall& g = p.small[l];
+      auto a1 = at.find(g.attn_norm), m1 = at.find(g.mlp_norm);
+      if (a1 == at.end() || a1->second.tensor != SRC_ATTN_NORM || a1->second.layer != l || m1 == at.end() ||
+          m1->second.tensor != SRC_MLP_NORM || m1->second.layer != l)
+        return fail(err, TILES_E_PLAN, "norm gains misplaced");
+      if (s.qk_norm) {
+        auto q1 = at.find(g.q_norm), k1 = at.find(g.k_norm);
+        if (q1 == at.end() || q1->second.tensor != SRC_Q_NORM || q1->second.layer != l || k1 == at.end() ||
+            k1->second.tensor != SRC_K_NORM || k1->second.layer != l)
+          return fail(err, TILES_E_PLAN, "norm gains misplaced");
+      }
+    }
+  }
 
   // split-KV: for every attended length the splits partition [0, L) and exactly one holds L-1
   for (int64_t L = 1; L <= s.max_positions; ++L) {
@@ -587,41 +818,11 @@ int validate_plan(const HostPlan& p, std::string& err) {
     // the KV write happens in the split holding L-1; the kernel makes that split write
   }
 
-  // byte balance: max/mean over the wave's busy workers within one row of a perfect split
-  for (int wv = 0; wv < nw; ++wv) {
-    if (p.wave_bytes.empty() || p.wave_bytes[wv] == 0 || p.wave_busy[wv] == 0) continue;
-    const double mean = (double)p.wave_bytes[wv] / p.wave_busy[wv];
-    int64_t row_bytes = 0;
-    for (int w = 0; w < W; ++w) {
-      const TileDesc& t = p.tiles[(size_t)wv * W + w];
-      if (t.kind != KIND_NONE) row_bytes = std::max<int64_t>(row_bytes, (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1));
-    }
-    if ((double)p.wave_max_bytes[wv] > mean + row_bytes + 0.5) return fail(err, TILES_E_PLAN, "worker bytes unbalanced");
-  }
-
-  // tagged buffers: every wave but the LM head owns a 4-word aligned buffer, disjoint from the others
-  {
-    std::vector<std::pair<int64_t, int64_t>> bufs;
-    for (int wv = 0; wv < nw; ++wv) {
-      const int64_t n = wave_out_words(s, p.S, p.waves[wv].kind);
-      const int32_t off = p.waves[wv].ll_off;
-      if (n == 0) {
-        if (off != -1) return fail(err, TILES_E_PLAN, "LM-head wave with a tagged buffer");
-        continue;
-      }
-      if (off < 0 || off % 4 != 0 || n % 4 != 0 || off + n > p.ll_words)
-        return fail(err, TILES_E_PLAN, "tagged buffer misaligned or out of bounds");
-      bufs.push_back({off, off + n});
-    }
-    std::sort(bufs.begin(), bufs.end());
-    for (size_t i = 1; i < bufs.size(); ++i)
-      if (bufs[i].first < bufs[i - 1].second) return fail(err, TILES_E_PLAN, "tagged buffers overlap");
-  }
-
   // LDS capacity for every wave's staging
   if (p.lds_part_floats / NCOMP < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
   if (p.stage_batches < 0 || p.stage_batches > MAX_STAGE_BATCHES ||
-      p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT)
+      p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT ||
+      p.lds_stage_floats * 4 > 65536)
     return fail(err, TILES_E_PLAN, "bad LDS staging area");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
   if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
@@ -629,6 +830,129 @@ int validate_plan(const HostPlan& p, std::string& err) {
   if ((int64_t)p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
   if (p.lds_xres_floats < s.Hpad) return fail(err, TILES_E_PLAN, "LDS residual area too small");
   return TILES_OK;
+}
+
+int debug_mutate_plan(HostPlan& p, int32_t m, std::string& err) {
+  const int32_t W = p.W;
+  const int nw = (int)p.waves.size();
+  auto tile = [&](int wv, int w) -> TileDesc& { return p.tiles[(size_t)wv * W + w]; };
+  auto first_wave = [&](int32_t kind) {
+    for (int wv = 0; wv < nw; ++wv)
+      if (p.waves[wv].kind == kind) return wv;
+    return -1;
+  };
+  // two workers of a GEMV wave whose tiles are adjacent in rows (a's rows end where b's begin)
+  auto adjacent = [&](int wv, int& a, int& b, int min_b_rows) {
+    for (a = 0; a < W; ++a) {
+      if (tile(wv, a).kind == KIND_NONE) continue;
+      for (b = 0; b < W; ++b)
+        if (b != a && tile(wv, b).kind != KIND_NONE && tile(wv, b).row0 == tile(wv, a).row0 + tile(wv, a).nrows &&
+            tile(wv, b).nrows > min_b_rows)
+          return true;
+    }
+    return false;
+  };
+  int a = 0, b = 0;
+  switch (m) {
+    case DBG_NONE:
+      return TILES_OK;
+    case DBG_ROW_OVERLAP: {
+      const int wv = first_wave(KIND_GU);
+      if (!adjacent(wv, a, b, 0)) break;
+      tile(wv, a).nrows += 1;
+      return TILES_OK;
+    }
+    case DBG_ROW_GAP: {
+      const int wv = first_wave(KIND_GU);
+      for (a = 0; a < W; ++a)
+        if (tile(wv, a).kind != KIND_NONE && tile(wv, a).nrows >= 2) {
+          tile(wv, a).nrows -= 1;
+          return TILES_OK;
+        }
+      break;
+    }
+    case DBG_ATTN_DUPLICATE: case DBG_ATTN_MISSING: {
+      const int wv = first_wave(KIND_ATTN);
+      for (a = 0; a < W; ++a)
+        if (tile(wv, a).kind == KIND_ATTN) break;
+      if (a == W) break;
+      if (m == DBG_ATTN_MISSING) {
+        std::memset(&tile(wv, a), 0, sizeof(TileDesc));
+        return TILES_OK;
+      }
+      for (b = 0; b < W; ++b)
+        if (tile(wv, b).kind == KIND_NONE) {
+          tile(wv, b) = tile(wv, a);
+          return TILES_OK;
+        }
+      break;
+    }
+    case DBG_SPLIT_OUT_OF_RANGE: {
+      const int wv = first_wave(KIND_ATTN);
+      for (a = 0; a < W; ++a)
+        if (tile(wv, a).kind == KIND_ATTN) {
+          tile(wv, a).nrows = p.S;
+          return TILES_OK;
+        }
+      break;
+    }
+    case DBG_TAGGED_OVERLAP:
+      if (nw < 3) break;
+      p.waves[1].ll_off = p.waves[0].ll_off;
+      return TILES_OK;
+    case DBG_TAGGED_OUT_OF_BOUNDS:
+      p.waves[0].ll_off = (int32_t)p.ll_words;
+      return TILES_OK;
+    case DBG_UNBALANCED: {
+      // worker a takes the first two rows of worker b: coverage and packing stay exact, the bytes do not
+      const int wv = first_wave(KIND_DOWN);
+      if (!adjacent(wv, a, b, 2)) break;
+      const int64_t row_bytes = (int64_t)tile(wv, b).kpad * 2;
+      tile(wv, a).nrows += 2;
+      tile(wv, b).row0 += 2;
+      tile(wv, b).nrows -= 2;
+      tile(wv, b).woff += 2 * row_bytes;
+      return TILES_OK;
+    }
+    case DBG_WAVE_ORDER:
+      if (nw < 3) break;
+      std::swap(p.waves[1], p.waves[2]);
+      return TILES_OK;
+    case DBG_LM_NOT_LAST:
+      p.waves.back().kind = KIND_DOWN;
+      return TILES_OK;
+    case DBG_PACKED_OVERLAP: {
+      const int wv = first_wave(KIND_QKV);
+      if (!adjacent(wv, a, b, 0)) break;
+      tile(wv, b).woff = tile(wv, a).woff;
+      return TILES_OK;
+    }
+    case DBG_PACKED_SWAPPED: {
+      // two tiles of the LM-head wave with equal row counts exchange their packed rows
+      const int wv = nw - 1;
+      for (a = 0; a < W; ++a)
+        for (b = a + 1; b < W; ++b)
+          if (tile(wv, a).kind == KIND_LM && tile(wv, b).kind == KIND_LM && tile(wv, a).nrows == tile(wv, b).nrows) {
+            std::swap(tile(wv, a).woff, tile(wv, b).woff);
+            return TILES_OK;
+          }
+      break;
+    }
+    case DBG_COPY_DROPPED:
+      if (p.copies.empty()) break;
+      p.copies.erase(p.copies.begin() + (long)(p.copies.size() / 2));
+      return TILES_OK;
+    case DBG_GAIN_MISPLACED:
+      if (p.small.size() < 2) break;
+      p.small[1].mlp_norm = p.small[0].mlp_norm;
+      return TILES_OK;
+    case DBG_STAGING:
+      p.stage_batches = MAX_STAGE_BATCHES + 1;
+      return TILES_OK;
+    default:
+      return fail(err, TILES_E_ARG, "unknown plan mutation");
+  }
+  return fail(err, TILES_E_ARG, "plan mutation not applicable to this plan");
 }
 
 }  // namespace tiles

@@ -78,6 +78,31 @@ int validate_plan(const HostPlan& plan, std::string& err);
 // 64-bit FNV-1a over the schedule and its geometry.
 uint64_t plan_checksum(const HostPlan& plan);
 
+// Per-worker hash of the schedule words each worker loads into LDS (its TileDesc of every wave,
+// every WaveDesc, every LayerSmall; see table_mix): W entries, re-checked by the kernel.
+std::vector<uint64_t> worker_table_hashes(const HostPlan& plan);
+
+// Planted mistakes for tests of validate_plan (host only): each makes one rule fail.
+enum DebugMutation : int32_t {
+  DBG_NONE = 0,
+  DBG_ROW_OVERLAP = 1,        // a gate/up tile takes one row more: rows covered twice
+  DBG_ROW_GAP = 2,            // a gate/up tile gives up a row: a row covered by nobody
+  DBG_ATTN_DUPLICATE = 3,     // an attention tile copied to an idle worker
+  DBG_ATTN_MISSING = 4,       // an attention tile removed
+  DBG_SPLIT_OUT_OF_RANGE = 5, // an attention tile's split index = S
+  DBG_TAGGED_OVERLAP = 6,     // wave 1's tagged buffer placed on wave 0's
+  DBG_TAGGED_OUT_OF_BOUNDS = 7,
+  DBG_UNBALANCED = 8,         // a down tile takes two rows of its neighbour (coverage and packing stay exact)
+  DBG_WAVE_ORDER = 9,         // waves 1 and 2 swapped
+  DBG_LM_NOT_LAST = 10,       // the step does not end with the LM head (no per-step all-to-all)
+  DBG_PACKED_OVERLAP = 11,    // two QKV tiles read the same packed bytes
+  DBG_PACKED_SWAPPED = 12,    // two LM-head tiles exchange their packed rows
+  DBG_COPY_DROPPED = 13,      // one packing copy removed
+  DBG_GAIN_MISPLACED = 14,    // layer 1's MLP gain offset points at layer 0's
+  DBG_STAGING = 15,           // more staging batches than the LDS layout allows
+};
+int debug_mutate_plan(HostPlan& plan, int32_t mutation, std::string& err);
+
 // Words of wave `kind`'s tagged output buffer (0 for the LM head, whose partials live apart).
 inline int64_t wave_out_words(const Shape& s, int32_t S, int32_t kind) {
   switch (kind) {

@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.tiles_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]
         L.tiles_plan_wave.restype = ctypes.c_int
         L.tiles_plan_wave.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(WaveInfo)]
+        L.tiles_plan_debug_validate.restype = ctypes.c_int
+        L.tiles_plan_debug_validate.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32]
         L.tiles_plan_dry_run.restype = ctypes.c_int
         L.tiles_plan_dry_run.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.POINTER(PlanInfo)]
         L.tiles_plan_set_stream.restype = ctypes.c_int
@@ -119,6 +121,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_int32)]
         L.tiles_plan_debug_corrupt.restype = ctypes.c_int
         L.tiles_plan_debug_corrupt.argtypes = [ctypes.c_void_p]
+        L.tiles_plan_debug_corrupt_device.restype = ctypes.c_int
+        L.tiles_plan_debug_corrupt_device.argtypes = [ctypes.c_void_p]
         L.tiles_plan_debug_spin_limit.restype = ctypes.c_int
         L.tiles_plan_debug_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
         L.tiles_stream_read.restype = ctypes.c_int
@@ -153,6 +157,13 @@ def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> P
     cfg = make_config(m, max_positions, **kw)
     _check(lib().tiles_plan_dry_run(ctypes.byref(cfg), n_workers, ctypes.byref(info)))
     return info
+
+
+def debug_validate(m: ModelConfig, max_positions: int, mutation: int, n_workers: int = 256, **kw) -> int:
+    """Plan on the host, plant mistake number `mutation` (tiles_plan_debug_validate) and return the
+    validator's status code (the message is in last_error())."""
+    cfg = make_config(m, max_positions, **kw)
+    return lib().tiles_plan_debug_validate(ctypes.byref(cfg), n_workers, mutation)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -297,6 +308,10 @@ class Plan:
 
     def debug_corrupt(self):
         _check(lib().tiles_plan_debug_corrupt(self._h))
+
+    def debug_corrupt_device(self):
+        """Flip one bit of the device copy of the schedule (the next launch must detect it)."""
+        _check(lib().tiles_plan_debug_corrupt_device(self._h))
 
     def debug_spin_limit(self, rounds: int):
         """Watchdog of every wait in later decodes (0 restores the default)."""
