@@ -18,6 +18,7 @@ from tile_scheduled_persistent_amd import synth, tiles
 HIDDEN_REL_L2 = 1e-2
 LOGIT_MAX_ABS = 5e-2
 MARGIN = 0.1
+FLIP_FRACTION = 0.05  # cached BF16 entries that may differ (see kv_rows_close)
 
 
 def top2_margin(logits: np.ndarray) -> float:
@@ -113,8 +114,11 @@ def compare_teacher_forced(tag, g_tokens, g_logits, g_hidden, o_res):
 
 def kv_rows_close(tag, g_cache, o_bits, pos: int, n: int):
     """The K or V rows a launch wrote (positions pos .. pos + n - 1) against the oracle's: the same
-    relative-L2 bar per (layer, head, position) row as the hidden states (entries near cancellation
-    may differ by a few BF16 ulps), and at most 1 % of the entries differing at all."""
+    relative-L2 bar per (layer, head, position) row as the hidden states.  Both sides round the same
+    FP32 values to BF16, which differ only by summation order; an entry flips to the neighbouring BF16
+    value with a probability of about its relative FP32 difference times 2^8 (about 1 % at the 4e-5
+    the residual stream reaches after 28 layers), while a rounding-mode mistake (truncation) would
+    flip about half of them: at most FLIP_FRACTION of the entries may differ."""
     gb = synth.bits(g_cache)[:, :, pos:pos + n]
     ob = o_bits[:, :, pos:pos + n]
     gf = (gb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -122,7 +126,7 @@ def kv_rows_close(tag, g_cache, o_bits, pos: int, n: int):
     rel = np.linalg.norm(gf - of, axis=-1) / np.linalg.norm(of, axis=-1)
     assert rel.max() <= HIDDEN_REL_L2, f"{tag}: cached rows rel L2 {rel.max():.3e}"
     frac = float(np.mean(gb != ob))
-    assert frac < 1e-2, f"{tag}: {frac:.3%} of cached entries differ"
+    assert frac < FLIP_FRACTION, f"{tag}: {frac:.3%} of cached entries differ"
     return float(rel.max()), frac
 
 

@@ -436,11 +436,15 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
   }
   if (bidx < 0 || bidx >= a.V) bidx = 0;  // only reachable with non-finite logits
   tok = bidx;
-  // Acquire: having seen every worker's (released) partial of the step, this worker sees every
-  // store any worker made in that step.  This is what lets one parity bit separate generations:
-  // when a consumer polls a buffer at step s + 2, the buffer already shows step s + 1's value (the
-  // other parity) or a newer one, never step s's (nor, at step 1, the fill value).
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // The acquire side of the per-step all-to-all: having seen every worker's (released) partial of
+  // the step, this worker sees every store any worker made in that step, so one parity bit separates
+  // generations -- when a consumer polls a buffer at step s + 2, the buffer already shows step s + 1's
+  // value (the other parity) or a newer one, never step s's (nor, at step 1, the fill value).  No
+  // cache invalidation is needed for that: every later load of another worker's data is issued after
+  // these loads returned and either reads the device-coherent level (the polls) or is a KV row that no
+  // worker read before it was written in this launch (see load_kv); only the compiler must not move
+  // loads above this point.
+  COMPILER_FENCE();
   return false;
 }
 
