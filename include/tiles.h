@@ -162,6 +162,19 @@ tiles_plan_t *tiles_plan_create(const tiles_config_t *cfg, const tiles_weights_t
 int tiles_decode(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, int32_t *out_tokens,
                  float *out_logits);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): tiles_decode with the same arguments, semantics and results,
+ * except that the launch's tagged-data buffers, LM-head partials and status words live in a
+ * file-scope device array of this library, 8 MiB per GPU, held from the first call on a GPU until
+ * the process ends, instead of the plan's own buffers.  Calls no allocating routine (the plan must
+ * exist already).  Errors as tiles_decode, plus TILES_E_ARG when the plan's scratch (its tagged
+ * buffers: about (qkv rows + n_heads * splits * (head_dim + 4) + 2 * hidden + ffn) words per layer)
+ * exceeds 8 MiB.  Every call on one GPU shares that array and each launch first clears what it
+ * uses: calls that overlap on one GPU (in different streams, or from different threads) race and
+ * give undefined results; sequential calls, also of different plans, are fine. */
+int tiles_decode_noalloc(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, int32_t *out_tokens,
+                         float *out_logits);
+
 /* Release every resource of the plan (synchronizes its stream first).  NULL-safe. */
 void tiles_plan_destroy(tiles_plan_t *plan);
 

@@ -33,6 +33,7 @@ hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t cou
 hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, int n_groups, uint32_t* sink, hipStream_t stream);
 hipError_t launch_edge_latency(uint32_t* words, int peer, int iters, uint32_t spin_limit, uint64_t* out,
                                hipStream_t stream);
+hipError_t noalloc_scratch(int device, uint32_t** out);
 }
 
 using namespace tiles;
@@ -85,6 +86,7 @@ struct tiles_plan {
   uint32_t* sync = nullptr;
   size_t sync_bytes = 0;
   uint64_t* d_table_check = nullptr;  // [W] per-worker schedule hashes, then the build id
+  uint32_t* last_sync = nullptr;      // status words of the last launch (plan-owned or the static scratch)
   float* dbg_hidden = nullptr;
   uint64_t* trace = nullptr;
   int last_steps = 0;
@@ -304,20 +306,11 @@ int check_identity(const tiles_plan* p) {
   return TILES_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-tiles_plan_t* tiles_plan_create(const tiles_config_t* cfg, const tiles_weights_t* w) {
-  g_err.clear();
-  tiles_plan* p = nullptr;
-  int rc = create_impl(cfg, w, &p);
-  if (rc != TILES_OK) return nullptr;
-  return p;
-}
-
-int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
-                 float* out_logits) {
+// One cooperative launch of the worker.  `noalloc`: the launch's tagged-data buffers, LM-head
+// partials and status words live in the file-scope scratch array of this GPU (see
+// noalloc_scratch) instead of the plan's own buffers; the layout is the same.
+int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
+                float* out_logits, bool noalloc) {
   if (!p || !kv || !out_tokens) return set_err(TILES_E_ARG, "null plan, kv or out_tokens");
   if (!kv->k || !kv->v) return set_err(TILES_E_ARG, "null KV buffers");
   if (n_steps < 1 || n_steps > MAX_STEPS) return set_err(TILES_E_ARG, "n_steps must be in [1, 64]");
@@ -339,9 +332,26 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.final_norm_off = hp.final_norm_off;
   a.embed_off = hp.embed_off;
   a.embed_stride = hp.embed_stride;
-  a.ll = p->ll;
-  a.lmpart = p->lmpart;
-  a.sync = p->sync;
+  uint32_t* ll = p->ll;
+  uint32_t* lmpart = p->lmpart;
+  uint32_t* sync = p->sync;
+  if (noalloc) {
+    const int64_t ll_bytes = ((int64_t)hp.ll_words * 4 + 255) / 256 * 256;
+    const int64_t lm_bytes = ((int64_t)hp.W * 8 + 255) / 256 * 256;
+    const int64_t need = ll_bytes + lm_bytes + SYNC_WORDS * 4;
+    if (need > NOALLOC_SCRATCH_BYTES)
+      return set_err(TILES_E_ARG, "this plan's tagged scratch (" + std::to_string(need) +
+                                      " bytes) exceeds the allocation-free entry point's " +
+                                      std::to_string(NOALLOC_SCRATCH_BYTES) + " bytes; use tiles_decode");
+    uint32_t* base = nullptr;
+    HIP_TRY(noalloc_scratch(p->device, &base));
+    ll = base;
+    lmpart = base + ll_bytes / 4;
+    sync = lmpart + lm_bytes / 4;
+  }
+  a.ll = ll;
+  a.lmpart = lmpart;
+  a.sync = sync;
   a.table_check = p->d_table_check;
   a.kv_k = static_cast<uint16_t*>(kv->k);
   a.kv_v = static_cast<uint16_t*>(kv->v);
@@ -378,8 +388,8 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   a.stage_batches = hp.stage_batches;
 
   // Kernels rather than memsets, so that the launch sequence can be captured in a graph.
-  HIP_TRY(launch_fill(p->ll, p->fill_words, TAG_FILL, p->stream));
-  HIP_TRY(launch_fill(p->sync, SYNC_WORDS, 0u, p->stream));
+  HIP_TRY(launch_fill(ll, p->fill_words, TAG_FILL, p->stream));
+  HIP_TRY(launch_fill(sync, SYNC_WORDS, 0u, p->stream));
   if (p->cfg.flags & TILES_POISON) {
     // NaN into the rows this launch writes: a read before the write would surface as NaN
     const int nblk = hp.s.n_layers * hp.s.n_kv;
@@ -394,7 +404,31 @@ int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps
   HIP_TRY(hipLaunchCooperativeKernel(kern, dim3(hp.W), dim3(BLOCK_THREADS), args, hp.lds_bytes, p->stream));
   kv->length += n_steps;
   p->last_steps = n_steps;
+  p->last_sync = sync;
   return TILES_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+tiles_plan_t* tiles_plan_create(const tiles_config_t* cfg, const tiles_weights_t* w) {
+  g_err.clear();
+  tiles_plan* p = nullptr;
+  int rc = create_impl(cfg, w, &p);
+  if (rc != TILES_OK) return nullptr;
+  return p;
+}
+
+int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
+                 float* out_logits) {
+  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, false);
+}
+
+int tiles_decode_noalloc(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
+                         float* out_logits) {
+  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, true);
 }
 
 void tiles_plan_destroy(tiles_plan_t* p) { release(p); }
@@ -478,9 +512,10 @@ int tiles_plan_status(tiles_plan_t* p) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   HIP_TRY(hipStreamSynchronize(p->stream));
   uint32_t status = 0;
-  HIP_TRY(hipMemcpy(&status, p->sync + SYNC_STATUS_WORD, 4, hipMemcpyDeviceToHost));
+  uint32_t* sync = p->last_sync ? p->last_sync : p->sync;
+  HIP_TRY(hipMemcpy(&status, sync + SYNC_STATUS_WORD, 4, hipMemcpyDeviceToHost));
   if (status != 0) {
-    HIP_TRY(hipMemset(p->sync, 0, p->sync_bytes));
+    HIP_TRY(hipMemset(sync, 0, p->sync_bytes));
     if (status == STATUS_TABLES)
       return set_err(TILES_E_PLAN, "a worker's device-resident schedule or build id failed its check in the last launch");
     return set_err(TILES_E_KERNEL, "a wait's watchdog expired in the last launch");

@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "plan_types.h"
@@ -1855,6 +1856,32 @@ hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t 
   const int grid = nseg < 4096 ? (nseg > 0 ? nseg : 1) : 4096;
   hipLaunchKernelGGL(pack_weights, dim3(grid), dim3(256), 0, stream, segs, nseg, dst);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free decode entry point (tiles_decode_noalloc): the tagged-data
+// buffers, the LM-head partials and the status words of a launch, in one file-scope array per
+// GPU instead of plan-owned memory.  Host code never uses the array's name as an address (on the
+// host it names a stand-in): the device address comes from hipGetSymbolAddress, once per device,
+// with that device current.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) uint32_t scratch[NOALLOC_SCRATCH_BYTES / 4];
+
+hipError_t noalloc_scratch(int device, uint32_t** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static uint32_t* ptr[MAX_DEVICES] = {};
+  if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[device] = static_cast<uint32_t*>(p);
+  }
+  *out = ptr[device];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

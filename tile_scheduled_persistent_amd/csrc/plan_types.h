@@ -79,6 +79,9 @@ constexpr uint32_t STATUS_WATCHDOG = 1;  // a wait's watchdog expired
 constexpr uint32_t STATUS_TABLES = 2;    // a worker's device-resident schedule failed its check
 constexpr int SYNC_ABORT_WORD = 16;      // set by any worker that gives up waiting
 constexpr int SYNC_WORDS = 32;
+// Size of the file-scope scratch array of the allocation-free decode entry point (per GPU): the
+// tagged-data buffers, LM-head partials and status words of one launch must fit in it.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = 8ll << 20;
 
 // In-kernel trace record per (step, wave, worker), 100 MHz wall clock:
 //   0 wave start, 1 inputs staged (after barrier P), 2 compute done (after barrier B),

@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_decode.restype = ctypes.c_int
         L.tiles_decode.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_decode_noalloc.restype = ctypes.c_int
+        L.tiles_decode_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p]
         L.tiles_plan_destroy.restype = None
         L.tiles_plan_destroy.argtypes = [ctypes.c_void_p]
         L.tiles_last_error.restype = ctypes.c_char_p
@@ -253,8 +256,9 @@ class Plan:
 
     # ------------------------------------------------------------------
     def decode(self, kv: KVCache, token: int, n_steps: int, out_tokens: torch.Tensor,
-               out_logits: Optional[torch.Tensor] = None) -> int:
-        """Enqueue one cooperative launch of ``n_steps`` greedy steps; returns TILES_OK or raises."""
+               out_logits: Optional[torch.Tensor] = None, noalloc: bool = False) -> int:
+        """Enqueue one cooperative launch of ``n_steps`` greedy steps; returns TILES_OK or raises.
+        ``noalloc`` calls tiles_decode_noalloc (scratch in the library's static device array)."""
         if out_tokens.dtype != torch.int32 or not out_tokens.is_cuda or out_tokens.numel() < n_steps:
             raise ValueError("out_tokens must be a device int32 tensor with n_steps entries")
         if out_logits is not None and (out_logits.dtype != torch.float32 or not out_logits.is_cuda
@@ -264,8 +268,8 @@ class Plan:
             if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError("KV tensors must be contiguous device bf16")
         c = KV(_ptr(kv.k), _ptr(kv.v), kv.capacity, kv.length)
-        rc = lib().tiles_decode(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(out_tokens),
-                                _ptr(out_logits))
+        fn = lib().tiles_decode_noalloc if noalloc else lib().tiles_decode
+        rc = fn(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(out_tokens), _ptr(out_logits))
         _check(rc)
         kv.length = c.length
         return rc
