@@ -17,7 +17,8 @@ computes, written from the pages' description of the workload:
   (which the oracle does NOT split: it is the unsplit softmax definition).
 
 Arithmetic: FP32 activations and FP32 accumulation over BF16-rounded weights
-and a BF16 KV cache (``dtype=np.float64`` switches every activation to FP64
+(or, with ``weight_format="int8"``, the weights of every linear layer dequantized
+from per-row INT8 codes) and a BF16 KV cache (``dtype=np.float64`` switches every activation to FP64
 for pinning).  Every reading of a point the pages leave open is listed in the
 module docstring of :mod:`oracle.decoder`.
 """
@@ -26,6 +27,9 @@ from .decoder import (  # noqa: F401
     bf16_round,
     bf16_bits_to_float,
     float_to_bf16_bits,
+    quantize_rows_int8,
+    dequantize_rows_int8,
+    LINEAR_WEIGHTS,
     rmsnorm,
     rope_cos_sin,
     apply_rope,

@@ -36,6 +36,13 @@ R8  Greedy selection is argmax over the logits, lowest index on ties.
 R9  The per-layer hidden state is the residual stream after the layer's MLP
     residual add.
 R10 With tied embeddings the LM head is the embedding matrix.
+Q1  Weight-only INT8 ("History and roadmap" (TileInfer.jl), "M8 so far" table: weight-only INT8
+    linear layers; "Tried and not kept": group-wise quantization was not tried, so the scales are
+    per output row): every linear layer -- Wq, Wk, Wv, Wo, W_gate, W_up, W_down and the LM head --
+    is replaced by symmetric per-row INT8 codes and one FP32 scale per row, s = max|W_row| / 127 and
+    q = round-half-even(W / s) clamped to [-127, 127], every operation in FP32 on the BF16 values; a
+    row of zeros has s = 0 and q = 0.  The layer computes with the dequantized weights q * s.  The
+    embedding lookup and the norm gains keep their BF16 values.
 """
 
 from __future__ import annotations
@@ -49,6 +56,9 @@ __all__ = [
     "bf16_round",
     "bf16_bits_to_float",
     "float_to_bf16_bits",
+    "quantize_rows_int8",
+    "dequantize_rows_int8",
+    "LINEAR_WEIGHTS",
     "rmsnorm",
     "rope_cos_sin",
     "apply_rope",
@@ -103,6 +113,34 @@ def bf16_bits_to_float(u: np.ndarray, dtype=np.float32) -> np.ndarray:
     u = np.asarray(u, dtype=np.uint16)
     f = (u.astype(np.uint32) << 16).view(np.float32)
     return f.astype(dtype, copy=False)
+
+
+# ---------------------------------------------------------------------------
+# Weight-only INT8 (reading Q1)
+# ---------------------------------------------------------------------------
+
+LINEAR_WEIGHTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def quantize_rows_int8(w_bits: np.ndarray):
+    """Q1: symmetric per-row INT8 codes and FP32 scales of a BF16 matrix (uint16 bits [R, C]).
+
+    s_r = max_j |W_rj| / 127 and q_rj = round-half-even(W_rj / s_r), clamped to [-127, 127], each
+    operation in FP32 (the division correctly rounded, as IEEE-754 prescribes); s_r = 0 and q = 0 for
+    a row of zeros.  Returns (q int8 [R, C], s float32 [R])."""
+    w = bf16_bits_to_float(np.atleast_2d(w_bits), np.float32)
+    amax = np.max(np.abs(w), axis=-1)                      # exact
+    s = (amax / np.float32(127.0)).astype(np.float32)      # FP32 division
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = (w / safe[:, None]).astype(np.float32)             # FP32 division
+    q = np.clip(np.rint(r), -127, 127)                     # np.rint: half to even
+    q = np.where(s[:, None] > 0, q, 0).astype(np.int8)
+    return q, s
+
+
+def dequantize_rows_int8(q: np.ndarray, s: np.ndarray, dtype=np.float32) -> np.ndarray:
+    """Q1: the weights a quantized layer computes with, q * s per row (rounded to ``dtype``)."""
+    return q.astype(dtype) * s.astype(dtype)[:, None]
 
 
 # ---------------------------------------------------------------------------
@@ -171,20 +209,28 @@ class OracleModel:
     [n_layers, n_kv_heads, capacity, hd]; :meth:`step` writes position ``pos``.
     """
 
-    def __init__(self, cfg, weights: dict, dtype=np.float32, widen_once: bool = True):
+    def __init__(self, cfg, weights: dict, dtype=np.float32, widen_once: bool = True, weight_format: str = "bf16"):
         self.cfg = cfg
         self.dtype = np.dtype(dtype)
         self.w = weights
         self.widen_once = widen_once
+        if weight_format not in ("bf16", "int8"):
+            raise ValueError("weight_format must be 'bf16' or 'int8'")
+        self.int8 = weight_format == "int8"                # Q1
         self._cache: dict = {}
 
     # widened weights -------------------------------------------------------
-    def _get(self, layer: Optional[int], name: str) -> np.ndarray:
-        key = (layer, name)
+    def _get(self, layer: Optional[int], name: str, linear: bool = False) -> np.ndarray:
+        """The weights a stage computes with: the BF16 values widened, or (INT8 model, a linear
+        layer) its dequantized INT8 codes (Q1)."""
+        key = (layer, name, linear)
         if key in self._cache:
             return self._cache[key]
         src = self.w[name] if layer is None else self.w["layers"][layer][name]
-        arr = bf16_bits_to_float(src, self.dtype)
+        if self.int8 and (linear or name in LINEAR_WEIGHTS):
+            arr = dequantize_rows_int8(*quantize_rows_int8(src), self.dtype)
+        else:
+            arr = bf16_bits_to_float(src, self.dtype)
         if self.widen_once:
             self._cache[key] = arr
         return arr
@@ -193,9 +239,11 @@ class OracleModel:
         return bf16_bits_to_float(self.w["embed"][token], self.dtype).copy()
 
     def _lm_head(self) -> np.ndarray:
+        # (INT8 model: the head is a linear layer, quantized like the others; the lookup of the
+        # input token's embedding row stays BF16)
         if self.cfg.tie_embeddings or self.w.get("lm_head") is None:
-            return self._get(None, "embed")
-        return self._get(None, "lm_head")
+            return self._get(None, "embed", linear=True)
+        return self._get(None, "lm_head", linear=True)
 
     # one step ----------------------------------------------------------------
     def step(self, kv: dict, token: int, pos: int, kv_wide: Optional[dict] = None):

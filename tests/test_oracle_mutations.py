@@ -59,6 +59,12 @@ MUTATIONS = [
      'rmsnorm(x, self._get(l, "attn_norm"), eps)', False),
     ("widened cache row written unrounded", 'kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)',
      'kv_wide["v"][l, :, pos, :] = v', False),
+    ("INT8 codes truncated", "q = np.clip(np.rint(r), -127, 127)", "q = np.clip(np.trunc(r), -127, 127)", False),
+    ("INT8 scale over 128", "s = (amax / np.float32(127.0)).astype(np.float32)", "s = (amax / np.float32(128.0)).astype(np.float32)", False),
+    ("INT8 scale dropped", "return q.astype(dtype) * s.astype(dtype)[:, None]", "return q.astype(dtype) / np.float32(127.0) + 0 * s[:, None]", False),
+    ("INT8 LM head left in BF16", 'return self._get(None, "embed", linear=True)', 'return self._get(None, "embed")', False),
+    ("INT8 embedding lookup quantized", "return bf16_bits_to_float(self.w[\"embed\"][token], self.dtype).copy()",
+     "return self._get(None, \"embed\", linear=True)[token].copy()", False),
     ("argmax keeps the last maximum", "toks[i] = int(np.argmax(logits))",
      "toks[i] = int(len(logits) - 1 - np.argmax(logits[::-1]))", False),
 ]

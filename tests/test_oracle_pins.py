@@ -577,3 +577,72 @@ def test_widened_cache_path_equals_the_plain_path():
     for key in ("tokens", "logits", "hidden"):
         assert np.array_equal(a[key], b[key])
     assert np.array_equal(kva["k"], kvb["k"]) and np.array_equal(kva["v"], kvb["v"])
+
+
+# ---------------------------------------------------------------------------
+# Weight-only INT8 (per-row symmetric codes, FP32 scales).  Catches: truncation
+# instead of round-half-even, a scale of max/128, a dropped scale, the LM head
+# left in BF16, the embedding lookup quantized.
+# ---------------------------------------------------------------------------
+
+from oracle import dequantize_rows_int8, quantize_rows_int8  # noqa: E402
+
+
+def test_int8_quantizer_hand_worked_ties_and_zero_row():
+    # max |W| = 127/128, so s = 2^-7 exactly; W / s = 127, 2.5, 3.5, -2.5, 0 -> ties go to the even code
+    w = _b([[127 / 128, 2.5 * 2 ** -7, 3.5 * 2 ** -7, -2.5 * 2 ** -7, 0.0], [0.0, 0.0, 0.0, 0.0, 0.0]])
+    q, s = quantize_rows_int8(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert q.tolist() == [[127, 2, 4, -2, 0], [0, 0, 0, 0, 0]]
+    assert s.tolist() == [2 ** -7, 0.0]
+    assert np.array_equal(dequantize_rows_int8(q, s, np.float64)[1], np.zeros(5))
+
+
+def test_int8_quantizer_bounds_on_random_rows():
+    rng = np.random.default_rng(19)
+    mags = 10.0 ** rng.integers(-6, 4, 300)
+    w = _b(rng.standard_normal((300, 257)) * mags[:, None])
+    q, s = quantize_rows_int8(w)
+    W = bf16_bits_to_float(w, np.float64)
+    amax = np.abs(W).max(axis=1)
+    assert np.array_equal(s, (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32))
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    # the largest entry of each row takes the code +-127
+    assert np.all(np.abs(q.astype(np.int32)).max(axis=1) == 127)
+    # every entry within half a step (plus the FP32 division's rounding) of its dequantized value
+    err = np.abs(W - q.astype(np.float64) * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 128 * 2.0 ** -23))
+
+
+def test_int8_step_computes_with_the_dequantized_codes():
+    """One layer, attention off, an MLP whose down projection has rows [1, 0.3] and [0.6, -1]: in the
+    INT8 model the output is x + (q * s) a with the hand-computed codes (127, 38) / 127 and
+    (64, -127) / 127, not the BF16 product; the embedding row is looked up unquantized and the tied
+    head is quantized (its rows E[r] give codes of their own).  Catches: INT8 ignored, the scale
+    dropped, the head left in BF16, the lookup quantized."""
+    c = Cfg(n_layers=1, hidden=2, ffn=2, n_heads=1, n_kv_heads=1, head_dim=2, vocab=4)
+    rng = np.random.default_rng(20)
+    w = _zero_model(c, rng)
+    w["embed"] = _b([[0.5, -1.25], [1.0, 0.3], [0.75, 0.5], [-0.25, 0.125]])
+    w["layers"][0]["w_gate"] = _b(np.eye(2) * 2.0)
+    w["layers"][0]["w_up"] = _b(np.eye(2))
+    w["layers"][0]["w_down"] = _b([[1.0, 0.3], [0.6, -1.0]])
+    m = OracleModel(c, w, np.float64, weight_format="int8")
+    logits, hidden = m.step(_kv(c, 2), 0, 0)
+    x = np.array([0.5, -1.25])                                   # BF16 lookup, exact
+    h = x / math.sqrt(np.mean(x * x) + c.rms_eps)
+    # gate 2I and up I quantize exactly (codes 127 with scales 2/127 and 1/127)
+    s_g, s_u = np.float32(2.0) / np.float32(127.0), np.float32(1.0) / np.float32(127.0)
+    gate = 127 * float(s_g) * h
+    up = 127 * float(s_u) * h
+    a = gate / (1.0 + np.exp(-gate)) * up
+    sd = float(s_u)
+    w_down = np.array([[127, 38], [round(0.6015625 * 127), -127]]) * sd  # 0.6 is 0.6015625 in BF16: code 76
+    assert round(0.6015625 * 127) == 76
+    x1 = x + w_down @ a
+    assert np.allclose(hidden[0], x1, rtol=1e-12, atol=0)
+    E = bf16_bits_to_float(w["embed"], np.float64)
+    qE, sE = quantize_rows_int8(w["embed"])
+    hf = x1 / math.sqrt(np.mean(x1 * x1) + c.rms_eps)
+    assert np.allclose(logits, (qE.astype(np.float64) * sE.astype(np.float64)[:, None]) @ hf, rtol=1e-12)
+    assert not np.allclose(logits, E @ hf, rtol=1e-6)            # the head really is quantized
