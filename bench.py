@@ -48,7 +48,7 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
     from oracle import OracleModel
 
     w_bits, kv_bits = setup_bits
-    o = OracleModel(m, w_bits, np.float32)
+    o = OracleModel(m, w_bits, np.float32, weight_format=wl.weights)
     kv = {"k": kv_bits["k"].copy(), "v": kv_bits["v"].copy()}
     t_prep = time.perf_counter()
     logits, _ = o.step(kv, token, wl.n_cached)  # warm-up (also widens the weights once)
@@ -171,7 +171,7 @@ def main():
     token = synth.make_tokens(m, 1)[0]
     stream = torch.cuda.current_stream()
     plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
-                      attn_heads=args.attn_heads, o_placement=args.o_placement,
+                      attn_heads=args.attn_heads, o_placement=args.o_placement, weight_format=wl.weights,
                       stream=stream)
     info = plan.info()
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
@@ -228,7 +228,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if wl.weights == "bf16" else "int8 weights, bf16 KV, fp32 activations",
         "data": "synthetic",
         "config": {"workload": wl.description, "batch": 1, "cached_positions": wl.n_cached,
                    "tokens_per_step": n_tok, "parallelism": "single GPU, one workgroup per CU"},
@@ -270,7 +270,7 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     from tile_scheduled_persistent_amd import tiles
 
     plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits, attn_heads=args.attn_heads,
-                      combine_mode=args.combine_mode, o_placement=args.o_placement)
+                      combine_mode=args.combine_mode, o_placement=args.o_placement, weight_format=wl.weights)
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
     plan.decode(kv, token, wl.n_steps, out_t, None)

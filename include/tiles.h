@@ -79,7 +79,15 @@ typedef struct tiles_config {
   int32_t o_placement;    /* workers of the o_proj tiles: 0 planner choice (all), 1 all workers, 2 those
                              without an attention tile, when there are any and the splits merge in the
                              o_proj prologue */
+  int32_t weight_format;  /* TILES_WEIGHTS_BF16, or TILES_WEIGHTS_INT8: every linear layer (Wq, Wk, Wv, Wo,
+                             W_gate, W_up, W_down and the LM head) packed as symmetric per-row INT8
+                             codes with one FP32 scale per row, quantized from the BF16 weights at plan
+                             creation (see tiles_quantize_rows_int8) and dequantized in registers; the
+                             norm gains and the embedding lookup stay BF16 */
 } tiles_config_t;
+
+#define TILES_WEIGHTS_BF16 0
+#define TILES_WEIGHTS_INT8 1
 
 /* Per-layer weights, BF16, row-major [out, in]:
  *   attn_norm, mlp_norm [H]; q_norm, k_norm [head_dim] (only read when qk_norm);
@@ -128,6 +136,7 @@ typedef struct tiles_plan_info {
   uint64_t build_id;          /* worker-kernel build id the plan was made for */
   int32_t attn_heads;         /* query heads per attention tile */
   int32_t o_workers;          /* workers holding o_proj tiles (all, or those without an attention tile) */
+  int32_t weight_format;      /* TILES_WEIGHTS_BF16 or TILES_WEIGHTS_INT8 */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */
@@ -243,6 +252,14 @@ int tiles_plan_debug_corrupt_device(tiles_plan_t *plan);
  * checks its watchdog every round (one query head per attention tile only: TILES_E_CONFIG
  * otherwise).  Host only (plus an occupancy query of that instantiation). */
 int tiles_plan_debug_spin_limit(tiles_plan_t *plan, uint32_t rounds);
+
+/* The weight-only INT8 quantizer plan creation applies to every linear layer ("History and roadmap"
+ * (TileInfer.jl), "M8 so far" table: weight-only INT8 linear layers; per-row scales, as group-wise
+ * scales were not tried there): for each of `rows` rows of `cols` BF16 values (host memory, row-major),
+ * s = max |w| / 127 and q = round-half-even(w / s) clamped to [-127, 127], each operation in IEEE FP32;
+ * a row of zeros gets s = 0 and q = 0.  q: host int8 [rows][cols]; scales: host float [rows].  Host
+ * only (no GPU).  Errors: TILES_E_ARG for a null pointer or a negative size. */
+int tiles_quantize_rows_int8(const uint16_t *bf16, int64_t rows, int64_t cols, int8_t *q, float *scales);
 
 /* Measurement helper, not part of the decode path: the stream-read ceiling against which the
  * decode kernel's HBM rate is compared ("History and roadmap" page, "Where it stands": decode

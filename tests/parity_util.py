@@ -31,8 +31,9 @@ class Setup:
     views for the oracle.  `gen_device` is where the generators run."""
 
     def __init__(self, m, capacity: int, n_cached: int, key_scale: bool = False, gen_device: str = "cpu",
-                 widen_once: bool = True):
+                 widen_once: bool = True, weights: str = "bf16"):
         self.m = m
+        self.weights = weights  # "int8": weight-only INT8 linear layers on both sides
         self.capacity = capacity
         self.n_cached = n_cached
         w = synth.make_weights(m, device=gen_device)
@@ -54,14 +55,15 @@ class Setup:
 
     def oracle(self) -> OracleModel:
         if self._oracle is None:
-            self._oracle = OracleModel(self.m, self.w_bits, np.float32, widen_once=self.widen_once)
+            self._oracle = OracleModel(self.m, self.w_bits, np.float32, widen_once=self.widen_once,
+                                       weight_format=self.weights)
         return self._oracle
 
     def oracle_kv(self):
         return {"k": self.kv_bits["k"].copy(), "v": self.kv_bits["v"].copy()}
 
     def plan(self, flags=tiles.TILES_DEBUG_HIDDEN, **kw) -> tiles.Plan:
-        return tiles.Plan(self.m, self.w_dev, self.capacity, flags=flags, **kw)
+        return tiles.Plan(self.m, self.w_dev, self.capacity, flags=flags, weight_format=self.weights, **kw)
 
 
 def run_gpu(plan: tiles.Plan, kv: tiles.KVCache, token: int, n: int, want_hidden=True):

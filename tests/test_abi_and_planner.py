@@ -198,3 +198,49 @@ def test_validator_rejects_planted_mistake(mutation, message):
 def test_validator_mutation_hook_arguments():
     assert tiles.debug_validate(TINY, 64, 99) == tiles.TILES_E_ARG
     assert tiles.lib().tiles_plan_debug_validate(None, 256, 0) == tiles.TILES_E_ARG
+
+
+# ---------------------------------------------------------------------------
+# weight-only INT8: the library's quantizer gives the oracle's codes and scales bit for bit, and
+# INT8 plans build, validate and stream the bytes the workload definition counts
+# ---------------------------------------------------------------------------
+
+def test_library_int8_quantizer_matches_the_oracle_bit_for_bit():
+    import numpy as np
+    import torch
+
+    from oracle import quantize_rows_int8 as oracle_quantize
+    rng = np.random.default_rng(21)
+    rows = [rng.standard_normal((200, 333)) * (10.0 ** rng.integers(-8, 6, 200))[:, None],
+            np.zeros((3, 333)),                                       # rows of zeros
+            np.full((2, 333), 2.5 * 2 ** -7), ]                      # ties: W / s = 127 and 2.5 (after the max)
+    rows[2][:, 0] = 127 / 128
+    w32 = np.concatenate(rows).astype(np.float32)
+    bits = torch.from_numpy(w32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bits[5, 7] = 0x0001  # a subnormal BF16
+    bits[6, 9] = 0x8000  # -0
+    q_lib, s_lib = tiles.quantize_rows_int8(bits)
+    q_orc, s_orc = oracle_quantize(bits)
+    assert np.array_equal(s_lib.view(np.uint32), s_orc.view(np.uint32))
+    assert np.array_equal(q_lib, q_orc)
+    assert q_lib[-1, 1] == 2 and q_lib[-1, 0] == 127
+    assert tiles.lib().tiles_quantize_rows_int8(None, 1, 1, None, None) == tiles.TILES_E_ARG
+
+
+@pytest.mark.parametrize("key", ["llama1b_int8", "qwen06b_int8", "qwen4b_int8"])
+def test_int8_plans_validate_and_count_the_workload_bytes(key):
+    wl = WORKLOADS[key]
+    info = tiles.dry_run(wl.model, wl.capacity, weights="int8")
+    assert info.weight_format == 1
+    assert info.weight_bytes_per_step == wl.model.int8_weight_bytes_per_token()
+    assert tiles.debug_validate(wl.model, wl.capacity, 0, weights="int8") == tiles.TILES_OK, tiles.last_error()
+    bf = tiles.dry_run(wl.model, wl.capacity)
+    assert bf.weight_format == 0 and bf.weight_bytes_per_step == wl.model.weight_bytes_per_token()
+
+
+def test_int8_plan_of_ragged_and_untied_shapes():
+    m = scaled(TINY, name="ragged-untied", n_layers=3, hidden=384, n_heads=6, n_kv_heads=2, ffn=1000, vocab=1000,
+               tie_embeddings=False)
+    assert tiles.debug_validate(m, 64, 0, weights="int8") == tiles.TILES_OK, tiles.last_error()
+    for mutation in (12, 13):  # packed rows exchanged, a packing copy dropped
+        assert tiles.debug_validate(m, 64, mutation, weights="int8") == tiles.TILES_E_PLAN

@@ -266,7 +266,7 @@ def test_corrupted_device_schedule_is_detected_in_the_launch():
 # full-size workloads: the launch bench.py times (one launch of all steps)
 # ---------------------------------------------------------------------------
 
-FULL = ["llama1b", "qwen06b", "qwen4b", "qwen4b_32k"]
+FULL = ["llama1b", "qwen06b", "qwen4b", "qwen4b_32k", "llama1b_int8"]
 
 
 @pytest.mark.slow
@@ -280,7 +280,7 @@ def test_full_size_workload_every_step(key):
     wl = WORKLOADS[key]
     m = wl.model
     n = wl.n_steps
-    s = Setup(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda")
+    s = Setup(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda", weights=wl.weights)
     tok = synth.make_tokens(m, 1)[0]
     kv_timed = s.fresh_kv()
     with s.plan(flags=0) as plan:
@@ -432,3 +432,50 @@ def test_trace_is_bit_neutral_and_its_stamps_are_ordered():
     first_cw_done = tr[..., 4]
     has = first_cw_done != 0
     assert (first_cw_done[has] >= staged[has]).all() and (first_cw_done[has] <= published[has]).all()
+
+
+# ---------------------------------------------------------------------------
+# weight-only INT8 linear layers: the GPU's INT8 tiles against the oracle's INT8 model
+# ---------------------------------------------------------------------------
+
+def test_int8_tiny_every_step_against_oracle():
+    wl = WORKLOADS["tiny"]
+    s = Setup(TINY, wl.capacity, 0, weights="int8")
+    prompt = synth.make_tokens(TINY, wl.prompt_len)
+    with s.plan() as plan:
+        assert plan.info().weight_format == 1
+        _oracle_forced(s, prompt, wl.prompt_len + wl.n_steps, plan, tag="tiny int8")
+
+
+def test_int8_ragged_untied_padding():
+    # hidden 384 and ffn 1000 pad to 1024-column INT8 chunks; an untied head of its own
+    m = scaled(RAGGED, name="ragged-untied", tie_embeddings=False)
+    s = Setup(m, 64, 37, weights="int8")
+    toks = synth.make_tokens(m, 1)
+    with s.plan() as plan:
+        _oracle_forced(s, toks, 10, plan, tag="ragged int8")
+
+
+def test_int8_wide_layers_and_qk_norm():
+    s = Setup(WIDE, 96, 70, weights="int8")
+    with s.plan() as plan:
+        _oracle_forced(s, synth.make_tokens(WIDE, 1), 6, plan, tag="wide int8")
+    s = Setup(QK128, 64, 29, weights="int8")
+    with s.plan(attn_heads=2) as plan:
+        _oracle_forced(s, synth.make_tokens(QK128, 1), 8, plan, tag="qk128 int8")
+
+
+def test_int8_repeatable_and_chunk_invariant():
+    s = Setup(WIDE, 96, 70, weights="int8")
+    tok = synth.make_tokens(WIDE, 1)[0]
+    a = _full_run(s, tok, 10)
+    b = _full_run(s, tok, 10)
+    _bits_equal(a, b)
+    kv = s.fresh_kv()
+    with s.plan() as plan:
+        t = tok
+        for i in range(10):
+            t1, l1, h1 = run_gpu(plan, kv, t, 1)
+            assert int(t1[0]) == int(a[0][i])
+            assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
+            t = int(t1[0])

@@ -52,6 +52,18 @@ class ModelConfig:
     def weight_bytes_per_token(self) -> int:
         return 2 * self.param_count()
 
+    def linear_rows(self) -> int:
+        """Output rows of every linear layer (the LM head included): one INT8 scale each."""
+        return self.n_layers * (self.q_rows + 2 * self.kv_rows + self.hidden + 2 * self.ffn + self.hidden) + self.vocab
+
+    def int8_weight_bytes_per_token(self) -> int:
+        """Weight-only INT8: one byte per linear weight, one FP32 scale per linear row, and the BF16
+        norm gains and embedding row."""
+        H, F, V = self.hidden, self.ffn, self.vocab
+        linear = self.n_layers * (H * (self.q_rows + 2 * self.kv_rows) + self.q_rows * H + 3 * H * F) + V * H
+        gains = self.n_layers * (2 * H + (2 * self.head_dim if self.qk_norm else 0)) + H
+        return linear + 4 * self.linear_rows() + 2 * gains + 2 * H
+
     def kv_bytes_per_position(self) -> int:
         """K and V bytes of one position over all layers (BF16)."""
         return 2 * 2 * self.n_layers * self.n_kv_heads * self.head_dim
@@ -68,6 +80,7 @@ class Workload:
     prompt_len: int = 0          # >0: prefill that many prompt tokens one step at a time
     key_scale: bool = False      # per-(layer, kv head, channel) key scales ~ U(0.5, 4)
     description: str = ""
+    weights: str = "bf16"        # "int8": weight-only INT8 linear layers (per-row codes and scales)
 
     @property
     def capacity(self) -> int:
@@ -82,8 +95,8 @@ class Workload:
         """Algorithmic HBM bytes per decoded token: weights read once, K/V of
         every attended position read once, one K/V position written."""
         m = self.model
-        return (m.weight_bytes_per_token() + m.kv_bytes_per_position() * self.avg_attended()
-                + m.kv_bytes_per_position())
+        wb = m.int8_weight_bytes_per_token() if self.weights == "int8" else m.weight_bytes_per_token()
+        return wb + m.kv_bytes_per_position() * self.avg_attended() + m.kv_bytes_per_position()
 
 
 TINY = ModelConfig("tiny", 2, 256, 4, 2, 64, 1024, 4096, 1e4, 1e-5, False)
@@ -104,6 +117,16 @@ WORKLOADS: Dict[str, Workload] = {
     "qwen4b_32k": Workload("qwen4b_32k", QWEN3_4B, 32767, 32, key_scale=True,
                            description="Qwen3-4B-shaped decode, 32 tokens after 32767 cached positions, "
                                        "per-channel key scales"),
+    # weight-only INT8 linear layers (the roadmap page's "M8 so far" row), same shapes and inputs
+    "llama1b_int8": Workload("llama1b_int8", LLAMA_1B, 1023, 64, weights="int8",
+                             description="Llama-3.2-1B-shaped decode with weight-only INT8 linear layers, "
+                                         "64 tokens after 1023 cached positions"),
+    "qwen06b_int8": Workload("qwen06b_int8", QWEN3_06B, 1023, 64, weights="int8",
+                             description="Qwen3-0.6B-shaped decode with weight-only INT8 linear layers, "
+                                         "64 tokens after 1023 cached positions"),
+    "qwen4b_int8": Workload("qwen4b_int8", QWEN3_4B, 1023, 64, weights="int8",
+                            description="Qwen3-4B-shaped decode with weight-only INT8 linear layers, "
+                                        "64 tokens after 1023 cached positions"),
 }
 
 

@@ -10,8 +10,12 @@
 // against its own compiled-in build id.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
+#include <mutex>
+#include <thread>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -26,7 +30,7 @@
 #endif
 
 namespace tiles {
-const void* worker_kernel(int head_dim, int group, bool short_watchdog);
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
@@ -138,6 +142,64 @@ void release(tiles_plan* p) {
   delete p;
 }
 
+// Weight-only INT8 plans: the packed image (INT8 codes and scales of every linear layer, BF16 gains
+// and embedding rows) is built on the host -- device-resident sources are read back one copy
+// segment at a time -- by a few threads over disjoint segments, and uploaded in one copy.
+int pack_int8_on_host(tiles_plan* p, const tiles_weights_t* w) {
+  const HostPlan& hp = p->hp;
+  std::vector<uint8_t> img((size_t)hp.packed_bytes, 0);
+  std::atomic<size_t> next{0};
+  std::atomic<int> failed{0};
+  std::string first_err;
+  std::mutex err_mu;
+  int dev = p->device;
+  auto work = [&]() {
+    if (w->on_device && hipSetDevice(dev) != hipSuccess) {
+      failed = 1;
+      return;
+    }
+    std::vector<uint16_t> tmp;
+    for (size_t i = next++; i < hp.copies.size() && !failed; i = next++) {
+      const CopySeg& c = hp.copies[i];
+      const uint8_t* src = static_cast<const uint8_t*>(src_ptr(w, c.tensor, c.layer));
+      if (!src) {
+        std::lock_guard<std::mutex> g(err_mu);
+        first_err = "missing weight tensor for packing";
+        failed = 1;
+        return;
+      }
+      src += c.src_row * c.cols * 2;
+      const uint16_t* rows = reinterpret_cast<const uint16_t*>(src);
+      if (w->on_device) {
+        tmp.resize((size_t)(c.nrows * c.cols));
+        const hipError_t e = hipMemcpy(tmp.data(), src, (size_t)(c.nrows * c.cols * 2), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) {
+          std::lock_guard<std::mutex> g(err_mu);
+          first_err = std::string("reading back weights: ") + hipGetErrorString(e);
+          failed = 1;
+          return;
+        }
+        rows = tmp.data();
+      }
+      if (c.scale_off >= 0) {
+        quantize_rows_int8(rows, c.cols, c.nrows, c.cols, reinterpret_cast<int8_t*>(img.data() + c.dst_off), c.dst_pitch,
+                           reinterpret_cast<float*>(img.data() + c.scale_off), c.scale_pitch / 4);
+      } else {
+        for (int64_t r = 0; r < c.nrows; ++r)
+          std::memcpy(img.data() + c.dst_off + r * c.dst_pitch, rows + r * c.cols, (size_t)(c.cols * 2));
+      }
+    }
+  };
+  const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::vector<std::thread> threads;
+  for (unsigned t = 0; t < nt; ++t) threads.emplace_back(work);
+  for (auto& t : threads) t.join();
+  if (failed) return set_err(first_err.empty() ? TILES_E_HIP : TILES_E_ARG, first_err.empty() ? "packing failed" : first_err);
+  HIP_TRY(hipSetDevice(dev));
+  HIP_TRY(hipMemcpy(p->packed, img.data(), (size_t)hp.packed_bytes, hipMemcpyHostToDevice));
+  return TILES_OK;
+}
+
 int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan** out) {
   *out = nullptr;
   if (!cfg || !w) return set_err(TILES_E_ARG, "null config or weights");
@@ -169,7 +231,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.T, false);
+  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -198,7 +260,13 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   // packed weights
   TRY(hipMalloc(&p->packed, hp.packed_bytes));
   TRY(hipMemsetAsync(p->packed, 0, hp.packed_bytes, p->stream));
-  if (w->on_device) {
+  if (hp.q8) {
+    rc = pack_int8_on_host(p, w);
+    if (rc != TILES_OK) {
+      release(p);
+      return rc;
+    }
+  } else if (w->on_device) {
     // device-resident sources: one packing kernel for every segment
     std::vector<PackSeg> segs;
     segs.reserve(hp.copies.size());
@@ -447,6 +515,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->kv_splits = hp.S;
   info->combine_mode = hp.combine_in_o ? 1 : 2;
   info->attn_heads = hp.T;
+  info->weight_format = hp.q8 ? TILES_WEIGHTS_INT8 : TILES_WEIGHTS_BF16;
   for (size_t wv = 0; wv < hp.waves.size(); ++wv)
     if (hp.waves[wv].kind == KIND_O) {
       info->o_workers = hp.wave_busy[wv];
@@ -545,8 +614,8 @@ int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   const uint32_t limit = rounds ? rounds : DEFAULT_SPIN_LIMIT;
   if (limit < 32 && !p->kernel_wd) {
-    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true);
-    if (!k) return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs one query head per attention tile");
+    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0);
+    if (!k) return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and one query head per attention tile");
     HIP_TRY(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p->hp.lds_bytes));
     int occ = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, BLOCK_THREADS, p->hp.lds_bytes));
@@ -575,6 +644,13 @@ int tiles_plan_debug_corrupt_device(tiles_plan_t* p) {
   HIP_TRY(hipMemcpy(&v, byte, 1, hipMemcpyDeviceToHost));
   v ^= 0x04;
   HIP_TRY(hipMemcpy(byte, &v, 1, hipMemcpyHostToDevice));
+  return TILES_OK;
+}
+
+int tiles_quantize_rows_int8(const uint16_t* bf16, int64_t rows, int64_t cols, int8_t* q, float* scales) {
+  if (!bf16 || !q || !scales) return set_err(TILES_E_ARG, "null pointer");
+  if (rows < 0 || cols < 0) return set_err(TILES_E_ARG, "negative size");
+  quantize_rows_int8(bf16, cols, rows, cols, q, cols, scales, 1);
   return TILES_OK;
 }
 

@@ -199,6 +199,7 @@ struct Lds {
   float* vec;
   float* part;
   float* xres;
+  float* scl;           // weight-only INT8: the scales of the rows of the GEMV block being worked
   float* stage;
   float* small;
   SegDesc* segs;
@@ -491,6 +492,38 @@ __device__ __forceinline__ float dot8(const u32x4 w, const float* v) {
   return s0 + s1;
 }
 
+// 16 INT8 codes (one 16-byte load, weight-only INT8 tiles) times 16 FP32 inputs: the codes are
+// converted in registers and the row's scale is applied once to the row's total (by the control
+// wavefront).
+__device__ __forceinline__ float i8(uint32_t x, int k) { return (float)(int8_t)(uint8_t)(x >> (8 * k)); }
+__device__ __forceinline__ float dot16_i8(const u32x4 w, const float* v) {
+  const f32x4 v0 = *reinterpret_cast<const f32x4*>(v);
+  const f32x4 v1 = *reinterpret_cast<const f32x4*>(v + 4);
+  const f32x4 v2 = *reinterpret_cast<const f32x4*>(v + 8);
+  const f32x4 v3 = *reinterpret_cast<const f32x4*>(v + 12);
+  float s0 = i8(w.x, 0) * v0.x;
+  float s1 = i8(w.x, 1) * v0.y;
+  s0 = fmaf(i8(w.x, 2), v0.z, s0);
+  s1 = fmaf(i8(w.x, 3), v0.w, s1);
+  s0 = fmaf(i8(w.y, 0), v1.x, s0);
+  s1 = fmaf(i8(w.y, 1), v1.y, s1);
+  s0 = fmaf(i8(w.y, 2), v1.z, s0);
+  s1 = fmaf(i8(w.y, 3), v1.w, s1);
+  s0 = fmaf(i8(w.z, 0), v2.x, s0);
+  s1 = fmaf(i8(w.z, 1), v2.y, s1);
+  s0 = fmaf(i8(w.z, 2), v2.z, s0);
+  s1 = fmaf(i8(w.z, 3), v2.w, s1);
+  s0 = fmaf(i8(w.w, 0), v3.x, s0);
+  s1 = fmaf(i8(w.w, 1), v3.y, s1);
+  s0 = fmaf(i8(w.w, 2), v3.z, s0);
+  s1 = fmaf(i8(w.w, 3), v3.w, s1);
+  return s0 + s1;
+}
+
+// Columns of one packed chunk: 512 BF16 weights, or 1024 INT8 codes.
+template <bool Q8>
+constexpr int chunk_cols() { return Q8 ? CHUNK_COLS_I8 : CHUNK_COLS; }
+
 // Chunk range [i, ihi) of compute wave c in block r0 of a GEMV segment.
 struct Range {
   int k;         // schedule wave (-1: none)
@@ -649,20 +682,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Consume chunks [r.i, r.ihi) in batches; st holds batches 0 .. NB - 1 when `have` (else they
 // are loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the
 // last NB batches fetch next_src(0) .. next_src(NB - 1) into the NB register sets.
-template <int B, int NB, typename NextSrc>
+// Q8: the chunks hold INT8 codes (16 per lane, 1024 columns) instead of BF16 weights (8, 512).
+template <int B, int NB, bool Q8, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
                                              Stream<B, NB>& st, bool have, NextSrc next_src, const float* stage,
                                              uint64_t* ts) {
+  constexpr int VPL = Q8 ? 16 : 8;            // input values per lane per chunk
+  constexpr int CC = chunk_cols<Q8>();
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
   float acc = 0.f;
-  const float* vlane = L.vec + lane * 8;
+  const float* vlane = L.vec + lane * VPL;
   // Every slot is consumed (a slot past the range contributes zero and does not advance the
   // row), so no branch sits between a load and the use of its registers.
   auto consume = [&](const u32x4& w, bool valid, const float* xv) {
-    const float d = dot8(w, xv);
+    const float d = Q8 ? dot16_i8(w, xv) : dot8(w, xv);
     acc += valid ? d : 0.f;
     seg += valid ? 1 : 0;
     if (seg == C) {
@@ -677,14 +713,16 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   // so their latencies overlap (the row-end branches would otherwise serialise them).  A slot
   // past the range reads a slice too (in bounds, masked).
   auto consume_batch = [&](const u32x4* w, int jb) {
-    float xv[B][8];
+    float xv[B][VPL];
     int s = seg;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const f32x4* px = reinterpret_cast<const f32x4*>(vlane + s * CHUNK_COLS);
-      const f32x4 x0 = px[0], x1 = px[1];
-      xv[u][0] = x0.x; xv[u][1] = x0.y; xv[u][2] = x0.z; xv[u][3] = x0.w;
-      xv[u][4] = x1.x; xv[u][5] = x1.y; xv[u][6] = x1.z; xv[u][7] = x1.w;
+      const f32x4* px = reinterpret_cast<const f32x4*>(vlane + s * CC);
+#pragma unroll
+      for (int q = 0; q < VPL / 4; ++q) {
+        const f32x4 x = px[q];
+        xv[u][4 * q] = x.x; xv[u][4 * q + 1] = x.y; xv[u][4 * q + 2] = x.z; xv[u][4 * q + 3] = x.w;
+      }
       s = s + 1 == C ? 0 : s + 1;
     }
 #pragma unroll
@@ -1379,7 +1417,33 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
 // control wave loop
 // ---------------------------------------------------------------------------
 
-template <int HD, int G, bool WD>
+// (weight-only INT8) The scales of rows [r0, r0 + block) of GEMV tile t, this lane's share (row
+// lane + 64 i in register i): loaded into registers before the tile's input gather, so that they
+// arrive while it waits, and put into LDS after it for the epilogue.
+constexpr int SCALE_REGS = MAX_BLOCK_ROWS / 64;
+__device__ __forceinline__ int tile_rows(const TileDesc& t) { return t.kind == KIND_GU ? 2 * t.nrows : t.nrows; }
+__device__ __forceinline__ void load_scales(const KernelArgs& a, const TileDesc& t, int r0, int block_rows, int lane,
+                                            float* sreg) {
+  const int rows = tile_rows(t);
+  const int nr = min(block_rows, rows - r0);
+  const float* sp = reinterpret_cast<const float*>(a.packed + t.woff + (int64_t)rows * t.kpad) + r0;
+#pragma unroll
+  for (int i = 0; i < SCALE_REGS; ++i) {
+    const int r = lane + 64 * i;
+    sreg[i] = r < nr ? sp[r] : 0.f;
+  }
+}
+__device__ __forceinline__ void put_scales(const Lds& L, const TileDesc& t, int r0, int block_rows, int lane,
+                                           const float* sreg) {
+  const int nr = min(block_rows, tile_rows(t) - r0);
+#pragma unroll
+  for (int i = 0; i < SCALE_REGS; ++i) {
+    const int r = lane + 64 * i;
+    if (r < nr) L.scl[r] = sreg[i];
+  }
+}
+
+template <int HD, int G, bool WD, bool Q8>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1406,7 +1470,14 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* wds = reinterpret_cast<const uint64_t*>(L.small + SM_WDONE) + (k & 1) * 8;
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
+      float sreg[SCALE_REGS];
+      if constexpr (Q8) {
+        if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
+      }
       if (gather_inputs<HD, G, true, WD>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if constexpr (Q8) {
+        if (is_gemv(t.kind)) put_scales(L, t, 0, block_rows, lane, sreg);
+      }
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1418,9 +1489,20 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
         const int rows = t.kind == KIND_GU ? 2 * t.nrows : t.nrows;
-        const int C = t.kpad / CHUNK_COLS;
+        const int C = t.kpad / chunk_cols<Q8>();
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const int nr = min(block_rows, rows - r0);
+          // a row's total over the compute wavefronts' partials, times its scale in an INT8 tile
+          auto total = [&](int r) {
+            const float x = row_total(L, nr, C, r);
+            return Q8 ? L.scl[r] * x : x;
+          };
+          if constexpr (Q8) {
+            if (r0 > 0) {  // a later block's scales (a tile of more rows than one block holds)
+              load_scales(a, t, r0, block_rows, lane, sreg);
+              put_scales(L, t, r0, block_rows, lane, sreg);
+            }
+          }
           __syncthreads();  // B: partials of this block ready
           if (a.trace && r0 == 0) {
             t_cmp = wall_clock64();
@@ -1429,32 +1511,32 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           }
           switch (t.kind) {
             case KIND_QKV:
-              for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * row_total(L, nr, C, r), par);
+              for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * total(r), par);
               break;
             case KIND_O:
               for (int r = lane; r < nr; r += 64) {
                 const int j = t.row0 + r0 + r;
-                publish(out, j, L.xres[j] + row_total(L, nr, C, r), par);
+                publish(out, j, L.xres[j] + total(r), par);
               }
               break;
             case KIND_GU:  // interleaved gate/up rows
               for (int p = lane; p < nr / 2; p += 64) {
-                const float gt = rs * row_total(L, nr, C, 2 * p);
-                const float up = rs * row_total(L, nr, C, 2 * p + 1);
+                const float gt = rs * total(2 * p);
+                const float up = rs * total(2 * p + 1);
                 publish(out, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
               }
               break;
             case KIND_DOWN:
               for (int r = lane; r < nr; r += 64) {
                 const int j = t.row0 + r0 + r;
-                const float nx = L.xres[j] + row_total(L, nr, C, r);
+                const float nx = L.xres[j] + total(r);
                 publish(out, j, nx, par);
                 if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = tag_clear(nx);
               }
               break;
             case KIND_LM:
               for (int r = lane; r < nr; r += 64) {
-                const float v = rs * row_total(L, nr, C, r);
+                const float v = rs * total(r);
                 const int idx = t.row0 + r0 + r;
                 if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
                 if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
@@ -1538,7 +1620,7 @@ constexpr int stream_sets() {
   return 2;
 }
 
-template <int HD, int G, bool WD>
+template <int HD, int G, bool WD, bool Q8>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
@@ -1640,7 +1722,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                              : next_attn ? no_range()
                                          : ng;
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
-            stream_range<B, NB>(
+            stream_range<B, NB, Q8>(
                 L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
                 [&](int h) { return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
                 stage_w, r0 == 0 ? ts : nullptr);
@@ -1671,7 +1753,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int HD, int G, bool WD>
+// Q8: weight-only INT8 GEMV tiles (INT8 codes, per-row FP32 scales); else BF16 weights.
+template <int HD, int G, bool WD, bool Q8>
 __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
@@ -1680,6 +1763,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   L.vec = L.stage + a.lds_stage_floats;
   L.part = L.vec + a.lds_vec_floats;
   L.xres = L.part + a.lds_part_floats;
+  L.scl = L.xres + (Q8 ? a.lds_xres_floats - MAX_BLOCK_ROWS : 0);  // (INT8 plans reserve a block's scales there)
   L.small = L.xres + a.lds_xres_floats;
   L.segs = reinterpret_cast<SegDesc*>(L.small + SMALL_FLOATS);
   L.tiles = reinterpret_cast<TileDesc*>(L.segs + a.n_waves);
@@ -1691,7 +1775,7 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
     const TileDesc t = a.tiles[(int64_t)k * a.W + bid];
     SegDesc s;
     s.woff = t.woff;
-    s.chunks_per_row = t.kpad / CHUNK_COLS;
+    s.chunks_per_row = t.kpad / chunk_cols<Q8>();
     s.rows = is_gemv(t.kind) ? (t.kind == KIND_GU ? 2 * t.nrows : t.nrows) : 0;
     L.segs[k] = s;
     L.tiles[k] = t;
@@ -1723,8 +1807,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   __syncthreads();
   if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G, WD>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G, WD>(a, L, bid, wave, lane, block_rows);
+  if (wave == 0) control_loop<HD, G, WD, Q8>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G, WD, Q8>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -1888,31 +1972,37 @@ hipError_t noalloc_scratch(int device, uint32_t** out) {
 // host-visible handles of the instantiations
 // ---------------------------------------------------------------------------
 
-// The worker for a head size and query heads per attention tile; `short_watchdog` selects the test
-// instantiation whose waits check their watchdog every polling round (one query head per tile only).
-const void* worker_kernel(int head_dim, int group, bool short_watchdog) {
-  if (short_watchdog) {
-    if (group != 1) return nullptr;
-    if (head_dim == 64) return reinterpret_cast<const void*>(&tiles_worker<64, 1, true>);
-    if (head_dim == 128) return reinterpret_cast<const void*>(&tiles_worker<128, 1, true>);
-    return nullptr;
-  }
+// The worker for a head size, query heads per attention tile and weight format; `short_watchdog`
+// selects the test instantiation whose waits check their watchdog every polling round (BF16, one
+// query head per tile only).
+template <bool Q8>
+const void* worker_for(int head_dim, int group) {
   if (head_dim == 64) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false, Q8>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false, Q8>);
     }
   } else if (head_dim == 128) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false, Q8>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false, Q8>);
     }
   }
   return nullptr;
+}
+
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8) {
+  if (short_watchdog) {
+    if (group != 1 || q8) return nullptr;
+    if (head_dim == 64) return reinterpret_cast<const void*>(&tiles_worker<64, 1, true, false>);
+    if (head_dim == 128) return reinterpret_cast<const void*>(&tiles_worker<128, 1, true, false>);
+    return nullptr;
+  }
+  return q8 ? worker_for<true>(head_dim, group) : worker_for<false>(head_dim, group);
 }
 
 }  // namespace tiles

@@ -25,6 +25,10 @@ enum : int32_t {
 // columns of one row.  Every GEMV row is padded to a multiple of CHUNK_COLS.
 constexpr int CHUNK_COLS = 512;
 constexpr int CHUNK_BYTES = 1024;
+// Weight-only INT8 plans pack every linear layer as signed 8-bit codes, 1024 columns per chunk, each
+// tile's rows followed by their FP32 scales (one per row, padded to a whole chunk).
+constexpr int CHUNK_COLS_I8 = 1024;
+enum : int32_t { WEIGHTS_BF16 = 0, WEIGHTS_INT8 = 1 };
 constexpr int XCDS = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2; workgroup i runs on XCD i % 8
 constexpr int BLOCK_THREADS = 512;
 constexpr int NWAVES = BLOCK_THREADS / 64;
@@ -55,7 +59,7 @@ struct TileDesc {   // 32 bytes
   int32_t kind;
   int32_t row0;     // GEMV: first output row (GU: first j). ATTN: KV head. COMBINE: query head.
   int32_t nrows;    // GEMV: output rows (GU: number of j; the tile holds 2*nrows rows, gate/up interleaved). ATTN: split.
-  int32_t kpad;     // GEMV: packed columns per row (multiple of CHUNK_COLS)
+  int32_t kpad;     // GEMV: packed columns per row (a multiple of the plan's columns per chunk)
   int64_t woff;     // GEMV: byte offset of the tile's first packed row
   int32_t aux0;     // reserved
   int32_t aux1;     // reserved

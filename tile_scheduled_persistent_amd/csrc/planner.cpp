@@ -20,6 +20,7 @@
 #include <cstring>
 #include <map>
 #include <sstream>
+#include <tuple>
 #include <unordered_map>
 
 namespace tiles {
@@ -71,6 +72,29 @@ int32_t choose_splits(const Shape& s, int32_t W) {
 
 }  // namespace
 
+void quantize_rows_int8(const uint16_t* src, int64_t src_pitch, int64_t rows, int64_t cols, int8_t* q,
+                        int64_t q_pitch, float* scales, int64_t scale_pitch_floats) {
+  auto widen = [](uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  };
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* w = src + r * src_pitch;
+    float amax = 0.0f;
+    for (int64_t j = 0; j < cols; ++j) amax = std::max(amax, std::fabs(widen(w[j])));
+    const float sc = amax / 127.0f;  // IEEE FP32 division
+    int8_t* qr = q + r * q_pitch;
+    for (int64_t j = 0; j < cols; ++j) {
+      float v = sc > 0.0f ? std::nearbyint(widen(w[j]) / sc) : 0.0f;  // round half to even (default mode)
+      v = std::min(127.0f, std::max(-127.0f, v));
+      qr[j] = (int8_t)v;
+    }
+    scales[r * scale_pitch_floats] = sc;
+  }
+}
+
 uint64_t plan_checksum(const HostPlan& p) {
   // 64-bit words mixed with a multiply-xorshift step (FNV-style); fast enough to run before every launch.
   uint64_t h = 1469598103934665603ull;
@@ -93,7 +117,7 @@ uint64_t plan_checksum(const HostPlan& p) {
   };
   const Shape& s = p.s;
   const int64_t dims[] = {s.n_layers, s.H, s.n_heads, s.n_kv, s.hd, s.F, s.V, s.G, s.qkv_rows, s.Hpad, s.Qpad, s.Fpad,
-                          s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o, p.T,
+                          s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o, p.T, p.q8, p.wb,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
                           p.stage_batches};
@@ -154,9 +178,16 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.W = n_workers;
   const int32_t W = n_workers;
   s.qkv_rows = (s.n_heads + 2 * s.n_kv) * s.hd;
-  s.Hpad = (int32_t)round_up(s.H, CHUNK_COLS);
-  s.Qpad = (int32_t)round_up((int64_t)s.n_heads * s.hd, CHUNK_COLS);
-  s.Fpad = (int32_t)round_up(s.F, CHUNK_COLS);
+  // weight format: BF16, or weight-only INT8 (every linear layer as per-row INT8 codes + FP32 scales)
+  if (cfg.weight_format != WEIGHTS_BF16 && cfg.weight_format != WEIGHTS_INT8)
+    return fail(err, TILES_E_CONFIG, "weight_format must be 0 (BF16) or 1 (INT8)");
+  p.q8 = cfg.weight_format == WEIGHTS_INT8;
+  p.wb = p.q8 ? 1 : 2;
+  const int32_t ccols = CHUNK_BYTES / p.wb;  // columns per packed chunk
+  s.Hpad = (int32_t)round_up(s.H, ccols);
+  s.Qpad = (int32_t)round_up((int64_t)s.n_heads * s.hd, ccols);
+  s.Fpad = (int32_t)round_up(s.F, ccols);
+  const int64_t wb = p.wb;
 
   // split-KV and combine placement
   p.S = cfg.kv_splits > 0 ? cfg.kv_splits : choose_splits(s, W);
@@ -247,10 +278,11 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
       seg(lo, hi, off);
       const int64_t rows = (hi - lo) * rows_per_out;
       max_rows = std::max<int32_t>(max_rows, (int32_t)rows);
-      off += rows * kpad * 2;
+      off += tile_packed_bytes(p, t);
     }
     p.waves[wv].max_rows = max_rows;
-    wbytes += R * rows_per_out * (int64_t)K * 2;
+    // algorithmic bytes: the weights (and, INT8, one FP32 scale per row)
+    wbytes += R * rows_per_out * ((int64_t)K * wb + (p.q8 ? 4 : 0));
     return wv;
   };
 
@@ -288,9 +320,12 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
     gemv_wave(KIND_QKV, l, s.qkv_rows, s.H, s.Hpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
       const int64_t bounds[4] = {0, qr, qr + kr, qr + 2 * kr};
       const int32_t src[3] = {SRC_WQ, SRC_WK, SRC_WV};
+      const int64_t scl = dst + (hi - lo) * s.Hpad * wb;
       for (int m = 0; m < 3; ++m) {
         int64_t a = std::max(lo, bounds[m]), b = std::min(hi, bounds[m + 1]);
-        if (b > a) p.copies.push_back({src[m], l, a - bounds[m], b - a, s.H, dst + (a - lo) * s.Hpad * 2, (int64_t)s.Hpad * 2});
+        if (b > a)
+          p.copies.push_back({src[m], l, a - bounds[m], b - a, s.H, dst + (a - lo) * s.Hpad * wb, (int64_t)s.Hpad * wb,
+                              p.q8 ? scl + (a - lo) * 4 : -1, p.q8 ? 4 : 0});
       }
     }, kv_per_xcd ? &qkv_on : nullptr);
     // attention: one tile per (KV head, group of T query heads, split).  The tiles that read the
@@ -335,30 +370,38 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
       for (int w = 0; w < W; ++w)
         if (tile_at(attn_wv, w).kind == KIND_NONE) o_workers.push_back(w);
     gemv_wave(KIND_O, l, s.H, s.n_heads * s.hd, s.Qpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
-      p.copies.push_back({SRC_WO, l, lo, hi - lo, (int64_t)s.n_heads * s.hd, dst, (int64_t)s.Qpad * 2});
+      p.copies.push_back({SRC_WO, l, lo, hi - lo, (int64_t)s.n_heads * s.hd, dst, (int64_t)s.Qpad * wb,
+                          p.q8 ? dst + (hi - lo) * s.Qpad * wb : -1, p.q8 ? 4 : 0});
     }, o_workers.empty() ? nullptr : &o_workers);
     // gate and up rows interleaved (gate j, up j, gate j+1, ...) so any even row block holds whole pairs
     gemv_wave(KIND_GU, l, s.F, s.H, s.Hpad, 2, [&](int64_t lo, int64_t hi, int64_t dst) {
-      p.copies.push_back({SRC_WGATE, l, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * 2 * 2});
-      p.copies.push_back({SRC_WUP, l, lo, hi - lo, s.H, dst + (int64_t)s.Hpad * 2, (int64_t)s.Hpad * 2 * 2});
+      const int64_t scl = dst + 2 * (hi - lo) * s.Hpad * wb;  // scales interleaved like the rows
+      p.copies.push_back({SRC_WGATE, l, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * wb * 2, p.q8 ? scl : -1, p.q8 ? 8 : 0});
+      p.copies.push_back({SRC_WUP, l, lo, hi - lo, s.H, dst + (int64_t)s.Hpad * wb, (int64_t)s.Hpad * wb * 2,
+                          p.q8 ? scl + 4 : -1, p.q8 ? 8 : 0});
     });
     gemv_wave(KIND_DOWN, l, s.H, s.F, s.Fpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
-      p.copies.push_back({SRC_WDOWN, l, lo, hi - lo, s.F, dst, (int64_t)s.Fpad * 2});
+      p.copies.push_back({SRC_WDOWN, l, lo, hi - lo, s.F, dst, (int64_t)s.Fpad * wb,
+                          p.q8 ? dst + (hi - lo) * s.Fpad * wb : -1, p.q8 ? 4 : 0});
     });
   }
   const int64_t lm_base = off;
   gemv_wave(KIND_LM, -1, s.V, s.H, s.Hpad, 1, [&](int64_t lo, int64_t hi, int64_t dst) {
-    p.copies.push_back({s.tied ? SRC_EMBED : SRC_LM_HEAD, -1, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * 2});
+    p.copies.push_back({s.tied ? SRC_EMBED : SRC_LM_HEAD, -1, lo, hi - lo, s.H, dst, (int64_t)s.Hpad * wb,
+                        p.q8 ? dst + (hi - lo) * s.Hpad * wb : -1, p.q8 ? 4 : 0});
   });
-  wbytes += (int64_t)s.H * 2;  // one embedding row per token
-  if (s.tied) {
+  wbytes += (int64_t)s.H * 2;  // one (BF16) embedding row per token
+  if (s.tied && !p.q8) {
     p.embed_off = lm_base;  // LM-head rows are the embedding rows, in order
+    p.embed_stride = (int64_t)s.Hpad * 2;
   } else {
+    // the lookup reads BF16 rows of their own (untied, or an INT8 head)
+    const int64_t stride = round_up((int64_t)s.H * 2, 256);
     p.embed_off = off;
-    p.copies.push_back({SRC_EMBED, -1, 0, s.V, s.H, off, (int64_t)s.Hpad * 2});
-    off += (int64_t)s.V * s.Hpad * 2;
+    p.embed_stride = stride;
+    p.copies.push_back({SRC_EMBED, -1, 0, s.V, s.H, off, stride});
+    off += (int64_t)s.V * stride;
   }
-  p.embed_stride = (int64_t)s.Hpad * 2;
   p.packed_bytes = round_up(off, 4096);
   p.weight_bytes_per_step = wbytes;
 
@@ -393,8 +436,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
       int64_t b = 0;
       if (t.kind != KIND_ATTN && t.kind != KIND_COMBINE) {
         const int64_t rows = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1);
-        b = rows * t.kpad * 2;
-        row_bytes = (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1);
+        b = rows * t.kpad * p.wb;
+        row_bytes = (int64_t)t.kpad * p.wb * (t.kind == KIND_GU ? 2 : 1);
       }
       tot += b;
       mx = std::max(mx, b);
@@ -424,7 +467,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
-  p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64);
+  p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0);  // (INT8: then a block's scales)
   // schedule tables: per wave a SegDesc, this worker's TileDesc and the WaveDesc; per layer a LayerSmall
   p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
                 (int32_t)round_up((int64_t)p.waves.size() * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
@@ -573,10 +616,10 @@ int validate_plan(const HostPlan& p, std::string& err) {
           int32_t kp = kind == KIND_O ? s.Qpad : kind == KIND_DOWN ? s.Fpad : s.Hpad;
           if (t.nrows < 1 || t.row0 < 0 || t.row0 + (int64_t)t.nrows > R)
             return fail(err, TILES_E_PLAN, "GEMV rows out of range");
-          if (t.kpad != kp || kp % CHUNK_COLS != 0) return fail(err, TILES_E_PLAN, "bad GEMV width");
+          if (t.kpad != kp || kp % (CHUNK_BYTES / p.wb) != 0) return fail(err, TILES_E_PLAN, "bad GEMV width");
           spans.push_back({t.row0, t.nrows});
           covered += t.nrows;
-          const int64_t bytes = (int64_t)t.nrows * (kind == KIND_GU ? 2 : 1) * t.kpad * 2;
+          const int64_t bytes = tile_packed_bytes(p, t);
           if (t.woff % CHUNK_BYTES != 0 || t.woff < 0 || t.woff + bytes > p.packed_bytes)
             return fail(err, TILES_E_PLAN, "packed weights out of bounds or misaligned");
           packed_ranges.push_back({t.woff, t.woff + bytes});
@@ -707,11 +750,11 @@ int validate_plan(const HostPlan& p, std::string& err) {
     for (int w = 0; w < W; ++w) {
       const TileDesc& t = p.tiles[(size_t)wv * W + w];
       if (t.kind == KIND_NONE || t.kind == KIND_ATTN || t.kind == KIND_COMBINE) continue;
-      const int64_t b = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1) * t.kpad * 2;
+      const int64_t b = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1) * t.kpad * p.wb;
       ++busy;
       tot += b;
       mx = std::max(mx, b);
-      row_bytes = std::max<int64_t>(row_bytes, (int64_t)t.kpad * 2 * (t.kind == KIND_GU ? 2 : 1));
+      row_bytes = std::max<int64_t>(row_bytes, (int64_t)t.kpad * p.wb * (t.kind == KIND_GU ? 2 : 1));
     }
     if (busy == 0) continue;
     if ((double)mx > (double)tot / busy + row_bytes + 0.5) {
@@ -730,23 +773,32 @@ int validate_plan(const HostPlan& p, std::string& err) {
   // with (QKV rows from Wq, Wk, Wv in turn; gate/up rows alternating; LM-head rows from the embedding
   // when tied), so that a packing mistake cannot go unnoticed until the numbers come out wrong.
   {
-    struct Src { int32_t tensor, layer; int64_t row, cols; };
+    struct Src { int32_t tensor, layer; int64_t row, cols, scale; };  // scale: its offset (quantized copy) or -1
     std::unordered_map<int64_t, Src> at;  // destination byte offset of a packed row -> its source
     at.reserve(1 << 16);
-    std::map<std::pair<int32_t, int32_t>, std::vector<std::pair<int64_t, int64_t>>> rows_of;  // source rows copied
+    // source rows copied, per (tensor, layer, form): a tied INT8 head copies the embedding twice, as
+    // INT8 codes for the head and as BF16 rows for the lookup
+    std::map<std::tuple<int32_t, int32_t, int32_t>, std::vector<std::pair<int64_t, int64_t>>> rows_of;
     for (const CopySeg& c : p.copies) {
       int64_t R = 0, C = 0;
+      const bool quant = c.scale_off >= 0;
+      const int64_t eb = quant ? 1 : 2;  // bytes per packed value of this copy
+      const bool gain = c.tensor == SRC_ATTN_NORM || c.tensor == SRC_MLP_NORM || c.tensor == SRC_Q_NORM ||
+                        c.tensor == SRC_K_NORM || c.tensor == SRC_FINAL_NORM;
       if (!source_geometry(s, c.tensor, R, C) || c.cols != C || c.nrows < 1 || c.src_row < 0 || c.src_row + c.nrows > R ||
-          c.dst_off < 0 || c.dst_pitch < c.cols * 2 || c.dst_off + (c.nrows - 1) * c.dst_pitch + c.cols * 2 > p.packed_bytes)
+          c.dst_off < 0 || c.dst_pitch < c.cols * eb || c.dst_off + (c.nrows - 1) * c.dst_pitch + c.cols * eb > p.packed_bytes ||
+          (quant && (!p.q8 || gain || c.scale_off + (c.nrows - 1) * c.scale_pitch + 4 > p.packed_bytes)))
         return fail(err, TILES_E_PLAN, "packing copy out of range");
-      rows_of[{c.tensor, c.layer}].push_back({c.src_row, c.src_row + c.nrows});
+      rows_of[std::make_tuple(c.tensor, c.layer, quant ? 1 : 0)].push_back({c.src_row, c.src_row + c.nrows});
       for (int64_t r = 0; r < c.nrows; ++r)
-        if (!at.emplace(c.dst_off + r * c.dst_pitch, Src{c.tensor, c.layer, c.src_row + r, c.cols}).second)
+        if (!at.emplace(c.dst_off + r * c.dst_pitch,
+                        Src{c.tensor, c.layer, c.src_row + r, c.cols, quant ? c.scale_off + r * c.scale_pitch : -1})
+                 .second)
           return fail(err, TILES_E_PLAN, "two packing copies write the same packed row");
     }
     for (auto& kvp : rows_of) {
       int64_t R = 0, C = 0;
-      source_geometry(s, kvp.first.first, R, C);
+      source_geometry(s, std::get<0>(kvp.first), R, C);
       auto& v = kvp.second;
       std::sort(v.begin(), v.end());
       int64_t next = 0;
@@ -758,7 +810,8 @@ int validate_plan(const HostPlan& p, std::string& err) {
     }
     // every source tensor the model has is packed
     const size_t per_layer = s.qk_norm ? 11 : 9;
-    const size_t want = (size_t)s.n_layers * per_layer + 2 /*final norm, embedding or LM head*/ + (s.tied ? 0 : 1);
+    const size_t want = (size_t)s.n_layers * per_layer + 2 /*final norm, embedding or LM head*/ +
+                        (s.tied && !p.q8 ? 0 : 1) /*a lookup table of its own*/;
     if (rows_of.size() != want) return fail(err, TILES_E_PLAN, "source rows not packed exactly once");
     for (int wv = 0; wv < nw; ++wv) {
       const int32_t kind = p.waves[wv].kind;
@@ -771,9 +824,10 @@ int validate_plan(const HostPlan& p, std::string& err) {
           int32_t tensor, layer;
           int64_t srow;
           expected_source(s, kind, p.waves[wv].layer, s.tied, t.row0 + (kind == KIND_GU ? r / 2 : r), r, tensor, layer, srow);
-          auto it = at.find(t.woff + r * t.kpad * 2);
+          auto it = at.find(t.woff + r * t.kpad * p.wb);
+          const int64_t want_scale = p.q8 ? t.woff + nr * t.kpad + r * 4 : -1;  // INT8: scales follow the rows
           if (it == at.end() || it->second.tensor != tensor || it->second.layer != layer || it->second.row != srow ||
-              it->second.cols * 2 > (int64_t)t.kpad * 2) {
+              it->second.cols > (int64_t)t.kpad || it->second.scale != want_scale) {
             os << "packed row " << r << " of worker " << w << "'s tile in wave " << wv << " is not its source row";
             return fail(err, TILES_E_PLAN, os.str());
           }
@@ -782,7 +836,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
     }
     // the embedding rows the first wave reads, and the gains, are where the plan says
     auto it = at.find(p.embed_off + (int64_t)(s.V - 1) * p.embed_stride);
-    if (it == at.end() || it->second.tensor != SRC_EMBED || it->second.row != s.V - 1)
+    if (it == at.end() || it->second.tensor != SRC_EMBED || it->second.row != s.V - 1 || it->second.scale != -1)
       return fail(err, TILES_E_PLAN, "embedding rows not where the plan reads them");
     it = at.find(p.final_norm_off);
     if (it == at.end() || it->second.tensor != SRC_FINAL_NORM) return fail(err, TILES_E_PLAN, "final-norm gain misplaced");
@@ -907,7 +961,7 @@ int debug_mutate_plan(HostPlan& p, int32_t m, std::string& err) {
       // worker a takes the first two rows of worker b: coverage and packing stay exact, the bytes do not
       const int wv = first_wave(KIND_DOWN);
       if (!adjacent(wv, a, b, 2)) break;
-      const int64_t row_bytes = (int64_t)tile(wv, b).kpad * 2;
+      const int64_t row_bytes = (int64_t)tile(wv, b).kpad * p.wb;
       tile(wv, a).nrows += 2;
       tile(wv, b).row0 += 2;
       tile(wv, b).nrows -= 2;

@@ -27,6 +27,10 @@ struct CopySeg {
   int64_t cols;
   int64_t dst_off;
   int64_t dst_pitch;
+  // Quantized copy (weight-only INT8): the rows are written as INT8 codes (cols bytes each) and row i's
+  // FP32 scale goes to scale_off + i * scale_pitch; -1 for a plain BF16 copy.
+  int64_t scale_off = -1;
+  int64_t scale_pitch = 0;
 };
 
 // Buffers named by the hazard check.
@@ -50,6 +54,8 @@ struct Shape {
 struct HostPlan {
   Shape s;
   int32_t W = 0;               // workers
+  int32_t q8 = 0;              // 1: weight-only INT8 linear layers (codes + per-row FP32 scales)
+  int32_t wb = 2;              // bytes per packed weight: 2 (BF16) or 1 (INT8)
   int32_t S = 1;               // KV splits
   int32_t combine_in_o = 1;    // 1 prologue, 0 own wave
   int32_t T = 1;               // query heads per attention tile (divides G)
@@ -68,6 +74,19 @@ struct HostPlan {
   int64_t ll_words = 0;        // tagged-data buffers of all waves (uint32 words)
   uint64_t checksum = 0;
 };
+
+// Bytes of a GEMV tile in the packed buffer: its rows, then (INT8) their scales padded to a chunk.
+inline int64_t tile_packed_bytes(const HostPlan& p, const TileDesc& t) {
+  const int64_t rows = (int64_t)t.nrows * (t.kind == KIND_GU ? 2 : 1);
+  const int64_t scales = p.q8 ? (rows * 4 + CHUNK_BYTES - 1) / CHUNK_BYTES * CHUNK_BYTES : 0;
+  return rows * t.kpad * p.wb + scales;
+}
+
+// Symmetric per-row INT8 codes of BF16 rows (weight-only INT8): s = max |w| / 127 and
+// q = round-half-even(w / s) clamped to [-127, 127], each operation in IEEE FP32; s = 0, q = 0 for
+// a row of zeros.  src: `rows` rows of `cols` BF16 values, `src_pitch` values apart.
+void quantize_rows_int8(const uint16_t* src, int64_t src_pitch, int64_t rows, int64_t cols, int8_t* q,
+                        int64_t q_pitch, float* scales, int64_t scale_pitch_floats);
 
 // Build and validate a plan.  Returns TILES_OK or a TILES_E_* code with `err` set.
 int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& plan, std::string& err);

@@ -50,7 +50,7 @@ class Config(ctypes.Structure):
         ("qk_norm", ctypes.c_int32), ("tie_embeddings", ctypes.c_int32), ("max_positions", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("kv_splits", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
         ("attn_heads", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
-        ("o_placement", ctypes.c_int32),
+        ("o_placement", ctypes.c_int32), ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -76,7 +76,7 @@ class PlanInfo(ctypes.Structure):
         ("combine_mode", ctypes.c_int32), ("occupancy", ctypes.c_int32), ("packed_bytes", ctypes.c_int64),
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
-        ("o_workers", ctypes.c_int32),
+        ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -128,6 +128,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_plan_debug_corrupt_device.argtypes = [ctypes.c_void_p]
         L.tiles_plan_debug_spin_limit.restype = ctypes.c_int
         L.tiles_plan_debug_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
+        L.tiles_quantize_rows_int8.restype = ctypes.c_int
+        L.tiles_quantize_rows_int8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                               ctypes.c_void_p]
         L.tiles_stream_read.restype = ctypes.c_int
         L.tiles_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
@@ -147,11 +150,16 @@ def _check(rc: int):
         raise TilesError(rc, last_error())
 
 
+WEIGHTS = {"bf16": 0, "int8": 1}
+
+
 def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
-                n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0) -> Config:
+                n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0,
+                weights: str = "bf16") -> Config:
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
                   float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
-                  int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement))
+                  int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement),
+                  WEIGHTS[weights])
 
 
 def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
@@ -167,6 +175,16 @@ def debug_validate(m: ModelConfig, max_positions: int, mutation: int, n_workers:
     validator's status code (the message is in last_error())."""
     cfg = make_config(m, max_positions, **kw)
     return lib().tiles_plan_debug_validate(ctypes.byref(cfg), n_workers, mutation)
+
+
+def quantize_rows_int8(bf16_bits: np.ndarray):
+    """The library's weight-only INT8 quantizer (tiles_quantize_rows_int8, host only) on a uint16
+    [rows, cols] array of BF16 bit patterns: (int8 codes [rows, cols], float32 scales [rows])."""
+    w = np.ascontiguousarray(np.atleast_2d(bf16_bits), dtype=np.uint16)
+    q = np.zeros(w.shape, dtype=np.int8)
+    s = np.zeros(w.shape[0], dtype=np.float32)
+    _check(lib().tiles_quantize_rows_int8(w.ctypes.data, w.shape[0], w.shape[1], q.ctypes.data, s.ctypes.data))
+    return q, s
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -214,11 +232,11 @@ class Plan:
 
     def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
                  combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0,
-                 o_placement: int = 0):
+                 o_placement: int = 0, weight_format: str = "bf16"):
         self.model = m
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream,
-                                attn_heads, o_placement)
+                                attn_heads, o_placement, weight_format)
         on_device = weights["embed"].is_cuda
         layers = (LayerWeights * m.n_layers)()
         for i, d in enumerate(weights["layers"]):
