@@ -327,8 +327,24 @@ struct NoPrep {
   __device__ void operator()(int, int) const {}
 };
 
-// x (n floats, tagged) -> xres = x, vec = x * gain, and this wavefront's sum of squares of its share
-template <bool WD>
+// Columns of one packed chunk: 512 BF16 weights, or 1024 INT8 codes.
+template <bool Q8>
+constexpr int chunk_cols() { return Q8 ? CHUNK_COLS_I8 : CHUNK_COLS; }
+
+// LDS position of GEMV input element i.  In a packed chunk lane l holds VPL = columns / 64
+// consecutive columns, 4 per dword (INT8) or per two dwords (BF16); group h (of 4 columns) of
+// lane l is stored at chunk offset 256 h + 4 l, so that the 64 lanes' 16-byte reads of one group
+// are consecutive in LDS (no bank conflicts; consecutive columns 4 apart by lane would collide).
+// Groups of four stay contiguous, so 16-byte aligned writes of four elements stay 16-byte writes.
+template <bool Q8>
+__device__ __forceinline__ int vperm(int i) {
+  constexpr int CC = chunk_cols<Q8>(), VPL = CC / 64;
+  return (i & ~(CC - 1)) | (((i & (VPL - 1)) >> 2) << 8) | (((i & (CC - 1)) / VPL) << 2) | (i & 3);
+}
+
+// x (n floats, tagged) -> xres = x, vec = x * gain (GEMV input order, vperm), and this
+// wavefront's sum of squares of its share
+template <bool WD, bool Q8>
 __device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, const uint32_t* src, int n, const uint16_t* gain,
                             int slot, int lane, uint32_t par, float& ss) {
   uint2 gv[GATHER_UNITS];
@@ -339,22 +355,26 @@ __device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, c
       [&](int i, int u, const f32x4 x) {
         *reinterpret_cast<f32x4*>(L.xres + u * 4) = x;
         const f32x4 v = {x.x * bf16_lo(gv[i].x), x.y * bf16_hi(gv[i].x), x.z * bf16_lo(gv[i].y), x.w * bf16_hi(gv[i].y)};
-        *reinterpret_cast<f32x4*>(L.vec + u * 4) = v;
+        *reinterpret_cast<f32x4*>(L.vec + vperm<Q8>(u * 4)) = v;
         s += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
       });
   ss = wave_sum(s);
   return ab;
 }
 
-// plain tagged vector -> dst
-template <bool WD>
+// plain tagged vector -> dst (in GEMV input order, vperm, when `perm`)
+template <bool WD, bool Q8>
 __device__ __forceinline__ bool gather_plain(const KernelArgs& a, float* dst, const uint32_t* src, int n, int slot, int lane,
-                             uint32_t par) {
+                             uint32_t par, bool perm) {
   return gather<GATHER_UNITS_PLAIN, WD>(a, src, n / 4, slot, NWAVES, par, lane, Identity{}, NoPrep{},
-                              [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(dst + u * 4) = x; });
+                              [&](int, int u, const f32x4 x) {
+                                *reinterpret_cast<f32x4*>(dst + (perm ? vperm<Q8>(u * 4) : u * 4)) = x;
+                              });
 }
 
-// embedding row of `tok` (BF16, exact in FP32) -> xres, vec = x * gain; returns the sum of squares
+// embedding row of `tok` (BF16, exact in FP32) -> xres, vec = x * gain (vperm order); returns the
+// sum of squares
+template <bool Q8>
 __device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds& L, int tok, const uint16_t* gain, int lane) {
   const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)tok * a.embed_stride);
   constexpr int B = 8;
@@ -378,7 +398,7 @@ __device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds&
         const f32x4 x = {bf16_lo(ev[u].x), bf16_hi(ev[u].x), bf16_lo(ev[u].y), bf16_hi(ev[u].y)};
         *reinterpret_cast<f32x4*>(L.xres + i) = x;
         const f32x4 v = {x.x * bf16_lo(gv[u].x), x.y * bf16_hi(gv[u].x), x.z * bf16_lo(gv[u].y), x.w * bf16_hi(gv[u].y)};
-        *reinterpret_cast<f32x4*>(L.vec + i) = v;
+        *reinterpret_cast<f32x4*>(L.vec + vperm<Q8>(i)) = v;
         ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
       }
     }
@@ -519,10 +539,6 @@ __device__ __forceinline__ float dot16_i8(const u32x4 w, const float* v) {
   s1 = fmaf(i8(w.w, 3), v3.w, s1);
   return s0 + s1;
 }
-
-// Columns of one packed chunk: 512 BF16 weights, or 1024 INT8 codes.
-template <bool Q8>
-constexpr int chunk_cols() { return Q8 ? CHUNK_COLS_I8 : CHUNK_COLS; }
 
 // Chunk range [i, ihi) of compute wave c in block r0 of a GEMV segment.
 struct Range {
@@ -694,7 +710,7 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
   float acc = 0.f;
-  const float* vlane = L.vec + lane * VPL;
+  const float* vlane = L.vec + lane * 4;  // group q of this lane's columns of chunk s: vlane[s * CC + 256 q] (vperm)
   // Every slot is consumed (a slot past the range contributes zero and does not advance the
   // row), so no branch sits between a load and the use of its registers.
   auto consume = [&](const u32x4& w, bool valid, const float* xv) {
@@ -717,10 +733,10 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
     int s = seg;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const f32x4* px = reinterpret_cast<const f32x4*>(vlane + s * CC);
+      const float* px = vlane + s * CC;
 #pragma unroll
       for (int q = 0; q < VPL / 4; ++q) {
-        const f32x4 x = px[q];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(px + 256 * q);
         xv[u][4 * q] = x.x; xv[u][4 * q + 1] = x.y; xv[u][4 * q + 2] = x.z; xv[u][4 * q + 3] = x.w;
       }
       s = s + 1 == C ? 0 : s + 1;
@@ -814,9 +830,9 @@ constexpr int pstride() { return HD + 4; }
 // weighted l ("Tiles", split-KV attention combine).  Each thread takes four consecutive
 // dimensions of one head; a split's (m, l) pair and accumulator slice are read with
 // independent loads, and both loops over the splits are unrolled, so the LDS latencies overlap.  Empty splits (l = 0) carry no weight; a head
-// with no positions gives 0.
-template <int HD>
-__device__ __forceinline__ void merge_heads(const float* part, int nh, int S, int tid, float* out) {
+// with no positions gives 0.  `perm`: out is a GEMV input (vperm order).
+template <int HD, bool Q8>
+__device__ __forceinline__ void merge_heads(const float* part, int nh, int S, int tid, float* out, bool perm) {
   constexpr int PS = pstride<HD>();
   for (int o = tid * 4; o < nh * HD; o += BLOCK_THREADS * 4) {
     const int h = o / HD, d = o % HD;
@@ -843,7 +859,7 @@ __device__ __forceinline__ void merge_heads(const float* part, int nh, int S, in
       a3 = fmaf(f, v23.y, a3);
     }
     const float inv = ll > 0.f ? 1.0f / ll : 0.f;
-    *reinterpret_cast<f32x4*>(out + o) = f32x4{a0 * inv, a1 * inv, a2 * inv, a3 * inv};
+    *reinterpret_cast<f32x4*>(out + (perm ? vperm<Q8>(o) : o)) = f32x4{a0 * inv, a1 * inv, a2 * inv, a3 * inv};
   }
 }
 
@@ -1294,7 +1310,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G, bool CTRL, bool WD>
+template <int HD, int G, bool CTRL, bool WD, bool Q8>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
@@ -1320,12 +1336,12 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
             ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
             if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
           }
-          if (!ab) ss = stage_embedding(a, L, tok, gain, lane);
+          if (!ab) ss = stage_embedding<Q8>(a, L, tok, gain, lane);
         }
       } else {
-        ab = gather_norm<WD>(a, L, in, a.H, gain, wave, lane, par, ss);
+        ab = gather_norm<WD, Q8>(a, L, in, a.H, gain, wave, lane, par, ss);
       }
-      for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+      for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
       if (lane == 0) L.small[SM_SS + wave] = ss;
       break;
     }
@@ -1347,8 +1363,8 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         n = a.S * PS;
         nz = t.kpad;  // no GEMV input to pad
       }
-      ab = gather_plain<WD>(a, dst, src, n, wave, lane, par);
-      for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[i] = 0.f;
+      ab = gather_plain<WD, Q8>(a, dst, src, n, wave, lane, par, dst == L.vec);
+      for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
       break;
     }
     case KIND_ATTN: {
@@ -1394,7 +1410,7 @@ __device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileD
 }
 
 // LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale.
-template <int HD, int G>
+template <int HD, int G, bool Q8>
 __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
                                               const TileDesc& t, int layer, int pos) {
   float rs = 1.0f;
@@ -1407,7 +1423,7 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
   } else if ((t.kind == KIND_O && a.combine_in_o) || t.kind == KIND_COMBINE) {
     // all heads' splits (o_proj prologue) or one head's (combine tile): one copy of the merge
-    merge_heads<HD>(L.part, t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane, L.vec);
+    merge_heads<HD, Q8>(L.part, t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane, L.vec, t.kind == KIND_O);
   }
   return rs;
 }
@@ -1474,7 +1490,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       if constexpr (Q8) {
         if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
       }
-      if (gather_inputs<HD, G, true, WD>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true, WD, Q8>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       if constexpr (Q8) {
         if (is_gemv(t.kind)) put_scales(L, t, 0, block_rows, lane, sreg);
       }
@@ -1484,7 +1500,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         break;
       }
       if (a.trace) t_pro = wall_clock64();
-      const float rs = lds_prologue<HD, G>(a, L, 0, lane, t, layer, pos);
+      const float rs = lds_prologue<HD, G, Q8>(a, L, 0, lane, t, layer, pos);
       if (needs_barrier_a(a, t)) __syncthreads();  // A: inputs ready
       const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
@@ -1700,7 +1716,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G, false, WD>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false, WD, Q8>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
@@ -1708,7 +1724,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         break;
       }
       if (needs_barrier_a(a, t)) {
-        lds_prologue<HD, G>(a, L, wave, lane, t, layer, pos);
+        lds_prologue<HD, G, Q8>(a, L, wave, lane, t, layer, pos);
         __syncthreads();  // A
       }
       stamp(ts, TS_AFTER_A, lane);
