@@ -64,7 +64,16 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
         if el >= budget_s or n >= wl.n_steps - 1:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": n / el, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / el, "unit": "tok/s", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{n} free-running decode steps of the same workload after 1 warm-up step "
                       f"({el:.1f} s timed; warm-up incl. BF16->FP32 widening {prep:.1f} s), NumPy FP32"}
 

@@ -28,3 +28,37 @@ def test_workload_bytes_per_token():
     assert LLAMA_1B.kv_bytes_per_position() == 32_768
     assert wl.bytes_per_token() == 2_471_632_896 + 32_768 * 1055.5 + 32_768
     assert WORKLOADS["qwen4b_32k"].bytes_per_token() == QWEN3_4B.weight_bytes_per_token() + 147_456 * (32767 + 16.5) + 147_456
+
+
+def _fake_counter_db(path, counter, rows):
+    import sqlite3
+
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, dispatch_id integer, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)", [(k, d, counter, v) for k, d, v in rows])
+    con.commit()
+    con.close()
+
+
+def test_counter_traffic_calibration(tmp_path):
+    """The traffic summary scales FETCH_SIZE by the stream-read dispatches (known bytes, the decode
+    kernel's load form) and WRITE_SIZE by the copy kernel; per-dispatch values of one counter are
+    summed over the rows (instances) of that dispatch."""
+    from tile_scheduled_persistent_amd import prof
+
+    read_bytes, copy_bytes = 2 << 30, 1 << 30
+    worker = "void tiles::tiles_worker<64, 4, false, false>(tiles::KernelArgs)"
+    sr = "tiles::stream_read(unsigned char const*, long, unsigned int*)"
+    copy = "__amd_rocclr_copyBuffer"
+    # the counter reads half the bytes a kernel fetches; a dispatch's value arrives in two rows
+    fetch = [(worker, 1, 40.0e6), (worker, 1, 40.0e6), (worker, 2, 80.0e6), (sr, 3, 2 ** 20 / 2), (sr, 3, 2 ** 20 / 2),
+             (sr, 4, 2 ** 20), (copy, 5, copy_bytes / 2048)]
+    write = [(worker, 1, 1000.0), (worker, 2, 1000.0), (copy, 5, copy_bytes / 1024)]
+    _fake_counter_db(str(tmp_path / "f.db"), "FETCH_SIZE", fetch)
+    _fake_counter_db(str(tmp_path / "w.db"), "WRITE_SIZE", write)
+    d = prof.traffic(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "tiles_worker", copy_bytes, read_bytes)
+    assert d["FETCH_SIZE"]["kib_per_dispatch"] == [80.0e6, 80.0e6]
+    assert d["FETCH_SIZE"]["stream_read_factor"] == 2.0
+    assert d["FETCH_SIZE"]["copy_factor"] == 2.0
+    assert d["WRITE_SIZE"]["factor"] == 1.0
+    assert d["traffic_bytes_per_launch"] == 80.0e6 * 1024 * 2 + 1000.0 * 1024

@@ -4,10 +4,12 @@
         per-kernel calls, total / average / min / max duration (from --kernel-trace)
     python -m tile_scheduled_persistent_amd.prof counters DB --kernel NAME [--cmd "..."]
         per-dispatch counter values of one kernel (from --pmc runs), e.g. FETCH_SIZE / WRITE_SIZE
-    python -m tile_scheduled_persistent_amd.prof traffic FETCH_DB WRITE_DB --calib-bytes B --build-id ID [--cmd "..."]
-        HBM bytes per launch of one kernel as JSON: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-        each scaled by what the same counter reads for the largest copy-kernel dispatch in the
-        same run, a plain copy of B bytes (reads B, writes B)
+    python -m tile_scheduled_persistent_amd.prof traffic FETCH_DB WRITE_DB --calib-bytes B --read-bytes R --build-id ID [--cmd "..."]
+        HBM bytes per launch of one kernel as JSON: FETCH_SIZE (KiB per dispatch) scaled by what
+        the same counter reads for the library's stream-read kernel in the same run (each dispatch
+        reads exactly R bytes with the decode kernel's own load form), WRITE_SIZE scaled by what it
+        reads for the largest copy-kernel dispatch, a plain copy of B bytes (the stream read writes
+        nothing); the copy-based FETCH factor is reported beside it as a cross-check
 
 The text goes to stdout; the command that produced the database is echoed in the header.
 """
@@ -69,18 +71,32 @@ def _per_kernel(db: str, counter: str) -> dict:
     return out
 
 
-def traffic(fetch_db: str, write_db: str, kernel: str, calib_bytes: int) -> dict:
+def _stream_read_kib(per: dict) -> list:
+    return [v for name, d in per.items() if "stream_read" in name for v in d.values()]
+
+
+def traffic(fetch_db: str, write_db: str, kernel: str, calib_bytes: int, read_bytes: int) -> dict:
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         per = _per_kernel(db, counter)
         copy_kib = _largest_copy(per)
-        factor = calib_bytes / (copy_kib * 1024.0)
-        mine = [v for name, d in per.items() if kernel in name for v in d.values()]
+        copy_factor = calib_bytes / (copy_kib * 1024.0)
+        mine = [v for name, d in per.items() if kernel in name and "stream_read" not in name for v in d.values()]
         if not mine:
             raise SystemExit(f"no dispatch of {kernel} in {db}")
-        res[counter] = {"kib_per_dispatch": [round(v, 1) for v in mine], "mean_kib": statistics.mean(mine),
-                        "copy_kib": copy_kib, "factor": factor,
-                        "bytes_per_launch": statistics.mean(mine) * 1024.0 * factor}
+        rec = {"kib_per_dispatch": [round(v, 1) for v in mine], "mean_kib": statistics.mean(mine),
+               "copy_kib": copy_kib, "copy_factor": copy_factor}
+        factor = copy_factor
+        if counter == "FETCH_SIZE":
+            sr = _stream_read_kib(per)
+            if not sr:
+                raise SystemExit("no stream_read dispatch in the FETCH_SIZE database")
+            rec["stream_read_kib"] = [round(v, 1) for v in sr]
+            factor = read_bytes / (statistics.median(sr) * 1024.0)
+            rec["stream_read_factor"] = factor
+        rec["factor"] = factor
+        rec["bytes_per_launch"] = statistics.mean(mine) * 1024.0 * factor
+        res[counter] = rec
     res["traffic_bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
     return res
 
@@ -91,6 +107,7 @@ def main(argv=None):
     ap.add_argument("db")
     ap.add_argument("db2", nargs="?")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--read-bytes", type=int, default=2 << 30)
     ap.add_argument("--build-id", default="")
     ap.add_argument("--workload", default="")
     ap.add_argument("--kernel", default="tiles_worker")
@@ -100,9 +117,11 @@ def main(argv=None):
         import json
         if not args.db2:
             raise SystemExit("traffic needs the FETCH_SIZE and the WRITE_SIZE database")
-        d = traffic(args.db, args.db2, args.kernel, args.calib_bytes)
+        d = traffic(args.db, args.db2, args.kernel, args.calib_bytes, args.read_bytes)
         d.update({"kernel": args.kernel, "workload": args.workload, "build_id": args.build_id,
-                  "calibration": f"largest __amd_rocclr_copyBuffer dispatch of the same run, a copy of {args.calib_bytes} bytes",
+                  "calibration": (f"FETCH_SIZE: median stream_read dispatch of the same run (each reads {args.read_bytes} "
+                                  f"bytes with 16-byte non-temporal loads); WRITE_SIZE: largest __amd_rocclr_copyBuffer "
+                                  f"dispatch of the same run, a copy of {args.calib_bytes} bytes"),
                   "command": args.cmd})
         print(json.dumps(d, indent=1))
         return 0
