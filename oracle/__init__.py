@@ -29,6 +29,7 @@ from .decoder import (  # noqa: F401
     float_to_bf16_bits,
     quantize_rows_int8,
     dequantize_rows_int8,
+    sample_token,
     LINEAR_WEIGHTS,
     rmsnorm,
     rope_cos_sin,

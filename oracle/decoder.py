@@ -43,6 +43,17 @@ Q1  Weight-only INT8 ("History and roadmap" (TileInfer.jl), "M8 so far" table: w
     q = round-half-even(W / s) clamped to [-127, 127], every operation in FP32 on the BF16 values; a
     row of zeros has s = 0 and q = 0.  The layer computes with the dequantized weights q * s.  The
     embedding lookup and the norm gains keep their BF16 values.
+S1  Top-k / top-p sampling ("History and roadmap" (TileInfer.jl), "M8 so far" table: top-k/top-p
+    sampling on the device, inside the graph, as fast as greedy; the pages give no order of the
+    filters, no random number source and no precision).  A sampled step ranks the logits in decreasing order (equal
+    logits by increasing token index, as for R8) and keeps the first top_k; weighs them by
+    w_i = exp((z_i - z_0) / T) at temperature T (z_0 the largest); keeps the shortest prefix of that
+    ranking whose cumulative weight reaches top_p times the kept total (at least one token); and
+    draws one token of the prefix by inverse CDF: the first whose cumulative weight exceeds
+    u * (prefix total), with one uniform u in [0, 1) per step, given as an input (the last token of
+    the prefix if rounding leaves none).  The decision is an integer taken by floating point, so it
+    is taken in FP32, the kernel's precision, with the sums accumulated in ranking order.
+    Limits: T > 0, 0 < top_p <= 1, 1 <= top_k <= V.
 """
 
 from __future__ import annotations
@@ -58,6 +69,7 @@ __all__ = [
     "float_to_bf16_bits",
     "quantize_rows_int8",
     "dequantize_rows_int8",
+    "sample_token",
     "LINEAR_WEIGHTS",
     "rmsnorm",
     "rope_cos_sin",
@@ -189,6 +201,29 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (one + np.exp(-z))
 
 
+def sample_token(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: float,
+                 detail: bool = False):
+    """S1: one token drawn from ``logits`` by top-k, then temperature softmax, then top-p, with the
+    step's uniform ``u`` in [0, 1).  Every sum and comparison is FP32.  With ``detail`` also returns
+    the ranking (token ids), the kept count, the FP32 cumulative weights and the drawn position."""
+    z = np.asarray(logits, dtype=np.float32)
+    if not (temperature > 0 and 0 < top_p <= 1 and 1 <= top_k <= z.shape[0] and 0 <= u < 1):
+        raise ValueError("sampling parameters out of range")
+    order = np.lexsort((np.arange(z.shape[0]), -z))[:top_k]   # decreasing logit, then increasing id
+    zk = z[order]
+    w = np.exp((zk - zk[0]) / np.float32(temperature)).astype(np.float32)
+    cum = np.cumsum(w, dtype=np.float32)                       # sums in ranking order
+    need = np.float32(top_p) * cum[-1]
+    n = int(np.argmax(cum >= need)) + 1 if np.any(cum >= need) else top_k
+    target = np.float32(u) * cum[n - 1]
+    above = np.nonzero(cum[:n] > target)[0]
+    i = int(above[0]) if above.size else n - 1
+    tok = int(order[i])
+    if detail:
+        return tok, {"order": order, "n": n, "cum": cum, "pos": i, "target": target, "need": need}
+    return tok
+
+
 # ---------------------------------------------------------------------------
 # Whole decode step
 # ---------------------------------------------------------------------------
@@ -315,12 +350,14 @@ class OracleModel:
 
     def decode(self, kv: dict, token: int, pos0: int, n_steps: int,
                teacher: Optional[Sequence[int]] = None, keep_hidden: bool = True,
-               widen_kv_once: bool = False):
-        """Greedy decode ``n_steps`` steps starting with ``token`` at ``pos0``.
+               widen_kv_once: bool = False, sampling: Optional[tuple] = None,
+               uniforms: Optional[Sequence[float]] = None):
+        """Decode ``n_steps`` steps starting with ``token`` at ``pos0``.
 
-        Step i consumes ``token`` (i = 0), else the previous step's argmax
-        (free-running) or ``teacher[i - 1]`` (teacher-forced).  Returns a dict
-        with ``tokens`` [n] (argmax of each step, R8), ``logits`` [n, V] and
+        Step i consumes ``token`` (i = 0), else the previous step's selected token
+        (free-running) or ``teacher[i - 1]`` (teacher-forced).  The selected token is
+        the argmax (R8), or with ``sampling`` = (temperature, top_k, top_p) the S1 draw
+        with ``uniforms[i]``.  Returns a dict with ``tokens`` [n], ``logits`` [n, V] and
         ``hidden`` [n, n_layers, H] (or None).  ``widen_kv_once`` widens the cache
         once up front (see :meth:`widen_kv`); the results are the same.
         """
@@ -334,7 +371,10 @@ class OracleModel:
             if i > 0:
                 t = int(teacher[i - 1]) if teacher is not None else int(toks[i - 1])
             logits, hidden = self.step(kv, t, pos0 + i, kv_wide)
-            toks[i] = int(np.argmax(logits))                       # R8: first max
+            if sampling is None:
+                toks[i] = int(np.argmax(logits))                   # R8: first max
+            else:
+                toks[i] = sample_token(logits, *sampling, float(uniforms[i]))  # S1
             logits_all[i] = logits
             if keep_hidden:
                 hidden_all[i] = hidden

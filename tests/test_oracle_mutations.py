@@ -5,8 +5,10 @@ that part of the oracle.
 
 The mistakes cover the readings the oracle rests on (RoPE pairing, frequency and sign,
 GQA map, attention scale and causal range, RMSNorm form, BF16 rounding, SwiGLU branch,
-residual source) and the plumbing of the step (which layer's weights and which gain
-each stage reads, q/k norm before RoPE, the argmax tie rule).
+residual source), the plumbing of the step (which layer's weights and which gain
+each stage reads, q/k norm before RoPE, the argmax tie rule), the INT8 weight codes and the
+sampling draw (tie order, temperature, top-k and top-p supports, the draw's scale and
+strictness, the per-step uniform).
 """
 
 import importlib.util
@@ -65,6 +67,18 @@ MUTATIONS = [
     ("INT8 LM head left in BF16", 'return self._get(None, "embed", linear=True)', 'return self._get(None, "embed")', False),
     ("INT8 embedding lookup quantized", "return bf16_bits_to_float(self.w[\"embed\"][token], self.dtype).copy()",
      "return self._get(None, \"embed\", linear=True)[token].copy()", False),
+    ("sampling ranks equal logits by decreasing id", "np.lexsort((np.arange(z.shape[0]), -z))",
+     "np.lexsort((-np.arange(z.shape[0]), -z))", False),
+    ("sampling temperature applied as a product", "(zk - zk[0]) / np.float32(temperature)",
+     "(zk - zk[0]) * np.float32(temperature)", False),
+    ("top-p prefix needs more than p", "cum >= need", "cum > need", True),
+    ("top-p threshold over the unfiltered total", "need = np.float32(top_p) * cum[-1]",
+     "need = np.float32(top_p) * np.float32(np.exp((z - zk[0]) / np.float32(temperature)).sum())", False),
+    ("draw scaled by the kept total, not the prefix's", "target = np.float32(u) * cum[n - 1]",
+     "target = np.float32(u) * cum[-1]", False),
+    ("draw non-strict", "np.nonzero(cum[:n] > target)", "np.nonzero(cum[:n] >= target)", False),
+    ("top-k keeps one more", ")[:top_k]   # decreasing", ")[:top_k + 1]   # decreasing", False),
+    ("decode samples with the previous step's uniform", "float(uniforms[i])", "float(uniforms[i - 1])", False),
     ("argmax keeps the last maximum", "toks[i] = int(np.argmax(logits))",
      "toks[i] = int(len(logits) - 1 - np.argmax(logits[::-1]))", False),
 ]

@@ -646,3 +646,113 @@ def test_int8_step_computes_with_the_dequantized_codes():
     hf = x1 / math.sqrt(np.mean(x1 * x1) + c.rms_eps)
     assert np.allclose(logits, (qE.astype(np.float64) * sE.astype(np.float64)[:, None]) @ hf, rtol=1e-12)
     assert not np.allclose(logits, E @ hf, rtol=1e-6)            # the head really is quantized
+
+
+# ---------------------------------------------------------------------------
+# Sampling (S1): hand-worked draws, closed-form frequencies over a grid of uniforms, support of
+# the top-k and top-p filters, the tie order, and the per-step uniform in decode.
+# ---------------------------------------------------------------------------
+from oracle import sample_token  # noqa: E402
+
+
+def _grid_frequencies(z, temperature, top_k, top_p, n=20000):
+    counts = np.zeros(len(z))
+    for j in range(n):
+        counts[sample_token(z, temperature, top_k, top_p, (j + 0.5) / n)] += 1
+    return counts / n
+
+
+def test_sampling_hand_worked_example():
+    """Logits 2, 1, 0, -1 on token ids 3, 0, 2, 1 at T = 1: weights 1, 1/e, 1/e^2 for the three kept
+    (top_k = 3); cumulative 1, 1 + 1/e = 1.368, 1.503.  top_p = 0.8 needs 0.8 * 1.503 = 1.203, so the
+    prefix is ids (3, 0) with total 1.368: u = 0.5 -> 0.684 < 1 -> id 3; u = 0.75 -> 1.026 > 1 -> id 0.
+    top_p = 1: u = 0.95 -> 1.428 > 1.368 -> id 2.  Catches: ids not carried with their logits, the
+    temperature or the top-p threshold misapplied, the draw scaled by the wrong total."""
+    z = np.zeros(4, np.float32)
+    z[[3, 0, 2, 1]] = [2, 1, 0, -1]
+    e1, e2 = math.exp(-1), math.exp(-2)
+    assert 0.8 * (1 + e1 + e2) > 1 and 0.8 * (1 + e1 + e2) < 1 + e1
+    assert sample_token(z, 1.0, 3, 0.8, 0.5) == 3
+    assert sample_token(z, 1.0, 3, 0.8, 0.75) == 0
+    assert sample_token(z, 1.0, 3, 0.8, 0.999) == 0
+    assert sample_token(z, 1.0, 3, 1.0, 0.95) == 2
+    assert sample_token(z, 1.0, 3, 1.0, 0.0) == 3
+    assert 0.95 * (1 + e1 + e2) > 1 + e1
+    # T = 0.5 doubles the gaps: weights 1, e^-2, e^-4; u = 0.9 of 1.154 = 1.039 > 1 -> id 0
+    assert 0.9 * (1 + e2 + math.exp(-4)) > 1
+    assert sample_token(z, 0.5, 3, 1.0, 0.9) == 0
+    # at T = 2 the gaps halve: weights 1, e^-0.5, e^-1 (total 1.974); u = 0.6 -> 1.185 < 1.607 -> id 0,
+    # u = 0.9 -> 1.777 > 1.607 -> id 2
+    assert 1 < 0.6 * (1 + math.exp(-0.5) + e1) < 1 + math.exp(-0.5) < 0.9 * (1 + math.exp(-0.5) + e1)
+    assert sample_token(z, 2.0, 3, 1.0, 0.6) == 0
+    assert sample_token(z, 2.0, 3, 1.0, 0.9) == 2
+
+
+def test_sampling_top1_and_tiny_top_p_are_the_argmax():
+    """top_k = 1, or top_p below the largest probability, leaves only the argmax (lowest id on
+    ties) whatever u is.  Catches: a filter that keeps too much, ties broken by the higher id."""
+    rng = np.random.default_rng(41)
+    for trial in range(20):
+        z = rng.standard_normal(50).astype(np.float32)
+        z[[7, 31]] = z.max() + 1.0  # a tie for the maximum: id 7 wins
+        for u in (0.0, 0.3, 0.999):
+            assert sample_token(z, 0.8, 1, 1.0, u) == 7
+            assert sample_token(z, 0.8, 10, 1e-6, u) == 7
+
+
+def test_sampling_frequencies_are_the_softmax():
+    """With every token kept, the fraction of a fine grid of uniforms that draws each token is
+    its softmax probability at temperature T (closed form, FP64).  Catches: temperature applied
+    as a product, a missing or doubled exponent, an offset draw."""
+    z = np.array([0.3, -1.2, 2.0, 0.7, -0.1, 1.1], np.float32)
+    for T in (0.7, 1.5):
+        p = np.exp(z.astype(np.float64) / T)
+        p /= p.sum()
+        f = _grid_frequencies(z, T, len(z), 1.0)
+        assert np.abs(f - p).max() < 2e-4, (T, f, p)
+
+
+def test_sampling_top_k_and_top_p_supports():
+    """top_k keeps the k largest logits and renormalises over them; top_p keeps the shortest
+    prefix reaching p of that total.  Frequencies equal the renormalised closed form and no other
+    token is ever drawn.  Catches: top-p taken over all V logits, the prefix one short or long,
+    no renormalisation."""
+    z = np.array([0.5, 2.5, -0.3, 1.9, 0.1, 2.2, -2.0, 1.0, 0.0, 1.4], np.float32)
+    T = 0.9
+    rank = np.argsort(-z, kind="stable")
+    for k, p in ((4, 1.0), (4, 0.6), (10, 0.9), (6, 0.5)):
+        w = np.exp((z[rank[:k]].astype(np.float64) - z[rank[0]]) / T)
+        c = np.cumsum(w) / w.sum()
+        n = int(np.argmax(c >= p)) + 1
+        expect = np.zeros(len(z))
+        expect[rank[:n]] = w[:n] / w[:n].sum()
+        f = _grid_frequencies(z, T, k, p)
+        assert np.abs(f - expect).max() < 2e-4, (k, p, f, expect)
+
+
+def test_sampling_equal_logits_take_increasing_ids():
+    """Equal logits rank by increasing token id: with logits 0, 3, 3, 3, 1 and top_k = 2 only ids 1
+    and 2 are ever drawn, half the time each.  Catches: ties by decreasing id, a top-p prefix
+    that must exceed p rather than reach it."""
+    z = np.array([0, 3, 3, 3, 1], np.float32)
+    f = _grid_frequencies(z, 1.0, 2, 1.0, n=4000)
+    assert np.allclose(f, [0, 0.5, 0.5, 0, 0])
+    # a prefix that reaches top_p exactly is long enough: four equal weights, top_p = 1/2 needs
+    # exactly 2 of 4 (exact in FP32), so only ids 0 and 1 are drawn
+    z = np.array([3, 3, 3, 3, 0], np.float32)
+    f = _grid_frequencies(z, 1.0, 4, 0.5, n=4000)
+    assert np.allclose(f, [0.5, 0.5, 0, 0, 0])
+
+
+def test_decode_sampling_uses_each_steps_uniform():
+    """A model whose logits are all exactly equal (identical embedding rows, tied head): with
+    top_k = 4 and T = 1 the weights are 1, 1, 1, 1 and the draw at step i is id floor(4 u_i), the
+    strict inequality putting u = 0.25 at id 1.  Catches: the uniform of another step, a
+    non-strict draw, decode not sampling."""
+    c = Cfg(vocab=16)
+    w = _zero_model(c, np.random.default_rng(19))
+    w["embed"] = _b(np.full((c.vocab, c.hidden), 0.25))
+    u = [0.1, 0.25, 0.6, 0.99, 0.5]
+    res = OracleModel(c, w, np.float32).decode(_kv(c, 8), 3, 0, 5, sampling=(1.0, 4, 1.0), uniforms=u)
+    assert np.all(res["logits"] == res["logits"][0][0])
+    assert list(res["tokens"]) == [0, 1, 2, 3, 2]

@@ -10,7 +10,8 @@ the shapes of the decoders in :mod:`configs`:
 * every RMSNorm gain ~ 1 + N(0, 0.01), rounded to BF16;
 * the KV cache ~ N(0, 1), rounded to BF16, optionally with keys multiplied by
   a per-(layer, KV head, channel) scale ~ U(0.5, 4) before rounding;
-* tokens ~ U[0, vocab).
+* tokens ~ U[0, vocab);
+* the uniforms of sampled decoding ~ U[0, 1), one per step, FP32.
 
 Each tensor has its own torch generator seeded from (seed, model, tensor
 index), in the canonical order embed, then per layer attn_norm, wq, wk, wv,
@@ -33,6 +34,7 @@ SEED_WEIGHTS = 0
 SEED_KV = 1
 SEED_TOKENS = 2
 SEED_KEY_SCALE = 3
+SEED_UNIFORMS = 4
 
 WEIGHT_STD = 0.02
 GAIN_STD = 0.01
@@ -134,6 +136,13 @@ def make_tokens(cfg: ModelConfig, n: int, seed: int = SEED_TOKENS) -> List[int]:
     """``n`` tokens ~ U[0, vocab) (CPU generator: identical on every box)."""
     g = _gen("cpu", _seed(seed, cfg, 0))
     return [int(t) for t in torch.randint(0, cfg.vocab, (n,), generator=g)]
+
+
+def make_uniforms(cfg: ModelConfig, n: int, seed: int = SEED_UNIFORMS) -> np.ndarray:
+    """``n`` FP32 uniforms in [0, 1), one per sampled step (CPU generator: identical on every box)."""
+    g = _gen("cpu", _seed(seed, cfg, 0))
+    u = torch.rand(n, generator=g, dtype=torch.float32).numpy()
+    return np.minimum(u, np.float32(1.0) - np.float32(2.0 ** -24))  # strictly below 1
 
 
 # --------------------------------------------------------------------------
