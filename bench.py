@@ -45,20 +45,26 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from oracle import OracleModel
+    from oracle import OracleModel, sample_token
+    from tile_scheduled_persistent_amd import synth
 
     w_bits, kv_bits = setup_bits
     o = OracleModel(m, w_bits, np.float32, weight_format=wl.weights)
     kv = {"k": kv_bits["k"].copy(), "v": kv_bits["v"].copy()}
+    uniforms = synth.make_uniforms(m, wl.n_steps)
+
+    def select(logits, i):
+        return int(np.argmax(logits)) if wl.sampling is None else sample_token(logits, *wl.sampling, float(uniforms[i]))
+
     t_prep = time.perf_counter()
     logits, _ = o.step(kv, token, wl.n_cached)  # warm-up (also widens the weights once)
     prep = time.perf_counter() - t_prep
-    tok = int(np.argmax(logits))
+    tok = select(logits, 0)
     n = 0
     t0 = time.perf_counter()
     while True:
         logits, _ = o.step(kv, tok, wl.n_cached + 1 + n)
-        tok = int(np.argmax(logits))
+        tok = select(logits, n + 1)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= wl.n_steps - 1:
@@ -181,6 +187,7 @@ def main():
     stream = torch.cuda.current_stream()
     plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
                       attn_heads=args.attn_heads, o_placement=args.o_placement, weight_format=wl.weights,
+                      sampling=wl.sampling,
                       stream=stream)
     info = plan.info()
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
@@ -188,9 +195,11 @@ def main():
     out_t = torch.zeros(n_tok, dtype=torch.int32, device=dev)
     out_l = torch.zeros((n_tok, m.vocab), dtype=torch.float32, device=dev)
 
+    uniforms = (torch.from_numpy(synth.make_uniforms(m, n_tok)).to(dev) if wl.sampling is not None else None)
+
     def launch():
         kv.length = wl.n_cached
-        plan.decode(kv, token, n_tok, out_t, None)
+        plan.decode(kv, token, n_tok, out_t, None, uniforms=uniforms)
 
     for _ in range(args.warmup):
         launch()
@@ -279,10 +288,13 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     from tile_scheduled_persistent_amd import tiles
 
     plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits, attn_heads=args.attn_heads,
-                      combine_mode=args.combine_mode, o_placement=args.o_placement, weight_format=wl.weights)
+                      combine_mode=args.combine_mode, o_placement=args.o_placement, weight_format=wl.weights,
+                      sampling=wl.sampling)
     kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
-    plan.decode(kv, token, wl.n_steps, out_t, None)
+    from tile_scheduled_persistent_amd import synth
+    uniforms = torch.from_numpy(synth.make_uniforms(m, wl.n_steps)).cuda() if wl.sampling is not None else None
+    plan.decode(kv, token, wl.n_steps, out_t, None, uniforms=uniforms)
     _, tr = plan.read_debug(hidden=False, trace=True)
     waves = plan.waves()
     plan.close()

@@ -84,6 +84,17 @@ typedef struct tiles_config {
                              codes with one FP32 scale per row, quantized from the BF16 weights at plan
                              creation (see tiles_quantize_rows_int8) and dequantized in registers; the
                              norm gains and the embedding lookup stay BF16 */
+  /* Sampled decoding ("History and roadmap" (TileInfer.jl), "M8 so far" table: top-k/top-p sampling
+   * on the device, inside the graph).  top_k = 0: greedy (tiles_decode).  1 <= top_k <= 32 (and
+   * <= vocab): the plan samples (tiles_decode_sampled): rank the logits in decreasing order (equal
+   * logits by increasing id), keep the first top_k, weigh them by exp((z - z_max) / temperature),
+   * keep the shortest prefix whose cumulative weight reaches top_p of the kept total (at least one
+   * token), and draw the first token of the prefix whose cumulative weight exceeds u * (prefix
+   * total), u being the step's uniform; every sum and comparison in FP32, sums in ranking order.
+   * Needs temperature > 0 (finite) and 0 < top_p <= 1; both ignored when top_k = 0. */
+  int32_t top_k;
+  float temperature;
+  float top_p;
 } tiles_config_t;
 
 #define TILES_WEIGHTS_BF16 0
@@ -137,6 +148,7 @@ typedef struct tiles_plan_info {
   int32_t attn_heads;         /* query heads per attention tile */
   int32_t o_workers;          /* workers holding o_proj tiles (all, or those without an attention tile) */
   int32_t weight_format;      /* TILES_WEIGHTS_BF16 or TILES_WEIGHTS_INT8 */
+  int32_t top_k;              /* 0: greedy plan; else the plan samples (tiles_decode_sampled) */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */
@@ -170,6 +182,18 @@ tiles_plan_t *tiles_plan_create(const tiles_config_t *cfg, const tiles_weights_t
  * Allocates nothing. */
 int tiles_decode(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, int32_t *out_tokens,
                  float *out_logits);
+
+/* Sampled decoding ("History and roadmap" (TileInfer.jl), "M8 so far" table: top-k/top-p sampling on
+ * the device, inside the graph): as tiles_decode, but step i stores in out_tokens[i] the token drawn
+ * from its logits with the plan's top_k / temperature / top_p (see tiles_config_t) and the uniform
+ * uniforms[i], in the same cooperative launch (every worker draws the same token from every
+ * worker's top_k candidates; no host round trip).
+ *   uniforms : device float [n_steps], each in [0, 1) (values outside are clamped into it; NaN
+ *              counts as 0).  The caller owns it; it is read during the launch.
+ * Errors as tiles_decode, plus TILES_E_ARG for a greedy plan (top_k = 0) or null uniforms;
+ * tiles_decode and tiles_decode_noalloc return TILES_E_ARG for a sampling plan.  Allocates nothing. */
+int tiles_decode_sampled(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, const float *uniforms,
+                         int32_t *out_tokens, float *out_logits);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): tiles_decode with the same arguments, semantics and results,

@@ -144,3 +144,68 @@ def compare_free_running(tag, g_tokens, g_logits, g_hidden, o_res, n_check: int)
         if int(g_tokens[i]) != int(o_res["tokens"][i]):
             break  # inputs of later steps differ; allowed only at a low-margin step (checked above)
     return compared
+
+
+# Sampled decoding: both sides draw in FP32 from logits that differ by summation order (max-abs
+# about 1e-4 on the shapes tested), so a draw is compared exactly unless the oracle's sits near a
+# decision boundary: the K-th and (K+1)-th largest logits within SAMPLE_DELTA_Z, or a cumulative
+# weight within SAMPLE_DELTA_REL (relative) of the top-p threshold or of the draw's target.  A logit
+# error e moves a weight by about e / T relative: at T >= 0.3 and e <= 2e-4 that is 7e-4, under the
+# 2e-3 band.  Near a boundary the GPU's token must be one of the oracle's top_k + 1 candidates.
+SAMPLE_DELTA_Z = 1e-3
+SAMPLE_DELTA_REL = 2e-3
+
+
+def check_sampled_token(tag: str, g_tok: int, o_logits: np.ndarray, sampling, u: float) -> bool:
+    """Assert the GPU's sampled token against the oracle's S1 draw from the oracle's logits with
+    the same uniform.  Returns True when the draw was compared exactly."""
+    from oracle import sample_token
+
+    T, K, P = sampling
+    tok, d = sample_token(o_logits, T, K, P, float(u), detail=True)
+    z = np.asarray(o_logits, np.float32)
+    rank = np.lexsort((np.arange(len(z)), -z))
+    cum = d["cum"].astype(np.float64)
+    n, total = d["n"], float(cum[-1])
+    near = K < len(z) and float(z[rank[K - 1]]) - float(z[rank[K]]) < SAMPLE_DELTA_Z
+    # (the last candidate's sum is the total: whether it reaches the threshold never changes the prefix)
+    near = near or bool(np.any(np.abs(cum[:-1] - float(d["need"])) < SAMPLE_DELTA_REL * total))
+    near = near or bool(np.any(np.abs(cum[:n] - float(d["target"])) < SAMPLE_DELTA_REL * float(cum[n - 1])))
+    if not near:
+        assert g_tok == tok, f"{tag}: sampled token {g_tok} != oracle {tok} (u = {u})"
+        return True
+    assert g_tok in set(int(x) for x in rank[:K + 1]), f"{tag}: sampled token {g_tok} not among the top {K + 1}"
+    return False
+
+
+def run_gpu_sampled(plan: tiles.Plan, kv: tiles.KVCache, token: int, n: int, uniforms: np.ndarray, want_hidden=True):
+    """One sampled launch of n steps with the given uniforms: (tokens [n], logits [n, V], hidden)."""
+    out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+    out_l = torch.zeros((n, plan.model.vocab), dtype=torch.float32, device="cuda")
+    u = torch.from_numpy(np.ascontiguousarray(uniforms[:n], dtype=np.float32)).cuda()
+    plan.decode(kv, token, n, out_t, out_l, uniforms=u)
+    assert plan.status() == tiles.TILES_OK, tiles.last_error()
+    torch.cuda.synchronize()
+    hid = plan.read_debug(hidden=True)[0] if want_hidden else None
+    return out_t.cpu().numpy().astype(np.int64), out_l.cpu().numpy(), hid
+
+
+def compare_sampled_teacher_forced(tag, g_tokens, g_logits, g_hidden, o_res, sampling, uniforms):
+    """Every step of a sampled GPU launch against an oracle teacher-forced on the GPU's tokens
+    (same uniforms): hidden and logit bars as for greedy steps, and check_sampled_token.
+    Returns the observed errors and the number of exactly compared draws."""
+    n = len(g_tokens)
+    assert o_res["logits"].shape[0] == n
+    worst_h, worst_l, exact = 0.0, 0.0, 0
+    for i in range(n):
+        if g_hidden is not None:
+            num = np.linalg.norm((g_hidden[i] - o_res["hidden"][i]).astype(np.float64), axis=-1)
+            den = np.linalg.norm(o_res["hidden"][i].astype(np.float64), axis=-1)
+            h = float((num / den).max())
+            assert h <= HIDDEN_REL_L2, f"{tag} step {i}: hidden rel L2 {h:.3e}"  # (fails on NaN too)
+            worst_h = max(worst_h, h)
+        err = float(np.abs(g_logits[i].astype(np.float64) - o_res["logits"][i]).max())
+        assert err <= LOGIT_MAX_ABS, f"{tag} step {i}: logits max abs err {err:.3e}"
+        worst_l = max(worst_l, err)
+        exact += check_sampled_token(f"{tag} step {i}", int(g_tokens[i]), o_res["logits"][i], sampling, uniforms[i])
+    return {"steps": n, "hidden_rel_l2_max": worst_h, "logit_abs_max": worst_l, "draws_exact": exact}

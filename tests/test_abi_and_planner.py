@@ -35,6 +35,7 @@ def test_null_arguments_are_rejected_without_a_gpu():
     L = tiles.lib()
     assert L.tiles_decode(None, None, 0, 1, None, None) == tiles.TILES_E_ARG
     assert L.tiles_decode_noalloc(None, None, 0, 1, None, None) == tiles.TILES_E_ARG
+    assert L.tiles_decode_sampled(None, None, 0, 1, None, None, None) == tiles.TILES_E_ARG
     assert "null" in tiles.last_error()
     assert L.tiles_plan_create(None, None) is None
     L.tiles_plan_destroy(None)  # NULL-safe
@@ -244,3 +245,34 @@ def test_int8_plan_of_ragged_and_untied_shapes():
     assert tiles.debug_validate(m, 64, 0, weights="int8") == tiles.TILES_OK, tiles.last_error()
     for mutation in (12, 13):  # packed rows exchanged, a packing copy dropped
         assert tiles.debug_validate(m, 64, mutation, weights="int8") == tiles.TILES_E_PLAN
+
+
+@pytest.mark.parametrize("m,sampling", [(TINY, (0.7, 32, 0.9)), (LLAMA_1B, (0.6, 20, 0.95)), (QWEN3_06B, (1.0, 1, 1.0)),
+                                        (QWEN3_4B, (0.6, 32, 0.95))])
+def test_sampling_plans_validate(m, sampling):
+    """Sampling plans carry top_k and leave room in LDS for every worker's top_k candidates
+    (2 words each) in the token gather; the LDS total stays within the CU's 160 KB."""
+    info = tiles.dry_run(m, 1100, sampling=sampling)
+    assert info.top_k == sampling[1]
+    assert info.lds_bytes <= 160 * 1024
+    greedy = tiles.dry_run(m, 1100)
+    assert greedy.top_k == 0 and greedy.checksum != info.checksum
+
+
+@pytest.mark.parametrize("sampling", [(1.0, 33, 0.9), (0.0, 8, 0.9), (-1.0, 8, 0.9), (float("inf"), 8, 0.9),
+                                      (float("nan"), 8, 0.9), (1.0, 8, 0.0), (1.0, 8, 1.5), (1.0, 8, float("nan")),
+                                      (1.0, -1, 0.9)])
+def test_bad_sampling_parameters_are_rejected(sampling):
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(TINY, 40, sampling=sampling)
+    assert e.value.code == tiles.TILES_E_CONFIG
+
+
+def test_sampling_limits_top_k_by_vocab_and_workers():
+    small_vocab = scaled(TINY, name="v16", vocab=16)
+    with pytest.raises(tiles.TilesError):
+        tiles.dry_run(small_vocab, 40, sampling=(1.0, 17, 1.0))
+    assert tiles.dry_run(small_vocab, 40, sampling=(1.0, 16, 1.0)).top_k == 16
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(TINY, 40, n_workers=300, sampling=(1.0, 8, 1.0))
+    assert "256 workers" in tiles.last_error() or e.value.code == tiles.TILES_E_CONFIG

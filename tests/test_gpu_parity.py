@@ -2,6 +2,8 @@
 the C ABI).  Small models are compared at every step; the full-size workloads
 are compared on the steps the oracle can reproduce from its own inputs."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -9,8 +11,8 @@ import torch
 from tile_scheduled_persistent_amd import synth, tiles
 from tile_scheduled_persistent_amd.configs import TINY, WORKLOADS, scaled
 
-from parity_util import (HIDDEN_REL_L2, Setup, check_step, compare_free_running, compare_teacher_forced,
-                         kv_rows_close, run_gpu, top2_margin)
+from parity_util import (HIDDEN_REL_L2, Setup, check_step, compare_free_running, compare_sampled_teacher_forced,
+                         compare_teacher_forced, kv_rows_close, run_gpu, run_gpu_sampled, top2_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -479,3 +481,154 @@ def test_int8_repeatable_and_chunk_invariant():
             assert int(t1[0]) == int(a[0][i])
             assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
             t = int(t1[0])
+
+
+
+# ---------------------------------------------------------------------------
+# sampled decoding (top-k / top-p inside the launch)
+# ---------------------------------------------------------------------------
+
+SAMPLINGS = [(0.7, 20, 0.95), (1.5, 32, 1.0), (0.3, 5, 0.5), (1.0, 1, 1.0)]
+
+
+@pytest.mark.parametrize("sampling", SAMPLINGS, ids=[f"T{t}-k{k}-p{p}" for t, k, p in SAMPLINGS])
+def test_sampled_tiny_every_step_against_oracle(sampling):
+    """One sampled launch of 20 steps after 10 cached positions, every step against the oracle
+    teacher-forced on the GPU's tokens with the same uniforms: hidden states, logits and the draw
+    (exact away from a decision boundary, among the top k + 1 near one); the K/V rows written."""
+    n, cached = 20, 10
+    s = Setup(TINY, cached + n + 2, cached)
+    tok = synth.make_tokens(TINY, 1)[0]
+    u = synth.make_uniforms(TINY, n)
+    kv = s.fresh_kv()
+    with s.plan(sampling=sampling) as plan:
+        assert plan.info().top_k == sampling[1]
+        g_t, g_l, g_h = run_gpu_sampled(plan, kv, tok, n, u)
+    okv = s.oracle_kv()
+    o_res = s.oracle().decode(okv, tok, cached, n, teacher=[int(t) for t in g_t[:-1]], sampling=sampling, uniforms=u)
+    stats = compare_sampled_teacher_forced(f"tiny sampled {sampling}", g_t, g_l, g_h, o_res, sampling, u)
+    print(f"tiny sampled {sampling}: {stats}", flush=True)
+    assert stats["steps"] == n and stats["draws_exact"] >= n // 2
+    kv_rows_close("tiny sampled K", kv.k, okv["k"], cached, n)
+    kv_rows_close("tiny sampled V", kv.v, okv["v"], cached, n)
+
+
+def test_sampled_top1_equals_greedy_bit_for_bit():
+    """top_k = 1 keeps only the argmax (lowest id on ties), whatever T, top_p and u: the sampled
+    launch gives the greedy launch's tokens, logits and cache bytes exactly."""
+    s = Setup(WIDE, 96, 70)
+    tok = synth.make_tokens(WIDE, 1)[0]
+    n = 12
+    kv_g = s.fresh_kv()
+    with s.plan() as plan:
+        g = run_gpu(plan, kv_g, tok, n)
+    kv_s = s.fresh_kv()
+    with s.plan(sampling=(0.8, 1, 0.5)) as plan:
+        r = run_gpu_sampled(plan, kv_s, tok, n, synth.make_uniforms(WIDE, n))
+    assert np.array_equal(g[0], r[0])
+    assert np.array_equal(g[1].view(np.uint32), r[1].view(np.uint32))
+    assert torch.equal(kv_g.k, kv_s.k) and torch.equal(kv_g.v, kv_s.v)
+
+
+def test_sampled_repeatable_and_chunk_invariant():
+    """A sampled launch repeats bit for bit, and n one-step launches (each with its step's uniform)
+    give the n-step launch's tokens and logits exactly."""
+    s = Setup(WIDE, 96, 70)
+    sampling = (0.8, 16, 0.9)
+    tok = synth.make_tokens(WIDE, 1)[0]
+    n = 10
+    u = synth.make_uniforms(WIDE, n)
+    with s.plan(sampling=sampling) as plan:
+        kv_a = s.fresh_kv()
+        a = run_gpu_sampled(plan, kv_a, tok, n, u)
+        kv_b = s.fresh_kv()
+        b = run_gpu_sampled(plan, kv_b, tok, n, u)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+        assert torch.equal(kv_a.k, kv_b.k) and torch.equal(kv_a.v, kv_b.v)
+        kv = s.fresh_kv()
+        t = tok
+        for i in range(n):
+            t1, l1, _ = run_gpu_sampled(plan, kv, t, 1, u[i:i + 1], want_hidden=False)
+            assert int(t1[0]) == int(a[0][i])
+            assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
+            t = int(t1[0])
+        assert torch.equal(kv.k, kv_a.k) and torch.equal(kv.v, kv_a.v)
+
+
+def test_sampled_equal_logits_draw_in_closed_form():
+    """A model whose logits are all exactly equal (zero linear weights, identical embedding rows,
+    tied head): the top_k candidates are ids 0 .. k - 1 with weight 1 each, so with top_k = 32 the
+    draw at step i is id floor(32 u_i), and with top_p = 1/2 the prefix is 16 long and the draw
+    floor(16 u_i) (exact in FP32: the cumulative weights are the integers 1 .. 32)."""
+    m = TINY
+    w = synth.make_weights(m, device="cuda")
+    for d in w["layers"]:
+        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            d[name].zero_()
+    w["embed"].fill_(0.25)
+    k = torch.zeros((m.n_layers, m.n_kv_heads, 16, m.head_dim), dtype=torch.bfloat16, device="cuda")
+    u = np.array([0.0, 0.03, 0.5, 0.249, 0.25, 0.97, 0.999, 0.6, 0.7812, 0.1], np.float32)
+    n = len(u)
+    for top_p, width in ((1.0, 32), (0.5, 16)):
+        kv = tiles.KVCache(k.clone(), k.clone(), 2)
+        with tiles.Plan(m, w, 16, sampling=(0.9, 32, top_p)) as plan:
+            g_t, g_l, _ = run_gpu_sampled(plan, kv, 7, n, u, want_hidden=False)
+        assert np.all(g_l == g_l[:, :1]), "logits not all equal"
+        assert list(g_t) == [int(np.floor(width * float(x))) for x in u], (top_p, list(g_t))
+
+
+def test_sampling_entry_point_errors():
+    s = Setup(TINY, 40, 10)
+    out = torch.zeros(2, dtype=torch.int32, device="cuda")
+    u = torch.full((2,), 0.5, dtype=torch.float32, device="cuda")
+    kv = s.fresh_kv()
+    with s.plan(sampling=(1.0, 4, 1.0)) as plan:
+        with pytest.raises(tiles.TilesError) as e:
+            plan.decode(kv, 0, 2, out)  # a sampling plan needs the uniforms
+        assert e.value.code == tiles.TILES_E_ARG
+        c = tiles.KV(kv.k.data_ptr(), kv.v.data_ptr(), kv.capacity, kv.length)
+        assert tiles.lib().tiles_decode(plan._h, ctypes.byref(c), 0, 2, out.data_ptr(), None) == tiles.TILES_E_ARG
+        assert "tiles_decode_sampled" in tiles.last_error()
+        assert tiles.lib().tiles_decode_noalloc(plan._h, ctypes.byref(c), 0, 2, out.data_ptr(), None) == tiles.TILES_E_ARG
+    with s.plan() as greedy:
+        with pytest.raises(tiles.TilesError) as e:
+            greedy.decode(kv, 0, 2, out, uniforms=u)
+        assert e.value.code == tiles.TILES_E_ARG
+    assert kv.length == 10
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_size_sampled_every_step():
+    """The sampled launch bench.py times (Llama-3.2-1B shape, 64 steps, T 0.6, top-k 20, top-p
+    0.95), every step against the oracle teacher-forced on the GPU's tokens with the same
+    uniforms; the timed configuration (no debug buffers, no logits) gives the same tokens and
+    cache bytes."""
+    key = "llama1b_sampled"
+    wl = WORKLOADS[key]
+    m, n = wl.model, wl.n_steps
+    s = Setup(m, wl.capacity, wl.n_cached, gen_device="cuda")
+    tok = synth.make_tokens(m, 1)[0]
+    u = synth.make_uniforms(m, n)
+    kv_timed = s.fresh_kv()
+    with s.plan(flags=0, sampling=wl.sampling) as plan:
+        out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+        plan.decode(kv_timed, tok, n, out_t, None, uniforms=torch.from_numpy(u).cuda())
+        assert plan.status() == tiles.TILES_OK, tiles.last_error()
+        timed_tokens = out_t.cpu().numpy().astype(np.int64)
+    kv = s.fresh_kv()
+    with s.plan(sampling=wl.sampling) as plan:
+        g_t, g_l, g_h = run_gpu_sampled(plan, kv, tok, n, u)
+    assert np.array_equal(timed_tokens, g_t), "timed configuration gives other tokens"
+    assert torch.equal(kv_timed.k.view(torch.int16), kv.k.view(torch.int16))
+    assert torch.equal(kv_timed.v.view(torch.int16), kv.v.view(torch.int16))
+    del kv_timed
+    print(f"{key}: GPU launch of {n} steps done; teacher-forced oracle for all {n} steps", flush=True)
+    okv = s.oracle_kv()
+    o_res = s.oracle().decode(okv, tok, wl.n_cached, n, teacher=[int(t) for t in g_t[:-1]], widen_kv_once=True,
+                              sampling=wl.sampling, uniforms=u)
+    stats = compare_sampled_teacher_forced(key, g_t, g_l, g_h, o_res, wl.sampling, u)
+    assert stats["steps"] == n and stats["draws_exact"] >= n // 2
+    print(f"{key}: {n} of {n} steps compared; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
+          f"{stats['logit_abs_max']:.2e}, draws compared exactly {stats['draws_exact']} of {n}; distinct tokens "
+          f"{len(set(g_t.tolist()))}", flush=True)

@@ -15,7 +15,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtiles.so")
-SOURCES = ["kernel.hip", "planner.cpp", "api.cpp"]
+# The worker units each instantiate the persistent worker for one weight format and token selection
+# (they include kernel.hip); every source compiles to an object of its own, in parallel, then links.
+SOURCES = ["kernel.hip", "workers_bf16.hip", "workers_bf16_sampled.hip", "workers_int8.hip",
+           "workers_int8_sampled.hip", "planner.cpp", "api.cpp"]
 HEADERS = ["plan_types.h", "planner.h"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -36,18 +39,33 @@ def build_id() -> str:
     return "0x" + h.hexdigest()[:16] + "ull"
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", *DEVICE_FLAGS,
-           f"-DTILES_BUILD_ID={build_id()}", "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd[-3:])}\n{errs}")
     if verbose and errs:
         print(errs, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
+
+    bid = build_id()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    common = [HIPCC, "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", *DEVICE_FLAGS,
+              f"-DTILES_BUILD_ID={bid}", "-I", os.path.join(ROOT, "include")]
+    objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_run, common + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+                for src, obj in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -12,7 +12,7 @@ positions).  Weights are random (no checkpoints are used); see ``synth``.
 from __future__ import annotations
 
 from dataclasses import dataclass, field, replace
-from typing import Dict
+from typing import Dict, Optional
 
 
 @dataclass(frozen=True)
@@ -81,6 +81,7 @@ class Workload:
     key_scale: bool = False      # per-(layer, kv head, channel) key scales ~ U(0.5, 4)
     description: str = ""
     weights: str = "bf16"        # "int8": weight-only INT8 linear layers (per-row codes and scales)
+    sampling: Optional[tuple] = None  # (temperature, top_k, top_p): sampled steps instead of greedy
 
     @property
     def capacity(self) -> int:
@@ -118,6 +119,10 @@ WORKLOADS: Dict[str, Workload] = {
                            description="Qwen3-4B-shaped decode, 32 tokens after 32767 cached positions, "
                                        "per-channel key scales"),
     # weight-only INT8 linear layers (the roadmap page's "M8 so far" row), same shapes and inputs
+    "llama1b_sampled": Workload("llama1b_sampled", LLAMA_1B, 1023, 64, sampling=(0.6, 20, 0.95),
+                                description="Llama-3.2-1B-shaped decode with top-k/top-p sampling inside the launch "
+                                            "(temperature 0.6, top-k 20, top-p 0.95), 64 tokens after 1023 cached "
+                                            "positions"),
     "llama1b_int8": Workload("llama1b_int8", LLAMA_1B, 1023, 64, weights="int8",
                              description="Llama-3.2-1B-shaped decode with weight-only INT8 linear layers, "
                                          "64 tokens after 1023 cached positions"),

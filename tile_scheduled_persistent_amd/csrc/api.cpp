@@ -30,7 +30,7 @@
 #endif
 
 namespace tiles {
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8);
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
@@ -231,7 +231,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0);
+  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0, hp.top_k > 0);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -337,7 +337,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
       return o;
     };
     const size_t o_ll = piece((size_t)hp.ll_words * 4);
-    const size_t o_lm = piece((size_t)hp.W * 8);
+    const size_t o_lm = piece((size_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1));
     const size_t lm_end = off;
     p->sync_bytes = (size_t)SYNC_WORDS * 4;
     const size_t o_sync = piece(p->sync_bytes);
@@ -378,8 +378,11 @@ int check_identity(const tiles_plan* p) {
 // partials and status words live in the file-scope scratch array of this GPU (see
 // noalloc_scratch) instead of the plan's own buffers; the layout is the same.
 int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
-                float* out_logits, bool noalloc) {
+                float* out_logits, bool noalloc, const float* uniforms) {
   if (!p || !kv || !out_tokens) return set_err(TILES_E_ARG, "null plan, kv or out_tokens");
+  if (p->hp.top_k > 0 && !uniforms)
+    return set_err(TILES_E_ARG, "this plan samples (top_k > 0): use tiles_decode_sampled with the step uniforms");
+  if (p->hp.top_k == 0 && uniforms) return set_err(TILES_E_ARG, "this plan is greedy (top_k = 0): use tiles_decode");
   if (!kv->k || !kv->v) return set_err(TILES_E_ARG, "null KV buffers");
   if (n_steps < 1 || n_steps > MAX_STEPS) return set_err(TILES_E_ARG, "n_steps must be in [1, 64]");
   const HostPlan& hp = p->hp;
@@ -405,7 +408,7 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   uint32_t* sync = p->sync;
   if (noalloc) {
     const int64_t ll_bytes = ((int64_t)hp.ll_words * 4 + 255) / 256 * 256;
-    const int64_t lm_bytes = ((int64_t)hp.W * 8 + 255) / 256 * 256;
+    const int64_t lm_bytes = ((int64_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1) + 255) / 256 * 256;
     const int64_t need = ll_bytes + lm_bytes + SYNC_WORDS * 4;
     if (need > NOALLOC_SCRATCH_BYTES)
       return set_err(TILES_E_ARG, "this plan's tagged scratch (" + std::to_string(need) +
@@ -426,6 +429,10 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   a.kv_cap = kv->capacity;
   a.out_tokens = out_tokens;
   a.out_logits = out_logits;
+  a.uniforms = uniforms;
+  a.top_k = hp.top_k;
+  a.temperature = hp.temperature;
+  a.top_p = hp.top_p;
   a.dbg_hidden = p->dbg_hidden;
   a.trace = p->trace;
   a.token0 = token;
@@ -491,12 +498,19 @@ tiles_plan_t* tiles_plan_create(const tiles_config_t* cfg, const tiles_weights_t
 
 int tiles_decode(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
                  float* out_logits) {
-  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, false);
+  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, false, nullptr);
+}
+
+int tiles_decode_sampled(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, const float* uniforms,
+                         int32_t* out_tokens, float* out_logits) {
+  if (p && p->hp.top_k == 0) return set_err(TILES_E_ARG, "this plan is greedy (top_k = 0): use tiles_decode");
+  if (!uniforms) return set_err(TILES_E_ARG, "null uniforms");
+  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, false, uniforms);
 }
 
 int tiles_decode_noalloc(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
                          float* out_logits) {
-  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, true);
+  return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, true, nullptr);
 }
 
 void tiles_plan_destroy(tiles_plan_t* p) { release(p); }
@@ -516,6 +530,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->combine_mode = hp.combine_in_o ? 1 : 2;
   info->attn_heads = hp.T;
   info->weight_format = hp.q8 ? TILES_WEIGHTS_INT8 : TILES_WEIGHTS_BF16;
+  info->top_k = hp.top_k;
   for (size_t wv = 0; wv < hp.waves.size(); ++wv)
     if (hp.waves[wv].kind == KIND_O) {
       info->o_workers = hp.wave_busy[wv];
@@ -614,8 +629,10 @@ int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   const uint32_t limit = rounds ? rounds : DEFAULT_SPIN_LIMIT;
   if (limit < 32 && !p->kernel_wd) {
-    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0);
-    if (!k) return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and one query head per attention tile");
+    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0);
+    if (!k)
+      return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights, greedy decoding and one query head "
+                                     "per attention tile");
     HIP_TRY(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p->hp.lds_bytes));
     int occ = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, BLOCK_THREADS, p->hp.lds_bytes));

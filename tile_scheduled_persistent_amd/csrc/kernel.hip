@@ -83,6 +83,9 @@ __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void st_u64_release(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Buffer descriptor over a scratch array (byte offsets < 4 GB).  Device-coherent buffer
 // loads through it are plain (non-atomic) loads the compiler can issue back to back.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
@@ -468,6 +471,180 @@ __device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint
   // loads above this point.
   COMPILER_FENCE();
   return false;
+}
+
+// ---------------------------------------------------------------------------
+// sampled decoding (top-k / top-p): every worker publishes its top_k logits; every worker then
+// merges all W lists and draws the same token with the step's uniform
+// ---------------------------------------------------------------------------
+
+// A candidate as one 64-bit key: larger logit first, then lower token id (the order of ranking and
+// of ties); 0 stands for "none" (no real candidate has key 0: its low word ~id is >= 2^31).
+__device__ __forceinline__ uint64_t cand_key(float v, int idx) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;  // -0 ranks as +0
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~(uint32_t)idx;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t b = (uint32_t)(k >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t xor16_64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const bool up = (lane >> 4) & 1;
+  return ((uint64_t)(up ? b[0] : b[1]) << 32) | (up ? a[0] : a[1]);
+}
+__device__ __forceinline__ uint64_t xor32_64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const bool up = lane >= 32;
+  return ((uint64_t)(up ? b[0] : b[1]) << 32) | (up ? a[0] : a[1]);
+}
+// the largest key of the wavefront, in every lane
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k, int lane) {
+  k = key_max(k, dpp64<DPP_XOR1>(k));
+  k = key_max(k, dpp64<DPP_XOR2>(k));
+  k = key_max(k, dpp64<DPP_HALF_MIRROR>(k));
+  k = key_max(k, dpp64<DPP_MIRROR>(k));
+  k = key_max(k, xor16_64(k, lane));
+  return key_max(k, xor32_64(k, lane));
+}
+
+// The K largest of a running list (lane i holds its i-th entry, 0 if none) and this lane's NC
+// candidates c[] (0 = none): K rounds of a wavefront maximum, each removing its winner.
+template <int NC>
+__device__ __forceinline__ void topk_merge(uint64_t& run, uint64_t (&c)[NC], int K, int lane) {
+  uint64_t nk = 0;
+  for (int r = 0; r < K; ++r) {
+    uint64_t m = run;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) m = key_max(m, c[j]);
+    const uint64_t w = wave_max_key(m, lane);
+    if (w == 0) break;  // (uniform) nothing left
+    if (run == w) run = 0;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) c[j] = c[j] == w ? 0 : c[j];
+    nk = lane == r ? w : nk;
+  }
+  run = nk;
+}
+
+// Poll the W x top_k candidate words of the step with parity `par` (value bits, id | parity << 31)
+// into LDS (from L.vec on, in worker-major order): one wavefront, GB 16-byte units per lane in
+// flight.  Returns true when the wait was abandoned.
+template <bool WD>
+__device__ __forceinline__ bool poll_candidates(const KernelArgs& a, const Lds& L, int lane, uint32_t par) {
+  constexpr int GB = 16;
+  constexpr int slot = 0, nslots = 1;
+  const int nwords = a.W * a.top_k;
+  const int nunits = (nwords + 1) / 2;
+  const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
+  for (int base = 0; base < nunits; base += GB * nslots * 64) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int i = 0; i < GB; ++i)
+      if (base + (i * nslots + slot) * 64 + lane < nunits) pending |= 1u << i;
+    uint32_t spins = 0;
+    for (;;) {
+      u32x4 v[GB];
+      COMPILER_FENCE();
+#pragma unroll
+      for (int i = 0; i < GB; ++i) {
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        if ((pending >> i) & 1u) v[i] = cld4(r, (uint32_t)(base + (i * nslots + slot) * 64 + lane) * 16u);
+      }
+      COMPILER_FENCE();
+#pragma unroll
+      for (int i = 0; i < GB; ++i) {
+        const int u = base + (i * nslots + slot) * 64 + lane;
+        const bool two = 2 * u + 1 < nwords;
+        if (((pending >> i) & 1u) && (v[i].y >> 31) == par && (!two || (v[i].w >> 31) == par)) {
+          *reinterpret_cast<u32x4*>(L.vec + 4 * u) = v[i];
+          pending &= ~(1u << i);
+        }
+      }
+      if (__all(pending == 0)) break;
+      if (watch_tick<WD>(a, spins, lane)) return true;
+    }
+  }
+  return false;
+}
+
+// The sampled token from the candidates in LDS (control wavefront, after poll_candidates): the W
+// sorted lists merged into the global top_k (K rounds of a wavefront maximum over the list heads;
+// lane l merges lists l, l + 64, l + 128, l + 192), then the top-k / temperature / top-p draw with
+// the uniform u, in FP32, the running sums taken in ranking order.
+__device__ __forceinline__ int draw_token(const KernelArgs& a, const Lds& L, int lane, float u) {
+  constexpr int NL = 4;  // W <= 256
+  const int K = a.top_k;
+  auto load = [&](int w, int i) -> uint64_t {
+    if (w >= a.W || i >= K) return 0;
+    const uint2 c = *reinterpret_cast<const uint2*>(L.vec + 2 * (w * K + i));
+    return cand_key(__uint_as_float(c.x), (int)(c.y & 0x7fffffffu));
+  };
+  int ptr[NL];
+  uint64_t head[NL], next[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    ptr[q] = 0;
+    head[q] = load(lane + 64 * q, 0);
+    next[q] = load(lane + 64 * q, 1);
+  }
+  uint64_t mine = 0;  // lane r: the r-th largest candidate
+  for (int r = 0; r < K; ++r) {
+    uint64_t m = head[0];
+#pragma unroll
+    for (int q = 1; q < NL; ++q) m = key_max(m, head[q]);
+    const uint64_t w = wave_max_key(m, lane);
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      if (w != 0 && head[q] == w) {
+        head[q] = next[q];
+        ++ptr[q];
+        next[q] = load(lane + 64 * q, ptr[q] + 1);
+      }
+    }
+    mine = lane == r ? w : mine;
+  }
+  const bool valid = lane < K && mine != 0;
+  const float z = valid ? key_value(mine) : 0.f;
+  const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 0));
+  const float wgt = valid ? expf((z - z0) / a.temperature) : 0.f;
+  float run = 0.f, cum = 0.f;
+  for (int r = 0; r < K; ++r) {
+    run += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), r));
+    cum = lane == r ? run : cum;
+  }
+  const int nvalid = __popcll(__ballot(valid));
+  // the shortest prefix whose sum reaches top_p of the total (at least one candidate)
+  const float need = a.top_p * run;
+  int n = __popcll(__ballot(valid && cum < need)) + 1;
+  n = n < nvalid ? n : nvalid;
+  if (n < 1) n = 1;
+  const float pref = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), n - 1));
+  u = fminf(fmaxf(u, 0.f), 0x1.fffffep-1f);  // [0, 1); NaN -> 0
+  const float target = u * pref;
+  int pos = __popcll(__ballot(lane < n && cum <= target));  // the first prefix entry whose sum exceeds it
+  pos = pos < n ? pos : n - 1;
+  const uint64_t pick = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), pos) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, pos);
+  int tok = pick ? key_index(pick) : 0;
+  if (tok < 0 || tok >= a.V) tok = 0;  // only reachable with non-finite logits
+  // the acquire side of the per-step all-to-all, as for the greedy token (see gather_token)
+  COMPILER_FENCE();
+  return tok;
 }
 
 // ---------------------------------------------------------------------------
@@ -1310,7 +1487,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G, bool CTRL, bool WD, bool Q8>
+template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
@@ -1330,18 +1507,35 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
                                            : a.final_norm_off;
       const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
       float ss = 0.f;
+      bool ctrl_pads = false;  // the control wavefront alone zeroes the input's padding (after its LDS use)
       if (gk == KIND_QKV && layer == 0) {
-        if (CTRL) {
-          if (step > 0) {
-            ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
-            if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+        if (SMP && step > 0) {
+          ctrl_pads = true;
+          // sampled decoding: the control wavefront polls the previous step's candidates into LDS
+          // (over the input-vector and row-partial areas: the compute wavefronts have left the LM
+          // tile and wait at barrier P, and its own epilogue is done) and draws the token; its
+          // uniform is loaded before the polls.  The compute wavefronts' code is the greedy one.
+          if (CTRL) {
+            const float u = a.uniforms[step - 1];
+            ab = poll_candidates<WD>(a, L, lane, step_parity(step - 1));
+            if (!ab) {
+              tok = draw_token(a, L, lane, u);
+              if (bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+            }
           }
-          if (!ab) ss = stage_embedding<Q8>(a, L, tok, gain, lane);
+        } else if (CTRL && step > 0) {
+          ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
+          if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
         }
+        if (CTRL && !ab) ss = stage_embedding<Q8>(a, L, tok, gain, lane);
       } else {
         ab = gather_norm<WD, Q8>(a, L, in, a.H, gain, wave, lane, par, ss);
       }
-      for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
+      if (!ctrl_pads) {
+        for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
+      } else if (CTRL) {  // (the candidates the control wavefront polled also covered the padding)
+        for (int i = a.H + lane; i < t.kpad; i += 64) L.vec[vperm<Q8>(i)] = 0.f;
+      }
       if (lane == 0) L.small[SM_SS + wave] = ss;
       break;
     }
@@ -1437,6 +1631,7 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
 // lane + 64 i in register i): loaded into registers before the tile's input gather, so that they
 // arrive while it waits, and put into LDS after it for the epilogue.
 constexpr int SCALE_REGS = MAX_BLOCK_ROWS / 64;
+constexpr int ROWS_PER_LANE = MAX_BLOCK_ROWS / 64;  // rows of a block per control-wave lane
 __device__ __forceinline__ int tile_rows(const TileDesc& t) { return t.kind == KIND_GU ? 2 * t.nrows : t.nrows; }
 __device__ __forceinline__ void load_scales(const KernelArgs& a, const TileDesc& t, int r0, int block_rows, int lane,
                                             float* sreg) {
@@ -1459,7 +1654,7 @@ __device__ __forceinline__ void put_scales(const Lds& L, const TileDesc& t, int 
   }
 }
 
-template <int HD, int G, bool WD, bool Q8>
+template <int HD, int G, bool WD, bool Q8, bool SMP>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1475,6 +1670,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
     const int64_t L_att = (int64_t)pos + 1;
     float lm_best = -INFINITY;
     int lm_idx = 0x7fffffff;
+    uint64_t lm_run = 0;  // sampled decoding: lane i holds this worker's i-th largest logit so far
     for (int k = 0; k < a.n_waves; ++k) {
       const TileDesc t = tile_of(L, k);
       const WaveDesc wd = wave_of(L, k);
@@ -1490,7 +1686,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       if constexpr (Q8) {
         if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
       }
-      if (gather_inputs<HD, G, true, WD, Q8>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true, WD, Q8, SMP>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       if constexpr (Q8) {
         if (is_gemv(t.kind)) put_scales(L, t, 0, block_rows, lane, sreg);
       }
@@ -1551,6 +1747,22 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
               }
               break;
             case KIND_LM:
+              if constexpr (SMP) {
+                uint64_t cand[ROWS_PER_LANE];  // this lane's rows of the block, r = lane + 64 j
+#pragma unroll
+                for (int j = 0; j < ROWS_PER_LANE; ++j) {
+                  const int r = lane + 64 * j;
+                  cand[j] = 0;
+                  if (r < nr) {
+                    const float v = rs * total(r);
+                    const int idx = t.row0 + r0 + r;
+                    if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
+                    cand[j] = cand_key(v, idx);
+                  }
+                }
+                topk_merge(lm_run, cand, a.top_k, lane);
+                break;
+              }
               for (int r = lane; r < nr; r += 64) {
                 const float v = rs * total(r);
                 const int idx = t.row0 + r0 + r;
@@ -1583,7 +1795,16 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         if (a.trace) t_cmp = wall_clock64();
         for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);
       }
-      if (wd.kind == KIND_LM) {
+      if (SMP && wd.kind == KIND_LM) {
+        // this worker's top_k candidates in decreasing order, lane i the i-th ((-inf, 0x7fffffff) where
+        // the worker has fewer rows); the first one last, as the release of the worker's step
+        uint64_t* dst = reinterpret_cast<uint64_t*>(a.lmpart) + (int64_t)bid * a.top_k;
+        const float v = lm_run ? key_value(lm_run) : -INFINITY;
+        const uint32_t ix = lm_run ? (uint32_t)key_index(lm_run) : 0x7fffffffu;
+        const uint64_t word = (uint64_t)__float_as_uint(v) | ((uint64_t)(ix | (par << 31)) << 32);
+        if (lane > 0 && lane < a.top_k) st_u64(dst + lane, word);
+        if (lane == 0) st_u64_release(dst, word);
+      } else if (wd.kind == KIND_LM) {
         // worker partial (max, lowest index); also published by workers without vocabulary rows
         for (int off = 32; off >= 1; off >>= 1) {
           const float ov = __shfl_xor(lm_best, off);
@@ -1618,7 +1839,15 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
   // the last step's token
   if (!stop && bid == 0) {
     int last = 0;
-    if (!gather_token<WD>(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
+    if constexpr (SMP) {
+      const float u = a.uniforms[a.n_steps - 1];
+      if (!poll_candidates<WD>(a, L, lane, step_parity(a.n_steps - 1))) {
+        last = draw_token(a, L, lane, u);
+        if (lane == 0) a.out_tokens[a.n_steps - 1] = last;
+      }
+    } else {
+      if (!gather_token<WD>(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
+    }
   }
 }
 
@@ -1636,7 +1865,7 @@ constexpr int stream_sets() {
   return 2;
 }
 
-template <int HD, int G, bool WD, bool Q8>
+template <int HD, int G, bool WD, bool Q8, bool SMP>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
@@ -1716,7 +1945,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G, false, WD, Q8>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false, WD, Q8, SMP>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
@@ -1770,7 +1999,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
 }
 
 // Q8: weight-only INT8 GEMV tiles (INT8 codes, per-row FP32 scales); else BF16 weights.
-template <int HD, int G, bool WD, bool Q8>
+// SMP: sampled decoding (top-k / top-p draw from every worker's candidates); else greedy.
+template <int HD, int G, bool WD, bool Q8, bool SMP>
 __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
@@ -1823,14 +2053,15 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   __syncthreads();
   if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G, WD, Q8>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G, WD, Q8>(a, L, bid, wave, lane, block_rows);
+  if (wave == 0) control_loop<HD, G, WD, Q8, SMP>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G, WD, Q8, SMP>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
 // stream-read ceiling: what HBM delivers to streams of the decode kernel's load form (16-byte
 // non-temporal loads, one 1 KB chunk per wavefront instruction), each wavefront reading one
 // contiguous share with STREAM_DEPTH chunks in flight; an XOR of everything read goes to `sink`
+#ifndef TILES_WORKER_UNIT
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(BLOCK_THREADS) stream_read(const uint8_t* __restrict__ p, int64_t chunks_per_wave,
@@ -1988,37 +2219,46 @@ hipError_t noalloc_scratch(int device, uint32_t** out) {
 // host-visible handles of the instantiations
 // ---------------------------------------------------------------------------
 
-// The worker for a head size, query heads per attention tile and weight format; `short_watchdog`
-// selects the test instantiation whose waits check their watchdog every polling round (BF16, one
-// query head per tile only).
-template <bool Q8>
+#endif  // TILES_WORKER_UNIT
+
+#ifdef TILES_WORKER_UNIT
+// The worker for a head size and query heads per attention tile, for one weight format and token
+// selection (each worker unit instantiates one pair, so that the build compiles them in parallel).
+template <bool Q8, bool SMP>
 const void* worker_for(int head_dim, int group) {
   if (head_dim == 64) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false, Q8>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false, Q8>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, SMP>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, SMP>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false, Q8, SMP>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false, Q8, SMP>);
     }
   } else if (head_dim == 128) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false, Q8>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false, Q8>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, SMP>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, SMP>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false, Q8, SMP>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false, Q8, SMP>);
     }
   }
   return nullptr;
 }
+#else
+// (defined by the worker units)
+const void* worker_bf16_greedy(int head_dim, int group);
+const void* worker_bf16_sampled(int head_dim, int group);
+const void* worker_int8_greedy(int head_dim, int group);
+const void* worker_int8_sampled(int head_dim, int group);
+const void* worker_watchdog(int head_dim);
 
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8) {
-  if (short_watchdog) {
-    if (group != 1 || q8) return nullptr;
-    if (head_dim == 64) return reinterpret_cast<const void*>(&tiles_worker<64, 1, true, false>);
-    if (head_dim == 128) return reinterpret_cast<const void*>(&tiles_worker<128, 1, true, false>);
-    return nullptr;
-  }
-  return q8 ? worker_for<true>(head_dim, group) : worker_for<false>(head_dim, group);
+// The worker for a head size, query heads per attention tile, weight format and token selection;
+// `short_watchdog` selects the test instantiation whose waits check their watchdog every polling
+// round (BF16, greedy, one query head per tile only).
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled) {
+  if (short_watchdog) return group == 1 && !q8 && !sampled ? worker_watchdog(head_dim) : nullptr;
+  if (sampled) return q8 ? worker_int8_sampled(head_dim, group) : worker_bf16_sampled(head_dim, group);
+  return q8 ? worker_int8_greedy(head_dim, group) : worker_bf16_greedy(head_dim, group);
 }
+#endif
 
 }  // namespace tiles

@@ -53,7 +53,9 @@ constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 // area by direct-to-LDS loads issued with the register prefetch (as many as the LDS holds).
 constexpr int MAX_STAGE_BATCHES = 2;
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;  // polling rounds before a wait gives up (watchdog)
-constexpr int32_t MAX_POSITIONS = 1 << 23;  // KV capacity limit: positions and per-head row offsets stay 32-bit
+constexpr int32_t MAX_POSITIONS = 1 << 23;
+// Sampled decoding (top-k / top-p): each worker publishes its top_k largest logits, at most this many.
+constexpr int32_t MAX_TOP_K = 32;  // KV capacity limit: positions and per-head row offsets stay 32-bit
 
 struct TileDesc {   // 32 bytes
   int32_t kind;
@@ -134,7 +136,8 @@ struct KernelArgs {
   int64_t embed_stride;      // bytes between embedding rows
   // tagged-data buffers (see the kernel): one per wave, and the LM-head partials
   uint32_t* ll;              // FP32 values, parity in bit 0; wave k's output at ll + waves[k].ll_off
-  uint32_t* lmpart;          // [W][2] (max logit bits, index | parity << 31)
+  uint32_t* lmpart;          // [W][max(1, top_k)][2] (logit bits, index | parity << 31): the worker's
+                             // maximum (greedy) or its top_k logits in decreasing order (sampled)
   uint32_t* sync;            // SYNC_WORDS status / abort words
   const uint64_t* table_check;  // [W + 1]: per-worker hash of the schedule it loads, then the build id
   uint16_t* kv_k;            // BF16 cache
@@ -142,6 +145,7 @@ struct KernelArgs {
   int64_t kv_cap;
   int32_t* out_tokens;
   float* out_logits;         // may be null
+  const float* uniforms;     // [n_steps] FP32 in [0, 1): the draw of each sampled step (null: greedy)
   float* dbg_hidden;         // [n_steps][n_layers][H] or null
   uint64_t* trace;           // [n_steps][n_waves][W][TRACE_WORDS] or null
   int32_t token0, pos0, n_steps, n_waves;
@@ -155,6 +159,9 @@ struct KernelArgs {
   int32_t lds_xres_floats;
   int32_t lds_stage_floats;  // NCOMP staging areas of stage_batches batches
   int32_t stage_batches;
+  int32_t top_k;             // 0: greedy; 1 .. MAX_TOP_K: sampled (top-k, temperature, top-p)
+  float temperature;
+  float top_p;
 };
 
 }  // namespace tiles

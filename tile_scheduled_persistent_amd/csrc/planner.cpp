@@ -29,6 +29,12 @@ namespace {
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
+uint32_t float_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
 // rows [lo, hi) of `R` rows for worker w of W: balanced to within one row.
 void row_split(int64_t R, int32_t W, int32_t w, int64_t& lo, int64_t& hi) {
   lo = R * w / W;
@@ -120,7 +126,7 @@ uint64_t plan_checksum(const HostPlan& p) {
                           s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o, p.T, p.q8, p.wb,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
-                          p.stage_batches};
+                          p.stage_batches, p.top_k, (int64_t)float_bits(p.temperature), (int64_t)float_bits(p.top_p)};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -183,6 +189,15 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
     return fail(err, TILES_E_CONFIG, "weight_format must be 0 (BF16) or 1 (INT8)");
   p.q8 = cfg.weight_format == WEIGHTS_INT8;
   p.wb = p.q8 ? 1 : 2;
+  if (cfg.top_k < 0 || cfg.top_k > MAX_TOP_K || cfg.top_k > cfg.vocab)
+    return fail(err, TILES_E_CONFIG, "top_k must be 0 (greedy) or in [1, min(32, vocab)]");
+  if (cfg.top_k > 0 && !(cfg.temperature > 0.0f && cfg.temperature < 1e30f && cfg.top_p > 0.0f && cfg.top_p <= 1.0f))
+    return fail(err, TILES_E_CONFIG, "sampling needs 0 < temperature (finite) and 0 < top_p <= 1");
+  if (cfg.top_k > 0 && n_workers > 256)
+    return fail(err, TILES_E_CONFIG, "sampled decoding supports at most 256 workers (the token draw merges 4 lists per lane)");
+  p.top_k = cfg.top_k;
+  p.temperature = cfg.top_k > 0 ? cfg.temperature : 1.0f;
+  p.top_p = cfg.top_k > 0 ? cfg.top_p : 1.0f;
   const int32_t ccols = CHUNK_BYTES / p.wb;  // columns per packed chunk
   s.Hpad = (int32_t)round_up(s.H, ccols);
   s.Qpad = (int32_t)round_up((int64_t)s.n_heads * s.hd, ccols);
@@ -467,6 +482,11 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
+  // sampled decoding: the token gather holds every worker's top_k (value, index) pairs in vec + part
+  // (whole 16-byte units: two candidates each)
+  const int64_t cand_floats = ((int64_t)p.W * p.top_k + 1) / 2 * 4;
+  if (p.top_k > 0 && p.lds_vec_floats + p.lds_part_floats < cand_floats)
+    p.lds_part_floats = (int32_t)round_up(cand_floats - p.lds_vec_floats, 64);
   p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0);  // (INT8: then a block's scales)
   // schedule tables: per wave a SegDesc, this worker's TileDesc and the WaveDesc; per layer a LayerSmall
   p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
@@ -883,6 +903,10 @@ int validate_plan(const HostPlan& p, std::string& err) {
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
   if ((int64_t)p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
   if (p.lds_xres_floats < s.Hpad) return fail(err, TILES_E_PLAN, "LDS residual area too small");
+  if (p.top_k < 0 || p.top_k > MAX_TOP_K || p.top_k > s.V || (p.top_k > 0 && p.W > 256))
+    return fail(err, TILES_E_PLAN, "top_k out of range (1..32, <= vocab, at most 256 workers)");
+  if (p.top_k > 0 && (int64_t)p.lds_vec_floats + p.lds_part_floats < ((int64_t)p.W * p.top_k + 1) / 2 * 4)
+    return fail(err, TILES_E_PLAN, "LDS too small for the sampled token gather (W x top_k pairs)");
   return TILES_OK;
 }
 

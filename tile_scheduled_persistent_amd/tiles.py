@@ -51,6 +51,7 @@ class Config(ctypes.Structure):
         ("flags", ctypes.c_uint32), ("kv_splits", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
         ("attn_heads", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
         ("o_placement", ctypes.c_int32), ("weight_format", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
     ]
 
 
@@ -76,7 +77,7 @@ class PlanInfo(ctypes.Structure):
         ("combine_mode", ctypes.c_int32), ("occupancy", ctypes.c_int32), ("packed_bytes", ctypes.c_int64),
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
-        ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32),
+        ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("top_k", ctypes.c_int32),
     ]
 
 
@@ -103,6 +104,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_decode_noalloc.restype = ctypes.c_int
         L.tiles_decode_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_decode_sampled.restype = ctypes.c_int
+        L.tiles_decode_sampled.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.tiles_plan_destroy.restype = None
         L.tiles_plan_destroy.argtypes = [ctypes.c_void_p]
         L.tiles_last_error.restype = ctypes.c_char_p
@@ -155,11 +159,13 @@ WEIGHTS = {"bf16": 0, "int8": 1}
 
 def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
                 n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0,
-                weights: str = "bf16") -> Config:
+                weights: str = "bf16", sampling: Optional[tuple] = None) -> Config:
+    """``sampling`` = (temperature, top_k, top_p) makes a sampling plan (tiles_decode_sampled)."""
+    temperature, top_k, top_p = sampling if sampling is not None else (1.0, 0, 1.0)
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
                   float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
                   int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement),
-                  WEIGHTS[weights])
+                  WEIGHTS[weights], int(top_k), float(temperature), float(top_p))
 
 
 def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
@@ -232,11 +238,12 @@ class Plan:
 
     def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
                  combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0,
-                 o_placement: int = 0, weight_format: str = "bf16"):
+                 o_placement: int = 0, weight_format: str = "bf16", sampling: Optional[tuple] = None):
         self.model = m
+        self.sampling = sampling
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream,
-                                attn_heads, o_placement, weight_format)
+                                attn_heads, o_placement, weight_format, sampling)
         on_device = weights["embed"].is_cuda
         layers = (LayerWeights * m.n_layers)()
         for i, d in enumerate(weights["layers"]):
@@ -274,9 +281,15 @@ class Plan:
 
     # ------------------------------------------------------------------
     def decode(self, kv: KVCache, token: int, n_steps: int, out_tokens: torch.Tensor,
-               out_logits: Optional[torch.Tensor] = None, noalloc: bool = False) -> int:
-        """Enqueue one cooperative launch of ``n_steps`` greedy steps; returns TILES_OK or raises.
-        ``noalloc`` calls tiles_decode_noalloc (scratch in the library's static device array)."""
+               out_logits: Optional[torch.Tensor] = None, noalloc: bool = False,
+               uniforms: Optional[torch.Tensor] = None) -> int:
+        """Enqueue one cooperative launch of ``n_steps`` steps; returns TILES_OK or raises.
+        Greedy plans call tiles_decode (``noalloc``: tiles_decode_noalloc, scratch in the library's
+        static device array); sampling plans call tiles_decode_sampled with ``uniforms`` (a device
+        float32 tensor of n_steps values in [0, 1))."""
+        if uniforms is not None and (uniforms.dtype != torch.float32 or not uniforms.is_cuda
+                                     or uniforms.numel() < n_steps):
+            raise ValueError("uniforms must be a device float32 tensor with n_steps entries")
         if out_tokens.dtype != torch.int32 or not out_tokens.is_cuda or out_tokens.numel() < n_steps:
             raise ValueError("out_tokens must be a device int32 tensor with n_steps entries")
         if out_logits is not None and (out_logits.dtype != torch.float32 or not out_logits.is_cuda
@@ -286,8 +299,12 @@ class Plan:
             if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
                 raise ValueError("KV tensors must be contiguous device bf16")
         c = KV(_ptr(kv.k), _ptr(kv.v), kv.capacity, kv.length)
-        fn = lib().tiles_decode_noalloc if noalloc else lib().tiles_decode
-        rc = fn(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(out_tokens), _ptr(out_logits))
+        if uniforms is not None or self.sampling is not None:
+            rc = lib().tiles_decode_sampled(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(uniforms),
+                                            _ptr(out_tokens), _ptr(out_logits))
+        else:
+            fn = lib().tiles_decode_noalloc if noalloc else lib().tiles_decode
+            rc = fn(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(out_tokens), _ptr(out_logits))
         _check(rc)
         kv.length = c.length
         return rc
