@@ -1683,17 +1683,16 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
       float sreg[SCALE_REGS];
-      if constexpr (Q8) {
-        if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
-      }
       if (gather_inputs<HD, G, true, WD, Q8, SMP>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
-      if constexpr (Q8) {
-        if (is_gemv(t.kind)) put_scales(L, t, 0, block_rows, lane, sreg);
-      }
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
         break;
+      }
+      // (INT8) the first block's row scales, issued after the input gather (its polls would complete
+      // behind them) and arriving while the compute wavefronts stream the block
+      if constexpr (Q8) {
+        if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
       }
       if (a.trace) t_pro = wall_clock64();
       const float rs = lds_prologue<HD, G, Q8>(a, L, 0, lane, t, layer, pos);
@@ -1710,12 +1709,10 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
             return Q8 ? L.scl[r] * x : x;
           };
           if constexpr (Q8) {
-            if (r0 > 0) {  // a later block's scales (a tile of more rows than one block holds)
-              load_scales(a, t, r0, block_rows, lane, sreg);
-              put_scales(L, t, r0, block_rows, lane, sreg);
-            }
+            if (r0 > 0) load_scales(a, t, r0, block_rows, lane, sreg);  // a later block's scales
           }
           __syncthreads();  // B: partials of this block ready
+          if constexpr (Q8) put_scales(L, t, r0, block_rows, lane, sreg);  // (read by this wavefront only)
           if (a.trace && r0 == 0) {
             t_cmp = wall_clock64();
             for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
