@@ -30,6 +30,9 @@ from .decoder import (  # noqa: F401
     quantize_rows_int8,
     dequantize_rows_int8,
     sample_token,
+    quantize_rows_f32_int8,
+    convert_kv_int8,
+    dequantize_kv_rows,
     LINEAR_WEIGHTS,
     rmsnorm,
     rope_cos_sin,

@@ -54,6 +54,18 @@ S1  Top-k / top-p sampling ("History and roadmap" (TileInfer.jl), "M8 so far" ta
     the prefix if rounding leaves none).  The decision is an integer taken by floating point, so it
     is taken in FP32, the kernel's precision, with the sums accumulated in ranking order.
     Limits: T > 0, 0 < top_p <= 1, 1 <= top_k <= V.
+K1  INT8 KV cache with smoothed keys ("History and roadmap" (TileInfer.jl), "M8 so far" table: INT8
+    KV cache with smoothed keys, INT8 attention; "Tried and not kept": quantized queries undid the
+    accuracy key smoothing gained, so queries stay FP32).  Each cached K row is divided by a
+    per-(layer, KV head, channel) smoothing factor sigma_c > 0 and each K and V row is stored as
+    symmetric INT8 codes with one FP32 scale per (layer, KV head, position), quantized as in Q1 but
+    from FP32 values: s = max|r| / 127, q = round-half-even(r / s) clamped to [-127, 127] (s = 0,
+    q = 0 for a row of zeros).  A step attends to the dequantized rows, K = (q * s) * sigma_c and
+    V = q * s, each product in FP32; the current position's K and V are quantized from their FP32
+    values (after q/k norm and RoPE) and the step attends to what was stored (as R5).
+K2  sigma_c is the largest |K| of channel c over the positions cached when a BF16 cache is
+    converted (1 for a channel that is zero there); positions decoded later keep those factors.
+    Conversion: the BF16 values widened, divided by sigma, quantized per row.
 """
 
 from __future__ import annotations
@@ -70,6 +82,9 @@ __all__ = [
     "quantize_rows_int8",
     "dequantize_rows_int8",
     "sample_token",
+    "quantize_rows_f32_int8",
+    "convert_kv_int8",
+    "dequantize_kv_rows",
     "LINEAR_WEIGHTS",
     "rmsnorm",
     "rope_cos_sin",
@@ -153,6 +168,45 @@ def quantize_rows_int8(w_bits: np.ndarray):
 def dequantize_rows_int8(q: np.ndarray, s: np.ndarray, dtype=np.float32) -> np.ndarray:
     """Q1: the weights a quantized layer computes with, q * s per row (rounded to ``dtype``)."""
     return q.astype(dtype) * s.astype(dtype)[:, None]
+
+
+def quantize_rows_f32_int8(x: np.ndarray):
+    """K1: symmetric INT8 codes and FP32 scales of FP32 rows (last axis), as Q1: s = max|x| / 127,
+    q = round-half-even(x / s) clamped to [-127, 127], FP32 divisions; s = 0, q = 0 for a zero row.
+    Returns (q int8 [..., n], s float32 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = (x / safe[..., None]).astype(np.float32)
+    q = np.clip(np.rint(r), -127, 127)
+    q = np.where(s[..., None] > 0, q, 0).astype(np.int8)
+    return q, s
+
+
+def convert_kv_int8(kv_bits: dict, length: int) -> dict:
+    """K1/K2: the INT8 cache of a BF16 cache (uint16 bits [layers, kv heads, capacity, hd]) whose
+    first ``length`` positions are filled: sigma [layers, kv heads, hd] from those positions, codes
+    and scales of those positions (later positions zero).  Returns a dict with ``kq``, ``vq`` (int8,
+    the cache's shape), ``ks``, ``vs`` (float32 [layers, kv heads, capacity]) and ``sigma``."""
+    k = bf16_bits_to_float(kv_bits["k"][:, :, :length], np.float32)
+    v = bf16_bits_to_float(kv_bits["v"][:, :, :length], np.float32)
+    sigma = np.max(np.abs(k), axis=2) if length > 0 else np.zeros(k.shape[:2] + k.shape[3:], np.float32)
+    sigma = np.where(sigma > 0, sigma, np.float32(1.0)).astype(np.float32)
+    shape = kv_bits["k"].shape
+    out = {"kq": np.zeros(shape, np.int8), "vq": np.zeros(shape, np.int8),
+           "ks": np.zeros(shape[:3], np.float32), "vs": np.zeros(shape[:3], np.float32), "sigma": sigma}
+    out["kq"][:, :, :length], out["ks"][:, :, :length] = quantize_rows_f32_int8((k / sigma[:, :, None, :]).astype(np.float32))
+    out["vq"][:, :, :length], out["vs"][:, :, :length] = quantize_rows_f32_int8(v)
+    return out
+
+
+def dequantize_kv_rows(q: np.ndarray, s: np.ndarray, sigma: Optional[np.ndarray] = None, dtype=np.float32):
+    """K1: the rows a step attends to: (q * s) [* sigma], each product in FP32, then widened."""
+    r = (q.astype(np.float32) * s.astype(np.float32)[..., None]).astype(np.float32)
+    if sigma is not None:
+        r = (r * sigma.astype(np.float32)).astype(np.float32)
+    return r.astype(dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -297,7 +351,8 @@ class OracleModel:
         eps = float(c.rms_eps)
         if not (0 <= token < c.vocab):
             raise ValueError("token out of range")
-        if pos >= kv["k"].shape[2]:
+        int8_kv = "kq" in kv                                      # K1: an INT8 cache (convert_kv_int8)
+        if pos >= (kv["kq"] if int8_kv else kv["k"]).shape[2]:
             raise ValueError("KV capacity exceeded")
         x = self._embed_row(token)
         hidden = np.empty((c.n_layers, c.hidden), dtype=dt)
@@ -315,17 +370,31 @@ class OracleModel:
                 k = rmsnorm(k, self._get(l, "k_norm"), eps)
             q = apply_rope(q, cos, sin)
             k = apply_rope(k, cos, sin)
-            kv["k"][l, :, pos, :] = float_to_bf16_bits(k)        # R5
-            kv["v"][l, :, pos, :] = float_to_bf16_bits(v)
+            if int8_kv:                                            # K1: quantized from FP32
+                sg = kv["sigma"][l]
+                kv["kq"][l, :, pos, :], kv["ks"][l, :, pos] = quantize_rows_f32_int8(
+                    (k.astype(np.float32) / sg).astype(np.float32))
+                kv["vq"][l, :, pos, :], kv["vs"][l, :, pos] = quantize_rows_f32_int8(v.astype(np.float32))
+            else:
+                kv["k"][l, :, pos, :] = float_to_bf16_bits(k)        # R5
+                kv["v"][l, :, pos, :] = float_to_bf16_bits(v)
             if kv_wide is not None:
-                kv_wide["k"][l, :, pos, :] = bf16_bits_to_float(kv["k"][l, :, pos, :], dt)
-                kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)
+                if int8_kv:
+                    kv_wide["k"][l, :, pos, :] = dequantize_kv_rows(kv["kq"][l, :, pos], kv["ks"][l, :, pos],
+                                                                    kv["sigma"][l], dt)
+                    kv_wide["v"][l, :, pos, :] = dequantize_kv_rows(kv["vq"][l, :, pos], kv["vs"][l, :, pos], None, dt)
+                else:
+                    kv_wide["k"][l, :, pos, :] = bf16_bits_to_float(kv["k"][l, :, pos, :], dt)
+                    kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)
             attn = np.empty((nq, hd), dtype=dt)
             for hh in range(nq):
                 g = hh // group                                    # R3
                 if kv_wide is not None:
                     Kc = kv_wide["k"][l, g, : pos + 1]
                     Vc = kv_wide["v"][l, g, : pos + 1]
+                elif int8_kv:
+                    Kc = dequantize_kv_rows(kv["kq"][l, g, : pos + 1], kv["ks"][l, g, : pos + 1], kv["sigma"][l, g], dt)
+                    Vc = dequantize_kv_rows(kv["vq"][l, g, : pos + 1], kv["vs"][l, g, : pos + 1], None, dt)
                 else:
                     Kc = bf16_bits_to_float(kv["k"][l, g, : pos + 1], dt)
                     Vc = bf16_bits_to_float(kv["v"][l, g, : pos + 1], dt)
@@ -344,7 +413,11 @@ class OracleModel:
     # drivers -----------------------------------------------------------------
     def widen_kv(self, kv: dict) -> dict:
         """The whole cache widened (exactly) to this model's dtype, for :meth:`step`'s
-        ``kv_wide``: long caches are then widened once instead of at every step."""
+        ``kv_wide``: long caches are then widened once instead of at every step (an INT8 cache:
+        its dequantized rows, K1)."""
+        if "kq" in kv:
+            return {"k": dequantize_kv_rows(kv["kq"], kv["ks"], kv["sigma"][:, :, None, :], self.dtype),
+                    "v": dequantize_kv_rows(kv["vq"], kv["vs"], None, self.dtype)}
         return {"k": bf16_bits_to_float(kv["k"], self.dtype).copy(),
                 "v": bf16_bits_to_float(kv["v"], self.dtype).copy()}
 

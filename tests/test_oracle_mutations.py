@@ -6,8 +6,8 @@ that part of the oracle.
 The mistakes cover the readings the oracle rests on (RoPE pairing, frequency and sign,
 GQA map, attention scale and causal range, RMSNorm form, BF16 rounding, SwiGLU branch,
 residual source), the plumbing of the step (which layer's weights and which gain
-each stage reads, q/k norm before RoPE, the argmax tie rule), the INT8 weight codes and the
-sampling draw (tie order, temperature, top-k and top-p supports, the draw's scale and
+each stage reads, q/k norm before RoPE, the argmax tie rule), the INT8 weight codes, the INT8
+KV cache (smoothing, scales, codes, dequantization) and the sampling draw (tie order, temperature, top-k and top-p supports, the draw's scale and
 strictness, the per-step uniform).
 """
 
@@ -61,8 +61,10 @@ MUTATIONS = [
      'rmsnorm(x, self._get(l, "attn_norm"), eps)', False),
     ("widened cache row written unrounded", 'kv_wide["v"][l, :, pos, :] = bf16_bits_to_float(kv["v"][l, :, pos, :], dt)',
      'kv_wide["v"][l, :, pos, :] = v', False),
-    ("INT8 codes truncated", "q = np.clip(np.rint(r), -127, 127)", "q = np.clip(np.trunc(r), -127, 127)", False),
-    ("INT8 scale over 128", "s = (amax / np.float32(127.0)).astype(np.float32)", "s = (amax / np.float32(128.0)).astype(np.float32)", False),
+    ("INT8 codes truncated", "q = np.clip(np.rint(r), -127, 127)                     # np.rint",
+     "q = np.clip(np.trunc(r), -127, 127)                     # np.rint", False),
+    ("INT8 scale over 128", "s = (amax / np.float32(127.0)).astype(np.float32)      # FP32 division",
+     "s = (amax / np.float32(128.0)).astype(np.float32)      # FP32 division", False),
     ("INT8 scale dropped", "return q.astype(dtype) * s.astype(dtype)[:, None]", "return q.astype(dtype) / np.float32(127.0) + 0 * s[:, None]", False),
     ("INT8 LM head left in BF16", 'return self._get(None, "embed", linear=True)', 'return self._get(None, "embed")', False),
     ("INT8 embedding lookup quantized", "return bf16_bits_to_float(self.w[\"embed\"][token], self.dtype).copy()",
@@ -79,6 +81,15 @@ MUTATIONS = [
     ("draw non-strict", "np.nonzero(cum[:n] > target)", "np.nonzero(cum[:n] >= target)", False),
     ("top-k keeps one more", ")[:top_k]   # decreasing", ")[:top_k + 1]   # decreasing", False),
     ("decode samples with the previous step's uniform", "float(uniforms[i])", "float(uniforms[i - 1])", False),
+    ("INT8 KV without smoothing", "sigma = np.where(sigma > 0, sigma, np.float32(1.0)).astype(np.float32)",
+     "sigma = np.ones_like(sigma, dtype=np.float32)", False),
+    ("INT8 KV smooths V too", "quantize_rows_f32_int8(v)\n", "quantize_rows_f32_int8((v / sigma[:, :, None, :]).astype(np.float32))\n", False),
+    ("INT8 KV scale over 128", "s = (amax / np.float32(127.0)).astype(np.float32)\n    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)\n    r = (x /",
+     "s = (amax / np.float32(128.0)).astype(np.float32)\n    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)\n    r = (x /", False),
+    ("INT8 KV codes truncated", "q = np.clip(np.rint(r), -127, 127)\n    q = np.where(s[..., None]", "q = np.clip(np.trunc(r), -127, 127)\n    q = np.where(s[..., None]", False),
+    ("INT8 KV keys dequantized without sigma", "    if sigma is not None:\n        r = (r * sigma", "    if False:\n        r = (r * sigma", False),
+    ("INT8 KV current V row stored unquantized", "kv[\"vq\"][l, :, pos, :], kv[\"vs\"][l, :, pos] = quantize_rows_f32_int8(v.astype(np.float32))",
+     "kv[\"vq\"][l, :, pos, :], kv[\"vs\"][l, :, pos] = quantize_rows_f32_int8(v.astype(np.float32)); kv[\"vs\"][l, :, pos] *= 1.01", False),
     ("argmax keeps the last maximum", "toks[i] = int(np.argmax(logits))",
      "toks[i] = int(len(logits) - 1 - np.argmax(logits[::-1]))", False),
 ]

@@ -756,3 +756,108 @@ def test_decode_sampling_uses_each_steps_uniform():
     res = OracleModel(c, w, np.float32).decode(_kv(c, 8), 3, 0, 5, sampling=(1.0, 4, 1.0), uniforms=u)
     assert np.all(res["logits"] == res["logits"][0][0])
     assert list(res["tokens"]) == [0, 1, 2, 3, 2]
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache with smoothed keys (K1, K2): a hand-worked conversion, bounds per channel that only
+# hold with smoothing, zero channels, and a step whose attention is the mean of the stored V.
+# ---------------------------------------------------------------------------
+from oracle import convert_kv_int8, dequantize_kv_rows, quantize_rows_f32_int8  # noqa: E402
+
+
+def test_kv_int8_conversion_hand_worked():
+    """K rows (1, 100) and (-2, 50): sigma = (2, 100); smoothed rows (0.5, 1) and (-1, 0.5), scale
+    1/127 each; codes (64, 127) (63.5 rounds half to even) and (-127, 64); dequantized (64/127 * 2,
+    100) and (-2, 64/127 * 100).  V rows (0.5, -0.25) and (1, 2): no smoothing; scales 0.5/127 and
+    2/127; codes (127, -64) (-63.5 to even) and (64, 127).  Catches: no smoothing, smoothing of V,
+    scale over 128, truncated codes, sigma left out of the dequantized K."""
+    k = np.array([[1, 100], [-2, 50]], np.float32)[None, None]
+    v = np.array([[0.5, -0.25], [1, 2]], np.float32)[None, None]
+    c = convert_kv_int8({"k": float_to_bf16_bits(k), "v": float_to_bf16_bits(v)}, 2)
+    assert np.array_equal(c["sigma"][0, 0], np.array([2, 100], np.float32))
+    assert np.array_equal(c["kq"][0, 0], np.array([[64, 127], [-127, 64]], np.int8))
+    assert np.array_equal(c["ks"][0, 0], np.full(2, np.float32(1) / np.float32(127), np.float32))
+    assert np.array_equal(c["vq"][0, 0], np.array([[127, -64], [64, 127]], np.int8))
+    assert np.array_equal(c["vs"][0, 0], np.array([np.float32(0.5) / np.float32(127), np.float32(2) / np.float32(127)]))
+    kd = dequantize_kv_rows(c["kq"], c["ks"], c["sigma"][:, :, None, :], np.float64)[0, 0]
+    assert np.allclose(kd, [[64 / 127 * 2, 100], [-2, 64 / 127 * 100]], rtol=1e-6)
+    vd = dequantize_kv_rows(c["vq"], c["vs"], None, np.float64)[0, 0]
+    assert np.allclose(vd, [[0.5, -0.5 * 64 / 127], [2 * 64 / 127, 2]], rtol=1e-6)
+
+
+def test_kv_int8_errors_are_bounded_per_channel_by_smoothing():
+    """Keys with per-channel scales U(0.5, 4) and one outlier channel (x100): sigma is each channel's
+    largest |K| over the cached positions (computed here independently), and every dequantized entry
+    is within sigma_c / 254 (half a code of the smoothed row, whose largest entry is at most 1) of
+    the true key -- without smoothing the outlier's scale would swamp the small channels.  V entries
+    are within half a code of their row's scale."""
+    rng = np.random.default_rng(77)
+    L, G, P, hd = 2, 3, 40, 16
+    scale = rng.uniform(0.5, 4.0, size=(L, G, 1, hd))
+    scale[:, :, :, 5] *= 100.0
+    k = (rng.standard_normal((L, G, P, hd)) * scale).astype(np.float32)
+    v = rng.standard_normal((L, G, P, hd)).astype(np.float32)
+    kb, vb = float_to_bf16_bits(k), float_to_bf16_bits(v)
+    c = convert_kv_int8({"k": kb, "v": vb}, P)
+    kw = bf16_bits_to_float(kb, np.float64)
+    vw = bf16_bits_to_float(vb, np.float64)
+    assert np.array_equal(c["sigma"], np.abs(kw).max(axis=2).astype(np.float32))
+    kd = dequantize_kv_rows(c["kq"], c["ks"], c["sigma"][:, :, None, :], np.float64)
+    err = np.abs(kd - kw)
+    assert np.all(err <= c["sigma"][:, :, None, :].astype(np.float64) / 254 * (1 + 1e-5) + 1e-30)
+    vd = dequantize_kv_rows(c["vq"], c["vs"], None, np.float64)
+    assert np.all(np.abs(vd - vw) <= c["vs"][..., None].astype(np.float64) / 2 * (1 + 1e-5))
+    # the smoothing is what makes the small channels precise
+    small = err[..., :5].max() / np.abs(kw[..., :5]).max()
+    assert small < 1 / 200
+
+
+def test_kv_int8_zero_channel_zero_row_and_unfilled_positions():
+    k = np.zeros((1, 1, 4, 4), np.float32)
+    k[0, 0, 0] = [1, 0, -3, 0]
+    k[0, 0, 1] = [0.5, 0, 0, 0]
+    v = np.zeros((1, 1, 4, 4), np.float32)
+    c = convert_kv_int8({"k": float_to_bf16_bits(k), "v": float_to_bf16_bits(v)}, 2)
+    assert np.array_equal(c["sigma"][0, 0], np.array([1, 1, 3, 1], np.float32))  # zero channels: 1
+    assert np.all(c["vq"] == 0) and np.all(c["vs"] == 0)                          # zero rows: s = 0, q = 0
+    assert np.all(c["kq"][0, 0, 2:] == 0) and np.all(c["ks"][0, 0, 2:] == 0)     # not filled
+    assert np.array_equal(c["kq"][0, 0, 1], np.array([127, 0, 0, 0], np.int8))
+
+
+def test_kv_int8_step_attends_the_stored_rows():
+    """Zero W_q makes every score 0, so each head's attention output is the plain mean of the V rows
+    it attends, the current one included, as stored (dequantized); with W_o the identity the layer's
+    residual gains exactly that mean.  The current position's stored K and V are within half a code
+    of their FP32 values (K as smoothed by the cache's sigma).  Catches: attending FP32 rows of the
+    current position, V rows not dequantized with their own scale, the current row not written."""
+    c = Cfg(n_layers=1)
+    rng = np.random.default_rng(31)
+    w = _zero_model(c, rng)
+    H, nq, hd = c.hidden, c.n_heads, c.head_dim
+    assert nq * hd == H
+    w["layers"][0]["wo"] = _b(np.eye(H))
+    wk = rng.standard_normal((c.n_kv_heads * hd, H)) * 0.05
+    wv = rng.standard_normal((c.n_kv_heads * hd, H)) * 0.05
+    w["layers"][0]["wk"] = _b(wk)
+    w["layers"][0]["wv"] = _b(wv)
+    cap, pos = 8, 5
+    kvb = {"k": float_to_bf16_bits(rng.standard_normal((1, c.n_kv_heads, cap, hd)).astype(np.float32)),
+           "v": float_to_bf16_bits(rng.standard_normal((1, c.n_kv_heads, cap, hd)).astype(np.float32))}
+    kv8 = convert_kv_int8(kvb, pos)
+    o = OracleModel(c, w, np.float64)
+    tok = 3
+    _, hidden = o.step(kv8, tok, pos)
+    x = bf16_bits_to_float(w["embed"][tok], np.float64)
+    attn = hidden[0] - x
+    group = nq // c.n_kv_heads
+    for hh in range(nq):
+        g = hh // group
+        vd = dequantize_kv_rows(kv8["vq"][0, g, :pos + 1], kv8["vs"][0, g, :pos + 1], None, np.float64)
+        assert np.allclose(attn[hh * hd:(hh + 1) * hd], vd.mean(axis=0), rtol=1e-9, atol=1e-12)
+    # the current row: FP32 k and v of this step (position 0 of RoPE is not used: pos = 5, so k is
+    # rotated; compare V, which is not rotated, and K's stored scale against its definition)
+    h = x / np.sqrt(np.mean(x * x) + c.rms_eps) * bf16_bits_to_float(w["layers"][0]["attn_norm"], np.float64)
+    v_true = (bf16_bits_to_float(w["layers"][0]["wv"], np.float64) @ h).reshape(c.n_kv_heads, hd)
+    vd = dequantize_kv_rows(kv8["vq"][0, :, pos], kv8["vs"][0, :, pos], None, np.float64)
+    assert np.all(np.abs(vd - v_true) <= kv8["vs"][0, :, pos, None] / 2 * (1 + 1e-4) + 1e-7)
+    assert np.all(kv8["ks"][0, :, pos] > 0) and np.any(kv8["kq"][0, :, pos] != 0)
