@@ -45,12 +45,15 @@ def cpu_baseline(setup_bits, m, wl, token, budget_s: float):
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from oracle import OracleModel, sample_token
+    from oracle import OracleModel, convert_kv_int8, sample_token
     from tile_scheduled_persistent_amd import synth
 
     w_bits, kv_bits = setup_bits
     o = OracleModel(m, w_bits, np.float32, weight_format=wl.weights)
-    kv = {"k": kv_bits["k"].copy(), "v": kv_bits["v"].copy()}
+    if wl.kv == "int8":
+        kv = convert_kv_int8(kv_bits, wl.n_cached)
+    else:
+        kv = {"k": kv_bits["k"].copy(), "v": kv_bits["v"].copy()}
     uniforms = synth.make_uniforms(m, wl.n_steps)
 
     def select(logits, i):
@@ -187,10 +190,13 @@ def main():
     stream = torch.cuda.current_stream()
     plan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, combine_mode=args.combine_mode,
                       attn_heads=args.attn_heads, o_placement=args.o_placement, weight_format=wl.weights,
-                      sampling=wl.sampling,
+                      sampling=wl.sampling, kv_format=wl.kv,
                       stream=stream)
     info = plan.info()
-    kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
+    if wl.kv == "int8":  # the INT8 cache of the same prefix (setup: not timed)
+        kv = tiles.KVCache.convert_int8(plan, k0, v0, wl.n_cached)
+    else:
+        kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     n_tok = wl.n_steps
     out_t = torch.zeros(n_tok, dtype=torch.int32, device=dev)
     out_l = torch.zeros((n_tok, m.vocab), dtype=torch.float32, device=dev)
@@ -246,7 +252,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.weights == "bf16" else "int8 weights, bf16 KV, fp32 activations",
+        "dtype": ("bf16" if wl.weights == "bf16" and wl.kv == "bf16" else
+                  f"{wl.weights} weights, {wl.kv} KV, fp32 activations"),
         "data": "synthetic",
         "config": {"workload": wl.description, "batch": 1, "cached_positions": wl.n_cached,
                    "tokens_per_step": n_tok, "parallelism": "single GPU, one workgroup per CU"},
@@ -289,8 +296,11 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
 
     plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits, attn_heads=args.attn_heads,
                       combine_mode=args.combine_mode, o_placement=args.o_placement, weight_format=wl.weights,
-                      sampling=wl.sampling)
-    kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
+                      sampling=wl.sampling, kv_format=wl.kv)
+    if wl.kv == "int8":
+        kv = tiles.KVCache.convert_int8(plan, k0, v0, wl.n_cached)
+    else:
+        kv = tiles.KVCache(k0.clone(), v0.clone(), wl.n_cached)
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
     from tile_scheduled_persistent_amd import synth
     uniforms = torch.from_numpy(synth.make_uniforms(m, wl.n_steps)).cuda() if wl.sampling is not None else None

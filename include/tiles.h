@@ -95,7 +95,16 @@ typedef struct tiles_config {
   int32_t top_k;
   float temperature;
   float top_p;
+  /* KV cache format ("History and roadmap" (TileInfer.jl), "M8 so far" table: INT8 KV cache with
+   * smoothed keys): TILES_KV_BF16, or TILES_KV_INT8: every cached K and V row as symmetric INT8 codes
+   * with one FP32 scale per (layer, KV head, position), keys divided by a per-(layer, KV head,
+   * channel) smoothing factor before quantization; attention reads the codes and computes with the
+   * dequantized rows (queries stay FP32).  See tiles_kv_t and tiles_kv_convert_int8. */
+  int32_t kv_format;
 } tiles_config_t;
+
+#define TILES_KV_BF16 0
+#define TILES_KV_INT8 1
 
 #define TILES_WEIGHTS_BF16 0
 #define TILES_WEIGHTS_INT8 1
@@ -116,19 +125,42 @@ typedef struct tiles_weights {
   int32_t on_device;                   /* 1: the tensors are device memory, 0: host memory */
 } tiles_weights_t;
 
-/* KV cache, caller-owned device memory, BF16 [n_layers][n_kv_heads][capacity][head_dim].
+typedef struct tiles_plan tiles_plan_t;
+
+/* KV cache, caller-owned device memory.  BF16 plans: k, v are BF16 [n_layers][n_kv_heads][capacity]
+ * [head_dim].  INT8 KV plans (kv_format = TILES_KV_INT8): k holds the int8 codes of K and V interleaved,
+ * [n_layers][n_kv_heads][capacity][2 * head_dim] with, for every group of 8 dimensions, the 8 K codes
+ * followed by the 8 V codes (one 16-byte load then reads both for a position); v is unused (may be
+ * NULL); k_scale and v_scale are float [n_layers][n_kv_heads][capacity] (a row is codes * scale,
+ * keys then times k_smooth); k_smooth is float [n_layers][n_kv_heads][head_dim] (> 0; see
+ * tiles_kv_convert_int8).
  * Keys are stored after q/k norm and RoPE.  A decode reads positions [0, length + i) at step i
  * (position length + i itself from the values it has just computed) and writes position
- * length + i; the contents of every other row -- the unused tail, NaN included -- never affect
- * any result. */
+ * length + i (INT8: its codes and scales, quantized from FP32); the contents of every other row --
+ * the unused tail, NaN included -- never affect any result. */
 typedef struct tiles_kv {
   void *k;
   void *v;
   int64_t capacity; /* positions allocated */
   int64_t length;   /* positions already cached; tiles_decode adds n_steps on success */
+  float *k_scale;   /* INT8 KV only (else ignored) */
+  float *v_scale;
+  float *k_smooth;
 } tiles_kv_t;
 
-typedef struct tiles_plan tiles_plan_t;
+/* Convert the first `length` positions of a BF16 cache (k_bf16, v_bf16: device BF16 [n_layers]
+ * [n_kv_heads][capacity][head_dim]) into the INT8 cache `dst` of an INT8 KV plan ("History and
+ * roadmap" (TileInfer.jl), "M8 so far" table: INT8 KV cache with smoothed keys): k_smooth[l][h][c]
+ * = the largest |K| of channel c over those positions (1 for a channel that is zero there), then
+ * every row r quantized symmetrically, keys divided by k_smooth first: s = max|r| / 127, code =
+ * round-half-even(r / s) clamped to [-127, 127] (s = 0 and codes 0 for a zero row), FP32 divisions.
+ * dst: device buffers as tiles_kv_t describes (dst->v unused), capacity equal to `capacity`; dst->length is set to
+ * `length`.  Positions from `length` on are left as they are.  Runs on the plan's stream
+ * (asynchronous); allocates nothing.  TILES_E_ARG for a BF16 plan, null pointers, or a length
+ * beyond the capacity. */
+int tiles_kv_convert_int8(tiles_plan_t *plan, const void *k_bf16, const void *v_bf16, int64_t capacity,
+                          int64_t length, tiles_kv_t *dst);
+
 
 /* Summary of a plan (see tiles_plan_info). */
 typedef struct tiles_plan_info {
@@ -149,6 +181,7 @@ typedef struct tiles_plan_info {
   int32_t o_workers;          /* workers holding o_proj tiles (all, or those without an attention tile) */
   int32_t weight_format;      /* TILES_WEIGHTS_BF16 or TILES_WEIGHTS_INT8 */
   int32_t top_k;              /* 0: greedy plan; else the plan samples (tiles_decode_sampled) */
+  int32_t kv_format;          /* TILES_KV_BF16 or TILES_KV_INT8 */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */

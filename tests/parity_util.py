@@ -12,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from oracle import OracleModel
+from oracle import OracleModel, convert_kv_int8, dequantize_kv_rows
 from tile_scheduled_persistent_amd import synth, tiles
 
 HIDDEN_REL_L2 = 1e-2
@@ -31,9 +31,10 @@ class Setup:
     views for the oracle.  `gen_device` is where the generators run."""
 
     def __init__(self, m, capacity: int, n_cached: int, key_scale: bool = False, gen_device: str = "cpu",
-                 widen_once: bool = True, weights: str = "bf16"):
+                 widen_once: bool = True, weights: str = "bf16", kv: str = "bf16"):
         self.m = m
         self.weights = weights  # "int8": weight-only INT8 linear layers on both sides
+        self.kv = kv            # "int8": INT8 KV cache with smoothed keys on both sides
         self.capacity = capacity
         self.n_cached = n_cached
         w = synth.make_weights(m, device=gen_device)
@@ -50,7 +51,12 @@ class Setup:
         self.widen_once = widen_once
         self._oracle = None
 
-    def fresh_kv(self) -> tiles.KVCache:
+    def fresh_kv(self, plan: "tiles.Plan" = None) -> tiles.KVCache:
+        """A fresh device cache (INT8 KV: converted from the BF16 one by the library, with `plan`)."""
+        if self.kv == "int8":
+            kv = tiles.KVCache.convert_int8(plan, self.k0, self.v0, self.n_cached)
+            torch.cuda.synchronize()
+            return kv
         return tiles.KVCache(self.k0.clone(), self.v0.clone(), self.n_cached)
 
     def oracle(self) -> OracleModel:
@@ -60,9 +66,12 @@ class Setup:
         return self._oracle
 
     def oracle_kv(self):
+        if self.kv == "int8":
+            return convert_kv_int8(self.kv_bits, self.n_cached)
         return {"k": self.kv_bits["k"].copy(), "v": self.kv_bits["v"].copy()}
 
     def plan(self, flags=tiles.TILES_DEBUG_HIDDEN, **kw) -> tiles.Plan:
+        kw.setdefault("kv_format", self.kv)
         return tiles.Plan(self.m, self.w_dev, self.capacity, flags=flags, weight_format=self.weights, **kw)
 
 
@@ -209,3 +218,44 @@ def compare_sampled_teacher_forced(tag, g_tokens, g_logits, g_hidden, o_res, sam
         worst_l = max(worst_l, err)
         exact += check_sampled_token(f"{tag} step {i}", int(g_tokens[i]), o_res["logits"][i], sampling, uniforms[i])
     return {"steps": n, "hidden_rel_l2_max": worst_h, "logit_abs_max": worst_l, "draws_exact": exact}
+
+
+def split_int8_cache(kv: tiles.KVCache):
+    """The device INT8 cache as host arrays in the oracle's form: K codes, V codes (de-interleaved:
+    per group of 8 dimensions the K codes come first), K and V scales, smoothing factors."""
+    codes = kv.k.cpu().numpy()
+    L, H, cap, hd2 = codes.shape
+    g = codes.reshape(L, H, cap, hd2 // 16, 2, 8)
+    kq = np.ascontiguousarray(g[:, :, :, :, 0, :]).reshape(L, H, cap, hd2 // 2)
+    vq = np.ascontiguousarray(g[:, :, :, :, 1, :]).reshape(L, H, cap, hd2 // 2)
+    return kq, vq, kv.k_scale.cpu().numpy(), kv.v_scale.cpu().numpy(), kv.k_smooth.cpu().numpy()
+
+
+def kv8_rows_close(tag, kv: tiles.KVCache, okv: dict, pos: int, n: int):
+    """The INT8 rows a launch wrote (positions pos .. pos + n - 1) against the oracle's.  Both sides
+    quantize FP32 rows x (K: divided by the smoothing factors) that differ by summation order, within
+    the hidden-state bar: ||dx||_2 <= HIDDEN_REL_L2 ||x||_2.  A scale is max|x| / 127, and a maximum
+    moves by at most ||dx||_inf <= ||dx||_2, so |ds| <= HIDDEN_REL_L2 ||x||_2 / 127 (||x||_2 taken from
+    the oracle's codes times its scale).  A code may land one step away, rarely (at most FLIP_FRACTION
+    of them).  Returned per K / V: the largest dequantized-row relative L2 difference, the fraction of
+    differing codes and the largest relative scale difference (for the report; a flip in an outlier
+    channel of a smoothed key is worth about 1/127 of the row on its own, so no fixed row bar fits)."""
+    kq, vq, ks, vs, sg = split_int8_cache(kv)
+    assert np.array_equal(sg, okv["sigma"]), f"{tag}: smoothing factors changed"
+    out = {}
+    for name, gq, gs, oq, os_, sig in (("K", kq, ks, okv["kq"], okv["ks"], okv["sigma"]),
+                                      ("V", vq, vs, okv["vq"], okv["vs"], None)):
+        gq, oq = gq[:, :, pos:pos + n].astype(np.int32), oq[:, :, pos:pos + n].astype(np.int32)
+        gs, os_ = gs[:, :, pos:pos + n].astype(np.float64), os_[:, :, pos:pos + n].astype(np.float64)
+        assert np.abs(gq - oq).max() <= 1, f"{tag} {name}: a code off by more than one step"
+        frac = float(np.mean(gq != oq))
+        assert frac < FLIP_FRACTION, f"{tag} {name}: {frac:.3%} of codes differ"
+        xnorm = np.linalg.norm(oq * os_[..., None], axis=-1)  # ||x||_2 of the oracle's row (smoothed units)
+        assert np.all(np.abs(gs - os_) <= HIDDEN_REL_L2 * xnorm / 127.0 + 1e-30), f"{tag} {name}: scale beyond bound"
+        rs = np.abs(gs - os_) / np.maximum(os_, 1e-30)
+        s4 = None if sig is None else sig[:, :, None, :]
+        gd = dequantize_kv_rows(gq.astype(np.int8), gs, s4, np.float64)
+        od = dequantize_kv_rows(oq.astype(np.int8), os_, s4, np.float64)
+        rel = np.linalg.norm(gd - od, axis=-1) / np.maximum(np.linalg.norm(od, axis=-1), 1e-30)
+        out[name] = (float(rel.max()), frac, float(rs.max()))
+    return out

@@ -2,6 +2,7 @@
 declared entry point, and the planner builds, balances and validates schedules
 (dry runs) or rejects shapes it cannot tile."""
 
+import ctypes
 import os
 import re
 
@@ -276,3 +277,28 @@ def test_sampling_limits_top_k_by_vocab_and_workers():
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(TINY, 40, n_workers=300, sampling=(1.0, 8, 1.0))
     assert "256 workers" in tiles.last_error() or e.value.code == tiles.TILES_E_CONFIG
+
+
+
+@pytest.mark.parametrize("key", ["qwen4b_32k_kv8", "llama1b_kv8"])
+def test_int8_kv_plans_validate(key):
+    """INT8 KV plans: at most 2048 positions per split (the split count is raised to fit), LDS for the
+    split's scales, the KV format in the plan info; the same shapes with BF16 KV plan differently."""
+    wl = WORKLOADS[key]
+    info = tiles.dry_run(wl.model, wl.capacity, kv="int8")
+    assert info.kv_format == 1
+    assert info.lds_bytes <= 160 * 1024
+    assert (wl.capacity + info.kv_splits - 1) // info.kv_splits <= 2048
+    assert tiles.dry_run(wl.model, wl.capacity).checksum != info.checksum
+    assert tiles.lib().tiles_plan_debug_validate(ctypes.byref(tiles.make_config(wl.model, wl.capacity, kv="int8")),
+                                                 256, 0) == tiles.TILES_OK
+
+
+def test_int8_kv_format_and_split_limits_rejected():
+    cfg = tiles.make_config(TINY, 40)
+    cfg.kv_format = 2
+    info = tiles.PlanInfo()
+    assert tiles.lib().tiles_plan_dry_run(ctypes.byref(cfg), 256, ctypes.byref(info)) == tiles.TILES_E_CONFIG
+    with pytest.raises(tiles.TilesError):  # a forced split count leaving more than 2048 positions per split
+        tiles.dry_run(TINY, 5000, kv="int8", kv_splits=2)
+    assert tiles.lib().tiles_kv_convert_int8(None, None, None, 1, 0, None) == tiles.TILES_E_ARG

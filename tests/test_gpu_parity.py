@@ -12,7 +12,8 @@ from tile_scheduled_persistent_amd import synth, tiles
 from tile_scheduled_persistent_amd.configs import TINY, WORKLOADS, scaled
 
 from parity_util import (HIDDEN_REL_L2, Setup, check_step, compare_free_running, compare_sampled_teacher_forced,
-                         compare_teacher_forced, kv_rows_close, run_gpu, run_gpu_sampled, top2_margin)
+                         compare_teacher_forced, kv8_rows_close, kv_rows_close, run_gpu, run_gpu_sampled,
+                         split_int8_cache, top2_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +30,7 @@ def _oracle_forced(setup: Setup, inputs_prefix, n_steps, plan, pos0=None, tag=""
     """GPU one step per launch, fed the oracle's tokens (prompt first); every step compared."""
     o = setup.oracle()
     okv = setup.oracle_kv()
-    kv = setup.fresh_kv()
+    kv = setup.fresh_kv(plan)
     pos = setup.n_cached if pos0 is None else pos0
     tok = inputs_prefix[0]
     margins = []
@@ -40,8 +41,11 @@ def _oracle_forced(setup: Setup, inputs_prefix, n_steps, plan, pos0=None, tag=""
         margins.append(check_step(f"{tag} step {i}", g_l[0], g_h[0], o_l, o_h, int(g_t[0]), o_t))
         tok = inputs_prefix[i + 1] if i + 1 < len(inputs_prefix) else o_t
     # the KV rows the GPU wrote against the oracle's (same bar as the hidden states)
-    kv_rows_close(f"{tag} K", kv.k, okv["k"], pos, n_steps)
-    kv_rows_close(f"{tag} V", kv.v, okv["v"], pos, n_steps)
+    if setup.kv == "int8":
+        kv8_rows_close(tag, kv, okv, pos, n_steps)
+    else:
+        kv_rows_close(f"{tag} K", kv.k, okv["k"], pos, n_steps)
+        kv_rows_close(f"{tag} V", kv.v, okv["v"], pos, n_steps)
     return margins
 
 
@@ -632,3 +636,139 @@ def test_full_size_sampled_every_step():
     print(f"{key}: {n} of {n} steps compared; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
           f"{stats['logit_abs_max']:.2e}, draws compared exactly {stats['draws_exact']} of {n}; distinct tokens "
           f"{len(set(g_t.tolist()))}", flush=True)
+
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache with smoothed keys
+# ---------------------------------------------------------------------------
+
+def test_kv8_conversion_matches_the_oracle_bit_for_bit():
+    """The library's conversion of a BF16 cache prefix (smoothing factors, codes, scales) equals the
+    oracle's bit for bit (the same FP32 operations, correctly rounded divisions)."""
+    from oracle import convert_kv_int8
+
+    for m, cap, cached in ((TINY, 40, 29), (QK128, 64, 37), (TINY, 16, 0)):
+        s = Setup(m, cap, cached, key_scale=True)
+        with s.plan(kv_format="int8") as plan:
+            assert plan.info().kv_format == 1
+            kv = tiles.KVCache.convert_int8(plan, s.k0, s.v0, cached)
+            torch.cuda.synchronize()
+        o = convert_kv_int8(s.kv_bits, cached)
+        kq, vq, ks, vs, sg = split_int8_cache(kv)
+        assert kv.length == cached
+        assert np.array_equal(sg, o["sigma"])
+        assert np.array_equal(kq[:, :, :cached], o["kq"][:, :, :cached])
+        assert np.array_equal(vq[:, :, :cached], o["vq"][:, :, :cached])
+        assert np.array_equal(ks[:, :, :cached], o["ks"][:, :, :cached])
+        assert np.array_equal(vs[:, :, :cached], o["vs"][:, :, :cached])
+
+
+def test_kv8_tiny_every_step_against_oracle():
+    wl = WORKLOADS["tiny"]
+    s = Setup(TINY, wl.capacity, 0, kv="int8")
+    prompt = synth.make_tokens(TINY, wl.prompt_len)
+    with s.plan() as plan:
+        _oracle_forced(s, prompt, wl.prompt_len + wl.n_steps, plan, tag="tiny kv8")
+
+
+@pytest.mark.parametrize("heads", [0, 2, 4])
+def test_kv8_qk_norm_head_dim_128_with_outlier_keys(heads):
+    # cached keys with per-channel scales U(0.5, 4): what the smoothing is for
+    s = Setup(QK128, 64, 37, key_scale=True, kv="int8")
+    with s.plan(attn_heads=heads) as plan:
+        _oracle_forced(s, synth.make_tokens(QK128, 1), 10, plan, tag=f"qk128 kv8 heads {heads}")
+
+
+@pytest.mark.parametrize("splits,mode", [(1, 1), (3, 2), (7, 2)])
+def test_kv8_split_counts_ragged_and_wide(splits, mode):
+    s = Setup(RAGGED, 48, 30, kv="int8")
+    with s.plan(kv_splits=splits, combine_mode=mode) as plan:
+        _oracle_forced(s, synth.make_tokens(RAGGED, 1), 6, plan, tag=f"ragged kv8 S{splits}")
+    s = Setup(WIDE, 96, 70, kv="int8")
+    with s.plan() as plan:
+        _oracle_forced(s, synth.make_tokens(WIDE, 1), 6, plan, tag="wide kv8")
+
+
+def test_kv8_repeatable_chunk_invariant_and_poison_at_capacity():
+    """Bit-identical repeats; one-step launches equal the multi-step launch; with the cache filled to
+    capacity, poisoned (NaN) scales of the rows a launch writes change nothing."""
+    s = Setup(WIDE, 80, 70, kv="int8")
+    tok = synth.make_tokens(WIDE, 1)[0]
+    n = 10
+    with s.plan() as plan:
+        kv_a = s.fresh_kv(plan)
+        a = run_gpu(plan, kv_a, tok, n)
+        kv_b = s.fresh_kv(plan)
+        b = run_gpu(plan, kv_b, tok, n)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+        assert torch.equal(kv_a.k, kv_b.k) and torch.equal(kv_a.k_scale, kv_b.k_scale)
+        kv = s.fresh_kv(plan)
+        t = tok
+        for i in range(n):
+            t1, l1, _ = run_gpu(plan, kv, t, 1, want_hidden=False)
+            assert int(t1[0]) == int(a[0][i])
+            assert np.array_equal(l1[0].view(np.uint32), a[1][i].view(np.uint32))
+            t = int(t1[0])
+        assert torch.equal(kv.k, kv_a.k) and torch.equal(kv.v_scale, kv_a.v_scale)
+    with s.plan(flags=tiles.TILES_POISON | tiles.TILES_DEBUG_HIDDEN) as plan:
+        kv_p = s.fresh_kv(plan)
+        p = run_gpu(plan, kv_p, tok, n)
+    assert kv_p.length == kv_p.capacity
+    assert np.array_equal(a[0], p[0]) and np.array_equal(a[1].view(np.uint32), p[1].view(np.uint32))
+    assert torch.equal(kv_p.k, kv_a.k) and torch.equal(kv_p.k_scale, kv_a.k_scale)
+
+
+def test_kv8_entry_point_errors():
+    s = Setup(TINY, 40, 10, kv="int8")
+    with s.plan() as plan:
+        kv = s.fresh_kv(plan)
+        out = torch.zeros(2, dtype=torch.int32, device="cuda")
+        bad = tiles.KVCache(kv.k, None, kv.length, kv.k_scale, None, kv.k_smooth)
+        c = bad.struct()
+        assert tiles.lib().tiles_decode(plan._h, ctypes.byref(c), 0, 2, out.data_ptr(), None) == tiles.TILES_E_ARG
+        assert "k_scale" in tiles.last_error()
+        with pytest.raises(tiles.TilesError):
+            tiles.KVCache.convert_int8(plan, s.k0, s.v0, 41)  # length beyond the capacity
+    s16 = Setup(TINY, 40, 10)
+    with s16.plan() as plan:  # a BF16 plan converts nothing
+        with pytest.raises(tiles.TilesError):
+            tiles.KVCache.convert_int8(plan, s16.k0, s16.v0, 10)
+
+
+FULL_KV8 = ["qwen4b_32k_kv8", "llama1b_kv8"]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", FULL_KV8)
+def test_full_size_kv8_every_step(key):
+    """The INT8 KV launch bench.py times, every step against the oracle teacher-forced on the GPU's
+    tokens (its own INT8 cache converted from the same BF16 prefix); the timed configuration gives the
+    same tokens and cache bytes."""
+    wl = WORKLOADS[key]
+    m, n = wl.model, wl.n_steps
+    s = Setup(m, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda", kv="int8")
+    tok = synth.make_tokens(m, 1)[0]
+    with s.plan(flags=0) as plan:
+        kv_timed = s.fresh_kv(plan)
+        out_t = torch.zeros(n, dtype=torch.int32, device="cuda")
+        plan.decode(kv_timed, tok, n, out_t, None)
+        assert plan.status() == tiles.TILES_OK, tiles.last_error()
+        timed_tokens = out_t.cpu().numpy().astype(np.int64)
+    with s.plan() as plan:
+        kv = s.fresh_kv(plan)
+        g_t, g_l, g_h = run_gpu(plan, kv, tok, n)
+    assert np.array_equal(timed_tokens, g_t), "timed configuration gives other tokens"
+    assert torch.equal(kv_timed.k, kv.k) and torch.equal(kv_timed.k_scale, kv.k_scale)
+    del kv_timed
+    print(f"{key}: GPU launch of {n} steps done; teacher-forced oracle for all {n} steps", flush=True)
+    okv = s.oracle_kv()
+    o_res = s.oracle().decode(okv, tok, wl.n_cached, n, teacher=[int(t) for t in g_t[:-1]], widen_kv_once=True)
+    stats = compare_teacher_forced(key, g_t, g_l, g_h, o_res)
+    assert stats["steps"] == n
+    rows = kv8_rows_close(key, kv, okv, wl.n_cached, n)
+    print(f"{key}: {n} of {n} steps compared; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
+          f"{stats['logit_abs_max']:.2e}, tokens checked at margin > 0.1: {stats['tokens_checked']}; written rows "
+          f"(dequantized rel L2, codes differing, scale rel) K {rows['K'][0]:.2e} {rows['K'][1]:.3%} {rows['K'][2]:.1e}, "
+          f"V {rows['V'][0]:.2e} {rows['V'][1]:.3%} {rows['V'][2]:.1e}", flush=True)

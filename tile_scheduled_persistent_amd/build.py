@@ -15,10 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtiles.so")
-# The worker units each instantiate the persistent worker for one weight format and token selection
-# (they include kernel.hip); every source compiles to an object of its own, in parallel, then links.
-SOURCES = ["kernel.hip", "workers_bf16.hip", "workers_bf16_sampled.hip", "workers_int8.hip",
-           "workers_int8_sampled.hip", "planner.cpp", "api.cpp"]
+# The worker units each instantiate the persistent worker for one weight format, token selection
+# and KV format (they include kernel.hip); every source compiles to an object of its own, in
+# parallel, then links.
+WORKER_UNITS = [f"workers_{w}{s}{k}.hip" for w in ("bf16", "int8") for s in ("", "_sampled") for k in ("", "_kv8")]
+SOURCES = ["kernel.hip", *WORKER_UNITS, "planner.cpp", "api.cpp"]
 HEADERS = ["plan_types.h", "planner.h"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -59,7 +60,7 @@ def build(verbose: bool = False) -> str:
     common = [HIPCC, "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", *DEVICE_FLAGS,
               f"-DTILES_BUILD_ID={bid}", "-I", os.path.join(ROOT, "include")]
     objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_run, common + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
                 for src, obj in zip(SOURCES, objs)]

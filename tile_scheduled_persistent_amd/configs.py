@@ -68,6 +68,10 @@ class ModelConfig:
         """K and V bytes of one position over all layers (BF16)."""
         return 2 * 2 * self.n_layers * self.n_kv_heads * self.head_dim
 
+    def int8_kv_bytes_per_position(self) -> int:
+        """INT8 KV cache: K and V codes (one byte per element) and their two FP32 scales, all layers."""
+        return self.n_layers * self.n_kv_heads * (2 * self.head_dim + 8)
+
 
 @dataclass(frozen=True)
 class Workload:
@@ -82,6 +86,7 @@ class Workload:
     description: str = ""
     weights: str = "bf16"        # "int8": weight-only INT8 linear layers (per-row codes and scales)
     sampling: Optional[tuple] = None  # (temperature, top_k, top_p): sampled steps instead of greedy
+    kv: str = "bf16"             # "int8": INT8 KV cache with smoothed keys
 
     @property
     def capacity(self) -> int:
@@ -97,7 +102,8 @@ class Workload:
         every attended position read once, one K/V position written."""
         m = self.model
         wb = m.int8_weight_bytes_per_token() if self.weights == "int8" else m.weight_bytes_per_token()
-        return wb + m.kv_bytes_per_position() * self.avg_attended() + m.kv_bytes_per_position()
+        kvp = m.int8_kv_bytes_per_position() if self.kv == "int8" else m.kv_bytes_per_position()
+        return wb + kvp * self.avg_attended() + kvp
 
 
 TINY = ModelConfig("tiny", 2, 256, 4, 2, 64, 1024, 4096, 1e4, 1e-5, False)
@@ -123,6 +129,13 @@ WORKLOADS: Dict[str, Workload] = {
                                 description="Llama-3.2-1B-shaped decode with top-k/top-p sampling inside the launch "
                                             "(temperature 0.6, top-k 20, top-p 0.95), 64 tokens after 1023 cached "
                                             "positions"),
+    "llama1b_kv8": Workload("llama1b_kv8", LLAMA_1B, 1023, 64, kv="int8",
+                            description="Llama-3.2-1B-shaped decode with an INT8 KV cache (smoothed keys), "
+                                        "64 tokens after 1023 cached positions"),
+    "qwen4b_32k_kv8": Workload("qwen4b_32k_kv8", QWEN3_4B, 32767, 32, key_scale=True, kv="int8",
+                               description="Qwen3-4B-shaped decode with an INT8 KV cache (smoothed keys), 32 tokens "
+                                           "after 32767 cached positions, cached keys with per-channel scales "
+                                           "U(0.5, 4)"),
     "llama1b_int8": Workload("llama1b_int8", LLAMA_1B, 1023, 64, weights="int8",
                              description="Llama-3.2-1B-shaped decode with weight-only INT8 linear layers, "
                                          "64 tokens after 1023 cached positions"),

@@ -30,7 +30,9 @@
 #endif
 
 namespace tiles {
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled);
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8);
+hipError_t launch_kv_convert(const uint16_t* k, const uint16_t* v, int64_t cap, int64_t length, int hd, int64_t nheads,
+                             int8_t* codes, float* ks, float* vs, float* sigma, hipStream_t stream);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
 hipError_t launch_fill(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_fill_blocks(uint16_t* p, int nblk, int64_t stride, int64_t count, uint16_t v, hipStream_t stream);
@@ -231,7 +233,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0, hp.top_k > 0);
+  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0, hp.top_k > 0, hp.kv8 != 0);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -383,7 +385,9 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   if (p->hp.top_k > 0 && !uniforms)
     return set_err(TILES_E_ARG, "this plan samples (top_k > 0): use tiles_decode_sampled with the step uniforms");
   if (p->hp.top_k == 0 && uniforms) return set_err(TILES_E_ARG, "this plan is greedy (top_k = 0): use tiles_decode");
-  if (!kv->k || !kv->v) return set_err(TILES_E_ARG, "null KV buffers");
+  if (!kv->k || (!kv->v && !p->hp.kv8)) return set_err(TILES_E_ARG, "null KV buffers");
+  if (p->hp.kv8 && (!kv->k_scale || !kv->v_scale || !kv->k_smooth))
+    return set_err(TILES_E_ARG, "an INT8 KV plan needs the cache's k_scale, v_scale and k_smooth");
   if (n_steps < 1 || n_steps > MAX_STEPS) return set_err(TILES_E_ARG, "n_steps must be in [1, 64]");
   const HostPlan& hp = p->hp;
   if (token < 0 || token >= hp.s.V) return set_err(TILES_E_ARG, "token out of range");
@@ -425,7 +429,10 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   a.sync = sync;
   a.table_check = p->d_table_check;
   a.kv_k = static_cast<uint16_t*>(kv->k);
-  a.kv_v = static_cast<uint16_t*>(kv->v);
+  a.kv_v = static_cast<uint16_t*>(p->hp.kv8 ? kv->k : kv->v);  // (INT8 KV: one interleaved array)
+  a.kv_ks = hp.kv8 ? kv->k_scale : nullptr;
+  a.kv_vs = hp.kv8 ? kv->v_scale : nullptr;
+  a.kv_sigma = hp.kv8 ? kv->k_smooth : nullptr;
   a.kv_cap = kv->capacity;
   a.out_tokens = out_tokens;
   a.out_logits = out_logits;
@@ -468,9 +475,15 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   if (p->cfg.flags & TILES_POISON) {
     // NaN into the rows this launch writes: a read before the write would surface as NaN
     const int nblk = hp.s.n_layers * hp.s.n_kv;
-    const int64_t stride = kv->capacity * hp.s.hd, first = kv->length * hp.s.hd, count = (int64_t)n_steps * hp.s.hd;
-    HIP_TRY(launch_fill_blocks(a.kv_k + first, nblk, stride, count, 0x7fc0, p->stream));
-    HIP_TRY(launch_fill_blocks(a.kv_v + first, nblk, stride, count, 0x7fc0, p->stream));
+    if (hp.kv8) {  // INT8 codes cannot be NaN: the rows' scales are (two BF16 NaN halves make an FP32 NaN)
+      const int64_t stride = kv->capacity * 2, first = kv->length * 2, count = (int64_t)n_steps * 2;
+      HIP_TRY(launch_fill_blocks(reinterpret_cast<uint16_t*>(a.kv_ks) + first, nblk, stride, count, 0x7fc0, p->stream));
+      HIP_TRY(launch_fill_blocks(reinterpret_cast<uint16_t*>(a.kv_vs) + first, nblk, stride, count, 0x7fc0, p->stream));
+    } else {
+      const int64_t stride = kv->capacity * hp.s.hd, first = kv->length * hp.s.hd, count = (int64_t)n_steps * hp.s.hd;
+      HIP_TRY(launch_fill_blocks(a.kv_k + first, nblk, stride, count, 0x7fc0, p->stream));
+      HIP_TRY(launch_fill_blocks(a.kv_v + first, nblk, stride, count, 0x7fc0, p->stream));
+    }
   }
   void* args[] = {&a};
   // (the worker checks its watchdog every 32 polling rounds; a short test watchdog runs the test
@@ -513,6 +526,24 @@ int tiles_decode_noalloc(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t
   return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, true, nullptr);
 }
 
+int tiles_kv_convert_int8(tiles_plan_t* p, const void* k_bf16, const void* v_bf16, int64_t capacity, int64_t length,
+                          tiles_kv_t* dst) {
+  if (!p || !k_bf16 || !v_bf16 || !dst) return set_err(TILES_E_ARG, "null plan, source or destination");
+  if (!p->hp.kv8) return set_err(TILES_E_ARG, "the plan's KV format is BF16");
+  if (!dst->k || !dst->k_scale || !dst->v_scale || !dst->k_smooth) return set_err(TILES_E_ARG, "null INT8 KV buffers");
+  if (capacity < 1 || length < 0 || length > capacity || dst->capacity != capacity)
+    return set_err(TILES_E_ARG, "bad capacity or length (dst->capacity must equal capacity)");
+  const Shape& s = p->hp.s;
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != p->device) return set_err(TILES_E_DEVICE, "plan was created for another device");
+  HIP_TRY(launch_kv_convert(static_cast<const uint16_t*>(k_bf16), static_cast<const uint16_t*>(v_bf16), capacity, length,
+                            s.hd, (int64_t)s.n_layers * s.n_kv, static_cast<int8_t*>(dst->k), dst->k_scale,
+                            dst->v_scale, dst->k_smooth, p->stream));
+  dst->length = length;
+  return TILES_OK;
+}
+
 void tiles_plan_destroy(tiles_plan_t* p) { release(p); }
 
 const char* tiles_last_error(void) { return g_err.c_str(); }
@@ -531,6 +562,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->attn_heads = hp.T;
   info->weight_format = hp.q8 ? TILES_WEIGHTS_INT8 : TILES_WEIGHTS_BF16;
   info->top_k = hp.top_k;
+  info->kv_format = hp.kv8 ? TILES_KV_INT8 : TILES_KV_BF16;
   for (size_t wv = 0; wv < hp.waves.size(); ++wv)
     if (hp.waves[wv].kind == KIND_O) {
       info->o_workers = hp.wave_busy[wv];
@@ -629,10 +661,10 @@ int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   const uint32_t limit = rounds ? rounds : DEFAULT_SPIN_LIMIT;
   if (limit < 32 && !p->kernel_wd) {
-    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0);
+    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0, p->hp.kv8 != 0);
     if (!k)
-      return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights, greedy decoding and one query head "
-                                     "per attention tile");
+      return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and KV, greedy decoding and one "
+                                     "query head per attention tile");
     HIP_TRY(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p->hp.lds_bytes));
     int occ = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, BLOCK_THREADS, p->hp.lds_bytes));

@@ -141,6 +141,11 @@ constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within 16
 
+__device__ __forceinline__ float sum4(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  return v;
+}
 __device__ __forceinline__ float sum8(float v) {
   v += dpp<DPP_XOR1>(v);
   v += dpp<DPP_XOR2>(v);
@@ -152,8 +157,10 @@ __device__ __forceinline__ float sum16(float v) {
   v += dpp<DPP_MIRROR>(v);
   return v;
 }
-// Lane exchanges across 8, 16 and 32 lanes without the LDS crossbar: a DPP rotation by 8
-// within each 16-lane row, and the gfx950 permlane swaps of 16-lane rows and 32-lane halves.
+// Lane exchanges across 4, 8, 16 and 32 lanes without the LDS crossbar: DPP rotations by 4 and 8
+// within each 16-lane row (for sums and maxima over lanes of equal residue a rotation does what an
+// exchange does), and the gfx950 permlane swaps of 16-lane rows and 32-lane halves.
+__device__ __forceinline__ float xor4(float v) { return dpp<0x124>(v); }  // row_ror:4
 __device__ __forceinline__ float xor8(float v) { return dpp<0x128>(v); }  // row_ror:8
 __device__ __forceinline__ float xor16(float v, int lane) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -165,12 +172,22 @@ __device__ __forceinline__ float xor32(float v, int lane) {
 }
 template <int OFF>
 __device__ __forceinline__ float lane_xor(float v, int lane) {
-  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane_xor offsets: 8, 16, 32");
-  if constexpr (OFF == 8) return xor8(v);
+  static_assert(OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "lane_xor offsets: 4, 8, 16, 32");
+  if constexpr (OFF == 4) return xor4(v);
+  else if constexpr (OFF == 8) return xor8(v);
   else if constexpr (OFF == 16) return xor16(v, lane);
   else return xor32(v, lane);
 }
 
+// the largest value of the wavefront, in every lane
+__device__ __forceinline__ float wave_max(float v, int lane) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  v = fmaxf(v, lane_xor<16>(v, lane));
+  return fmaxf(v, lane_xor<32>(v, lane));
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v = sum16(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -197,6 +214,8 @@ constexpr int SM_WDONE = 64;   // uint64[2][8]: each compute wavefront's done st
 constexpr int SM_ROPE = 256;   // float[head_dim]: (cos, sin) pairs of the current position (attention tiles)
 constexpr int SM_QGAIN = 512;  // float[head_dim]: q-norm gains (attention tiles with q/k norm)
 constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
+constexpr int SM_KSMOOTH = 768;  // float[head_dim]: INT8 KV key smoothing factors of the tile's KV head
+constexpr int SM_KVCUR = 896;    // float[2]: INT8 KV scales of the current position's K and V rows
 
 struct Lds {
   float* vec;
@@ -852,6 +871,18 @@ __device__ __forceinline__ void stage_batch(const uint8_t* packed, const Range& 
         : "memory");
   }
 }
+// One 4-byte direct-to-LDS load per lane: lane i's word lands at LDS byte address lds + 4 i (lanes
+// outside EXEC write nothing).  Like the 16-byte form, it is invisible to the compiler: a consumer
+// waits for it explicitly.
+__device__ __forceinline__ void stage_dword(const float* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
 // Stage batches NB .. NB + n of GEMV range r (n = what the range has beyond its first NB
 // batches, at most `limit`); returns n.  The area's previous contents must have been read.
 template <int B, int NB>
@@ -1047,6 +1078,24 @@ template <int HD, int G>
 __device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + G * HD + 2 * HD; }
 template <int HD, int G>
 __device__ __forceinline__ float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * pstride<HD>(); }
+// INT8 KV: the split's K scales, then its V scales, by position - split start (MAX_SPLIT_POSITIONS_KV8
+// each at most; the planner sizes the area)
+template <int HD, int G>
+__device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merged<HD, G>(L) + G * pstride<HD>(); }
+
+// The split [lo, hi) that split sp of S covers at attended length L_att (positions < 2^31).
+__device__ __forceinline__ void split_bounds(int S, int sp, int L_att, int& lo, int& hi) {
+  const int ch = (int)((uint32_t)(L_att + S - 1) / (uint32_t)S);
+  lo = sp * ch;
+  hi = lo + ch < L_att ? lo + ch : L_att;
+  if (lo > L_att) lo = L_att;
+}
+
+// INT8 KV: symmetric INT8 code of r at scale s (r / s rounded half to even, clamped; 0 when s = 0),
+// the divisions correctly rounded
+__device__ __forceinline__ float kv_code(float r, float s) {
+  return s > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(r, s)), -127.f), 127.f) : 0.f;
+}
 
 // all wavefronts: raw q (the tile's G query heads, from head qa), k, v of KV head g into vec from
 // the QKV wave's output
@@ -1065,13 +1114,23 @@ __device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, co
 
 // all wavefronts, between barriers P and A: wave u < G normalises (optional) and rotates query
 // head u, wave G the key; wave G + 1 rounds the value.  LDS only (plus read-only tables).
-template <int HD, int G>
-__device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos) {
+// INT8 KV (KV8): the query heads are also multiplied by the key smoothing factors (a score is then the
+// key row's scale times the dot product of these with its codes), and the current K and V rows are
+// quantized: kc / vc hold their codes, SM_KVCUR their scales (also put at the split's scale area
+// when the split holds the current position, split sp).
+template <int HD, int G, bool KV8>
+__device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos,
+                                              int sp) {
   constexpr int HALF = HD / 2;
   float* q = L.part;
   float* kc = q + G * HD;
   float* vc = kc + HD;
   const float* raw = L.vec;
+  int slo = 0, shi = 0;
+  if (KV8) split_bounds(a.S, sp, pos + 1, slo, shi);
+  const bool own_cur = KV8 && slo <= pos && pos < shi;
+  float* kss = attn_kscales<HD, G>(L);
+  float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
   if (wave_index <= G) {
     const int u = wave_index;
     float u0 = 0.f, u1 = 0.f;
@@ -1088,11 +1147,34 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
         u1 = u1 * rs * gn[lane + HALF];
       }
     }
+    float r0 = 0.f, r1 = 0.f;
     if (lane < HALF) {
       const float* cs = L.small + SM_ROPE + lane * 2;
       const float co = cs[0], si = cs[1];
-      const float r0 = u0 * co - u1 * si;
-      const float r1 = u1 * co + u0 * si;
+      r0 = u0 * co - u1 * si;
+      r1 = u1 * co + u0 * si;
+    }
+    if constexpr (KV8) {
+      const float* sg = L.small + SM_KSMOOTH;
+      if (u < G) {
+        if (lane < HALF) {
+          q[u * HD + lane] = r0 * a.qscale * sg[lane];
+          q[u * HD + lane + HALF] = r1 * a.qscale * sg[lane + HALF];
+        }
+      } else {  // the key: smoothed, then quantized per row
+        const float k0 = lane < HALF ? __fdiv_rn(r0, sg[lane]) : 0.f;
+        const float k1 = lane < HALF ? __fdiv_rn(r1, sg[lane + HALF]) : 0.f;
+        const float sk = __fdiv_rn(wave_max(fmaxf(fabsf(k0), fabsf(k1)), lane), 127.f);
+        if (lane < HALF) {
+          kc[lane] = kv_code(k0, sk);
+          kc[lane + HALF] = kv_code(k1, sk);
+        }
+        if (lane == 0) {
+          L.small[SM_KVCUR] = sk;
+          if (own_cur) kss[pos - slo] = sk;
+        }
+      }
+    } else if (lane < HALF) {
       if (u < G) {
         q[u * HD + lane] = r0 * a.qscale;
         q[u * HD + lane + HALF] = r1 * a.qscale;
@@ -1102,13 +1184,31 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
       }
     }
   } else if (wave_index == G + 1) {
-    for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
+    if constexpr (KV8) {
+      constexpr int NV = (HD + 63) / 64;
+      float v[NV], am = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        v[i] = lane + 64 * i < HD ? raw[(G + 1) * HD + lane + 64 * i] : 0.f;
+        am = fmaxf(am, fabsf(v[i]));
+      }
+      const float sv = __fdiv_rn(wave_max(am, lane), 127.f);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (lane + 64 * i < HD) vc[lane + 64 * i] = kv_code(v[i], sv);
+      if (lane == 0) {
+        L.small[SM_KVCUR + 1] = sv;
+        if (own_cur) vss[pos - slo] = sv;
+      }
+    } else {
+      for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
+    }
   }
 }
 
 // control wave, after barrier A: the split holding the current position writes its K/V row (the
 // tile of the KV head's first query heads, when the heads are spread over several tiles)
-template <int HD, int G>
+template <int HD, int G, bool KV8>
 __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
                                  int qa, int64_t L_att) {
   if (qa != g * (a.n_heads / a.n_kv)) return;
@@ -1118,7 +1218,21 @@ __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds&
   const int64_t lo = (int64_t)sp * ch;
   const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
   const int64_t cur = L_att - 1;
-  if (lo <= cur && cur < hi && lane < HD / 2) {
+  if (KV8 && lo <= cur && cur < hi) {  // the interleaved codes, four per lane, and the two scales
+    const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
+    if (lane < HD / 2) {
+      // word `lane` of the row: group lane / 4 of 8 dimensions, its K codes in words 0-1, V in 2-3
+      const int grp = lane >> 2, part = lane & 3;
+      const float* c = (part < 2 ? kc : vc) + grp * 8 + (part & 1) * 4;
+      const uint32_t w = ((uint32_t)(uint8_t)(int8_t)(int)c[0]) | ((uint32_t)(uint8_t)(int8_t)(int)c[1] << 8) |
+                         ((uint32_t)(uint8_t)(int8_t)(int)c[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)c[3] << 24);
+      st_u32(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.kv_k) + row * HD * 2) + lane, w);
+    }
+    if (lane == 0) {
+      st_u32(reinterpret_cast<uint32_t*>(a.kv_ks + row), __float_as_uint(L.small[SM_KVCUR]));
+      st_u32(reinterpret_cast<uint32_t*>(a.kv_vs + row), __float_as_uint(L.small[SM_KVCUR + 1]));
+    }
+  } else if (!KV8 && lo <= cur && cur < hi && lane < HD / 2) {
     const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
     const uint32_t kb = f32_to_bf16_bits(kc[2 * lane]) | (f32_to_bf16_bits(kc[2 * lane + 1]) << 16);
     const uint32_t vb = f32_to_bf16_bits(vc[2 * lane]) | (f32_to_bf16_bits(vc[2 * lane + 1]) << 16);
@@ -1131,6 +1245,7 @@ __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds&
 // Positions are below 2^31 (the planner bounds the cache capacity), so 32-bit arithmetic.
 struct AttnRange {
   int wlo, whi;
+  int lo;  // the split's first position
 };
 __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int c, int64_t L_att64) {
   const int L_att = (int)L_att64;
@@ -1141,6 +1256,7 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
   if (lo > L_att) lo = L_att;
   const int n = hi > lo ? hi - lo : 0;
   AttnRange r;
+  r.lo = lo;
   r.wlo = lo + (int)((uint32_t)(n * c) / NCOMP);
   r.whi = lo + (int)((uint32_t)(n * (c + 1)) / NCOMP);
   return r;
@@ -1158,6 +1274,11 @@ __device__ __forceinline__ AttnRange attn_range(const KernelArgs& a, int sp, int
 // maintenance at kernel boundaries.  The consumer discards what such a slot read (its weight
 // and V values are selected away, not multiplied by 0), so that row's contents never matter:
 // it may hold anything, NaN included.
+// Lanes per position: a lane's 16-byte load holds 8 dimensions of a position -- 8 BF16 values of a K
+// or a V row, or (INT8 KV) 8 K codes followed by the same 8 dimensions' V codes (the INT8 cache
+// interleaves K and V per group of 8 dimensions, one row of 2 x head_dim bytes per position).
+template <int HD, bool KV8>
+constexpr int kv_lpp() { return HD / 8; }
 template <int HD>
 __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j, int whi,
                                         int cur, int dummy, int dseg, u32x4& kw, u32x4& vw) {
@@ -1167,8 +1288,19 @@ __device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk, __amdgpu_buff
   kw = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, NT);
   vw = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, NT);
 }
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache, int64_t kvrow0, int hd) {
-  return rsrc(cache + kvrow0 * hd);
+// INT8 KV: one load per position group (each position's interleaved K and V codes)
+template <int HD>
+__device__ __forceinline__ void load_kv8(__amdgpu_buffer_rsrc_t rkv, int j, int whi, int cur, int dummy, int dseg,
+                                         u32x4& w) {
+  constexpr int LPP = HD / 8;
+  const int jj = (j < whi && j != cur) ? j : dummy;
+  w = __builtin_amdgcn_raw_buffer_load_b128(rkv, ((uint32_t)jj * LPP + dseg) * 16u, 0, NT);
+}
+// The first row of a KV head's cache (row bytes: head_dim BF16 values of K or of V, or (INT8 KV)
+// 2 x head_dim interleaved K and V codes)
+template <bool KV8>
+__device__ __forceinline__ const uint8_t* kv_head_base(const uint16_t* cache, int64_t kvrow0, int hd) {
+  return reinterpret_cast<const uint8_t*>(cache) + kvrow0 * hd * 2;
 }
 
 // The opening loads of an attention split -- the first NP (K, V) position-group pairs of this
@@ -1176,20 +1308,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* cache,
 // per-lane byte offset (a slot without a position reads the dummy row, as in load_kv).
 template <int NP>
 struct KvOpen {
-  const uint16_t* kbase;
-  const uint16_t* vbase;
+  const uint8_t* kbase;
+  const uint8_t* vbase;
   uint32_t off[NP];
 };
-template <int HD, int NP>
+template <int HD, int NP, bool KV8>
 __device__ __forceinline__ KvOpen<NP> kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c,
                                              int lane) {
-  constexpr int LPP = HD / 8, P = 64 / LPP;
+  constexpr int LPP = kv_lpp<HD, KV8>(), P = 64 / LPP;
   const int pp = lane / LPP, dseg = lane % LPP;
   KvOpen<NP> o;
   const AttnRange r = attn_range(a, sp, c, L_att);
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
-  o.kbase = a.kv_k + kvrow0 * HD;
-  o.vbase = a.kv_v + kvrow0 * HD;
+  o.kbase = kv_head_base<KV8>(a.kv_k, kvrow0, HD);
+  o.vbase = kv_head_base<KV8>(a.kv_v, kvrow0, HD);
   const int cur = (int)L_att - 1, dummy = (int)a.kv_cap - 1;
 #pragma unroll
   for (int s = 0; s < NP; ++s) {
@@ -1224,6 +1356,7 @@ __device__ __forceinline__ BatchSrc<B> kv_half_src(const KvOpen<NP>& o, int h) {
 __device__ __forceinline__ void pin(int& x) { asm volatile("" : "+s"(x)); }
 __device__ __forceinline__ void pin(int64_t& x) { asm volatile("" : "+s"(x)); }
 __device__ __forceinline__ void pin(const uint16_t*& p) { asm volatile("" : "+s"(p)); }
+__device__ __forceinline__ void pin(const uint8_t*& p) { asm volatile("" : "+s"(p)); }
 __device__ __forceinline__ void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(Range& r) {
   pin(r.k);
@@ -1241,10 +1374,21 @@ __device__ __forceinline__ void pin(KvOpen<NP>& o) {
   for (int s = 0; s < NP; ++s) pin_v(o.off[s]);
 }
 
-template <int HD>
-__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
-  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+// The values of a 16-byte K or V load: 8 BF16 values, or (INT8 KV) 16 codes
+template <bool KV8>
+__device__ __forceinline__ void unpack_kv(const u32x4 w, float* f) {
+  if constexpr (KV8) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f[b] = i8(w.x, b);
+      f[4 + b] = i8(w.y, b);
+      f[8 + b] = i8(w.z, b);
+      f[12 + b] = i8(w.w, b);
+    }
+  } else {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  }
 }
 
 // compute wave: one share of an attention split.  The position groups run through a ring of
@@ -1253,12 +1397,19 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 // steps ahead (past the range the reload reads the dummy row; every load is unconditional, see
 // the weight streaming above).  after(h) reuses the registers of batch slot h to fetch batch h
 // of the next GEMV tile.
-template <int HD, int G, int B, int NB, typename After>
+// INT8 KV (KV8): a slot is the first register of its pair, one load of the position group's
+// interleaved K and V codes (the second register is left alone in the loop: the ring keeps the BF16
+// shape, which the register budget needs; the opening fills it with the same row); a score
+// is the position's K scale times the dot product of the smoothed query (prepared in LDS) with the
+// K codes, and a V row contributes its codes times its scale times the weight; the split's scales
+// are staged in LDS.
+template <int HD, int G, int B, int NB, bool KV8, typename After>
 __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
                                                   int g, int sp, int64_t L_att, Stream<B, NB>& pf, After after,
                                                   uint64_t* ts) {
   constexpr int PS = pstride<HD>();
-  constexpr int D = NB * B / 2;  // ring slots: (K, V) pairs in the NB * B stream registers
+  constexpr int D = NB * B / 2;  // ring slots: register pairs in the NB * B stream registers
+  constexpr int SPB = B / 2;     // slots per batch of stream registers
   const float* q = L.part;
   const float* kc = q + G * HD;
   const float* vc = kc + HD;
@@ -1272,7 +1423,10 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const int ngroups = whi > wlo ? (whi - wlo + P - 1) / P : 0;
   const int pp = lane / LPP, dseg = lane % LPP;
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
-  const __amdgpu_buffer_rsrc_t rk = kv_rsrc(a.kv_k, kvrow0, HD), rv = kv_rsrc(a.kv_v, kvrow0, HD);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kv_head_base<KV8>(a.kv_k, kvrow0, HD));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(kv_head_base<KV8>(a.kv_v, kvrow0, HD));
+  const float* kss = attn_kscales<HD, G>(L) - rg.lo;  // (KV8) scales by position
+  const float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
   const int dummy = (int)a.kv_cap - 1;
   // Running state per query head: m[h] is the same in every lane (the largest score the wave has
   // seen so far, base 2); l[h] and acc[h][] are this lane's sums over its positions, weighted
@@ -1318,81 +1472,126 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
       m[h] = mn;
     }
   };
-  // weighted V of one position.  A slot without a position contributes exactly nothing: its
-  // weight is 0 and its V values are replaced by 0 (selects, not a multiplication by 0, so that
-  // whatever the masked load read -- a NaN in an unwritten cache row included -- cannot reach
-  // the sums).
-  auto accumulate = [&](bool valid, const float* sc, float* vf) {
+  // weighted V of one position (sv: its scale, INT8 KV; 1 for BF16 rows).  A slot without a
+  // position contributes exactly nothing: its weight is 0 and its V values are replaced by 0
+  // (selects, not a multiplication by 0, so that whatever the masked load read -- a NaN in an
+  // unwritten cache row included -- cannot reach the sums).
+  auto accumulate = [&](bool valid, const float* sc, float* vf, float sv) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.0f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = valid ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
       l[h] += p;
+      const float pv = KV8 ? p * sv : p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
     }
+  };
+  // slot s: its K and V values (8 dimensions each) from the stream registers
+  auto slot_k = [&](int s, float* kf) {
+    if constexpr (KV8) {
+      const u32x4 w = pf.v[2 * s];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        kf[b] = i8(w.x, b);
+        kf[4 + b] = i8(w.y, b);
+      }
+    } else {
+      unpack_kv<false>(pf.v[2 * s], kf);
+    }
+  };
+  auto slot_v = [&](int s, float* vf) {
+    if constexpr (KV8) {
+      const u32x4 w = pf.v[2 * s];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        vf[b] = i8(w.z, b);
+        vf[4 + b] = i8(w.w, b);
+      }
+    } else {
+      unpack_kv<false>(pf.v[2 * s + 1], vf);
+    }
+  };
+  auto slot_load = [&](int s, int j) {
+    if constexpr (KV8) load_kv8<HD>(rk, j, whi, cur, dummy, dseg, pf.v[2 * s]);
+    else load_kv<HD>(rk, rv, j, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
   };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_kv<HD>(rk, rv, wlo + s * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+    for (int s = 0; s < D; ++s) slot_load(s, wlo + s * P + pp);
   }
   stamp(ts, TS_ENTRY, lane);
   // One pass per D position groups (the ring): scores of every slot from its K row, one raise of
   // the running maximum, then the weighted V rows.  Slots past the range, or holding the current
   // position (taken from LDS below), are masked.  In every pass but the last each slot is
-  // reloaded (group + D) as soon as its V row is used; in the last pass each batch of B / 2
+  // reloaded (group + D) as soon as its V row is used; in the last pass each batch of SPB
   // slots, once used, fetches batch h of the next GEMV tile instead (after(h)).
+  constexpr int SUB = D;
   auto pass = [&](int g0, bool last) {
-    float sc[D][G], bm[G];
-    bool valid[D];
 #pragma unroll
-    for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
+    for (int s0 = 0; s0 < D; s0 += SUB) {
+      float sc[SUB][G], bm[G], svs[SUB];
+      bool valid[SUB];
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int j = wlo + (g0 + s) * P + pp;
-      valid[s] = j < whi && j != cur;
-      float kf[8];
-      unpack8<HD>(pf.v[2 * s], kf);
+      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sc[s][h] = score(kf, h);
-        bm[h] = valid[s] ? fmaxf(bm[h], sc[s][h]) : bm[h];
+      for (int t = 0; t < SUB; ++t) {
+        const int s = s0 + t;
+        const int j = wlo + (g0 + s) * P + pp;
+        valid[t] = j < whi && j != cur;
+        float ks = 1.f;
+        svs[t] = 1.f;
+        if constexpr (KV8) {  // the row's scales (a slot without a position reads the split's first)
+          const int jj = valid[t] ? j : rg.lo;
+          ks = kss[jj];
+          svs[t] = vss[jj];
+        }
+        float kf[8];
+        slot_k(s, kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          sc[t][h] = KV8 ? ks * score(kf, h) : score(kf, h);
+          bm[h] = valid[t] ? fmaxf(bm[h], sc[t][h]) : bm[h];
+        }
       }
-    }
-    raise(bm);
+      raise(bm);
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-      float vf[8];
-      unpack8<HD>(pf.v[2 * s + 1], vf);
-      accumulate(valid[s], sc[s], vf);
-      if (!last) {
-        load_kv<HD>(rk, rv, wlo + (g0 + s + D) * P + pp, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
-        __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
-      } else if (s % (B / 2) == B / 2 - 1) {
-        after(s / (B / 2));
-        __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < SUB; ++t) {
+        const int s = s0 + t;
+        float vf[8];
+        slot_v(s, vf);
+        accumulate(valid[t], sc[t], vf, svs[t]);
+        if (!last) {
+          slot_load(s, wlo + (g0 + s + D) * P + pp);
+          __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its slot's use (the overlap)
+        } else if (s % SPB == SPB - 1) {
+          after(s / SPB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
       }
-      if (s == 0 && g0 == 0) stamp(ts, TS_FIRST, lane);
     }
   };
   int g0 = 0;
   for (; g0 + D < ngroups; g0 += D) pass(g0, false);
   pass(g0, true);
-  if (wlo <= cur && cur < whi) {  // the current position (its K/V row is in LDS): lane group 0
+  if (wlo <= cur && cur < whi) {  // the current position (its K/V row, or its codes, in LDS): lane group 0
     float kf[8], vf[8], sc[G], bm[G];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kf[e] = kc[dseg * 8 + e];
       vf[e] = vc[dseg * 8 + e];
     }
+    const float ks = KV8 ? L.small[SM_KVCUR] : 1.f;
+    const float sv = KV8 ? L.small[SM_KVCUR + 1] : 1.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      sc[h] = score(kf, h);
+      sc[h] = KV8 ? ks * score(kf, h) : score(kf, h);
       bm[h] = pp == 0 ? sc[h] : -INFINITY;
     }
     raise(bm);
-    accumulate(pp == 0, sc, vf);
+    accumulate(pp == 0, sc, vf, sv);
   }
   // every lane's sums are relative to the same maximum: add up the lanes of equal dimensions
   auto sum_lanes = [&](auto off_tag) {
@@ -1487,7 +1686,7 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP>
+template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP, bool KV8>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
@@ -1579,7 +1778,36 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           gk1 = bf16_to_f32(gkk[lane + HALF]);
         }
       }
+      // INT8 KV: the control wave also loads the KV head's key smoothing factors, and every
+      // wavefront stages a share of the split's K and V scales of the cached positions straight into
+      // LDS (64 positions per load, no registers held across the polls; issued before the polls
+      // like the others; the current position's come from the LDS prologue)
+      constexpr int SPT = MAX_SPLIT_POSITIONS_KV8 / BLOCK_THREADS;  // 64-position loads per wavefront
+      float sg0 = 0.f, sg1 = 0.f;
+      if constexpr (KV8) {
+        const int64_t kvrow0 = ((int64_t)layer * a.n_kv + t.row0) * a.kv_cap;
+        if (CTRL && lane < HALF) {
+          const float* sg = a.kv_sigma + ((int64_t)layer * a.n_kv + t.row0) * HD;
+          sg0 = sg[lane];
+          sg1 = sg[lane + HALF];
+        }
+        const int pos = a.pos0 + step;
+        int slo = 0, shi = 0;
+        split_bounds(a.S, t.nrows, pos + 1, slo, shi);
+        const int sn = (shi < pos ? shi : pos) - slo;  // cached positions of the split
+        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)attn_kscales<HD, G>(L);
+        for (int i = 0; i < SPT; ++i) {
+          const int e0 = (wave + i * (BLOCK_THREADS / 64)) * 64;  // wavefront-uniform
+          if (e0 >= sn) break;
+          if (e0 + lane < sn) {
+            const int64_t g = kvrow0 + slo + e0 + lane;
+            stage_dword(a.kv_ks + g, kl + 4u * (uint32_t)e0);
+            stage_dword(a.kv_vs + g, kl + 4u * (uint32_t)(MAX_SPLIT_POSITIONS_KV8 + e0));
+          }
+        }
+      }
       ab = gather_qkv<HD, G, WD>(a, L, in, t.row0, t.aux0, wave, lane, par);
+      if constexpr (KV8) wait_vmcnt<0>();  // the staged scales are in LDS before the tile's barrier
       if (CTRL && lane < HALF) {
         L.small[SM_ROPE + 2 * lane] = cs.x;
         L.small[SM_ROPE + 2 * lane + 1] = cs.y;
@@ -1587,6 +1815,10 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         L.small[SM_QGAIN + lane + HALF] = gq1;
         L.small[SM_KGAIN + lane] = gk0;
         L.small[SM_KGAIN + lane + HALF] = gk1;
+        if (KV8) {
+          L.small[SM_KSMOOTH + lane] = sg0;
+          L.small[SM_KSMOOTH + lane + HALF] = sg1;
+        }
       }
       break;
     }
@@ -1604,7 +1836,7 @@ __device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileD
 }
 
 // LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale.
-template <int HD, int G, bool Q8>
+template <int HD, int G, bool Q8, bool KV8>
 __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
                                               const TileDesc& t, int layer, int pos) {
   float rs = 1.0f;
@@ -1614,7 +1846,7 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     for (int w = 0; w < NWAVES; ++w) tot += L.small[SM_SS + w];
     rs = 1.0f / sqrtf(tot / (float)a.H + a.eps);
   } else if (t.kind == KIND_ATTN) {
-    attn_lds_prep<HD, G>(a, L, wave, lane, layer, pos);
+    attn_lds_prep<HD, G, KV8>(a, L, wave, lane, layer, pos, t.nrows);
   } else if ((t.kind == KIND_O && a.combine_in_o) || t.kind == KIND_COMBINE) {
     // all heads' splits (o_proj prologue) or one head's (combine tile): one copy of the merge
     merge_heads<HD, Q8>(L.part, t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane, L.vec, t.kind == KIND_O);
@@ -1654,7 +1886,7 @@ __device__ __forceinline__ void put_scales(const Lds& L, const TileDesc& t, int 
   }
 }
 
-template <int HD, int G, bool WD, bool Q8, bool SMP>
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1683,7 +1915,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
       float sreg[SCALE_REGS];
-      if (gather_inputs<HD, G, true, WD, Q8, SMP>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true, WD, Q8, SMP, KV8>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1695,7 +1927,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
       }
       if (a.trace) t_pro = wall_clock64();
-      const float rs = lds_prologue<HD, G, Q8>(a, L, 0, lane, t, layer, pos);
+      const float rs = lds_prologue<HD, G, Q8, KV8>(a, L, 0, lane, t, layer, pos);
       if (needs_barrier_a(a, t)) __syncthreads();  // A: inputs ready
       const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
@@ -1774,7 +2006,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
         }
       } else if (t.kind == KIND_ATTN) {
-        cw_attn_kv_write<HD, G>(a, L, lane, layer, t.row0, t.nrows, t.aux0, L_att);
+        cw_attn_kv_write<HD, G, KV8>(a, L, lane, layer, t.row0, t.nrows, t.aux0, L_att);
         // The KV row must be complete before this worker publishes anything later readers of
         // the row depend on (its split partial, below); the wait overlaps the compute waves.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1862,12 +2094,12 @@ constexpr int stream_sets() {
   return 2;
 }
 
-template <int HD, int G, bool WD, bool Q8, bool SMP>
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
   constexpr int NB = stream_sets<HD, G>();
-  constexpr int NP = NB * B / 2;  // (K, V) pairs of the attention ring
+  constexpr int NP = NB * B / 2;  // (K, V) register pairs of the attention ring
   const int c = wave - 1;
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1914,7 +2146,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const bool one_block = block_rows >= rows;
       const Range nr_first0 = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng0;
       const bool kv_first0 = one_block && next_attn;
-      KvOpen<NP> ko = kv_open<HD, NP>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
+      KvOpen<NP> ko = kv_open<HD, NP, KV8>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
       Range ng = ng0, r_first = r_first0, nr_first = nr_first0;
       int kv_first = kv_first0;
       pin(ng);
@@ -1942,7 +2174,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G, false, WD, Q8, SMP>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false, WD, Q8, SMP, KV8>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
@@ -1950,7 +2182,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         break;
       }
       if (needs_barrier_a(a, t)) {
-        lds_prologue<HD, G, Q8>(a, L, wave, lane, t, layer, pos);
+        lds_prologue<HD, G, Q8, KV8>(a, L, wave, lane, t, layer, pos);
         __syncthreads();  // A
       }
       stamp(ts, TS_AFTER_A, lane);
@@ -1966,7 +2198,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
             stream_range<B, NB, Q8>(
                 L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
-                [&](int h) { return select_src<B>(kv_next, kv_half_src<B>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
+                [&](int h) { return select_src<B>(kv_next, kv_half_src<B, NP>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
                 stage_w, r0 == 0 ? ts : nullptr);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
@@ -1977,7 +2209,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           if (r0 + block_rows < rows) __syncthreads();  // C
         }
       } else if (t.kind == KIND_ATTN) {
-        compute_attention<HD, G, B, NB>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&](int h) {
+        compute_attention<HD, G, B, NB, KV8>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&](int h) {
           load_gemv_batch<B>(st.v + h * B, a.packed, ng, h, lane);
         }, ts);
         st.k = ng.k;
@@ -1997,7 +2229,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
 
 // Q8: weight-only INT8 GEMV tiles (INT8 codes, per-row FP32 scales); else BF16 weights.
 // SMP: sampled decoding (top-k / top-p draw from every worker's candidates); else greedy.
-template <int HD, int G, bool WD, bool Q8, bool SMP>
+// KV8: INT8 KV cache (codes, per-position scales, smoothed keys); else BF16 rows.
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
 __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
@@ -2050,8 +2283,8 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   __syncthreads();
   if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
   const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G, WD, Q8, SMP>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G, WD, Q8, SMP>(a, L, bid, wave, lane, block_rows);
+  if (wave == 0) control_loop<HD, G, WD, Q8, SMP, KV8>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G, WD, Q8, SMP, KV8>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -2180,6 +2413,73 @@ __global__ void __launch_bounds__(256) pack_weights(const PackSeg* __restrict__ 
   }
 }
 
+// INT8 KV cache conversion of a BF16 cache prefix ("History and roadmap" (TileInfer.jl), "M8 so
+// far": INT8 KV cache with smoothed keys).  kv_sigma: the largest |K| of every (layer, KV head,
+// channel) over positions [0, length), 1 for a channel that is zero there; one block per KV head.
+__global__ void __launch_bounds__(256) kv_sigma(const uint16_t* __restrict__ k, int64_t cap, int64_t length, int hd,
+                                                float* __restrict__ sigma) {
+  __shared__ float red[256];
+  const int64_t head = blockIdx.x;
+  const int np = 256 / hd, c = threadIdx.x % hd, pl = threadIdx.x / hd;
+  float m = 0.f;
+  if (pl < np)
+    for (int64_t p = pl; p < length; p += np) m = fmaxf(m, fabsf(bf16_to_f32(k[(head * cap + p) * hd + c])));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  if (pl == 0) {
+    for (int j = 1; j < np; ++j) m = fmaxf(m, red[j * hd + c]);
+    sigma[head * hd + c] = m > 0.f ? m : 1.f;
+  }
+}
+
+// kv_quantize: every row (head, position < length) of a BF16 cache as symmetric INT8 codes and an
+// FP32 scale, divided by sigma first when given (keys); one wavefront per row, head_dim <= 128.  The
+// codes go to the interleaved INT8 cache (rows of 2 x head_dim bytes; per group of 8 dimensions the
+// K codes, then the V codes): `vpart` is 0 for K, 8 for V.
+__global__ void __launch_bounds__(256) kv_quantize(const uint16_t* __restrict__ src, int64_t cap, int64_t length,
+                                                   int hd, int64_t nheads, const float* __restrict__ sigma,
+                                                   int8_t* __restrict__ codes, int vpart, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = nheads * length;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < nrows; r += (int64_t)gridDim.x * 4) {
+    const int64_t head = r / length, p = r - head * length;
+    const int64_t row = head * cap + p;
+    float x[2] = {0.f, 0.f}, am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = lane + 64 * i;
+      if (c < hd) {
+        x[i] = bf16_to_f32(src[row * hd + c]);
+        if (sigma) x[i] = __fdiv_rn(x[i], sigma[head * hd + c]);
+        am = fmaxf(am, fabsf(x[i]));
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    const float sc = __fdiv_rn(am, 127.f);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = lane + 64 * i;
+      if (c < hd) codes[row * hd * 2 + (c >> 3) * 16 + vpart + (c & 7)] = (int8_t)(int)kv_code(x[i], sc);
+    }
+    if (lane == 0) scales[row] = sc;
+  }
+}
+
+hipError_t launch_kv_convert(const uint16_t* k, const uint16_t* v, int64_t cap, int64_t length, int hd, int64_t nheads,
+                             int8_t* codes, float* ks, float* vs, float* sigma, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_sigma, dim3((unsigned)nheads), dim3(256), 0, stream, k, cap, length, hd, sigma);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = nheads * length;
+  const int64_t blocks = (rows + 3) / 4;
+  const unsigned grid = (unsigned)(blocks < 1 ? 1 : blocks > 65536 ? 65536 : blocks);
+  hipLaunchKernelGGL(kv_quantize, dim3(grid), dim3(256), 0, stream, k, cap, length, hd, nheads, sigma, codes, 0, ks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_quantize, dim3(grid), dim3(256), 0, stream, v, cap, length, hd, nheads, nullptr, codes, 8, vs);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream) {
   const int grid = nseg < 4096 ? (nseg > 0 ? nseg : 1) : 4096;
   hipLaunchKernelGGL(pack_weights, dim3(grid), dim3(256), 0, stream, segs, nseg, dst);
@@ -2219,42 +2519,60 @@ hipError_t noalloc_scratch(int device, uint32_t** out) {
 #endif  // TILES_WORKER_UNIT
 
 #ifdef TILES_WORKER_UNIT
-// The worker for a head size and query heads per attention tile, for one weight format and token
-// selection (each worker unit instantiates one pair, so that the build compiles them in parallel).
-template <bool Q8, bool SMP>
+// The worker for a head size and query heads per attention tile, for one weight format, token
+// selection and KV format (each worker unit instantiates one combination, so that the build
+// compiles them in parallel).
+template <bool Q8, bool SMP, bool KV8>
 const void* worker_for(int head_dim, int group) {
   if (head_dim == 64) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, SMP>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, SMP>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false, Q8, SMP>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false, Q8, SMP>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, SMP, KV8>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, SMP, KV8>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<64, 3, false, Q8, SMP, KV8>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<64, 4, false, Q8, SMP, KV8>);
     }
   } else if (head_dim == 128) {
     switch (group) {
-      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, SMP>);
-      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, SMP>);
-      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false, Q8, SMP>);
-      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false, Q8, SMP>);
+      case 1: return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, SMP, KV8>);
+      case 2: return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, SMP, KV8>);
+      case 3: return reinterpret_cast<const void*>(&tiles_worker<128, 3, false, Q8, SMP, KV8>);
+      case 4: return reinterpret_cast<const void*>(&tiles_worker<128, 4, false, Q8, SMP, KV8>);
     }
   }
   return nullptr;
 }
 #else
-// (defined by the worker units)
-const void* worker_bf16_greedy(int head_dim, int group);
-const void* worker_bf16_sampled(int head_dim, int group);
-const void* worker_int8_greedy(int head_dim, int group);
-const void* worker_int8_sampled(int head_dim, int group);
+// (defined by the worker units; variant: INT8 weights * 4 + sampled * 2 + INT8 KV)
+const void* worker_unit_0(int head_dim, int group);
+const void* worker_unit_1(int head_dim, int group);
+const void* worker_unit_2(int head_dim, int group);
+const void* worker_unit_3(int head_dim, int group);
+const void* worker_unit_4(int head_dim, int group);
+const void* worker_unit_5(int head_dim, int group);
+const void* worker_unit_6(int head_dim, int group);
+const void* worker_unit_7(int head_dim, int group);
 const void* worker_watchdog(int head_dim);
 
-// The worker for a head size, query heads per attention tile, weight format and token selection;
-// `short_watchdog` selects the test instantiation whose waits check their watchdog every polling
-// round (BF16, greedy, one query head per tile only).
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled) {
-  if (short_watchdog) return group == 1 && !q8 && !sampled ? worker_watchdog(head_dim) : nullptr;
-  if (sampled) return q8 ? worker_int8_sampled(head_dim, group) : worker_bf16_sampled(head_dim, group);
-  return q8 ? worker_int8_greedy(head_dim, group) : worker_bf16_greedy(head_dim, group);
+const void* worker_unit(int variant, int head_dim, int group) {
+  switch (variant) {
+    case 0: return worker_unit_0(head_dim, group);
+    case 1: return worker_unit_1(head_dim, group);
+    case 2: return worker_unit_2(head_dim, group);
+    case 3: return worker_unit_3(head_dim, group);
+    case 4: return worker_unit_4(head_dim, group);
+    case 5: return worker_unit_5(head_dim, group);
+    case 6: return worker_unit_6(head_dim, group);
+    case 7: return worker_unit_7(head_dim, group);
+  }
+  return nullptr;
+}
+
+// The worker for a head size, query heads per attention tile, weight format, token selection and
+// KV format; `short_watchdog` selects the test instantiation whose waits check their watchdog every
+// polling round (BF16 weights and KV, greedy, one query head per tile only).
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8) {
+  if (short_watchdog) return group == 1 && !q8 && !sampled && !kv8 ? worker_watchdog(head_dim) : nullptr;
+  return worker_unit((q8 ? 4 : 0) + (sampled ? 2 : 0) + (kv8 ? 1 : 0), head_dim, group);
 }
 #endif
 

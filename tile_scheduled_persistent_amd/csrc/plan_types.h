@@ -55,7 +55,13 @@ constexpr int MAX_STAGE_BATCHES = 2;
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;  // polling rounds before a wait gives up (watchdog)
 constexpr int32_t MAX_POSITIONS = 1 << 23;
 // Sampled decoding (top-k / top-p): each worker publishes its top_k largest logits, at most this many.
-constexpr int32_t MAX_TOP_K = 32;  // KV capacity limit: positions and per-head row offsets stay 32-bit
+constexpr int32_t MAX_TOP_K = 32;
+// KV cache formats: BF16 rows, or INT8 codes with one FP32 scale per (layer, KV head, position) and
+// keys smoothed by a per-(layer, KV head, channel) factor.
+enum : int32_t { KVFMT_BF16 = 0, KVFMT_INT8 = 1 };
+// INT8 KV: an attention tile stages its split's per-position K and V scales in LDS; at most this many
+// positions per split (the planner raises the split count, or rejects the plan).
+constexpr int32_t MAX_SPLIT_POSITIONS_KV8 = 2048;  // KV capacity limit: positions and per-head row offsets stay 32-bit
 
 struct TileDesc {   // 32 bytes
   int32_t kind;
@@ -140,8 +146,11 @@ struct KernelArgs {
                              // maximum (greedy) or its top_k logits in decreasing order (sampled)
   uint32_t* sync;            // SYNC_WORDS status / abort words
   const uint64_t* table_check;  // [W + 1]: per-worker hash of the schedule it loads, then the build id
-  uint16_t* kv_k;            // BF16 cache
+  uint16_t* kv_k;            // BF16 cache, or (INT8 KV) INT8 codes [layer][kv head][capacity][head_dim]
   uint16_t* kv_v;
+  float* kv_ks;              // INT8 KV: K and V scales [layer][kv head][capacity], smoothing factors
+  float* kv_vs;              //   [layer][kv head][head_dim]
+  const float* kv_sigma;
   int64_t kv_cap;
   int32_t* out_tokens;
   float* out_logits;         // may be null

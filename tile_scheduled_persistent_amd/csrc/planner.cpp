@@ -126,7 +126,8 @@ uint64_t plan_checksum(const HostPlan& p) {
                           s.qk_norm ? 1 : 0, s.tied ? 1 : 0, s.max_positions, p.W, p.S, p.combine_in_o, p.T, p.q8, p.wb,
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
-                          p.stage_batches, p.top_k, (int64_t)float_bits(p.temperature), (int64_t)float_bits(p.top_p)};
+                          p.stage_batches, p.top_k, (int64_t)float_bits(p.temperature), (int64_t)float_bits(p.top_p),
+                          p.kv8};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -195,6 +196,9 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
     return fail(err, TILES_E_CONFIG, "sampling needs 0 < temperature (finite) and 0 < top_p <= 1");
   if (cfg.top_k > 0 && n_workers > 256)
     return fail(err, TILES_E_CONFIG, "sampled decoding supports at most 256 workers (the token draw merges 4 lists per lane)");
+  if (cfg.kv_format != KVFMT_BF16 && cfg.kv_format != KVFMT_INT8)
+    return fail(err, TILES_E_CONFIG, "kv_format must be 0 (BF16) or 1 (INT8)");
+  p.kv8 = cfg.kv_format == KVFMT_INT8;
   p.top_k = cfg.top_k;
   p.temperature = cfg.top_k > 0 ? cfg.temperature : 1.0f;
   p.top_p = cfg.top_k > 0 ? cfg.top_p : 1.0f;
@@ -206,6 +210,11 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
 
   // split-KV and combine placement
   p.S = cfg.kv_splits > 0 ? cfg.kv_splits : choose_splits(s, W);
+  // INT8 KV: a split's per-position scales are staged in LDS, at most MAX_SPLIT_POSITIONS_KV8 of them
+  if (p.kv8 && cfg.kv_splits <= 0)
+    p.S = std::max<int32_t>(p.S, (int32_t)((s.max_positions + MAX_SPLIT_POSITIONS_KV8 - 1) / MAX_SPLIT_POSITIONS_KV8));
+  if (p.kv8 && (s.max_positions + p.S - 1) / p.S > MAX_SPLIT_POSITIONS_KV8)
+    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 2048 positions per split (raise kv_splits)");
   // query heads per attention tile: the group's heads spread over as many tiles as the workers
   // allow (each re-reads the split's K/V rows; attention is bound by arithmetic per head)
   if (cfg.attn_heads > 0) {
@@ -477,7 +486,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
   // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
   const int32_t ps = s.hd + 4;
-  part = std::max(part, p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * ps);
+  part = std::max(part, p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * ps + (p.kv8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0));
   part = std::max(part, p.S * ps);                                  // one head's splits (combine tile)
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
@@ -903,6 +912,12 @@ int validate_plan(const HostPlan& p, std::string& err) {
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
   if ((int64_t)p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
   if (p.lds_xres_floats < s.Hpad) return fail(err, TILES_E_PLAN, "LDS residual area too small");
+  if (p.kv8) {
+    const int64_t np = (s.max_positions + p.S - 1) / p.S;
+    if (np > MAX_SPLIT_POSITIONS_KV8) return fail(err, TILES_E_PLAN, "INT8 KV: a split longer than 2048 positions");
+    if (p.lds_part_floats < p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * (s.hd + 4) + 2 * MAX_SPLIT_POSITIONS_KV8)
+      return fail(err, TILES_E_PLAN, "LDS too small for an INT8 KV split's scales");
+  }
   if (p.top_k < 0 || p.top_k > MAX_TOP_K || p.top_k > s.V || (p.top_k > 0 && p.W > 256))
     return fail(err, TILES_E_PLAN, "top_k out of range (1..32, <= vocab, at most 256 workers)");
   if (p.top_k > 0 && (int64_t)p.lds_vec_floats + p.lds_part_floats < ((int64_t)p.W * p.top_k + 1) / 2 * 4)

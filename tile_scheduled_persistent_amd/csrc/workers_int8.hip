@@ -1,10 +1,12 @@
-// Instantiations of the persistent tile worker for weight-only INT8 weights, greedy token selection: one translation unit per weight
-// format and token selection, so that the build compiles them in parallel.
+// Instantiations of the persistent tile worker for weight-only INT8 weights, greedy token selection, BF16 KV cache: one translation unit
+// per combination, so that the build compiles them in parallel.
 #define TILES_WORKER_UNIT
 #include "kernel.hip"
 
 namespace tiles {
 
-const void* worker_int8_greedy(int head_dim, int group) { return worker_for<true, false>(head_dim, group); }
+const void* worker_unit_4(int head_dim, int group) {
+  return worker_for<true, false, false>(head_dim, group);
+}
 
 }  // namespace tiles

@@ -1,0 +1,12 @@
+// Instantiations of the persistent tile worker for weight-only INT8 weights, sampled token selection, INT8 KV cache: one translation unit
+// per combination, so that the build compiles them in parallel.
+#define TILES_WORKER_UNIT
+#include "kernel.hip"
+
+namespace tiles {
+
+const void* worker_unit_7(int head_dim, int group) {
+  return worker_for<true, true, true>(head_dim, group);
+}
+
+}  // namespace tiles

@@ -52,6 +52,7 @@ class Config(ctypes.Structure):
         ("attn_heads", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
         ("o_placement", ctypes.c_int32), ("weight_format", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -67,7 +68,8 @@ class Weights(ctypes.Structure):
 
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64),
-                ("length", ctypes.c_int64)]
+                ("length", ctypes.c_int64), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_smooth", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -78,6 +80,7 @@ class PlanInfo(ctypes.Structure):
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
         ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -104,6 +107,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_decode_noalloc.restype = ctypes.c_int
         L.tiles_decode_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_kv_convert_int8.restype = ctypes.c_int
+        L.tiles_kv_convert_int8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.POINTER(KV)]
         L.tiles_decode_sampled.restype = ctypes.c_int
         L.tiles_decode_sampled.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -155,17 +161,19 @@ def _check(rc: int):
 
 
 WEIGHTS = {"bf16": 0, "int8": 1}
+KV_FORMATS = {"bf16": 0, "int8": 1}
 
 
 def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
                 n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0,
-                weights: str = "bf16", sampling: Optional[tuple] = None) -> Config:
-    """``sampling`` = (temperature, top_k, top_p) makes a sampling plan (tiles_decode_sampled)."""
+                weights: str = "bf16", sampling: Optional[tuple] = None, kv: str = "bf16") -> Config:
+    """``sampling`` = (temperature, top_k, top_p) makes a sampling plan (tiles_decode_sampled);
+    ``kv`` = "int8" an INT8 KV plan (see KVCache.int8)."""
     temperature, top_k, top_p = sampling if sampling is not None else (1.0, 0, 1.0)
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
                   float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
                   int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement),
-                  WEIGHTS[weights], int(top_k), float(temperature), float(top_p))
+                  WEIGHTS[weights], int(top_k), float(temperature), float(top_p), KV_FORMATS[kv])
 
 
 def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
@@ -223,14 +231,48 @@ def edge_latency(words: torch.Tensor, peer: int, iters: int, out: torch.Tensor, 
 
 @dataclass
 class KVCache:
-    """Caller-owned BF16 cache [n_layers, n_kv_heads, capacity, head_dim] (device)."""
+    """Caller-owned cache (device): BF16 k, v [n_layers, n_kv_heads, capacity, head_dim]; or, for an
+    INT8 KV plan, k the interleaved int8 codes [n_layers, n_kv_heads, capacity, 2 * head_dim] (v None),
+    k_scale, v_scale float32 [n_layers, n_kv_heads, capacity] and k_smooth float32 [n_layers,
+    n_kv_heads, head_dim] (see tiles_kv_convert_int8 in include/tiles.h)."""
     k: torch.Tensor
-    v: torch.Tensor
+    v: Optional[torch.Tensor]
     length: int = 0
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+    k_smooth: Optional[torch.Tensor] = None
 
     @property
     def capacity(self) -> int:
         return self.k.shape[2]
+
+    @property
+    def int8(self) -> bool:
+        return self.k.dtype == torch.int8
+
+    def struct(self) -> "KV":
+        return KV(_ptr(self.k), _ptr(self.v), self.capacity, self.length, _ptr(self.k_scale), _ptr(self.v_scale),
+                  _ptr(self.k_smooth))
+
+    def clone(self) -> "KVCache":
+        c = lambda t: None if t is None else t.clone()
+        return KVCache(c(self.k), c(self.v), self.length, c(self.k_scale), c(self.v_scale), c(self.k_smooth))
+
+    @staticmethod
+    def convert_int8(plan: "Plan", k_bf16: torch.Tensor, v_bf16: torch.Tensor, length: int) -> "KVCache":
+        """The INT8 cache of an INT8 KV plan from the first ``length`` positions of a BF16 cache
+        (tiles_kv_convert_int8, on the plan's stream; smoothing factors from those positions)."""
+        L, H, cap, hd = k_bf16.shape
+        dev = k_bf16.device
+        out = KVCache(torch.zeros((L, H, cap, 2 * hd), dtype=torch.int8, device=dev), None, 0,
+                      torch.zeros((L, H, cap), dtype=torch.float32, device=dev),
+                      torch.zeros((L, H, cap), dtype=torch.float32, device=dev),
+                      torch.zeros((L, H, hd), dtype=torch.float32, device=dev))
+        c = out.struct()
+        _check(lib().tiles_kv_convert_int8(plan._h, _ptr(k_bf16.contiguous()), _ptr(v_bf16.contiguous()), cap, length,
+                                           ctypes.byref(c)))
+        out.length = c.length
+        return out
 
 
 class Plan:
@@ -238,12 +280,14 @@ class Plan:
 
     def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
                  combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0,
-                 o_placement: int = 0, weight_format: str = "bf16", sampling: Optional[tuple] = None):
+                 o_placement: int = 0, weight_format: str = "bf16", sampling: Optional[tuple] = None,
+                 kv_format: str = "bf16"):
         self.model = m
         self.sampling = sampling
+        self.kv_format = kv_format
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream,
-                                attn_heads, o_placement, weight_format, sampling)
+                                attn_heads, o_placement, weight_format, sampling, kv_format)
         on_device = weights["embed"].is_cuda
         layers = (LayerWeights * m.n_layers)()
         for i, d in enumerate(weights["layers"]):
@@ -295,10 +339,15 @@ class Plan:
         if out_logits is not None and (out_logits.dtype != torch.float32 or not out_logits.is_cuda
                                        or out_logits.numel() < n_steps * self.model.vocab):
             raise ValueError("out_logits must be a device float32 tensor [n_steps, vocab]")
-        for t in (kv.k, kv.v):
-            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("KV tensors must be contiguous device bf16")
-        c = KV(_ptr(kv.k), _ptr(kv.v), kv.capacity, kv.length)
+        if kv.int8:
+            for t in (kv.k, kv.k_scale, kv.v_scale, kv.k_smooth):
+                if t is None or not t.is_cuda or not t.is_contiguous():
+                    raise ValueError("INT8 KV tensors must be contiguous device tensors")
+        else:
+            for t in (kv.k, kv.v):
+                if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                    raise ValueError("KV tensors must be contiguous device bf16")
+        c = kv.struct()
         if uniforms is not None or self.sampling is not None:
             rc = lib().tiles_decode_sampled(self._h, ctypes.byref(c), int(token), int(n_steps), _ptr(uniforms),
                                             _ptr(out_tokens), _ptr(out_logits))
