@@ -9,12 +9,17 @@ bit-identical results across repeated GPU runs.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
 from oracle import OracleModel, convert_kv_int8, dequantize_kv_rows
 from tile_scheduled_persistent_amd import synth, tiles
 
+# plan flags added to every plan the parity tests create (e.g. TILES_TEST_EXTRA_FLAGS=0x8 runs the
+# suite with the attention scores on the matrix cores)
+EXTRA_FLAGS = int(os.environ.get("TILES_TEST_EXTRA_FLAGS", "0"), 0)
 HIDDEN_REL_L2 = 1e-2
 LOGIT_MAX_ABS = 5e-2
 MARGIN = 0.1
@@ -71,6 +76,7 @@ class Setup:
         return {"k": self.kv_bits["k"].copy(), "v": self.kv_bits["v"].copy()}
 
     def plan(self, flags=tiles.TILES_DEBUG_HIDDEN, **kw) -> tiles.Plan:
+        flags |= EXTRA_FLAGS
         kw.setdefault("kv_format", self.kv)
         return tiles.Plan(self.m, self.w_dev, self.capacity, flags=flags, weight_format=self.weights, **kw)
 
