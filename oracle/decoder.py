@@ -66,6 +66,13 @@ K1  INT8 KV cache with smoothed keys ("History and roadmap" (TileInfer.jl), "M8 
 K2  sigma_c is the largest |K| of channel c over the positions cached when a BF16 cache is
     converted (1 for a channel that is zero there); positions decoded later keep those factors.
     Conversion: the BF16 values widened, divided by sigma, quantized per row.
+V1  Greedy verify steps ("History and roadmap" (TileInfer.jl), "M8 so far" table: verify steps of
+    up to 16 tokens on the split-KV decode kernels; "Milestones" M7: exact verification for greedy
+    decoding).  A verify step of m tokens is m decode steps in which every position consumes the
+    given token (the last accepted one, then the drafts); a draft is accepted while it equals the
+    argmax after the position before it, and the step yields the accepted drafts followed by the
+    argmax after the last of them.  The pages give no acceptance rule beyond "exact": this is the
+    rule under which the accepted output equals what greedy decoding would have produced.
 """
 
 from __future__ import annotations
@@ -420,6 +427,27 @@ class OracleModel:
                     "v": dequantize_kv_rows(kv["vq"], kv["vs"], None, self.dtype)}
         return {"k": bf16_bits_to_float(kv["k"], self.dtype).copy(),
                 "v": bf16_bits_to_float(kv["v"], self.dtype).copy()}
+
+    def verify(self, kv: dict, tokens: Sequence[int], pos0: int, widen_kv_once: bool = False):
+        """V1: a greedy verify step of m = len(tokens) tokens [t_0, d_1, .., d_{m-1}]: the last
+        accepted token at ``pos0`` and m - 1 draft tokens at the following positions.  Every
+        position consumes its given token (teacher forcing), so a_i, the argmax after position
+        pos0 + i, is the greedy token that follows t_0, d_1 .. d_i.  Draft d_{i+1} is accepted while
+        a_i == d_{i+1}; the accepted count n is the length of that prefix, and the step yields
+        d_1 .. d_n followed by a_n (the correction, or after n = m - 1 the bonus token).  The cache
+        receives the rows of all m positions (those after pos0 + n are overwritten by later steps).
+        Returns a dict with ``argmax`` [m], ``accepted`` n, ``tokens`` [n + 1] and ``logits`` [m, V].
+        """
+        tokens = [int(t) for t in tokens]
+        m = len(tokens)
+        res = self.decode(kv, tokens[0], pos0, m, teacher=tokens[1:], keep_hidden=False,
+                          widen_kv_once=widen_kv_once)
+        a = res["tokens"]
+        n = 0
+        while n < m - 1 and int(a[n]) == tokens[n + 1]:
+            n += 1
+        out = np.array(tokens[1:n + 1] + [int(a[n])], dtype=np.int64)
+        return {"argmax": a, "accepted": n, "tokens": out, "logits": res["logits"]}
 
     def decode(self, kv: dict, token: int, pos0: int, n_steps: int,
                teacher: Optional[Sequence[int]] = None, keep_hidden: bool = True,

@@ -8,7 +8,7 @@ GQA map, attention scale and causal range, RMSNorm form, BF16 rounding, SwiGLU b
 residual source), the plumbing of the step (which layer's weights and which gain
 each stage reads, q/k norm before RoPE, the argmax tie rule), the INT8 weight codes, the INT8
 KV cache (smoothing, scales, codes, dequantization) and the sampling draw (tie order, temperature, top-k and top-p supports, the draw's scale and
-strictness, the per-step uniform).
+strictness, the per-step uniform) and the verify step's acceptance rule.
 """
 
 import importlib.util
@@ -25,6 +25,10 @@ PINS = os.path.join(HERE, "test_oracle_pins.py")
 
 # (name, text in decoder.py, replacement, replace every occurrence)
 MUTATIONS = [
+    ("verify compares the wrong draft", "int(a[n]) == tokens[n + 1]", "int(a[n]) == tokens[n]", False),
+    ("verify yields the argmax after the next position", "[int(a[n])]", "[int(a[min(n + 1, m - 1)])]", False),
+    ("verify without the correction token", "out = np.array(tokens[1:n + 1] + [int(a[n])], dtype=np.int64)",
+     "out = np.array(tokens[1:n + 1], dtype=np.int64)", False),
     ("interleaved RoPE pairs", "a = u[..., :half]\n    b = u[..., half:]", "a = u[..., 0::2]\n    b = u[..., 1::2]", False),
     ("RoPE rotation sign", "a * cos - b * sin, b * cos + a * sin", "a * cos + b * sin, b * cos - a * sin", False),
     ("RoPE frequency exponent", "float(theta) ** (-2.0 * i / hd)", "float(theta) ** (-1.0 * i / hd)", False),

@@ -443,6 +443,53 @@ def test_decode_teacher_forced_on_own_tokens_equals_free_running():
     assert np.array_equal(free["logits"], forced["logits"])
 
 
+def _verify_model(c, seed):
+    rng = np.random.default_rng(seed)
+    w = _zero_model(c, rng)
+    for d in w["layers"]:
+        for k in ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]:
+            d[k] = _b(rng.standard_normal(bf16_bits_to_float(d[k]).shape) * 0.3)
+    w["embed"] = _b(rng.standard_normal((c.vocab, 8)))
+    return OracleModel(c, w, np.float32)
+
+
+def test_verify_accepts_the_greedy_continuation_whole():
+    """V1: drafts equal to free-running greedy decoding are all accepted, and the step yields that
+    continuation one token further (the bonus token), with the greedy tokens as its argmaxes."""
+    c = Cfg(vocab=32)
+    m = _verify_model(c, 21)
+    free = m.decode(_kv(c, 12), 7, 0, 9)
+    g = [int(t) for t in free["tokens"]]
+    r = m.verify(_kv(c, 12), [7] + g[:7], 0)
+    assert r["accepted"] == 7
+    assert list(r["tokens"]) == g[:8]
+    assert list(r["argmax"]) == g[:8]
+
+
+def test_verify_stops_at_the_first_wrong_draft():
+    """V1: a wrong draft at position j (1-based) ends acceptance at j - 1 drafts and the step yields
+    the greedy token there instead; drafts after it do not matter."""
+    c = Cfg(vocab=32)
+    m = _verify_model(c, 22)
+    g = [int(t) for t in m.decode(_kv(c, 12), 3, 0, 8)["tokens"]]
+    for j in (1, 3, 6):
+        drafts = list(g[:7])
+        drafts[j - 1] = (g[j - 1] + 5) % 32
+        for k in range(j, 7):  # later drafts: anything, even the greedy ones
+            drafts[k] = (g[k] + 11) % 32 if k % 2 else g[k]
+        r = m.verify(_kv(c, 12), [3] + drafts, 0)
+        assert r["accepted"] == j - 1, j
+        assert list(r["tokens"]) == g[:j], j
+
+
+def test_verify_of_one_token_is_one_greedy_step():
+    c = Cfg(vocab=32)
+    m = _verify_model(c, 23)
+    g = int(m.decode(_kv(c, 12), 5, 2, 1)["tokens"][0])
+    r = m.verify(_kv(c, 12), [5], 2)
+    assert r["accepted"] == 0 and list(r["tokens"]) == [g] and list(r["argmax"]) == [g]
+
+
 def test_fp32_oracle_close_to_fp64_on_tiny_synthetic_model():
     from tile_scheduled_persistent_amd import synth
     from tile_scheduled_persistent_amd.configs import TINY
