@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
+    ap.add_argument("--verify-tokens", type=int, default=0,
+                    help="also time greedy verify steps of this many tokens (added to the line as 'verify')")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")
@@ -273,6 +275,9 @@ def main():
         "edge_floor": edge,
     }
 
+    if args.verify_tokens > 0:
+        result["verify"] = _verify_timing(plan, kv, wl, token, out_t, args, stream)
+
     if args.trace_report:
         _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info)
 
@@ -285,6 +290,52 @@ def main():
         result["cpu_baseline"] = None
     plan.close()
     print(json.dumps(result), flush=True)
+
+
+def _verify_timing(plan, kv, wl, token, out_t, args, stream):
+    """Greedy verify steps of M tokens (tiles_verify) from the same cached prefix: the drafts are the
+    workload's own greedy continuation (all accepted), each launch timed with HIP events on the
+    plan's stream (the draft copy into the plan's buffer included)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from tile_scheduled_persistent_amd import tiles
+
+    M = min(args.verify_tokens, wl.n_steps)
+    toks = [int(token)] + [int(t) for t in out_t[:M - 1].cpu().tolist()]
+    buf = (ctypes.c_int32 * M)(*toks)
+    out_a = torch.zeros(M, dtype=torch.int32, device="cuda")
+    L = tiles.lib()
+
+    def launch():
+        kv.length = wl.n_cached
+        c = kv.struct()
+        rc = L.tiles_verify(plan._h, ctypes.byref(c), buf, M, ctypes.c_void_p(out_a.data_ptr()), None)
+        if rc != tiles.TILES_OK:
+            raise RuntimeError(tiles.last_error())
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s0, e0 in ev:
+        s0.record(stream)
+        launch()
+        e0.record(stream)
+    torch.cuda.synchronize()
+    if plan.status() != tiles.TILES_OK:
+        raise RuntimeError(tiles.last_error())
+    ms = float(np.median([s0.elapsed_time(e0) for s0, e0 in ev]))
+    a = out_a.cpu().numpy()
+    accepted = 0
+    while accepted < M - 1 and int(a[accepted]) == toks[accepted + 1]:
+        accepted += 1
+    return {"tokens_per_step": M, "accepted": accepted, "ms_per_step": round(ms, 4),
+            "positions_per_s": round(M / (ms * 1e-3), 1),
+            "how": "tiles_verify launches (m positions each, one weight stream per position), median of "
+                   f"{args.steps}, HIP events on the plan's stream"}
 
 
 def _trace_report(path, m, wl, w, k0, v0, token, args, info):

@@ -228,6 +228,24 @@ int tiles_decode(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_st
 int tiles_decode_sampled(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int32_t n_steps, const float *uniforms,
                          int32_t *out_tokens, float *out_logits);
 
+/* Greedy verify step ("History and roadmap" (TileInfer.jl), "M8 so far" table: verify steps of up
+ * to 16 tokens on the split-KV decode kernels; "Milestones" M7: exact verification for greedy
+ * decoding): m positions in one cooperative launch, position i (at kv->length + i) consuming the given
+ * token tokens[i] -- the last accepted token, then m - 1 drafts -- and storing its argmax in
+ * out_argmax[i] (lowest index on ties).  Draft tokens[i + 1] is accepted while out_argmax[i] equals it;
+ * with n accepted, the verified output is tokens[1 .. n] followed by out_argmax[n], and the caller
+ * sets the cache length to (length before the call) + n + 1 (rows written past it are overwritten
+ * by later steps).  The m positions run as m steps of the decode launch (each streams the weights
+ * once; the tiles do not take several tokens at a time).
+ *   tokens     : host int32 [m], each 0 <= t < vocab; read during the call.
+ *   m          : 1 .. 64.
+ *   out_argmax : device int32 [m].   out_logits : device float [m][vocab], or NULL.
+ * kv as tiles_decode (kv->length is advanced by m).  Errors as tiles_decode, plus TILES_E_ARG for a
+ * sampling plan, null tokens or a token out of range.  Copies tokens[1 ..] into a buffer the plan
+ * owns, on the plan's stream; allocates nothing. */
+int tiles_verify(tiles_plan_t *plan, tiles_kv_t *kv, const int32_t *tokens, int32_t m, int32_t *out_argmax,
+                 float *out_logits);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): tiles_decode with the same arguments, semantics and results,
  * except that the launch's tagged-data buffers, LM-head partials and status words live in a

@@ -37,6 +37,7 @@ def test_null_arguments_are_rejected_without_a_gpu():
     assert L.tiles_decode(None, None, 0, 1, None, None) == tiles.TILES_E_ARG
     assert L.tiles_decode_noalloc(None, None, 0, 1, None, None) == tiles.TILES_E_ARG
     assert L.tiles_decode_sampled(None, None, 0, 1, None, None, None) == tiles.TILES_E_ARG
+    assert L.tiles_verify(None, None, None, 1, None, None) == tiles.TILES_E_ARG
     assert "null" in tiles.last_error()
     assert L.tiles_plan_create(None, None) is None
     L.tiles_plan_destroy(None)  # NULL-safe

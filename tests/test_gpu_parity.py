@@ -13,7 +13,7 @@ from tile_scheduled_persistent_amd.configs import TINY, WORKLOADS, scaled
 
 from parity_util import (HIDDEN_REL_L2, Setup, check_step, compare_free_running, compare_sampled_teacher_forced,
                          compare_teacher_forced, kv8_rows_close, kv_rows_close, run_gpu, run_gpu_sampled,
-                         split_int8_cache, top2_margin)
+                         split_int8_cache, top2_margin, MARGIN)
 
 pytestmark = pytest.mark.gpu
 
@@ -772,3 +772,109 @@ def test_full_size_kv8_every_step(key):
           f"{stats['logit_abs_max']:.2e}, tokens checked at margin > 0.1: {stats['tokens_checked']}; written rows "
           f"(dequantized rel L2, codes differing, scale rel) K {rows['K'][0]:.2e} {rows['K'][1]:.3%} {rows['K'][2]:.1e}, "
           f"V {rows['V'][0]:.2e} {rows['V'][1]:.3%} {rows['V'][2]:.1e}", flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# greedy verify steps (tiles_verify)
+# ---------------------------------------------------------------------------------------------
+
+def _greedy_continuation(s, plan, tok, n):
+    """The GPU's own free-running greedy tokens, logits and cache after n steps from a fresh cache."""
+    kv = s.fresh_kv(plan)
+    g_t, g_l, _ = run_gpu(plan, kv, tok, n, want_hidden=False)
+    return kv, [int(t) for t in g_t], g_l
+
+
+@pytest.mark.parametrize("kvfmt", ["bf16", "int8"])
+def test_verify_of_the_greedy_continuation_is_the_greedy_launch_bit_for_bit(kvfmt):
+    """Drafts equal to the launch's own greedy tokens: every draft accepted, the argmaxes, logits and
+    written cache bytes identical to the free-running launch (each position consumes the same token),
+    and the verified output is that continuation one token further."""
+    s = Setup(WIDE, 96, 60, kv=kvfmt)
+    tok = synth.make_tokens(WIDE, 1)[0]
+    m = 12
+    with s.plan() as plan:
+        kv_g, g, g_l = _greedy_continuation(s, plan, tok, m)
+        kv = s.fresh_kv(plan)
+        out_l = torch.zeros((m, WIDE.vocab), dtype=torch.float32, device="cuda")
+        a, n, out = plan.verify(kv, [tok] + g[:m - 1], out_logits=out_l)
+    assert n == m - 1 and list(a) == g and list(out) == g
+    assert np.array_equal(out_l.cpu().numpy(), g_l)
+    assert torch.equal(kv.k, kv_g.k) and (kv.v is None or torch.equal(kv.v, kv_g.v))
+    if kv.int8:
+        assert torch.equal(kv.k_scale, kv_g.k_scale) and torch.equal(kv.v_scale, kv_g.v_scale)
+    assert kv.length == 60 + m
+
+
+def test_verify_wrong_drafts_against_the_oracle():
+    """A wrong draft at position j: the GPU accepts j - 1 drafts and yields the greedy token there, as
+    the oracle's verify does; every position's logits and hidden states against the oracle
+    teacher-forced on the same tokens."""
+    s = Setup(WIDE, 96, 60)
+    tok = synth.make_tokens(WIDE, 1)[0]
+    m = 10
+    with s.plan() as plan:
+        _, g, _ = _greedy_continuation(s, plan, tok, m)
+        for j in (1, 4, 9):
+            drafts = list(g[:m - 1])
+            drafts[j - 1] = (g[j - 1] + 7) % WIDE.vocab
+            tokens = [tok] + drafts
+            kv = s.fresh_kv(plan)
+            out_l = torch.zeros((m, WIDE.vocab), dtype=torch.float32, device="cuda")
+            a, n, out = plan.verify(kv, tokens, out_logits=out_l)
+            hid = plan.read_debug(hidden=True)[0]
+            o = s.oracle()
+            o_dec = o.decode(s.oracle_kv(), tokens[0], 60, m, teacher=tokens[1:])
+            compare_teacher_forced(f"verify j={j}", a, out_l.cpu().numpy(), hid, o_dec)
+            o_ver = o.verify(s.oracle_kv(), tokens, 60)
+            margins = [top2_margin(o_dec["logits"][i]) for i in range(m)]
+            if min(margins[:j]) > MARGIN:  # every decision up to the wrong draft is clear
+                assert n == o_ver["accepted"] == j - 1, (j, n, o_ver["accepted"])
+                assert list(out) == list(o_ver["tokens"]) == g[:j]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_full_size_verify_sixteen_tokens():
+    """A 16-token verify step on the Llama-3.2-1B shape at 1023 cached positions, drafts the GPU's own
+    greedy continuation with a wrong token at position 10: nine accepted, and all 16 positions against
+    the oracle teacher-forced on the same tokens."""
+    wl = WORKLOADS["llama1b"]
+    mdl = wl.model
+    s = Setup(mdl, wl.capacity, wl.n_cached, gen_device="cuda")
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 16
+    with s.plan(flags=0) as plan:
+        _, g, _ = _greedy_continuation(s, plan, tok, m)
+        drafts = list(g[:m - 1])
+        drafts[9] = (g[9] + 1) % mdl.vocab
+        tokens = [tok] + drafts
+        kv = s.fresh_kv(plan)
+        out_l = torch.zeros((m, mdl.vocab), dtype=torch.float32, device="cuda")
+        a, n, out = plan.verify(kv, tokens, out_logits=out_l)
+    assert n == 9 and list(out) == g[:10]
+    o_dec = s.oracle().decode(s.oracle_kv(), tokens[0], wl.n_cached, m, teacher=tokens[1:], keep_hidden=True,
+                              widen_kv_once=True)
+    stats = compare_teacher_forced("llama1b verify", a, out_l.cpu().numpy(), None, o_dec)
+    print(f"llama1b verify: {m} positions compared, accepted {n}; max logit abs err {stats['logit_abs_max']:.2e}",
+          flush=True)
+
+
+def test_verify_entry_point_errors():
+    s = Setup(TINY, 40, 10)
+    with s.plan() as plan:
+        kv = s.fresh_kv(plan)
+        L = tiles.lib()
+        c = kv.struct()
+        out = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for toks, m in (([1, 2], 0), ([1] * 65, 65), ([1, TINY.vocab], 2), ([-1], 1)):
+            buf = (ctypes.c_int32 * len(toks))(*toks)
+            assert L.tiles_verify(plan._h, ctypes.byref(c), buf, m, ctypes.c_void_p(out.data_ptr()), None) == tiles.TILES_E_ARG
+        assert L.tiles_verify(plan._h, ctypes.byref(c), None, 1, ctypes.c_void_p(out.data_ptr()), None) == tiles.TILES_E_ARG
+    s = Setup(TINY, 40, 10)
+    with s.plan(sampling=(1.0, 4, 1.0)) as plan:
+        kv = s.fresh_kv(plan)
+        c = kv.struct()
+        buf = (ctypes.c_int32 * 1)(1)
+        assert tiles.lib().tiles_verify(plan._h, ctypes.byref(c), buf, 1, ctypes.c_void_p(out.data_ptr()), None) == tiles.TILES_E_ARG
+        assert "greedy" in tiles.last_error()

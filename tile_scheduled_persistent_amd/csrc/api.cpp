@@ -91,6 +91,7 @@ struct tiles_plan {
   int64_t fill_words = 0;      // ll .. lmpart end, refilled before every launch
   uint32_t* sync = nullptr;
   size_t sync_bytes = 0;
+  int32_t* d_forced = nullptr;        // [MAX_STEPS]: the given tokens of a verify step
   uint64_t* d_table_check = nullptr;  // [W] per-worker schedule hashes, then the build id
   uint32_t* last_sync = nullptr;      // status words of the last launch (plan-owned or the static scratch)
   float* dbg_hidden = nullptr;
@@ -343,6 +344,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
     const size_t lm_end = off;
     p->sync_bytes = (size_t)SYNC_WORDS * 4;
     const size_t o_sync = piece(p->sync_bytes);
+    const size_t o_forced = piece((size_t)MAX_STEPS * 4);
     p->scratch_bytes = off;
     TRY(hipMalloc(&p->scratch, p->scratch_bytes));
     TRY(hipMemsetAsync(p->scratch, 0, p->scratch_bytes, p->stream));
@@ -350,6 +352,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
     p->lmpart = reinterpret_cast<uint32_t*>(p->scratch + o_lm);
     p->fill_words = (int64_t)(lm_end - o_ll) / 4;
     p->sync = reinterpret_cast<uint32_t*>(p->scratch + o_sync);
+    p->d_forced = reinterpret_cast<int32_t*>(p->scratch + o_forced);
   }
   if (cfg->flags & TILES_DEBUG_HIDDEN) {
     const size_t n = (size_t)MAX_STEPS * hp.s.n_layers * hp.s.H;
@@ -380,7 +383,7 @@ int check_identity(const tiles_plan* p) {
 // partials and status words live in the file-scope scratch array of this GPU (see
 // noalloc_scratch) instead of the plan's own buffers; the layout is the same.
 int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
-                float* out_logits, bool noalloc, const float* uniforms) {
+                float* out_logits, bool noalloc, const float* uniforms, const int32_t* forced = nullptr) {
   if (!p || !kv || !out_tokens) return set_err(TILES_E_ARG, "null plan, kv or out_tokens");
   if (p->hp.top_k > 0 && !uniforms)
     return set_err(TILES_E_ARG, "this plan samples (top_k > 0): use tiles_decode_sampled with the step uniforms");
@@ -440,6 +443,7 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   a.top_k = hp.top_k;
   a.temperature = hp.temperature;
   a.top_p = hp.top_p;
+  a.forced = forced;
   a.dbg_hidden = p->dbg_hidden;
   a.trace = p->trace;
   a.token0 = token;
@@ -524,6 +528,17 @@ int tiles_decode_sampled(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t
 int tiles_decode_noalloc(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
                          float* out_logits) {
   return decode_impl(p, kv, token, n_steps, out_tokens, out_logits, true, nullptr);
+}
+
+int tiles_verify(tiles_plan_t* p, tiles_kv_t* kv, const int32_t* tokens, int32_t m, int32_t* out_argmax,
+                 float* out_logits) {
+  if (!p || !tokens) return set_err(TILES_E_ARG, "null plan or tokens");
+  if (p->hp.top_k > 0) return set_err(TILES_E_ARG, "verify steps are greedy: this plan samples (top_k > 0)");
+  if (m < 1 || m > MAX_STEPS) return set_err(TILES_E_ARG, "m must be in [1, 64]");
+  for (int32_t i = 0; i < m; ++i)
+    if (tokens[i] < 0 || tokens[i] >= p->hp.s.V) return set_err(TILES_E_ARG, "token out of range");
+  if (m > 1) HIP_TRY(hipMemcpyAsync(p->d_forced, tokens + 1, (size_t)(m - 1) * 4, hipMemcpyHostToDevice, p->stream));
+  return decode_impl(p, kv, tokens[0], m, out_argmax, out_logits, false, nullptr, p->d_forced);
 }
 
 int tiles_kv_convert_int8(tiles_plan_t* p, const void* k_bf16, const void* v_bf16, int64_t capacity, int64_t length,

@@ -1725,6 +1725,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         } else if (CTRL && step > 0) {
           ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
           if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+          if (!ab && a.forced) tok = a.forced[step - 1];  // a verify step: the given token, not the argmax
         }
         if (CTRL && !ab) ss = stage_embedding<Q8>(a, L, tok, gain, lane);
       } else {

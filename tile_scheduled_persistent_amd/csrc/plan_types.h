@@ -171,6 +171,8 @@ struct KernelArgs {
   int32_t top_k;             // 0: greedy; 1 .. MAX_TOP_K: sampled (top-k, temperature, top-p)
   float temperature;
   float top_p;
+  const int32_t* forced;     // [n_steps - 1] or null: step s > 0 consumes forced[s - 1] (verify steps); the
+                             // argmax is still recorded in out_tokens
 };
 
 }  // namespace tiles

@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 import torch
@@ -113,6 +113,9 @@ def lib() -> ctypes.CDLL:
         L.tiles_decode_sampled.restype = ctypes.c_int
         L.tiles_decode_sampled.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.tiles_verify.restype = ctypes.c_int
+        L.tiles_verify.argtypes = [ctypes.c_void_p, ctypes.POINTER(KV), ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
         L.tiles_plan_destroy.restype = None
         L.tiles_plan_destroy.argtypes = [ctypes.c_void_p]
         L.tiles_last_error.restype = ctypes.c_char_p
@@ -357,6 +360,36 @@ class Plan:
         _check(rc)
         kv.length = c.length
         return rc
+
+    def verify(self, kv: KVCache, tokens: Sequence[int], out_argmax: Optional[torch.Tensor] = None,
+               out_logits: Optional[torch.Tensor] = None):
+        """A greedy verify step (tiles_verify): ``tokens`` = [last accepted token, draft 1, ...].
+        Synchronizes the device and returns (argmax int64 [m], accepted count n, verified tokens
+        [n + 1]: the accepted drafts, then the argmax after them); kv.length becomes its value before
+        the call + n + 1."""
+        tokens = [int(t) for t in tokens]
+        m = len(tokens)
+        if out_argmax is None:
+            out_argmax = torch.empty(m, dtype=torch.int32, device="cuda")
+        if out_argmax.dtype != torch.int32 or not out_argmax.is_cuda or out_argmax.numel() < m:
+            raise ValueError("out_argmax must be a device int32 tensor with m entries")
+        if out_logits is not None and (out_logits.dtype != torch.float32 or not out_logits.is_cuda
+                                       or out_logits.numel() < m * self.model.vocab):
+            raise ValueError("out_logits must be a device float32 tensor [m, vocab]")
+        length0 = kv.length
+        c = kv.struct()
+        buf = (ctypes.c_int32 * max(m, 1))(*tokens)
+        _check(lib().tiles_verify(self._h, ctypes.byref(c), buf, m, _ptr(out_argmax), _ptr(out_logits)))
+        torch.cuda.synchronize()
+        st = self.status()
+        if st != TILES_OK:
+            raise RuntimeError(f"tiles_verify: launch status {st}: {last_error()}")
+        a = out_argmax[:m].cpu().numpy().astype(np.int64)
+        n = 0
+        while n < m - 1 and int(a[n]) == tokens[n + 1]:
+            n += 1
+        kv.length = length0 + n + 1
+        return a, n, np.array(tokens[1:n + 1] + [int(a[n])], dtype=np.int64)
 
     def status(self) -> int:
         return lib().tiles_plan_status(self._h)
