@@ -785,12 +785,13 @@ def _greedy_continuation(s, plan, tok, n):
     return kv, [int(t) for t in g_t], g_l
 
 
-@pytest.mark.parametrize("kvfmt", ["bf16", "int8"])
-def test_verify_of_the_greedy_continuation_is_the_greedy_launch_bit_for_bit(kvfmt):
+@pytest.mark.parametrize("kvfmt,weights", [("bf16", "bf16"), ("int8", "bf16"), ("bf16", "int8")])
+def test_verify_of_the_greedy_continuation_is_the_greedy_launch_bit_for_bit(kvfmt, weights):
     """Drafts equal to the launch's own greedy tokens: every draft accepted, the argmaxes, logits and
     written cache bytes identical to the free-running launch (each position consumes the same token),
-    and the verified output is that continuation one token further."""
-    s = Setup(WIDE, 96, 60, kv=kvfmt)
+    and the verified output is that continuation one token further (BF16 or INT8 cache, BF16 or INT8
+    weights)."""
+    s = Setup(WIDE, 96, 60, kv=kvfmt, weights=weights)
     tok = synth.make_tokens(WIDE, 1)[0]
     m = 12
     with s.plan() as plan:
