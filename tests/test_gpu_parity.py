@@ -861,6 +861,25 @@ def test_full_size_verify_sixteen_tokens():
           flush=True)
 
 
+def test_verify_of_sixty_four_positions_to_capacity():
+    """The longest verify step (64 positions) ending exactly at the cache's capacity, without logits:
+    with drafts the greedy continuation every draft is accepted and the argmaxes equal the greedy
+    launch's; the cache length the binding reports is the one before the call + 64."""
+    s = Setup(TINY, 74, 10)
+    tok = synth.make_tokens(TINY, 1)[0]
+    with s.plan() as plan:
+        kv_g, g, _ = _greedy_continuation(s, plan, tok, 64)
+        kv = s.fresh_kv(plan)
+        a, n, out = plan.verify(kv, [tok] + g[:63])
+        assert n == 63 and list(a) == g and list(out) == g
+        assert kv.length == 74
+        assert torch.equal(kv.k, kv_g.k) and torch.equal(kv.v, kv_g.v)
+        kv = s.fresh_kv(plan)
+        kv.length = 11  # one position past what 64 more fit
+        with pytest.raises(tiles.TilesError):
+            plan.verify(kv, [tok] + g[:63])
+
+
 def test_verify_entry_point_errors():
     s = Setup(TINY, 40, 10)
     with s.plan() as plan:
