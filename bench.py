@@ -172,8 +172,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode path has no multi-GPU "
-                                   "component (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "one GPU only: the decode path has no multi-GPU component (it would shard "
+                                   "per layer by KV head, with two all-reduces of the hidden state per layer)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np

@@ -16,7 +16,7 @@ Sources (the pages give the workload, not the formulas):
   decode ops are q/k norm + RoPE + KV write, residual add + RMSNorm, and
   SwiGLU; "Milestones" M2: the reference model computes in Float32.
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
 
 R1  RMSNorm is y = x / sqrt(mean(x^2) + eps) * g (plain gain), the mean taken
     over the whole vector (over head_dim for the per-head q/k norm).

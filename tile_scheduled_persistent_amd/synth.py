@@ -133,13 +133,13 @@ def make_kv(cfg: ModelConfig, capacity: int, n_cached: int, seed: int = SEED_KV,
 
 
 def make_tokens(cfg: ModelConfig, n: int, seed: int = SEED_TOKENS) -> List[int]:
-    """``n`` tokens ~ U[0, vocab) (CPU generator: identical on every box)."""
+    """``n`` tokens ~ U[0, vocab) (CPU generator: identical on every machine)."""
     g = _gen("cpu", _seed(seed, cfg, 0))
     return [int(t) for t in torch.randint(0, cfg.vocab, (n,), generator=g)]
 
 
 def make_uniforms(cfg: ModelConfig, n: int, seed: int = SEED_UNIFORMS) -> np.ndarray:
-    """``n`` FP32 uniforms in [0, 1), one per sampled step (CPU generator: identical on every box)."""
+    """``n`` FP32 uniforms in [0, 1), one per sampled step (CPU generator: identical on every machine)."""
     g = _gen("cpu", _seed(seed, cfg, 0))
     u = torch.rand(n, generator=g, dtype=torch.float32).numpy()
     return np.minimum(u, np.float32(1.0) - np.float32(2.0 ** -24))  # strictly below 1
