@@ -26,14 +26,25 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # CDNA4 code generation flags: packed-FP32 instructions are disabled everywhere.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-unit scheduling: the worker units use the backend's iterative ILP scheduler (measured faster:
+# +1.4 % on the Llama-3.2-1B shape, +3 % sampled and at 32K positions, +1.2 % INT8 weights), except
+# those with the INT8 KV cache, which were 1.5 % faster with the default scheduler.
+ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+
+
+def unit_flags(src: str) -> list:
+    return ILP_SCHED if src.startswith("workers_") and "_kv8" not in src else []
 
 
 def build_id() -> str:
-    """64-bit id of the worker binary: hash of every source and header."""
+    """64-bit id of the worker binary: hash of every source and header and of the flags each source
+    is compiled with."""
     h = hashlib.sha256()
+    h.update(" ".join(DEVICE_FLAGS).encode())
     for name in SOURCES + HEADERS:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
+            h.update(" ".join(unit_flags(name)).encode())
             h.update(f.read())
     with open(os.path.join(ROOT, "include", "tiles.h"), "rb") as f:
         h.update(f.read())
@@ -62,7 +73,7 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
     jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, common + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        futs = [ex.submit(_run, common + unit_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
                 for src, obj in zip(SOURCES, objs)]
         for f in futs:
             f.result()
