@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
     ap.add_argument("--verify-tokens", type=int, default=0,
                     help="also time greedy verify steps of this many tokens (added to the line as 'verify')")
+    ap.add_argument("--verify-plan-tokens", type=int, default=0,
+                    help="with --verify-tokens: time them with a verify plan taking this many positions per step "
+                         "through every tile (2 or 4; 0: the decode plan, one position per step)")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")
@@ -277,7 +280,16 @@ def main():
     }
 
     if args.verify_tokens > 0:
-        result["verify"] = _verify_timing(plan, kv, wl, token, out_t, args, stream)
+        vplan = plan
+        if args.verify_plan_tokens > 1:
+            vplan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, weight_format=wl.weights,
+                               kv_format=wl.kv, stream=stream, tokens_per_step=args.verify_plan_tokens)
+        result["verify"] = _verify_timing(vplan, kv, wl, token, out_t, args, stream)
+        if vplan is not plan:
+            result["verify"]["plan"] = {"positions_per_step": vplan.info().tokens_per_step,
+                                        "waves_per_step": vplan.info().waves_per_step,
+                                        "combine": "own wave"}
+            vplan.close()
 
     if args.trace_report:
         _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info)
@@ -305,6 +317,8 @@ def _verify_timing(plan, kv, wl, token, out_t, args, stream):
     from tile_scheduled_persistent_amd import tiles
 
     M = min(args.verify_tokens, wl.n_steps)
+    T = plan.info().tokens_per_step
+    M -= M % T  # a verify plan takes a multiple of its positions per step
     toks = [int(token)] + [int(t) for t in out_t[:M - 1].cpu().tolist()]
     buf = (ctypes.c_int32 * M)(*toks)
     out_a = torch.zeros(M, dtype=torch.int32, device="cuda")
@@ -333,10 +347,12 @@ def _verify_timing(plan, kv, wl, token, out_t, args, stream):
     accepted = 0
     while accepted < M - 1 and int(a[accepted]) == toks[accepted + 1]:
         accepted += 1
+    how = ("one weight stream per position" if T == 1 else
+           f"a verify plan: {T} positions per kernel step, one weight stream per {T} positions")
     return {"tokens_per_step": M, "accepted": accepted, "ms_per_step": round(ms, 4),
             "positions_per_s": round(M / (ms * 1e-3), 1),
-            "how": "tiles_verify launches (m positions each, one weight stream per position), median of "
-                   f"{args.steps}, HIP events on the plan's stream"}
+            "how": f"tiles_verify launches (m positions each, {how}), median of {args.steps}, HIP events on the "
+                   "plan's stream"}
 
 
 def _trace_report(path, m, wl, w, k0, v0, token, args, info):

@@ -101,6 +101,19 @@ typedef struct tiles_config {
    * channel) smoothing factor before quantization; attention reads the codes and computes with the
    * dequantized rows (queries stay FP32).  See tiles_kv_t and tiles_kv_convert_int8. */
   int32_t kv_format;
+  /* Positions per step of a verify plan ("History and roadmap" (TileInfer.jl), "M8 so far" table:
+   * verify steps of up to 16 tokens; "Tried and not kept" table: verify GEMMs at 2-64 tokens).  0 or 1:
+   * one position per step (decode plans; tiles_verify then runs its m positions as m steps).  2 or 4:
+   * a verify plan, usable with tiles_verify only: every step takes tokens_per_step consecutive
+   * teacher-forced positions through each tile, so that each GEMV tile streams its weights once for
+   * all of them (its LDS holds one input vector per position) and each attention tile serves all of
+   * them with one pass over the cached rows, the step's own rows entering the positions at or after
+   * them.  Needs greedy selection (top_k = 0), the BF16 KV cache, no TILES_TRACE, splits merged in a
+   * wave of their own (combine_mode 0 or 2), tokens_per_step x head_dim <= 256, and query heads per
+   * attention tile x tokens_per_step <= 4 (the planner lowers its choice of attn_heads to fit).  The
+   * LDS must hold tokens_per_step input vectors of max(hidden, ffn) floats (padded); plan creation
+   * fails with TILES_E_CONFIG otherwise. */
+  int32_t tokens_per_step;
 } tiles_config_t;
 
 #define TILES_KV_BF16 0
@@ -182,6 +195,7 @@ typedef struct tiles_plan_info {
   int32_t weight_format;      /* TILES_WEIGHTS_BF16 or TILES_WEIGHTS_INT8 */
   int32_t top_k;              /* 0: greedy plan; else the plan samples (tiles_decode_sampled) */
   int32_t kv_format;          /* TILES_KV_BF16 or TILES_KV_INT8 */
+  int32_t tokens_per_step;    /* positions per step: 1, or 2 / 4 for a verify plan */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */
@@ -235,13 +249,15 @@ int tiles_decode_sampled(tiles_plan_t *plan, tiles_kv_t *kv, int32_t token, int3
  * out_argmax[i] (lowest index on ties).  Draft tokens[i + 1] is accepted while out_argmax[i] equals it;
  * with n accepted, the verified output is tokens[1 .. n] followed by out_argmax[n], and the caller
  * sets the cache length to (length before the call) + n + 1 (rows written past it are overwritten
- * by later steps).  The m positions run as m steps of the decode launch (each streams the weights
- * once; the tiles do not take several tokens at a time).
+ * by later steps).  With a decode plan the m positions run as m steps of the decode launch (each
+ * streams the weights once); a verify plan (tokens_per_step = T > 1) runs them as m / T steps of T
+ * positions each, every tile taking the T positions of a step at once (one weight stream per step).
  *   tokens     : host int32 [m], each 0 <= t < vocab; read during the call.
- *   m          : 1 .. 64.
+ *   m          : 1 .. 64, a multiple of the plan's tokens_per_step.
  *   out_argmax : device int32 [m].   out_logits : device float [m][vocab], or NULL.
  * kv as tiles_decode (kv->length is advanced by m).  Errors as tiles_decode, plus TILES_E_ARG for a
- * sampling plan, null tokens or a token out of range.  Copies tokens[1 ..] into a buffer the plan
+ * sampling plan, null tokens, a token out of range or m not a multiple of tokens_per_step.  The
+ * decode entry points return TILES_E_ARG for a verify plan.  Copies tokens[1 ..] into a buffer the plan
  * owns, on the plan's stream; allocates nothing. */
 int tiles_verify(tiles_plan_t *plan, tiles_kv_t *kv, const int32_t *tokens, int32_t m, int32_t *out_argmax,
                  float *out_logits);

@@ -303,3 +303,57 @@ def test_int8_kv_format_and_split_limits_rejected():
     with pytest.raises(tiles.TilesError):  # a forced split count leaving more than 2048 positions per split
         tiles.dry_run(TINY, 5000, kv="int8", kv_splits=2)
     assert tiles.lib().tiles_kv_convert_int8(None, None, None, 1, 0, None) == tiles.TILES_E_ARG
+
+
+# ---------------------------------------------------------------------------------------------
+# verify plans (tokens_per_step > 1)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,pos,mt", [(LLAMA_1B, 1087, 2), (QWEN3_06B, 1087, 2), (QWEN3_4B, 1087, 2), (TINY, 80, 2),
+                                      (TINY, 80, 4)], ids=["llama1b-2", "qwen06b-2", "qwen4b-2", "tiny-2", "tiny-4"])
+def test_verify_plans_validate(m, pos, mt):
+    """A verify plan merges the splits in a wave of its own (one more wave per layer than a plan whose
+    o_proj prologue merges them), holds at most 4 query rows per attention tile, fits the LDS, records
+    its positions per step, and is not the decode plan's schedule."""
+    info = tiles.dry_run(m, pos, tokens_per_step=mt)
+    dec = tiles.dry_run(m, pos)
+    assert info.tokens_per_step == mt and dec.tokens_per_step == 1
+    assert info.combine_mode == 2
+    assert info.waves_per_step == m.n_layers * 6 + 1
+    assert info.attn_heads * mt <= 4
+    assert info.lds_bytes <= 160 * 1024
+    assert info.checksum != dec.checksum
+    cfg = tiles.make_config(m, pos, tokens_per_step=mt)
+    assert tiles.lib().tiles_plan_debug_validate(ctypes.byref(cfg), 256, 0) == tiles.TILES_OK, tiles.last_error()
+
+
+def test_verify_plans_bound_the_heads_per_attention_tile():
+    """Qwen3-4B has 4 query heads per KV head: with 2 positions per step a tile holds at most 2 heads.
+    The planner takes the fewest heads per tile whose tiles fit the workers; where only 4 would fit
+    (40 workers, 4 splits), the verify plan is rejected, as is an explicit attn_heads of 4."""
+    assert tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, attn_heads=2).attn_heads == 2
+    assert tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, kv_splits=4, n_workers=64).attn_heads == 2
+    assert tiles.dry_run(QWEN3_4B, 1087, kv_splits=4, n_workers=40).attn_heads == 4
+    for kw in (dict(kv_splits=4, n_workers=40), dict(attn_heads=4)):
+        with pytest.raises(tiles.TilesError):
+            tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, **kw)
+
+
+@pytest.mark.parametrize("kw", [dict(tokens_per_step=3), dict(tokens_per_step=8), dict(tokens_per_step=-1),
+                                dict(tokens_per_step=2, sampling=(1.0, 4, 1.0)), dict(tokens_per_step=2, kv="int8"),
+                                dict(tokens_per_step=2, flags=tiles.TILES_TRACE), dict(tokens_per_step=2, combine_mode=1)],
+                         ids=["three", "eight", "negative", "sampled", "int8-kv", "traced", "merge-in-o-proj"])
+def test_verify_plan_options_rejected(kw):
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(TINY, 80, **kw)
+    assert e.value.code == tiles.TILES_E_CONFIG
+
+
+def test_verify_plan_limits():
+    """4 positions per step need head_dim 64 (one RoPE row per position in LDS) and room for four input
+    vectors of the FFN width: the Llama-3.2-1B shape (ffn 8192) does not fit, nor does head_dim 128."""
+    for m in (LLAMA_1B, QWEN3_06B):
+        with pytest.raises(tiles.TilesError):
+            tiles.dry_run(m, 1087, tokens_per_step=4)
+    assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=0).tokens_per_step == 1
+    assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=1).checksum == tiles.dry_run(LLAMA_1B, 1087).checksum

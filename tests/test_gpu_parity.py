@@ -880,6 +880,128 @@ def test_verify_of_sixty_four_positions_to_capacity():
             plan.verify(kv, [tok] + g[:63])
 
 
+# ---------------------------------------------------------------------------------------------
+# verify plans: tokens_per_step consecutive positions through every tile per step
+# ---------------------------------------------------------------------------------------------
+
+VERIFY_PLANS = [("tiny", 2, "bf16"), ("tiny", 4, "bf16"), ("wide", 2, "bf16"), ("wide", 2, "int8")]
+
+
+def _verify_plan_case(s, plan, tag, tokens, pos, check_hidden=True):
+    """One verify call of a verify plan against the oracle: every position's argmax, logits (and hidden
+    states) teacher-forced on the same tokens, the K/V rows written for every position, and the
+    accepted count and verified tokens against the oracle's verify where its decisions are clear."""
+    m = len(tokens)
+    mdl = s.m
+    kv = s.fresh_kv(plan)
+    kv.length = pos
+    out_l = torch.zeros((m, mdl.vocab), dtype=torch.float32, device="cuda")
+    a, n, out = plan.verify(kv, tokens, out_logits=out_l)
+    hid = plan.read_debug(hidden=True)[0] if check_hidden else None
+    o = s.oracle()
+    okv = s.oracle_kv()
+    o_dec = o.decode(okv, tokens[0], pos, m, teacher=tokens[1:], widen_kv_once=True)
+    stats = compare_teacher_forced(tag, a, out_l.cpu().numpy(), hid, o_dec)
+    kv_rows_close(f"{tag} K", kv.k, okv["k"], pos, m)
+    kv_rows_close(f"{tag} V", kv.v, okv["v"], pos, m)
+    o_acc = 0
+    while o_acc < m - 1 and int(o_dec["tokens"][o_acc]) == tokens[o_acc + 1]:
+        o_acc += 1
+    margins = [top2_margin(o_dec["logits"][i]) for i in range(m)]
+    if min(margins[:o_acc + 1]) > MARGIN:  # every decision the acceptance depends on is clear
+        assert n == o_acc, (tag, n, o_acc)
+        assert list(out) == list(tokens[1:n + 1]) + [int(o_dec["tokens"][n])]
+    assert kv.length == pos + n + 1
+    return a, n, stats
+
+
+@pytest.mark.parametrize("shape,mt,weights", VERIFY_PLANS, ids=[f"{a}-{b}-{c}" for a, b, c in VERIFY_PLANS])
+def test_verify_plan_against_the_oracle(shape, mt, weights):
+    """A verify plan (mt positions per step through every tile, BF16 or INT8 weights), drafts the
+    decode plan's greedy continuation, whole or with a wrong token at position 3 or 8: every position
+    against the oracle teacher-forced on the same tokens, the written K/V rows, and the acceptance
+    against the oracle's."""
+    mdl = TINY if shape == "tiny" else WIDE
+    s = Setup(mdl, 96, 60, weights=weights)
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 12
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    with s.plan(tokens_per_step=mt) as plan:
+        info = plan.info()
+        assert info.tokens_per_step == mt and info.combine_mode == 2
+        for j in (None, 3, 8):
+            drafts = list(g[:m - 1])
+            if j is not None:
+                drafts[j - 1] = (g[j - 1] + 7) % mdl.vocab
+            tag = f"{shape} mt={mt} {weights} j={j}"
+            _, n, stats = _verify_plan_case(s, plan, tag, [tok] + drafts, 60)
+            print(f"{tag}: accepted {n}; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
+                  f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}", flush=True)
+
+
+def test_verify_plan_of_sixty_four_positions_to_capacity():
+    """A 4-position verify plan over 64 positions (16 steps) ending exactly at the cache's capacity, the
+    drafts the greedy continuation: against the oracle; one position more is rejected."""
+    s = Setup(TINY, 74, 10)
+    tok = synth.make_tokens(TINY, 1)[0]
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, 64)
+    with s.plan(tokens_per_step=4) as plan:
+        _, n, stats = _verify_plan_case(s, plan, "tiny mt=4 to capacity", [tok] + g[:63], 10)
+        print(f"tiny mt=4 64 positions: accepted {n}; {stats}", flush=True)
+        kv = s.fresh_kv(plan)
+        kv.length = 11
+        with pytest.raises(tiles.TilesError):
+            plan.verify(kv, [tok] + g[:63])
+
+
+def test_verify_plan_entry_point_errors():
+    """A verify plan runs tiles_verify only, with m a multiple of its positions per step; a plan that
+    cannot hold the step's input vectors is not created."""
+    s = Setup(TINY, 40, 10)
+    with s.plan(tokens_per_step=2) as plan:
+        kv = s.fresh_kv(plan)
+        L = tiles.lib()
+        c = kv.struct()
+        out = torch.zeros(8, dtype=torch.int32, device="cuda")
+        for toks in ([1, 2, 3], [1]):
+            buf = (ctypes.c_int32 * len(toks))(*toks)
+            assert L.tiles_verify(plan._h, ctypes.byref(c), buf, len(toks), ctypes.c_void_p(out.data_ptr()),
+                                  None) == tiles.TILES_E_ARG
+            assert "multiple" in tiles.last_error()
+        assert L.tiles_decode(plan._h, ctypes.byref(c), 1, 2, ctypes.c_void_p(out.data_ptr()), None) == tiles.TILES_E_ARG
+        assert "tiles_verify" in tiles.last_error()
+        assert L.tiles_decode_noalloc(plan._h, ctypes.byref(c), 1, 2, ctypes.c_void_p(out.data_ptr()),
+                                      None) == tiles.TILES_E_ARG
+        assert kv.length == 10
+    with pytest.raises(tiles.TilesError):
+        Setup(WIDE, 40, 10).plan(tokens_per_step=4)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_full_size_verify_plan_sixteen_tokens():
+    """A 16-position verify step of a 2-position verify plan on the Llama-3.2-1B shape at 1023 cached
+    positions, drafts the decode plan's greedy continuation with a wrong token at position 10: all 16
+    positions and the written K/V rows against the oracle teacher-forced on the same tokens, and the
+    acceptance against the oracle's."""
+    wl = WORKLOADS["llama1b"]
+    mdl = wl.model
+    s = Setup(mdl, wl.capacity, wl.n_cached, gen_device="cuda")
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 16
+    with s.plan(flags=0) as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    drafts = list(g[:m - 1])
+    drafts[9] = (g[9] + 1) % mdl.vocab
+    with s.plan(flags=0, tokens_per_step=2) as plan:
+        _, n, stats = _verify_plan_case(s, plan, "llama1b verify plan", [tok] + drafts, wl.n_cached,
+                                        check_hidden=False)
+    print(f"llama1b verify plan: {m} positions compared, accepted {n}; max logit abs err {stats['logit_abs_max']:.2e}, "
+          f"tokens checked {stats['tokens_checked']}", flush=True)
+
+
 def test_verify_entry_point_errors():
     s = Setup(TINY, 40, 10)
     with s.plan() as plan:

@@ -16,9 +16,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtiles.so")
 # The worker units each instantiate the persistent worker for one weight format, token selection
-# and KV format (they include kernel.hip); every source compiles to an object of its own, in
-# parallel, then links.
-WORKER_UNITS = [f"workers_{w}{s}{k}.hip" for w in ("bf16", "int8") for s in ("", "_sampled") for k in ("", "_kv8")]
+# and KV format, or (the _mt units) the multi-token verify workers of one weight format (they
+# include kernel.hip); every source compiles to an object of its own, in parallel, then links.
+WORKER_UNITS = [f"workers_{w}{s}{k}.hip" for w in ("bf16", "int8") for s in ("", "_sampled") for k in ("", "_kv8")] + [
+    "workers_bf16_mt.hip", "workers_int8_mt.hip"]
 SOURCES = ["kernel.hip", *WORKER_UNITS, "planner.cpp", "api.cpp"]
 HEADERS = ["plan_types.h", "planner.h"]
 ARCH = "gfx950"

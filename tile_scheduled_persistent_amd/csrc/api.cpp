@@ -30,7 +30,7 @@
 #endif
 
 namespace tiles {
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8);
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8, int mt);
 hipError_t launch_kv_convert(const uint16_t* k, const uint16_t* v, int64_t cap, int64_t length, int hd, int64_t nheads,
                              int8_t* codes, float* ks, float* vs, float* sigma, hipStream_t stream);
 hipError_t launch_pack(const PackSeg* segs, int nseg, uint8_t* dst, hipStream_t stream);
@@ -234,7 +234,7 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
   }
   const HostPlan& hp = p->hp;
   // occupancy probe of the worker binary
-  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0, hp.top_k > 0, hp.kv8 != 0);
+  p->kernel = worker_kernel(hp.s.hd, hp.T, false, hp.q8 != 0, hp.top_k > 0, hp.kv8 != 0, hp.mt);
   if (!p->kernel) {
     release(p);
     return set_err(TILES_E_CONFIG, "no worker instantiation for this head_dim / group size");
@@ -339,8 +339,9 @@ int create_impl(const tiles_config_t* cfg, const tiles_weights_t* w, tiles_plan*
       off += (bytes + 255) / 256 * 256;
       return o;
     };
-    const size_t o_ll = piece((size_t)hp.ll_words * 4);
-    const size_t o_lm = piece((size_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1));
+    // (multi-token plans: one set of tagged buffers and LM-head partials per position of a step)
+    const size_t o_ll = piece((size_t)hp.ll_words * 4 * hp.mt);
+    const size_t o_lm = piece((size_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1) * hp.mt);
     const size_t lm_end = off;
     p->sync_bytes = (size_t)SYNC_WORDS * 4;
     const size_t o_sync = piece(p->sync_bytes);
@@ -379,12 +380,15 @@ int check_identity(const tiles_plan* p) {
   return TILES_OK;
 }
 
-// One cooperative launch of the worker.  `noalloc`: the launch's tagged-data buffers, LM-head
-// partials and status words live in the file-scope scratch array of this GPU (see
-// noalloc_scratch) instead of the plan's own buffers; the layout is the same.
+// One cooperative launch of the worker over n_steps positions (a multi-token plan runs them
+// tokens_per_step at a time: n_steps / tokens_per_step kernel steps).  `noalloc`: the launch's
+// tagged-data buffers, LM-head partials and status words live in the file-scope scratch array of
+// this GPU (see noalloc_scratch) instead of the plan's own buffers; the layout is the same.
 int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps, int32_t* out_tokens,
                 float* out_logits, bool noalloc, const float* uniforms, const int32_t* forced = nullptr) {
   if (!p || !kv || !out_tokens) return set_err(TILES_E_ARG, "null plan, kv or out_tokens");
+  if (p->hp.mt > 1 && !forced)
+    return set_err(TILES_E_ARG, "this plan runs multi-token verify steps (tokens_per_step > 1): use tiles_verify");
   if (p->hp.top_k > 0 && !uniforms)
     return set_err(TILES_E_ARG, "this plan samples (top_k > 0): use tiles_decode_sampled with the step uniforms");
   if (p->hp.top_k == 0 && uniforms) return set_err(TILES_E_ARG, "this plan is greedy (top_k = 0): use tiles_decode");
@@ -414,8 +418,8 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   uint32_t* lmpart = p->lmpart;
   uint32_t* sync = p->sync;
   if (noalloc) {
-    const int64_t ll_bytes = ((int64_t)hp.ll_words * 4 + 255) / 256 * 256;
-    const int64_t lm_bytes = ((int64_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1) + 255) / 256 * 256;
+    const int64_t ll_bytes = ((int64_t)hp.ll_words * 4 * hp.mt + 255) / 256 * 256;
+    const int64_t lm_bytes = ((int64_t)hp.W * 8 * (hp.top_k > 0 ? hp.top_k : 1) * hp.mt + 255) / 256 * 256;
     const int64_t need = ll_bytes + lm_bytes + SYNC_WORDS * 4;
     if (need > NOALLOC_SCRATCH_BYTES)
       return set_err(TILES_E_ARG, "this plan's tagged scratch (" + std::to_string(need) +
@@ -448,7 +452,9 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   a.trace = p->trace;
   a.token0 = token;
   a.pos0 = (int32_t)kv->length;
-  a.n_steps = n_steps;
+  a.n_steps = n_steps / hp.mt;
+  a.mt = hp.mt;
+  a.ll_tok = hp.ll_words;
   a.n_waves = (int32_t)hp.waves.size();
   a.W = hp.W;
   a.n_layers = hp.s.n_layers;
@@ -535,6 +541,7 @@ int tiles_verify(tiles_plan_t* p, tiles_kv_t* kv, const int32_t* tokens, int32_t
   if (!p || !tokens) return set_err(TILES_E_ARG, "null plan or tokens");
   if (p->hp.top_k > 0) return set_err(TILES_E_ARG, "verify steps are greedy: this plan samples (top_k > 0)");
   if (m < 1 || m > MAX_STEPS) return set_err(TILES_E_ARG, "m must be in [1, 64]");
+  if (m % p->hp.mt != 0) return set_err(TILES_E_ARG, "m must be a multiple of the plan's tokens_per_step");
   for (int32_t i = 0; i < m; ++i)
     if (tokens[i] < 0 || tokens[i] >= p->hp.s.V) return set_err(TILES_E_ARG, "token out of range");
   if (m > 1) HIP_TRY(hipMemcpyAsync(p->d_forced, tokens + 1, (size_t)(m - 1) * 4, hipMemcpyHostToDevice, p->stream));
@@ -578,6 +585,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->weight_format = hp.q8 ? TILES_WEIGHTS_INT8 : TILES_WEIGHTS_BF16;
   info->top_k = hp.top_k;
   info->kv_format = hp.kv8 ? TILES_KV_INT8 : TILES_KV_BF16;
+  info->tokens_per_step = hp.mt;
   for (size_t wv = 0; wv < hp.waves.size(); ++wv)
     if (hp.waves[wv].kind == KIND_O) {
       info->o_workers = hp.wave_busy[wv];
@@ -676,7 +684,7 @@ int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
   if (!p) return set_err(TILES_E_ARG, "null plan");
   const uint32_t limit = rounds ? rounds : DEFAULT_SPIN_LIMIT;
   if (limit < 32 && !p->kernel_wd) {
-    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0, p->hp.kv8 != 0);
+    const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0, p->hp.kv8 != 0, p->hp.mt);
     if (!k)
       return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and KV, greedy decoding and one "
                                      "query head per attention tile");

@@ -216,6 +216,9 @@ constexpr int SM_QGAIN = 512;  // float[head_dim]: q-norm gains (attention tiles
 constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
 constexpr int SM_KSMOOTH = 768;  // float[head_dim]: INT8 KV key smoothing factors of the tile's KV head
 constexpr int SM_KVCUR = 896;    // float[2]: INT8 KV scales of the current position's K and V rows
+constexpr int SM_SS2 = 960;      // float[3][NWAVES]: as SM_SS, for positions 1 .. 3 of a multi-token step
+// (multi-token steps: SM_ROPE holds one (cos, sin) row per position of the step, tokens x head_dim <= 256)
+__device__ __forceinline__ int sm_ss(int t) { return t == 0 ? SM_SS : SM_SS2 + (t - 1) * NWAVES; }
 
 struct Lds {
   float* vec;
@@ -337,6 +340,38 @@ __device__ __forceinline__ bool gather(const KernelArgs& a, const uint32_t* src,
   return false;
 }
 
+// The same over the MT positions of a multi-token step in one polling loop: position t's n units
+// are those of src + t * tok_words (units t * n .. t * n + n - 1 of the combined range); map, prep
+// and sink see the position and the unit within it.
+template <int GB, int MT, bool WD, typename Map, typename Prep, typename Sink>
+__device__ __forceinline__ bool gather_mt(const KernelArgs& a, const uint32_t* src, int n, int64_t tok_words, int slot,
+                                          int nslots, uint32_t par, int lane, Map map, Prep prep, Sink sink) {
+  const int tok_units = (int)(tok_words / 4);
+  auto split = [&](int u, int& t) {
+    t = 0;
+#pragma unroll
+    for (int k = 1; k < MT; ++k) t += u >= k * n ? 1 : 0;
+    return u - t * n;
+  };
+  return gather<GB, WD>(
+      a, src, MT * n, slot, nslots, par, lane,
+      [&](int u) {
+        int t;
+        const int w = split(u, t);
+        return t * tok_units + map(w);
+      },
+      [&](int i, int u) {
+        int t;
+        const int w = split(u, t);
+        prep(i, t, w);
+      },
+      [&](int i, int u, const f32x4 x) {
+        int t;
+        const int w = split(u, t);
+        sink(i, t, w, x);
+      });
+}
+
 constexpr int GATHER_UNITS = 4;  // units per lane per polling pass (8 wavefronts x 64 lanes x 4 = 8192 floats)
 // Plain gathers (split partials into the o_proj prologue, the down input) poll twice as many
 // units per pass: the partials of 32 heads x 5 splits then arrive in one round trip.
@@ -367,17 +402,17 @@ __device__ __forceinline__ int vperm(int i) {
 // x (n floats, tagged) -> xres = x, vec = x * gain (GEMV input order, vperm), and this
 // wavefront's sum of squares of its share
 template <bool WD, bool Q8>
-__device__ __forceinline__ bool gather_norm(const KernelArgs& a, const Lds& L, const uint32_t* src, int n, const uint16_t* gain,
-                            int slot, int lane, uint32_t par, float& ss) {
+__device__ __forceinline__ bool gather_norm(const KernelArgs& a, float* vec, float* xres, const uint32_t* src, int n,
+                                            const uint16_t* gain, int slot, int lane, uint32_t par, float& ss) {
   uint2 gv[GATHER_UNITS];
   float s = 0.f;
   const bool ab = gather<GATHER_UNITS, WD>(
       a, src, n / 4, slot, NWAVES, par, lane, Identity{},
       [&](int i, int u) { gv[i] = *reinterpret_cast<const uint2*>(gain + u * 4); },
       [&](int i, int u, const f32x4 x) {
-        *reinterpret_cast<f32x4*>(L.xres + u * 4) = x;
+        *reinterpret_cast<f32x4*>(xres + u * 4) = x;
         const f32x4 v = {x.x * bf16_lo(gv[i].x), x.y * bf16_hi(gv[i].x), x.z * bf16_lo(gv[i].y), x.w * bf16_hi(gv[i].y)};
-        *reinterpret_cast<f32x4*>(L.vec + vperm<Q8>(u * 4)) = v;
+        *reinterpret_cast<f32x4*>(vec + vperm<Q8>(u * 4)) = v;
         s += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
       });
   ss = wave_sum(s);
@@ -394,10 +429,50 @@ __device__ __forceinline__ bool gather_plain(const KernelArgs& a, float* dst, co
                               });
 }
 
+// Multi-token steps: gather_norm for the MT positions in one polling loop (position t into
+// vec + t * vs, xres + t * xs, its sum of squares in ss[t]).
+template <bool WD, bool Q8, int MT>
+__device__ __forceinline__ bool gather_norm_mt(const KernelArgs& a, float* vec, float* xres, int vs, int xs,
+                                               const uint32_t* src, int n, const uint16_t* gain, int slot, int lane,
+                                               uint32_t par, float (&ss)[MT]) {
+  uint2 gv[GATHER_UNITS];
+  float s[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) s[t] = 0.f;
+  const bool ab = gather_mt<GATHER_UNITS, MT, WD>(
+      a, src, n / 4, a.ll_tok, slot, NWAVES, par, lane, Identity{},
+      [&](int i, int, int u) { gv[i] = *reinterpret_cast<const uint2*>(gain + u * 4); },
+      [&](int i, int t, int u, const f32x4 x) {
+        *reinterpret_cast<f32x4*>(xres + t * xs + u * 4) = x;
+        const f32x4 v = {x.x * bf16_lo(gv[i].x), x.y * bf16_hi(gv[i].x), x.z * bf16_lo(gv[i].y), x.w * bf16_hi(gv[i].y)};
+        *reinterpret_cast<f32x4*>(vec + t * vs + vperm<Q8>(u * 4)) = v;
+        const float q = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+#pragma unroll
+        for (int k = 0; k < MT; ++k) s[k] += t == k ? q : 0.f;
+      });
+#pragma unroll
+  for (int t = 0; t < MT; ++t) ss[t] = wave_sum(s[t]);
+  return ab;
+}
+
+// Multi-token steps: gather_plain for the MT positions in one polling loop (position t into
+// dst + t * dstride)
+template <bool WD, bool Q8, int MT>
+__device__ __forceinline__ bool gather_plain_mt(const KernelArgs& a, float* dst, int dstride, const uint32_t* src, int n,
+                                                int slot, int lane, uint32_t par, bool perm) {
+  return gather_mt<GATHER_UNITS_PLAIN, MT, WD>(a, src, n / 4, a.ll_tok, slot, NWAVES, par, lane, Identity{},
+                                               [&](int, int, int) {},
+                                               [&](int, int t, int u, const f32x4 x) {
+                                                 *reinterpret_cast<f32x4*>(dst + t * dstride +
+                                                                           (perm ? vperm<Q8>(u * 4) : u * 4)) = x;
+                                               });
+}
+
 // embedding row of `tok` (BF16, exact in FP32) -> xres, vec = x * gain (vperm order); returns the
 // sum of squares
 template <bool Q8>
-__device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds& L, int tok, const uint16_t* gain, int lane) {
+__device__ __forceinline__ float stage_embedding(const KernelArgs& a, float* vec, float* xres, int tok, const uint16_t* gain,
+                                                 int lane) {
   const uint16_t* erow = reinterpret_cast<const uint16_t*>(a.packed + a.embed_off + (int64_t)tok * a.embed_stride);
   constexpr int B = 8;
   float ss = 0.f;
@@ -418,9 +493,9 @@ __device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds&
       const int i = base + u * 256 + lane * 4;
       if (i < a.H) {
         const f32x4 x = {bf16_lo(ev[u].x), bf16_hi(ev[u].x), bf16_lo(ev[u].y), bf16_hi(ev[u].y)};
-        *reinterpret_cast<f32x4*>(L.xres + i) = x;
+        *reinterpret_cast<f32x4*>(xres + i) = x;
         const f32x4 v = {x.x * bf16_lo(gv[u].x), x.y * bf16_hi(gv[u].x), x.z * bf16_lo(gv[u].y), x.w * bf16_hi(gv[u].y)};
-        *reinterpret_cast<f32x4*>(L.vec + vperm<Q8>(i)) = v;
+        *reinterpret_cast<f32x4*>(vec + vperm<Q8>(i)) = v;
         ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
       }
     }
@@ -430,10 +505,11 @@ __device__ __forceinline__ float stage_embedding(const KernelArgs& a, const Lds&
 
 // Next token: reduce the W LM-head partials (value, index | parity << 31) of the step with
 // parity `par`, greater value first, lower index on ties.  Returns true when abandoned.
+// (Multi-token steps: the partials of position t of the step, at lmpart + t * W * 2.)
 template <bool WD>
-__device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint32_t par, int& tok) {
+__device__ __forceinline__ bool gather_token(const KernelArgs& a, int lane, uint32_t par, int& tok, int t = 0) {
   constexpr int B = 4;  // up to 4 x 128 workers
-  const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart);
+  const __amdgpu_buffer_rsrc_t r = rsrc(a.lmpart + (int64_t)t * a.W * 2);
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   uint32_t pending = 0;
@@ -907,28 +983,38 @@ __device__ __forceinline__ void wait_vmcnt() {
 // are loaded first).  Per-row partial sums go to part[row * NCOMP + c].  The reloads after the
 // last NB batches fetch next_src(0) .. next_src(NB - 1) into the NB register sets.
 // Q8: the chunks hold INT8 codes (16 per lane, 1024 columns) instead of BF16 weights (8, 512).
-template <int B, int NB, bool Q8, typename NextSrc>
+// MT > 1 (multi-token steps): every chunk is multiplied with the MT input vectors of the step (vs
+// floats apart in LDS), and row partials of position t go to part[t * pt + row * NCOMP + c].
+template <int B, int NB, bool Q8, int MT, typename NextSrc>
 __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed, const Range& r, int c, int lane,
                                              Stream<B, NB>& st, bool have, NextSrc next_src, const float* stage,
-                                             uint64_t* ts) {
+                                             uint64_t* ts, int vs, int pt) {
   constexpr int VPL = Q8 ? 16 : 8;            // input values per lane per chunk
   constexpr int CC = chunk_cols<Q8>();
   const int C = r.C;
   const int i = r.i;
   const int ihi = r.ihi;
   int row = i / C, seg = i - row * C;
-  float acc = 0.f;
+  float acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = 0.f;
   const float* vlane = L.vec + lane * 4;  // group q of this lane's columns of chunk s: vlane[s * CC + 256 q] (vperm)
   // Every slot is consumed (a slot past the range contributes zero and does not advance the
   // row), so no branch sits between a load and the use of its registers.
-  auto consume = [&](const u32x4& w, bool valid, const float* xv) {
-    const float d = Q8 ? dot16_i8(w, xv) : dot8(w, xv);
-    acc += valid ? d : 0.f;
+  auto consume = [&](const u32x4& w, bool valid, const float* xv) {  // xv: [MT][VPL]
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float d = Q8 ? dot16_i8(w, xv + t * VPL) : dot8(w, xv + t * VPL);
+      acc[t] += valid ? d : 0.f;
+    }
     seg += valid ? 1 : 0;
     if (seg == C) {
-      const float s = wave_sum(acc);
-      if (lane == 0) L.part[row * NCOMP + c] = s;
-      acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const float s = wave_sum(acc[t]);
+        if (lane == 0) L.part[t * pt + row * NCOMP + c] = s;
+        acc[t] = 0.f;
+      }
       seg = 0;
       ++row;
     }
@@ -937,15 +1023,19 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   // so their latencies overlap (the row-end branches would otherwise serialise them).  A slot
   // past the range reads a slice too (in bounds, masked).
   auto consume_batch = [&](const u32x4* w, int jb) {
-    float xv[B][VPL];
+    float xv[B][MT * VPL];
     int s = seg;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const float* px = vlane + s * CC;
 #pragma unroll
-      for (int q = 0; q < VPL / 4; ++q) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(px + 256 * q);
-        xv[u][4 * q] = x.x; xv[u][4 * q + 1] = x.y; xv[u][4 * q + 2] = x.z; xv[u][4 * q + 3] = x.w;
+      for (int t = 0; t < MT; ++t) {
+        const float* px = vlane + t * vs + s * CC;
+#pragma unroll
+        for (int q = 0; q < VPL / 4; ++q) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(px + 256 * q);
+          float* xo = xv[u] + t * VPL + 4 * q;
+          xo[0] = x.x; xo[1] = x.y; xo[2] = x.z; xo[3] = x.w;
+        }
       }
       s = s + 1 == C ? 0 : s + 1;
     }
@@ -1001,20 +1091,23 @@ __device__ __forceinline__ void stream_range(const Lds& L, const uint8_t* packed
   if (b == 0) consume_staged();
   if (ls > 0) st.sk = -1;
   if (seg != 0) {
-    const float s = wave_sum(acc);
-    if (lane == 0) L.part[row * NCOMP + c] = s;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) L.part[t * pt + row * NCOMP + c] = s;
+    }
   }
 }
 
 // total of row r of a block: partials of the compute waves whose ranges touch it, in order.
 // Every slot of the row is read (independent loads); those of waves that did not write it are
 // dropped by a select.
-__device__ __forceinline__ float row_total(const Lds& L, int nr, int C, int r) {
+__device__ __forceinline__ float row_total(const float* part, int nr, int C, int r) {
   const int n = nr * C;
   const int first = r * C, last = r * C + C - 1;
   float v[NCOMP];
 #pragma unroll
-  for (int c = 0; c < NCOMP; ++c) v[c] = L.part[r * NCOMP + c];
+  for (int c = 0; c < NCOMP; ++c) v[c] = part[r * NCOMP + c];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < NCOMP; ++c) {
@@ -1074,10 +1167,14 @@ __device__ __forceinline__ void merge_heads(const float* part, int nh, int S, in
 // Attention tile LDS layout (inside `part`): q[G][HD] (normed, roped, scaled to the base-2
 // domain) | kc[HD] (normed, roped, BF16-rounded) | vc[HD] (BF16-rounded) | compute-wave states
 // [NCOMP][G][HD + 4] | merged partial [G][HD + 4].  The raw q/k/v are gathered into `vec`.
-template <int HD, int G>
-__device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + G * HD + 2 * HD; }
-template <int HD, int G>
-__device__ __forceinline__ float* attn_merged(const Lds& L) { return L.part + G * HD + 2 * HD + NCOMP * G * pstride<HD>(); }
+// Multi-token steps (MT positions): q holds MT * G rows, row t * G + h being query head h at
+// position t of the step, and kc / vc one row per position: q[MT * G][HD] | kc[MT][HD] |
+// vc[MT][HD] | states [NCOMP][MT * G][HD + 4] | merged [MT * G][HD + 4]; position t's raw q/k/v
+// are at vec + t * lds_vec_floats.
+template <int HD, int G, int MT = 1>
+__device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + MT * G * HD + 2 * MT * HD; }
+template <int HD, int G, int MT = 1>
+__device__ __forceinline__ float* attn_merged(const Lds& L) { return attn_ws<HD, G, MT>(L) + NCOMP * MT * G * pstride<HD>(); }
 // INT8 KV: the split's K scales, then its V scales, by position - split start (MAX_SPLIT_POSITIONS_KV8
 // each at most; the planner sizes the area)
 template <int HD, int G>
@@ -1100,7 +1197,7 @@ __device__ __forceinline__ float kv_code(float r, float s) {
 // all wavefronts: raw q (the tile's G query heads, from head qa), k, v of KV head g into vec from
 // the QKV wave's output
 template <int HD, int G, bool WD>
-__device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, const uint32_t* src, int g, int qa, int slot,
+__device__ __forceinline__ bool gather_qkv(const KernelArgs& a, float* vec, const uint32_t* src, int g, int qa, int slot,
                                            int lane, uint32_t par) {
   constexpr int NQ = G * HD / 4, NK = HD / 4;
   const int q0 = qa * HD / 4;
@@ -1109,7 +1206,21 @@ __device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, co
   return gather<2, WD>(
       a, src, NQ + 2 * NK, slot, NWAVES, par, lane,
       [&](int u) { return u < NQ ? q0 + u : u < NQ + NK ? k0 + (u - NQ) : v0 + (u - NQ - NK); }, NoPrep{},
-      [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(L.vec + u * 4) = x; });
+      [&](int, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(vec + u * 4) = x; });
+}
+
+// Multi-token steps: gather_qkv for the MT positions in one polling loop (position t into vec + t * vs)
+template <int HD, int G, bool WD, int MT>
+__device__ __forceinline__ bool gather_qkv_mt(const KernelArgs& a, float* vec, int vs, const uint32_t* src, int g, int qa,
+                                              int slot, int lane, uint32_t par) {
+  constexpr int NQ = G * HD / 4, NK = HD / 4;
+  const int q0 = qa * HD / 4;
+  const int k0 = (a.n_heads * HD + g * HD) / 4;
+  const int v0 = (a.n_heads * HD + a.n_kv * HD + g * HD) / 4;
+  return gather_mt<2, MT, WD>(
+      a, src, NQ + 2 * NK, a.ll_tok, slot, NWAVES, par, lane,
+      [&](int u) { return u < NQ ? q0 + u : u < NQ + NK ? k0 + (u - NQ) : v0 + (u - NQ - NK); }, [&](int, int, int) {},
+      [&](int, int t, int u, const f32x4 x) { *reinterpret_cast<f32x4*>(vec + t * vs + u * 4) = x; });
 }
 
 // all wavefronts, between barriers P and A: wave u < G normalises (optional) and rotates query
@@ -1118,126 +1229,138 @@ __device__ __forceinline__ bool gather_qkv(const KernelArgs& a, const Lds& L, co
 // key row's scale times the dot product of these with its codes), and the current K and V rows are
 // quantized: kc / vc hold their codes, SM_KVCUR their scales (also put at the split's scale area
 // when the split holds the current position, split sp).
-template <int HD, int G, bool KV8>
+// MT > 1: the same for every position t of the step (pos = its first position), each with its own
+// RoPE row.
+template <int HD, int G, bool KV8, int MT = 1>
 __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos,
                                               int sp) {
   constexpr int HALF = HD / 2;
+  static_assert(MT == 1 || !KV8, "multi-token steps use the BF16 cache");
   float* q = L.part;
-  float* kc = q + G * HD;
-  float* vc = kc + HD;
-  const float* raw = L.vec;
+  float* kc = q + MT * G * HD;
+  float* vc = kc + MT * HD;
   int slo = 0, shi = 0;
   if (KV8) split_bounds(a.S, sp, pos + 1, slo, shi);
   const bool own_cur = KV8 && slo <= pos && pos < shi;
   float* kss = attn_kscales<HD, G>(L);
   float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
-  if (wave_index <= G) {
-    const int u = wave_index;
-    float u0 = 0.f, u1 = 0.f;
-    if (lane < HALF) {
-      u0 = raw[u * HD + lane];
-      u1 = raw[u * HD + lane + HALF];
-    }
-    if (gain_off(L, layer, 2) >= 0) {
-      const float ss = wave_sum(u0 * u0 + u1 * u1);
-      const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
-      const float* gn = L.small + (u < G ? SM_QGAIN : SM_KGAIN);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const float* raw = L.vec + t * a.lds_vec_floats;
+    if (wave_index <= G) {
+      const int u = wave_index;
+      float u0 = 0.f, u1 = 0.f;
       if (lane < HALF) {
-        u0 = u0 * rs * gn[lane];
-        u1 = u1 * rs * gn[lane + HALF];
+        u0 = raw[u * HD + lane];
+        u1 = raw[u * HD + lane + HALF];
       }
-    }
-    float r0 = 0.f, r1 = 0.f;
-    if (lane < HALF) {
-      const float* cs = L.small + SM_ROPE + lane * 2;
-      const float co = cs[0], si = cs[1];
-      r0 = u0 * co - u1 * si;
-      r1 = u1 * co + u0 * si;
-    }
-    if constexpr (KV8) {
-      const float* sg = L.small + SM_KSMOOTH;
-      if (u < G) {
+      if (gain_off(L, layer, 2) >= 0) {
+        const float ss = wave_sum(u0 * u0 + u1 * u1);
+        const float rs = 1.0f / sqrtf(ss / (float)HD + a.eps);
+        const float* gn = L.small + (u < G ? SM_QGAIN : SM_KGAIN);
         if (lane < HALF) {
-          q[u * HD + lane] = r0 * a.qscale * sg[lane];
-          q[u * HD + lane + HALF] = r1 * a.qscale * sg[lane + HALF];
+          u0 = u0 * rs * gn[lane];
+          u1 = u1 * rs * gn[lane + HALF];
         }
-      } else {  // the key: smoothed, then quantized per row
-        const float k0 = lane < HALF ? __fdiv_rn(r0, sg[lane]) : 0.f;
-        const float k1 = lane < HALF ? __fdiv_rn(r1, sg[lane + HALF]) : 0.f;
-        const float sk = __fdiv_rn(wave_max(fmaxf(fabsf(k0), fabsf(k1)), lane), 127.f);
-        if (lane < HALF) {
-          kc[lane] = kv_code(k0, sk);
-          kc[lane + HALF] = kv_code(k1, sk);
+      }
+      float r0 = 0.f, r1 = 0.f;
+      if (lane < HALF) {
+        const float* cs = L.small + SM_ROPE + t * HD + lane * 2;
+        const float co = cs[0], si = cs[1];
+        r0 = u0 * co - u1 * si;
+        r1 = u1 * co + u0 * si;
+      }
+      if constexpr (KV8) {
+        const float* sg = L.small + SM_KSMOOTH;
+        if (u < G) {
+          if (lane < HALF) {
+            q[u * HD + lane] = r0 * a.qscale * sg[lane];
+            q[u * HD + lane + HALF] = r1 * a.qscale * sg[lane + HALF];
+          }
+        } else {  // the key: smoothed, then quantized per row
+          const float k0 = lane < HALF ? __fdiv_rn(r0, sg[lane]) : 0.f;
+          const float k1 = lane < HALF ? __fdiv_rn(r1, sg[lane + HALF]) : 0.f;
+          const float sk = __fdiv_rn(wave_max(fmaxf(fabsf(k0), fabsf(k1)), lane), 127.f);
+          if (lane < HALF) {
+            kc[lane] = kv_code(k0, sk);
+            kc[lane + HALF] = kv_code(k1, sk);
+          }
+          if (lane == 0) {
+            L.small[SM_KVCUR] = sk;
+            if (own_cur) kss[pos - slo] = sk;
+          }
         }
+      } else if (lane < HALF) {
+        if (u < G) {
+          q[(t * G + u) * HD + lane] = r0 * a.qscale;
+          q[(t * G + u) * HD + lane + HALF] = r1 * a.qscale;
+        } else {
+          kc[t * HD + lane] = bf16_round(r0);
+          kc[t * HD + lane + HALF] = bf16_round(r1);
+        }
+      }
+    } else if (wave_index == G + 1) {
+      if constexpr (KV8) {
+        constexpr int NV = (HD + 63) / 64;
+        float v[NV], am = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          v[i] = lane + 64 * i < HD ? raw[(G + 1) * HD + lane + 64 * i] : 0.f;
+          am = fmaxf(am, fabsf(v[i]));
+        }
+        const float sv = __fdiv_rn(wave_max(am, lane), 127.f);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (lane + 64 * i < HD) vc[lane + 64 * i] = kv_code(v[i], sv);
         if (lane == 0) {
-          L.small[SM_KVCUR] = sk;
-          if (own_cur) kss[pos - slo] = sk;
+          L.small[SM_KVCUR + 1] = sv;
+          if (own_cur) vss[pos - slo] = sv;
         }
-      }
-    } else if (lane < HALF) {
-      if (u < G) {
-        q[u * HD + lane] = r0 * a.qscale;
-        q[u * HD + lane + HALF] = r1 * a.qscale;
       } else {
-        kc[lane] = bf16_round(r0);
-        kc[lane + HALF] = bf16_round(r1);
+        for (int i = lane; i < HD; i += 64) vc[t * HD + i] = bf16_round(raw[(G + 1) * HD + i]);
       }
-    }
-  } else if (wave_index == G + 1) {
-    if constexpr (KV8) {
-      constexpr int NV = (HD + 63) / 64;
-      float v[NV], am = 0.f;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        v[i] = lane + 64 * i < HD ? raw[(G + 1) * HD + lane + 64 * i] : 0.f;
-        am = fmaxf(am, fabsf(v[i]));
-      }
-      const float sv = __fdiv_rn(wave_max(am, lane), 127.f);
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (lane + 64 * i < HD) vc[lane + 64 * i] = kv_code(v[i], sv);
-      if (lane == 0) {
-        L.small[SM_KVCUR + 1] = sv;
-        if (own_cur) vss[pos - slo] = sv;
-      }
-    } else {
-      for (int i = lane; i < HD; i += 64) vc[i] = bf16_round(raw[(G + 1) * HD + i]);
     }
   }
 }
 
 // control wave, after barrier A: the split holding the current position writes its K/V row (the
-// tile of the KV head's first query heads, when the heads are spread over several tiles)
-template <int HD, int G, bool KV8>
+// tile of the KV head's first query heads, when the heads are spread over several tiles).  MT > 1:
+// the rows of the step's MT positions (L_att - MT .. L_att - 1), each by the split that holds it.
+template <int HD, int G, bool KV8, int MT = 1>
 __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds& L, int lane, int layer, int g, int sp,
                                  int qa, int64_t L_att) {
   if (qa != g * (a.n_heads / a.n_kv)) return;
-  const float* kc = L.part + G * HD;
-  const float* vc = kc + HD;
+  const float* kc0 = L.part + MT * G * HD;
+  const float* vc0 = kc0 + MT * HD;
   const int64_t ch = (L_att + a.S - 1) / a.S;
   const int64_t lo = (int64_t)sp * ch;
   const int64_t hi = lo + ch < L_att ? lo + ch : L_att;
-  const int64_t cur = L_att - 1;
-  if (KV8 && lo <= cur && cur < hi) {  // the interleaved codes, four per lane, and the two scales
-    const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
-    if (lane < HD / 2) {
-      // word `lane` of the row: group lane / 4 of 8 dimensions, its K codes in words 0-1, V in 2-3
-      const int grp = lane >> 2, part = lane & 3;
-      const float* c = (part < 2 ? kc : vc) + grp * 8 + (part & 1) * 4;
-      const uint32_t w = ((uint32_t)(uint8_t)(int8_t)(int)c[0]) | ((uint32_t)(uint8_t)(int8_t)(int)c[1] << 8) |
-                         ((uint32_t)(uint8_t)(int8_t)(int)c[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)c[3] << 24);
-      st_u32(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.kv_k) + row * HD * 2) + lane, w);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const float* kc = kc0 + t * HD;
+    const float* vc = vc0 + t * HD;
+    const int64_t cur = L_att - MT + t;
+    if (KV8 && lo <= cur && cur < hi) {  // the interleaved codes, four per lane, and the two scales
+      const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
+      if (lane < HD / 2) {
+        // word `lane` of the row: group lane / 4 of 8 dimensions, its K codes in words 0-1, V in 2-3
+        const int grp = lane >> 2, part = lane & 3;
+        const float* c = (part < 2 ? kc : vc) + grp * 8 + (part & 1) * 4;
+        const uint32_t w = ((uint32_t)(uint8_t)(int8_t)(int)c[0]) | ((uint32_t)(uint8_t)(int8_t)(int)c[1] << 8) |
+                           ((uint32_t)(uint8_t)(int8_t)(int)c[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)c[3] << 24);
+        st_u32(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.kv_k) + row * HD * 2) + lane, w);
+      }
+      if (lane == 0) {
+        st_u32(reinterpret_cast<uint32_t*>(a.kv_ks + row), __float_as_uint(L.small[SM_KVCUR]));
+        st_u32(reinterpret_cast<uint32_t*>(a.kv_vs + row), __float_as_uint(L.small[SM_KVCUR + 1]));
+      }
+    } else if (!KV8 && lo <= cur && cur < hi && lane < HD / 2) {
+      const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
+      const uint32_t kb = f32_to_bf16_bits(kc[2 * lane]) | (f32_to_bf16_bits(kc[2 * lane + 1]) << 16);
+      const uint32_t vb = f32_to_bf16_bits(vc[2 * lane]) | (f32_to_bf16_bits(vc[2 * lane + 1]) << 16);
+      st_u32(reinterpret_cast<uint32_t*>(a.kv_k + row * HD) + lane, kb);
+      st_u32(reinterpret_cast<uint32_t*>(a.kv_v + row * HD) + lane, vb);
     }
-    if (lane == 0) {
-      st_u32(reinterpret_cast<uint32_t*>(a.kv_ks + row), __float_as_uint(L.small[SM_KVCUR]));
-      st_u32(reinterpret_cast<uint32_t*>(a.kv_vs + row), __float_as_uint(L.small[SM_KVCUR + 1]));
-    }
-  } else if (!KV8 && lo <= cur && cur < hi && lane < HD / 2) {
-    const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
-    const uint32_t kb = f32_to_bf16_bits(kc[2 * lane]) | (f32_to_bf16_bits(kc[2 * lane + 1]) << 16);
-    const uint32_t vb = f32_to_bf16_bits(vc[2 * lane]) | (f32_to_bf16_bits(vc[2 * lane + 1]) << 16);
-    st_u32(reinterpret_cast<uint32_t*>(a.kv_k + row * HD) + lane, kb);
-    st_u32(reinterpret_cast<uint32_t*>(a.kv_v + row * HD) + lane, vb);
   }
 }
 
@@ -1312,7 +1435,7 @@ struct KvOpen {
   const uint8_t* vbase;
   uint32_t off[NP];
 };
-template <int HD, int NP, bool KV8>
+template <int HD, int NP, bool KV8, int MT = 1>
 __device__ __forceinline__ KvOpen<NP> kv_open(const KernelArgs& a, int layer, int g, int sp, int64_t L_att, int c,
                                              int lane) {
   constexpr int LPP = kv_lpp<HD, KV8>(), P = 64 / LPP;
@@ -1323,10 +1446,12 @@ __device__ __forceinline__ KvOpen<NP> kv_open(const KernelArgs& a, int layer, in
   o.kbase = kv_head_base<KV8>(a.kv_k, kvrow0, HD);
   o.vbase = kv_head_base<KV8>(a.kv_v, kvrow0, HD);
   const int cur = (int)L_att - 1, dummy = (int)a.kv_cap - 1;
+  const int cut = (int)L_att - MT;  // (MT > 1) the step's own positions, from cut on, come from LDS
 #pragma unroll
   for (int s = 0; s < NP; ++s) {
     const int j = r.wlo + s * P + pp;
-    const int jj = (j < r.whi && j != cur) ? j : dummy;
+    const bool real = MT == 1 ? (j < r.whi && j != cur) : (j < r.whi && j < cut);
+    const int jj = real ? j : dummy;
     o.off[s] = ((uint32_t)jj * LPP + dseg) * 16u;
   }
   return o;
@@ -1403,24 +1528,34 @@ __device__ __forceinline__ void unpack_kv(const u32x4 w, float* f) {
 // is the position's K scale times the dot product of the smoothed query (prepared in LDS) with the
 // K codes, and a V row contributes its codes times its scale times the weight; the split's scales
 // are staged in LDS.
-template <int HD, int G, int B, int NB, bool KV8, typename After>
+// MT > 1 (multi-token steps): MT * G query rows (row t * G + h: head h at position t of the step);
+// the ring covers the cached positions (before the step's first), and each of the step's own
+// positions (K/V rows in LDS) is added, by the wave whose range holds it, to the rows at that
+// position or later (causal).
+template <int HD, int G, int B, int NB, bool KV8, int MT, typename After>
 __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds& L, int k, int c, int lane, int layer,
                                                   int g, int sp, int64_t L_att, Stream<B, NB>& pf, After after,
                                                   uint64_t* ts) {
   constexpr int PS = pstride<HD>();
   constexpr int D = NB * B / 2;  // ring slots: register pairs in the NB * B stream registers
   constexpr int SPB = B / 2;     // slots per batch of stream registers
+  constexpr int GM = G * MT;     // query rows
   const float* q = L.part;
-  const float* kc = q + G * HD;
-  const float* vc = kc + HD;
-  float* ws = attn_ws<HD, G>(L);
+  const float* kc = q + GM * HD;
+  const float* vc = kc + MT * HD;
+  float* ws = attn_ws<HD, G, MT>(L);
   const int cur = (int)L_att - 1;
+  const int cut = (int)L_att - MT;  // first position of the step
   const int64_t kvrow0 = ((int64_t)layer * a.n_kv + g) * a.kv_cap;
   constexpr int LPP = HD / 8;  // lanes per position
   constexpr int P = 64 / LPP;  // positions per load
   const AttnRange rg = attn_range(a, sp, c, L_att);
   const int wlo = rg.wlo, whi = rg.whi;
-  const int ngroups = whi > wlo ? (whi - wlo + P - 1) / P : 0;
+  // the ring's positions: the whole range (MT = 1: the current position is masked in it), or
+  // (MT > 1) the range's cached positions
+  const int whr = MT == 1 ? whi : (whi < cut ? whi : cut);
+  const int curr = MT == 1 ? cur : -1;
+  const int ngroups = whr > wlo ? (whr - wlo + P - 1) / P : 0;
   const int pp = lane / LPP, dseg = lane % LPP;
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   const __amdgpu_buffer_rsrc_t rk = rsrc(kv_head_base<KV8>(a.kv_k, kvrow0, HD));
@@ -1431,9 +1566,9 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   // Running state per query head: m[h] is the same in every lane (the largest score the wave has
   // seen so far, base 2); l[h] and acc[h][] are this lane's sums over its positions, weighted
   // by 2^(score - m[h]).
-  float m[G], l[G], acc[G][8];
+  float m[GM], l[GM], acc[GM][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < GM; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
 #pragma unroll
@@ -1463,7 +1598,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   // rescale the sums to it
   auto raise = [&](const float* bm) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GM; ++h) {
       const float mn = fmaxf(m[h], pos_max(bm[h]));
       const float al = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[h] - mn);
       l[h] *= al;
@@ -1480,7 +1615,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 #pragma unroll
     for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GM; ++h) {
       const float p = valid ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
       l[h] += p;
       const float pv = KV8 ? p * sv : p;
@@ -1515,7 +1650,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   };
   auto slot_load = [&](int s, int j) {
     if constexpr (KV8) load_kv8<HD>(rk, j, whi, cur, dummy, dseg, pf.v[2 * s]);
-    else load_kv<HD>(rk, rv, j, whi, cur, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
+    else load_kv<HD>(rk, rv, j, whr, curr, dummy, dseg, pf.v[2 * s], pf.v[2 * s + 1]);
   };
   if (pf.k != k) {  // no prefetch (e.g. this worker had no tile in the previous wave): fill the ring now
 #pragma unroll
@@ -1531,15 +1666,15 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   auto pass = [&](int g0, bool last) {
 #pragma unroll
     for (int s0 = 0; s0 < D; s0 += SUB) {
-      float sc[SUB][G], bm[G], svs[SUB];
+      float sc[SUB][GM], bm[GM], svs[SUB];
       bool valid[SUB];
 #pragma unroll
-      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
+      for (int h = 0; h < GM; ++h) bm[h] = -INFINITY;
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
         const int s = s0 + t;
         const int j = wlo + (g0 + s) * P + pp;
-        valid[t] = j < whi && j != cur;
+        valid[t] = j < whr && j != curr;
         float ks = 1.f;
         svs[t] = 1.f;
         if constexpr (KV8) {  // the row's scales (a slot without a position reads the split's first)
@@ -1550,7 +1685,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
         float kf[8];
         slot_k(s, kf);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < GM; ++h) {
           sc[t][h] = KV8 ? ks * score(kf, h) : score(kf, h);
           bm[h] = valid[t] ? fmaxf(bm[h], sc[t][h]) : bm[h];
         }
@@ -1576,7 +1711,35 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   int g0 = 0;
   for (; g0 + D < ngroups; g0 += D) pass(g0, false);
   pass(g0, true);
-  if (wlo <= cur && cur < whi) {  // the current position (its K/V row, or its codes, in LDS): lane group 0
+  if constexpr (MT > 1) {
+    // the step's positions (K/V rows in LDS), lane group 0: position u of the step reaches the
+    // rows of positions u and later only
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      const int pu = cut + u;
+      if (wlo <= pu && pu < whi) {
+        float kf[8], vf[8], sc[GM], bm[GM];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kf[e] = kc[u * HD + dseg * 8 + e];
+          vf[e] = pp == 0 ? vc[u * HD + dseg * 8 + e] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          sc[h] = score(kf, h);
+          bm[h] = pp == 0 && u <= h / G ? sc[h] : -INFINITY;
+        }
+        raise(bm);
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          const float p = pp == 0 && u <= h / G ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+      }
+    }
+  } else if (wlo <= cur && cur < whi) {  // the current position (its K/V row, or its codes, in LDS): lane group 0
     float kf[8], vf[8], sc[G], bm[G];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1597,7 +1760,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   auto sum_lanes = [&](auto off_tag) {
     constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GM; ++h) {
       l[h] += lane_xor<OFF>(l[h], lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] += lane_xor<OFF>(acc[h][e], lane);
@@ -1608,8 +1771,8 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   sum_lanes(std::integral_constant<int, 32>{});
   if (pp == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* st = ws + (c * G + h) * PS;
+    for (int h = 0; h < GM; ++h) {
+      float* st = ws + (c * GM + h) * PS;
       if (dseg == 0) {
         st[0] = m[h];
         st[1] = l[h];
@@ -1622,18 +1785,19 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
 
 // all wavefronts, between barriers B and E: merge the compute waves' states in wave order into
 // the tile's partial (m, l, acc, pad) per query head
-template <int HD, int G>
+template <int HD, int G, int MT = 1>
 __device__ __forceinline__ void attn_merge_phase(const Lds& L, int wave_index, int lane) {
   constexpr int PS = pstride<HD>();
-  const float* ws = attn_ws<HD, G>(L);
-  float* mrg = attn_merged<HD, G>(L);
-  for (int idx = wave_index * 64 + lane; idx < G * HD; idx += BLOCK_THREADS) {
+  constexpr int GM = G * MT;  // query rows
+  const float* ws = attn_ws<HD, G, MT>(L);
+  float* mrg = attn_merged<HD, G, MT>(L);
+  for (int idx = wave_index * 64 + lane; idx < GM * HD; idx += BLOCK_THREADS) {
     const int h = idx / HD, d = idx % HD;
     // every compute wave's state of head h (independent loads), then one common maximum
     float mv[NCOMP], lv[NCOMP], av[NCOMP];
 #pragma unroll
     for (int c = 0; c < NCOMP; ++c) {
-      const float* st = ws + (c * G + h) * PS;
+      const float* st = ws + (c * GM + h) * PS;
       mv[c] = st[0];
       lv[c] = st[1];
       av[c] = st[2 + d];
@@ -1660,19 +1824,26 @@ __device__ __forceinline__ void attn_merge_phase(const Lds& L, int wave_index, i
 }
 
 // control wave, after barrier E: publish the merged partials of query heads qa .. qa + G - 1, split sp
-template <int HD, int G>
+// (MT > 1: the rows of position t of the step go to out + t * ll_tok)
+template <int HD, int G, int MT = 1>
 __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& L, uint32_t* out, int lane, int qa, int sp,
                                 uint32_t par) {
   constexpr int PS = pstride<HD>();
-  constexpr int N = (G * PS + 63) / 64;  // values per lane
-  const float* mrg = attn_merged<HD, G>(L);
+  constexpr int GM = G * MT;  // query rows
+  constexpr int N = (GM * PS + 63) / 64;  // values per lane
+  const float* mrg = attn_merged<HD, G, MT>(L);
   float v[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = lane + 64 * i < G * PS ? mrg[lane + 64 * i] : 0.f;  // reads first, then the stores
+  for (int i = 0; i < N; ++i) v[i] = lane + 64 * i < GM * PS ? mrg[lane + 64 * i] : 0.f;  // reads first, then the stores
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int idx = lane + 64 * i;
-    if (idx < G * PS) publish(out, ((int64_t)(qa + idx / PS) * a.S + sp) * PS + idx % PS, v[i], par);
+    if constexpr (MT == 1) {
+      if (idx < G * PS) publish(out, ((int64_t)(qa + idx / PS) * a.S + sp) * PS + idx % PS, v[i], par);
+    } else if (idx < GM * PS) {
+      const int r = idx / PS, t = r / G;
+      publish(out + t * a.ll_tok, ((int64_t)(qa + r - t * G) * a.S + sp) * PS + idx % PS, v[i], par);
+    }
   }
 }
 
@@ -1686,11 +1857,17 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP, bool KV8>
+// MT > 1 (multi-token steps): the inputs of every position tp of the step, position tp's in
+// vec + tp * lds_vec_floats (xres + tp * XS, part + tp * S * (HD + 4) for split partials) from the
+// producer's buffer of that position (ll_tok words after the previous one's); the step's tokens
+// are the given ones (verify), and the previous step's argmaxes are recorded.
+template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP, bool KV8, int MT = 1>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
   constexpr int PS = pstride<HD>();
+  static_assert(MT == 1 || (!SMP && !KV8), "multi-token steps are greedy verify steps with the BF16 cache");
+  const int VS = a.lds_vec_floats, XS = (a.Hpad + 63) & ~63;
   const int layer = wd.layer;
   const uint32_t* in = a.ll + (k > 0 ? wave_of(L, k - 1).ll_off : 0);
   // Every worker gathers x in the QKV and gate/up waves, tile or not: the o_proj and down
@@ -1705,7 +1882,9 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
                            : gk == KIND_GU ? gain_off(L, layer, 1)
                                            : a.final_norm_off;
       const uint16_t* gain = reinterpret_cast<const uint16_t*>(a.packed + goff);
-      float ss = 0.f;
+      float ss[MT];
+#pragma unroll
+      for (int tp = 0; tp < MT; ++tp) ss[tp] = 0.f;
       bool ctrl_pads = false;  // the control wavefront alone zeroes the input's padding (after its LDS use)
       if (gk == KIND_QKV && layer == 0) {
         if (SMP && step > 0) {
@@ -1723,20 +1902,47 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
             }
           }
         } else if (CTRL && step > 0) {
-          ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
-          if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
-          if (!ab && a.forced) tok = a.forced[step - 1];  // a verify step: the given token, not the argmax
+          if constexpr (MT == 1) {
+            ab = gather_token<WD>(a, lane, step_parity(step - 1), tok);
+            if (!ab && bid == 0 && lane == 0) a.out_tokens[step - 1] = tok;
+            if (!ab && a.forced) tok = a.forced[step - 1];  // a verify step: the given token, not the argmax
+          } else {
+#pragma unroll
+            for (int tp = 0; tp < MT; ++tp) {
+              int am = 0;
+              if (!ab) ab = gather_token<WD>(a, lane, step_parity(step - 1), am, tp);
+              if (!ab && bid == 0 && lane == 0) a.out_tokens[(step - 1) * MT + tp] = am;
+            }
+          }
         }
-        if (CTRL && !ab) ss = stage_embedding<Q8>(a, L, tok, gain, lane);
+        if (CTRL && !ab) {
+          if constexpr (MT == 1) {
+            ss[0] = stage_embedding<Q8>(a, L.vec, L.xres, tok, gain, lane);
+          } else {
+#pragma unroll
+            for (int tp = 0; tp < MT; ++tp) {
+              const int i = step * MT + tp;  // position of the launch
+              ss[tp] = stage_embedding<Q8>(a, L.vec + tp * VS, L.xres + tp * XS, i == 0 ? a.token0 : a.forced[i - 1], gain,
+                                           lane);
+            }
+          }
+        }
+      } else if constexpr (MT == 1) {
+        ab = gather_norm<WD, Q8>(a, L.vec, L.xres, in, a.H, gain, wave, lane, par, ss[0]);
       } else {
-        ab = gather_norm<WD, Q8>(a, L, in, a.H, gain, wave, lane, par, ss);
+        ab = gather_norm_mt<WD, Q8, MT>(a, L.vec, L.xres, VS, XS, in, a.H, gain, wave, lane, par, ss);
       }
       if (!ctrl_pads) {
-        for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp)
+          for (int i = a.H + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[tp * VS + vperm<Q8>(i)] = 0.f;
       } else if (CTRL) {  // (the candidates the control wavefront polled also covered the padding)
         for (int i = a.H + lane; i < t.kpad; i += 64) L.vec[vperm<Q8>(i)] = 0.f;
       }
-      if (lane == 0) L.small[SM_SS + wave] = ss;
+      if (lane == 0) {
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp) L.small[sm_ss(tp) + wave] = ss[tp];
+      }
       break;
     }
     case KIND_O:
@@ -1757,19 +1963,30 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
         n = a.S * PS;
         nz = t.kpad;  // no GEMV input to pad
       }
-      ab = gather_plain<WD, Q8>(a, dst, src, n, wave, lane, par, dst == L.vec);
-      for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[vperm<Q8>(i)] = 0.f;
+      if constexpr (MT == 1) {
+        ab = gather_plain<WD, Q8>(a, dst, src, n, wave, lane, par, dst == L.vec);
+      } else {
+        const int dstride = dst == L.vec ? VS : a.S * PS;  // (COMBINE: one head's partials per position)
+        ab = gather_plain_mt<WD, Q8, MT>(a, dst, dstride, src, n, wave, lane, par, dst == L.vec);
+      }
+#pragma unroll
+      for (int tp = 0; tp < MT; ++tp)
+        for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[tp * VS + vperm<Q8>(i)] = 0.f;
       break;
     }
     case KIND_ATTN: {
       // the control wave also stages the current position's RoPE row and the q/k-norm gains;
       // the loads are issued before the poll and complete while it waits for the producers
       constexpr int HALF = HD / 2;
-      float2 cs = {0.f, 0.f};
+      float2 cs[MT];
       float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;
       const int64_t qoff = gain_off(L, layer, 2);
+#pragma unroll
+      for (int tp = 0; tp < MT; ++tp) cs[tp] = {0.f, 0.f};
       if (CTRL && lane < HALF) {
-        cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(a.pos0 + step) * HALF + lane) * 2);
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp)
+          cs[tp] = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(a.pos0 + step * MT + tp) * HALF + lane) * 2);
         if (qoff >= 0) {
           const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.packed + qoff);
           const uint16_t* gkk = reinterpret_cast<const uint16_t*>(a.packed + gain_off(L, layer, 3));
@@ -1807,11 +2024,15 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           }
         }
       }
-      ab = gather_qkv<HD, G, WD>(a, L, in, t.row0, t.aux0, wave, lane, par);
+      if constexpr (MT == 1) ab = gather_qkv<HD, G, WD>(a, L.vec, in, t.row0, t.aux0, wave, lane, par);
+      else ab = gather_qkv_mt<HD, G, WD, MT>(a, L.vec, VS, in, t.row0, t.aux0, wave, lane, par);
       if constexpr (KV8) wait_vmcnt<0>();  // the staged scales are in LDS before the tile's barrier
       if (CTRL && lane < HALF) {
-        L.small[SM_ROPE + 2 * lane] = cs.x;
-        L.small[SM_ROPE + 2 * lane + 1] = cs.y;
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp) {
+          L.small[SM_ROPE + tp * HD + 2 * lane] = cs[tp].x;
+          L.small[SM_ROPE + tp * HD + 2 * lane + 1] = cs[tp].y;
+        }
         L.small[SM_QGAIN + lane] = gq0;
         L.small[SM_QGAIN + lane + HALF] = gq1;
         L.small[SM_KGAIN + lane] = gk0;
@@ -1836,8 +2057,17 @@ __device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileD
   return t.kind == KIND_ATTN || t.kind == KIND_COMBINE || (t.kind == KIND_O && a.combine_in_o);
 }
 
-// LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale.
-template <int HD, int G, bool Q8, bool KV8>
+// The folded RMSNorm scale of position tp of the step (after barrier P).
+__device__ __forceinline__ float norm_scale(const KernelArgs& a, const Lds& L, int tp) {
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) tot += L.small[sm_ss(tp) + w];
+  return 1.0f / sqrtf(tot / (float)a.H + a.eps);
+}
+
+// LDS-only prologue work between barriers P and A; returns the folded RMSNorm scale (of the step's
+// first position; MT > 1: norm_scale gives the others).  pos: the step's first position.
+template <int HD, int G, bool Q8, bool KV8, int MT = 1>
 __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L, int wave, int lane,
                                               const TileDesc& t, int layer, int pos) {
   float rs = 1.0f;
@@ -1847,10 +2077,14 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     for (int w = 0; w < NWAVES; ++w) tot += L.small[SM_SS + w];
     rs = 1.0f / sqrtf(tot / (float)a.H + a.eps);
   } else if (t.kind == KIND_ATTN) {
-    attn_lds_prep<HD, G, KV8>(a, L, wave, lane, layer, pos, t.nrows);
+    attn_lds_prep<HD, G, KV8, MT>(a, L, wave, lane, layer, pos, t.nrows);
   } else if ((t.kind == KIND_O && a.combine_in_o) || t.kind == KIND_COMBINE) {
     // all heads' splits (o_proj prologue) or one head's (combine tile): one copy of the merge
-    merge_heads<HD, Q8>(L.part, t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane, L.vec, t.kind == KIND_O);
+    // (MT > 1: combine tiles only, one merge per position of the step)
+#pragma unroll
+    for (int tp = 0; tp < MT; ++tp)
+      merge_heads<HD, Q8>(L.part + tp * a.S * pstride<HD>(), t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane,
+                          L.vec + tp * a.lds_vec_floats, t.kind == KIND_O);
   }
   return rs;
 }
@@ -1887,7 +2121,10 @@ __device__ __forceinline__ void put_scales(const Lds& L, const TileDesc& t, int 
   }
 }
 
-template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
+// MT > 1 (multi-token steps): each step runs positions pos0 + step * MT .. + MT - 1; every epilogue
+// runs once per position (its partials at part + tp * block_rows * NCOMP, its outputs at out + tp *
+// ll_tok), and the LM head publishes one (max, index) partial per position (lmpart + tp * W).
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8, int MT = 1>
 __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, int bid, int lane, int block_rows) {
   // The abort word lives in LDS and is written and read only on either side of a barrier (which
   // orders them), so plain accesses: the compiler then emits LDS instructions.  A volatile access
@@ -1896,13 +2133,19 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
   int* smi = reinterpret_cast<int*>(L.small);
   int tok = a.token0;
   const int H = a.H;
+  const int VS = a.lds_vec_floats, XS = (a.Hpad + 63) & ~63, PT = block_rows * NCOMP;
   bool stop = false;
   for (int step = 0; step < a.n_steps && !stop; ++step) {
     const uint32_t par = step_parity(step);
-    const int pos = a.pos0 + step;
-    const int64_t L_att = (int64_t)pos + 1;
-    float lm_best = -INFINITY;
-    int lm_idx = 0x7fffffff;
+    const int pos = a.pos0 + step * MT;  // the step's first position
+    const int64_t L_att = (int64_t)pos + MT;
+    float lm_best[MT];
+    int lm_idx[MT];
+#pragma unroll
+    for (int tp = 0; tp < MT; ++tp) {
+      lm_best[tp] = -INFINITY;
+      lm_idx[tp] = 0x7fffffff;
+    }
     uint64_t lm_run = 0;  // sampled decoding: lane i holds this worker's i-th largest logit so far
     for (int k = 0; k < a.n_waves; ++k) {
       const TileDesc t = tile_of(L, k);
@@ -1916,7 +2159,7 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
       const uint64_t* cts = reinterpret_cast<const uint64_t*>(L.small + SM_CTRACE) + (k & 1) * 8;
       if (a.trace) t0 = wall_clock64();
       float sreg[SCALE_REGS];
-      if (gather_inputs<HD, G, true, WD, Q8, SMP, KV8>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, true, WD, Q8, SMP, KV8, MT>(a, L, bid, 0, lane, k, t, wd, step, par, tok)) smi[SM_ABORT] = 1;
       __syncthreads();  // P: inputs staged in LDS
       if (smi[SM_ABORT]) {
         stop = true;
@@ -1928,7 +2171,11 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         if (is_gemv(t.kind)) load_scales(a, t, 0, block_rows, lane, sreg);
       }
       if (a.trace) t_pro = wall_clock64();
-      const float rs = lds_prologue<HD, G, Q8, KV8>(a, L, 0, lane, t, layer, pos);
+      float rs[MT];
+      rs[0] = lds_prologue<HD, G, Q8, KV8, MT>(a, L, 0, lane, t, layer, pos);
+#pragma unroll
+      for (int tp = 1; tp < MT; ++tp)
+        rs[tp] = t.kind == KIND_QKV || t.kind == KIND_GU || t.kind == KIND_LM ? norm_scale(a, L, tp) : 1.0f;
       if (needs_barrier_a(a, t)) __syncthreads();  // A: inputs ready
       const uint64_t t_a = a.trace ? wall_clock64() : 0;
       if (is_gemv(t.kind)) {
@@ -1937,8 +2184,8 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         for (int r0 = 0; r0 < rows; r0 += block_rows) {
           const int nr = min(block_rows, rows - r0);
           // a row's total over the compute wavefronts' partials, times its scale in an INT8 tile
-          auto total = [&](int r) {
-            const float x = row_total(L, nr, C, r);
+          auto total = [&](const float* part, int r) {
+            const float x = row_total(part, nr, C, r);
             return Q8 ? L.scl[r] * x : x;
           };
           if constexpr (Q8) {
@@ -1951,63 +2198,70 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
             for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
             for (int w = 1; w < NWAVES; ++w) t_last = wds[w] > t_last ? wds[w] : t_last;
           }
-          switch (t.kind) {
-            case KIND_QKV:
-              for (int r = lane; r < nr; r += 64) publish(out, t.row0 + r0 + r, rs * total(r), par);
-              break;
-            case KIND_O:
-              for (int r = lane; r < nr; r += 64) {
-                const int j = t.row0 + r0 + r;
-                publish(out, j, L.xres[j] + total(r), par);
-              }
-              break;
-            case KIND_GU:  // interleaved gate/up rows
-              for (int p = lane; p < nr / 2; p += 64) {
-                const float gt = rs * total(2 * p);
-                const float up = rs * total(2 * p + 1);
-                publish(out, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
-              }
-              break;
-            case KIND_DOWN:
-              for (int r = lane; r < nr; r += 64) {
-                const int j = t.row0 + r0 + r;
-                const float nx = L.xres[j] + total(r);
-                publish(out, j, nx, par);
-                if (a.dbg_hidden) a.dbg_hidden[((int64_t)step * a.n_layers + layer) * H + j] = tag_clear(nx);
-              }
-              break;
-            case KIND_LM:
-              if constexpr (SMP) {
-                uint64_t cand[ROWS_PER_LANE];  // this lane's rows of the block, r = lane + 64 j
 #pragma unroll
-                for (int j = 0; j < ROWS_PER_LANE; ++j) {
-                  const int r = lane + 64 * j;
-                  cand[j] = 0;
-                  if (r < nr) {
-                    const float v = rs * total(r);
-                    const int idx = t.row0 + r0 + r;
-                    if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
-                    cand[j] = cand_key(v, idx);
+          for (int tp = 0; tp < MT; ++tp) {  // (the step's positions)
+            uint32_t* o = out + tp * a.ll_tok;
+            const float* pa = L.part + tp * PT;
+            const float* xr = L.xres + tp * XS;
+            const int64_t srow = (int64_t)step * MT + tp;  // position of the launch
+            switch (t.kind) {
+              case KIND_QKV:
+                for (int r = lane; r < nr; r += 64) publish(o, t.row0 + r0 + r, rs[tp] * total(pa, r), par);
+                break;
+              case KIND_O:
+                for (int r = lane; r < nr; r += 64) {
+                  const int j = t.row0 + r0 + r;
+                  publish(o, j, xr[j] + total(pa, r), par);
+                }
+                break;
+              case KIND_GU:  // interleaved gate/up rows
+                for (int p = lane; p < nr / 2; p += 64) {
+                  const float gt = rs[tp] * total(pa, 2 * p);
+                  const float up = rs[tp] * total(pa, 2 * p + 1);
+                  publish(o, t.row0 + r0 / 2 + p, gt / (1.0f + __expf(-gt)) * up, par);
+                }
+                break;
+              case KIND_DOWN:
+                for (int r = lane; r < nr; r += 64) {
+                  const int j = t.row0 + r0 + r;
+                  const float nx = xr[j] + total(pa, r);
+                  publish(o, j, nx, par);
+                  if (a.dbg_hidden) a.dbg_hidden[(srow * a.n_layers + layer) * H + j] = tag_clear(nx);
+                }
+                break;
+              case KIND_LM:
+                if constexpr (SMP) {
+                  uint64_t cand[ROWS_PER_LANE];  // this lane's rows of the block, r = lane + 64 j
+#pragma unroll
+                  for (int j = 0; j < ROWS_PER_LANE; ++j) {
+                    const int r = lane + 64 * j;
+                    cand[j] = 0;
+                    if (r < nr) {
+                      const float v = rs[tp] * total(pa, r);
+                      const int idx = t.row0 + r0 + r;
+                      if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + srow * a.V + idx);
+                      cand[j] = cand_key(v, idx);
+                    }
+                  }
+                  topk_merge(lm_run, cand, a.top_k, lane);
+                  break;
+                }
+                for (int r = lane; r < nr; r += 64) {
+                  const float v = rs[tp] * total(pa, r);
+                  const int idx = t.row0 + r0 + r;
+                  if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + srow * a.V + idx);
+                  if (v > lm_best[tp]) {  // each lane visits its rows in increasing order: first maximum kept
+                    lm_best[tp] = v;
+                    lm_idx[tp] = idx;
                   }
                 }
-                topk_merge(lm_run, cand, a.top_k, lane);
                 break;
-              }
-              for (int r = lane; r < nr; r += 64) {
-                const float v = rs * total(r);
-                const int idx = t.row0 + r0 + r;
-                if (a.out_logits) __builtin_nontemporal_store(v, a.out_logits + (int64_t)step * a.V + idx);
-                if (v > lm_best) {  // each lane visits its rows in increasing order: first maximum kept
-                  lm_best = v;
-                  lm_idx = idx;
-                }
-              }
-              break;
+            }
           }
           if (r0 + block_rows < rows) __syncthreads();  // C: partials consumed
         }
       } else if (t.kind == KIND_ATTN) {
-        cw_attn_kv_write<HD, G, KV8>(a, L, lane, layer, t.row0, t.nrows, t.aux0, L_att);
+        cw_attn_kv_write<HD, G, KV8, MT>(a, L, lane, layer, t.row0, t.nrows, t.aux0, L_att);
         // The KV row must be complete before this worker publishes anything later readers of
         // the row depend on (its split partial, below); the wait overlaps the compute waves.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -2018,12 +2272,14 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
           for (int i = 0; i < TS_COUNT; ++i) cw[i] = cts[i];
           for (int w = 1; w < NWAVES; ++w) t_last = wds[w] > t_last ? wds[w] : t_last;
         }
-        attn_merge_phase<HD, G>(L, 0, lane);
+        attn_merge_phase<HD, G, MT>(L, 0, lane);
         __syncthreads();  // E: merged partial ready
-        cw_attn_publish<HD, G>(a, L, out, lane, t.aux0, t.nrows, par);
+        cw_attn_publish<HD, G, MT>(a, L, out, lane, t.aux0, t.nrows, par);
       } else if (t.kind == KIND_COMBINE) {
         if (a.trace) t_cmp = wall_clock64();
-        for (int d = lane; d < HD; d += 64) publish(out, (int64_t)t.row0 * HD + d, L.vec[d], par);
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp)
+          for (int d = lane; d < HD; d += 64) publish(out + tp * a.ll_tok, (int64_t)t.row0 * HD + d, L.vec[tp * VS + d], par);
       }
       if (SMP && wd.kind == KIND_LM) {
         // this worker's top_k candidates in decreasing order, lane i the i-th ((-inf, 0x7fffffff) where
@@ -2036,17 +2292,22 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         if (lane == 0) st_u64_release(dst, word);
       } else if (wd.kind == KIND_LM) {
         // worker partial (max, lowest index); also published by workers without vocabulary rows
-        for (int off = 32; off >= 1; off >>= 1) {
-          const float ov = __shfl_xor(lm_best, off);
-          const int oi = __shfl_xor(lm_idx, off);
-          if (ov > lm_best || (ov == lm_best && oi < lm_idx)) {
-            lm_best = ov;
-            lm_idx = oi;
+#pragma unroll
+        for (int tp = 0; tp < MT; ++tp) {
+          float best = lm_best[tp];
+          int bi = lm_idx[tp];
+          for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(best, off);
+            const int oi = __shfl_xor(bi, off);
+            if (ov > best || (ov == best && oi < bi)) {
+              best = ov;
+              bi = oi;
+            }
           }
+          if (lane == 0)
+            st_u64_release(reinterpret_cast<uint64_t*>(a.lmpart) + (int64_t)tp * a.W + bid,
+                           (uint64_t)__float_as_uint(best) | ((uint64_t)((uint32_t)bi | (par << 31)) << 32));
         }
-        if (lane == 0)
-          st_u64_release(reinterpret_cast<uint64_t*>(a.lmpart) + bid,
-                 (uint64_t)__float_as_uint(lm_best) | ((uint64_t)((uint32_t)lm_idx | (par << 31)) << 32));
       }
       if (a.trace && lane == 0) {
         const uint64_t t1 = wall_clock64();
@@ -2076,7 +2337,12 @@ __device__ __forceinline__ void control_loop(const KernelArgs& a, const Lds& L, 
         if (lane == 0) a.out_tokens[a.n_steps - 1] = last;
       }
     } else {
-      if (!gather_token<WD>(a, lane, step_parity(a.n_steps - 1), last) && lane == 0) a.out_tokens[a.n_steps - 1] = last;
+      bool ab = false;
+#pragma unroll
+      for (int tp = 0; tp < MT; ++tp) {
+        if (!ab) ab = gather_token<WD>(a, lane, step_parity(a.n_steps - 1), last, tp);
+        if (!ab && lane == 0) a.out_tokens[(a.n_steps - 1) * MT + tp] = last;
+      }
     }
   }
 }
@@ -2095,7 +2361,7 @@ constexpr int stream_sets() {
   return 2;
 }
 
-template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8, int MT = 1>
 __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, int bid, int wave, int lane,
                                              int block_rows) {
   constexpr int B = STREAM_BATCH;
@@ -2124,8 +2390,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
   bool stop = false;
   for (int step = 0; step < a.n_steps && !stop; ++step) {
     const uint32_t par = step_parity(step);
-    const int pos = a.pos0 + step;
-    const int64_t L_att = (int64_t)pos + 1;
+    const int pos = a.pos0 + step * MT;  // the step's first position
+    const int64_t L_att = (int64_t)pos + MT;
     for (int k = 0; k < a.n_waves; ++k) {
       const TileDesc t = tile_of(L, k);
       const WaveDesc wd = wave_of(L, k);
@@ -2147,7 +2413,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
       const bool one_block = block_rows >= rows;
       const Range nr_first0 = !one_block ? block_range(sd, k, block_rows, block_rows, c) : next_attn ? no_range() : ng0;
       const bool kv_first0 = one_block && next_attn;
-      KvOpen<NP> ko = kv_open<HD, NP, KV8>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
+      KvOpen<NP> ko = kv_open<HD, NP, KV8, MT>(a, layer, tn.row0, tn.nrows, L_att, c, lane);
       Range ng = ng0, r_first = r_first0, nr_first = nr_first0;
       int kv_first = kv_first0;
       pin(ng);
@@ -2175,7 +2441,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }
-      if (gather_inputs<HD, G, false, WD, Q8, SMP, KV8>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused)) smi[SM_ABORT] = 1;
+      if (gather_inputs<HD, G, false, WD, Q8, SMP, KV8, MT>(a, L, bid, wave, lane, k, t, wd, step, par, tok_unused))
+        smi[SM_ABORT] = 1;
       stamp(ts, TS_GATHERED, lane);
       __syncthreads();  // P
       if (smi[SM_ABORT]) {
@@ -2183,7 +2450,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         break;
       }
       if (needs_barrier_a(a, t)) {
-        lds_prologue<HD, G, Q8, KV8>(a, L, wave, lane, t, layer, pos);
+        lds_prologue<HD, G, Q8, KV8, MT>(a, L, wave, lane, t, layer, pos);
         __syncthreads();  // A
       }
       stamp(ts, TS_AFTER_A, lane);
@@ -2197,10 +2464,10 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
                              : next_attn ? no_range()
                                          : ng;
             const bool kv_next = r0 == 0 ? kv_first : last_block && next_attn;
-            stream_range<B, NB, Q8>(
+            stream_range<B, NB, Q8, MT>(
                 L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
                 [&](int h) { return select_src<B>(kv_next, kv_half_src<B, NP>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
-                stage_w, r0 == 0 ? ts : nullptr);
+                stage_w, r0 == 0 ? ts : nullptr, a.lds_vec_floats, block_rows * NCOMP);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
             if (r0 == 0) stamp(ts, TS_DONE, lane);
@@ -2210,7 +2477,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
           if (r0 + block_rows < rows) __syncthreads();  // C
         }
       } else if (t.kind == KIND_ATTN) {
-        compute_attention<HD, G, B, NB, KV8>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&](int h) {
+        compute_attention<HD, G, B, NB, KV8, MT>(a, L, k, c, lane, layer, t.row0, t.nrows, L_att, st, [&](int h) {
           load_gemv_batch<B>(st.v + h * B, a.packed, ng, h, lane);
         }, ts);
         st.k = ng.k;
@@ -2218,7 +2485,7 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         stamp(ts, TS_DONE, lane);
         if (wdone && lane == 0) *wdone = wall_clock64();
         __syncthreads();  // B
-        attn_merge_phase<HD, G>(L, wave, lane);
+        attn_merge_phase<HD, G, MT>(L, wave, lane);
         __syncthreads();  // E
       }
     }
@@ -2231,14 +2498,16 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
 // Q8: weight-only INT8 GEMV tiles (INT8 codes, per-row FP32 scales); else BF16 weights.
 // SMP: sampled decoding (top-k / top-p draw from every worker's candidates); else greedy.
 // KV8: INT8 KV cache (codes, per-position scales, smoothed keys); else BF16 rows.
-template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8>
+// MT: positions per step (1 decode; 2 .. MAX_STEP_TOKENS: teacher-forced verify steps whose tiles
+// run all MT positions, each weight stream serving them all).
+template <int HD, int G, bool WD, bool Q8, bool SMP, bool KV8, int MT = 1>
 __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const KernelArgs& a = args;
   Lds L;
   L.stage = reinterpret_cast<float*>(lds_raw);
   L.vec = L.stage + a.lds_stage_floats;
-  L.part = L.vec + a.lds_vec_floats;
+  L.part = L.vec + MT * a.lds_vec_floats;  // (lds_vec_floats per position of the step)
   L.xres = L.part + a.lds_part_floats;
   L.scl = L.xres + (Q8 ? a.lds_xres_floats - MAX_BLOCK_ROWS : 0);  // (INT8 plans reserve a block's scales there)
   L.small = L.xres + a.lds_xres_floats;
@@ -2283,9 +2552,9 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   }
   __syncthreads();
   if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
-  const int block_rows = (a.lds_part_floats / NCOMP) & ~1;
-  if (wave == 0) control_loop<HD, G, WD, Q8, SMP, KV8>(a, L, bid, lane, block_rows);
-  else compute_loop<HD, G, WD, Q8, SMP, KV8>(a, L, bid, wave, lane, block_rows);
+  const int block_rows = (a.lds_part_floats / (NCOMP * MT)) & ~1;  // (MT > 1: a block's partials per position)
+  if (wave == 0) control_loop<HD, G, WD, Q8, SMP, KV8, MT>(a, L, bid, lane, block_rows);
+  else compute_loop<HD, G, WD, Q8, SMP, KV8, MT>(a, L, bid, wave, lane, block_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -2542,6 +2811,21 @@ const void* worker_for(int head_dim, int group) {
   }
   return nullptr;
 }
+// The multi-token (verify-plan) worker for a head size, query heads per attention tile and positions
+// per step, greedy with the BF16 cache: query rows (group x positions) at most MAX_GROUP, and one
+// RoPE row per position in the small LDS area (positions x head_dim <= 256).
+template <bool Q8>
+const void* worker_mt_for(int head_dim, int group, int mt) {
+  if (head_dim == 64) {
+    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 2>);
+    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, false, false, 2>);
+    if (mt == 4 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 4>);
+  } else if (head_dim == 128) {
+    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, false, 2>);
+    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, false, false, 2>);
+  }
+  return nullptr;
+}
 #else
 // (defined by the worker units; variant: INT8 weights * 4 + sampled * 2 + INT8 KV)
 const void* worker_unit_0(int head_dim, int group);
@@ -2553,6 +2837,8 @@ const void* worker_unit_5(int head_dim, int group);
 const void* worker_unit_6(int head_dim, int group);
 const void* worker_unit_7(int head_dim, int group);
 const void* worker_watchdog(int head_dim);
+const void* worker_mt_unit_0(int head_dim, int group, int mt);  // BF16 weights
+const void* worker_mt_unit_1(int head_dim, int group, int mt);  // INT8 weights
 
 const void* worker_unit(int variant, int head_dim, int group) {
   switch (variant) {
@@ -2568,10 +2854,15 @@ const void* worker_unit(int variant, int head_dim, int group) {
   return nullptr;
 }
 
-// The worker for a head size, query heads per attention tile, weight format, token selection and
-// KV format; `short_watchdog` selects the test instantiation whose waits check their watchdog every
-// polling round (BF16 weights and KV, greedy, one query head per tile only).
-const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8) {
+// The worker for a head size, query heads per attention tile, weight format, token selection, KV
+// format and positions per step; `short_watchdog` selects the test instantiation whose waits check
+// their watchdog every polling round (BF16 weights and KV, greedy, one query head per tile, one
+// position per step only).
+const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8, int mt) {
+  if (mt > 1) {
+    if (short_watchdog || sampled || kv8) return nullptr;
+    return q8 ? worker_mt_unit_1(head_dim, group, mt) : worker_mt_unit_0(head_dim, group, mt);
+  }
   if (short_watchdog) return group == 1 && !q8 && !sampled && !kv8 ? worker_watchdog(head_dim) : nullptr;
   return worker_unit((q8 ? 4 : 0) + (sampled ? 2 : 0) + (kv8 ? 1 : 0), head_dim, group);
 }

@@ -52,6 +52,9 @@ constexpr int STREAM_DEPTH = 2 * STREAM_BATCH;
 // Up to this many further batches of a compute wavefront's next GEMV range are staged in its LDS
 // area by direct-to-LDS loads issued with the register prefetch (as many as the LDS holds).
 constexpr int MAX_STAGE_BATCHES = 2;
+// Verify plans: positions per step at most (each GEMV tile streams its weights once for all of them;
+// the step's input vectors are held in LDS side by side).
+constexpr int MAX_STEP_TOKENS = 4;
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;  // polling rounds before a wait gives up (watchdog)
 constexpr int32_t MAX_POSITIONS = 1 << 23;
 // Sampled decoding (top-k / top-p): each worker publishes its top_k largest logits, at most this many.
@@ -171,8 +174,11 @@ struct KernelArgs {
   int32_t top_k;             // 0: greedy; 1 .. MAX_TOP_K: sampled (top-k, temperature, top-p)
   float temperature;
   float top_p;
-  const int32_t* forced;     // [n_steps - 1] or null: step s > 0 consumes forced[s - 1] (verify steps); the
-                             // argmax is still recorded in out_tokens
+  const int32_t* forced;     // [n_steps * mt - 1] or null: position i > 0 of the launch consumes forced[i - 1]
+                             // (verify steps); the argmax is still recorded in out_tokens
+  int32_t mt;                // positions per step: 1 (decode), or 2 .. MAX_STEP_TOKENS (verify plans: every
+                             // step runs mt consecutive teacher-forced positions through each tile)
+  int64_t ll_tok;            // words between the tagged buffers of consecutive positions of a step
 };
 
 }  // namespace tiles

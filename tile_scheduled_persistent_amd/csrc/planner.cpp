@@ -127,7 +127,7 @@ uint64_t plan_checksum(const HostPlan& p) {
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
                           p.stage_batches, p.top_k, (int64_t)float_bits(p.temperature), (int64_t)float_bits(p.top_p),
-                          p.kv8};
+                          p.kv8, p.mt};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -153,6 +153,16 @@ std::vector<uint64_t> worker_table_hashes(const HostPlan& p) {
     out[w] = h;
   }
   return out;
+}
+
+// Multi-token plans: GEMV row blocks of at least this many rows (their partials are held per position).
+constexpr int32_t MIN_MT_BLOCK_ROWS = 64;
+
+// LDS floats of an attention tile's work areas: q[mt * T][hd], kc[mt][hd], vc[mt][hd], the compute
+// waves' states [NCOMP][mt * T][hd + 4] and the merged partial [mt * T][hd + 4].
+static int64_t attn_lds_floats(const HostPlan& p) {
+  const int64_t rows = (int64_t)p.mt * p.T, hd = p.s.hd;
+  return rows * hd + 2 * p.mt * hd + (NCOMP + 1) * rows * (hd + 4);
 }
 
 int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::string& err) {
@@ -199,6 +209,18 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (cfg.kv_format != KVFMT_BF16 && cfg.kv_format != KVFMT_INT8)
     return fail(err, TILES_E_CONFIG, "kv_format must be 0 (BF16) or 1 (INT8)");
   p.kv8 = cfg.kv_format == KVFMT_INT8;
+  // verify plans: every step runs tokens_per_step consecutive teacher-forced positions through each
+  // tile (one weight stream for all of them)
+  if (cfg.tokens_per_step < 0 || cfg.tokens_per_step == 3 || cfg.tokens_per_step > MAX_STEP_TOKENS)
+    return fail(err, TILES_E_CONFIG, "tokens_per_step must be 0, 1, 2 or 4");
+  p.mt = cfg.tokens_per_step > 1 ? cfg.tokens_per_step : 1;
+  if (p.mt > 1 && (cfg.top_k > 0 || p.kv8))
+    return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps with the BF16 KV cache");
+  if (p.mt > 1 && (cfg.flags & TILES_TRACE)) return fail(err, TILES_E_CONFIG, "multi-token steps are not traced");
+  if (p.mt > 1 && p.mt * cfg.head_dim > 256)
+    return fail(err, TILES_E_CONFIG, "tokens_per_step x head_dim above 256 (one RoPE row per position in LDS)");
+  if (p.mt > 1 && cfg.combine_mode == 1)
+    return fail(err, TILES_E_CONFIG, "multi-token steps merge the KV splits in a wave of their own (combine_mode 0 or 2)");
   p.top_k = cfg.top_k;
   p.temperature = cfg.top_k > 0 ? cfg.temperature : 1.0f;
   p.top_p = cfg.top_k > 0 ? cfg.top_p : 1.0f;
@@ -221,20 +243,24 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
     p.T = cfg.attn_heads;
     if (s.G % p.T != 0) return fail(err, TILES_E_CONFIG, "attn_heads must divide n_heads / n_kv_heads");
   } else {
-    p.T = s.G;
+    // the first divisor whose tiles fit the workers, else the largest (then rejected below); multi-token
+    // steps: at most MAX_GROUP query rows per tile, heads x positions
+    p.T = 0;
     for (int32_t t = 1; t <= s.G; ++t)
-      if (s.G % t == 0 && (int64_t)s.n_kv * (s.G / t) * std::max(p.S, 1) <= W) {
+      if (s.G % t == 0 && t * p.mt <= MAX_GROUP) {
         p.T = t;
-        break;
+        if ((int64_t)s.n_kv * (s.G / t) * std::max(p.S, 1) <= W) break;
       }
   }
+  if (p.T * p.mt > MAX_GROUP)
+    return fail(err, TILES_E_CONFIG, "attn_heads x tokens_per_step exceeds 4 query rows per attention tile");
   if (p.S < 1 || (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads * (query heads per KV head / attn_heads) exceeds workers");
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
   if (cfg.o_placement < 0 || cfg.o_placement > 2) return fail(err, TILES_E_CONFIG, "o_placement must be 0, 1 or 2");
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
-  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES ? 1 : 0;
+  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES && p.mt == 1 ? 1 : 0;
   else return fail(err, TILES_E_CONFIG, "combine_mode must be 0, 1 or 2");
 
   // ---- packed layout: norm gains first, then the GEMV waves in execution order ----
@@ -481,13 +507,28 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // ---- LDS sizing ----
   // vec: GEMV input vector, or the raw q/k/v of an attention tile
   int32_t vec = std::max({s.Hpad, s.Qpad, s.Fpad, (s.G + 2) * s.hd});
-  // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS)
+  // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS).
+  // Multi-token steps (mt positions): mt input vectors, mt residual rows and mt partials per row, in
+  // blocks of as many rows as the LDS holds beside the other areas and one staging batch (at least
+  // MIN_MT_BLOCK_ROWS); attention tiles hold mt x T query rows and mt K/V rows.
+  const int32_t mt = p.mt;
+  const int64_t tables_bytes = round_up((int64_t)p.waves.size() * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) +
+                                                                             sizeof(WaveDesc)) +
+                                            (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
+  int32_t brows = MAX_BLOCK_ROWS;
+  if (mt > 1) {
+    const int64_t other_floats = (int64_t)mt * round_up(vec, 64) + mt * round_up(s.Hpad, 64) +
+                                 (p.q8 ? MAX_BLOCK_ROWS : 0) + SMALL_FLOATS;
+    const int64_t room = (LDS_LIMIT - other_floats * 4 - tables_bytes - (int64_t)NCOMP * STREAM_BATCH * CHUNK_BYTES) /
+                         (4 * (int64_t)NCOMP * mt);
+    brows = (int32_t)(std::max<int64_t>(MIN_MT_BLOCK_ROWS, std::min<int64_t>(MAX_BLOCK_ROWS, room)) & ~1);
+  }
   int32_t part = 0;
-  for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, MAX_BLOCK_ROWS) * NCOMP);
+  for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, brows) * NCOMP * mt);
   // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
   const int32_t ps = s.hd + 4;
-  part = std::max(part, p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * ps + (p.kv8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0));
-  part = std::max(part, p.S * ps);                                  // one head's splits (combine tile)
+  part = std::max(part, (int32_t)attn_lds_floats(p) + (p.kv8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0));
+  part = std::max(part, mt * p.S * ps);                             // one head's splits (combine tile)
   if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
@@ -496,11 +537,9 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   const int64_t cand_floats = ((int64_t)p.W * p.top_k + 1) / 2 * 4;
   if (p.top_k > 0 && p.lds_vec_floats + p.lds_part_floats < cand_floats)
     p.lds_part_floats = (int32_t)round_up(cand_floats - p.lds_vec_floats, 64);
-  p.lds_xres_floats = (int32_t)round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0);  // (INT8: then a block's scales)
+  p.lds_xres_floats = mt * (int32_t)round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0);  // (INT8: then a block's scales)
   // schedule tables: per wave a SegDesc, this worker's TileDesc and the WaveDesc; per layer a LayerSmall
-  p.lds_bytes = (p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 +
-                (int32_t)round_up((int64_t)p.waves.size() * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
-                                      (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
+  p.lds_bytes = (mt * p.lds_vec_floats + p.lds_part_floats + p.lds_xres_floats + SMALL_FLOATS) * 4 + (int32_t)tables_bytes;
   if (p.lds_bytes > LDS_LIMIT) return fail(err, TILES_E_CONFIG, "LDS demand exceeds 160 KB");
   // staging areas for the next GEMV range's chunks, as many batches per compute wave as fit
   const int32_t stage_batch_bytes = NCOMP * STREAM_BATCH * CHUNK_BYTES;
@@ -901,8 +940,12 @@ int validate_plan(const HostPlan& p, std::string& err) {
     // the KV write happens in the split holding L-1; the kernel makes that split write
   }
 
+  // multi-token steps
+  if (p.mt != 1 && p.mt != 2 && p.mt != 4) return fail(err, TILES_E_PLAN, "tokens per step must be 1, 2 or 4");
+  if (p.mt > 1 && (p.combine_in_o || p.top_k > 0 || p.kv8 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
+    return fail(err, TILES_E_PLAN, "multi-token plan with an unsupported option");
   // LDS capacity for every wave's staging
-  if (p.lds_part_floats / NCOMP < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
+  if (p.lds_part_floats / (NCOMP * p.mt) < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
   if (p.stage_batches < 0 || p.stage_batches > MAX_STAGE_BATCHES ||
       p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT ||
       p.lds_stage_floats * 4 > 65536)
@@ -910,8 +953,10 @@ int validate_plan(const HostPlan& p, std::string& err) {
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
   if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
-  if ((int64_t)p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
-  if (p.lds_xres_floats < s.Hpad) return fail(err, TILES_E_PLAN, "LDS residual area too small");
+  if ((int64_t)p.mt * p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
+  if (attn_lds_floats(p) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for an attention tile");
+  if (p.lds_xres_floats < p.mt * round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0))
+    return fail(err, TILES_E_PLAN, "LDS residual area too small");
   if (p.kv8) {
     const int64_t np = (s.max_positions + p.S - 1) / p.S;
     if (np > MAX_SPLIT_POSITIONS_KV8) return fail(err, TILES_E_PLAN, "INT8 KV: a split longer than 2048 positions");

@@ -52,7 +52,7 @@ class Config(ctypes.Structure):
         ("attn_heads", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("stream", ctypes.c_void_p),
         ("o_placement", ctypes.c_int32), ("weight_format", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
-        ("kv_format", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("tokens_per_step", ctypes.c_int32),
     ]
 
 
@@ -80,7 +80,7 @@ class PlanInfo(ctypes.Structure):
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
         ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("top_k", ctypes.c_int32),
-        ("kv_format", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("tokens_per_step", ctypes.c_int32),
     ]
 
 
@@ -169,14 +169,17 @@ KV_FORMATS = {"bf16": 0, "int8": 1}
 
 def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: int = 0, combine_mode: int = 0,
                 n_workers: int = 0, stream: Optional[int] = None, attn_heads: int = 0, o_placement: int = 0,
-                weights: str = "bf16", sampling: Optional[tuple] = None, kv: str = "bf16") -> Config:
+                weights: str = "bf16", sampling: Optional[tuple] = None, kv: str = "bf16",
+                tokens_per_step: int = 0) -> Config:
     """``sampling`` = (temperature, top_k, top_p) makes a sampling plan (tiles_decode_sampled);
-    ``kv`` = "int8" an INT8 KV plan (see KVCache.int8)."""
+    ``kv`` = "int8" an INT8 KV plan (see KVCache.int8); ``tokens_per_step`` = 2 or 4 a verify plan
+    (tiles_verify only) whose steps take that many positions through every tile at once."""
     temperature, top_k, top_p = sampling if sampling is not None else (1.0, 0, 1.0)
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
                   float(m.rms_eps), int(m.qk_norm), int(m.tie_embeddings), int(max_positions), int(flags),
                   int(kv_splits), int(combine_mode), int(attn_heads), int(n_workers), stream, int(o_placement),
-                  WEIGHTS[weights], int(top_k), float(temperature), float(top_p), KV_FORMATS[kv])
+                  WEIGHTS[weights], int(top_k), float(temperature), float(top_p), KV_FORMATS[kv],
+                  int(tokens_per_step))
 
 
 def dry_run(m: ModelConfig, max_positions: int, n_workers: int = 256, **kw) -> PlanInfo:
@@ -284,13 +287,13 @@ class Plan:
     def __init__(self, m: ModelConfig, weights: Dict, max_positions: int, flags: int = 0, kv_splits: int = 0,
                  combine_mode: int = 0, stream: Optional[torch.cuda.Stream] = None, attn_heads: int = 0,
                  o_placement: int = 0, weight_format: str = "bf16", sampling: Optional[tuple] = None,
-                 kv_format: str = "bf16"):
+                 kv_format: str = "bf16", tokens_per_step: int = 0):
         self.model = m
         self.sampling = sampling
         self.kv_format = kv_format
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._cfg = make_config(m, max_positions, flags, kv_splits, combine_mode, 0, self.stream.cuda_stream,
-                                attn_heads, o_placement, weight_format, sampling, kv_format)
+                                attn_heads, o_placement, weight_format, sampling, kv_format, tokens_per_step)
         on_device = weights["embed"].is_cuda
         layers = (LayerWeights * m.n_layers)()
         for i, d in enumerate(weights["layers"]):
@@ -363,10 +366,10 @@ class Plan:
 
     def verify(self, kv: KVCache, tokens: Sequence[int], out_argmax: Optional[torch.Tensor] = None,
                out_logits: Optional[torch.Tensor] = None):
-        """A greedy verify step (tiles_verify): ``tokens`` = [last accepted token, draft 1, ...].
-        Synchronizes the device and returns (argmax int64 [m], accepted count n, verified tokens
-        [n + 1]: the accepted drafts, then the argmax after them); kv.length becomes its value before
-        the call + n + 1."""
+        """A greedy verify step (tiles_verify): ``tokens`` = [last accepted token, draft 1, ...]
+        (a verify plan: a multiple of its tokens_per_step).  Synchronizes the device and returns
+        (argmax int64 [m], accepted count n, verified tokens [n + 1]: the accepted drafts, then the
+        argmax after them); kv.length becomes its value before the call + n + 1."""
         tokens = [int(t) for t in tokens]
         m = len(tokens)
         if out_argmax is None:
