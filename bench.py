@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
     ap.add_argument("--verify-tokens", type=int, default=0,
                     help="also time greedy verify steps of this many tokens (added to the line as 'verify')")
+    ap.add_argument("--trace-plan-tokens", type=int, default=0,
+                    help="with --trace-report: trace a verify plan of this many positions per step (2 or 4) running "
+                         "the workload's greedy continuation as drafts, instead of the decode launch")
     ap.add_argument("--verify-plan-tokens", type=int, default=0,
                     help="with --verify-tokens: time them with a verify plan taking this many positions per step "
                          "through every tile (2 or 4; 0: the decode plan, one position per step)")
@@ -286,13 +289,13 @@ def main():
                                kv_format=wl.kv, stream=stream, tokens_per_step=args.verify_plan_tokens)
         result["verify"] = _verify_timing(vplan, kv, wl, token, out_t, args, stream)
         if vplan is not plan:
-            result["verify"]["plan"] = {"positions_per_step": vplan.info().tokens_per_step,
-                                        "waves_per_step": vplan.info().waves_per_step,
-                                        "combine": "own wave"}
+            vi = vplan.info()
+            result["verify"]["plan"] = {"positions_per_step": vi.tokens_per_step, "waves_per_step": vi.waves_per_step,
+                                        "combine": "o_proj prologue" if vi.combine_mode == 1 else "own wave"}
             vplan.close()
 
     if args.trace_report:
-        _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info)
+        _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info, out_t)
 
     if not args.no_cpu_baseline:
         w_bits = synth.weights_as_bits(w)
@@ -355,16 +358,19 @@ def _verify_timing(plan, kv, wl, token, out_t, args, stream):
                    "plan's stream"}
 
 
-def _trace_report(path, m, wl, w, k0, v0, token, args, info):
-    """Per-wave timing from the in-kernel trace (separate launch)."""
+def _trace_report(path, m, wl, w, k0, v0, token, args, info, drafts):
+    """Per-wave timing from the in-kernel trace (separate launch).  With --trace-plan-tokens T: a verify
+    plan of T positions per step verifying the workload's greedy continuation (``drafts``); its times
+    per kernel step then cover T positions."""
     import numpy as np
     import torch
 
     from tile_scheduled_persistent_amd import tiles
 
+    T = args.trace_plan_tokens
     plan = tiles.Plan(m, w, wl.capacity, flags=tiles.TILES_TRACE, kv_splits=args.kv_splits, attn_heads=args.attn_heads,
                       combine_mode=args.combine_mode, o_placement=args.o_placement, weight_format=wl.weights,
-                      sampling=wl.sampling, kv_format=wl.kv)
+                      sampling=wl.sampling, kv_format=wl.kv, tokens_per_step=T)
     if wl.kv == "int8":
         kv = tiles.KVCache.convert_int8(plan, k0, v0, wl.n_cached)
     else:
@@ -372,7 +378,11 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
     out_t = torch.zeros(wl.n_steps, dtype=torch.int32, device="cuda")
     from tile_scheduled_persistent_amd import synth
     uniforms = torch.from_numpy(synth.make_uniforms(m, wl.n_steps)).cuda() if wl.sampling is not None else None
-    plan.decode(kv, token, wl.n_steps, out_t, None, uniforms=uniforms)
+    if T > 1:
+        n = wl.n_steps - wl.n_steps % T
+        plan.verify(kv, [int(token)] + [int(t) for t in drafts[:n - 1].cpu().tolist()])
+    else:
+        plan.decode(kv, token, wl.n_steps, out_t, None, uniforms=uniforms)
     _, tr = plan.read_debug(hidden=False, trace=True)
     waves = plan.waves()
     plan.close()
@@ -402,7 +412,8 @@ def _trace_report(path, m, wl, w, k0, v0, token, args, info):
              "# prologue = LDS prologue (P -> A); cw1 = first compute wavefront's own work after A (max over workers);",
              "# setup = its A -> streaming loop entry; first = loop entry -> first batch consumed (max over workers);",
              "# lastw = A -> last compute wavefront done; ctlB = A -> control wavefront ready for B (attention)",
-             f"# workload: {wl.description}; steps traced: {steps}; waves per step: {nw}",
+             f"# workload: {wl.description}; steps traced: {steps}; waves per step: {nw}" +
+             (f"; a verify plan, {T} positions per step (times per step)" if T > 1 else ""),
              "wave\tkind\tlayer\tMB\tdur_us\tGB/s\tedge_us\twait_us\tcompute_us\tpublish_us\tprologue_us\tcw1_us\tsetup_us\tfirst_us\tlastw_us\tctlB_us"]
     sl = slice(1, None) if steps > 2 else slice(None)  # the first step includes the launch ramp
     tot = 0.0

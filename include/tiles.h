@@ -108,9 +108,9 @@ typedef struct tiles_config {
    * teacher-forced positions through each tile, so that each GEMV tile streams its weights once for
    * all of them (its LDS holds one input vector per position) and each attention tile serves all of
    * them with one pass over the cached rows, the step's own rows entering the positions at or after
-   * them.  Needs greedy selection (top_k = 0), the BF16 KV cache, no TILES_TRACE, splits merged in a
+   * them.  Needs greedy selection (top_k = 0), the BF16 KV cache, splits merged in a
    * wave of their own (combine_mode 0 or 2), tokens_per_step x head_dim <= 256, and query heads per
-   * attention tile x tokens_per_step <= 4 (the planner lowers its choice of attn_heads to fit).  The
+   * attention tile x tokens_per_step <= 4 (the planner's choice of attn_heads keeps to that).  The
    * LDS must hold tokens_per_step input vectors of max(hidden, ffn) floats (padded); plan creation
    * fails with TILES_E_CONFIG otherwise. */
   int32_t tokens_per_step;
@@ -313,7 +313,8 @@ int tiles_plan_status(tiles_plan_t *plan);
 
 /* Copy debug buffers to host memory after synchronizing the plan's stream.
  *   hidden : host float [n_steps_of_last_decode][n_layers][H] or NULL (needs TILES_DEBUG_HIDDEN);
- *   trace  : host uint64 [n_steps][waves_per_step][n_workers][12] or NULL (needs TILES_TRACE),
+ *   trace  : host uint64 [n_steps / tokens_per_step][waves_per_step][n_workers][12] or NULL (needs
+ *            TILES_TRACE; one record per kernel step, which a verify plan runs per tokens_per_step positions),
  *            100 MHz wall-clock ticks per (step, wave, worker): 0 wave start, 1 inputs staged,
  *            2 compute done, 3 outputs published, 7 after the LDS prologue (control wavefront);
  *            5 own gather done, 6 after the LDS prologue, 9 streaming loop entered, 8 first
@@ -322,7 +323,7 @@ int tiles_plan_status(tiles_plan_t *plan);
  *            tiles); 11 the last compute wavefront's share done (GEMV and attention tiles),
  *            10 the control wavefront ready for barrier B after its KV-row write (attention
  *            tiles, else 0).
- *   *n_steps_out receives the step count of the last decode. */
+ *   *n_steps_out receives the position count of the last decode or verify call. */
 int tiles_read_debug(tiles_plan_t *plan, float *hidden, uint64_t *trace, int32_t *n_steps_out);
 
 /* Test hook: corrupt one byte of the host copy of the schedule so that the next

@@ -312,19 +312,33 @@ def test_int8_kv_format_and_split_limits_rejected():
 @pytest.mark.parametrize("m,pos,mt", [(LLAMA_1B, 1087, 2), (QWEN3_06B, 1087, 2), (QWEN3_4B, 1087, 2), (TINY, 80, 2),
                                       (TINY, 80, 4)], ids=["llama1b-2", "qwen06b-2", "qwen4b-2", "tiny-2", "tiny-4"])
 def test_verify_plans_validate(m, pos, mt):
-    """A verify plan merges the splits in a wave of its own (one more wave per layer than a plan whose
-    o_proj prologue merges them), holds at most 4 query rows per attention tile, fits the LDS, records
-    its positions per step, and is not the decode plan's schedule."""
+    """A verify plan holds at most 4 query rows per attention tile, fits the LDS, records its positions
+    per step, merges the splits in the o_proj prologue or in a wave of its own (one more per layer),
+    and is not the decode plan's schedule."""
     info = tiles.dry_run(m, pos, tokens_per_step=mt)
     dec = tiles.dry_run(m, pos)
     assert info.tokens_per_step == mt and dec.tokens_per_step == 1
-    assert info.combine_mode == 2
-    assert info.waves_per_step == m.n_layers * 6 + 1
+    assert info.waves_per_step == m.n_layers * (5 if info.combine_mode == 1 else 6) + 1
     assert info.attn_heads * mt <= 4
     assert info.lds_bytes <= 160 * 1024
     assert info.checksum != dec.checksum
     cfg = tiles.make_config(m, pos, tokens_per_step=mt)
     assert tiles.lib().tiles_plan_debug_validate(ctypes.byref(cfg), 256, 0) == tiles.TILES_OK, tiles.last_error()
+
+
+def test_verify_plan_split_merge_placement():
+    """The o_proj prologue merges the splits of every position where the input and partial areas hold
+    mt * (Qpad + n_heads * S * (head_dim + 4)) floats beside the rest and one staging batch (the
+    Llama-3.2-1B shape at 2 positions, 5 splits); the Qwen3 shapes merge in a wave of their own.  Forced,
+    the prologue merge fits the Qwen3-0.6B shape without staging and not the Qwen3-4B shape; a forced own
+    wave is honoured."""
+    assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=2).combine_mode == 1
+    assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=2, combine_mode=2).combine_mode == 2
+    for m in (QWEN3_06B, QWEN3_4B):
+        assert tiles.dry_run(m, 1087, tokens_per_step=2).combine_mode == 2
+    assert tiles.dry_run(QWEN3_06B, 1087, tokens_per_step=2, combine_mode=1).combine_mode == 1
+    with pytest.raises(tiles.TilesError):
+        tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, combine_mode=1)
 
 
 def test_verify_plans_bound_the_heads_per_attention_tile():
@@ -341,8 +355,8 @@ def test_verify_plans_bound_the_heads_per_attention_tile():
 
 @pytest.mark.parametrize("kw", [dict(tokens_per_step=3), dict(tokens_per_step=8), dict(tokens_per_step=-1),
                                 dict(tokens_per_step=2, sampling=(1.0, 4, 1.0)), dict(tokens_per_step=2, kv="int8"),
-                                dict(tokens_per_step=2, flags=tiles.TILES_TRACE), dict(tokens_per_step=2, combine_mode=1)],
-                         ids=["three", "eight", "negative", "sampled", "int8-kv", "traced", "merge-in-o-proj"])
+                                dict(tokens_per_step=2, combine_mode=3)],
+                         ids=["three", "eight", "negative", "sampled", "int8-kv", "bad-combine-mode"])
 def test_verify_plan_options_rejected(kw):
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(TINY, 80, **kw)
@@ -357,3 +371,15 @@ def test_verify_plan_limits():
             tiles.dry_run(m, 1087, tokens_per_step=4)
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=0).tokens_per_step == 1
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=1).checksum == tiles.dry_run(LLAMA_1B, 1087).checksum
+
+
+def test_long_gemv_tiles_in_int8_and_sampling_plans_rejected():
+    """The kernel's INT8 scales and sampled candidates cover 640 rows of a GEMV block: with a 200,000-word
+    vocabulary the LM-head tiles hold 782 rows while the row blocks of these plans may be longer, so
+    INT8 and sampling plans are rejected (a greedy BF16 plan is fine)."""
+    big = scaled(LLAMA_1B, name="bigvocab", vocab=200000)
+    assert tiles.dry_run(big, 1100).lds_bytes > 0
+    for kw in (dict(weights="int8"), dict(sampling=(1.0, 8, 1.0))):
+        with pytest.raises(tiles.TilesError) as e:
+            tiles.dry_run(big, 1100, **kw)
+        assert e.value.code == tiles.TILES_E_PLAN and "640 rows" in tiles.last_error()

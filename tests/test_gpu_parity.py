@@ -884,7 +884,10 @@ def test_verify_of_sixty_four_positions_to_capacity():
 # verify plans: tokens_per_step consecutive positions through every tile per step
 # ---------------------------------------------------------------------------------------------
 
-VERIFY_PLANS = [("tiny", 2, "bf16"), ("tiny", 4, "bf16"), ("wide", 2, "bf16"), ("wide", 2, "int8")]
+# (shape, positions per step, weights, combine_mode: 0 planner choice -- the o_proj prologue for these
+# shapes -- or 2, the splits merged in a wave of their own)
+VERIFY_PLANS = [("tiny", 2, "bf16", 0), ("tiny", 4, "bf16", 0), ("wide", 2, "bf16", 0), ("wide", 2, "int8", 0),
+                ("wide", 2, "bf16", 2), ("tiny", 4, "bf16", 2)]
 
 
 def _verify_plan_case(s, plan, tag, tokens, pos, check_hidden=True):
@@ -915,26 +918,27 @@ def _verify_plan_case(s, plan, tag, tokens, pos, check_hidden=True):
     return a, n, stats
 
 
-@pytest.mark.parametrize("shape,mt,weights", VERIFY_PLANS, ids=[f"{a}-{b}-{c}" for a, b, c in VERIFY_PLANS])
-def test_verify_plan_against_the_oracle(shape, mt, weights):
-    """A verify plan (mt positions per step through every tile, BF16 or INT8 weights), drafts the
-    decode plan's greedy continuation, whole or with a wrong token at position 3 or 8: every position
-    against the oracle teacher-forced on the same tokens, the written K/V rows, and the acceptance
-    against the oracle's."""
+@pytest.mark.parametrize("shape,mt,weights,combine", VERIFY_PLANS,
+                         ids=[f"{a}-{b}-{c}-c{d}" for a, b, c, d in VERIFY_PLANS])
+def test_verify_plan_against_the_oracle(shape, mt, weights, combine):
+    """A verify plan (mt positions per step through every tile, BF16 or INT8 weights, the splits merged
+    in the o_proj prologue or in a wave of their own), drafts the decode plan's greedy continuation,
+    whole or with a wrong token at position 3 or 8: every position against the oracle teacher-forced
+    on the same tokens, the written K/V rows, and the acceptance against the oracle's."""
     mdl = TINY if shape == "tiny" else WIDE
     s = Setup(mdl, 96, 60, weights=weights)
     tok = synth.make_tokens(mdl, 1)[0]
     m = 12
     with s.plan() as dplan:
         _, g, _ = _greedy_continuation(s, dplan, tok, m)
-    with s.plan(tokens_per_step=mt) as plan:
+    with s.plan(tokens_per_step=mt, combine_mode=combine) as plan:
         info = plan.info()
-        assert info.tokens_per_step == mt and info.combine_mode == 2
+        assert info.tokens_per_step == mt and info.combine_mode == (combine or 1)
         for j in (None, 3, 8):
             drafts = list(g[:m - 1])
             if j is not None:
                 drafts[j - 1] = (g[j - 1] + 7) % mdl.vocab
-            tag = f"{shape} mt={mt} {weights} j={j}"
+            tag = f"{shape} mt={mt} {weights} combine={info.combine_mode} j={j}"
             _, n, stats = _verify_plan_case(s, plan, tag, [tok] + drafts, 60)
             print(f"{tag}: accepted {n}; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs err "
                   f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}", flush=True)

@@ -674,7 +674,9 @@ int tiles_read_debug(tiles_plan_t* p, float* hidden, uint64_t* trace, int32_t* n
   }
   if (trace) {
     if (!p->trace) return set_err(TILES_E_ARG, "plan was created without TILES_TRACE");
-    HIP_TRY(hipMemcpy(trace, p->trace, (size_t)p->last_steps * hp.waves.size() * hp.W * TRACE_WORDS * sizeof(uint64_t),
+    // one record per kernel step (a verify plan's step runs hp.mt positions)
+    HIP_TRY(hipMemcpy(trace, p->trace,
+                      (size_t)(p->last_steps / hp.mt) * hp.waves.size() * hp.W * TRACE_WORDS * sizeof(uint64_t),
                       hipMemcpyDeviceToHost));
   }
   return TILES_OK;

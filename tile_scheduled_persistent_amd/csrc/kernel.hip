@@ -1953,10 +1953,12 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       float* dst = L.vec;
       const uint32_t* src = in;
       int n = a.F, nz = a.F;
+      int vs = VS;  // (MT > 1) floats between the positions' GEMV inputs
       if (gk == KIND_O) {
-        dst = a.combine_in_o ? L.part : L.vec;
+        dst = a.combine_in_o ? o_partials<HD, MT>(a, L) : L.vec;
         n = a.combine_in_o ? a.n_heads * a.S * PS : a.n_heads * HD;
         nz = a.n_heads * HD;
+        vs = o_in_stride<MT>(a);
       } else if (gk == KIND_COMBINE) {
         dst = L.part;
         src = in + (int64_t)t.row0 * a.S * PS;
@@ -1966,12 +1968,13 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       if constexpr (MT == 1) {
         ab = gather_plain<WD, Q8>(a, dst, src, n, wave, lane, par, dst == L.vec);
       } else {
-        const int dstride = dst == L.vec ? VS : a.S * PS;  // (COMBINE: one head's partials per position)
-        ab = gather_plain_mt<WD, Q8, MT>(a, dst, dstride, src, n, wave, lane, par, dst == L.vec);
+        // per position: the GEMV input (vs apart), or split partials (n apart)
+        const bool vin = gk != KIND_COMBINE && !(gk == KIND_O && a.combine_in_o);
+        ab = gather_plain_mt<WD, Q8, MT>(a, dst, vin ? vs : n, src, n, wave, lane, par, vin);
       }
 #pragma unroll
       for (int tp = 0; tp < MT; ++tp)
-        for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[tp * VS + vperm<Q8>(i)] = 0.f;
+        for (int i = nz + wave * 64 + lane; i < t.kpad; i += BLOCK_THREADS) L.vec[tp * vs + vperm<Q8>(i)] = 0.f;
       break;
     }
     case KIND_ATTN: {
@@ -2057,6 +2060,17 @@ __device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileD
   return t.kind == KIND_ATTN || t.kind == KIND_COMBINE || (t.kind == KIND_O && a.combine_in_o);
 }
 
+// Multi-token steps whose o_proj prologue merges the splits: the merged heads of position t are at
+// vec + t * Qpad (the o_proj tile's input stride), and the split partials of every position sit
+// after them (position t's n_heads * S records at vec + MT * Qpad + t * n_heads * S * (HD + 4),
+// running on into the partial area, which o_proj's compute wavefronts write only after barrier A).
+template <int MT>
+__device__ __forceinline__ int o_in_stride(const KernelArgs& a) { return MT > 1 && a.combine_in_o ? a.Qpad : a.lds_vec_floats; }
+template <int HD, int MT>
+__device__ __forceinline__ float* o_partials(const KernelArgs& a, const Lds& L) {
+  return MT > 1 ? L.vec + MT * a.Qpad : L.part;
+}
+
 // The folded RMSNorm scale of position tp of the step (after barrier P).
 __device__ __forceinline__ float norm_scale(const KernelArgs& a, const Lds& L, int tp) {
   float tot = 0.f;
@@ -2080,11 +2094,14 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     attn_lds_prep<HD, G, KV8, MT>(a, L, wave, lane, layer, pos, t.nrows);
   } else if ((t.kind == KIND_O && a.combine_in_o) || t.kind == KIND_COMBINE) {
     // all heads' splits (o_proj prologue) or one head's (combine tile): one copy of the merge
-    // (MT > 1: combine tiles only, one merge per position of the step)
+    // (MT > 1: one merge per position of the step)
+    const bool o = t.kind == KIND_O;
+    const int nh = o ? a.n_heads : 1;
+    const float* src = o ? o_partials<HD, MT>(a, L) : L.part;
+    const int ostride = o ? o_in_stride<MT>(a) : a.lds_vec_floats;
 #pragma unroll
     for (int tp = 0; tp < MT; ++tp)
-      merge_heads<HD, Q8>(L.part + tp * a.S * pstride<HD>(), t.kind == KIND_O ? a.n_heads : 1, a.S, wave * 64 + lane,
-                          L.vec + tp * a.lds_vec_floats, t.kind == KIND_O);
+      merge_heads<HD, Q8>(src + tp * nh * a.S * pstride<HD>(), nh, a.S, wave * 64 + lane, L.vec + tp * ostride, o);
   }
   return rs;
 }
@@ -2467,7 +2484,8 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
             stream_range<B, NB, Q8, MT>(
                 L, a.packed, r, c, lane, st, st.k == k && st.r0 == r0,
                 [&](int h) { return select_src<B>(kv_next, kv_half_src<B, NP>(ko, h), gemv_src<B>(a.packed, nr, h, lane)); },
-                stage_w, r0 == 0 ? ts : nullptr, a.lds_vec_floats, block_rows * NCOMP);
+                stage_w, r0 == 0 ? ts : nullptr, t.kind == KIND_O ? o_in_stride<MT>(a) : a.lds_vec_floats,
+                block_rows * NCOMP);
             st.k = kv_next ? k + 1 : nr.k;
             st.r0 = kv_next ? 0 : nr.r0;
             if (r0 == 0) stamp(ts, TS_DONE, lane);
@@ -2552,7 +2570,11 @@ __global__ void __launch_bounds__(BLOCK_THREADS, 1) tiles_worker(KernelArgs args
   }
   __syncthreads();
   if (reinterpret_cast<const int*>(L.small)[SM_ABORT]) return;
-  const int block_rows = (a.lds_part_floats / (NCOMP * MT)) & ~1;  // (MT > 1: a block's partials per position)
+  // rows per GEMV block: the partial area's worth (MT > 1: per position, at most MAX_BLOCK_ROWS).  The
+  // INT8 scale registers and the sampled candidates of a block hold MAX_BLOCK_ROWS rows: the plan
+  // validator rejects INT8 and sampling plans with a longer tile where blocks may be longer.
+  const int block_rows = MT > 1 ? min((a.lds_part_floats / (NCOMP * MT)) & ~1, MAX_BLOCK_ROWS)
+                                : (a.lds_part_floats / NCOMP) & ~1;
   if (wave == 0) control_loop<HD, G, WD, Q8, SMP, KV8, MT>(a, L, bid, lane, block_rows);
   else compute_loop<HD, G, WD, Q8, SMP, KV8, MT>(a, L, bid, wave, lane, block_rows);
 }

@@ -165,6 +165,33 @@ static int64_t attn_lds_floats(const HostPlan& p) {
   return rows * hd + 2 * p.mt * hd + (NCOMP + 1) * rows * (hd + 4);
 }
 
+// Floats of one position's GEMV input area (the largest input, or an attention tile's raw q/k/v).
+static int64_t vec_floats(const Shape& s) {
+  return round_up(std::max<int64_t>({s.Hpad, s.Qpad, s.Fpad, (int64_t)(s.G + 2) * s.hd}), 64);
+}
+
+// Multi-token plans whose o_proj prologue merges the splits keep the merged heads of the mt positions
+// at the start of the input area (Qpad apart) and every position's split partials after them, on
+// into the partial area: those two areas together must hold mt * (Qpad + n_heads * S * (hd + 4)).
+static int64_t mt_merge_floats(const HostPlan& p) {
+  return (int64_t)p.mt * (p.s.Qpad + (int64_t)p.s.n_heads * p.S * (p.s.hd + 4));
+}
+
+// Whether that layout fits the LDS beside the residual rows, the small area, the schedule tables
+// (one wave per kind and layer, plus the LM head), the smallest GEMV row blocks and one staging batch.
+static bool mt_merge_in_o_fits(const HostPlan& p, int32_t W) {
+  if (p.mt == 1) return true;
+  const Shape& s = p.s;
+  const int64_t vs = vec_floats(s);
+  const int64_t vec_part = std::max<int64_t>(p.mt * vs + (int64_t)MIN_MT_BLOCK_ROWS * NCOMP * p.mt, mt_merge_floats(p));
+  const int64_t xres = p.mt * round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0);
+  const int64_t n_waves = (int64_t)s.n_layers * 5 + 1;
+  const int64_t tables = round_up(n_waves * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
+                                      (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
+  (void)W;
+  return (vec_part + xres + SMALL_FLOATS) * 4 + tables + (int64_t)NCOMP * STREAM_BATCH * CHUNK_BYTES <= LDS_LIMIT;
+}
+
 int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::string& err) {
   p = HostPlan();
   Shape& s = p.s;
@@ -216,11 +243,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.mt = cfg.tokens_per_step > 1 ? cfg.tokens_per_step : 1;
   if (p.mt > 1 && (cfg.top_k > 0 || p.kv8))
     return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps with the BF16 KV cache");
-  if (p.mt > 1 && (cfg.flags & TILES_TRACE)) return fail(err, TILES_E_CONFIG, "multi-token steps are not traced");
   if (p.mt > 1 && p.mt * cfg.head_dim > 256)
     return fail(err, TILES_E_CONFIG, "tokens_per_step x head_dim above 256 (one RoPE row per position in LDS)");
-  if (p.mt > 1 && cfg.combine_mode == 1)
-    return fail(err, TILES_E_CONFIG, "multi-token steps merge the KV splits in a wave of their own (combine_mode 0 or 2)");
   p.top_k = cfg.top_k;
   p.temperature = cfg.top_k > 0 ? cfg.temperature : 1.0f;
   p.top_p = cfg.top_k > 0 ? cfg.top_p : 1.0f;
@@ -260,7 +284,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (cfg.o_placement < 0 || cfg.o_placement > 2) return fail(err, TILES_E_CONFIG, "o_placement must be 0, 1 or 2");
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
-  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES && p.mt == 1 ? 1 : 0;
+  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES && mt_merge_in_o_fits(p, W) ? 1 : 0;
   else return fail(err, TILES_E_CONFIG, "combine_mode must be 0, 1 or 2");
 
   // ---- packed layout: norm gains first, then the GEMV waves in execution order ----
@@ -506,7 +530,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
 
   // ---- LDS sizing ----
   // vec: GEMV input vector, or the raw q/k/v of an attention tile
-  int32_t vec = std::max({s.Hpad, s.Qpad, s.Fpad, (s.G + 2) * s.hd});
+  int32_t vec = (int32_t)vec_floats(s);
   // GEMV tiles run in row blocks of at most MAX_BLOCK_ROWS rows (partials [rows][NCOMP] in LDS).
   // Multi-token steps (mt positions): mt input vectors, mt residual rows and mt partials per row, in
   // blocks of as many rows as the LDS holds beside the other areas and one staging batch (at least
@@ -517,8 +541,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
                                             (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
   int32_t brows = MAX_BLOCK_ROWS;
   if (mt > 1) {
-    const int64_t other_floats = (int64_t)mt * round_up(vec, 64) + mt * round_up(s.Hpad, 64) +
-                                 (p.q8 ? MAX_BLOCK_ROWS : 0) + SMALL_FLOATS;
+    const int64_t other_floats = (int64_t)mt * vec + mt * round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0) +
+                                 SMALL_FLOATS;
     const int64_t room = (LDS_LIMIT - other_floats * 4 - tables_bytes - (int64_t)NCOMP * STREAM_BATCH * CHUNK_BYTES) /
                          (4 * (int64_t)NCOMP * mt);
     brows = (int32_t)(std::max<int64_t>(MIN_MT_BLOCK_ROWS, std::min<int64_t>(MAX_BLOCK_ROWS, room)) & ~1);
@@ -528,8 +552,9 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
   const int32_t ps = s.hd + 4;
   part = std::max(part, (int32_t)attn_lds_floats(p) + (p.kv8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0));
-  part = std::max(part, mt * p.S * ps);                             // one head's splits (combine tile)
-  if (p.combine_in_o) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
+  part = std::max(part, mt * p.S * ps);  // one head's splits (combine tile)
+  if (p.combine_in_o && mt == 1) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
+  if (p.combine_in_o && mt > 1) part = std::max(part, (int32_t)(mt_merge_floats(p) - (int64_t)mt * vec));
   p.lds_vec_floats = (int32_t)round_up(vec, 64);
   p.lds_part_floats = (int32_t)round_up(part, 64);
   // sampled decoding: the token gather holds every worker's top_k (value, index) pairs in vec + part
@@ -942,16 +967,29 @@ int validate_plan(const HostPlan& p, std::string& err) {
 
   // multi-token steps
   if (p.mt != 1 && p.mt != 2 && p.mt != 4) return fail(err, TILES_E_PLAN, "tokens per step must be 1, 2 or 4");
-  if (p.mt > 1 && (p.combine_in_o || p.top_k > 0 || p.kv8 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
+  if (p.mt > 1 && (p.top_k > 0 || p.kv8 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
     return fail(err, TILES_E_PLAN, "multi-token plan with an unsupported option");
+  if (p.mt > 1 && p.combine_in_o && (int64_t)p.mt * p.lds_vec_floats + p.lds_part_floats < mt_merge_floats(p))
+    return fail(err, TILES_E_PLAN, "LDS too small for the split merge of every position");
   // LDS capacity for every wave's staging
   if (p.lds_part_floats / (NCOMP * p.mt) < 2) return fail(err, TILES_E_PLAN, "LDS partial area too small");
+  // the kernel's GEMV row blocks (see the worker); INT8 scales and sampled candidates cover MAX_BLOCK_ROWS
+  // rows of a block
+  {
+    const int32_t br = p.mt > 1 ? std::min((p.lds_part_floats / (NCOMP * p.mt)) & ~1, MAX_BLOCK_ROWS)
+                                : (p.lds_part_floats / NCOMP) & ~1;
+    if ((p.q8 || p.top_k > 0) && br > MAX_BLOCK_ROWS)
+      for (const TileDesc& t : p.tiles)
+        if ((t.kind == KIND_QKV || t.kind == KIND_O || t.kind == KIND_GU || t.kind == KIND_DOWN || t.kind == KIND_LM) &&
+            t.nrows * (t.kind == KIND_GU ? 2 : 1) > MAX_BLOCK_ROWS)
+          return fail(err, TILES_E_PLAN, "a GEMV tile of more than 640 rows in an INT8 or sampling plan");
+  }
   if (p.stage_batches < 0 || p.stage_batches > MAX_STAGE_BATCHES ||
       p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT ||
       p.lds_stage_floats * 4 > 65536)
     return fail(err, TILES_E_PLAN, "bad LDS staging area");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
-  if (p.combine_in_o && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
+  if (p.combine_in_o && p.mt == 1 && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");
   if ((int64_t)p.mt * p.S * (s.hd + 4) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for a combine tile");
   if (attn_lds_floats(p) > p.lds_part_floats) return fail(err, TILES_E_PLAN, "LDS too small for an attention tile");

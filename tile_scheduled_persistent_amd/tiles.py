@@ -411,7 +411,8 @@ class Plan:
         return out
 
     def read_debug(self, hidden: bool = True, trace: bool = False):
-        """(hidden [n_steps, n_layers, H] float32 or None, trace [n_steps, waves, W, TRACE_WORDS] uint64 or None)."""
+        """(hidden [n_steps, n_layers, H] float32 or None, trace [kernel steps, waves, W, TRACE_WORDS] uint64 or
+        None; a verify plan's kernel step runs tokens_per_step positions)."""
         info = self.info()
         n = ctypes.c_int32(0)
         _check(lib().tiles_read_debug(self._h, None, None, ctypes.byref(n)))
@@ -421,7 +422,8 @@ class Plan:
             hid = np.zeros((n.value, self.model.n_layers, self.model.hidden), dtype=np.float32)
             hp = hid.ctypes.data
         if trace:
-            tr = np.zeros((n.value, info.waves_per_step, info.n_workers, TRACE_WORDS), dtype=np.uint64)
+            tr = np.zeros((n.value // info.tokens_per_step, info.waves_per_step, info.n_workers, TRACE_WORDS),
+                          dtype=np.uint64)
             tp = tr.ctypes.data
         _check(lib().tiles_read_debug(self._h, hp, tp, None))
         return hid, tr
