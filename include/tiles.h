@@ -196,6 +196,7 @@ typedef struct tiles_plan_info {
   int32_t top_k;              /* 0: greedy plan; else the plan samples (tiles_decode_sampled) */
   int32_t kv_format;          /* TILES_KV_BF16 or TILES_KV_INT8 */
   int32_t tokens_per_step;    /* positions per step: 1, or 2 / 4 for a verify plan */
+  int32_t stage_batches;      /* LDS staging batches per compute wavefront (0 .. 2; a verify plan may have none) */
 } tiles_plan_info_t;
 
 /* One wave of the per-step schedule (see tiles_plan_wave). */

@@ -341,6 +341,20 @@ def test_verify_plan_split_merge_placement():
         tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, combine_mode=1)
 
 
+def test_verify_plan_at_32k_positions_takes_fewer_splits():
+    """The Qwen3-4B shape at 32K positions: the decode plan puts 4 query heads and one of 32 splits in each
+    of 256 attention tiles; a 2-position verify plan holds at most 2 heads per tile, so it takes 16
+    splits (a forced 32 is rejected)."""
+    wl = WORKLOADS["qwen4b_32k"]
+    dec = tiles.dry_run(wl.model, wl.capacity)
+    assert (dec.kv_splits, dec.attn_heads) == (32, 4)
+    info = tiles.dry_run(wl.model, wl.capacity, tokens_per_step=2)
+    assert (info.kv_splits, info.attn_heads) == (16, 2)
+    assert info.stage_batches == 0 and dec.stage_batches >= 1  # no LDS room left for a staging batch
+    with pytest.raises(tiles.TilesError):
+        tiles.dry_run(wl.model, wl.capacity, tokens_per_step=2, kv_splits=32)
+
+
 def test_verify_plans_bound_the_heads_per_attention_tile():
     """Qwen3-4B has 4 query heads per KV head: with 2 positions per step a tile holds at most 2 heads.
     The planner takes the fewest heads per tile whose tiles fit the workers; where only 4 would fit
@@ -383,3 +397,12 @@ def test_long_gemv_tiles_in_int8_and_sampling_plans_rejected():
         with pytest.raises(tiles.TilesError) as e:
             tiles.dry_run(big, 1100, **kw)
         assert e.value.code == tiles.TILES_E_PLAN and "640 rows" in tiles.last_error()
+
+
+def test_decode_plans_have_a_staging_batch():
+    """A one-position step stages a batch of a compute wavefront's own range in every plan, so every decode
+    plan must hold at least one staging batch (else the plan is rejected)."""
+    for key in ("llama1b", "qwen06b", "qwen4b", "qwen4b_32k", "llama1b_int8", "llama1b_kv8", "qwen4b_32k_kv8"):
+        wl = WORKLOADS[key]
+        info = tiles.dry_run(wl.model, wl.capacity, weights=wl.weights, kv=wl.kv)
+        assert 1 <= info.stage_batches <= 2, key

@@ -944,6 +944,64 @@ def test_verify_plan_against_the_oracle(shape, mt, weights, combine):
                   f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}", flush=True)
 
 
+@pytest.mark.parametrize("shape,heads", [("qk128", 1), ("qk128", 2), ("tiny", 2)])
+def test_verify_plan_heads_per_attention_tile(shape, heads):
+    """2-position verify plans with 1 or 2 query heads per attention tile (2 or 4 query rows), head_dim
+    128 with q/k norm and head_dim 64, against the oracle as above."""
+    mdl = QK128 if shape == "qk128" else TINY
+    s = Setup(mdl, 64, 29)
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 10
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    drafts = list(g[:m - 1])
+    drafts[5] = (g[5] + 3) % mdl.vocab
+    with s.plan(tokens_per_step=2, attn_heads=heads) as plan:
+        assert plan.info().attn_heads == heads
+        _, n, stats = _verify_plan_case(s, plan, f"{shape} mt=2 heads/tile={heads}", [tok] + drafts, 29)
+    print(f"{shape} heads/tile={heads}: accepted {n}; {stats}", flush=True)
+
+
+# Qwen3-4B widths (head_dim 128, q/k norm, 4 query heads per KV head) on two layers, FFN 12288: a
+# 2-position verify plan with 2 heads per attention tile and 16 splits has no LDS room for staging
+W128 = scaled(TINY, name="wide128-2layer", n_layers=2, hidden=2560, n_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
+              vocab=4096, qk_norm=True, rms_eps=1e-6, rope_theta=1e6)
+
+
+def test_verify_plan_without_staging():
+    """A verify plan whose LDS holds no staging batch (the case of the Qwen3-4B shape at 32K positions),
+    2 query heads per tile, 16 splits merged in their own wave, ~1000 cached positions: against the
+    oracle as above."""
+    s = Setup(W128, 1100, 1000)
+    tok = synth.make_tokens(W128, 1)[0]
+    m = 8
+    with s.plan() as dplan:
+        assert dplan.info().stage_batches >= 1
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    with s.plan(tokens_per_step=2, attn_heads=2, kv_splits=16, combine_mode=2) as plan:
+        info = plan.info()
+        assert (info.stage_batches, info.attn_heads, info.kv_splits) == (0, 2, 16)
+        _, n, stats = _verify_plan_case(s, plan, "no staging", [tok] + g[:m - 1], 1000)
+    print(f"no staging: accepted {n}; {stats}", flush=True)
+
+
+def test_verify_plan_split_boundary_inside_a_step():
+    """7 splits, a 2-position step at positions 41 and 42 with the last split starting at 42: position 42's
+    row sees it, position 41's sees none of that split (an empty partial that the merge must drop);
+    later steps keep both positions in one split.  Against the oracle as above."""
+    mdl = scaled(TINY, name="tiny-long")
+    s = Setup(mdl, 120, 41)
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 12
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    for combine in (1, 2):
+        with s.plan(tokens_per_step=2, kv_splits=7, combine_mode=combine) as plan:
+            assert plan.info().kv_splits == 7
+            _, n, stats = _verify_plan_case(s, plan, f"split boundary combine={combine}", [tok] + g[:m - 1], 41)
+        print(f"split boundary combine={combine}: accepted {n}; {stats}", flush=True)
+
+
 def test_verify_plan_of_sixty_four_positions_to_capacity():
     """A 4-position verify plan over 64 positions (16 steps) ending exactly at the cache's capacity, the
     drafts the greedy continuation: against the oracle; one position more is rejected."""
@@ -1024,3 +1082,27 @@ def test_verify_entry_point_errors():
         buf = (ctypes.c_int32 * 1)(1)
         assert tiles.lib().tiles_verify(plan._h, ctypes.byref(c), buf, 1, ctypes.c_void_p(out.data_ptr()), None) == tiles.TILES_E_ARG
         assert "greedy" in tiles.last_error()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_size_verify_plan_at_32k_positions():
+    """An 8-position step of a 2-position verify plan on the Qwen3-4B shape after 32767 cached positions
+    (16 splits, 2 query heads per attention tile, the splits merged in a wave of their own), drafts the
+    decode plan's greedy continuation: all 8 positions and the written K/V rows against the oracle
+    teacher-forced on the same tokens, and the acceptance against the oracle's."""
+    wl = WORKLOADS["qwen4b_32k"]
+    mdl = wl.model
+    s = Setup(mdl, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda")
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 8
+    with s.plan(flags=0) as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    with s.plan(flags=0, tokens_per_step=2) as plan:
+        info = plan.info()
+        assert (info.kv_splits, info.attn_heads, info.combine_mode) == (16, 2, 2)
+        _, n, stats = _verify_plan_case(s, plan, "qwen4b 32k verify plan", [tok] + g[:m - 1], wl.n_cached,
+                                        check_hidden=False)
+    print(f"qwen4b 32k verify plan: {m} positions compared, accepted {n}; max logit abs err "
+          f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}, smallest oracle margin "
+          f"{stats['min_margin']:.3f}", flush=True)

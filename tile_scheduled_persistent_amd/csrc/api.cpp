@@ -586,6 +586,7 @@ static void fill_info(const HostPlan& hp, int occupancy, uint64_t build_id, tile
   info->top_k = hp.top_k;
   info->kv_format = hp.kv8 ? TILES_KV_INT8 : TILES_KV_BF16;
   info->tokens_per_step = hp.mt;
+  info->stage_batches = hp.stage_batches;
   for (size_t wv = 0; wv < hp.waves.size(); ++wv)
     if (hp.waves[wv].kind == KIND_O) {
       info->o_workers = hp.wave_busy[wv];

@@ -2454,7 +2454,10 @@ __device__ __forceinline__ void compute_loop(const KernelArgs& a, const Lds& L, 
         if (own > NB || (ng.k == k + 1 && ng.r0 == 0)) {
           // own staging lands during this tile's input wait and delays its end: one batch, which
           // arrives within that wait; the next tile's staging may take the whole area
-          st.ls = stage_range<B, NB>(a.packed, sr, own > NB ? 1 : a.stage_batches, lane, stage_lds);
+          // (a plan without a staging area stages nothing: decode plans always have one, which the
+          // plan validator checks, so only the multi-token instantiations test for it)
+          const int own_limit = MT > 1 ? (a.stage_batches > 0 ? 1 : 0) : 1;
+          st.ls = stage_range<B, NB>(a.packed, sr, own > NB ? own_limit : a.stage_batches, lane, stage_lds);
           st.sk = st.ls > 0 ? sr.k : -1;
         }
       }

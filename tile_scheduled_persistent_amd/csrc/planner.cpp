@@ -278,6 +278,10 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   }
   if (p.T * p.mt > MAX_GROUP)
     return fail(err, TILES_E_CONFIG, "attn_heads x tokens_per_step exceeds 4 query rows per attention tile");
+  // a verify plan whose bound on heads per tile leaves more attention tiles than workers takes fewer
+  // splits (the planner's own count only; the Qwen3-4B shape at 32K positions: 16 instead of 32)
+  if (p.mt > 1 && cfg.kv_splits <= 0 && (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
+    p.S = std::max<int32_t>(1, W / (s.n_kv * (s.G / p.T)));
   if (p.S < 1 || (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads * (query heads per KV head / attn_heads) exceeds workers");
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
@@ -575,6 +579,14 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.lds_bytes += p.lds_stage_floats * 4;
   // more than half the LDS of a CU: at most one workgroup per compute unit
   p.lds_bytes = std::max(p.lds_bytes, 84 * 1024);
+  // a one-position plan needs a staging batch (see validate_plan): where the planner's own choice of
+  // the o_proj prologue merge leaves no room for one (Qwen3-4B shape, INT8 weights), merge in a wave
+  // of its own instead
+  if (p.mt == 1 && p.stage_batches < 1 && p.combine_in_o && cfg.combine_mode == 0) {
+    tiles_config_t own = cfg;
+    own.combine_mode = 2;
+    return build_plan(own, n_workers, p, err);
+  }
 
   int rc = validate_plan(p, err);
   if (rc != TILES_OK) return rc;
@@ -988,6 +1000,8 @@ int validate_plan(const HostPlan& p, std::string& err) {
       p.lds_stage_floats != p.stage_batches * NCOMP * STREAM_BATCH * CHUNK_BYTES / 4 || p.lds_bytes > LDS_LIMIT ||
       p.lds_stage_floats * 4 > 65536)
     return fail(err, TILES_E_PLAN, "bad LDS staging area");
+  // a one-position step stages one batch of a compute wavefront's own range whatever stage_batches says
+  if (p.mt == 1 && p.stage_batches < 1) return fail(err, TILES_E_PLAN, "no LDS room for a staging batch");
   if (p.lds_vec_floats < std::max({s.Hpad, s.Qpad, s.Fpad})) return fail(err, TILES_E_PLAN, "LDS vector area too small");
   if (p.combine_in_o && p.mt == 1 && (int64_t)s.n_heads * p.S * (s.hd + 4) > p.lds_part_floats)
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge");

@@ -80,7 +80,7 @@ class PlanInfo(ctypes.Structure):
         ("weight_bytes_per_step", ctypes.c_int64), ("max_over_mean", ctypes.c_double),
         ("checksum", ctypes.c_uint64), ("build_id", ctypes.c_uint64), ("attn_heads", ctypes.c_int32),
         ("o_workers", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("top_k", ctypes.c_int32),
-        ("kv_format", ctypes.c_int32), ("tokens_per_step", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("tokens_per_step", ctypes.c_int32), ("stage_batches", ctypes.c_int32),
     ]
 
 
