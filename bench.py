@@ -159,14 +159,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
-    ap.add_argument("--verify-tokens", type=int, default=0,
-                    help="also time greedy verify steps of this many tokens (added to the line as 'verify')")
+    ap.add_argument("--verify-tokens", type=int, default=16,
+                    help="also time greedy verify steps of this many tokens (added to the line as 'verify'; "
+                         "greedy workloads with the BF16 cache; 0: none)")
     ap.add_argument("--trace-plan-tokens", type=int, default=0,
                     help="with --trace-report: trace a verify plan of this many positions per step (2 or 4) running "
                          "the workload's greedy continuation as drafts, instead of the decode launch")
-    ap.add_argument("--verify-plan-tokens", type=int, default=0,
+    ap.add_argument("--verify-plan-tokens", type=int, default=2,
                     help="with --verify-tokens: time them with a verify plan taking this many positions per step "
-                         "through every tile (2 or 4; 0: the decode plan, one position per step)")
+                         "through every tile (2 or 4; 0 or 1: the decode plan, one position per step)")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")
@@ -282,17 +283,24 @@ def main():
         "edge_floor": edge,
     }
 
-    if args.verify_tokens > 0:
+    if args.verify_tokens > 0 and wl.sampling is None and wl.kv == "bf16":
+        # (after the timed decode launches; a failure here is reported in the line, not raised)
         vplan = plan
-        if args.verify_plan_tokens > 1:
-            vplan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, weight_format=wl.weights,
-                               kv_format=wl.kv, stream=stream, tokens_per_step=args.verify_plan_tokens)
-        result["verify"] = _verify_timing(vplan, kv, wl, token, out_t, args, stream)
-        if vplan is not plan:
-            vi = vplan.info()
-            result["verify"]["plan"] = {"positions_per_step": vi.tokens_per_step, "waves_per_step": vi.waves_per_step,
-                                        "combine": "o_proj prologue" if vi.combine_mode == 1 else "own wave"}
-            vplan.close()
+        try:
+            if args.verify_plan_tokens > 1:
+                vplan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, weight_format=wl.weights,
+                                   kv_format=wl.kv, stream=stream, tokens_per_step=args.verify_plan_tokens)
+            result["verify"] = _verify_timing(vplan, kv, wl, token, out_t, args, stream)
+            if vplan is not plan:
+                vi = vplan.info()
+                result["verify"]["plan"] = {"positions_per_step": vi.tokens_per_step,
+                                            "waves_per_step": vi.waves_per_step,
+                                            "combine": "o_proj prologue" if vi.combine_mode == 1 else "own wave"}
+        except (tiles.TilesError, RuntimeError) as e:
+            result["verify"] = {"error": str(e)}
+        finally:
+            if vplan is not plan:
+                vplan.close()
 
     if args.trace_report:
         _trace_report(args.trace_report, m, wl, w, k0, v0, token, args, info, out_t)
