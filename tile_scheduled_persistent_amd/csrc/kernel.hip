@@ -1855,12 +1855,25 @@ __device__ __forceinline__ void cw_attn_publish(const KernelArgs& a, const Lds& 
 // between blocks), for attention tiles B and E.
 // ---------------------------------------------------------------------------
 
+// Multi-token steps whose o_proj prologue merges the splits: the merged heads of position t are at
+// vec + t * Qpad (the o_proj tile's input stride), and the split partials of every position sit
+// after them (position t's n_heads * S records at vec + MT * Qpad + t * n_heads * S * (HD + 4),
+// running on into the partial area, which o_proj's compute wavefronts write only after barrier A).
+template <int MT>
+__device__ __forceinline__ int o_in_stride(const KernelArgs& a) { return MT > 1 && a.combine_in_o ? a.Qpad : a.lds_vec_floats; }
+template <int MT>
+__device__ __forceinline__ float* o_partials(const KernelArgs& a, const Lds& L) {
+  return MT > 1 ? L.vec + MT * a.Qpad : L.part;
+}
+
 // Gather this wavefront's share of wave k's inputs into LDS.  Returns true when a wait was
 // abandoned.  The control wave also reduces the previous step's token (tok).
-// MT > 1 (multi-token steps): the inputs of every position tp of the step, position tp's in
-// vec + tp * lds_vec_floats (xres + tp * XS, part + tp * S * (HD + 4) for split partials) from the
-// producer's buffer of that position (ll_tok words after the previous one's); the step's tokens
-// are the given ones (verify), and the previous step's argmaxes are recorded.
+// MT > 1 (multi-token steps): the inputs of every position tp of the step, from the producer's
+// buffer of that position (ll_tok words after the previous one's), in one polling loop: a GEMV input
+// at vec + tp * lds_vec_floats (o_proj's merged heads: o_in_stride apart) and its residual row at
+// xres + tp * XS; a combine tile's split partials at part + tp * S * (HD + 4), the o_proj prologue's
+// at o_partials.  The step's tokens are the given ones (verify), and the previous step's argmaxes
+// are recorded.
 template <int HD, int G, bool CTRL, bool WD, bool Q8, bool SMP, bool KV8, int MT = 1>
 __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L, int bid, int wave, int lane, int k,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
@@ -1955,7 +1968,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       int n = a.F, nz = a.F;
       int vs = VS;  // (MT > 1) floats between the positions' GEMV inputs
       if (gk == KIND_O) {
-        dst = a.combine_in_o ? o_partials<HD, MT>(a, L) : L.vec;
+        dst = a.combine_in_o ? o_partials<MT>(a, L) : L.vec;
         n = a.combine_in_o ? a.n_heads * a.S * PS : a.n_heads * HD;
         nz = a.n_heads * HD;
         vs = o_in_stride<MT>(a);
@@ -2060,17 +2073,6 @@ __device__ __forceinline__ bool needs_barrier_a(const KernelArgs& a, const TileD
   return t.kind == KIND_ATTN || t.kind == KIND_COMBINE || (t.kind == KIND_O && a.combine_in_o);
 }
 
-// Multi-token steps whose o_proj prologue merges the splits: the merged heads of position t are at
-// vec + t * Qpad (the o_proj tile's input stride), and the split partials of every position sit
-// after them (position t's n_heads * S records at vec + MT * Qpad + t * n_heads * S * (HD + 4),
-// running on into the partial area, which o_proj's compute wavefronts write only after barrier A).
-template <int MT>
-__device__ __forceinline__ int o_in_stride(const KernelArgs& a) { return MT > 1 && a.combine_in_o ? a.Qpad : a.lds_vec_floats; }
-template <int HD, int MT>
-__device__ __forceinline__ float* o_partials(const KernelArgs& a, const Lds& L) {
-  return MT > 1 ? L.vec + MT * a.Qpad : L.part;
-}
-
 // The folded RMSNorm scale of position tp of the step (after barrier P).
 __device__ __forceinline__ float norm_scale(const KernelArgs& a, const Lds& L, int tp) {
   float tot = 0.f;
@@ -2097,7 +2099,7 @@ __device__ __forceinline__ float lds_prologue(const KernelArgs& a, const Lds& L,
     // (MT > 1: one merge per position of the step)
     const bool o = t.kind == KIND_O;
     const int nh = o ? a.n_heads : 1;
-    const float* src = o ? o_partials<HD, MT>(a, L) : L.part;
+    const float* src = o ? o_partials<MT>(a, L) : L.part;
     const int ostride = o ? o_in_stride<MT>(a) : a.lds_vec_floats;
 #pragma unroll
     for (int tp = 0; tp < MT; ++tp)

@@ -179,7 +179,7 @@ static int64_t mt_merge_floats(const HostPlan& p) {
 
 // Whether that layout fits the LDS beside the residual rows, the small area, the schedule tables
 // (one wave per kind and layer, plus the LM head), the smallest GEMV row blocks and one staging batch.
-static bool mt_merge_in_o_fits(const HostPlan& p, int32_t W) {
+static bool mt_merge_in_o_fits(const HostPlan& p) {
   if (p.mt == 1) return true;
   const Shape& s = p.s;
   const int64_t vs = vec_floats(s);
@@ -188,7 +188,6 @@ static bool mt_merge_in_o_fits(const HostPlan& p, int32_t W) {
   const int64_t n_waves = (int64_t)s.n_layers * 5 + 1;
   const int64_t tables = round_up(n_waves * (int64_t)(sizeof(SegDesc) + sizeof(TileDesc) + sizeof(WaveDesc)) +
                                       (int64_t)s.n_layers * (int64_t)sizeof(LayerSmall), 256);
-  (void)W;
   return (vec_part + xres + SMALL_FLOATS) * 4 + tables + (int64_t)NCOMP * STREAM_BATCH * CHUNK_BYTES <= LDS_LIMIT;
 }
 
@@ -288,7 +287,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (cfg.o_placement < 0 || cfg.o_placement > 2) return fail(err, TILES_E_CONFIG, "o_placement must be 0, 1 or 2");
   if (cfg.combine_mode == 1) p.combine_in_o = 1;
   else if (cfg.combine_mode == 2) p.combine_in_o = 0;
-  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES && mt_merge_in_o_fits(p, W) ? 1 : 0;
+  else if (cfg.combine_mode == 0) p.combine_in_o = part_bytes <= COMBINE_IN_O_BYTES && mt_merge_in_o_fits(p) ? 1 : 0;
   else return fail(err, TILES_E_CONFIG, "combine_mode must be 0, 1 or 2");
 
   // ---- packed layout: norm gains first, then the GEMV waves in execution order ----
