@@ -689,8 +689,8 @@ int tiles_plan_debug_spin_limit(tiles_plan_t* p, uint32_t rounds) {
   if (limit < 32 && !p->kernel_wd) {
     const void* k = worker_kernel(p->hp.s.hd, p->hp.T, true, p->hp.q8 != 0, p->hp.top_k > 0, p->hp.kv8 != 0, p->hp.mt);
     if (!k)
-      return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and KV, greedy decoding and one "
-                                     "query head per attention tile");
+      return set_err(TILES_E_CONFIG, "a watchdog under 32 rounds needs BF16 weights and KV, greedy decoding, one "
+                                     "query head per attention tile and one position per step");
     HIP_TRY(hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p->hp.lds_bytes));
     int occ = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, BLOCK_THREADS, p->hp.lds_bytes));
