@@ -342,8 +342,9 @@ int tiles_plan_debug_corrupt_device(tiles_plan_t *plan);
  * its next input barrier) and tiles_plan_status reports TILES_E_KERNEL.  0 restores the default
  * (2^22 rounds, seconds).  A small value makes ordinary waits give up, which exercises that path
  * without any fault; under 32 rounds the plan launches a test instantiation of the worker that
- * checks its watchdog every round (one query head per attention tile only: TILES_E_CONFIG
- * otherwise).  Host only (plus an occupancy query of that instantiation). */
+ * checks its watchdog every round (BF16 weights and KV, greedy, one query head per attention tile
+ * and one position per step only: TILES_E_CONFIG otherwise).  Host only (plus an occupancy query of
+ * that instantiation). */
 int tiles_plan_debug_spin_limit(tiles_plan_t *plan, uint32_t rounds);
 
 /* The weight-only INT8 quantizer plan creation applies to every linear layer ("History and roadmap"
