@@ -163,11 +163,12 @@ def main():
                     help="also time greedy verify steps of this many tokens (added to the line as 'verify'; "
                          "greedy workloads with the BF16 cache; 0: none)")
     ap.add_argument("--trace-plan-tokens", type=int, default=0,
-                    help="with --trace-report: trace a verify plan of this many positions per step (2 or 4) running "
+                    help="with --trace-report: trace a verify plan of this many positions per step (2 .. 4) running "
                          "the workload's greedy continuation as drafts, instead of the decode launch")
-    ap.add_argument("--verify-plan-tokens", type=int, default=2,
+    ap.add_argument("--verify-plan-tokens", type=int, default=3,
                     help="with --verify-tokens: time them with a verify plan taking this many positions per step "
-                         "through every tile (2 or 4; 0 or 1: the decode plan, one position per step)")
+                         "through every tile (2 .. 4, the positions timed rounded down to a multiple; 0 or 1: the "
+                         "decode plan, one position per step)")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")

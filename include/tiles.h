@@ -103,16 +103,17 @@ typedef struct tiles_config {
   int32_t kv_format;
   /* Positions per step of a verify plan ("History and roadmap" (TileInfer.jl), "M8 so far" table:
    * verify steps of up to 16 tokens; "Tried and not kept" table: verify GEMMs at 2-64 tokens).  0 or 1:
-   * one position per step (decode plans; tiles_verify then runs its m positions as m steps).  2 or 4:
-   * a verify plan, usable with tiles_verify only: every step takes tokens_per_step consecutive
+   * one position per step (decode plans; tiles_verify then runs its m positions as m steps).  2, 3
+   * or 4: a verify plan, usable with tiles_verify only: every step takes tokens_per_step consecutive
    * teacher-forced positions through each tile, so that each GEMV tile streams its weights once for
    * all of them (its LDS holds one input vector per position) and each attention tile serves all of
    * them with one pass over the cached rows, the step's own rows entering the positions at or after
-   * them.  Needs greedy selection (top_k = 0), the BF16 KV cache, splits merged in a
-   * wave of their own (combine_mode 0 or 2), tokens_per_step x head_dim <= 256, and query heads per
-   * attention tile x tokens_per_step <= 4 (the planner's choice of attn_heads keeps to that).  The
-   * LDS must hold tokens_per_step input vectors of max(hidden, ffn) floats (padded); plan creation
-   * fails with TILES_E_CONFIG otherwise. */
+   * them.  Needs greedy selection (top_k = 0), the BF16 KV cache, tokens_per_step x head_dim <= 256,
+   * and query heads per attention tile x tokens_per_step <= 4 (the planner's choice of attn_heads and
+   * kv_splits keeps to that).  The LDS must hold tokens_per_step input vectors of max(hidden, ffn)
+   * floats (padded), plus the split merge of every position where the o_proj prologue merges the
+   * splits (combine_mode 1; the planner's choice takes it only where it fits); plan creation fails
+   * with TILES_E_CONFIG otherwise. */
   int32_t tokens_per_step;
 } tiles_config_t;
 
@@ -195,7 +196,7 @@ typedef struct tiles_plan_info {
   int32_t weight_format;      /* TILES_WEIGHTS_BF16 or TILES_WEIGHTS_INT8 */
   int32_t top_k;              /* 0: greedy plan; else the plan samples (tiles_decode_sampled) */
   int32_t kv_format;          /* TILES_KV_BF16 or TILES_KV_INT8 */
-  int32_t tokens_per_step;    /* positions per step: 1, or 2 / 4 for a verify plan */
+  int32_t tokens_per_step;    /* positions per step: 1, or 2 .. 4 for a verify plan */
   int32_t stage_batches;      /* LDS staging batches per compute wavefront (0 .. 2; a verify plan may have none) */
 } tiles_plan_info_t;
 

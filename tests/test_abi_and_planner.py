@@ -309,8 +309,9 @@ def test_int8_kv_format_and_split_limits_rejected():
 # verify plans (tokens_per_step > 1)
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("m,pos,mt", [(LLAMA_1B, 1087, 2), (QWEN3_06B, 1087, 2), (QWEN3_4B, 1087, 2), (TINY, 80, 2),
-                                      (TINY, 80, 4)], ids=["llama1b-2", "qwen06b-2", "qwen4b-2", "tiny-2", "tiny-4"])
+@pytest.mark.parametrize("m,pos,mt", [(LLAMA_1B, 1087, 2), (LLAMA_1B, 1087, 3), (QWEN3_06B, 1087, 2), (QWEN3_4B, 1087, 2),
+                                      (TINY, 80, 2), (TINY, 80, 3), (TINY, 80, 4)],
+                         ids=["llama1b-2", "llama1b-3", "qwen06b-2", "qwen4b-2", "tiny-2", "tiny-3", "tiny-4"])
 def test_verify_plans_validate(m, pos, mt):
     """A verify plan holds at most 4 query rows per attention tile, fits the LDS, records its positions
     per step, merges the splits in the o_proj prologue or in a wave of its own (one more per layer),
@@ -367,10 +368,10 @@ def test_verify_plans_bound_the_heads_per_attention_tile():
             tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2, **kw)
 
 
-@pytest.mark.parametrize("kw", [dict(tokens_per_step=3), dict(tokens_per_step=8), dict(tokens_per_step=-1),
+@pytest.mark.parametrize("kw", [dict(tokens_per_step=5), dict(tokens_per_step=8), dict(tokens_per_step=-1),
                                 dict(tokens_per_step=2, sampling=(1.0, 4, 1.0)), dict(tokens_per_step=2, kv="int8"),
                                 dict(tokens_per_step=2, combine_mode=3)],
-                         ids=["three", "eight", "negative", "sampled", "int8-kv", "bad-combine-mode"])
+                         ids=["five", "eight", "negative", "sampled", "int8-kv", "bad-combine-mode"])
 def test_verify_plan_options_rejected(kw):
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(TINY, 80, **kw)
@@ -378,11 +379,16 @@ def test_verify_plan_options_rejected(kw):
 
 
 def test_verify_plan_limits():
-    """4 positions per step need head_dim 64 (one RoPE row per position in LDS) and room for four input
-    vectors of the FFN width: the Llama-3.2-1B shape (ffn 8192) does not fit, nor does head_dim 128."""
-    for m in (LLAMA_1B, QWEN3_06B):
+    """3 or 4 positions per step need head_dim 64 (one RoPE row per position in LDS) and room for that many
+    input vectors of the FFN width: the Llama-3.2-1B shape (ffn 8192) holds 3 (without a staging batch)
+    and not 4; head_dim 128 allows 2."""
+    info = tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=3)
+    assert info.stage_batches == 0 and info.combine_mode == 2
+    with pytest.raises(tiles.TilesError):
+        tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=4)
+    for mt in (3, 4):
         with pytest.raises(tiles.TilesError):
-            tiles.dry_run(m, 1087, tokens_per_step=4)
+            tiles.dry_run(QWEN3_06B, 1087, tokens_per_step=mt)
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=0).tokens_per_step == 1
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=1).checksum == tiles.dry_run(LLAMA_1B, 1087).checksum
 

@@ -884,10 +884,11 @@ def test_verify_of_sixty_four_positions_to_capacity():
 # verify plans: tokens_per_step consecutive positions through every tile per step
 # ---------------------------------------------------------------------------------------------
 
-# (shape, positions per step, weights, combine_mode: 0 planner choice -- the o_proj prologue for these
-# shapes -- or 2, the splits merged in a wave of their own)
-VERIFY_PLANS = [("tiny", 2, "bf16", 0), ("tiny", 4, "bf16", 0), ("wide", 2, "bf16", 0), ("wide", 2, "int8", 0),
-                ("wide", 2, "bf16", 2), ("tiny", 4, "bf16", 2)]
+# (shape, positions per step, weights, combine_mode: 0 planner choice -- the o_proj prologue where the
+# LDS holds it, else a wave of its own --, or 2, the splits merged in a wave of their own)
+VERIFY_PLANS = [("tiny", 2, "bf16", 0), ("tiny", 3, "bf16", 0), ("tiny", 4, "bf16", 0), ("wide", 2, "bf16", 0),
+                ("wide", 3, "bf16", 0), ("wide", 2, "int8", 0), ("wide", 3, "int8", 0), ("wide", 2, "bf16", 2),
+                ("tiny", 4, "bf16", 2)]
 
 
 def _verify_plan_case(s, plan, tag, tokens, pos, check_hidden=True):
@@ -933,7 +934,7 @@ def test_verify_plan_against_the_oracle(shape, mt, weights, combine):
         _, g, _ = _greedy_continuation(s, dplan, tok, m)
     with s.plan(tokens_per_step=mt, combine_mode=combine) as plan:
         info = plan.info()
-        assert info.tokens_per_step == mt and info.combine_mode == (combine or 1)
+        assert info.tokens_per_step == mt and (info.combine_mode == combine if combine else info.combine_mode in (1, 2))
         for j in (None, 3, 8):
             drafts = list(g[:m - 1])
             if j is not None:
@@ -1043,24 +1044,26 @@ def test_verify_plan_entry_point_errors():
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-def test_full_size_verify_plan_sixteen_tokens():
-    """A 16-position verify step of a 2-position verify plan on the Llama-3.2-1B shape at 1023 cached
-    positions, drafts the decode plan's greedy continuation with a wrong token at position 10: all 16
-    positions and the written K/V rows against the oracle teacher-forced on the same tokens, and the
-    acceptance against the oracle's."""
+@pytest.mark.parametrize("mt", [2, 3])
+def test_full_size_verify_plan_sixteen_tokens(mt):
+    """A verify step of 16 positions (2-position plan) or 15 (3-position plan) on the Llama-3.2-1B shape at
+    1023 cached positions, drafts the decode plan's greedy continuation with a wrong token at position
+    10: every position and the written K/V rows against the oracle teacher-forced on the same tokens,
+    and the acceptance against the oracle's."""
     wl = WORKLOADS["llama1b"]
     mdl = wl.model
     s = Setup(mdl, wl.capacity, wl.n_cached, gen_device="cuda")
     tok = synth.make_tokens(mdl, 1)[0]
-    m = 16
+    m = 16 - 16 % mt
     with s.plan(flags=0) as dplan:
         _, g, _ = _greedy_continuation(s, dplan, tok, m)
     drafts = list(g[:m - 1])
     drafts[9] = (g[9] + 1) % mdl.vocab
-    with s.plan(flags=0, tokens_per_step=2) as plan:
-        _, n, stats = _verify_plan_case(s, plan, "llama1b verify plan", [tok] + drafts, wl.n_cached,
+    with s.plan(flags=0, tokens_per_step=mt) as plan:
+        _, n, stats = _verify_plan_case(s, plan, f"llama1b verify plan mt={mt}", [tok] + drafts, wl.n_cached,
                                         check_hidden=False)
-    print(f"llama1b verify plan: {m} positions compared, accepted {n}; max logit abs err {stats['logit_abs_max']:.2e}, "
+    print(f"llama1b verify plan mt={mt}: {m} positions compared, accepted {n}; max logit abs err "
+          f"{stats['logit_abs_max']:.2e}, "
           f"tokens checked {stats['tokens_checked']}", flush=True)
 
 

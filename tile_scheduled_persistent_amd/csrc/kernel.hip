@@ -2846,6 +2846,7 @@ const void* worker_mt_for(int head_dim, int group, int mt) {
   if (head_dim == 64) {
     if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 2>);
     if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, false, false, 2>);
+    if (mt == 3 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 3>);
     if (mt == 4 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 4>);
   } else if (head_dim == 128) {
     if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, false, 2>);

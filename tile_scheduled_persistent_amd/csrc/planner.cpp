@@ -237,8 +237,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   p.kv8 = cfg.kv_format == KVFMT_INT8;
   // verify plans: every step runs tokens_per_step consecutive teacher-forced positions through each
   // tile (one weight stream for all of them)
-  if (cfg.tokens_per_step < 0 || cfg.tokens_per_step == 3 || cfg.tokens_per_step > MAX_STEP_TOKENS)
-    return fail(err, TILES_E_CONFIG, "tokens_per_step must be 0, 1, 2 or 4");
+  if (cfg.tokens_per_step < 0 || cfg.tokens_per_step > MAX_STEP_TOKENS)
+    return fail(err, TILES_E_CONFIG, "tokens_per_step must be 0 .. 4");
   p.mt = cfg.tokens_per_step > 1 ? cfg.tokens_per_step : 1;
   if (p.mt > 1 && (cfg.top_k > 0 || p.kv8))
     return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps with the BF16 KV cache");
@@ -977,7 +977,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
   }
 
   // multi-token steps
-  if (p.mt != 1 && p.mt != 2 && p.mt != 4) return fail(err, TILES_E_PLAN, "tokens per step must be 1, 2 or 4");
+  if (p.mt < 1 || p.mt > MAX_STEP_TOKENS) return fail(err, TILES_E_PLAN, "tokens per step must be 1 .. 4");
   if (p.mt > 1 && (p.top_k > 0 || p.kv8 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
     return fail(err, TILES_E_PLAN, "multi-token plan with an unsupported option");
   if (p.mt > 1 && p.combine_in_o && (int64_t)p.mt * p.lds_vec_floats + p.lds_part_floats < mt_merge_floats(p))

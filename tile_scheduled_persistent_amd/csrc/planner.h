@@ -59,7 +59,7 @@ struct HostPlan {
   int32_t S = 1;               // KV splits
   int32_t combine_in_o = 1;    // 1 prologue, 0 own wave
   int32_t T = 1;               // query heads per attention tile (divides G)
-  int32_t mt = 1;              // positions per step: 1 (decode), 2 or 4 (verify plans)
+  int32_t mt = 1;              // positions per step: 1 (decode), 2 .. 4 (verify plans)
   int32_t top_k = 0;           // sampled decoding: 1 .. MAX_TOP_K; 0 greedy
   int32_t kv8 = 0;             // 1: INT8 KV cache (codes, per-position scales, smoothed keys)
   float temperature = 1.0f, top_p = 1.0f;

@@ -172,7 +172,7 @@ def make_config(m: ModelConfig, max_positions: int, flags: int = 0, kv_splits: i
                 weights: str = "bf16", sampling: Optional[tuple] = None, kv: str = "bf16",
                 tokens_per_step: int = 0) -> Config:
     """``sampling`` = (temperature, top_k, top_p) makes a sampling plan (tiles_decode_sampled);
-    ``kv`` = "int8" an INT8 KV plan (see KVCache.int8); ``tokens_per_step`` = 2 or 4 a verify plan
+    ``kv`` = "int8" an INT8 KV plan (see KVCache.int8); ``tokens_per_step`` = 2 .. 4 a verify plan
     (tiles_verify only) whose steps take that many positions through every tile at once."""
     temperature, top_k, top_p = sampling if sampling is not None else (1.0, 0, 1.0)
     return Config(m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab, float(m.rope_theta),
