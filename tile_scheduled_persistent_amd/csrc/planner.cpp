@@ -546,9 +546,14 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (mt > 1) {
     const int64_t other_floats = (int64_t)mt * vec + mt * round_up(s.Hpad, 64) + (p.q8 ? MAX_BLOCK_ROWS : 0) +
                                  SMALL_FLOATS;
-    const int64_t room = (LDS_LIMIT - other_floats * 4 - tables_bytes - (int64_t)NCOMP * STREAM_BATCH * CHUNK_BYTES) /
-                         (4 * (int64_t)NCOMP * mt);
-    brows = (int32_t)(std::max<int64_t>(MIN_MT_BLOCK_ROWS, std::min<int64_t>(MAX_BLOCK_ROWS, room)) & ~1);
+    // rows that fit beside `batches` staging batches; where not even MIN_MT_BLOCK_ROWS fit beside one,
+    // the plan stages nothing (the planner then finds no room for a batch) and the blocks take it all
+    auto room = [&](int64_t batches) {
+      return (LDS_LIMIT - other_floats * 4 - tables_bytes - batches * NCOMP * STREAM_BATCH * CHUNK_BYTES) /
+             (4 * (int64_t)NCOMP * mt);
+    };
+    const int64_t r = room(1) >= MIN_MT_BLOCK_ROWS ? room(1) : room(0);
+    brows = (int32_t)(std::max<int64_t>(MIN_MT_BLOCK_ROWS, std::min<int64_t>(MAX_BLOCK_ROWS, r)) & ~1);
   }
   int32_t part = 0;
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, brows) * NCOMP * mt);
