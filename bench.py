@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--trace-report", default="", help="write a per-wave timing table (in-kernel trace) here")
     ap.add_argument("--verify-tokens", type=int, default=16,
                     help="also time greedy verify steps of this many tokens (added to the line as 'verify'; "
-                         "greedy workloads with the BF16 cache; 0: none)")
+                         "greedy workloads; 0: none)")
     ap.add_argument("--trace-plan-tokens", type=int, default=0,
                     help="with --trace-report: trace a verify plan of this many positions per step (2 .. 4) running "
                          "the workload's greedy continuation as drafts, instead of the decode launch")
@@ -284,7 +284,7 @@ def main():
         "edge_floor": edge,
     }
 
-    if args.verify_tokens > 0 and wl.sampling is None and wl.kv == "bf16":
+    if args.verify_tokens > 0 and wl.sampling is None:
         # (after the timed decode launches; a failure here is reported in the line, not raised)
         vplan = plan
         try:

@@ -369,9 +369,8 @@ def test_verify_plans_bound_the_heads_per_attention_tile():
 
 
 @pytest.mark.parametrize("kw", [dict(tokens_per_step=5), dict(tokens_per_step=8), dict(tokens_per_step=-1),
-                                dict(tokens_per_step=2, sampling=(1.0, 4, 1.0)), dict(tokens_per_step=2, kv="int8"),
-                                dict(tokens_per_step=2, combine_mode=3)],
-                         ids=["five", "eight", "negative", "sampled", "int8-kv", "bad-combine-mode"])
+                                dict(tokens_per_step=2, sampling=(1.0, 4, 1.0)), dict(tokens_per_step=2, combine_mode=3)],
+                         ids=["five", "eight", "negative", "sampled", "bad-combine-mode"])
 def test_verify_plan_options_rejected(kw):
     with pytest.raises(tiles.TilesError) as e:
         tiles.dry_run(TINY, 80, **kw)
@@ -412,3 +411,18 @@ def test_decode_plans_have_a_staging_batch():
         wl = WORKLOADS[key]
         info = tiles.dry_run(wl.model, wl.capacity, weights=wl.weights, kv=wl.kv)
         assert 1 <= info.stage_batches <= 2, key
+
+
+def test_int8_kv_verify_plans():
+    """Verify plans with the INT8 KV cache: the split's scales area beside the attention tile's rows, the
+    KV format in the plan info; on the Qwen3-4B shape at 32K positions the 2-position plan's 16 splits
+    would hold more than 2048 positions each, so it is rejected (the one-position plan takes 32)."""
+    for key, mt in (("llama1b_kv8", 2), ("llama1b_kv8", 3)):
+        wl = WORKLOADS[key]
+        info = tiles.dry_run(wl.model, wl.capacity, kv="int8", tokens_per_step=mt)
+        assert info.kv_format == 1 and info.tokens_per_step == mt and info.lds_bytes <= 160 * 1024
+    wl = WORKLOADS["qwen4b_32k_kv8"]
+    assert tiles.dry_run(wl.model, wl.capacity, kv="int8").kv_splits == 32
+    with pytest.raises(tiles.TilesError) as e:
+        tiles.dry_run(wl.model, wl.capacity, kv="int8", tokens_per_step=2)
+    assert "2048 positions per split" in tiles.last_error()

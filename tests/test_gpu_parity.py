@@ -906,8 +906,11 @@ def _verify_plan_case(s, plan, tag, tokens, pos, check_hidden=True):
     okv = s.oracle_kv()
     o_dec = o.decode(okv, tokens[0], pos, m, teacher=tokens[1:], widen_kv_once=True)
     stats = compare_teacher_forced(tag, a, out_l.cpu().numpy(), hid, o_dec)
-    kv_rows_close(f"{tag} K", kv.k, okv["k"], pos, m)
-    kv_rows_close(f"{tag} V", kv.v, okv["v"], pos, m)
+    if s.kv == "int8":
+        kv8_rows_close(tag, kv, okv, pos, m)
+    else:
+        kv_rows_close(f"{tag} K", kv.k, okv["k"], pos, m)
+        kv_rows_close(f"{tag} V", kv.v, okv["v"], pos, m)
     o_acc = 0
     while o_acc < m - 1 and int(o_dec["tokens"][o_acc]) == tokens[o_acc + 1]:
         o_acc += 1
@@ -1001,6 +1004,27 @@ def test_verify_plan_split_boundary_inside_a_step():
             assert plan.info().kv_splits == 7
             _, n, stats = _verify_plan_case(s, plan, f"split boundary combine={combine}", [tok] + g[:m - 1], 41)
         print(f"split boundary combine={combine}: accepted {n}; {stats}", flush=True)
+
+
+@pytest.mark.parametrize("shape,mt", [("tiny", 2), ("tiny", 3), ("wide", 2), ("qk128", 2)])
+def test_verify_plan_int8_kv(shape, mt):
+    """Verify plans with the INT8 KV cache (each of the step's rows quantized in the attention prologue,
+    its scales beside the split's staged ones): drafts the INT8-cache decode plan's greedy continuation
+    with a wrong token at position 6, every position and the written codes and scales against the
+    oracle's INT8 cache teacher-forced on the same tokens, and the acceptance against the oracle's."""
+    mdl = {"tiny": TINY, "wide": WIDE, "qk128": QK128}[shape]
+    s = Setup(mdl, 96, 60, kv="int8")
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 12
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    drafts = list(g[:m - 1])
+    drafts[5] = (g[5] + 5) % mdl.vocab
+    with s.plan(tokens_per_step=mt) as plan:
+        assert plan.info().kv_format == 1 and plan.info().tokens_per_step == mt
+        _, n, stats = _verify_plan_case(s, plan, f"{shape} int8 kv mt={mt}", [tok] + drafts, 60)
+    print(f"{shape} int8 kv mt={mt}: accepted {n}; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs "
+          f"err {stats['logit_abs_max']:.2e}", flush=True)
 
 
 def test_verify_plan_of_sixty_four_positions_to_capacity():

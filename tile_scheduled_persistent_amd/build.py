@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libtiles.so")
 # and KV format, or (the _mt units) the multi-token verify workers of one weight format (they
 # include kernel.hip); every source compiles to an object of its own, in parallel, then links.
 WORKER_UNITS = [f"workers_{w}{s}{k}.hip" for w in ("bf16", "int8") for s in ("", "_sampled") for k in ("", "_kv8")] + [
-    "workers_bf16_mt.hip", "workers_int8_mt.hip"]
+    "workers_bf16_mt.hip", "workers_int8_mt.hip", "workers_bf16_mt_kv8.hip", "workers_int8_mt_kv8.hip"]
 SOURCES = ["kernel.hip", *WORKER_UNITS, "planner.cpp", "api.cpp"]
 HEADERS = ["plan_types.h", "planner.h"]
 ARCH = "gfx950"

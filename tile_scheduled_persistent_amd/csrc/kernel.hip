@@ -217,6 +217,7 @@ constexpr int SM_KGAIN = 640;  // float[head_dim]: k-norm gains
 constexpr int SM_KSMOOTH = 768;  // float[head_dim]: INT8 KV key smoothing factors of the tile's KV head
 constexpr int SM_KVCUR = 896;    // float[2]: INT8 KV scales of the current position's K and V rows
 constexpr int SM_SS2 = 960;      // float[3][NWAVES]: as SM_SS, for positions 1 .. 3 of a multi-token step
+// (multi-token steps, INT8 KV: SM_KVCUR holds the (K, V) scales of every position of the step, 2 x 4 at most)
 // (multi-token steps: SM_ROPE holds one (cos, sin) row per position of the step, tokens x head_dim <= 256)
 __device__ __forceinline__ int sm_ss(int t) { return t == 0 ? SM_SS : SM_SS2 + (t - 1) * NWAVES; }
 
@@ -1177,8 +1178,8 @@ template <int HD, int G, int MT = 1>
 __device__ __forceinline__ float* attn_merged(const Lds& L) { return attn_ws<HD, G, MT>(L) + NCOMP * MT * G * pstride<HD>(); }
 // INT8 KV: the split's K scales, then its V scales, by position - split start (MAX_SPLIT_POSITIONS_KV8
 // each at most; the planner sizes the area)
-template <int HD, int G>
-__device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merged<HD, G>(L) + G * pstride<HD>(); }
+template <int HD, int G, int MT = 1>
+__device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merged<HD, G, MT>(L) + MT * G * pstride<HD>(); }
 
 // The split [lo, hi) that split sp of S covers at attended length L_att (positions < 2^31).
 __device__ __forceinline__ void split_bounds(int S, int sp, int L_att, int& lo, int& hi) {
@@ -1230,22 +1231,21 @@ __device__ __forceinline__ bool gather_qkv_mt(const KernelArgs& a, float* vec, i
 // quantized: kc / vc hold their codes, SM_KVCUR their scales (also put at the split's scale area
 // when the split holds the current position, split sp).
 // MT > 1: the same for every position t of the step (pos = its first position), each with its own
-// RoPE row.
+// RoPE row (and, INT8 KV, its own scales at SM_KVCUR + 2 t).
 template <int HD, int G, bool KV8, int MT = 1>
 __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L, int wave_index, int lane, int layer, int pos,
                                               int sp) {
   constexpr int HALF = HD / 2;
-  static_assert(MT == 1 || !KV8, "multi-token steps use the BF16 cache");
   float* q = L.part;
   float* kc = q + MT * G * HD;
   float* vc = kc + MT * HD;
   int slo = 0, shi = 0;
-  if (KV8) split_bounds(a.S, sp, pos + 1, slo, shi);
-  const bool own_cur = KV8 && slo <= pos && pos < shi;
-  float* kss = attn_kscales<HD, G>(L);
+  if (KV8) split_bounds(a.S, sp, pos + MT, slo, shi);
+  float* kss = attn_kscales<HD, G, MT>(L);
   float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
+    const bool own_cur = KV8 && slo <= pos + t && pos + t < shi;
     const float* raw = L.vec + t * a.lds_vec_floats;
     if (wave_index <= G) {
       const int u = wave_index;
@@ -1274,20 +1274,20 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
         const float* sg = L.small + SM_KSMOOTH;
         if (u < G) {
           if (lane < HALF) {
-            q[u * HD + lane] = r0 * a.qscale * sg[lane];
-            q[u * HD + lane + HALF] = r1 * a.qscale * sg[lane + HALF];
+            q[(t * G + u) * HD + lane] = r0 * a.qscale * sg[lane];
+            q[(t * G + u) * HD + lane + HALF] = r1 * a.qscale * sg[lane + HALF];
           }
         } else {  // the key: smoothed, then quantized per row
           const float k0 = lane < HALF ? __fdiv_rn(r0, sg[lane]) : 0.f;
           const float k1 = lane < HALF ? __fdiv_rn(r1, sg[lane + HALF]) : 0.f;
           const float sk = __fdiv_rn(wave_max(fmaxf(fabsf(k0), fabsf(k1)), lane), 127.f);
           if (lane < HALF) {
-            kc[lane] = kv_code(k0, sk);
-            kc[lane + HALF] = kv_code(k1, sk);
+            kc[t * HD + lane] = kv_code(k0, sk);
+            kc[t * HD + lane + HALF] = kv_code(k1, sk);
           }
           if (lane == 0) {
-            L.small[SM_KVCUR] = sk;
-            if (own_cur) kss[pos - slo] = sk;
+            L.small[SM_KVCUR + 2 * t] = sk;
+            if (own_cur) kss[pos + t - slo] = sk;
           }
         }
       } else if (lane < HALF) {
@@ -1311,10 +1311,10 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
         const float sv = __fdiv_rn(wave_max(am, lane), 127.f);
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          if (lane + 64 * i < HD) vc[lane + 64 * i] = kv_code(v[i], sv);
+          if (lane + 64 * i < HD) vc[t * HD + lane + 64 * i] = kv_code(v[i], sv);
         if (lane == 0) {
-          L.small[SM_KVCUR + 1] = sv;
-          if (own_cur) vss[pos - slo] = sv;
+          L.small[SM_KVCUR + 2 * t + 1] = sv;
+          if (own_cur) vss[pos + t - slo] = sv;
         }
       } else {
         for (int i = lane; i < HD; i += 64) vc[t * HD + i] = bf16_round(raw[(G + 1) * HD + i]);
@@ -1351,8 +1351,8 @@ __device__ __forceinline__ void cw_attn_kv_write(const KernelArgs& a, const Lds&
         st_u32(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.kv_k) + row * HD * 2) + lane, w);
       }
       if (lane == 0) {
-        st_u32(reinterpret_cast<uint32_t*>(a.kv_ks + row), __float_as_uint(L.small[SM_KVCUR]));
-        st_u32(reinterpret_cast<uint32_t*>(a.kv_vs + row), __float_as_uint(L.small[SM_KVCUR + 1]));
+        st_u32(reinterpret_cast<uint32_t*>(a.kv_ks + row), __float_as_uint(L.small[SM_KVCUR + 2 * t]));
+        st_u32(reinterpret_cast<uint32_t*>(a.kv_vs + row), __float_as_uint(L.small[SM_KVCUR + 2 * t + 1]));
       }
     } else if (!KV8 && lo <= cur && cur < hi && lane < HD / 2) {
       const int64_t row = ((int64_t)layer * a.n_kv + g) * a.kv_cap + cur;
@@ -1560,7 +1560,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const float* qlane = q + dseg * 8;  // q values are re-read from LDS per use (register budget)
   const __amdgpu_buffer_rsrc_t rk = rsrc(kv_head_base<KV8>(a.kv_k, kvrow0, HD));
   const __amdgpu_buffer_rsrc_t rv = rsrc(kv_head_base<KV8>(a.kv_v, kvrow0, HD));
-  const float* kss = attn_kscales<HD, G>(L) - rg.lo;  // (KV8) scales by position
+  const float* kss = attn_kscales<HD, G, MT>(L) - rg.lo;  // (KV8) scales by position
   const float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
   const int dummy = (int)a.kv_cap - 1;
   // Running state per query head: m[h] is the same in every lane (the largest score the wave has
@@ -1724,9 +1724,12 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
           kf[e] = kc[u * HD + dseg * 8 + e];
           vf[e] = pp == 0 ? vc[u * HD + dseg * 8 + e] : 0.f;
         }
+        // (INT8 KV: kc / vc hold the row's codes, SM_KVCUR + 2 u its K and V scales)
+        const float ks = KV8 ? L.small[SM_KVCUR + 2 * u] : 1.f;
+        const float sv = KV8 ? L.small[SM_KVCUR + 2 * u + 1] : 1.f;
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-          sc[h] = score(kf, h);
+          sc[h] = KV8 ? ks * score(kf, h) : score(kf, h);
           bm[h] = pp == 0 && u <= h / G ? sc[h] : -INFINITY;
         }
         raise(bm);
@@ -1734,8 +1737,9 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
         for (int h = 0; h < GM; ++h) {
           const float p = pp == 0 && u <= h / G ? __builtin_amdgcn_exp2f(sc[h] - m[h]) : 0.0f;
           l[h] += p;
+          const float pv = KV8 ? p * sv : p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
         }
       }
     }
@@ -1879,7 +1883,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
                                               const TileDesc& t, const WaveDesc& wd, int step, uint32_t par,
                                               int& tok) {
   constexpr int PS = pstride<HD>();
-  static_assert(MT == 1 || (!SMP && !KV8), "multi-token steps are greedy verify steps with the BF16 cache");
+  static_assert(MT == 1 || !SMP, "multi-token steps are greedy verify steps");
   const int VS = a.lds_vec_floats, XS = (a.Hpad + 63) & ~63;
   const int layer = wd.layer;
   const uint32_t* in = a.ll + (k > 0 ? wave_of(L, k - 1).ll_off : 0);
@@ -2025,11 +2029,11 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           sg0 = sg[lane];
           sg1 = sg[lane + HALF];
         }
-        const int pos = a.pos0 + step;
+        const int pos = a.pos0 + step * MT;  // the step's first position
         int slo = 0, shi = 0;
-        split_bounds(a.S, t.nrows, pos + 1, slo, shi);
+        split_bounds(a.S, t.nrows, pos + MT, slo, shi);
         const int sn = (shi < pos ? shi : pos) - slo;  // cached positions of the split
-        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)attn_kscales<HD, G>(L);
+        const uint32_t kl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)attn_kscales<HD, G, MT>(L);
         for (int i = 0; i < SPT; ++i) {
           const int e0 = (wave + i * (BLOCK_THREADS / 64)) * 64;  // wavefront-uniform
           if (e0 >= sn) break;
@@ -2839,18 +2843,18 @@ const void* worker_for(int head_dim, int group) {
   return nullptr;
 }
 // The multi-token (verify-plan) worker for a head size, query heads per attention tile and positions
-// per step, greedy with the BF16 cache: query rows (group x positions) at most MAX_GROUP, and one
+// per step, greedy, BF16 or INT8 cache: query rows (group x positions) at most MAX_GROUP, and one
 // RoPE row per position in the small LDS area (positions x head_dim <= 256).
-template <bool Q8>
+template <bool Q8, bool KV8>
 const void* worker_mt_for(int head_dim, int group, int mt) {
   if (head_dim == 64) {
-    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 2>);
-    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, false, false, 2>);
-    if (mt == 3 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 3>);
-    if (mt == 4 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, false, 4>);
+    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, KV8, 2>);
+    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<64, 2, false, Q8, false, KV8, 2>);
+    if (mt == 3 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, KV8, 3>);
+    if (mt == 4 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<64, 1, false, Q8, false, KV8, 4>);
   } else if (head_dim == 128) {
-    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, false, 2>);
-    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, false, false, 2>);
+    if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, KV8, 2>);
+    if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, false, KV8, 2>);
   }
   return nullptr;
 }
@@ -2865,8 +2869,10 @@ const void* worker_unit_5(int head_dim, int group);
 const void* worker_unit_6(int head_dim, int group);
 const void* worker_unit_7(int head_dim, int group);
 const void* worker_watchdog(int head_dim);
-const void* worker_mt_unit_0(int head_dim, int group, int mt);  // BF16 weights
-const void* worker_mt_unit_1(int head_dim, int group, int mt);  // INT8 weights
+const void* worker_mt_unit_0(int head_dim, int group, int mt);  // BF16 weights, BF16 KV
+const void* worker_mt_unit_1(int head_dim, int group, int mt);  // INT8 weights, BF16 KV
+const void* worker_mt_unit_2(int head_dim, int group, int mt);  // BF16 weights, INT8 KV
+const void* worker_mt_unit_3(int head_dim, int group, int mt);  // INT8 weights, INT8 KV
 
 const void* worker_unit(int variant, int head_dim, int group) {
   switch (variant) {
@@ -2888,7 +2894,8 @@ const void* worker_unit(int variant, int head_dim, int group) {
 // position per step only).
 const void* worker_kernel(int head_dim, int group, bool short_watchdog, bool q8, bool sampled, bool kv8, int mt) {
   if (mt > 1) {
-    if (short_watchdog || sampled || kv8) return nullptr;
+    if (short_watchdog || sampled) return nullptr;
+    if (kv8) return q8 ? worker_mt_unit_3(head_dim, group, mt) : worker_mt_unit_2(head_dim, group, mt);
     return q8 ? worker_mt_unit_1(head_dim, group, mt) : worker_mt_unit_0(head_dim, group, mt);
   }
   if (short_watchdog) return group == 1 && !q8 && !sampled && !kv8 ? worker_watchdog(head_dim) : nullptr;

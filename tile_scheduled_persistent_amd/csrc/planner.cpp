@@ -240,8 +240,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (cfg.tokens_per_step < 0 || cfg.tokens_per_step > MAX_STEP_TOKENS)
     return fail(err, TILES_E_CONFIG, "tokens_per_step must be 0 .. 4");
   p.mt = cfg.tokens_per_step > 1 ? cfg.tokens_per_step : 1;
-  if (p.mt > 1 && (cfg.top_k > 0 || p.kv8))
-    return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps with the BF16 KV cache");
+  if (p.mt > 1 && cfg.top_k > 0) return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps");
   if (p.mt > 1 && p.mt * cfg.head_dim > 256)
     return fail(err, TILES_E_CONFIG, "tokens_per_step x head_dim above 256 (one RoPE row per position in LDS)");
   p.top_k = cfg.top_k;
@@ -281,6 +280,8 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   // splits (the planner's own count only; the Qwen3-4B shape at 32K positions: 16 instead of 32)
   if (p.mt > 1 && cfg.kv_splits <= 0 && (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     p.S = std::max<int32_t>(1, W / (s.n_kv * (s.G / p.T)));
+  if (p.kv8 && (s.max_positions + p.S - 1) / p.S > MAX_SPLIT_POSITIONS_KV8)
+    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 2048 positions per split (raise kv_splits, or fewer positions)");
   if (p.S < 1 || (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads * (query heads per KV head / attn_heads) exceeds workers");
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
@@ -983,7 +984,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
 
   // multi-token steps
   if (p.mt < 1 || p.mt > MAX_STEP_TOKENS) return fail(err, TILES_E_PLAN, "tokens per step must be 1 .. 4");
-  if (p.mt > 1 && (p.top_k > 0 || p.kv8 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
+  if (p.mt > 1 && (p.top_k > 0 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
     return fail(err, TILES_E_PLAN, "multi-token plan with an unsupported option");
   if (p.mt > 1 && p.combine_in_o && (int64_t)p.mt * p.lds_vec_floats + p.lds_part_floats < mt_merge_floats(p))
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge of every position");
@@ -1016,7 +1017,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
   if (p.kv8) {
     const int64_t np = (s.max_positions + p.S - 1) / p.S;
     if (np > MAX_SPLIT_POSITIONS_KV8) return fail(err, TILES_E_PLAN, "INT8 KV: a split longer than 2048 positions");
-    if (p.lds_part_floats < p.T * s.hd + 2 * s.hd + (NCOMP + 1) * p.T * (s.hd + 4) + 2 * MAX_SPLIT_POSITIONS_KV8)
+    if (p.lds_part_floats < attn_lds_floats(p) + 2 * MAX_SPLIT_POSITIONS_KV8)
       return fail(err, TILES_E_PLAN, "LDS too small for an INT8 KV split's scales");
   }
   if (p.top_k < 0 || p.top_k > MAX_TOP_K || p.top_k > s.V || (p.top_k > 0 && p.W > 256))

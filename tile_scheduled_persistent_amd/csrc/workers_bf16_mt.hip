@@ -5,6 +5,6 @@
 
 namespace tiles {
 
-const void* worker_mt_unit_0(int head_dim, int group, int mt) { return worker_mt_for<false>(head_dim, group, mt); }
+const void* worker_mt_unit_0(int head_dim, int group, int mt) { return worker_mt_for<false, false>(head_dim, group, mt); }
 
 }  // namespace tiles

@@ -5,6 +5,6 @@
 
 namespace tiles {
 
-const void* worker_mt_unit_1(int head_dim, int group, int mt) { return worker_mt_for<true>(head_dim, group, mt); }
+const void* worker_mt_unit_1(int head_dim, int group, int mt) { return worker_mt_for<true, false>(head_dim, group, mt); }
 
 }  // namespace tiles
