@@ -108,9 +108,9 @@ typedef struct tiles_config {
    * teacher-forced positions through each tile, so that each GEMV tile streams its weights once for
    * all of them (its LDS holds one input vector per position) and each attention tile serves all of
    * them with one pass over the cached rows, the step's own rows entering the positions at or after
-   * them (INT8 KV: each quantized as in a one-position step).  Needs greedy selection (top_k = 0),
-   * tokens_per_step x head_dim <= 256, and query heads per attention tile x tokens_per_step <= 4 (the
-   * planner's choice of attn_heads and kv_splits keeps to that).  The LDS must hold tokens_per_step input vectors of max(hidden, ffn)
+   * them (INT8 KV: each quantized as in a one-position step).  Needs greedy selection (top_k = 0) and
+   * query heads per attention tile x tokens_per_step <= 4 (the planner's choice of attn_heads and
+   * kv_splits keeps to that).  The LDS must hold tokens_per_step input vectors of max(hidden, ffn)
    * floats (padded), plus the split merge of every position where the o_proj prologue merges the
    * splits (combine_mode 1; the planner's choice takes it only where it fits); plan creation fails
    * with TILES_E_CONFIG otherwise. */

@@ -378,16 +378,16 @@ def test_verify_plan_options_rejected(kw):
 
 
 def test_verify_plan_limits():
-    """3 or 4 positions per step need head_dim 64 (one RoPE row per position in LDS) and room for that many
-    input vectors of the FFN width: the Llama-3.2-1B shape (ffn 8192) holds 3 (without a staging batch)
-    and not 4; head_dim 128 allows 2."""
+    """Positions per step are bounded by the LDS, which holds one input vector of the FFN width per
+    position: the Llama-3.2-1B shape (ffn 8192) holds 3 (without a staging batch) and not 4, the
+    Qwen3-0.6B shape (ffn 3072, head_dim 128) 4, the Qwen3-4B shape (ffn 9728) 2."""
     info = tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=3)
     assert info.stage_batches == 0 and info.combine_mode == 2
-    with pytest.raises(tiles.TilesError):
-        tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=4)
-    for mt in (3, 4):
+    assert tiles.dry_run(QWEN3_06B, 1087, tokens_per_step=4).tokens_per_step == 4
+    assert tiles.dry_run(QWEN3_4B, 1087, tokens_per_step=2).tokens_per_step == 2
+    for m, mt in ((LLAMA_1B, 4), (QWEN3_4B, 3)):
         with pytest.raises(tiles.TilesError):
-            tiles.dry_run(QWEN3_06B, 1087, tokens_per_step=mt)
+            tiles.dry_run(m, 1087, tokens_per_step=mt)
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=0).tokens_per_step == 1
     assert tiles.dry_run(LLAMA_1B, 1087, tokens_per_step=1).checksum == tiles.dry_run(LLAMA_1B, 1087).checksum
 

@@ -948,10 +948,12 @@ def test_verify_plan_against_the_oracle(shape, mt, weights, combine):
                   f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}", flush=True)
 
 
-@pytest.mark.parametrize("shape,heads", [("qk128", 1), ("qk128", 2), ("tiny", 2)])
-def test_verify_plan_heads_per_attention_tile(shape, heads):
-    """2-position verify plans with 1 or 2 query heads per attention tile (2 or 4 query rows), head_dim
-    128 with q/k norm and head_dim 64, against the oracle as above."""
+@pytest.mark.parametrize("shape,heads,mt", [("qk128", 1, 2), ("qk128", 2, 2), ("tiny", 2, 2), ("qk128", 1, 3),
+                                             ("qk128", 1, 4)])
+def test_verify_plan_heads_per_attention_tile(shape, heads, mt):
+    """Verify plans with 1 or 2 query heads per attention tile at 2 positions (2 or 4 query rows), and
+    with head_dim 128 at 3 and 4 positions (the RoPE rows of 4 x 128 dimensions beside the attention
+    tile's areas), q/k norm, against the oracle as above."""
     mdl = QK128 if shape == "qk128" else TINY
     s = Setup(mdl, 64, 29)
     tok = synth.make_tokens(mdl, 1)[0]
@@ -960,10 +962,11 @@ def test_verify_plan_heads_per_attention_tile(shape, heads):
         _, g, _ = _greedy_continuation(s, dplan, tok, m)
     drafts = list(g[:m - 1])
     drafts[5] = (g[5] + 3) % mdl.vocab
-    with s.plan(tokens_per_step=2, attn_heads=heads) as plan:
+    m = m - m % mt
+    with s.plan(tokens_per_step=mt, attn_heads=heads) as plan:
         assert plan.info().attn_heads == heads
-        _, n, stats = _verify_plan_case(s, plan, f"{shape} mt=2 heads/tile={heads}", [tok] + drafts, 29)
-    print(f"{shape} heads/tile={heads}: accepted {n}; {stats}", flush=True)
+        _, n, stats = _verify_plan_case(s, plan, f"{shape} mt={mt} heads/tile={heads}", [tok] + drafts[:m - 1], 29)
+    print(f"{shape} mt={mt} heads/tile={heads}: accepted {n}; {stats}", flush=True)
 
 
 # Qwen3-4B widths (head_dim 128, q/k norm, 4 query heads per KV head) on two layers, FFN 12288: a
@@ -1006,7 +1009,7 @@ def test_verify_plan_split_boundary_inside_a_step():
         print(f"split boundary combine={combine}: accepted {n}; {stats}", flush=True)
 
 
-@pytest.mark.parametrize("shape,mt", [("tiny", 2), ("tiny", 3), ("wide", 2), ("qk128", 2)])
+@pytest.mark.parametrize("shape,mt", [("tiny", 2), ("tiny", 3), ("wide", 2), ("qk128", 2), ("qk128", 3)])
 def test_verify_plan_int8_kv(shape, mt):
     """Verify plans with the INT8 KV cache (each of the step's rows quantized in the attention prologue,
     its scales beside the split's staged ones): drafts the INT8-cache decode plan's greedy continuation
@@ -1020,9 +1023,10 @@ def test_verify_plan_int8_kv(shape, mt):
         _, g, _ = _greedy_continuation(s, dplan, tok, m)
     drafts = list(g[:m - 1])
     drafts[5] = (g[5] + 5) % mdl.vocab
+    m = m - m % mt
     with s.plan(tokens_per_step=mt) as plan:
         assert plan.info().kv_format == 1 and plan.info().tokens_per_step == mt
-        _, n, stats = _verify_plan_case(s, plan, f"{shape} int8 kv mt={mt}", [tok] + drafts, 60)
+        _, n, stats = _verify_plan_case(s, plan, f"{shape} int8 kv mt={mt}", [tok] + drafts[:m - 1], 60)
     print(f"{shape} int8 kv mt={mt}: accepted {n}; max hidden rel L2 {stats['hidden_rel_l2_max']:.2e}, max logit abs "
           f"err {stats['logit_abs_max']:.2e}", flush=True)
 

@@ -218,7 +218,8 @@ constexpr int SM_KSMOOTH = 768;  // float[head_dim]: INT8 KV key smoothing facto
 constexpr int SM_KVCUR = 896;    // float[2]: INT8 KV scales of the current position's K and V rows
 constexpr int SM_SS2 = 960;      // float[3][NWAVES]: as SM_SS, for positions 1 .. 3 of a multi-token step
 // (multi-token steps, INT8 KV: SM_KVCUR holds the (K, V) scales of every position of the step, 2 x 4 at most)
-// (multi-token steps: SM_ROPE holds one (cos, sin) row per position of the step, tokens x head_dim <= 256)
+// (multi-token steps keep one (cos, sin) row per position of the step after the attention tile's areas
+// instead: see rope_rows)
 __device__ __forceinline__ int sm_ss(int t) { return t == 0 ? SM_SS : SM_SS2 + (t - 1) * NWAVES; }
 
 struct Lds {
@@ -1181,6 +1182,14 @@ __device__ __forceinline__ float* attn_merged(const Lds& L) { return attn_ws<HD,
 template <int HD, int G, int MT = 1>
 __device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merged<HD, G, MT>(L) + MT * G * pstride<HD>(); }
 
+// The (cos, sin) RoPE rows of an attention tile: the current position's in the small area (one-position
+// steps), or one row per position of a multi-token step after the tile's work areas (and, INT8 KV,
+// after the split's scales).
+template <int HD, int G, bool KV8, int MT>
+__device__ __forceinline__ float* rope_rows(const Lds& L) {
+  return MT == 1 ? L.small + SM_ROPE : attn_kscales<HD, G, MT>(L) + (KV8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0);
+}
+
 // The split [lo, hi) that split sp of S covers at attended length L_att (positions < 2^31).
 __device__ __forceinline__ void split_bounds(int S, int sp, int L_att, int& lo, int& hi) {
   const int ch = (int)((uint32_t)(L_att + S - 1) / (uint32_t)S);
@@ -1265,7 +1274,7 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
       }
       float r0 = 0.f, r1 = 0.f;
       if (lane < HALF) {
-        const float* cs = L.small + SM_ROPE + t * HD + lane * 2;
+        const float* cs = rope_rows<HD, G, KV8, MT>(L) + t * HD + lane * 2;
         const float co = cs[0], si = cs[1];
         r0 = u0 * co - u1 * si;
         r1 = u1 * co + u0 * si;
@@ -2050,8 +2059,9 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       if (CTRL && lane < HALF) {
 #pragma unroll
         for (int tp = 0; tp < MT; ++tp) {
-          L.small[SM_ROPE + tp * HD + 2 * lane] = cs[tp].x;
-          L.small[SM_ROPE + tp * HD + 2 * lane + 1] = cs[tp].y;
+          float* rr = rope_rows<HD, G, KV8, MT>(L) + tp * HD;
+          rr[2 * lane] = cs[tp].x;
+          rr[2 * lane + 1] = cs[tp].y;
         }
         L.small[SM_QGAIN + lane] = gq0;
         L.small[SM_QGAIN + lane + HALF] = gq1;
@@ -2843,8 +2853,7 @@ const void* worker_for(int head_dim, int group) {
   return nullptr;
 }
 // The multi-token (verify-plan) worker for a head size, query heads per attention tile and positions
-// per step, greedy, BF16 or INT8 cache: query rows (group x positions) at most MAX_GROUP, and one
-// RoPE row per position in the small LDS area (positions x head_dim <= 256).
+// per step, greedy, BF16 or INT8 cache: query rows (group x positions) at most MAX_GROUP.
 template <bool Q8, bool KV8>
 const void* worker_mt_for(int head_dim, int group, int mt) {
   if (head_dim == 64) {
@@ -2855,6 +2864,8 @@ const void* worker_mt_for(int head_dim, int group, int mt) {
   } else if (head_dim == 128) {
     if (mt == 2 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, KV8, 2>);
     if (mt == 2 && group == 2) return reinterpret_cast<const void*>(&tiles_worker<128, 2, false, Q8, false, KV8, 2>);
+    if (mt == 3 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, KV8, 3>);
+    if (mt == 4 && group == 1) return reinterpret_cast<const void*>(&tiles_worker<128, 1, false, Q8, false, KV8, 4>);
   }
   return nullptr;
 }

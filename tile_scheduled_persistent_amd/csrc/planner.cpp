@@ -159,10 +159,11 @@ std::vector<uint64_t> worker_table_hashes(const HostPlan& p) {
 constexpr int32_t MIN_MT_BLOCK_ROWS = 64;
 
 // LDS floats of an attention tile's work areas: q[mt * T][hd], kc[mt][hd], vc[mt][hd], the compute
-// waves' states [NCOMP][mt * T][hd + 4] and the merged partial [mt * T][hd + 4].
+// waves' states [NCOMP][mt * T][hd + 4] and the merged partial [mt * T][hd + 4]; multi-token steps add
+// one RoPE row (hd floats) per position (one-position steps keep theirs in the small area).
 static int64_t attn_lds_floats(const HostPlan& p) {
   const int64_t rows = (int64_t)p.mt * p.T, hd = p.s.hd;
-  return rows * hd + 2 * p.mt * hd + (NCOMP + 1) * rows * (hd + 4);
+  return rows * hd + 2 * p.mt * hd + (NCOMP + 1) * rows * (hd + 4) + (p.mt > 1 ? p.mt * hd : 0);
 }
 
 // Floats of one position's GEMV input area (the largest input, or an attention tile's raw q/k/v).
@@ -241,8 +242,6 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
     return fail(err, TILES_E_CONFIG, "tokens_per_step must be 0 .. 4");
   p.mt = cfg.tokens_per_step > 1 ? cfg.tokens_per_step : 1;
   if (p.mt > 1 && cfg.top_k > 0) return fail(err, TILES_E_CONFIG, "multi-token steps are greedy verify steps");
-  if (p.mt > 1 && p.mt * cfg.head_dim > 256)
-    return fail(err, TILES_E_CONFIG, "tokens_per_step x head_dim above 256 (one RoPE row per position in LDS)");
   p.top_k = cfg.top_k;
   p.temperature = cfg.top_k > 0 ? cfg.temperature : 1.0f;
   p.top_p = cfg.top_k > 0 ? cfg.top_p : 1.0f;
@@ -984,7 +983,7 @@ int validate_plan(const HostPlan& p, std::string& err) {
 
   // multi-token steps
   if (p.mt < 1 || p.mt > MAX_STEP_TOKENS) return fail(err, TILES_E_PLAN, "tokens per step must be 1 .. 4");
-  if (p.mt > 1 && (p.top_k > 0 || p.T * p.mt > MAX_GROUP || p.mt * s.hd > 256))
+  if (p.mt > 1 && (p.top_k > 0 || p.T * p.mt > MAX_GROUP))
     return fail(err, TILES_E_PLAN, "multi-token plan with an unsupported option");
   if (p.mt > 1 && p.combine_in_o && (int64_t)p.mt * p.lds_vec_floats + p.lds_part_floats < mt_merge_floats(p))
     return fail(err, TILES_E_PLAN, "LDS too small for the split merge of every position");
