@@ -165,10 +165,10 @@ def main():
     ap.add_argument("--trace-plan-tokens", type=int, default=0,
                     help="with --trace-report: trace a verify plan of this many positions per step (2 .. 4) running "
                          "the workload's greedy continuation as drafts, instead of the decode launch")
-    ap.add_argument("--verify-plan-tokens", type=int, default=3,
+    ap.add_argument("--verify-plan-tokens", type=int, default=-1,
                     help="with --verify-tokens: time them with a verify plan taking this many positions per step "
-                         "through every tile (2 .. 4, the positions timed rounded down to a multiple; 0 or 1: the "
-                         "decode plan, one position per step)")
+                         "through every tile (2 .. 4, the positions timed rounded down to a multiple; -1: the most "
+                         "the plan's LDS holds; 0 or 1: the decode plan, one position per step)")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--combine-mode", type=int, default=0)
     ap.add_argument("--attn-heads", type=int, default=0, help="query heads per attention tile (0: planner choice)")
@@ -288,9 +288,16 @@ def main():
         # (after the timed decode launches; a failure here is reported in the line, not raised)
         vplan = plan
         try:
-            if args.verify_plan_tokens > 1:
-                vplan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, weight_format=wl.weights,
-                                   kv_format=wl.kv, stream=stream, tokens_per_step=args.verify_plan_tokens)
+            for T in ((4, 3, 2) if args.verify_plan_tokens < 0 else (args.verify_plan_tokens,)):
+                if T < 2:
+                    break
+                try:
+                    vplan = tiles.Plan(m, w, wl.capacity, flags=0, kv_splits=args.kv_splits, weight_format=wl.weights,
+                                       kv_format=wl.kv, stream=stream, tokens_per_step=T)
+                    break
+                except tiles.TilesError:
+                    if args.verify_plan_tokens >= 0 or T == 2:
+                        raise
             result["verify"] = _verify_timing(vplan, kv, wl, token, out_t, args, stream)
             if vplan is not plan:
                 vi = vplan.info()
