@@ -99,7 +99,9 @@ typedef struct tiles_config {
    * smoothed keys): TILES_KV_BF16, or TILES_KV_INT8: every cached K and V row as symmetric INT8 codes
    * with one FP32 scale per (layer, KV head, position), keys divided by a per-(layer, KV head,
    * channel) smoothing factor before quantization; attention reads the codes and computes with the
-   * dequantized rows (queries stay FP32).  See tiles_kv_t and tiles_kv_convert_int8. */
+   * dequantized rows (queries stay FP32).  An attention tile stages its split's scales in LDS: at
+   * most 4096 positions per split (the planner raises its split count to fit; a kv_splits that
+   * leaves longer splits fails with TILES_E_CONFIG).  See tiles_kv_t and tiles_kv_convert_int8. */
   int32_t kv_format;
   /* Positions per step of a verify plan ("History and roadmap" (TileInfer.jl), "M8 so far" table:
    * verify steps of up to 16 tokens; "Tried and not kept" table: verify GEMMs at 2-64 tokens).  0 or 1:

@@ -283,13 +283,13 @@ def test_sampling_limits_top_k_by_vocab_and_workers():
 
 @pytest.mark.parametrize("key", ["qwen4b_32k_kv8", "llama1b_kv8"])
 def test_int8_kv_plans_validate(key):
-    """INT8 KV plans: at most 2048 positions per split (the split count is raised to fit), LDS for the
+    """INT8 KV plans: at most 4096 positions per split (the split count is raised to fit), LDS for the
     split's scales, the KV format in the plan info; the same shapes with BF16 KV plan differently."""
     wl = WORKLOADS[key]
     info = tiles.dry_run(wl.model, wl.capacity, kv="int8")
     assert info.kv_format == 1
     assert info.lds_bytes <= 160 * 1024
-    assert (wl.capacity + info.kv_splits - 1) // info.kv_splits <= 2048
+    assert (wl.capacity + info.kv_splits - 1) // info.kv_splits <= 4096
     assert tiles.dry_run(wl.model, wl.capacity).checksum != info.checksum
     assert tiles.lib().tiles_plan_debug_validate(ctypes.byref(tiles.make_config(wl.model, wl.capacity, kv="int8")),
                                                  256, 0) == tiles.TILES_OK
@@ -300,8 +300,12 @@ def test_int8_kv_format_and_split_limits_rejected():
     cfg.kv_format = 2
     info = tiles.PlanInfo()
     assert tiles.lib().tiles_plan_dry_run(ctypes.byref(cfg), 256, ctypes.byref(info)) == tiles.TILES_E_CONFIG
-    with pytest.raises(tiles.TilesError):  # a forced split count leaving more than 2048 positions per split
-        tiles.dry_run(TINY, 5000, kv="int8", kv_splits=2)
+    with pytest.raises(tiles.TilesError):  # a forced split count leaving more than 4096 positions per split
+        tiles.dry_run(TINY, 9000, kv="int8", kv_splits=2)
+    assert "4096 positions per split" in tiles.last_error()
+    # the planner raises its own split count to fit; 4096 positions per split are accepted
+    assert tiles.dry_run(TINY, 9000, kv="int8").kv_splits >= 3
+    assert tiles.dry_run(TINY, 8192, kv="int8", kv_splits=2).kv_splits == 2
     assert tiles.lib().tiles_kv_convert_int8(None, None, None, 1, 0, None) == tiles.TILES_E_ARG
 
 
@@ -415,14 +419,16 @@ def test_decode_plans_have_a_staging_batch():
 
 def test_int8_kv_verify_plans():
     """Verify plans with the INT8 KV cache: the split's scales area beside the attention tile's rows, the
-    KV format in the plan info; on the Qwen3-4B shape at 32K positions the 2-position plan's 16 splits
-    would hold more than 2048 positions each, so it is rejected (the one-position plan takes 32)."""
+    KV format in the plan info; on the Qwen3-4B shape at 32K positions the 2-position plan takes 16
+    splits of up to 2050 positions (scale areas of 2112), the one-position plan 32 (1088)."""
     for key, mt in (("llama1b_kv8", 2), ("llama1b_kv8", 3)):
         wl = WORKLOADS[key]
         info = tiles.dry_run(wl.model, wl.capacity, kv="int8", tokens_per_step=mt)
         assert info.kv_format == 1 and info.tokens_per_step == mt and info.lds_bytes <= 160 * 1024
     wl = WORKLOADS["qwen4b_32k_kv8"]
     assert tiles.dry_run(wl.model, wl.capacity, kv="int8").kv_splits == 32
-    with pytest.raises(tiles.TilesError) as e:
-        tiles.dry_run(wl.model, wl.capacity, kv="int8", tokens_per_step=2)
-    assert "2048 positions per split" in tiles.last_error()
+    info = tiles.dry_run(wl.model, wl.capacity, kv="int8", tokens_per_step=2)
+    assert info.kv_splits == 16 and info.tokens_per_step == 2 and info.attn_heads == 2
+    assert info.lds_bytes <= 160 * 1024
+    assert tiles.lib().tiles_plan_debug_validate(
+        ctypes.byref(tiles.make_config(wl.model, wl.capacity, kv="int8", tokens_per_step=2)), 256, 0) == tiles.TILES_OK

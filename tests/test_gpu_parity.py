@@ -1115,16 +1115,40 @@ def test_verify_entry_point_errors():
         assert "greedy" in tiles.last_error()
 
 
+def test_kv8_splits_longer_than_2048_positions():
+    """INT8 KV splits of up to 3,000 positions (the split's scale areas sized to the plan's longest
+    split, 3,008 positions, staged in 6 loads per wavefront): a decode plan and a 2-position verify plan
+    with 2 forced splits after 5,900 cached positions, against the oracle's INT8 cache as above."""
+    mdl = scaled(TINY, name="tiny-6k")
+    s = Setup(mdl, 6000, 5900, key_scale=True, kv="int8")
+    tok = synth.make_tokens(mdl, 1)[0]
+    with s.plan(kv_splits=2) as plan:
+        assert plan.info().kv_splits == 2
+        _oracle_forced(s, [tok], 6, plan, tag="kv8 3000-position splits")
+    m = 8
+    with s.plan(kv_splits=2) as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    drafts = list(g[:m - 1])
+    drafts[4] = (g[4] + 5) % mdl.vocab
+    with s.plan(kv_splits=2, tokens_per_step=2) as plan:
+        assert (plan.info().kv_splits, plan.info().tokens_per_step) == (2, 2)
+        _, n, stats = _verify_plan_case(s, plan, "kv8 3000-position splits mt=2", [tok] + drafts, 5900)
+    print(f"kv8 3000-position splits mt=2: accepted {n}; {stats}", flush=True)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_full_size_verify_plan_at_32k_positions():
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_full_size_verify_plan_at_32k_positions(kv):
     """An 8-position step of a 2-position verify plan on the Qwen3-4B shape after 32767 cached positions
-    (16 splits, 2 query heads per attention tile, the splits merged in a wave of their own), drafts the
-    decode plan's greedy continuation: all 8 positions and the written K/V rows against the oracle
-    teacher-forced on the same tokens, and the acceptance against the oracle's."""
-    wl = WORKLOADS["qwen4b_32k"]
+    (16 splits, 2 query heads per attention tile, the splits merged in a wave of their own; INT8 KV:
+    splits of up to 2,050 positions), drafts the decode plan's greedy continuation: all 8 positions and
+    the written K/V rows (codes and scales) against the oracle teacher-forced on the same tokens, and
+    the acceptance against the oracle's."""
+    key = "qwen4b_32k" if kv == "bf16" else "qwen4b_32k_kv8"
+    wl = WORKLOADS[key]
     mdl = wl.model
-    s = Setup(mdl, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda")
+    s = Setup(mdl, wl.capacity, wl.n_cached, key_scale=wl.key_scale, gen_device="cuda", kv=kv)
     tok = synth.make_tokens(mdl, 1)[0]
     m = 8
     with s.plan(flags=0) as dplan:
@@ -1132,8 +1156,8 @@ def test_full_size_verify_plan_at_32k_positions():
     with s.plan(flags=0, tokens_per_step=2) as plan:
         info = plan.info()
         assert (info.kv_splits, info.attn_heads, info.combine_mode) == (16, 2, 2)
-        _, n, stats = _verify_plan_case(s, plan, "qwen4b 32k verify plan", [tok] + g[:m - 1], wl.n_cached,
+        _, n, stats = _verify_plan_case(s, plan, f"{key} verify plan", [tok] + g[:m - 1], wl.n_cached,
                                         check_hidden=False)
-    print(f"qwen4b 32k verify plan: {m} positions compared, accepted {n}; max logit abs err "
+    print(f"{key} verify plan: {m} positions compared, accepted {n}; max logit abs err "
           f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}, smallest oracle margin "
           f"{stats['min_margin']:.3f}", flush=True)

@@ -455,6 +455,7 @@ int decode_impl(tiles_plan_t* p, tiles_kv_t* kv, int32_t token, int32_t n_steps,
   a.n_steps = n_steps / hp.mt;
   a.mt = hp.mt;
   a.ll_tok = hp.ll_words;
+  a.kv8_span = hp.kv8_span;
   a.n_waves = (int32_t)hp.waves.size();
   a.W = hp.W;
   a.n_layers = hp.s.n_layers;

@@ -1177,8 +1177,8 @@ template <int HD, int G, int MT = 1>
 __device__ __forceinline__ float* attn_ws(const Lds& L) { return L.part + MT * G * HD + 2 * MT * HD; }
 template <int HD, int G, int MT = 1>
 __device__ __forceinline__ float* attn_merged(const Lds& L) { return attn_ws<HD, G, MT>(L) + NCOMP * MT * G * pstride<HD>(); }
-// INT8 KV: the split's K scales, then its V scales, by position - split start (MAX_SPLIT_POSITIONS_KV8
-// each at most; the planner sizes the area)
+// INT8 KV: the split's K scales, then its V scales (kv8_span positions apart: the plan's longest
+// split, rounded up to 64), by position - split start
 template <int HD, int G, int MT = 1>
 __device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merged<HD, G, MT>(L) + MT * G * pstride<HD>(); }
 
@@ -1186,8 +1186,8 @@ __device__ __forceinline__ float* attn_kscales(const Lds& L) { return attn_merge
 // steps), or one row per position of a multi-token step after the tile's work areas (and, INT8 KV,
 // after the split's scales).
 template <int HD, int G, bool KV8, int MT>
-__device__ __forceinline__ float* rope_rows(const Lds& L) {
-  return MT == 1 ? L.small + SM_ROPE : attn_kscales<HD, G, MT>(L) + (KV8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0);
+__device__ __forceinline__ float* rope_rows(const Lds& L, int kv8_span) {
+  return MT == 1 ? L.small + SM_ROPE : attn_kscales<HD, G, MT>(L) + (KV8 ? 2 * kv8_span : 0);
 }
 
 // The split [lo, hi) that split sp of S covers at attended length L_att (positions < 2^31).
@@ -1251,7 +1251,7 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
   int slo = 0, shi = 0;
   if (KV8) split_bounds(a.S, sp, pos + MT, slo, shi);
   float* kss = attn_kscales<HD, G, MT>(L);
-  float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
+  float* vss = kss + a.kv8_span;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const bool own_cur = KV8 && slo <= pos + t && pos + t < shi;
@@ -1274,7 +1274,7 @@ __device__ __forceinline__ void attn_lds_prep(const KernelArgs& a, const Lds& L,
       }
       float r0 = 0.f, r1 = 0.f;
       if (lane < HALF) {
-        const float* cs = rope_rows<HD, G, KV8, MT>(L) + t * HD + lane * 2;
+        const float* cs = rope_rows<HD, G, KV8, MT>(L, a.kv8_span) + t * HD + lane * 2;
         const float co = cs[0], si = cs[1];
         r0 = u0 * co - u1 * si;
         r1 = u1 * co + u0 * si;
@@ -1570,7 +1570,7 @@ __device__ __forceinline__ void compute_attention(const KernelArgs& a, const Lds
   const __amdgpu_buffer_rsrc_t rk = rsrc(kv_head_base<KV8>(a.kv_k, kvrow0, HD));
   const __amdgpu_buffer_rsrc_t rv = rsrc(kv_head_base<KV8>(a.kv_v, kvrow0, HD));
   const float* kss = attn_kscales<HD, G, MT>(L) - rg.lo;  // (KV8) scales by position
-  const float* vss = kss + MAX_SPLIT_POSITIONS_KV8;
+  const float* vss = kss + a.kv8_span;
   const int dummy = (int)a.kv_cap - 1;
   // Running state per query head: m[h] is the same in every lane (the largest score the wave has
   // seen so far, base 2); l[h] and acc[h][] are this lane's sums over its positions, weighted
@@ -2049,7 +2049,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
           if (e0 + lane < sn) {
             const int64_t g = kvrow0 + slo + e0 + lane;
             stage_dword(a.kv_ks + g, kl + 4u * (uint32_t)e0);
-            stage_dword(a.kv_vs + g, kl + 4u * (uint32_t)(MAX_SPLIT_POSITIONS_KV8 + e0));
+            stage_dword(a.kv_vs + g, kl + 4u * (uint32_t)(a.kv8_span + e0));
           }
         }
       }
@@ -2059,7 +2059,7 @@ __device__ __forceinline__ bool gather_inputs(const KernelArgs& a, const Lds& L,
       if (CTRL && lane < HALF) {
 #pragma unroll
         for (int tp = 0; tp < MT; ++tp) {
-          float* rr = rope_rows<HD, G, KV8, MT>(L) + tp * HD;
+          float* rr = rope_rows<HD, G, KV8, MT>(L, a.kv8_span) + tp * HD;
           rr[2 * lane] = cs[tp].x;
           rr[2 * lane + 1] = cs[tp].y;
         }

@@ -62,9 +62,10 @@ constexpr int32_t MAX_TOP_K = 32;
 // KV cache formats: BF16 rows, or INT8 codes with one FP32 scale per (layer, KV head, position) and
 // keys smoothed by a per-(layer, KV head, channel) factor.
 enum : int32_t { KVFMT_BF16 = 0, KVFMT_INT8 = 1 };
-// INT8 KV: an attention tile stages its split's per-position K and V scales in LDS; at most this many
-// positions per split (the planner raises the split count, or rejects the plan).
-constexpr int32_t MAX_SPLIT_POSITIONS_KV8 = 2048;  // KV capacity limit: positions and per-head row offsets stay 32-bit
+// INT8 KV: an attention tile stages its split's per-position K and V scales in LDS, in an area of the
+// plan's kv8_span positions each (the longest split rounded up to 64); at most this many positions
+// per split (the planner raises the split count, or rejects the plan).
+constexpr int32_t MAX_SPLIT_POSITIONS_KV8 = 4096;
 
 struct TileDesc {   // 32 bytes
   int32_t kind;
@@ -179,6 +180,7 @@ struct KernelArgs {
   int32_t mt;                // positions per step: 1 (decode), or 2 .. MAX_STEP_TOKENS (verify plans: every
                              // step runs mt consecutive teacher-forced positions through each tile)
   int64_t ll_tok;            // words between the tagged buffers of consecutive positions of a step
+  int32_t kv8_span;          // INT8 KV: positions of each of the LDS scale areas (K, then V) of a split
 };
 
 }  // namespace tiles

@@ -127,7 +127,7 @@ uint64_t plan_checksum(const HostPlan& p) {
                           p.final_norm_off, p.embed_off, p.embed_stride, p.packed_bytes, p.lds_vec_floats,
                           p.lds_part_floats, p.lds_xres_floats, p.lds_bytes, p.ll_words, p.lds_stage_floats,
                           p.stage_batches, p.top_k, (int64_t)float_bits(p.temperature), (int64_t)float_bits(p.top_p),
-                          p.kv8, p.mt};
+                          p.kv8, p.mt, p.kv8_span};
   mix(dims, sizeof(dims));
   if (!p.waves.empty()) mix(p.waves.data(), p.waves.size() * sizeof(WaveDesc));
   if (!p.tiles.empty()) mix(p.tiles.data(), p.tiles.size() * sizeof(TileDesc));
@@ -257,7 +257,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (p.kv8 && cfg.kv_splits <= 0)
     p.S = std::max<int32_t>(p.S, (int32_t)((s.max_positions + MAX_SPLIT_POSITIONS_KV8 - 1) / MAX_SPLIT_POSITIONS_KV8));
   if (p.kv8 && (s.max_positions + p.S - 1) / p.S > MAX_SPLIT_POSITIONS_KV8)
-    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 2048 positions per split (raise kv_splits)");
+    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 4096 positions per split (raise kv_splits)");
   // query heads per attention tile: the group's heads spread over as many tiles as the workers
   // allow (each re-reads the split's K/V rows; attention is bound by arithmetic per head)
   if (cfg.attn_heads > 0) {
@@ -280,7 +280,10 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   if (p.mt > 1 && cfg.kv_splits <= 0 && (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     p.S = std::max<int32_t>(1, W / (s.n_kv * (s.G / p.T)));
   if (p.kv8 && (s.max_positions + p.S - 1) / p.S > MAX_SPLIT_POSITIONS_KV8)
-    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 2048 positions per split (raise kv_splits, or fewer positions)");
+    return fail(err, TILES_E_CONFIG, "INT8 KV: more than 4096 positions per split (raise kv_splits, or fewer positions)");
+  // INT8 KV: the LDS scale areas hold the longest split (a split of a launch's step never holds more
+  // positions than one at the cache's capacity)
+  if (p.kv8) p.kv8_span = (int32_t)round_up((s.max_positions + p.S - 1) / p.S, 64);
   if (p.S < 1 || (int64_t)p.S * s.n_kv * (s.G / p.T) > W)
     return fail(err, TILES_E_CONFIG, "kv_splits * n_kv_heads * (query heads per KV head / attn_heads) exceeds workers");
   const int64_t part_bytes = (int64_t)s.n_heads * p.S * (s.hd + 4) * 4;
@@ -559,7 +562,7 @@ int build_plan(const tiles_config_t& cfg, int32_t n_workers, HostPlan& p, std::s
   for (const WaveDesc& wd : p.waves) part = std::max(part, std::min(wd.max_rows, brows) * NCOMP * mt);
   // attention tile: q[G][hd], k[hd], v[hd], the compute-wave states [NCOMP][G][hd + 4] and the merged partial
   const int32_t ps = s.hd + 4;
-  part = std::max(part, (int32_t)attn_lds_floats(p) + (p.kv8 ? 2 * MAX_SPLIT_POSITIONS_KV8 : 0));
+  part = std::max(part, (int32_t)attn_lds_floats(p) + 2 * p.kv8_span);
   part = std::max(part, mt * p.S * ps);  // one head's splits (combine tile)
   if (p.combine_in_o && mt == 1) part = std::max(part, s.n_heads * p.S * ps);  // all splits (o_proj prologue)
   if (p.combine_in_o && mt > 1) part = std::max(part, (int32_t)(mt_merge_floats(p) - (int64_t)mt * vec));
@@ -1015,8 +1018,9 @@ int validate_plan(const HostPlan& p, std::string& err) {
     return fail(err, TILES_E_PLAN, "LDS residual area too small");
   if (p.kv8) {
     const int64_t np = (s.max_positions + p.S - 1) / p.S;
-    if (np > MAX_SPLIT_POSITIONS_KV8) return fail(err, TILES_E_PLAN, "INT8 KV: a split longer than 2048 positions");
-    if (p.lds_part_floats < attn_lds_floats(p) + 2 * MAX_SPLIT_POSITIONS_KV8)
+    if (np > p.kv8_span || p.kv8_span > MAX_SPLIT_POSITIONS_KV8 || p.kv8_span % 64 != 0)
+      return fail(err, TILES_E_PLAN, "INT8 KV: a split longer than its LDS scale area, or than 4096 positions");
+    if (p.lds_part_floats < attn_lds_floats(p) + 2 * (int64_t)p.kv8_span)
       return fail(err, TILES_E_PLAN, "LDS too small for an INT8 KV split's scales");
   }
   if (p.top_k < 0 || p.top_k > MAX_TOP_K || p.top_k > s.V || (p.top_k > 0 && p.W > 256))

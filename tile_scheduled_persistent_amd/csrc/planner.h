@@ -62,6 +62,7 @@ struct HostPlan {
   int32_t mt = 1;              // positions per step: 1 (decode), 2 .. 4 (verify plans)
   int32_t top_k = 0;           // sampled decoding: 1 .. MAX_TOP_K; 0 greedy
   int32_t kv8 = 0;             // 1: INT8 KV cache (codes, per-position scales, smoothed keys)
+  int32_t kv8_span = 0;        // INT8 KV: positions per LDS scale area (the longest split, rounded up to 64)
   float temperature = 1.0f, top_p = 1.0f;
   std::vector<WaveDesc> waves;
   std::vector<TileDesc> tiles; // [n_waves][W]
