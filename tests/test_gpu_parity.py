@@ -948,6 +948,62 @@ def test_verify_plan_against_the_oracle(shape, mt, weights, combine):
                   f"{stats['logit_abs_max']:.2e}, tokens checked {stats['tokens_checked']}", flush=True)
 
 
+@pytest.mark.parametrize("shape,mt,kvfmt", [("tiny", 3, "bf16"), ("wide", 2, "int8"), ("qk128", 4, "bf16")])
+def test_verify_plan_repeatable_and_chunk_invariant(shape, mt, kvfmt):
+    """A verify plan's results repeat bit for bit (argmax, logits, accepted count, every cache byte),
+    and one call of 12 positions equals two calls split at a step boundary (6 + 6, or 8 + 4 at 4
+    positions per step), with drafts that are all accepted, bit for bit."""
+    mdl = {"tiny": TINY, "wide": WIDE, "qk128": QK128}[shape]
+    s = Setup(mdl, 96, 60, kv=kvfmt)
+    tok = synth.make_tokens(mdl, 1)[0]
+    m = 12
+    with s.plan() as dplan:
+        _, g, _ = _greedy_continuation(s, dplan, tok, m)
+    g = [int(x) for x in g]
+
+    def cache_bytes(kv):
+        if kvfmt == "int8":
+            return [kv.k.clone(), kv.k_scale.clone(), kv.v_scale.clone()]
+        return [kv.k.clone(), kv.v.clone()]
+
+    def run(plan, calls):
+        kv = s.fresh_kv(plan)
+        kv.length = 60
+        argmax, logits, accepted = [], [], []
+        for toks in calls:
+            out_l = torch.zeros((len(toks), mdl.vocab), dtype=torch.float32, device="cuda")
+            a, n, _ = plan.verify(kv, toks, out_logits=out_l)
+            argmax += [int(x) for x in a]
+            logits.append(out_l.cpu().numpy().view(np.uint32))
+            accepted.append(n)
+        return argmax, np.concatenate(logits), accepted, cache_bytes(kv), kv.length
+
+    drafts = list(g[:m - 1])
+    drafts[6] = (g[6] + 9) % mdl.vocab
+    c1 = 8 if mt == 4 else 6
+    with s.plan(tokens_per_step=mt) as plan:
+        assert plan.info().tokens_per_step == mt
+        r1 = run(plan, [[tok] + drafts])
+        r2 = run(plan, [[tok] + drafts])
+        assert r1[0] == r2[0] and np.array_equal(r1[1], r2[1]) and r1[2] == r2[2] and r1[4] == r2[4]
+        assert all(torch.equal(x, y) for x, y in zip(r1[3], r2[3]))
+        # drafts the plan accepts in full: the decode plan's continuation, corrected with this plan's own
+        # argmax wherever a near-tie decides otherwise
+        seq = list(g[:m - 1])
+        for _ in range(m):
+            whole = run(plan, [[tok] + seq])
+            if whole[2][0] == m - 1:
+                break
+            seq[whole[2][0]] = whole[0][whole[2][0]]
+        assert whole[2] == [m - 1], whole[2]
+        split = run(plan, [[tok] + seq[:c1 - 1], [seq[c1 - 1]] + seq[c1:m - 1]])
+        assert split[2] == [c1 - 1, m - c1 - 1], split[2]
+        assert whole[0] == split[0] and np.array_equal(whole[1], split[1]) and whole[4] == split[4]
+        assert all(torch.equal(x, y) for x, y in zip(whole[3], split[3]))
+    print(f"{shape} mt={mt} {kvfmt}: repeats and a {c1} + {m - c1} split identical; accepted {r1[2][0]} of the "
+          f"drafts with a wrong token at position 7", flush=True)
+
+
 @pytest.mark.parametrize("shape,heads,mt", [("qk128", 1, 2), ("qk128", 2, 2), ("tiny", 2, 2), ("qk128", 1, 3),
                                              ("qk128", 1, 4)])
 def test_verify_plan_heads_per_attention_tile(shape, heads, mt):
